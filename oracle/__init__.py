@@ -1,0 +1,140 @@
+"""CPU oracle for the attention forward pass (ctypes wrapper around fa_oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+baseline of the benchmark may import this package.  The GPU library never
+links or calls it, and it imports nothing from the GPU package.
+
+Functions (all fp64, numpy in / numpy out):
+  attention(q, k, v, scale, causal, rows=None) -> (o, lse)
+      the plain two-pass definition (page "FlashAttention技术演进全景图"
+      §2.1/§2.3; output conventions of "FlashAttention-2实现与优化" §3.1).
+  attention_online(q, k, v, scale, causal, bq, bk) -> (o, lse)
+      the pages' tiled online-softmax recurrence ("FlashAttention-2实现与优化"
+      §3.1), used only to show that it reaches the two-pass result.
+  threads() -> int   OpenMP threads the oracle uses.
+
+Parity status: pinned by tests/test_oracle_pins.py (closed forms, invariants,
+brute force, a library witness and hand-derived worked examples).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "fa_oracle.c")
+LIBRARY = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(out: str = LIBRARY, source: str = SOURCE, extra_flags=()) -> str:
+    """Compile fa_oracle.c with gcc (-O2, OpenMP, IEEE semantics kept)."""
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+           "-Wall", "-Wextra", *extra_flags, "-o", tmp, source, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def _bind(path: str):
+    lib = ctypes.CDLL(path)
+    dp = ctypes.POINTER(ctypes.c_double)
+    i64 = ctypes.c_int64
+    lib.fa_oracle_attention.restype = ctypes.c_int
+    lib.fa_oracle_attention.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64, i64,
+                                        ctypes.c_double, ctypes.c_int,
+                                        ctypes.POINTER(i64), i64]
+    lib.fa_oracle_online.restype = ctypes.c_int
+    lib.fa_oracle_online.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64, i64,
+                                     ctypes.c_double, ctypes.c_int, i64, i64]
+    lib.fa_oracle_threads.restype = ctypes.c_int
+    lib.fa_oracle_threads.argtypes = []
+    return lib
+
+
+def load(path: Optional[str] = None):
+    """Load (building first if absent) the oracle library."""
+    global _lib
+    if path is not None:
+        return _bind(path)
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            build()
+        _lib = _bind(LIBRARY)
+    return _lib
+
+
+def _as4d(x) -> np.ndarray:
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    if a.ndim == 3:
+        a = a[:, None]
+    if a.ndim != 4:
+        raise ValueError("expected [B,N,D] or [B,H,N,D]")
+    return a
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def attention(q, k, v, scale: float, causal: bool, rows=None, lib=None
+              ) -> Tuple[np.ndarray, np.ndarray]:
+    """Two-pass fp64 attention.  q [B,(H,)Nq,D]; k, v [B,(H,)Nk,D].
+
+    Returns o and lse shaped like q / q[..., 0] (or [len(rows), D] and
+    [len(rows)] when ``rows`` lists flat row ids (b*H + h)*Nq + i).
+    """
+    lib = lib or load()
+    squeeze = np.asarray(q).ndim == 3
+    q4, k4, v4 = _as4d(q), _as4d(k), _as4d(v)
+    B, H, Nq, D = q4.shape
+    Nk = k4.shape[2]
+    if k4.shape != (B, H, Nk, D) or v4.shape != (B, H, Nk, D):
+        raise ValueError("q/k/v shapes disagree")
+    if rows is None:
+        o = np.empty((B, H, Nq, D))
+        lse = np.empty((B, H, Nq))
+        rp, nr = None, 0
+    else:
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        o = np.empty((r.size, D))
+        lse = np.empty((r.size,))
+        rp, nr = r.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), r.size
+    st = lib.fa_oracle_attention(_ptr(q4), _ptr(k4), _ptr(v4), _ptr(o), _ptr(lse),
+                                 B, H, Nq, Nk, D, float(scale), int(bool(causal)),
+                                 rp, nr)
+    if st != 0:
+        raise RuntimeError(f"oracle failed with status {st}")
+    if rows is None and squeeze:
+        return o[:, 0], lse[:, 0]
+    return o, lse
+
+
+def attention_online(q, k, v, scale: float, causal: bool, bq: int, bk: int, lib=None
+                     ) -> Tuple[np.ndarray, np.ndarray]:
+    """The pages' tiled online recurrence in fp64 (self-check only)."""
+    lib = lib or load()
+    squeeze = np.asarray(q).ndim == 3
+    q4, k4, v4 = _as4d(q), _as4d(k), _as4d(v)
+    B, H, Nq, D = q4.shape
+    Nk = k4.shape[2]
+    o = np.empty((B, H, Nq, D))
+    lse = np.empty((B, H, Nq))
+    st = lib.fa_oracle_online(_ptr(q4), _ptr(k4), _ptr(v4), _ptr(o), _ptr(lse),
+                              B, H, Nq, Nk, D, float(scale), int(bool(causal)),
+                              int(bq), int(bk))
+    if st != 0:
+        raise RuntimeError(f"oracle failed with status {st}")
+    if squeeze:
+        return o[:, 0], lse[:, 0]
+    return o, lse
+
+
+def threads(lib=None) -> int:
+    return int((lib or load()).fa_oracle_threads())

@@ -1,0 +1,245 @@
+/*
+ * fa_oracle.c -- plain, slow CPU reference for the attention forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file; it exists so that tests, the smoke check and the CPU
+ * baseline of the benchmark have an independent answer to compare with.  It
+ * shares no code, header, table or constant with the GPU library.
+ *
+ * Sources (cited by page title and section):
+ *   [impl] "FlashAttention-2实现与优化：高效注意力机制详解"
+ *          §3.1 (PyTorch forward), §3.2 (Triton forward), §4.2-4.3.
+ *   [evo]  "FlashAttention技术演进全景图" §2.1 (matmul -> softmax -> matmul),
+ *          §2.3 (max-subtracted softmax).
+ *   [mem]  "解释FlashAttention的显存优化原理" §一.1 (standard attention).
+ *
+ * Everything is computed in IEEE double precision, one query row at a time.
+ * Inputs arrive as double arrays (bf16 and fp32 values are exact in double).
+ * Layout: q [B,H,Nq,D], k and v [B,H,Nk,D], o [B,H,Nq,D], lse [B,H,Nq], all
+ * contiguous row-major.  "rows" optionally restricts the computation to a
+ * list of flat row ids r = (b*H + h)*Nq + i; then o is [nrows,D] and lse is
+ * [nrows], in list order.
+ *
+ * Readings of the pages that this file adopts:
+ *   - the valid key set of row i is { j < Nk : !causal || j <= i } (global
+ *     indices from 0, "top-left" alignment), so a causal row never sees a
+ *     later key and every row sees at least key 0 when Nk >= 1;
+ *   - masked keys are excluded from the softmax (the pages' -1e6 fill gives
+ *     the same numbers once a row has one valid key, see fa_oracle_online);
+ *   - keys j >= Nk never exist: a ragged last tile is cut at Nk;
+ *   - lse uses the natural logarithm: L = m + ln(l).
+ *
+ * Parity status: pinned (see tests/test_oracle_pins.py).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_OK = 0, ORACLE_EINVAL = 1, ORACLE_ENOMEM = 2 };
+
+/* Number of OpenMP threads a parallel region will use (1 without OpenMP). */
+int fa_oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+static int bad_shape(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D)
+{
+    return B < 1 || H < 1 || Nq < 1 || Nk < 1 || D < 1;
+}
+
+/* Number of keys row i may attend to: all Nk, or keys 0..i when causal. */
+static int64_t valid_keys(int64_t i, int64_t Nk, int causal)
+{
+    if (!causal)
+        return Nk;
+    return (i + 1 < Nk) ? i + 1 : Nk;
+}
+
+/*
+ * Two-pass attention, the plain definition ([evo] §2.1, §2.3; [mem] §一.1;
+ * output conventions from [impl] §3.1/§3.2):
+ *     s_j = scale * <q_i, k_j>               for j in the valid set
+ *     m   = max_j s_j
+ *     w_j = exp(s_j - m),  l = sum_j w_j
+ *     o_i = (sum_j w_j v_j) / l
+ *     L_i = m + ln l
+ */
+int fa_oracle_attention(const double *q, const double *k, const double *v,
+                        double *o, double *lse,
+                        int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+                        double scale, int causal,
+                        const int64_t *rows, int64_t nrows)
+{
+    if (!q || !k || !v || !o || !lse || bad_shape(B, H, Nq, Nk, D))
+        return ORACLE_EINVAL;
+    const int64_t total = B * H * Nq;
+    const int64_t count = rows ? nrows : total;
+    if (rows) {
+        for (int64_t t = 0; t < nrows; ++t)
+            if (rows[t] < 0 || rows[t] >= total)
+                return ORACLE_EINVAL;
+    }
+    int failed = 0;
+
+#pragma omp parallel
+    {
+        double *w = (double *)malloc((size_t)Nk * sizeof(double));
+        if (!w) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 8)
+        for (int64_t t = 0; t < count; ++t) {
+            if (!w)
+                continue;
+            const int64_t r = rows ? rows[t] : t;
+            const int64_t bh = r / Nq;
+            const int64_t i = r % Nq;
+            const double *qi = q + r * D;
+            const double *kb = k + bh * Nk * D;
+            const double *vb = v + bh * Nk * D;
+            const int64_t n = valid_keys(i, Nk, causal);
+
+            /* pass 1: scores and their maximum */
+            double m = -INFINITY;
+            for (int64_t j = 0; j < n; ++j) {
+                double dot = 0.0;
+                for (int64_t d = 0; d < D; ++d)
+                    dot += qi[d] * kb[j * D + d];
+                w[j] = scale * dot;
+                if (w[j] > m)
+                    m = w[j];
+            }
+            /* pass 2: max-subtracted exponentials and their sum */
+            double l = 0.0;
+            for (int64_t j = 0; j < n; ++j) {
+                w[j] = exp(w[j] - m);
+                l += w[j];
+            }
+            /* weighted sum of values, normalised by l */
+            double *oi = o + t * D;
+            for (int64_t d = 0; d < D; ++d)
+                oi[d] = 0.0;
+            for (int64_t j = 0; j < n; ++j)
+                for (int64_t d = 0; d < D; ++d)
+                    oi[d] += w[j] * vb[j * D + d];
+            for (int64_t d = 0; d < D; ++d)
+                oi[d] /= l;
+            lse[t] = m + log(l);
+        }
+        free(w);
+    }
+    return failed ? ORACLE_ENOMEM : ORACLE_OK;
+}
+
+/*
+ * The tiled online-softmax recurrence of [impl] §3.1 (the running statistics
+ * m, l and an unnormalised accumulator, updated once per key tile), in double
+ * precision, used only to show that the recurrence reaches the two-pass
+ * result.  Query rows are grouped in tiles of bq rows and keys in tiles of bk
+ * keys; the last tile of each is cut at Nq / Nk.  Causally hidden keys inside
+ * a visited tile get the pages' fill value -1e6 ([impl] §3.1, §4.3); every key
+ * tile is visited, as on the pages (no tile skipping).  Per key tile:
+ *     m' = max(m, max_j s_j)
+ *     p_j = exp(s_j - m')
+ *     l  = exp(m - m') * l + sum_j p_j
+ *     acc = exp(m - m') * acc + sum_j p_j v_j
+ * and at the end o = acc / l, L = m + ln l ([impl] §3.1).
+ */
+int fa_oracle_online(const double *q, const double *k, const double *v,
+                     double *o, double *lse,
+                     int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+                     double scale, int causal, int64_t bq, int64_t bk)
+{
+    if (!q || !k || !v || !o || !lse || bad_shape(B, H, Nq, Nk, D) || bq < 1 ||
+        bk < 1)
+        return ORACLE_EINVAL;
+    const int64_t ntiles_q = (Nq + bq - 1) / bq;
+    int failed = 0;
+
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)(bq * bk) * sizeof(double));
+        double *m = (double *)malloc((size_t)bq * sizeof(double));
+        double *l = (double *)malloc((size_t)bq * sizeof(double));
+        double *acc = (double *)malloc((size_t)(bq * D) * sizeof(double));
+        const int ok = s && m && l && acc;
+        if (!ok) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for collapse(2) schedule(dynamic, 1)
+        for (int64_t bh = 0; bh < B * H; ++bh) {
+            for (int64_t tq = 0; tq < ntiles_q; ++tq) {
+                if (!ok)
+                    continue;
+                const int64_t i0 = tq * bq;
+                const int64_t ni = (i0 + bq <= Nq) ? bq : Nq - i0;
+                const double *kb = k + bh * Nk * D;
+                const double *vb = v + bh * Nk * D;
+                for (int64_t r = 0; r < ni; ++r) {
+                    m[r] = -INFINITY;
+                    l[r] = 0.0;
+                    for (int64_t d = 0; d < D; ++d)
+                        acc[r * D + d] = 0.0;
+                }
+                for (int64_t j0 = 0; j0 < Nk; j0 += bk) {
+                    const int64_t nj = (j0 + bk <= Nk) ? bk : Nk - j0;
+                    for (int64_t r = 0; r < ni; ++r) {
+                        const int64_t i = i0 + r;
+                        const double *qi = q + (bh * Nq + i) * D;
+                        double *sr = s + r * bk;
+                        double tmax = -INFINITY;
+                        for (int64_t c = 0; c < nj; ++c) {
+                            const int64_t j = j0 + c;
+                            double dot = 0.0;
+                            for (int64_t d = 0; d < D; ++d)
+                                dot += qi[d] * kb[j * D + d];
+                            sr[c] = scale * dot;
+                            if (causal && !(i >= j))
+                                sr[c] = -1e6;
+                            if (sr[c] > tmax)
+                                tmax = sr[c];
+                        }
+                        const double mnew = (m[r] > tmax) ? m[r] : tmax;
+                        const double alpha = exp(m[r] - mnew);
+                        double psum = 0.0;
+                        for (int64_t c = 0; c < nj; ++c) {
+                            sr[c] = exp(sr[c] - mnew);
+                            psum += sr[c];
+                        }
+                        l[r] = alpha * l[r] + psum;
+                        double *ar = acc + r * D;
+                        for (int64_t d = 0; d < D; ++d) {
+                            double pv = 0.0;
+                            for (int64_t c = 0; c < nj; ++c)
+                                pv += sr[c] * vb[(j0 + c) * D + d];
+                            ar[d] = alpha * ar[d] + pv;
+                        }
+                        m[r] = mnew;
+                    }
+                }
+                for (int64_t r = 0; r < ni; ++r) {
+                    const int64_t row = bh * Nq + i0 + r;
+                    for (int64_t d = 0; d < D; ++d)
+                        o[row * D + d] = acc[r * D + d] / l[r];
+                    lse[row] = m[r] + log(l[r]);
+                }
+            }
+        }
+        free(s);
+        free(m);
+        free(l);
+        free(acc);
+    }
+    return failed ? ORACLE_ENOMEM : ORACLE_OK;
+}

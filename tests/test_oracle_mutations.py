@@ -1,0 +1,62 @@
+"""CPU tests: the pins are sensitive.  Each case plants one plausible mistake
+in a private copy of the oracle source (a dropped term, a wrong index or
+sign, a transposed operand, the wrong log base, an off-by-one mask), builds
+it into a temporary library, and checks that the pin battery rejects it.
+The real oracle is never modified."""
+import os
+
+import pytest
+
+import oracle
+from pins import ALL_PINS
+
+MUTATIONS = {
+    "drop_scale": ("w[j] = scale * dot;", "w[j] = dot;"),
+    "diagonal_hidden": ("return (i + 1 < Nk) ? i + 1 : Nk;", "return (i < Nk) ? i : Nk;"),
+    "log2_lse": ("lse[t] = m + log(l);", "lse[t] = m + log2(l);"),
+    "lse_without_max": ("lse[t] = m + log(l);", "lse[t] = log(l);"),
+    "no_normalisation": ("oi[d] /= l;", "oi[d] /= 1.0;"),
+    "transposed_values": ("oi[d] += w[j] * vb[j * D + d];",
+                          "oi[d] += w[j] * vb[d * Nk + j];"),
+    "transposed_keys": ("dot += qi[d] * kb[j * D + d];\n                w[j]",
+                        "dot += qi[d] * kb[d * Nk + j];\n                w[j]"),
+    "max_not_subtracted": ("w[j] = exp(w[j] - m);", "w[j] = exp(w[j]);"),
+    "min_instead_of_max": ("if (w[j] > m)\n                    m = w[j];",
+                           "if (w[j] < m || m == -INFINITY)\n                    m = w[j];"),
+    "row_index_uses_nk": ("const int64_t i = r % Nq;", "const int64_t i = r % Nk;"),
+    "squared_weights_in_sum": ("l += w[j];", "l += w[j] * w[j];"),
+    "online_alpha_not_applied_to_acc": ("ar[d] = alpha * ar[d] + pv;", "ar[d] = ar[d] + pv;"),
+    "online_alpha_not_applied_to_l": ("l[r] = alpha * l[r] + psum;", "l[r] = l[r] + psum;"),
+    "online_mask_direction": ("if (causal && !(i >= j))", "if (causal && !(i <= j))"),
+}
+
+
+def _mutated_lib(tmp_path, name, old, new):
+    with open(oracle.SOURCE) as f:
+        src = f.read()
+    assert src.count(old) == 1, f"mutation {name}: pattern must occur exactly once"
+    path = tmp_path / f"{name}.c"
+    path.write_text(src.replace(old, new))
+    so = str(tmp_path / f"lib{name}.so")
+    oracle.build(out=so, source=str(path), extra_flags=("-w",))
+    return oracle.load(so)
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(tmp_path, name):
+    old, new = MUTATIONS[name]
+    lib = _mutated_lib(tmp_path, name, old, new)
+    failures = []
+    for pin in ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, RuntimeError, FloatingPointError) as e:
+            failures.append((pin.__name__, str(e)[:80]))
+    assert failures, f"no pin caught the planted mistake {name!r}"
+
+
+def test_unmutated_source_passes_every_pin(tmp_path):
+    lib = _mutated_lib(tmp_path, "identity", "int fa_oracle_threads(void)",
+                       "int fa_oracle_threads(void)")
+    for pin in ALL_PINS:
+        pin(lib)
