@@ -1,0 +1,201 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one call of fa_fwd (the whole forward pass) over the workload's
+synthetic inputs, which are resident in device memory before timing starts.
+W untimed steps are followed by exactly K timed steps, bracketed by device
+synchronisation.  Prints ONE JSON line: throughput in TFLOP/s counting
+4*B*H*Nq*Nk*D flops (halved when causal), the dominant kernel's roofline
+(HIP-event time per launch on the launch stream against the dense MFMA peak
+of the input type), and the CPU oracle's throughput on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak (B8 N4096 D128 causal)"
+# MI355X published dense peaks (TFLOP/s).
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+HBM_GBPS = 8000.0
+SOURCE = os.path.join(ROOT, "transformer_attention_07_amd", "csrc", "fa_fwd.hip")
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
+
+
+def source_digest() -> str:
+    with open(SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; otherwise None."""
+    path = os.path.join(TRAFFIC_DIR, f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha256") != source_digest():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, target_s: float):
+    """Time the fp64 oracle on the host cores over a bounded sample of rows and
+    express it in the metric's unit (flops of the whole workload / time)."""
+    import numpy as np
+    import oracle
+    from workloads import gen_workload, sample_rows
+
+    q, k, v = gen_workload(w)
+    qn, kn, vn = (t.double().numpy() for t in (q, k, v))
+    scale = 1.0 / math.sqrt(w.D)
+    lib = oracle.load()
+    total = w.rows
+
+    def visible(rows):
+        i = rows % w.N
+        return (i + 1).sum() if w.causal else len(rows) * w.N
+
+    all_rows = np.arange(total)
+    work_total = float(visible(all_rows))
+    probe = sample_rows(total, 64, 7).numpy()
+    t0 = time.perf_counter()
+    oracle.attention(qn, kn, vn, scale, w.causal, rows=probe, lib=lib)
+    t_probe = time.perf_counter() - t0
+    est_full = t_probe * work_total / float(visible(probe))
+    if est_full <= target_s:
+        rows, desc = None, f"all {total} rows of the workload"
+        work = work_total
+    else:
+        n = int(max(64, min(total, 64 * target_s / max(t_probe, 1e-9))))
+        rows = sample_rows(total, n, 8).numpy()
+        work = float(visible(rows))
+        desc = (f"{n} of {total} rows drawn uniformly (seed 8); time scaled to the "
+                f"whole workload by the count of visible keys")
+    t0 = time.perf_counter()
+    oracle.attention(qn, kn, vn, scale, w.causal, rows=rows, lib=lib)
+    elapsed = time.perf_counter() - t0
+    t_full = elapsed * work_total / work
+    return {
+        "value": w.flops() / t_full / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.threads(lib),
+        "kind": "oracle",
+        "sample": desc,
+        "seconds": round(elapsed, 3),
+        "seconds_full_workload": round(t_full, 3),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None,
+                    help="workload name (default: B=8 N=4096 D=128 causal bf16)")
+    ap.add_argument("--out-f32", action="store_true",
+                    help="store O in fp32 (FA_BF16_OF32) instead of the input type")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the forward pass shards over batch*heads with no exchange; see the "
+              "design notes)", file=sys.stderr)
+        return 2
+
+    import torch
+    import transformer_attention_07_amd as fa
+    from workloads import HEADLINE, WORKLOADS, gen_workload
+
+    name = args.workload or HEADLINE
+    w = WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = (t.to(dev) for t in gen_workload(w))
+    in_dt = q.dtype
+    out_dt = torch.float32 if (args.out_f32 or in_dt == torch.float32) else in_dt
+    code = fa._dtype_code(torch, in_dt, out_dt)
+    o = torch.empty(q.shape, dtype=out_dt, device=dev)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(w.D)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    lib = fa.library()
+    argv = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            w.B, w.H, w.N, w.N, w.D, scale, int(w.causal), code, sp)
+    call = lib.fa_fwd
+
+    for _ in range(args.warmup):
+        st = call(*argv)
+        if st != 0:
+            raise RuntimeError(f"fa_fwd failed: {fa.fa_status_str(st)} "
+                               f"{fa.fa_last_hip_error()}")
+    torch.cuda.synchronize(dev)
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        call(*argv)
+    ev1.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+
+    ms_per_step = wall * 1e3 / args.steps
+    flops = w.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    dkey = "f32" if in_dt == torch.float32 else ("bf16" if in_dt == torch.bfloat16 else "f16")
+    peak = PEAK_TFLOPS[dkey]
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    props = torch.cuda.get_device_properties(dev)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dkey,
+        "data": "synthetic (seeded i.i.d. Gaussian q, k, v)",
+        "config": {"workload": name, "B": w.B, "H": w.H, "Nq": w.N, "Nk": w.N, "D": w.D,
+                   "causal": w.causal, "out": str(out_dt).replace("torch.", ""),
+                   "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic(name),
+                     "kernel_ms": round(kernel_ms, 5)},
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                   "cus": props.multi_processor_count},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

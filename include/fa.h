@@ -1,0 +1,112 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) FlashAttention-2 forward library.
+ *
+ * The operation (page "FlashAttention-2实现与优化：高效注意力机制详解",
+ * §3.1 PyTorch forward and §3.2 Triton forward; page
+ * "解释FlashAttention的显存优化原理" §一.2 tiling): for every batch b, head h
+ * and query row i,
+ *
+ *     s_ij = scale * <q_i, k_j>          for the keys j visible to row i
+ *     O_i  = sum_j softmax_j(s_i.) v_j
+ *     L_i  = ln sum_j exp(s_ij)          (the per-row logsumexp, m + ln l)
+ *
+ * computed tile by tile with an online softmax, so the Nq x Nk score matrix
+ * never exists in device memory.  With causal != 0, key j is visible to row
+ * i iff j <= i (indices from 0 in both sequences, the masking rule of the
+ * same page, §4.3); otherwise every key j < Nk is visible.
+ *
+ * Layout.  q is [B,H,Nq,D], k and v are [B,H,Nk,D], o is [B,H,Nq,D] and lse
+ * is [B,H,Nq]; all contiguous, row-major, in device memory.  Element types:
+ *
+ *   dtype           q, k, v   o      lse   contraction
+ *   FA_F32          fp32      fp32   fp32  fp32 products, fp32 sums
+ *   FA_BF16         bf16      bf16   fp32  bf16 products, fp32 sums
+ *   FA_BF16_OF32    bf16      fp32   fp32  as FA_BF16, O kept in fp32
+ *   FA_F16          fp16      fp16   fp32  fp16 products, fp32 sums
+ *   FA_F16_OF32     fp16      fp32   fp32  as FA_F16, O kept in fp32
+ *
+ * With 16-bit inputs the softmax, its statistics and the O accumulator are
+ * fp32; the probabilities are rounded to the input type before they
+ * multiply V, as in the Triton forward of the same page (§3.2, §4.2).  O is
+ * rounded to its storage type once, at the end.
+ *
+ * Ownership.  Every pointer belongs to the caller.  The library allocates,
+ * frees and synchronises nothing; it only enqueues work on `stream`.
+ *
+ * Thread safety.  Calls may be made concurrently from any host thread.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage types of (q, k, v ; o).  lse is always fp32. */
+enum fa_dtype {
+    FA_F32 = 0,
+    FA_BF16 = 1,
+    FA_BF16_OF32 = 2,
+    FA_F16 = 3,
+    FA_F16_OF32 = 4
+};
+
+/* Status codes.  Validation errors are reported before any device work is
+ * enqueued, so on a non-zero return nothing has been written. */
+enum fa_status {
+    FA_OK = 0,
+    FA_ERR_NULLPTR = 1,  /* q, k, v, o or lse is NULL                        */
+    FA_ERR_SHAPE = 2,    /* B, H, Nq or Nk < 1, or a size overflows          */
+    FA_ERR_HEAD_DIM = 3, /* D not in {16, 32, 64, 128}                       */
+    FA_ERR_DTYPE = 4,    /* dtype is not one of enum fa_dtype                */
+    FA_ERR_SCALE = 5,    /* scale is NaN or infinite                          */
+    FA_ERR_ALIGN = 6,    /* q, k, v or o not 16-byte aligned, lse not 4-byte */
+    FA_ERR_HIP = 7,      /* the HIP runtime refused the launch               */
+    FA_ERR_OVERLAP = 8   /* o or lse overlaps q, k, v or each other          */
+};
+
+/*
+ * fa_fwd -- enqueue one attention forward pass on `stream`.
+ *
+ *   q          device pointer, [B,H,Nq,D] of the dtype's input type
+ *   k, v       device pointers, [B,H,Nk,D] of the input type
+ *   o          device pointer, [B,H,Nq,D] of the dtype's output type (written)
+ *   lse        device pointer, [B,H,Nq] fp32, natural-log logsumexp (written)
+ *   B, H       batch size and number of heads (>= 1)
+ *   Nq, Nk     query and key sequence lengths (>= 1; need not be equal, need
+ *              not be multiples of any tile size)
+ *   D          head dimension: 16, 32, 64 or 128
+ *   scale      multiplier of q.k (the pages use 1/sqrt(D)); any finite value
+ *   causal     0: all keys visible; non-zero: key j visible to row i iff j<=i
+ *   dtype      one of enum fa_dtype
+ *   stream     a hipStream_t (NULL = the default stream)
+ *
+ * Returns FA_OK once the work is enqueued (asynchronous, like any launch:
+ * results are valid after the stream is synchronised), a validation error
+ * (nothing enqueued), or FA_ERR_HIP with the runtime's message available
+ * from fa_last_hip_error().  o and lse must not overlap q, k, v or each
+ * other (checked on the host: FA_ERR_OVERLAP).  Each (batch, head) slice is
+ * addressed with 32-bit byte offsets, so (Nq + 128) * D * 4 and
+ * (Nk + 64) * D * 4 must stay below 2^31 (FA_ERR_SHAPE otherwise), as must
+ * B*H*ceil(Nq/128).
+ */
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+           int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+           float scale, int causal, int dtype, void *stream);
+
+/* Static description of a status code; never NULL. */
+const char *fa_status_str(int status);
+
+/* Text of the last FA_ERR_HIP raised on the calling thread ("" if none). */
+const char *fa_last_hip_error(void);
+
+/* Library version, as major*10000 + minor*100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

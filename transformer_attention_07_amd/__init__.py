@@ -1,0 +1,158 @@
+"""Python binding of libfa.so, the MI355X FlashAttention-2 forward library.
+
+The binding marshals arguments only: every step of the forward pass runs in
+the HIP kernels of libfa.so (csrc/fa_fwd.hip).  PyTorch is used to allocate
+the outputs and to name the current HIP stream.  There is no fallback: if
+libfa.so is missing or fails to load, every call raises.
+
+C-ABI mirrors (same names and meaning as include/fa.h):
+    fa_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Nq, Nk, D, scale,
+           causal, dtype, stream) -> status
+    fa_status_str(status) -> str
+    fa_last_hip_error() -> str
+    fa_version() -> int
+Tensor convenience:
+    fwd(q, k, v, causal=False, scale=None, out_dtype=None) -> (o, lse)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "FA_F32", "FA_BF16", "FA_BF16_OF32", "FA_F16", "FA_F16_OF32",
+    "FA_OK", "FA_ERR_NULLPTR", "FA_ERR_SHAPE", "FA_ERR_HEAD_DIM", "FA_ERR_DTYPE",
+    "FA_ERR_SCALE", "FA_ERR_ALIGN", "FA_ERR_HIP", "FA_ERR_OVERLAP",
+    "LIBRARY", "EXPORTS", "library", "fa_fwd", "fa_status_str", "fa_last_hip_error",
+    "fa_version", "fwd", "FaError",
+]
+
+LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_F32, FA_BF16, FA_BF16_OF32, FA_F16, FA_F16_OF32 = 0, 1, 2, 3, 4
+(FA_OK, FA_ERR_NULLPTR, FA_ERR_SHAPE, FA_ERR_HEAD_DIM, FA_ERR_DTYPE, FA_ERR_SCALE,
+ FA_ERR_ALIGN, FA_ERR_HIP, FA_ERR_OVERLAP) = range(9)
+
+# Every symbol include/fa.h declares.
+EXPORTS = ("fa_fwd", "fa_status_str", "fa_last_hip_error", "fa_version")
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def library() -> ctypes.CDLL:
+    """Load libfa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY):
+        raise RuntimeError(
+            f"{LIBRARY} is missing: build it with `python -m "
+            "transformer_attention_07_amd.build` (or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIBRARY)
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
+                           ctypes.c_int, ctypes.c_int, vp]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_status_str.argtypes = [ctypes.c_int]
+    lib.fa_last_hip_error.restype = ctypes.c_char_p
+    lib.fa_last_hip_error.argtypes = []
+    lib.fa_version.restype = ctypes.c_int
+    lib.fa_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, dtype, stream) -> int:
+    """Raw C call; pointers are integers (device addresses) or None."""
+    return int(library().fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, D, float(scale),
+                                int(causal), int(dtype), stream))
+
+
+def fa_status_str(status: int) -> str:
+    return library().fa_status_str(int(status)).decode()
+
+
+def fa_last_hip_error() -> str:
+    return library().fa_last_hip_error().decode()
+
+
+def fa_version() -> int:
+    return int(library().fa_version())
+
+
+def _dtype_code(torch, in_dtype, out_dtype) -> int:
+    table = {
+        (torch.float32, torch.float32): FA_F32,
+        (torch.bfloat16, torch.bfloat16): FA_BF16,
+        (torch.bfloat16, torch.float32): FA_BF16_OF32,
+        (torch.float16, torch.float16): FA_F16,
+        (torch.float16, torch.float32): FA_F16_OF32,
+    }
+    key = (in_dtype, out_dtype)
+    if key not in table:
+        raise ValueError(f"unsupported (input, output) dtypes {key}")
+    return table[key]
+
+
+def fwd(q, k, v, causal: bool = False, scale: Optional[float] = None,
+        out_dtype=None, out=None, stream=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """Attention forward on device tensors.
+
+    q: [B,Nq,D] or [B,H,Nq,D]; k, v: [B,Nk,D] or [B,H,Nk,D]; same dtype
+    (fp32, bf16 or fp16), same device, contiguous.  Returns (o, lse) with o
+    shaped like q in ``out_dtype`` (default: q's dtype) and lse fp32 shaped
+    like q[..., 0].  ``scale`` defaults to 1/sqrt(D).  ``out`` may pass
+    preallocated (o, lse).  Runs on ``stream`` (default: torch's current
+    stream of q's device).
+    """
+    import torch
+
+    if q.dim() not in (3, 4) or k.dim() != q.dim() or v.dim() != q.dim():
+        raise ValueError("q, k, v must all be [B,N,D] or all [B,H,N,D]")
+    three = q.dim() == 3
+    q4 = q.unsqueeze(1) if three else q
+    k4 = k.unsqueeze(1) if three else k
+    v4 = v.unsqueeze(1) if three else v
+    B, H, Nq, D = q4.shape
+    Nk = k4.shape[2]
+    if tuple(k4.shape) != (B, H, Nk, D) or tuple(v4.shape) != (B, H, Nk, D):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} "
+                         f"v{tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on the same GPU device")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    code = _dtype_code(torch, q.dtype, out_dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        o = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+        if o.shape != q.shape or o.dtype != out_dtype or not o.is_contiguous():
+            raise ValueError("out[0] must be contiguous, shaped like q, of out_dtype")
+        if lse.shape != q.shape[:-1] or lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise ValueError("out[1] must be contiguous fp32 shaped like q[..., 0]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                B, H, Nq, Nk, D, scale, causal, code, stream)
+    if st != FA_OK:
+        msg = fa_status_str(st)
+        if st == FA_ERR_HIP:
+            msg += ": " + fa_last_hip_error()
+        raise FaError(st, msg)
+    return o, lse
