@@ -449,65 +449,77 @@ __device__ __forceinline__ uint32_t dma_src(int ins, int lane, int stride) {
   return col < D / 8 ? (uint32_t)(row * D + col * 8) * sizeof(T) : kOutOfRange;
 }
 
-// Orders a steady-state sub-step: each MFMA is followed by the LDS reads that
-// feed the next ones and a slice of the softmax VALU work, so the MFMA pipe
-// and the VALU run side by side and few fragments are live at once.
-template <int NMFMA>
-__device__ __forceinline__ void interleave_schedule() {
-  __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // DS read
-#pragma unroll
-  for (int i = 0; i < NMFMA; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
-    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
-  }
+// gfx9 buffer resource (raw, stride 0): base, num_records = bytes, word 3
+// as for make_rsrc.  Built by hand so it can be an SGPR operand of asm.
+__device__ __forceinline__ u32x4 raw_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, (uint32_t)kRsrcWord3};
+}
+
+// One 16-byte-per-lane global -> LDS load (buffer_load_dwordx4 ... lds).  The
+// 64 lanes' data land at lds_addr + 16 * lane.  Written as asm so that the
+// compiler does not order LDS reads of other ring stages behind it (it
+// cannot tell the stages apart and would wait for every load in flight);
+// ring_barrier() waits for these loads explicitly.
+__device__ __forceinline__ void dma16(u32x4 rs, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
+               "{m0}"(lds_addr)
+               : "memory");
 }
 
 template <typename T, typename OT, int D, bool CAUSAL>
 struct Pipe {
   typedef typename Mfma16<T>::frag frag;
   typedef PipeLayout<T, D> L;
-  static constexpr int QF = D / 16;
+  static constexpr int QF = D / 16;    // K.Q^T MFMAs per 32-key block
   static constexpr int NDB = D / 32;
+  static constexpr int NPV = 2 * NDB;  // P.V MFMAs per 32-key block
+  static_assert(QF == NPV, "slots pair one K.Q^T with one P.V MFMA");
+  static constexpr int NSLOT = QF + NPV;
 
   int lane, wave, l32, g, qw, my_q, Nk;
   float c;
   uint32_t kbase, vbase;  // per-lane LDS byte addresses of fragment 0
   frag qf[QF];
   f32x16 acc[NDB];
-  f32x16 s_cur, s_nxt;
-  frag p_prev[2];  // P of the block waiting for its P.V, rounded to T
+  f32x16 S0, S1;      // S^T blocks (alternate between the two blocks of a tile)
+  frag P0[2], P1[2];  // P blocks rounded to T (alternate likewise)
   float m_use;
   float l;   // half-wave sum of p (fp32): gives L
   float lr;  // half-wave sum of p as rounded to T for P.V: normalises O
 
-  // S^T of the 32 keys in K stage `st`, rows 32*half.. = K Q^T.
-  __device__ __forceinline__ void qk(const lds_char *ring, int st, int half,
-                                     f32x16 &sc) const {
-    const lds_char *kp = ring + kbase + st * L::K_BYTES + half * 32 * L::SK * 16;
-    sc = f32x16{};
-#pragma unroll
-    for (int f = 0; f < QF; ++f) {
-      const frag a = *(const __attribute__((address_space(3))) frag *)(kp + f * 32);
-      sc = Mfma16<T>::mma(a, qf[f], sc);
-    }
+  __device__ __forceinline__ frag kfrag(const lds_char *kp, int f) const {
+    return *(const __attribute__((address_space(3))) frag *)(kp + f * 32);
+  }
+  __device__ __forceinline__ frag vfrag(const lds_char *vp, int m) const {
+    const int ks = m / NDB, db = m % NDB;
+    const lds_char *a0 = vp + ks * 16 * L::SV * 16 + db * 64;
+    const u32x2 lo = read_tr16(a0);
+    const u32x2 hi = read_tr16(a0 + 8 * L::SV * 16);
+    const u32x4 raw = {lo[0], lo[1], hi[0], hi[1]};
+    return __builtin_bit_cast(frag, raw);
+  }
+  __device__ __forceinline__ const lds_char *kptr(const lds_char *ring, int st,
+                                                  int half) const {
+    return ring + kbase + st * L::K_BYTES + half * 32 * L::SK * 16;
+  }
+  __device__ __forceinline__ const lds_char *vptr(const lds_char *ring, int st,
+                                                  int half) const {
+    return ring + vbase + st * L::V_BYTES + half * 32 * L::SV * 16;
   }
 
-  // acc += V^T P^T for the 32 keys in V stage `st`, rows 32*half.., with P
-  // from p_prev.
-  __device__ __forceinline__ void pv(const lds_char *ring, int st, int half) {
-    const lds_char *vp = ring + vbase + st * L::V_BYTES + half * 32 * L::SV * 16;
+  // S^T of a 32-key block = K Q^T (no overlap; prologue only).
+  __device__ __forceinline__ void qk(const lds_char *kp, f32x16 &sc) const {
+    sc = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int f = 0; f < QF; ++f) sc = Mfma16<T>::mma(kfrag(kp, f), qf[f], sc);
+  }
+
+  // acc += V^T P^T of a 32-key block (no overlap; drain only).
+  __device__ __forceinline__ void pv(const lds_char *vp, const frag (&pin)[2]) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const lds_char *a0 = vp + ks * 16 * L::SV * 16 + db * 64;
-        const u32x2 lo = read_tr16(a0);
-        const u32x2 hi = read_tr16(a0 + 8 * L::SV * 16);
-        const u32x4 raw = {lo[0], lo[1], hi[0], hi[1]};
-        acc[db] = Mfma16<T>::mma(__builtin_bit_cast(frag, raw), p_prev[ks], acc[db]);
-      }
-    }
+    for (int m = 0; m < NPV; ++m)
+      acc[m % NDB] = Mfma16<T>::mma(vfrag(vp, m), pin[m / NDB], acc[m % NDB]);
   }
 
   // Hides keys >= Nk and (causal) keys after the row's query: S := -inf.
@@ -520,115 +532,159 @@ struct Pipe {
     }
   }
 
-  // Softmax of one block: moves the exponent reference lazily, writes p
-  // (rounded to T) into p_prev and updates l and lr.  Returns whether the
-  // reference moved for any lane (then acc must be scaled by alpha before the
-  // next P.V).  MASKED: S may hold -inf; the exponent is clamped so a hidden
-  // key gives p = 0 even when c == 0 (where -inf * c is NaN).
-  //
-  // O is normalised by lr, the sum of the probabilities exactly as rounded
-  // for P.V, so the weights applied to V sum to one: with a lagging reference
-  // the largest p is not 1 and its rounding would otherwise scale a nearly
-  // one-hot row.  L uses l, the sum before rounding.
+  // One 32-key block, software-pipelined by hand.  The MFMA stream
+  // alternates K.Q^T of the next block (into sout) with P.V of the previous
+  // block (with pin); after each MFMA the wave issues the LDS reads two
+  // MFMA pairs ahead and one slice of the softmax of this block (on sin,
+  // into pout), so the VALU work runs while the MFMA pipe is busy.  Slices:
+  //   0-1   row maximum of the block
+  //   2     half-wave exchange, lazy move of the exponent reference, alpha
+  //   3-10  p = 2^(c*s - m) and its fp32 sum, two elements per slice
+  //   11-12 rounding of p to T (the P.V operand) and the sum of the rounded p
+  //   13    l, lr
+  // The reference moves per lane, only when the block's maximum exceeds it
+  // by more than kLazy (both half-waves of a query take the same decision);
+  // acc is then scaled by alpha after the block (a rare, wave-uniform
+  // branch).  O is normalised by lr, the sum of p exactly as rounded for
+  // P.V, so the weights applied to V sum to one; L uses l.  MASKED: s may
+  // hold -inf, and the exponent is clamped so a hidden key gives p = 0 even
+  // when c == 0 (where -inf * c is NaN).
   template <bool MASKED>
-  __device__ __forceinline__ bool softmax(f32x16 &sc, float &alpha) {
-    float mx = fmaxf(sc[0], sc[1]);
-#pragma unroll
-    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-    const u32x2 sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mx),
-                                                      __builtin_bit_cast(uint32_t, mx),
-                                                      false, false);
-    mx = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
-    const float mt = mx * c;  // -inf or NaN when the row sees no key in this block
-    const bool need = mt > m_use + kLazy;
-    const bool any = __builtin_amdgcn_ballot_w64(need) != 0;
-    const float m_new = any ? fmaxf(m_use, mt) : m_use;
-    alpha = __builtin_amdgcn_exp2f(m_use - m_new);
-    m_use = m_new;
-    const float nm = -m_new;
-    float psum = 0.f, rsum = 0.f;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      f32x8 p8;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        float e = __builtin_fmaf(sc[8 * hh + t], c, nm);
-        if (MASKED) e = fmaxf(e, -3.0e38f);  // NaN or -inf -> 2^-3e38 = 0
-        const float p = __builtin_amdgcn_exp2f(e);
-        p8[t] = p;
-        psum += p;
-      }
-      p_prev[hh] = __builtin_convertvector(p8, frag);
-      const u32x4 packed = __builtin_bit_cast(u32x4, p_prev[hh]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rsum = Mfma16<T>::pair_sum(packed[i], rsum);
-    }
-    l = l * alpha + psum;
-    lr = lr * alpha + rsum;
-    return any;
-  }
+  __device__ __forceinline__ void block_step(const lds_char *kp, const lds_char *vp,
+                                             f32x16 &sin, f32x16 &sout,
+                                             const frag (&pin)[2], frag (&pout)[2]) {
+    constexpr int NCHUNK = 14;
+    frag kf[QF], vf[NPV];
+    float mx = 0.f, nm = 0.f, alpha = 1.f, psum = 0.f, rsum = 0.f;
+    bool need = false;
+    f32x16 pf;  // p in fp32
+    sout = f32x16{};
 
-  // One sub-step in one basic block: P.V of the previous block, K.Q^T of the
-  // next block and the softmax of the current one.
-  template <bool MASKED>
-  __device__ __forceinline__ void sub_step(const lds_char *ring, int vst, int vhalf,
-                                           int kst, int khalf) {
-    float alpha;
-    pv(ring, vst, vhalf);
-    qk(ring, kst, khalf, s_nxt);
-    const bool any = softmax<MASKED>(s_cur, alpha);
-    if (!MASKED) interleave_schedule<QF + 2 * NDB>();
-    if (any) {
+    auto chunk = [&](int ch) {
+      // Each slice ends with an empty asm that uses its results: the values
+      // must exist at that point, so the compiler cannot sink the slice out
+      // of its MFMA slot (e.g. past the rescale branch, towards its use).
+      if (ch == 0) {
+        mx = fmaxf(sin[0], sin[1]);
+#pragma unroll
+        for (int r = 2; r < 8; ++r) mx = fmaxf(mx, sin[r]);
+        asm volatile("" ::"v"(mx));
+      } else if (ch == 1) {
+#pragma unroll
+        for (int r = 8; r < 16; ++r) mx = fmaxf(mx, sin[r]);
+        asm volatile("" ::"v"(mx));
+      } else if (ch == 2) {
+        const u32x2 sw = __builtin_amdgcn_permlane32_swap(
+            __builtin_bit_cast(uint32_t, mx), __builtin_bit_cast(uint32_t, mx), false, false);
+        mx = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
+        const float mt = mx * c;  // -inf or NaN when the row sees no key of this block
+        need = mt > m_use + kLazy;
+        const float m_new = need ? mt : m_use;
+        alpha = __builtin_amdgcn_exp2f(m_use - m_new);
+        m_use = m_new;
+        nm = -m_new;
+        asm volatile("" ::"v"(alpha), "v"(nm));
+      } else if (ch <= 10) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int r = 2 * (ch - 3) + t;
+          float e = __builtin_fmaf(sin[r], c, nm);
+          if (MASKED) e = fmaxf(e, -3.0e38f);  // NaN or -inf -> 2^-3e38 = 0
+          pf[r] = __builtin_amdgcn_exp2f(e);
+          psum += pf[r];
+        }
+        asm volatile("" ::"v"(pf[2 * (ch - 3)]), "v"(pf[2 * (ch - 3) + 1]), "v"(psum));
+      } else if (ch <= 12) {
+        const int hh = ch - 11;
+        const f32x8 p8 = {pf[8 * hh + 0], pf[8 * hh + 1], pf[8 * hh + 2], pf[8 * hh + 3],
+                          pf[8 * hh + 4], pf[8 * hh + 5], pf[8 * hh + 6], pf[8 * hh + 7]};
+        pout[hh] = __builtin_convertvector(p8, frag);
+        const u32x4 packed = __builtin_bit_cast(u32x4, pout[hh]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rsum = Mfma16<T>::pair_sum(packed[i], rsum);
+        asm volatile("" ::"v"(pout[hh]), "v"(rsum));
+      } else {
+        l = l * alpha + psum;
+        lr = lr * alpha + rsum;
+        asm volatile("" ::"v"(l), "v"(lr));
+      }
+    };
+
+    // fragments for the first two MFMA pairs
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      kf[i] = kfrag(kp, i);
+      vf[i] = vfrag(vp, i);
+    }
+#pragma unroll
+    for (int i = 0; i < QF; ++i) {
+      // K.Q^T, then a slice of the softmax
+      sout = Mfma16<T>::mma(kf[i], qf[i], sout);
+      if (i + 2 < QF) kf[i + 2] = kfrag(kp, i + 2);
+#pragma unroll
+      for (int ch = (2 * i) * NCHUNK / NSLOT; ch < (2 * i + 1) * NCHUNK / NSLOT; ++ch)
+        chunk(ch);
+      __builtin_amdgcn_sched_barrier(0);
+      // P.V, then a slice of the softmax
+      acc[i % NDB] = Mfma16<T>::mma(vf[i], pin[i / NDB], acc[i % NDB]);
+      if (i + 2 < NPV) vf[i + 2] = vfrag(vp, i + 2);
+#pragma unroll
+      for (int ch = (2 * i + 1) * NCHUNK / NSLOT; ch < (2 * i + 2) * NCHUNK / NSLOT; ++ch)
+        chunk(ch);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
     }
   }
 
-  // Block b of this wave: full sub-step, diagonal/tail (masked) sub-step, the
-  // drain (P.V of the wave's last block) or nothing.
+  // Block b of this wave (its tile-local half and ring stages given): full
+  // step, masked step (causal diagonal / key tail), the drain (P.V of the
+  // wave's last block) or nothing.
+  template <bool ODD>
   __device__ __forceinline__ void block(const lds_char *ring, int b, int lastb,
                                         int vst, int vhalf, int kst, int khalf) {
+    f32x16 &sin = ODD ? S1 : S0;
+    f32x16 &sout = ODD ? S0 : S1;
+    frag(&pin)[2] = ODD ? P0 : P1;
+    frag(&pout)[2] = ODD ? P1 : P0;
+    const lds_char *kp = kptr(ring, kst, khalf);
+    const lds_char *vp = vptr(ring, vst, vhalf);
     if (b <= lastb) {
       const int k0 = b * 32;
       const bool need_mask = (k0 + 32 > Nk) || (CAUSAL && k0 + 31 > qw);
       if (need_mask) {
-        mask(s_cur, k0);
-        sub_step<true>(ring, vst, vhalf, kst, khalf);
+        mask(sin, k0);
+        block_step<true>(kp, vp, sin, sout, pin, pout);
       } else {
-        sub_step<false>(ring, vst, vhalf, kst, khalf);
+        block_step<false>(kp, vp, sin, sout, pin, pout);
       }
-      s_cur = s_nxt;
     } else if (b == lastb + 1) {
-      pv(ring, vst, vhalf);
+      pv(vp, pin);
     }
   }
 };
 
-// Issues the DMA of one K tile and one V tile into ring stages (kst, vst).
+// Issues the DMA of one K tile and one V tile into their ring stages.
 template <typename L>
-__device__ __forceinline__ void issue_unit(__amdgpu_buffer_rsrc_t k_rs,
-                                           __amdgpu_buffer_rsrc_t v_rs, lds_char *ring,
+__device__ __forceinline__ void issue_unit(u32x4 k_rs, u32x4 v_rs, uint32_t ring_addr,
                                            const uint32_t *ksrc, const uint32_t *vsrc,
-                                           int wave,
-                                           int ktile, int vtile) {
+                                           int wave, int ktile, int vtile) {
   const uint32_t koff = (uint32_t)ktile * L::TILE_GLOBAL;
   const uint32_t voff = (uint32_t)vtile * L::TILE_GLOBAL;
-  const int kst = ktile & (kStages - 1), vst = vtile & (kStages - 1);
+  const uint32_t kst = ktile & (kStages - 1), vst = vtile & (kStages - 1);
 #pragma unroll
   for (int i = 0; i < L::K_PER_WAVE; ++i) {
     if (i < L::K_PER_WAVE - 1 || L::K_EXTRA == 0 || wave < L::K_EXTRA) {
-      const int ins = i * kWaves + wave;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          k_rs, (lds_void *)(ring + kst * L::K_BYTES + ins * kWave * 16), 16,
-          ksrc[i] + koff, 0, 0, 0);
+      const uint32_t ins = i * kWaves + wave;
+      dma16(k_rs, ring_addr + kst * L::K_BYTES + ins * kWave * 16, ksrc[i] + koff);
     }
   }
 #pragma unroll
   for (int i = 0; i < L::V_PER_WAVE; ++i) {
-    const int ins = i * kWaves + wave;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        v_rs, (lds_void *)(ring + L::V_OFF + vst * L::V_BYTES + ins * kWave * 16), 16,
-        vsrc[i] + voff, 0, 0, 0);
+    const uint32_t ins = i * kWaves + wave;
+    dma16(v_rs, ring_addr + L::V_OFF + vst * L::V_BYTES + ins * kWave * 16, vsrc[i] + voff);
   }
 }
 
@@ -642,6 +698,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_pipe(
   typedef typename P::frag frag;
   __shared__ __attribute__((aligned(16))) char ring_[L::LDS_BYTES];
   lds_char *ring = (lds_char *)ring_;
+  const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
 
   P s;
   const int tid = threadIdx.x;
@@ -666,8 +723,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_pipe(
   const size_t qoff = (size_t)wi.bh * Nq * D;
   const size_t koff = (size_t)wi.bh * Nk * D;
   const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(q + qoff, (uint32_t)Nq * D * sizeof(T));
-  const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(k + koff, (uint32_t)Nk * D * sizeof(T));
-  const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(v + koff, (uint32_t)Nk * D * sizeof(T));
+  const u32x4 k_rs = raw_rsrc(k + koff, (uint32_t)Nk * D * sizeof(T));
+  const u32x4 v_rs = raw_rsrc(v + koff, (uint32_t)Nk * D * sizeof(T));
 
   uint32_t ksrc[L::K_PER_WAVE], vsrc[L::V_PER_WAVE];
 #pragma unroll
@@ -695,12 +752,14 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_pipe(
     if (negate) raw ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
     s.qf[f] = __builtin_bit_cast(frag, raw);
   }
+  // Q must be in registers before the ring's loads are counted by vmcnt.
+  wait_vmcnt<0>();
   // Prologue units: (K0,V0) (K1,V1) (K2,V2).  Step j then issues (K(j+3),
   // V(j+2)); every unit has the same per-wave load count, so "the previous
   // unit may still be in flight" is one vmcnt value.
-  issue_unit<L>(k_rs, v_rs, ring, ksrc, vsrc, s.wave, 0, 0);
-  issue_unit<L>(k_rs, v_rs, ring, ksrc, vsrc, s.wave, 1, 1);
-  issue_unit<L>(k_rs, v_rs, ring, ksrc, vsrc, s.wave, 2, 2);
+  issue_unit<L>(k_rs, v_rs, ring_addr, ksrc, vsrc, s.wave, 0, 0);
+  issue_unit<L>(k_rs, v_rs, ring_addr, ksrc, vsrc, s.wave, 1, 1);
+  issue_unit<L>(k_rs, v_rs, ring_addr, ksrc, vsrc, s.wave, 2, 2);
   if (L::K_EXTRA && s.wave < L::K_EXTRA)
     ring_barrier<2 * L::UNIT0>();  // (K0,V0) landed
   else
@@ -711,9 +770,9 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_pipe(
   s.m_use = -INFINITY;
   s.l = 0.f;
   s.lr = 0.f;
-  s.p_prev[0] = frag{};
-  s.p_prev[1] = frag{};
-  s.qk(ring, 0, 0, s.s_cur);
+  s.P1[0] = frag{};  // P.V of block -1 adds nothing
+  s.P1[1] = frag{};
+  s.qk(s.kptr(ring, 0, 0), s.S0);
 
   // Tile step j reads K tiles j, j+1 and V tiles j-1, j:
   //   block 2j  : P.V(V tile j-1, rows 32..63), K.Q^T(K tile j, rows 32..63)
@@ -728,12 +787,12 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_pipe(
       ring_barrier<L::UNIT0>();
     else
       ring_barrier<L::UNIT>();
-    issue_unit<L>(k_rs, v_rs, ring, ksrc, vsrc, s.wave, j + 3, j + 2);
+    issue_unit<L>(k_rs, v_rs, ring_addr, ksrc, vsrc, s.wave, j + 3, j + 2);
     const int st0 = j & (kStages - 1);
     const int stm = (j + kStages - 1) & (kStages - 1);
     const int st1 = (j + 1) & (kStages - 1);
-    s.block(ring, 2 * j, lastb, stm, 1, st0, 1);
-    s.block(ring, 2 * j + 1, lastb, st0, 0, st1, 0);
+    s.template block<false>(ring, 2 * j, lastb, stm, 1, st0, 1);
+    s.template block<true>(ring, 2 * j + 1, lastb, st0, 0, st1, 0);
   }
   wait_vmcnt<0>();  // no DMA may outlive the workgroup's LDS
 
