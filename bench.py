@@ -110,6 +110,10 @@ def main() -> int:
     ap.add_argument("--out-f32", action="store_true",
                     help="store O in fp32 (FA_BF16_OF32) instead of the input type")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before timing, copy this many MiB device-to-device once "
+                         "(a plain copy of known size, to calibrate HBM byte "
+                         "counters in a profiler run)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     args = ap.parse_args()
 
@@ -140,6 +144,15 @@ def main() -> int:
     argv = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
             w.B, w.H, w.N, w.N, w.D, scale, int(w.causal), code, sp)
     call = lib.fa_fwd
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize(dev)
+        dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        del src, dst
 
     for _ in range(args.warmup):
         st = call(*argv)
