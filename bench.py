@@ -3,13 +3,16 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-One step is one call of fa_fwd (the whole forward pass) over the workload's
-synthetic inputs, which are resident in device memory before timing starts.
+One step is one call of fa_fwd_ws (the whole forward pass: the attention
+kernel and, when the plan splits long query tiles, the kernel that combines
+the parts) over the workload's synthetic inputs, which are resident in
+device memory before timing starts; --entry fa_fwd times the unsplit entry.
 W untimed steps are followed by exactly K timed steps, bracketed by device
 synchronisation.  Prints ONE JSON line: throughput in TFLOP/s counting
-4*B*H*Nq*Nk*D flops (halved when causal), the dominant kernel's roofline
-(HIP-event time per launch on the launch stream against the dense MFMA peak
-of the input type), and the CPU oracle's throughput on the host cores.
+4*B*H*Nq*Nk*D flops (halved when causal), the roofline of the attention
+kernel (HIP-event time per step on the launch stream, which also holds the
+short combine kernel when the plan splits, against the dense MFMA peak of
+the input type), and the CPU oracle's throughput on the host cores.
 """
 from __future__ import annotations
 
@@ -115,6 +118,8 @@ def main() -> int:
                          "(a plain copy of known size, to calibrate HBM byte "
                          "counters in a profiler run)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--entry", choices=("fa_fwd_ws", "fa_fwd"), default="fa_fwd_ws",
+                    help="C entry point to time (default: fa_fwd_ws, with scratch)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -142,8 +147,19 @@ def main() -> int:
     sp = stream.cuda_stream
     lib = fa.library()
     argv = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-            w.B, w.H, w.N, w.N, w.D, scale, int(w.causal), code, sp)
-    call = lib.fa_fwd
+            w.B, w.H, w.N, w.N, w.D, scale, int(w.causal), code)
+    ws_bytes = 0
+    if args.entry == "fa_fwd_ws":
+        st, ws_bytes = fa.fa_fwd_workspace_size(w.B, w.H, w.N, w.N, w.D, int(w.causal),
+                                                code)
+        if st != 0:
+            raise RuntimeError(f"fa_fwd_workspace_size failed: {fa.fa_status_str(st)}")
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        argv = argv + (ws.data_ptr(), ws_bytes, sp)
+        call = lib.fa_fwd_ws
+    else:
+        argv = argv + (sp,)
+        call = lib.fa_fwd
 
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
@@ -157,7 +173,7 @@ def main() -> int:
     for _ in range(args.warmup):
         st = call(*argv)
         if st != 0:
-            raise RuntimeError(f"fa_fwd failed: {fa.fa_status_str(st)} "
+            raise RuntimeError(f"{args.entry} failed: {fa.fa_status_str(st)} "
                                f"{fa.fa_last_hip_error()}")
     torch.cuda.synchronize(dev)
 
@@ -196,7 +212,8 @@ def main() -> int:
         "data": "synthetic (seeded i.i.d. Gaussian q, k, v)",
         "config": {"workload": name, "B": w.B, "H": w.H, "Nq": w.N, "Nk": w.N, "D": w.D,
                    "causal": w.causal, "out": str(out_dt).replace("torch.", ""),
-                   "flops_per_step": flops},
+                   "flops_per_step": flops, "entry": args.entry,
+                   "workspace_bytes": ws_bytes},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(name),

@@ -38,6 +38,7 @@
 #ifndef FA_H
 #define FA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -64,7 +65,9 @@ enum fa_status {
     FA_ERR_SCALE = 5,    /* scale is NaN or infinite                          */
     FA_ERR_ALIGN = 6,    /* q, k, v or o not 16-byte aligned, lse not 4-byte */
     FA_ERR_HIP = 7,      /* the HIP runtime refused the launch               */
-    FA_ERR_OVERLAP = 8   /* o or lse overlaps q, k, v or each other          */
+    FA_ERR_OVERLAP = 8,  /* o, lse or workspace overlaps an input or another
+                            output                                           */
+    FA_ERR_WORKSPACE = 9 /* workspace NULL or smaller than fa_fwd_ws needs   */
 };
 
 /*
@@ -95,6 +98,51 @@ enum fa_status {
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
            int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
            float scale, int causal, int dtype, void *stream);
+
+/*
+ * fa_fwd_workspace_size -- device scratch bytes that fa_fwd_ws needs for
+ * this problem on the current device (written to *bytes; 0 when the call
+ * runs every query tile whole).
+ *
+ * Long rows of a causal pass see many more keys than short ones, so one
+ * workgroup per query tile leaves most compute units idle while the longest
+ * tiles finish.  fa_fwd_ws cuts the key range of long tiles into parts of
+ * about the mean per-unit work; each part keeps its own running max, sum
+ * and O in the workspace, and a second kernel combines the parts with the
+ * rescaling that the online softmax applies when it folds one key block
+ * into the running statistics (page "FlashAttention-2实现与优化：高效注意力
+ * 机制详解" §3.1, the incremental update of (m, l, o_acc)).  Cutting the
+ * work along the sequence is the sequence parallelism of page
+ * "FlashAttention技术演进全景图" §3.2.  The plan depends on the shape, dtype,
+ * causal flag and the device's compute-unit count, not on the data.
+ * Splitting is used with 16-bit inputs and D in {64, 128}.
+ *
+ * Returns FA_OK, FA_ERR_NULLPTR (bytes NULL), FA_ERR_SHAPE, FA_ERR_HEAD_DIM,
+ * FA_ERR_DTYPE or FA_ERR_HIP (device query failed).
+ */
+int fa_fwd_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                          int64_t D, int causal, int dtype, size_t *bytes);
+
+/*
+ * fa_fwd_ws -- fa_fwd with caller-owned device scratch.
+ *
+ * Arguments as fa_fwd, plus
+ *   workspace        device pointer, 16-byte aligned, or NULL when
+ *                    fa_fwd_workspace_size reports 0 bytes
+ *   workspace_bytes  its size in bytes
+ *
+ * Computes the same O and lse as fa_fwd up to fp32 rounding order (the
+ * parts are combined in a different order).  The workspace is overwritten
+ * and holds nothing of use afterwards; two calls that share one workspace
+ * must be ordered (the same stream).  Returns fa_fwd's codes, and
+ * FA_ERR_WORKSPACE when the plan needs scratch and `workspace` is NULL or
+ * smaller than fa_fwd_workspace_size reports; FA_ERR_ALIGN and
+ * FA_ERR_OVERLAP also cover the workspace.
+ */
+int fa_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse,
+              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+              float scale, int causal, int dtype, void *workspace,
+              size_t workspace_bytes, void *stream);
 
 /* Static description of a status code; never NULL. */
 const char *fa_status_str(int status);

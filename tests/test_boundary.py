@@ -52,12 +52,12 @@ def test_constants_match_header():
     enums = _header_enums()
     for name, val in enums.items():
         assert getattr(fa, name) == val, name
-    assert len(enums) == 14
+    assert len(enums) == 15
 
 
 def test_version_and_status_strings():
     assert fa.fa_version() >= 100
-    for s in range(9):
+    for s in range(10):
         assert fa.fa_status_str(s)
     assert fa.fa_status_str(1234) == "unknown status"
     assert fa.fa_last_hip_error() == ""
@@ -110,3 +110,45 @@ def test_lse_needs_only_four_byte_alignment_check_passes_to_overlap():
                                    (K - 16, L)])
 def test_outputs_must_not_overlap(o, lse):
     assert call(o=o, lse=lse) == fa.FA_ERR_OVERLAP
+
+
+def call_ws(ws=O + (1 << 24), ws_bytes=1 << 20, **kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, H=3, Nq=100, Nk=90, D=64, scale=0.125,
+             causal=1, dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return fa.fa_fwd_ws(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"],
+                        a["Nk"], a["D"], a["scale"], a["causal"], a["dtype"], ws, ws_bytes,
+                        a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), "FA_ERR_NULLPTR"), (dict(Nq=0), "FA_ERR_SHAPE"),
+    (dict(D=48), "FA_ERR_HEAD_DIM"), (dict(dtype=7), "FA_ERR_DTYPE"),
+    (dict(scale=math.nan), "FA_ERR_SCALE"), (dict(k=K + 2), "FA_ERR_ALIGN"),
+    (dict(lse=O + 4), "FA_ERR_OVERLAP"),
+])
+def test_ws_entry_validates_like_fa_fwd(kw, want):
+    assert call_ws(**kw) == getattr(fa, want)
+
+
+@pytest.mark.parametrize("ws,want", [(O + (1 << 24) + 8, "FA_ERR_ALIGN"),
+                                     (Q + 256, "FA_ERR_OVERLAP"), (L - 64, "FA_ERR_OVERLAP"),
+                                     (V - 16, "FA_ERR_OVERLAP")])
+def test_workspace_alignment_and_overlap(ws, want):
+    assert call_ws(ws=ws) == getattr(fa, want)
+
+
+@pytest.mark.parametrize("kw,want", [(dict(B=0), "FA_ERR_SHAPE"), (dict(Nk=-1), "FA_ERR_SHAPE"),
+                                     (dict(D=80), "FA_ERR_HEAD_DIM"),
+                                     (dict(dtype=5), "FA_ERR_DTYPE")])
+def test_workspace_size_validation(kw, want):
+    a = dict(B=2, H=3, Nq=100, Nk=90, D=64, causal=1, dtype=fa.FA_BF16)
+    a.update(kw)
+    st, n = fa.fa_fwd_workspace_size(**a)
+    assert st == getattr(fa, want) and n == 0
+
+
+def test_workspace_size_null_output():
+    lib = fa.library()
+    assert lib.fa_fwd_workspace_size(1, 1, 64, 64, 64, 0, fa.FA_BF16, None) == \
+        fa.FA_ERR_NULLPTR

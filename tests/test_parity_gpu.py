@@ -1,5 +1,9 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
 
+Every comparison runs both entry points: fa_fwd (one workgroup per query
+tile) and fa_fwd_ws (key ranges of long tiles split over the compute units
+and combined by a second kernel); each is held to the oracle on its own.
+
 Tolerances (max-abs over every checked element):
   fp32 inputs                      O <= 1e-4, L <= 1e-5
   bf16/fp16 inputs, fp32 O         O <= 1e-2, L <= 1e-3
@@ -44,9 +48,10 @@ def _half_ulp(x, dtype):
     return 2.0 ** (e - mant - 1)
 
 
-def run_gpu(q, k, v, causal, out_dtype, scale):
+def run_gpu(q, k, v, causal, out_dtype, scale, split=True):
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
-    o, lse = fa.fwd(qd, kd, vd, causal=causal, scale=scale, out_dtype=out_dtype)
+    o, lse = fa.fwd(qd, kd, vd, causal=causal, scale=scale, out_dtype=out_dtype,
+                    split=split)
     torch.cuda.synchronize()
     return o.float().cpu(), lse.cpu()
 
@@ -65,29 +70,32 @@ def compare(q, k, v, causal, scale, rows=None, what=""):
         ref_l = ref_l.reshape(-1)
     sel = slice(None) if rows is None else torch.as_tensor(rows)
 
-    o32, l32 = run_gpu(q, k, v, causal, torch.float32, scale)
-    o32 = o32.reshape(-1, D)[sel].double().numpy()
-    l32 = l32.reshape(-1)[sel].double().numpy()
-    assert np.isfinite(o32).all() and np.isfinite(l32).all(), "non-finite output"
-    err_o = float(np.abs(o32 - ref_o).max())
-    err_l = float(np.abs(l32 - ref_l).max())
-    _log(f"  fp32-O max-abs O {err_o:.3e} L {err_l:.3e}")
-    assert err_o <= tol_o, f"O error {err_o:.3e} > {tol_o}"
-    assert err_l <= tol_l, f"L error {err_l:.3e} > {tol_l}"
+    worst = (0.0, 0.0)
+    for split in (False, True):
+        o32, l32 = run_gpu(q, k, v, causal, torch.float32, scale, split)
+        o32 = o32.reshape(-1, D)[sel].double().numpy()
+        l32 = l32.reshape(-1)[sel].double().numpy()
+        assert np.isfinite(o32).all() and np.isfinite(l32).all(), "non-finite output"
+        err_o = float(np.abs(o32 - ref_o).max())
+        err_l = float(np.abs(l32 - ref_l).max())
+        _log(f"  split={split} fp32-O max-abs O {err_o:.3e} L {err_l:.3e}")
+        assert err_o <= tol_o, f"O error {err_o:.3e} > {tol_o} (split={split})"
+        assert err_l <= tol_l, f"L error {err_l:.3e} > {tol_l} (split={split})"
+        worst = (max(worst[0], err_o), max(worst[1], err_l))
 
-    if kind == "16":
-        o16, l16 = run_gpu(q, k, v, causal, q.dtype, scale)
-        o16 = o16.reshape(-1, D)[sel].double().numpy()
-        l16 = l16.reshape(-1)[sel].double().numpy()
-        rounded = torch.from_numpy(o32).to(q.dtype).double().numpy()
-        assert np.array_equal(o16, rounded), "16-bit O is not the rounding of fp32 O"
-        assert np.array_equal(l16, l32), "L differs between output modes"
-        bound = tol_o + _half_ulp(ref_o, q.dtype)
-        excess = np.abs(o16 - ref_o) - bound
-        assert excess.max() <= 0, f"16-bit O error exceeds bound by {excess.max():.3e}"
-        n_over = int((np.abs(o16 - ref_o) > tol_o).sum())
-        _log(f"  16-bit O: {n_over} elements beyond {tol_o} (storage rounding)")
-    return err_o, err_l
+        if kind == "16":
+            o16, l16 = run_gpu(q, k, v, causal, q.dtype, scale, split)
+            o16 = o16.reshape(-1, D)[sel].double().numpy()
+            l16 = l16.reshape(-1)[sel].double().numpy()
+            rounded = torch.from_numpy(o32).to(q.dtype).double().numpy()
+            assert np.array_equal(o16, rounded), "16-bit O is not the rounding of fp32 O"
+            assert np.array_equal(l16, l32), "L differs between output modes"
+            bound = tol_o + _half_ulp(ref_o, q.dtype)
+            excess = np.abs(o16 - ref_o) - bound
+            assert excess.max() <= 0, f"16-bit O error exceeds bound by {excess.max():.3e}"
+            n_over = int((np.abs(o16 - ref_o) > tol_o).sum())
+            _log(f"  16-bit O: {n_over} elements beyond {tol_o} (storage rounding)")
+    return worst
 
 
 def _check_workload(w, rows=None):
@@ -206,6 +214,95 @@ def test_three_dim_inputs_and_stream():
 
 def test_repeat_is_deterministic():
     q, k, v = gen_qkv(2, 2, 700, 700, 128, seed=4, dtype="bf16")
+    a = run_gpu(q, k, v, True, torch.bfloat16, 0.1)
+    b = run_gpu(q, k, v, True, torch.bfloat16, 0.1)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# --- key-range split (fa_fwd_ws) -------------------------------------------
+def _ws_bytes(B, H, Nq, Nk, D, causal, code):
+    st, n = fa.fa_fwd_workspace_size(B, H, Nq, Nk, D, causal, code)
+    assert st == fa.FA_OK, fa.fa_status_str(st)
+    return n
+
+
+SPLIT = [
+    # (B, H, Nq, Nk, D): shapes whose plan cuts tiles into several parts
+    (1, 1, 2048, 2048, 128),
+    (1, 2, 1000, 3000, 64),
+    (1, 1, 3000, 1000, 128),
+    (2, 1, 1500, 1700, 64),
+    (1, 3, 777, 4100, 128),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SPLIT, ids=lambda s: "x".join(map(str, s)))
+def test_split_shapes(shape, causal, dtype):
+    B, H, Nq, Nk, D = shape
+    code = fa.FA_BF16 if dtype == "bf16" else fa.FA_F16
+    assert _ws_bytes(B, H, Nq, Nk, D, causal, code) > 0, "plan does not split"
+    q, k, v = gen_qkv(B, H, Nq, Nk, D, seed=sum(shape) % 997, dtype=dtype)
+    compare(q, k, v, causal, 1.0 / math.sqrt(D), what=f"split {shape}")
+
+
+def test_split_workspace_contract():
+    """Missing or short scratch is refused before any launch; fp32 and small
+    head dims need none; the workspace size does not depend on O's type."""
+    B, H, Nq, Nk, D = 1, 1, 2048, 2048, 128
+    q, k, v = (t.to(DEV) for t in gen_qkv(B, H, Nq, Nk, D, seed=1, dtype="bf16"))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=DEV)
+    need = _ws_bytes(B, H, Nq, Nk, D, 1, fa.FA_BF16)
+    assert need > 0
+    assert need == _ws_bytes(B, H, Nq, Nk, D, 1, fa.FA_BF16_OF32)
+    assert _ws_bytes(B, H, Nq, Nk, D, 1, fa.FA_F32) == 0
+    assert _ws_bytes(B, H, Nq, Nk, 32, 1, fa.FA_BF16) == 0
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            B, H, Nq, Nk, D, 0.1, 1, fa.FA_BF16)
+    sp = torch.cuda.current_stream().cuda_stream
+    assert fa.fa_fwd_ws(*args, None, 0, sp) == fa.FA_ERR_WORKSPACE
+    assert fa.fa_fwd_ws(*args, ws.data_ptr(), need - 1, sp) == fa.FA_ERR_WORKSPACE
+    assert fa.fa_fwd_ws(*args, ws.data_ptr() + 8, need - 8, sp) == fa.FA_ERR_ALIGN
+    assert fa.fa_fwd_ws(*args, o.data_ptr(), need, sp) == fa.FA_ERR_OVERLAP
+    assert fa.fa_fwd_ws(*args, ws.data_ptr(), need, sp) == fa.FA_OK
+    # a shape that does not split runs without scratch
+    small = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+             1, 1, 64, 64, D, 0.1, 1, fa.FA_BF16)
+    assert _ws_bytes(1, 1, 64, 64, D, 1, fa.FA_BF16) == 0
+    assert fa.fa_fwd_ws(*small, None, 0, sp) == fa.FA_OK
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_split_no_writes_outside_outputs_and_workspace(causal):
+    B, H, Nq, Nk, D = 1, 2, 1000, 3000, 64
+    q, k, v = (t.to(DEV) for t in gen_qkv(B, H, Nq, Nk, D, seed=6, dtype="bf16"))
+    need = _ws_bytes(B, H, Nq, Nk, D, causal, fa.FA_BF16)
+    assert need > 0 and need % 16 == 0
+    guard = 4096
+    n_o, n_l = B * H * Nq * D, B * H * Nq
+    obuf = torch.full((n_o + 2 * guard,), 12345.0, dtype=torch.bfloat16, device=DEV)
+    lbuf = torch.full((n_l + 2 * guard,), -777.0, dtype=torch.float32, device=DEV)
+    wbuf = torch.full((need + 2 * guard,), 0xA5, dtype=torch.uint8, device=DEV)
+    o = obuf[guard:guard + n_o]
+    lse = lbuf[guard:guard + n_l]
+    st = fa.fa_fwd_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                      lse.data_ptr(), B, H, Nq, Nk, D, 0.125, int(causal), fa.FA_BF16,
+                      wbuf.data_ptr() + guard, need,
+                      torch.cuda.current_stream().cuda_stream)
+    assert st == fa.FA_OK
+    torch.cuda.synchronize()
+    assert (obuf[:guard] == 12345.0).all() and (obuf[guard + n_o:] == 12345.0).all()
+    assert (lbuf[:guard] == -777.0).all() and (lbuf[guard + n_l:] == -777.0).all()
+    assert (wbuf[:guard] == 0xA5).all() and (wbuf[guard + need:] == 0xA5).all()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+def test_split_repeat_is_deterministic():
+    q, k, v = gen_qkv(1, 2, 1000, 3000, 64, seed=12, dtype="bf16")
     a = run_gpu(q, k, v, True, torch.bfloat16, 0.1)
     b = run_gpu(q, k, v, True, torch.bfloat16, 0.1)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])

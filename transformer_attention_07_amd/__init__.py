@@ -8,11 +8,16 @@ libfa.so is missing or fails to load, every call raises.
 C-ABI mirrors (same names and meaning as include/fa.h):
     fa_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Nq, Nk, D, scale,
            causal, dtype, stream) -> status
+    fa_fwd_workspace_size(B, H, Nq, Nk, D, causal, dtype) -> (status, bytes)
+    fa_fwd_ws(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Nq, Nk, D, scale,
+              causal, dtype, ws_ptr, ws_bytes, stream) -> status
     fa_status_str(status) -> str
     fa_last_hip_error() -> str
     fa_version() -> int
 Tensor convenience:
-    fwd(q, k, v, causal=False, scale=None, out_dtype=None) -> (o, lse)
+    fwd(q, k, v, causal=False, scale=None, out_dtype=None, split=True)
+        -> (o, lse); split=True runs fa_fwd_ws with a workspace from torch's
+        allocator, split=False runs fa_fwd
 """
 from __future__ import annotations
 
@@ -24,8 +29,9 @@ from typing import Optional, Tuple
 __all__ = [
     "FA_F32", "FA_BF16", "FA_BF16_OF32", "FA_F16", "FA_F16_OF32",
     "FA_OK", "FA_ERR_NULLPTR", "FA_ERR_SHAPE", "FA_ERR_HEAD_DIM", "FA_ERR_DTYPE",
-    "FA_ERR_SCALE", "FA_ERR_ALIGN", "FA_ERR_HIP", "FA_ERR_OVERLAP",
-    "LIBRARY", "EXPORTS", "library", "fa_fwd", "fa_status_str", "fa_last_hip_error",
+    "FA_ERR_SCALE", "FA_ERR_ALIGN", "FA_ERR_HIP", "FA_ERR_OVERLAP", "FA_ERR_WORKSPACE",
+    "LIBRARY", "EXPORTS", "library", "fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws",
+    "fa_status_str", "fa_last_hip_error",
     "fa_version", "fwd", "FaError",
 ]
 
@@ -33,10 +39,11 @@ LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_F32, FA_BF16, FA_BF16_OF32, FA_F16, FA_F16_OF32 = 0, 1, 2, 3, 4
 (FA_OK, FA_ERR_NULLPTR, FA_ERR_SHAPE, FA_ERR_HEAD_DIM, FA_ERR_DTYPE, FA_ERR_SCALE,
- FA_ERR_ALIGN, FA_ERR_HIP, FA_ERR_OVERLAP) = range(9)
+ FA_ERR_ALIGN, FA_ERR_HIP, FA_ERR_OVERLAP, FA_ERR_WORKSPACE) = range(10)
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_fwd", "fa_status_str", "fa_last_hip_error", "fa_version")
+EXPORTS = ("fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws", "fa_status_str",
+           "fa_last_hip_error", "fa_version")
 
 _lib = None
 
@@ -61,6 +68,12 @@ def library() -> ctypes.CDLL:
     lib.fa_fwd.restype = ctypes.c_int
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
                            ctypes.c_int, ctypes.c_int, vp]
+    lib.fa_fwd_workspace_size.restype = ctypes.c_int
+    lib.fa_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int,
+                                          ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+    lib.fa_fwd_ws.restype = ctypes.c_int
+    lib.fa_fwd_ws.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
+                              ctypes.c_int, ctypes.c_int, vp, ctypes.c_size_t, vp]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_status_str.argtypes = [ctypes.c_int]
     lib.fa_last_hip_error.restype = ctypes.c_char_p
@@ -75,6 +88,21 @@ def fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, dtype, stream) -> in
     """Raw C call; pointers are integers (device addresses) or None."""
     return int(library().fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, D, float(scale),
                                 int(causal), int(dtype), stream))
+
+
+def fa_fwd_workspace_size(B, H, Nq, Nk, D, causal, dtype) -> Tuple[int, int]:
+    """Raw C call; returns (status, workspace bytes)."""
+    n = ctypes.c_size_t(0)
+    st = int(library().fa_fwd_workspace_size(B, H, Nq, Nk, D, int(causal), int(dtype),
+                                             ctypes.byref(n)))
+    return st, int(n.value)
+
+
+def fa_fwd_ws(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, dtype, ws, ws_bytes,
+              stream) -> int:
+    """Raw C call; pointers are integers (device addresses) or None."""
+    return int(library().fa_fwd_ws(q, k, v, o, lse, B, H, Nq, Nk, D, float(scale),
+                                   int(causal), int(dtype), ws, int(ws_bytes), stream))
 
 
 def fa_status_str(status: int) -> str:
@@ -104,7 +132,8 @@ def _dtype_code(torch, in_dtype, out_dtype) -> int:
 
 
 def fwd(q, k, v, causal: bool = False, scale: Optional[float] = None,
-        out_dtype=None, out=None, stream=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+        out_dtype=None, out=None, stream=None,
+        split: bool = True) -> Tuple["torch.Tensor", "torch.Tensor"]:
     """Attention forward on device tensors.
 
     q: [B,Nq,D] or [B,H,Nq,D]; k, v: [B,Nk,D] or [B,H,Nk,D]; same dtype
@@ -112,7 +141,9 @@ def fwd(q, k, v, causal: bool = False, scale: Optional[float] = None,
     shaped like q in ``out_dtype`` (default: q's dtype) and lse fp32 shaped
     like q[..., 0].  ``scale`` defaults to 1/sqrt(D).  ``out`` may pass
     preallocated (o, lse).  Runs on ``stream`` (default: torch's current
-    stream of q's device).
+    stream of q's device).  ``split`` selects fa_fwd_ws (the key ranges of
+    long query tiles cut over the compute units, scratch from torch's
+    allocator) or fa_fwd (one workgroup per query tile).
     """
     import torch
 
@@ -146,10 +177,24 @@ def fwd(q, k, v, causal: bool = False, scale: Optional[float] = None,
             raise ValueError("out[0] must be contiguous, shaped like q, of out_dtype")
         if lse.shape != q.shape[:-1] or lse.dtype != torch.float32 or not lse.is_contiguous():
             raise ValueError("out[1] must be contiguous fp32 shaped like q[..., 0]")
-    if stream is None:
+    own_stream = stream is None
+    if own_stream:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                B, H, Nq, Nk, D, scale, causal, code, stream)
+    if split:
+        st, nbytes = fa_fwd_workspace_size(B, H, Nq, Nk, D, causal, code)
+        if st == FA_OK:
+            # torch's allocator hands this block out again once the kernels
+            # queued on the current stream have run; on another stream the
+            # block is tied to that stream too.
+            ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+            if not own_stream:
+                ws.record_stream(torch.cuda.ExternalStream(stream, device=q.device))
+            st = fa_fwd_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                           lse.data_ptr(), B, H, Nq, Nk, D, scale, causal, code,
+                           ws.data_ptr(), nbytes, stream)
+    else:
+        st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                    lse.data_ptr(), B, H, Nq, Nk, D, scale, causal, code, stream)
     if st != FA_OK:
         msg = fa_status_str(st)
         if st == FA_ERR_HIP:

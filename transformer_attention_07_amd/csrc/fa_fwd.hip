@@ -416,6 +416,28 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Ring wait of one pipeline step: with `one` the youngest issue unit may
+// still be in flight (n0 loads for waves that issue the extra K load, n
+// for the others), otherwise nothing may.
+template <int N0, int N>
+__device__ __forceinline__ void ring_wait(bool one, bool extra) {
+  if (!one)
+    ring_barrier<0>();
+  else if (extra)
+    ring_barrier<N0>();
+  else
+    ring_barrier<N>();
+}
+
+// 16-byte buffer load into registers, as asm: the compiler does not count it
+// among the loads it waits for, so its wait must be explicit (loads return
+// in issue order, so a later wait that covers younger loads covers it).
+__device__ __forceinline__ u32x4 load16_async(u32x4 rs, uint32_t voff) {
+  u32x4 r;
+  asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(r) : "v"(voff), "s"(rs));
+  return r;
+}
+
 template <typename T, int D>
 struct PipeLayout {
   static constexpr int C = D / 8;                     // 16-byte chunks per row
@@ -666,14 +688,14 @@ struct Pipe {
   }
 };
 
-// Issues the DMA of one K tile and one V tile into their ring stages.
+// Issues the DMA of one K tile and one V tile (absolute tile indices) into
+// ring stages kst and vst.
 template <typename L>
 __device__ __forceinline__ void issue_unit(u32x4 k_rs, u32x4 v_rs, uint32_t ring_addr,
                                            const uint32_t *ksrc, const uint32_t *vsrc,
-                                           int wave, int ktile, int vtile) {
+                                           int wave, int ktile, int kst, int vtile, int vst) {
   const uint32_t koff = (uint32_t)ktile * L::TILE_GLOBAL;
   const uint32_t voff = (uint32_t)vtile * L::TILE_GLOBAL;
-  const uint32_t kst = ktile & (kStages - 1), vst = vtile & (kStages - 1);
 #pragma unroll
   for (int i = 0; i < L::K_PER_WAVE; ++i) {
     if (i < L::K_PER_WAVE - 1 || L::K_EXTRA == 0 || wave < L::K_EXTRA) {
@@ -688,11 +710,48 @@ __device__ __forceinline__ void issue_unit(u32x4 k_rs, u32x4 v_rs, uint32_t ring
   }
 }
 
+// The work of one workgroup: query rows [q0, q0 + 128) of head bh against
+// key tiles [kt0, kt1) (64 keys each).  slot < 0: the item covers every key
+// the rows see and writes O and L; slot >= 0: the item is one part of a
+// split key range and writes a partial result to workspace slot `slot`.
+struct PipeItem {
+  int bh, q0, kt0, kt1, slot;
+};
+
+// Partial result of one split part, per row: O_p = acc / lr (fp32, D values),
+// and the statistics (m, l, lr, 0) as one 16-byte record, m being the base-2
+// exponent reference.  A row that saw no
+// key in this part has l = lr = 0, m = -inf and O_p = 0.
+template <int D>
+__device__ __forceinline__ void epilogue_partial(const f32x16 (&acc)[D / 32], float m,
+                                                 float l, float lr, float *ws_o,
+                                                 float *ws_s, int row, int g) {
+  const float lt = l + __shfl_xor(l, 32);
+  const float lrt = lr + __shfl_xor(lr, 32);
+  const float inv = lrt > 0.f ? 1.0f / lrt : 0.f;
+  float *orow = ws_o + (size_t)row * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d = db * 32 + 8 * r4 + 4 * g;
+      const f32x4 x = {acc[db][4 * r4 + 0] * inv, acc[db][4 * r4 + 1] * inv,
+                       acc[db][4 * r4 + 2] * inv, acc[db][4 * r4 + 3] * inv};
+      *reinterpret_cast<f32x4 *>(orow + d) = x;
+    }
+  }
+  if (g == 0) {
+    const f32x4 st = {lrt > 0.f ? m : -INFINITY, lt, lrt, 0.f};
+    *reinterpret_cast<f32x4 *>(ws_s + row * 4) = st;
+  }
+}
+
 template <typename T, typename OT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void fa_fwd_pipe(
-    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-    OT *__restrict__ o, float *__restrict__ lse, int Nq, int Nk, int BH, int nqt,
-    float c, int negate) {
+__device__ __forceinline__ void pipe_run(const T *__restrict__ q, const T *__restrict__ k,
+                                         const T *__restrict__ v, OT *__restrict__ o,
+                                         float *__restrict__ lse, float *__restrict__ ws,
+                                         int Nq, int Nk, float c, int negate,
+                                         const PipeItem it, int nslots) {
   typedef Pipe<T, OT, D, CAUSAL> P;
   typedef typename P::L L;
   typedef typename P::frag frag;
@@ -717,12 +776,11 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_pipe(
     s.vbase = (uint32_t)L::V_OFF + (uint32_t)row * L::SV * 16 + (uint32_t)col * 2;
   }
 
-  const WorkItem wi = work_item(BH, nqt, CAUSAL);
-  s.qw = wi.q0 + s.wave * 32;
+  s.qw = it.q0 + s.wave * 32;
   s.my_q = s.qw + s.l32;
-  const size_t qoff = (size_t)wi.bh * Nq * D;
-  const size_t koff = (size_t)wi.bh * Nk * D;
-  const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(q + qoff, (uint32_t)Nq * D * sizeof(T));
+  const size_t qoff = (size_t)it.bh * Nq * D;
+  const size_t koff = (size_t)it.bh * Nk * D;
+  const u32x4 q_rs = raw_rsrc(q + qoff, (uint32_t)Nq * D * sizeof(T));
   const u32x4 k_rs = raw_rsrc(k + koff, (uint32_t)Nk * D * sizeof(T));
   const u32x4 v_rs = raw_rsrc(v + koff, (uint32_t)Nk * D * sizeof(T));
 
@@ -734,69 +792,206 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_pipe(
   for (int i = 0; i < L::V_PER_WAVE; ++i)
     vsrc[i] = dma_src<T, D>(i * kWaves + s.wave, s.lane, L::SV);
 
-  const int kend = CAUSAL ? min(Nk, wi.q0 + kBM) : Nk;
-  const int nkt = (kend + kBN - 1) / kBN;
-  // last 32-key block this wave needs
-  const int lastb = CAUSAL ? min(2 * nkt - 1, s.qw / 32) : 2 * nkt - 1;
+  const int kt0 = it.kt0;
+  const int ntiles = it.kt1 - it.kt0;
+  // last 32-key block (absolute index) this wave needs in this item
+  const int lastb = CAUSAL ? min(2 * it.kt1 - 1, s.qw / 32) : 2 * it.kt1 - 1;
+  const bool extra = L::K_EXTRA && s.wave < L::K_EXTRA;
 
-  // Rows past Nk may be left unwritten by the bounds-checked loads; start
-  // the ring at zero so such rows hold finite values.
-  for (int i = tid; i < L::LDS_BYTES / 16; i += kThreads)
-    *(__attribute__((address_space(3))) u32x4 *)(ring + i * 16) = u32x4{};
-  __syncthreads();
+  // Q first: its loads are the oldest in flight, so the prologue wait for
+  // the first K/V unit covers them too.
+  u32x4 qraw[P::QF];
+#pragma unroll
+  for (int f = 0; f < P::QF; ++f)
+    qraw[f] = load16_async(q_rs, ((uint32_t)s.my_q * D + 16 * f + 8 * s.g) * sizeof(T));
 
+  // The first block's P.V belongs to the block before the item (P = 0) and
+  // reads V rows 32..63 of stage 3, which no load has written yet: clear
+  // them so that 0 * stale LDS cannot give NaN.  Everything else the kernel
+  // reads was written by a load (rows past Nk by the bounds check, as zero).
+  {
+    constexpr int Z0 = L::V_OFF + 3 * L::V_BYTES + 32 * L::SV * 16;
+    constexpr int ZN = 32 * L::SV;  // 16-byte chunks
+    for (int i = tid; i < ZN; i += kThreads)
+      *(__attribute__((address_space(3))) u32x4 *)(ring + Z0 + i * 16) = u32x4{};
+  }
+
+  // Issue units: unit 0 = (K0,V0), 1 = (K1,V1), 2 = (K2,V2) in the
+  // prologue, then step r issues unit r+3 = (K(r+3), V(r+2)) (relative
+  // tiles; tile j lives in ring stage j % 4).  Unit j >= 1 is issued only
+  // when j <= ntiles: nothing is fetched past the item except one K tile
+  // whose scores are never used.  Every unit has the same per-wave load
+  // count, so "the youngest unit may be in flight" is one vmcnt value.
+  issue_unit<L>(k_rs, v_rs, ring_addr, ksrc, vsrc, s.wave, kt0, 0, kt0, 0);
+  issue_unit<L>(k_rs, v_rs, ring_addr, ksrc, vsrc, s.wave, kt0 + 1, 1, kt0 + 1, 1);
+  if (ntiles >= 2)
+    issue_unit<L>(k_rs, v_rs, ring_addr, ksrc, vsrc, s.wave, kt0 + 2, 2, kt0 + 2, 2);
+  // Q and unit 0 landed (units 1 and 2 may be in flight); the zeroed rows
+  // are visible to every wave.
+  if (ntiles >= 2) {
+    if (extra)
+      ring_barrier<2 * L::UNIT0>();
+    else
+      ring_barrier<2 * L::UNIT>();
+  } else {
+    ring_wait<L::UNIT0, L::UNIT>(true, extra);
+  }
 #pragma unroll
   for (int f = 0; f < P::QF; ++f) {
-    const uint32_t off = ((uint32_t)s.my_q * D + 16 * f + 8 * s.g) * sizeof(T);
-    u32x4 raw = load16(q_rs, off);
-    if (negate) raw ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
-    s.qf[f] = __builtin_bit_cast(frag, raw);
+    asm volatile("" : "+v"(qraw[f]));  // Q is read only after the wait above
+    if (negate) qraw[f] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+    s.qf[f] = __builtin_bit_cast(frag, qraw[f]);
   }
-  // Q must be in registers before the ring's loads are counted by vmcnt.
-  wait_vmcnt<0>();
-  // Prologue units: (K0,V0) (K1,V1) (K2,V2).  Step j then issues (K(j+3),
-  // V(j+2)); every unit has the same per-wave load count, so "the previous
-  // unit may still be in flight" is one vmcnt value.
-  issue_unit<L>(k_rs, v_rs, ring_addr, ksrc, vsrc, s.wave, 0, 0);
-  issue_unit<L>(k_rs, v_rs, ring_addr, ksrc, vsrc, s.wave, 1, 1);
-  issue_unit<L>(k_rs, v_rs, ring_addr, ksrc, vsrc, s.wave, 2, 2);
-  if (L::K_EXTRA && s.wave < L::K_EXTRA)
-    ring_barrier<2 * L::UNIT0>();  // (K0,V0) landed
-  else
-    ring_barrier<2 * L::UNIT>();
 
 #pragma unroll
   for (int db = 0; db < P::NDB; ++db) s.acc[db] = f32x16{};
   s.m_use = -INFINITY;
   s.l = 0.f;
   s.lr = 0.f;
-  s.P1[0] = frag{};  // P.V of block -1 adds nothing
+  s.P1[0] = frag{};  // P.V of the block before the first adds nothing
   s.P1[1] = frag{};
   s.qk(s.kptr(ring, 0, 0), s.S0);
 
-  // Tile step j reads K tiles j, j+1 and V tiles j-1, j:
-  //   block 2j  : P.V(V tile j-1, rows 32..63), K.Q^T(K tile j, rows 32..63)
-  //   block 2j+1: P.V(V tile j, rows 0..31),    K.Q^T(K tile j+1, rows 0..31)
-  // K(j+1) and V(j) were requested two steps earlier; the unit requested in
-  // step j-1 may still be in flight.  Step j requests K(j+3) into the stage
-  // of K(j-1) and V(j+2) into the stage of V(j-2), both last read in step
-  // j-1.  Every wave runs every step so that the loads and barriers line up.
-  const int nsteps = nkt + 1;
-  for (int j = 0; j < nsteps; ++j) {
-    if (L::K_EXTRA && s.wave < L::K_EXTRA)
-      ring_barrier<L::UNIT0>();
-    else
-      ring_barrier<L::UNIT>();
-    issue_unit<L>(k_rs, v_rs, ring_addr, ksrc, vsrc, s.wave, j + 3, j + 2);
-    const int st0 = j & (kStages - 1);
-    const int stm = (j + kStages - 1) & (kStages - 1);
-    const int st1 = (j + 1) & (kStages - 1);
-    s.template block<false>(ring, 2 * j, lastb, stm, 1, st0, 1);
-    s.template block<true>(ring, 2 * j + 1, lastb, st0, 0, st1, 0);
+  // Step r reads K tiles r, r+1 and V tiles r-1, r (relative):
+  //   block 2r  : P.V(V tile r-1, rows 32..63), K.Q^T(K tile r, rows 32..63)
+  //   block 2r+1: P.V(V tile r, rows 0..31),    K.Q^T(K tile r+1, rows 0..31)
+  // K(r+1) and V(r) belong to units <= r+1, issued at least two steps
+  // earlier; unit r+2 (issued in step r-1, if at all) may still be in
+  // flight.  Step r requests unit r+3: K(r+3) into the stage of K(r-1) and
+  // V(r+2) into the stage of V(r-2), both last read in step r-1.  Every
+  // wave runs every step so that the loads and barriers line up.
+  for (int r = 0; r <= ntiles; ++r) {
+    ring_wait<L::UNIT0, L::UNIT>(r + 2 <= ntiles, extra);
+    if (r + 3 <= ntiles)
+      issue_unit<L>(k_rs, v_rs, ring_addr, ksrc, vsrc, s.wave, kt0 + r + 3,
+                    (r + 3) & (kStages - 1), kt0 + r + 2, (r + 2) & (kStages - 1));
+    const int st0 = r & (kStages - 1);
+    const int stm = (r + kStages - 1) & (kStages - 1);
+    const int st1 = (r + 1) & (kStages - 1);
+    const int b = 2 * (kt0 + r);
+    s.template block<false>(ring, b, lastb, stm, 1, st0, 1);
+    s.template block<true>(ring, b + 1, lastb, st0, 0, st1, 0);
   }
   wait_vmcnt<0>();  // no DMA may outlive the workgroup's LDS
 
-  epilogue<D, OT>(s.acc, s.m_use, s.l, o, lse, wi.bh, Nq, s.my_q, s.g, s.lr);
+  if (it.slot < 0) {
+    epilogue<D, OT>(s.acc, s.m_use, s.l, o, lse, it.bh, Nq, s.my_q, s.g, s.lr);
+  } else {
+    float *ws_o = ws + (size_t)it.slot * kBM * D;
+    float *ws_s = ws + (size_t)nslots * kBM * D + (size_t)it.slot * kBM * 4;
+    epilogue_partial<D>(s.acc, s.m_use, s.l, s.lr, ws_o, ws_s, s.my_q - it.q0, s.g);
+  }
+}
+
+// One workgroup per 128-row query tile, longest causal tiles first.
+template <typename T, typename OT, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void fa_fwd_pipe(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    OT *__restrict__ o, float *__restrict__ lse, int Nq, int Nk, int BH, int nqt,
+    float c, int negate) {
+  const WorkItem wi = work_item(BH, nqt, CAUSAL);
+  const int kend = CAUSAL ? min(Nk, wi.q0 + kBM) : Nk;
+  const PipeItem it = {wi.bh, wi.q0, 0, (kend + kBN - 1) / kBN, -1};
+  pipe_run<T, OT, D, CAUSAL>(q, k, v, o, lse, nullptr, Nq, Nk, c, negate, it, 0);
+}
+
+// Key-range split of long query tiles (balances causal work over the CUs).
+// Query tile t (128 rows) needs w_t key tiles; it is cut into
+// p_t = ceil(w_t / W) parts of s_t = ceil(w_t / p_t) tiles, counted from the
+// top so that the last part holds the diagonal; part i covers tiles
+// [max(0, w_t - (p_t - i) s_t), w_t - (p_t - i - 1) s_t).  Tiles t >= t_split
+// are the split ones (w_t never decreases with t).  The table lists the
+// (t, part) pairs in decreasing part size; workgroup g takes pair g / BH of
+// head g % BH.
+constexpr int kMaxPairs = 1024;
+constexpr int kMaxParts = 8;
+struct SplitPlan {
+  int W;        // largest part, in key tiles
+  int t_split;  // first split query tile
+  int p_max;    // most parts of any tile
+  int npairs;
+  uint16_t pair[kMaxPairs];  // t | part << 11
+};
+
+__host__ __device__ inline int tile_keys(int t, int Nk, bool causal) {
+  const int kend = causal ? (Nk < (t + 1) * kBM ? Nk : (t + 1) * kBM) : Nk;
+  return (kend + kBN - 1) / kBN;
+}
+
+template <typename T, typename OT, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void fa_fwd_pipe_split(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    OT *__restrict__ o, float *__restrict__ lse, float *__restrict__ ws, int Nq, int Nk,
+    int BH, int nqt, float c, int negate, SplitPlan plan) {
+  const int g = blockIdx.x;
+  const int pr = plan.pair[g / BH];
+  const int t = pr & 0x7ff, part = pr >> 11;
+  const int w = tile_keys(t, Nk, CAUSAL);
+  const int p = (w + plan.W - 1) / plan.W;
+  const int st = (w + p - 1) / p;
+  PipeItem it;
+  it.bh = g % BH;
+  it.q0 = t * kBM;
+  it.kt0 = max(0, w - (p - part) * st);
+  it.kt1 = w - (p - part - 1) * st;
+  it.slot = p > 1 ? ((t - plan.t_split) * plan.p_max + part) * BH + it.bh : -1;
+  const int nslots = (nqt - plan.t_split) * plan.p_max * BH;
+  pipe_run<T, OT, D, CAUSAL>(q, k, v, o, lse, ws, Nq, Nk, c, negate, it, nslots);
+}
+
+// Combines the parts of each split query tile: with a_i = 2^(m_i - M),
+// M = max_i m_i, O = sum_i a_i lr_i O_i / sum_i a_i lr_i and
+// L = ln2 * (M + log2 sum_i a_i l_i).  Each thread owns one 4-wide slice of
+// one row and issues the loads of every part at once (the combine is one
+// memory round trip); a workgroup covers kThreads / (D/4) rows, so the grid
+// is (split tiles x heads x row groups).
+template <typename OT, int D>
+__global__ __launch_bounds__(kThreads) void fa_merge_parts(
+    const float *__restrict__ ws, OT *__restrict__ o, float *__restrict__ lse, int Nq,
+    int Nk, int BH, int nqt, int causal, int W, int t_split, int p_max) {
+  constexpr int C4 = D / 4;           // float4 per row
+  constexpr int RPB = kThreads / C4;  // rows per workgroup
+  constexpr int GROUPS = kBM / RPB;
+  const int grp = blockIdx.x % GROUPS;
+  const int tb = blockIdx.x / GROUPS;
+  const int bh = tb % BH;
+  const int t = t_split + tb / BH;
+  const int r = grp * RPB + threadIdx.x / C4;
+  const int c4 = threadIdx.x % C4;
+  const int row = t * kBM + r;
+  if (row >= Nq) return;
+  const int w = tile_keys(t, Nk, causal != 0);
+  const int p = (w + W - 1) / W;
+  const int nslots = (nqt - t_split) * p_max * BH;
+  const float *ws_s = ws + (size_t)nslots * kBM * D;
+  const int slot0 = (t - t_split) * p_max * BH + bh;
+  f32x4 st[kMaxParts], x[kMaxParts];
+#pragma unroll
+  for (int i = 0; i < kMaxParts; ++i) {
+    if (i < p) {
+      const size_t e = (size_t)(slot0 + i * BH) * kBM + r;
+      st[i] = *reinterpret_cast<const f32x4 *>(ws_s + e * 4);
+      x[i] = *reinterpret_cast<const f32x4 *>(ws + e * D + 4 * c4);
+    }
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kMaxParts; ++i)
+    if (i < p) M = fmaxf(M, st[i][0]);
+  float ls = 0.f, lrs = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kMaxParts; ++i) {
+    if (i < p) {
+      const float a = exp2f(st[i][0] - M);  // 0 for a part the row did not see
+      ls += a * st[i][1];
+      lrs += a * st[i][2];
+      acc += (a * st[i][2]) * x[i];
+    }
+  }
+  OT *orow = o + ((size_t)bh * Nq + row) * D;
+  store4<OT>(orow + 4 * c4, acc * (1.0f / lrs));
+  if (c4 == 0) lse[(size_t)bh * Nq + row] = (M + log2f(ls)) * 0.69314718055994531f;
 }
 
 // ---------------------------------------------------------------------------
@@ -947,24 +1142,41 @@ struct Launch {
   const void *q, *k, *v;
   void *o;
   float *lse;
+  float *ws;
   int Nq, Nk, BH, nqt;
   float c;
   hipStream_t stream;
+  const SplitPlan *plan;  // non-null: key-range split (pipelined kernel only)
 };
 
 template <typename T, typename OT, int D, bool CAUSAL>
 hipError_t launch16(const Launch &a) {
-  const dim3 grid((unsigned)(a.BH * a.nqt)), block(kThreads);
   if constexpr (D >= 64) {
     // c >= 0 here; a negative scale flips the sign of Q inside the kernel.
     const float c = a.c < 0.f ? -a.c : a.c;
-    hipLaunchKernelGGL((fa_fwd_pipe<T, OT, D, CAUSAL>), grid, block, 0, a.stream,
-                       (const T *)a.q, (const T *)a.k, (const T *)a.v, (OT *)a.o, a.lse,
-                       a.Nq, a.Nk, a.BH, a.nqt, c, a.c < 0.f ? 1 : 0);
+    const int neg = a.c < 0.f ? 1 : 0;
+    if (a.plan) {
+      const SplitPlan &pl = *a.plan;
+      hipLaunchKernelGGL((fa_fwd_pipe_split<T, OT, D, CAUSAL>),
+                         dim3((unsigned)(pl.npairs * a.BH)), dim3(kThreads), 0, a.stream,
+                         (const T *)a.q, (const T *)a.k, (const T *)a.v, (OT *)a.o, a.lse,
+                         a.ws, a.Nq, a.Nk, a.BH, a.nqt, c, neg, pl);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      constexpr int groups = kBM / (kThreads / (D / 4));
+      hipLaunchKernelGGL((fa_merge_parts<OT, D>),
+                         dim3((unsigned)((a.nqt - pl.t_split) * a.BH * groups)), dim3(kThreads), 0,
+                         a.stream, (const float *)a.ws, (OT *)a.o, a.lse, a.Nq, a.Nk, a.BH,
+                         a.nqt, CAUSAL ? 1 : 0, pl.W, pl.t_split, pl.p_max);
+    } else {
+      hipLaunchKernelGGL((fa_fwd_pipe<T, OT, D, CAUSAL>), dim3((unsigned)(a.BH * a.nqt)),
+                         dim3(kThreads), 0, a.stream, (const T *)a.q, (const T *)a.k,
+                         (const T *)a.v, (OT *)a.o, a.lse, a.Nq, a.Nk, a.BH, a.nqt, c, neg);
+    }
   } else {
-    hipLaunchKernelGGL((fa_fwd_mfma16<T, OT, D, CAUSAL>), grid, block, 0, a.stream,
-                       (const T *)a.q, (const T *)a.k, (const T *)a.v, (OT *)a.o, a.lse,
-                       a.Nq, a.Nk, a.BH, a.nqt, a.c);
+    hipLaunchKernelGGL((fa_fwd_mfma16<T, OT, D, CAUSAL>), dim3((unsigned)(a.BH * a.nqt)),
+                       dim3(kThreads), 0, a.stream, (const T *)a.q, (const T *)a.k,
+                       (const T *)a.v, (OT *)a.o, a.lse, a.Nq, a.Nk, a.BH, a.nqt, a.c);
   }
   return hipGetLastError();
 }
@@ -1007,72 +1219,140 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-}  // namespace
+// Sizes of the arguments of one call, filled by validate().
+struct Shape {
+  int64_t BH, nqt;
+  size_t qb, kb, ob, lb;
+};
 
-extern "C" {
-
-int fa_version(void) { return 100; }
-
-const char *fa_status_str(int s) {
-  switch (s) {
-    case FA_OK: return "ok";
-    case FA_ERR_NULLPTR: return "null pointer argument";
-    case FA_ERR_SHAPE: return "invalid shape (B, H, Nq, Nk must be >= 1 and sizes must fit)";
-    case FA_ERR_HEAD_DIM: return "unsupported head dimension (D must be 16, 32, 64 or 128)";
-    case FA_ERR_DTYPE: return "unknown dtype";
-    case FA_ERR_SCALE: return "scale is not finite";
-    case FA_ERR_ALIGN: return "misaligned pointer (q, k, v, o need 16 bytes, lse 4)";
-    case FA_ERR_HIP: return "HIP runtime error";
-    case FA_ERR_OVERLAP: return "output buffers overlap the inputs";
-    default: return "unknown status";
-  }
-}
-
-const char *fa_last_hip_error(void) { return g_hip_error; }
-
-int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
-           int64_t H, int64_t Nq, int64_t Nk, int64_t D, float scale, int causal,
-           int dtype, void *stream) {
+int validate(const void *q, const void *k, const void *v, const void *o, const float *lse,
+             int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, float scale,
+             int dtype, Shape &sh) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULLPTR;
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
   if (D != 16 && D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
   if (dtype < FA_F32 || dtype > FA_F16_OF32) return FA_ERR_DTYPE;
   if (!isfinite(scale)) return FA_ERR_SCALE;
-
   const int64_t in_size = (dtype == FA_F32) ? 4 : 2;
-  const int64_t out_size = (dtype == FA_F32 || dtype == FA_BF16_OF32 || dtype == FA_F16_OF32) ? 4 : 2;
-  // Per-head slices are addressed with 32-bit byte offsets (plus one tile of
-  // slack past the end for ragged rows); the grid is one-dimensional.
+  const int64_t out_size =
+      (dtype == FA_F32 || dtype == FA_BF16_OF32 || dtype == FA_F16_OF32) ? 4 : 2;
+  // Per-head slices are addressed with 32-bit byte offsets (plus slack past
+  // the end for ragged rows); the grid is one-dimensional.
   const int64_t lim = (int64_t)1 << 31;
-  if (Nq > lim / (D * 4) - kBM || Nk > lim / (D * 4) - kBN) return FA_ERR_SHAPE;
-  const int64_t BH = B * H;
-  if (B > lim || H > lim || BH > lim) return FA_ERR_SHAPE;
-  const int64_t nqt = (Nq + kBM - 1) / kBM;
-  if (BH * nqt >= lim) return FA_ERR_SHAPE;
-
+  if (Nq > lim / (D * 4) - kBM || Nk > lim / (D * 4) - 5 * kBN) return FA_ERR_SHAPE;
+  if (B > lim || H > lim || B * H > lim) return FA_ERR_SHAPE;
+  sh.BH = B * H;
+  sh.nqt = (Nq + kBM - 1) / kBM;
+  if (sh.BH * sh.nqt >= lim) return FA_ERR_SHAPE;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA_ERR_ALIGN;
   if ((uintptr_t)lse & 3u) return FA_ERR_ALIGN;
-
-  const size_t qb = (size_t)(BH * Nq * D * in_size), kb = (size_t)(BH * Nk * D * in_size);
-  const size_t ob = (size_t)(BH * Nq * D * out_size), lb = (size_t)(BH * Nq * 4);
-  if (overlaps(o, ob, q, qb) || overlaps(o, ob, k, kb) || overlaps(o, ob, v, kb) ||
-      overlaps(lse, lb, q, qb) || overlaps(lse, lb, k, kb) || overlaps(lse, lb, v, kb) ||
-      overlaps(o, ob, lse, lb))
+  sh.qb = (size_t)(sh.BH * Nq * D * in_size);
+  sh.kb = (size_t)(sh.BH * Nk * D * in_size);
+  sh.ob = (size_t)(sh.BH * Nq * D * out_size);
+  sh.lb = (size_t)(sh.BH * Nq * 4);
+  if (overlaps(o, sh.ob, q, sh.qb) || overlaps(o, sh.ob, k, sh.kb) ||
+      overlaps(o, sh.ob, v, sh.kb) || overlaps(lse, sh.lb, q, sh.qb) ||
+      overlaps(lse, sh.lb, k, sh.kb) || overlaps(lse, sh.lb, v, sh.kb) ||
+      overlaps(o, sh.ob, lse, sh.lb))
     return FA_ERR_OVERLAP;
+  return FA_OK;
+}
 
+// Compute units of the current device, queried once per device.
+int device_cus(int *cus) {
+  static int cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev >= 0 && dev < 64 && __atomic_load_n(&cache[dev], __ATOMIC_RELAXED) > 0) {
+    *cus = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+    return FA_OK;
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev >= 0 && dev < 64) __atomic_store_n(&cache[dev], n, __ATOMIC_RELAXED);
+  *cus = n;
+  return FA_OK;
+}
+
+constexpr int kMinPartTiles = 4;  // no part shorter than 256 keys
+
+// Decides whether (and how) the pipelined kernel splits the key ranges of
+// long query tiles: parts of about the mean per-CU work, so that the
+// longest-first order keeps every CU busy until the end.  Returns false when
+// every tile runs whole (no workspace needed).
+bool make_plan(int64_t BH, int64_t nqt, int64_t Nk, int64_t D, int dtype, bool causal,
+               int cus, SplitPlan &pl, size_t &ws_bytes) {
+  ws_bytes = 0;
+  if (dtype == FA_F32 || D < 64 || cus < 1 || nqt > 2047) return false;
+  int64_t total = 0, wmax = 0;
+  for (int t = 0; t < nqt; ++t) {
+    const int64_t w = tile_keys(t, (int)Nk, causal);
+    total += w;
+    wmax = w > wmax ? w : wmax;
+  }
+  total *= BH;
+  int64_t W = (total + cus - 1) / cus;
+  W = W < kMinPartTiles ? kMinPartTiles : W;
+  W = W < (wmax + kMaxParts - 1) / kMaxParts ? (wmax + kMaxParts - 1) / kMaxParts : W;
+  for (;; W *= 2) {
+    if (wmax <= W) return false;
+    int npairs = 0, pmax = 1, ts = -1;
+    for (int t = 0; t < nqt; ++t) {
+      const int64_t w = tile_keys(t, (int)Nk, causal);
+      const int p = (int)((w + W - 1) / W);
+      npairs += p;
+      pmax = p > pmax ? p : pmax;
+      if (p > 1 && ts < 0) ts = t;
+    }
+    if (npairs > kMaxPairs) continue;
+    pl.W = (int)W;
+    pl.t_split = ts;
+    pl.p_max = pmax;
+    pl.npairs = 0;
+    int size[kMaxPairs];
+    for (int t = (int)nqt - 1; t >= 0; --t) {
+      const int w = tile_keys(t, (int)Nk, causal);
+      const int p = (w + (int)W - 1) / (int)W;
+      const int st = (w + p - 1) / p;
+      for (int part = 0; part < p; ++part) {
+        const int kt0 = w - (p - part) * st > 0 ? w - (p - part) * st : 0;
+        const int kt1 = w - (p - part - 1) * st;
+        // insertion keeps the list in decreasing part size (stable)
+        int i = pl.npairs++;
+        while (i > 0 && size[i - 1] < kt1 - kt0) {
+          size[i] = size[i - 1];
+          pl.pair[i] = pl.pair[i - 1];
+          --i;
+        }
+        size[i] = kt1 - kt0;
+        pl.pair[i] = (uint16_t)(t | (part << 11));
+      }
+    }
+    const size_t nslots = (size_t)(nqt - ts) * pmax * BH;
+    ws_bytes = nslots * kBM * (size_t)(D + 4) * 4;
+    return true;
+  }
+}
+
+int run(const void *q, const void *k, const void *v, void *o, float *lse, int64_t Nq,
+        int64_t Nk, int64_t D, float scale, int causal, int dtype, const Shape &sh,
+        const SplitPlan *plan, void *ws, void *stream) {
   Launch a;
   a.q = q;
   a.k = k;
   a.v = v;
   a.o = o;
   a.lse = lse;
+  a.ws = (float *)ws;
   a.Nq = (int)Nq;
   a.Nk = (int)Nk;
-  a.BH = (int)BH;
-  a.nqt = (int)nqt;
+  a.BH = (int)sh.BH;
+  a.nqt = (int)sh.nqt;
   a.c = scale * 1.4426950408889634f;
   a.stream = (hipStream_t)stream;
-
+  a.plan = plan;
   hipError_t e;
   const bool cz = causal != 0;
   switch (dtype) {
@@ -1084,6 +1364,85 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int
   }
   if (e != hipSuccess) return hip_fail(e);
   return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_version(void) { return 200; }
+
+const char *fa_status_str(int s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULLPTR: return "null pointer argument";
+    case FA_ERR_SHAPE: return "invalid shape (B, H, Nq, Nk must be >= 1 and sizes must fit)";
+    case FA_ERR_HEAD_DIM: return "unsupported head dimension (D must be 16, 32, 64 or 128)";
+    case FA_ERR_DTYPE: return "unknown dtype";
+    case FA_ERR_SCALE: return "scale is not finite";
+    case FA_ERR_ALIGN: return "misaligned pointer (q, k, v, o, workspace need 16 bytes, lse 4)";
+    case FA_ERR_HIP: return "HIP runtime error";
+    case FA_ERR_OVERLAP: return "output or workspace buffers overlap each other or the inputs";
+    case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_fwd_workspace_size";
+    default: return "unknown status";
+  }
+}
+
+const char *fa_last_hip_error(void) { return g_hip_error; }
+
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
+           int64_t H, int64_t Nq, int64_t Nk, int64_t D, float scale, int causal,
+           int dtype, void *stream) {
+  Shape sh;
+  const int st = validate(q, k, v, o, lse, B, H, Nq, Nk, D, scale, dtype, sh);
+  if (st != FA_OK) return st;
+  return run(q, k, v, o, lse, Nq, Nk, D, scale, causal, dtype, sh, nullptr, nullptr, stream);
+}
+
+int fa_fwd_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+                          int causal, int dtype, size_t *bytes) {
+  if (!bytes) return FA_ERR_NULLPTR;
+  *bytes = 0;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
+  if (D != 16 && D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  if (dtype < FA_F32 || dtype > FA_F16_OF32) return FA_ERR_DTYPE;
+  const int64_t lim = (int64_t)1 << 31;
+  if (B > lim || H > lim || B * H > lim) return FA_ERR_SHAPE;
+  int cus = 0;
+  const int st = device_cus(&cus);
+  if (st != FA_OK) return st;
+  SplitPlan pl;
+  size_t ws = 0;
+  make_plan(B * H, (Nq + kBM - 1) / kBM, Nk, D, dtype, causal != 0, cus, pl, ws);
+  *bytes = ws;
+  return FA_OK;
+}
+
+int fa_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
+              int64_t H, int64_t Nq, int64_t Nk, int64_t D, float scale, int causal,
+              int dtype, void *workspace, size_t workspace_bytes, void *stream) {
+  Shape sh;
+  int st = validate(q, k, v, o, lse, B, H, Nq, Nk, D, scale, dtype, sh);
+  if (st != FA_OK) return st;
+  if (workspace) {
+    if ((uintptr_t)workspace & 15u) return FA_ERR_ALIGN;
+    if (overlaps(workspace, workspace_bytes, q, sh.qb) ||
+        overlaps(workspace, workspace_bytes, k, sh.kb) ||
+        overlaps(workspace, workspace_bytes, v, sh.kb) ||
+        overlaps(workspace, workspace_bytes, o, sh.ob) ||
+        overlaps(workspace, workspace_bytes, lse, sh.lb))
+      return FA_ERR_OVERLAP;
+  }
+  int cus = 0;
+  st = device_cus(&cus);
+  if (st != FA_OK) return st;
+  SplitPlan pl;
+  size_t need = 0;
+  if (!make_plan(sh.BH, sh.nqt, Nk, D, dtype, causal != 0, cus, pl, need))
+    return run(q, k, v, o, lse, Nq, Nk, D, scale, causal, dtype, sh, nullptr, nullptr,
+               stream);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  return run(q, k, v, o, lse, Nq, Nk, D, scale, causal, dtype, sh, &pl, workspace, stream);
 }
 
 }  // extern "C"
