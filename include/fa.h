@@ -101,21 +101,24 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
 
 /*
  * fa_fwd_workspace_size -- device scratch bytes that fa_fwd_ws needs for
- * this problem on the current device (written to *bytes; 0 when the call
- * runs every query tile whole).
+ * this problem on the current device (written to *bytes; 0 when fa_fwd_ws
+ * takes the same path as fa_fwd: fp32 inputs, D < 64, or at least four
+ * query tiles of 128 rows per compute unit, where one workgroup per tile
+ * already keeps every unit busy).
  *
- * Long rows of a causal pass see many more keys than short ones, so one
- * workgroup per query tile leaves most compute units idle while the longest
- * tiles finish.  fa_fwd_ws cuts the key range of long tiles into parts of
- * about the mean per-unit work; each part keeps its own running max, sum
- * and O in the workspace, and a second kernel combines the parts with the
- * rescaling that the online softmax applies when it folds one key block
- * into the running statistics (page "FlashAttention-2实现与优化：高效注意力
- * 机制详解" §3.1, the incremental update of (m, l, o_acc)).  Cutting the
- * work along the sequence is the sequence parallelism of page
- * "FlashAttention技术演进全景图" §3.2.  The plan depends on the shape, dtype,
- * causal flag and the device's compute-unit count, not on the data.
- * Splitting is used with 16-bit inputs and D in {64, 128}.
+ * One workgroup per query tile leaves compute units idle when tiles are
+ * few or, under the causal mask, of very unequal length.  fa_fwd_ws instead
+ * lays all the work out as one sequence of (query tile, 64-key tile) units
+ * and gives each compute unit an equal contiguous share of it (a stream-K
+ * schedule, with query tiles in zigzag order so that every share mixes
+ * short and long causal rows).  A query tile cut between two shares keeps
+ * one partial (running max, sum, O) per share in the workspace, and a
+ * second kernel combines them with the rescaling that the online softmax
+ * applies when it folds one key block into the running statistics (page
+ * "FlashAttention-2实现与优化：高效注意力机制详解" §3.1, the incremental
+ * update of (m, l, o_acc)).  Cutting the work along the sequence is the
+ * sequence parallelism of page "FlashAttention技术演进全景图" §3.2.  The size
+ * is 2 * G * 128 * (D + 4) * 4 bytes, G = min(compute units, units of work).
  *
  * Returns FA_OK, FA_ERR_NULLPTR (bytes NULL), FA_ERR_SHAPE, FA_ERR_HEAD_DIM,
  * FA_ERR_DTYPE or FA_ERR_HIP (device query failed).
@@ -128,7 +131,8 @@ int fa_fwd_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk,
  *
  * Arguments as fa_fwd, plus
  *   workspace        device pointer, 16-byte aligned, or NULL when
- *                    fa_fwd_workspace_size reports 0 bytes
+ *                    fa_fwd_workspace_size reports 0 bytes (then the call
+ *                    is fa_fwd)
  *   workspace_bytes  its size in bytes
  *
  * Computes the same O and lse as fa_fwd up to fp32 rounding order (the

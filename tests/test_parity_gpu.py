@@ -135,6 +135,9 @@ EDGE = [
     (1, 3, 77, 200, 128),
     (5, 3, 256, 256, 16),
     (2, 2, 513, 513, 128),
+    (2, 1, 100, 20, 64),    # every key in the first 32-key block
+    (1, 2, 70, 32, 128),    # second 32-key block of the only key tile empty
+    (1, 1, 300, 33, 128),
 ]
 
 
@@ -227,7 +230,10 @@ def _ws_bytes(B, H, Nq, Nk, D, causal, code):
 
 
 SPLIT = [
-    # (B, H, Nq, Nk, D): shapes whose plan cuts tiles into several parts
+    # (B, H, Nq, Nk, D): shapes whose schedule cuts tiles into several pieces
+    (1, 1, 1000, 1000, 128),  # 128 units over 128 CUs: every piece one key tile
+    (1, 1, 64, 64, 64),       # a single unit
+    (3, 1, 129, 4000, 64),    # two query tiles, the second of one row
     (1, 1, 2048, 2048, 128),
     (1, 2, 1000, 3000, 64),
     (1, 1, 3000, 1000, 128),
@@ -259,6 +265,8 @@ def test_split_workspace_contract():
     assert need == _ws_bytes(B, H, Nq, Nk, D, 1, fa.FA_BF16_OF32)
     assert _ws_bytes(B, H, Nq, Nk, D, 1, fa.FA_F32) == 0
     assert _ws_bytes(B, H, Nq, Nk, 32, 1, fa.FA_BF16) == 0
+    cus = torch.cuda.get_device_properties(DEV).multi_processor_count
+    assert _ws_bytes(4 * cus, 1, 128, 128, D, 1, fa.FA_BF16) == 0  # many tiles
     ws = torch.empty(need, dtype=torch.uint8, device=DEV)
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
             B, H, Nq, Nk, D, 0.1, 1, fa.FA_BF16)
@@ -268,10 +276,9 @@ def test_split_workspace_contract():
     assert fa.fa_fwd_ws(*args, ws.data_ptr() + 8, need - 8, sp) == fa.FA_ERR_ALIGN
     assert fa.fa_fwd_ws(*args, o.data_ptr(), need, sp) == fa.FA_ERR_OVERLAP
     assert fa.fa_fwd_ws(*args, ws.data_ptr(), need, sp) == fa.FA_OK
-    # a shape that does not split runs without scratch
+    # a path without a schedule (D < 64) runs without scratch
     small = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-             1, 1, 64, 64, D, 0.1, 1, fa.FA_BF16)
-    assert _ws_bytes(1, 1, 64, 64, D, 1, fa.FA_BF16) == 0
+             1, 1, 64, 64, 32, 0.1, 1, fa.FA_BF16)
     assert fa.fa_fwd_ws(*small, None, 0, sp) == fa.FA_OK
     torch.cuda.synchronize()
 

@@ -37,6 +37,7 @@
 //     scores, p = 2^(c*s - m2), and L = ln2 * (m2 + log2 l).
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 
 #include <math.h>
 #include <stdint.h>
@@ -55,6 +56,7 @@ constexpr int kBN = 64;           // keys per tile
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -92,6 +94,12 @@ template <> struct Mfma16<__bf16> {
     const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), one, acc, false);
   }
+  // (a, b) rounded to nearest-even bf16, a in the low half.
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const f32x2 x = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+  }
 };
 
 template <> struct Mfma16<_Float16> {
@@ -104,6 +112,12 @@ template <> struct Mfma16<_Float16> {
     typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
     const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), one, acc, false);
+  }
+  // (a, b) rounded to nearest-even fp16, a in the low half.
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f32x2 x = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2));
   }
 };
 
@@ -416,17 +430,13 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Ring wait of one pipeline step: with `one` the youngest issue unit may
-// still be in flight (n0 loads for waves that issue the extra K load, n
-// for the others), otherwise nothing may.
-template <int N0, int N>
-__device__ __forceinline__ void ring_wait(bool one, bool extra) {
-  if (!one)
-    ring_barrier<0>();
-  else if (extra)
-    ring_barrier<N0>();
-  else
+// Ring wait with one per-wave load count for every wave.
+template <int N>
+__device__ __forceinline__ void ring_barrier_sel(bool one) {
+  if (one)
     ring_barrier<N>();
+  else
+    ring_barrier<0>();
 }
 
 // 16-byte buffer load into registers, as asm: the compiler does not count it
@@ -447,17 +457,9 @@ struct PipeLayout {
   static constexpr int V_BYTES = kBN * SV * 16;
   static constexpr int K_INS = kBN * SK / kWave;      // DMA instructions per K tile
   static constexpr int V_INS = kBN * SV / kWave;
-  static constexpr int K_PER_WAVE = (K_INS + kWaves - 1) / kWaves;  // wave 0's share
-  static constexpr int V_PER_WAVE = V_INS / kWaves;
-  static constexpr int K_EXTRA = K_INS % kWaves;      // waves < K_EXTRA issue one more
   static constexpr int V_OFF = kStages * K_BYTES;     // V ring after the K ring
   static constexpr int LDS_BYTES = kStages * (K_BYTES + V_BYTES);
   static constexpr uint32_t TILE_GLOBAL = kBN * D * sizeof(T);  // bytes per tile in HBM
-  // loads one wave issues per issue_unit (wave 0 / the others)
-  static constexpr int UNIT0 = K_PER_WAVE + V_PER_WAVE;
-  static constexpr int UNIT = K_PER_WAVE - (K_EXTRA ? 1 : 0) + V_PER_WAVE;
-  static_assert(V_INS % kWaves == 0, "V DMA must split evenly");
-  static_assert(K_EXTRA <= 1, "at most wave 0 issues an extra K load");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
@@ -537,11 +539,19 @@ struct Pipe {
     for (int f = 0; f < QF; ++f) sc = Mfma16<T>::mma(kfrag(kp, f), qf[f], sc);
   }
 
-  // acc += V^T P^T of a 32-key block (no overlap; drain only).
+  // acc += V^T P^T of a 32-key block (no overlap; drain only).  Fragments
+  // are read two MFMAs ahead, as in block_step: this runs inside the ring
+  // loop, where the S and P registers of the pipeline are still live.
   __device__ __forceinline__ void pv(const lds_char *vp, const frag (&pin)[2]) {
+    frag vf[NPV];
+    vf[0] = vfrag(vp, 0);
+    vf[1] = vfrag(vp, 1);
 #pragma unroll
-    for (int m = 0; m < NPV; ++m)
-      acc[m % NDB] = Mfma16<T>::mma(vfrag(vp, m), pin[m / NDB], acc[m % NDB]);
+    for (int m = 0; m < NPV; ++m) {
+      acc[m % NDB] = Mfma16<T>::mma(vf[m], pin[m / NDB], acc[m % NDB]);
+      if (m + 2 < NPV) vf[m + 2] = vfrag(vp, m + 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // Hides keys >= Nk and (causal) keys after the row's query: S := -inf.
@@ -561,9 +571,9 @@ struct Pipe {
   // into pout), so the VALU work runs while the MFMA pipe is busy.  Slices:
   //   0-1   row maximum of the block
   //   2     half-wave exchange, lazy move of the exponent reference, alpha
-  //   3-10  p = 2^(c*s - m) and its fp32 sum, two elements per slice
-  //   11-12 rounding of p to T (the P.V operand) and the sum of the rounded p
-  //   13    l, lr
+  //   3-10  p = 2^(c*s - m) for two elements, their fp32 sum, their rounding
+  //         to T (one packed word of the P.V operand) and its sum
+  //   11    l, lr
   // The reference moves per lane, only when the block's maximum exceeds it
   // by more than kLazy (both half-waves of a query take the same decision);
   // acc is then scaled by alpha after the block (a rare, wave-uniform
@@ -575,11 +585,11 @@ struct Pipe {
   __device__ __forceinline__ void block_step(const lds_char *kp, const lds_char *vp,
                                              f32x16 &sin, f32x16 &sout,
                                              const frag (&pin)[2], frag (&pout)[2]) {
-    constexpr int NCHUNK = 14;
+    constexpr int NCHUNK = 12;
     frag kf[QF], vf[NPV];
     float mx = 0.f, nm = 0.f, alpha = 1.f, psum = 0.f, rsum = 0.f;
     bool need = false;
-    f32x16 pf;  // p in fp32
+    u32x4 pw[2];  // p rounded to T, packed in pairs (the two P.V operands)
     sout = f32x16{};
 
     auto chunk = [&](int ch) {
@@ -602,32 +612,32 @@ struct Pipe {
         const float mt = mx * c;  // -inf or NaN when the row sees no key of this block
         need = mt > m_use + kLazy;
         const float m_new = need ? mt : m_use;
-        alpha = __builtin_amdgcn_exp2f(m_use - m_new);
+        // exactly 1 when the reference stays (also while it is still -inf:
+        // a fully masked first block must not turn l into NaN)
+        alpha = need ? __builtin_amdgcn_exp2f(m_use - m_new) : 1.f;
         m_use = m_new;
         nm = -m_new;
         asm volatile("" ::"v"(alpha), "v"(nm));
       } else if (ch <= 10) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int r = 2 * (ch - 3) + t;
-          float e = __builtin_fmaf(sin[r], c, nm);
-          if (MASKED) e = fmaxf(e, -3.0e38f);  // NaN or -inf -> 2^-3e38 = 0
-          pf[r] = __builtin_amdgcn_exp2f(e);
-          psum += pf[r];
+        const int w = ch - 3;  // packed word: elements 2w, 2w+1
+        float e0 = __builtin_fmaf(sin[2 * w], c, nm);
+        float e1 = __builtin_fmaf(sin[2 * w + 1], c, nm);
+        if (MASKED) {  // NaN or -inf -> 2^-3e38 = 0
+          e0 = fmaxf(e0, -3.0e38f);
+          e1 = fmaxf(e1, -3.0e38f);
         }
-        asm volatile("" ::"v"(pf[2 * (ch - 3)]), "v"(pf[2 * (ch - 3) + 1]), "v"(psum));
-      } else if (ch <= 12) {
-        const int hh = ch - 11;
-        const f32x8 p8 = {pf[8 * hh + 0], pf[8 * hh + 1], pf[8 * hh + 2], pf[8 * hh + 3],
-                          pf[8 * hh + 4], pf[8 * hh + 5], pf[8 * hh + 6], pf[8 * hh + 7]};
-        pout[hh] = __builtin_convertvector(p8, frag);
-        const u32x4 packed = __builtin_bit_cast(u32x4, pout[hh]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rsum = Mfma16<T>::pair_sum(packed[i], rsum);
-        asm volatile("" ::"v"(pout[hh]), "v"(rsum));
+        const float p0 = __builtin_amdgcn_exp2f(e0);
+        const float p1 = __builtin_amdgcn_exp2f(e1);
+        psum += p0 + p1;
+        const uint32_t word = Mfma16<T>::pack2(p0, p1);
+        pw[w / 4][w % 4] = word;
+        rsum = Mfma16<T>::pair_sum(word, rsum);
+        asm volatile("" ::"v"(word), "v"(psum), "v"(rsum));
       } else {
         l = l * alpha + psum;
         lr = lr * alpha + rsum;
+        pout[0] = __builtin_bit_cast(frag, pw[0]);
+        pout[1] = __builtin_bit_cast(frag, pw[1]);
         asm volatile("" ::"v"(l), "v"(lr));
       }
     };
@@ -664,7 +674,10 @@ struct Pipe {
   // Block b of this wave (its tile-local half and ring stages given): full
   // step, masked step (causal diagonal / key tail), the drain (P.V of the
   // wave's last block) or nothing.
-  template <bool ODD>
+  // STRIDE: distance between this wave's consecutive blocks (1 when a wave
+  // takes every block, 2 when two waves share a query group by block parity).
+  // STRIDE 0: no drain here (the caller runs it after the ring loop).
+  template <bool ODD, int STRIDE = 1>
   __device__ __forceinline__ void block(const lds_char *ring, int b, int lastb,
                                         int vst, int vhalf, int kst, int khalf) {
     f32x16 &sin = ODD ? S1 : S0;
@@ -682,33 +695,11 @@ struct Pipe {
       } else {
         block_step<false>(kp, vp, sin, sout, pin, pout);
       }
-    } else if (b == lastb + 1) {
+    } else if (STRIDE > 0 && b - STRIDE <= lastb) {
       pv(vp, pin);
     }
   }
 };
-
-// Issues the DMA of one K tile and one V tile (absolute tile indices) into
-// ring stages kst and vst.
-template <typename L>
-__device__ __forceinline__ void issue_unit(u32x4 k_rs, u32x4 v_rs, uint32_t ring_addr,
-                                           const uint32_t *ksrc, const uint32_t *vsrc,
-                                           int wave, int ktile, int kst, int vtile, int vst) {
-  const uint32_t koff = (uint32_t)ktile * L::TILE_GLOBAL;
-  const uint32_t voff = (uint32_t)vtile * L::TILE_GLOBAL;
-#pragma unroll
-  for (int i = 0; i < L::K_PER_WAVE; ++i) {
-    if (i < L::K_PER_WAVE - 1 || L::K_EXTRA == 0 || wave < L::K_EXTRA) {
-      const uint32_t ins = i * kWaves + wave;
-      dma16(k_rs, ring_addr + kst * L::K_BYTES + ins * kWave * 16, ksrc[i] + koff);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < L::V_PER_WAVE; ++i) {
-    const uint32_t ins = i * kWaves + wave;
-    dma16(v_rs, ring_addr + L::V_OFF + vst * L::V_BYTES + ins * kWave * 16, vsrc[i] + voff);
-  }
-}
 
 // The work of one workgroup: query rows [q0, q0 + 128) of head bh against
 // key tiles [kt0, kt1) (64 keys each).  slot < 0: the item covers every key
@@ -746,24 +737,102 @@ __device__ __forceinline__ void epilogue_partial(const f32x16 (&acc)[D / 32], fl
   }
 }
 
+// ---------------------------------------------------------------------------
+// Eight waves per workgroup, two per SIMD.  Waves w and w + 4 hold the same
+// 32 query rows (group w % 4, on the same SIMD) and split the key blocks by
+// parity: wave w takes the even 32-key blocks, wave w + 4 the odd ones, so
+// in every ring step each wave runs one block (soft-max of its block, K.Q^T
+// of its next block, P.V of its previous block) while its partner's
+// instruction stream fills the SIMD's idle issue slots.  At the end the
+// pair's running statistics and accumulators are combined through LDS with
+// the online-softmax rescaling (2^(m_i - M)), and the even wave writes O and
+// L (or the split part's partial result).
+constexpr int kWaves8 = 8;
+constexpr int kThreads8 = kWave * kWaves8;
+
+// DMA of one ring unit (one K tile, one V tile): each tile's 16-byte-per-lane
+// load instructions are dealt to the eight waves round-robin, K in the first
+// KJ slots of every wave and V in the next VJ, each padded to a multiple of
+// eight with dummy loads (out of range, so they fetch nothing and write
+// zeros into a 1 KB LDS scratch line).  Every wave issues the same number of
+// loads per unit, so one vmcnt value describes "the youngest unit may still
+// be in flight" for all of them, and each slot's tile (K or V) is known at
+// compile time.
+template <typename T, int D>
+struct Dma8 {
+  typedef PipeLayout<T, D> L;
+  static constexpr int KJ = (L::K_INS + kWaves8 - 1) / kWaves8;
+  static constexpr int VJ = (L::V_INS + kWaves8 - 1) / kWaves8;
+  static constexpr int PER_WAVE = KJ + VJ;
+  static constexpr int SCRATCH = L::LDS_BYTES;
+  static constexpr int LDS_BYTES = L::LDS_BYTES + kWave * 16;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+
+  uint32_t src[PER_WAVE];    // per-lane byte offset in tile 0 (or out of range)
+  uint32_t lbase[PER_WAVE];  // LDS destination in stage 0 (wave-uniform)
+  uint32_t lstride[PER_WAVE];
+
+  __device__ __forceinline__ void init(uint32_t ring_addr, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const bool isk = j < KJ;
+      const int i = (isk ? j : j - KJ) * kWaves8 + wave;  // instruction within the tile
+      uint32_t lb, ls;
+      if (i < (isk ? L::K_INS : L::V_INS)) {
+        lb = ring_addr + (isk ? 0u : (uint32_t)L::V_OFF) + (uint32_t)i * kWave * 16;
+        ls = isk ? L::K_BYTES : L::V_BYTES;
+        src[j] = dma_src<T, D>(i, lane, isk ? L::SK : L::SV);
+      } else {
+        lb = ring_addr + SCRATCH;
+        ls = 0;
+        src[j] = kOutOfRange;
+      }
+      // wave-uniform: keep them in scalar registers
+      lbase[j] = __builtin_amdgcn_readfirstlane(lb);
+      lstride[j] = __builtin_amdgcn_readfirstlane(ls);
+    }
+  }
+
+  // K tile `ktile` into stage kst, V tile `vtile` into stage vst (absolute
+  // tile indices of the head's slice).
+  __device__ __forceinline__ void issue(u32x4 k_rs, u32x4 v_rs, int ktile, int kst,
+                                        int vtile, int vst) const {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const bool isk = j < KJ;
+      const uint32_t lds = lbase[j] + (uint32_t)(isk ? kst : vst) * lstride[j];
+      const uint32_t off = src[j] + (uint32_t)(isk ? ktile : vtile) * L::TILE_GLOBAL;
+      dma16(isk ? k_rs : v_rs, lds, off);
+    }
+  }
+};
+
 template <typename T, typename OT, int D, bool CAUSAL>
-__device__ __forceinline__ void pipe_run(const T *__restrict__ q, const T *__restrict__ k,
-                                         const T *__restrict__ v, OT *__restrict__ o,
-                                         float *__restrict__ lse, float *__restrict__ ws,
-                                         int Nq, int Nk, float c, int negate,
-                                         const PipeItem it, int nslots) {
+__device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__restrict__ k,
+                                          const T *__restrict__ v, OT *__restrict__ o,
+                                          float *__restrict__ lse, float *__restrict__ ws,
+                                          int Nq, int Nk, float c, int negate,
+                                          const PipeItem it, int nslots) {
   typedef Pipe<T, OT, D, CAUSAL> P;
   typedef typename P::L L;
   typedef typename P::frag frag;
-  __shared__ __attribute__((aligned(16))) char ring_[L::LDS_BYTES];
+  typedef Dma8<T, D> DM;
+  constexpr int UNIT = DM::PER_WAVE;
+  __shared__ __attribute__((aligned(16))) char ring_[DM::LDS_BYTES];
   lds_char *ring = (lds_char *)ring_;
   const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
 
   P s;
-  const int tid = threadIdx.x;
+  // Opaque per call: a workgroup running several items recomputes the
+  // lane-derived addresses for each one instead of keeping them in
+  // registers across items (there are none to spare).
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qg = wave & 3;  // query group (32 rows)
+  const int h = wave >> 2;  // block parity
   s.lane = tid & 63;
-  // wave-uniform: keeps the per-wave causal decisions in scalar branches
-  s.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  s.wave = qg;
   s.l32 = s.lane & 31;
   s.g = s.lane >> 5;
   s.Nk = Nk;
@@ -775,66 +844,44 @@ __device__ __forceinline__ void pipe_run(const T *__restrict__ q, const T *__res
     const int col = 16 * (G & 1) + 4 * (s16 & 3);  // element within the 32-wide d block
     s.vbase = (uint32_t)L::V_OFF + (uint32_t)row * L::SV * 16 + (uint32_t)col * 2;
   }
-
-  s.qw = it.q0 + s.wave * 32;
+  s.qw = it.q0 + qg * 32;
   s.my_q = s.qw + s.l32;
   const size_t qoff = (size_t)it.bh * Nq * D;
   const size_t koff = (size_t)it.bh * Nk * D;
   const u32x4 q_rs = raw_rsrc(q + qoff, (uint32_t)Nq * D * sizeof(T));
   const u32x4 k_rs = raw_rsrc(k + koff, (uint32_t)Nk * D * sizeof(T));
   const u32x4 v_rs = raw_rsrc(v + koff, (uint32_t)Nk * D * sizeof(T));
-
-  uint32_t ksrc[L::K_PER_WAVE], vsrc[L::V_PER_WAVE];
-#pragma unroll
-  for (int i = 0; i < L::K_PER_WAVE; ++i)
-    ksrc[i] = dma_src<T, D>(i * kWaves + s.wave, s.lane, L::SK);
-#pragma unroll
-  for (int i = 0; i < L::V_PER_WAVE; ++i)
-    vsrc[i] = dma_src<T, D>(i * kWaves + s.wave, s.lane, L::SV);
+  DM dm;
+  dm.init(ring_addr, wave, s.lane);
 
   const int kt0 = it.kt0;
   const int ntiles = it.kt1 - it.kt0;
-  // last 32-key block (absolute index) this wave needs in this item
   const int lastb = CAUSAL ? min(2 * it.kt1 - 1, s.qw / 32) : 2 * it.kt1 - 1;
-  const bool extra = L::K_EXTRA && s.wave < L::K_EXTRA;
 
-  // Q first: its loads are the oldest in flight, so the prologue wait for
-  // the first K/V unit covers them too.
+  // Q first (see pipe_run): the prologue wait covers it.
   u32x4 qraw[P::QF];
 #pragma unroll
   for (int f = 0; f < P::QF; ++f)
     qraw[f] = load16_async(q_rs, ((uint32_t)s.my_q * D + 16 * f + 8 * s.g) * sizeof(T));
 
-  // The first block's P.V belongs to the block before the item (P = 0) and
-  // reads V rows 32..63 of stage 3, which no load has written yet: clear
-  // them so that 0 * stale LDS cannot give NaN.  Everything else the kernel
-  // reads was written by a load (rows past Nk by the bounds check, as zero).
+  // The first step's P.V belongs to the block before the item (P = 0) and
+  // reads V stage 3 (both halves), which no load has written yet: clear it.
   {
-    constexpr int Z0 = L::V_OFF + 3 * L::V_BYTES + 32 * L::SV * 16;
-    constexpr int ZN = 32 * L::SV;  // 16-byte chunks
-    for (int i = tid; i < ZN; i += kThreads)
+    constexpr int Z0 = L::V_OFF + 3 * L::V_BYTES;
+    constexpr int ZN = L::V_BYTES / 16;
+    for (int i = tid; i < ZN; i += kThreads8)
       *(__attribute__((address_space(3))) u32x4 *)(ring + Z0 + i * 16) = u32x4{};
   }
 
-  // Issue units: unit 0 = (K0,V0), 1 = (K1,V1), 2 = (K2,V2) in the
-  // prologue, then step r issues unit r+3 = (K(r+3), V(r+2)) (relative
-  // tiles; tile j lives in ring stage j % 4).  Unit j >= 1 is issued only
-  // when j <= ntiles: nothing is fetched past the item except one K tile
-  // whose scores are never used.  Every unit has the same per-wave load
-  // count, so "the youngest unit may be in flight" is one vmcnt value.
-  issue_unit<L>(k_rs, v_rs, ring_addr, ksrc, vsrc, s.wave, kt0, 0, kt0, 0);
-  issue_unit<L>(k_rs, v_rs, ring_addr, ksrc, vsrc, s.wave, kt0 + 1, 1, kt0 + 1, 1);
-  if (ntiles >= 2)
-    issue_unit<L>(k_rs, v_rs, ring_addr, ksrc, vsrc, s.wave, kt0 + 2, 2, kt0 + 2, 2);
-  // Q and unit 0 landed (units 1 and 2 may be in flight); the zeroed rows
-  // are visible to every wave.
+  // Units as in pipe_run: 0..2 in the prologue, unit r+3 = (K(r+3), V(r+2))
+  // in step r; unit j >= 1 only when j <= ntiles.
+  dm.issue(k_rs, v_rs, kt0, 0, kt0, 0);
+  dm.issue(k_rs, v_rs, kt0 + 1, 1, kt0 + 1, 1);
   if (ntiles >= 2) {
-    if (extra)
-      ring_barrier<2 * L::UNIT0>();
-    else
-      ring_barrier<2 * L::UNIT>();
+    dm.issue(k_rs, v_rs, kt0 + 2, 2, kt0 + 2, 2);
+    ring_barrier<2 * UNIT>();
   } else {
-    ring_wait<L::UNIT0, L::UNIT>(true, extra);
+    ring_barrier<UNIT>();
   }
 #pragma unroll
   for (int f = 0; f < P::QF; ++f) {
@@ -850,148 +897,299 @@ __device__ __forceinline__ void pipe_run(const T *__restrict__ q, const T *__res
   s.lr = 0.f;
   s.P1[0] = frag{};  // P.V of the block before the first adds nothing
   s.P1[1] = frag{};
-  s.qk(s.kptr(ring, 0, 0), s.S0);
+  s.qk(s.kptr(ring, 0, h), s.S0);
 
-  // Step r reads K tiles r, r+1 and V tiles r-1, r (relative):
-  //   block 2r  : P.V(V tile r-1, rows 32..63), K.Q^T(K tile r, rows 32..63)
-  //   block 2r+1: P.V(V tile r, rows 0..31),    K.Q^T(K tile r+1, rows 0..31)
-  // K(r+1) and V(r) belong to units <= r+1, issued at least two steps
-  // earlier; unit r+2 (issued in step r-1, if at all) may still be in
-  // flight.  Step r requests unit r+3: K(r+3) into the stage of K(r-1) and
-  // V(r+2) into the stage of V(r-2), both last read in step r-1.  Every
-  // wave runs every step so that the loads and barriers line up.
-  for (int r = 0; r <= ntiles; ++r) {
-    ring_wait<L::UNIT0, L::UNIT>(r + 2 <= ntiles, extra);
+  // Step r: this wave's block b = 2(kt0 + r) + h.  It reads K tile r+1
+  // (half h, for the K.Q^T of block b+2) and V tile r-1 (half h, for the
+  // P.V of block b-2).  K(r+1) was requested in step r-2 and V(r-1) in step
+  // r-3 (or the prologue); unit r+2 may still be in flight.  Step r's
+  // request of unit r+3 overwrites K(r-1) and V(r-2), last read in steps
+  // r-2 and r-1.  Two steps per iteration: S and P alternate registers.
+  auto step = [&](int r, auto odd) {
+    ring_barrier_sel<UNIT>(r + 2 <= ntiles);
     if (r + 3 <= ntiles)
-      issue_unit<L>(k_rs, v_rs, ring_addr, ksrc, vsrc, s.wave, kt0 + r + 3,
-                    (r + 3) & (kStages - 1), kt0 + r + 2, (r + 2) & (kStages - 1));
-    const int st0 = r & (kStages - 1);
-    const int stm = (r + kStages - 1) & (kStages - 1);
-    const int st1 = (r + 1) & (kStages - 1);
-    const int b = 2 * (kt0 + r);
-    s.template block<false>(ring, b, lastb, stm, 1, st0, 1);
-    s.template block<true>(ring, b + 1, lastb, st0, 0, st1, 0);
+      dm.issue(k_rs, v_rs, kt0 + r + 3, (r + 3) & (kStages - 1), kt0 + r + 2,
+               (r + 2) & (kStages - 1));
+    const int b = 2 * (kt0 + r) + h;
+    s.template block<decltype(odd)::value, 0>(ring, b, lastb, (r + kStages - 1) & (kStages - 1),
+                                              h, (r + 1) & (kStages - 1), h);
+  };
+  for (int r = 0; r < ntiles; r += 2) {
+    step(r, std::false_type{});
+    if (r + 1 < ntiles) step(r + 1, std::true_type{});
   }
-  wait_vmcnt<0>();  // no DMA may outlive the workgroup's LDS
+  // Drain: P.V of this wave's last block.  The last step's wait covered
+  // every unit issued (units <= ntiles), and no unit overwrites the V tiles
+  // of the item's last four steps, so that block's V is still in the ring.
+  // Its P sits in P0 or P1 by the parity of the step that made it.
+  {
+    const int mylast = lastb - ((lastb - h) & 1);  // last block of parity h
+    if (mylast >= 2 * kt0 + h) {
+      const int rl = mylast / 2 - kt0;
+      frag pl[2];
+      pl[0] = (rl & 1) ? s.P1[0] : s.P0[0];
+      pl[1] = (rl & 1) ? s.P1[1] : s.P0[1];
+      s.pv(s.vptr(ring, rl & (kStages - 1), h), pl);
+    }
+  }
+  wait_vmcnt<0>();  // no DMA may outlive the ring
+
+  // Combine the pair: the odd wave hands (m, l, lr, acc) to the even one.
+  ring_barrier<0>();  // every wave is done with the ring
+  constexpr int NR = P::NDB * 4;  // f32x4 registers of acc per lane
+  lds_char *xch = ring + (uint32_t)qg * (NR + 1) * kWave * 16;
+  if (h == 1) {
+#pragma unroll
+    for (int db = 0; db < P::NDB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 x = {s.acc[db][4 * r4], s.acc[db][4 * r4 + 1], s.acc[db][4 * r4 + 2],
+                         s.acc[db][4 * r4 + 3]};
+        *(__attribute__((address_space(3))) f32x4 *)(xch + ((db * 4 + r4) * kWave + s.lane) * 16) = x;
+      }
+    const f32x4 st = {s.m_use, s.l, s.lr, 0.f};
+    *(__attribute__((address_space(3))) f32x4 *)(xch + (NR * kWave + s.lane) * 16) = st;
+  }
+  ring_barrier<0>();
+  f32x4 st = {0.f, 0.f, 0.f, 0.f};
+  if (h == 0) st = *(const __attribute__((address_space(3))) f32x4 *)(xch + (NR * kWave + s.lane) * 16);
+  // A wave that saw no key of a row (its blocks lie past the row under the
+  // causal mask, or the item starts there) has m = -inf, l = 0, acc = 0 and
+  // weight 0; when neither wave saw one the row's partial is empty (l = 0).
+  const float M = fmaxf(s.m_use, st[0]);
+  const float a0 = s.m_use == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s.m_use - M);
+  const float a1 = st[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st[0] - M);
+  const float l = s.l * a0 + st[1] * a1;
+  const float lr = s.lr * a0 + st[2] * a1;
+  if (h == 0) {
+#pragma unroll
+    for (int db = 0; db < P::NDB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 x = *(const __attribute__((address_space(3))) f32x4 *)(
+            xch + ((db * 4 + r4) * kWave + s.lane) * 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          s.acc[db][4 * r4 + e] = s.acc[db][4 * r4 + e] * a0 + x[e] * a1;
+      }
+  }
+  // The ring is free for the workgroup's next item once every read of the
+  // exchange area is done.
+  ring_barrier<0>();
+  if (h == 1) return;
 
   if (it.slot < 0) {
-    epilogue<D, OT>(s.acc, s.m_use, s.l, o, lse, it.bh, Nq, s.my_q, s.g, s.lr);
+    epilogue<D, OT>(s.acc, M, l, o, lse, it.bh, Nq, s.my_q, s.g, lr);
   } else {
     float *ws_o = ws + (size_t)it.slot * kBM * D;
     float *ws_s = ws + (size_t)nslots * kBM * D + (size_t)it.slot * kBM * 4;
-    epilogue_partial<D>(s.acc, s.m_use, s.l, s.lr, ws_o, ws_s, s.my_q - it.q0, s.g);
+    epilogue_partial<D>(s.acc, M, l, lr, ws_o, ws_s, s.my_q - it.q0, s.g);
   }
 }
 
-// One workgroup per 128-row query tile, longest causal tiles first.
 template <typename T, typename OT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void fa_fwd_pipe(
+__global__ __launch_bounds__(kThreads8) void fa_fwd_pipe8(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     OT *__restrict__ o, float *__restrict__ lse, int Nq, int Nk, int BH, int nqt,
     float c, int negate) {
   const WorkItem wi = work_item(BH, nqt, CAUSAL);
   const int kend = CAUSAL ? min(Nk, wi.q0 + kBM) : Nk;
   const PipeItem it = {wi.bh, wi.q0, 0, (kend + kBN - 1) / kBN, -1};
-  pipe_run<T, OT, D, CAUSAL>(q, k, v, o, lse, nullptr, Nq, Nk, c, negate, it, 0);
+  pipe8_run<T, OT, D, CAUSAL>(q, k, v, o, lse, nullptr, Nq, Nk, c, negate, it, 0);
 }
 
-// Key-range split of long query tiles (balances causal work over the CUs).
-// Query tile t (128 rows) needs w_t key tiles; it is cut into
-// p_t = ceil(w_t / W) parts of s_t = ceil(w_t / p_t) tiles, counted from the
-// top so that the last part holds the diagonal; part i covers tiles
-// [max(0, w_t - (p_t - i) s_t), w_t - (p_t - i - 1) s_t).  Tiles t >= t_split
-// are the split ones (w_t never decreases with t).  The table lists the
-// (t, part) pairs in decreasing part size; workgroup g takes pair g / BH of
-// head g % BH.
-constexpr int kMaxPairs = 1024;
-constexpr int kMaxParts = 8;
-struct SplitPlan {
-  int W;        // largest part, in key tiles
-  int t_split;  // first split query tile
-  int p_max;    // most parts of any tile
-  int npairs;
-  uint16_t pair[kMaxPairs];  // t | part << 11
+// ---------------------------------------------------------------------------
+// Stream-K schedule (persistent workgroups).  The work of a call is laid out
+// as one sequence of units, a unit being one 64-key tile of one 128-row query
+// tile: head by head, and within a head the query tiles in zigzag order
+// 0, nqt-1, 1, nqt-2, ... (under the causal mask tile t needs
+// min(2t+2, nkt) key tiles, so neighbours in this order pair short and long
+// tiles).  Chunk c of G holds units [b(c), b(c+1)) with b(c) = floor(c*T/G);
+// each workgroup runs one chunk, so every CU gets the same number of units.
+// A chunk is a list of pieces (a query tile's key range, or part of it); a
+// piece that covers its whole tile writes O and L, any other writes a
+// partial result to workspace slot 2c (the chunk's first piece) or 2c + 1
+// (its last), and fa_merge_stream combines the pieces of each cut tile.
+struct StreamPlan {
+  long long T;         // units in the call
+  long long per_head;  // units per head
+  long long cq;        // T / G
+  int cr;              // T % G
+  int G;               // chunks = workgroups, 1 <= G <= min(T, 65535)
+  int nqt, nkt;        // query tiles (128 rows), key tiles (64 keys)
 };
 
-__host__ __device__ inline int tile_keys(int t, int Nk, bool causal) {
-  const int kend = causal ? (Nk < (t + 1) * kBM ? Nk : (t + 1) * kBM) : Nk;
-  return (kend + kBN - 1) / kBN;
+// Key tiles of query tile t.
+__host__ __device__ inline int tile_w(int t, int nkt, bool causal) {
+  return causal ? (2 * t + 2 < nkt ? 2 * t + 2 : nkt) : nkt;
+}
+
+// Units of query tiles 0..t-1.
+__host__ __device__ inline long long prefix_nat(int t, int nkt, bool causal) {
+  if (!causal) return (long long)t * nkt;
+  const int a = nkt / 2;  // tiles i < a have 2i+2 <= nkt keys tiles
+  if (t <= a) return (long long)t * (t + 1);
+  return (long long)a * (a + 1) + (long long)(t - a) * nkt;
+}
+
+// Query tile at zigzag position o, and units of positions 0..o-1.
+__host__ __device__ inline int zz_tile(int o, int nqt) {
+  return (o & 1) ? nqt - 1 - (o >> 1) : (o >> 1);
+}
+__host__ __device__ inline long long zz_prefix(int o, int nqt, int nkt, bool causal) {
+  return prefix_nat((o + 1) >> 1, nkt, causal) +
+         (prefix_nat(nqt, nkt, causal) - prefix_nat(nqt - (o >> 1), nkt, causal));
+}
+
+// Zigzag position of the tile holding head-relative unit r (0 <= r < per_head).
+__host__ __device__ inline int zz_find(long long r, int nqt, int nkt, bool causal) {
+  int lo = 0, hi = nqt - 1;  // zz_prefix(lo) <= r always holds
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (zz_prefix(mid, nqt, nkt, causal) <= r)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+// floor(c * T / G), without 64-bit division (c * cr < G^2 < 2^32).
+__host__ __device__ inline long long chunk_start(const StreamPlan &sp, int c) {
+  return (long long)c * sp.cq + (long long)((uint32_t)c * (uint32_t)sp.cr / (uint32_t)sp.G);
+}
+
+// Chunk run by workgroup g: consecutive chunks go to one XCD (workgroups are
+// dealt to the 8 XCDs round robin), so an XCD's workgroups share heads and
+// their K/V in its L2.
+__device__ __forceinline__ int chunk_of(int g, int G) {
+  return (G % 8 == 0) ? (g % 8) * (G / 8) + g / 8 : g;
 }
 
 template <typename T, typename OT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void fa_fwd_pipe_split(
+__global__ __launch_bounds__(kThreads8) void fa_fwd_stream(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     OT *__restrict__ o, float *__restrict__ lse, float *__restrict__ ws, int Nq, int Nk,
-    int BH, int nqt, float c, int negate, SplitPlan plan) {
-  const int g = blockIdx.x;
-  const int pr = plan.pair[g / BH];
-  const int t = pr & 0x7ff, part = pr >> 11;
-  const int w = tile_keys(t, Nk, CAUSAL);
-  const int p = (w + plan.W - 1) / plan.W;
-  const int st = (w + p - 1) / p;
-  PipeItem it;
-  it.bh = g % BH;
-  it.q0 = t * kBM;
-  it.kt0 = max(0, w - (p - part) * st);
-  it.kt1 = w - (p - part - 1) * st;
-  it.slot = p > 1 ? ((t - plan.t_split) * plan.p_max + part) * BH + it.bh : -1;
-  const int nslots = (nqt - plan.t_split) * plan.p_max * BH;
-  pipe_run<T, OT, D, CAUSAL>(q, k, v, o, lse, ws, Nq, Nk, c, negate, it, nslots);
+    float c, int negate, StreamPlan sp) {
+  const int ch = chunk_of(blockIdx.x, sp.G);
+  const long long u0 = chunk_start(sp, ch);
+  long long left = chunk_start(sp, ch + 1) - u0;
+  // position of the chunk's first unit: head, zigzag tile position, key tile
+  int bh = (int)(u0 / sp.per_head);
+  const long long r0 = u0 - (long long)bh * sp.per_head;
+  int zo = zz_find(r0, sp.nqt, sp.nkt, CAUSAL);
+  int kt0 = (int)(r0 - zz_prefix(zo, sp.nqt, sp.nkt, CAUSAL));
+  bool first = true;
+  while (left > 0) {
+    const int t = zz_tile(zo, sp.nqt);
+    const int w = tile_w(t, sp.nkt, CAUSAL);
+    const int kt1 = left < (long long)(w - kt0) ? kt0 + (int)left : w;
+    PipeItem it;
+    it.bh = bh;
+    it.q0 = t * kBM;
+    it.kt0 = kt0;
+    it.kt1 = kt1;
+    it.slot = (kt0 == 0 && kt1 == w) ? -1 : 2 * ch + (first ? 0 : 1);
+    pipe8_run<T, OT, D, CAUSAL>(q, k, v, o, lse, ws, Nq, Nk, c, negate, it, 2 * sp.G);
+    left -= kt1 - kt0;
+    first = false;
+    kt0 = 0;  // the next piece starts a tile
+    if (++zo == sp.nqt) {
+      zo = 0;
+      ++bh;
+    }
+  }
 }
 
-// Combines the parts of each split query tile: with a_i = 2^(m_i - M),
-// M = max_i m_i, O = sum_i a_i lr_i O_i / sum_i a_i lr_i and
-// L = ln2 * (M + log2 sum_i a_i l_i).  Each thread owns one 4-wide slice of
-// one row and issues the loads of every part at once (the combine is one
-// memory round trip); a workgroup covers kThreads / (D/4) rows, so the grid
-// is (split tiles x heads x row groups).
-template <typename OT, int D>
-__global__ __launch_bounds__(kThreads) void fa_merge_parts(
-    const float *__restrict__ ws, OT *__restrict__ o, float *__restrict__ lse, int Nq,
-    int Nk, int BH, int nqt, int causal, int W, int t_split, int p_max) {
+// Cut query tiles of a stream-K schedule, named by the first chunk boundary
+// j that falls strictly inside each (host-computed).
+constexpr int kMaxChunks = 1024;
+struct CutList {
+  int n;
+  uint16_t j[kMaxChunks - 1];
+};
+
+// Combines the pieces of the cut query tiles, kMergeSplit workgroups per
+// tile, with a_i = 2^(m_i - M), M = max_i m_i:
+// O = sum_i a_i lr_i O_i / sum_i a_i lr_i, L = ln2 * (M + log2 sum_i a_i l_i).
+// The tile's pieces: chunk j-1 (its first piece when it starts at the tile,
+// else its last), then every chunk c >= j that starts inside the tile (its
+// first piece).  Each thread owns one 4-wide column slice of NR rows and
+// loads two pieces per round trip.
+constexpr int kMergeSplit = 8;
+
+template <typename OT, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void fa_merge_stream(const float *__restrict__ ws,
+                                                            OT *__restrict__ o,
+                                                            float *__restrict__ lse, int Nq,
+                                                            StreamPlan sp, CutList cuts) {
   constexpr int C4 = D / 4;           // float4 per row
-  constexpr int RPB = kThreads / C4;  // rows per workgroup
-  constexpr int GROUPS = kBM / RPB;
-  const int grp = blockIdx.x % GROUPS;
-  const int tb = blockIdx.x / GROUPS;
-  const int bh = tb % BH;
-  const int t = t_split + tb / BH;
-  const int r = grp * RPB + threadIdx.x / C4;
+  constexpr int RPP = kThreads / C4;  // rows per pass of the workgroup
+  constexpr int ROWS = kBM / kMergeSplit;
+  constexpr int NR = ROWS / RPP;      // rows per thread
+  static_assert(NR >= 1 && ROWS % RPP == 0, "merge tiling");
+  const int j = cuts.j[blockIdx.x / kMergeSplit];
+  const int rbase = (blockIdx.x % kMergeSplit) * ROWS;
+  const long long bj = chunk_start(sp, j);
+  const int bh = (int)(bj / sp.per_head);
+  const long long base = (long long)bh * sp.per_head;
+  const int zo = zz_find(bj - base, sp.nqt, sp.nkt, CAUSAL);
+  const long long s0 = base + zz_prefix(zo, sp.nqt, sp.nkt, CAUSAL);  // tile's first unit
+  const long long bprev = chunk_start(sp, j - 1);
+  const int t = zz_tile(zo, sp.nqt);
+  const long long s1 = s0 + tile_w(t, sp.nkt, CAUSAL);
   const int c4 = threadIdx.x % C4;
-  const int row = t * kBM + r;
-  if (row >= Nq) return;
-  const int w = tile_keys(t, Nk, causal != 0);
-  const int p = (w + W - 1) / W;
-  const int nslots = (nqt - t_split) * p_max * BH;
+  const int r0 = rbase + threadIdx.x / C4;
+  const int nslots = 2 * sp.G;
   const float *ws_s = ws + (size_t)nslots * kBM * D;
-  const int slot0 = (t - t_split) * p_max * BH + bh;
-  f32x4 st[kMaxParts], x[kMaxParts];
+  float M[NR], ls[NR], lrs[NR];
+  f32x4 acc[NR];
 #pragma unroll
-  for (int i = 0; i < kMaxParts; ++i) {
-    if (i < p) {
-      const size_t e = (size_t)(slot0 + i * BH) * kBM + r;
-      st[i] = *reinterpret_cast<const f32x4 *>(ws_s + e * 4);
-      x[i] = *reinterpret_cast<const f32x4 *>(ws + e * D + 4 * c4);
+  for (int i = 0; i < NR; ++i) {
+    M[i] = -INFINITY;
+    ls[i] = lrs[i] = 0.f;
+    acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  auto piece_slot = [&](int cc) {  // -1 past the tile's last piece
+    if (cc >= sp.G || (cc >= j && chunk_start(sp, cc) >= s1)) return -1;
+    return (cc == j - 1 && bprev != s0) ? 2 * cc + 1 : 2 * cc;
+  };
+  for (int cc = j - 1;; cc += 2) {
+    const int sl[2] = {piece_slot(cc), piece_slot(cc + 1)};
+    if (sl[0] < 0) break;
+    f32x4 st[2][NR], x[2][NR];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        if (sl[u] < 0) continue;
+        const size_t e = (size_t)sl[u] * kBM + r0 + i * RPP;
+        st[u][i] = *reinterpret_cast<const f32x4 *>(ws_s + e * 4);
+        x[u][i] = *reinterpret_cast<const f32x4 *>(ws + e * D + 4 * c4);
+      }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        if (sl[u] < 0 || st[u][i][0] == -INFINITY) continue;  // no key of this row
+        const float Mn = fmaxf(M[i], st[u][i][0]);
+        const float a_old = exp2f(M[i] - Mn);  // 0 while M = -inf
+        const float a = exp2f(st[u][i][0] - Mn);
+        ls[i] = ls[i] * a_old + a * st[u][i][1];
+        lrs[i] = lrs[i] * a_old + a * st[u][i][2];
+        acc[i] = acc[i] * a_old + (a * st[u][i][2]) * x[u][i];
+        M[i] = Mn;
+      }
+    if (sl[1] < 0) break;
+  }
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int row = t * kBM + r0 + i * RPP;
+    if (row < Nq) {
+      store4<OT>(o + ((size_t)bh * Nq + row) * D + 4 * c4, acc[i] * (1.0f / lrs[i]));
+      if (c4 == 0) lse[(size_t)bh * Nq + row] = (M[i] + log2f(ls[i])) * 0.69314718055994531f;
     }
   }
-  float M = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < kMaxParts; ++i)
-    if (i < p) M = fmaxf(M, st[i][0]);
-  float ls = 0.f, lrs = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < kMaxParts; ++i) {
-    if (i < p) {
-      const float a = exp2f(st[i][0] - M);  // 0 for a part the row did not see
-      ls += a * st[i][1];
-      lrs += a * st[i][2];
-      acc += (a * st[i][2]) * x[i];
-    }
-  }
-  OT *orow = o + ((size_t)bh * Nq + row) * D;
-  store4<OT>(orow + 4 * c4, acc * (1.0f / lrs));
-  if (c4 == 0) lse[(size_t)bh * Nq + row] = (M + log2f(ls)) * 0.69314718055994531f;
 }
 
 // ---------------------------------------------------------------------------
@@ -1146,7 +1344,8 @@ struct Launch {
   int Nq, Nk, BH, nqt;
   float c;
   hipStream_t stream;
-  const SplitPlan *plan;  // non-null: key-range split (pipelined kernel only)
+  const StreamPlan *plan;  // non-null: stream-K schedule (pipelined kernel only)
+  const CutList *cuts;     // the schedule's cut tiles
 };
 
 template <typename T, typename OT, int D, bool CAUSAL>
@@ -1156,21 +1355,21 @@ hipError_t launch16(const Launch &a) {
     const float c = a.c < 0.f ? -a.c : a.c;
     const int neg = a.c < 0.f ? 1 : 0;
     if (a.plan) {
-      const SplitPlan &pl = *a.plan;
-      hipLaunchKernelGGL((fa_fwd_pipe_split<T, OT, D, CAUSAL>),
-                         dim3((unsigned)(pl.npairs * a.BH)), dim3(kThreads), 0, a.stream,
-                         (const T *)a.q, (const T *)a.k, (const T *)a.v, (OT *)a.o, a.lse,
-                         a.ws, a.Nq, a.Nk, a.BH, a.nqt, c, neg, pl);
+      const StreamPlan &sp = *a.plan;
+      hipLaunchKernelGGL((fa_fwd_stream<T, OT, D, CAUSAL>), dim3((unsigned)sp.G),
+                         dim3(kThreads8), 0, a.stream, (const T *)a.q, (const T *)a.k,
+                         (const T *)a.v, (OT *)a.o, a.lse, a.ws, a.Nq, a.Nk, c, neg, sp);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      constexpr int groups = kBM / (kThreads / (D / 4));
-      hipLaunchKernelGGL((fa_merge_parts<OT, D>),
-                         dim3((unsigned)((a.nqt - pl.t_split) * a.BH * groups)), dim3(kThreads), 0,
-                         a.stream, (const float *)a.ws, (OT *)a.o, a.lse, a.Nq, a.Nk, a.BH,
-                         a.nqt, CAUSAL ? 1 : 0, pl.W, pl.t_split, pl.p_max);
+      if (a.cuts && a.cuts->n > 0) {
+        hipLaunchKernelGGL((fa_merge_stream<OT, D, CAUSAL>),
+                           dim3((unsigned)(a.cuts->n * kMergeSplit)),
+                           dim3(kThreads), 0, a.stream, (const float *)a.ws, (OT *)a.o,
+                           a.lse, a.Nq, sp, *a.cuts);
+      }
     } else {
-      hipLaunchKernelGGL((fa_fwd_pipe<T, OT, D, CAUSAL>), dim3((unsigned)(a.BH * a.nqt)),
-                         dim3(kThreads), 0, a.stream, (const T *)a.q, (const T *)a.k,
+      hipLaunchKernelGGL((fa_fwd_pipe8<T, OT, D, CAUSAL>), dim3((unsigned)(a.BH * a.nqt)),
+                         dim3(kThreads8), 0, a.stream, (const T *)a.q, (const T *)a.k,
                          (const T *)a.v, (OT *)a.o, a.lse, a.Nq, a.Nk, a.BH, a.nqt, c, neg);
     }
   } else {
@@ -1276,69 +1475,49 @@ int device_cus(int *cus) {
   return FA_OK;
 }
 
-constexpr int kMinPartTiles = 4;  // no part shorter than 256 keys
-
-// Decides whether (and how) the pipelined kernel splits the key ranges of
-// long query tiles: parts of about the mean per-CU work, so that the
-// longest-first order keeps every CU busy until the end.  Returns false when
-// every tile runs whole (no workspace needed).
+// Stream-K schedule of the pipelined kernel (16-bit inputs, D >= 64): one
+// chunk per compute unit.  With four or more query tiles per compute unit
+// the longest-first grid of fa_fwd already keeps every unit busy to the
+// end, and a chunk would hold many pieces, each paying its own prologue: the
+// call then takes that grid.  Returns false for the paths that take no
+// workspace.
 bool make_plan(int64_t BH, int64_t nqt, int64_t Nk, int64_t D, int dtype, bool causal,
-               int cus, SplitPlan &pl, size_t &ws_bytes) {
+               int cus, StreamPlan &sp, size_t &ws_bytes) {
   ws_bytes = 0;
-  if (dtype == FA_F32 || D < 64 || cus < 1 || nqt > 2047) return false;
-  int64_t total = 0, wmax = 0;
-  for (int t = 0; t < nqt; ++t) {
-    const int64_t w = tile_keys(t, (int)Nk, causal);
-    total += w;
-    wmax = w > wmax ? w : wmax;
-  }
-  total *= BH;
-  int64_t W = (total + cus - 1) / cus;
-  W = W < kMinPartTiles ? kMinPartTiles : W;
-  W = W < (wmax + kMaxParts - 1) / kMaxParts ? (wmax + kMaxParts - 1) / kMaxParts : W;
-  for (;; W *= 2) {
-    if (wmax <= W) return false;
-    int npairs = 0, pmax = 1, ts = -1;
-    for (int t = 0; t < nqt; ++t) {
-      const int64_t w = tile_keys(t, (int)Nk, causal);
-      const int p = (int)((w + W - 1) / W);
-      npairs += p;
-      pmax = p > pmax ? p : pmax;
-      if (p > 1 && ts < 0) ts = t;
-    }
-    if (npairs > kMaxPairs) continue;
-    pl.W = (int)W;
-    pl.t_split = ts;
-    pl.p_max = pmax;
-    pl.npairs = 0;
-    int size[kMaxPairs];
-    for (int t = (int)nqt - 1; t >= 0; --t) {
-      const int w = tile_keys(t, (int)Nk, causal);
-      const int p = (w + (int)W - 1) / (int)W;
-      const int st = (w + p - 1) / p;
-      for (int part = 0; part < p; ++part) {
-        const int kt0 = w - (p - part) * st > 0 ? w - (p - part) * st : 0;
-        const int kt1 = w - (p - part - 1) * st;
-        // insertion keeps the list in decreasing part size (stable)
-        int i = pl.npairs++;
-        while (i > 0 && size[i - 1] < kt1 - kt0) {
-          size[i] = size[i - 1];
-          pl.pair[i] = pl.pair[i - 1];
-          --i;
-        }
-        size[i] = kt1 - kt0;
-        pl.pair[i] = (uint16_t)(t | (part << 11));
-      }
-    }
-    const size_t nslots = (size_t)(nqt - ts) * pmax * BH;
-    ws_bytes = nslots * kBM * (size_t)(D + 4) * 4;
-    return true;
+  if (dtype == FA_F32 || D < 64 || cus < 1) return false;
+  if (BH * nqt >= 4 * (int64_t)cus) return false;
+  const int nkt = (int)((Nk + kBN - 1) / kBN);
+  sp.nqt = (int)nqt;
+  sp.nkt = nkt;
+  sp.per_head = prefix_nat((int)nqt, nkt, causal);
+  sp.T = BH * sp.per_head;
+  const int gmax = cus < kMaxChunks ? cus : kMaxChunks;
+  sp.G = (int)(sp.T < gmax ? sp.T : gmax);
+  sp.cq = sp.T / sp.G;
+  sp.cr = (int)(sp.T % sp.G);
+  ws_bytes = (size_t)2 * sp.G * kBM * (size_t)(D + 4) * 4;
+  return true;
+}
+
+// The cut tiles of a schedule: boundary j (1 <= j < G) names the tile that
+// holds unit b(j) when b(j) is not that tile's first unit and no earlier
+// boundary lies inside it.
+void make_cuts(const StreamPlan &sp, bool causal, CutList &cl) {
+  cl.n = 0;
+  for (int j = 1; j < sp.G; ++j) {
+    const long long bj = chunk_start(sp, j);
+    const long long bh = bj / sp.per_head;
+    const long long base = bh * sp.per_head;
+    const int zo = zz_find(bj - base, sp.nqt, sp.nkt, causal);
+    const long long s0 = base + zz_prefix(zo, sp.nqt, sp.nkt, causal);
+    if (s0 == bj || chunk_start(sp, j - 1) > s0) continue;
+    cl.j[cl.n++] = (uint16_t)j;
   }
 }
 
 int run(const void *q, const void *k, const void *v, void *o, float *lse, int64_t Nq,
         int64_t Nk, int64_t D, float scale, int causal, int dtype, const Shape &sh,
-        const SplitPlan *plan, void *ws, void *stream) {
+        const StreamPlan *plan, void *ws, void *stream) {
   Launch a;
   a.q = q;
   a.k = k;
@@ -1353,6 +1532,12 @@ int run(const void *q, const void *k, const void *v, void *o, float *lse, int64_
   a.c = scale * 1.4426950408889634f;
   a.stream = (hipStream_t)stream;
   a.plan = plan;
+  CutList cuts;
+  a.cuts = nullptr;
+  if (plan) {
+    make_cuts(*plan, causal != 0, cuts);
+    a.cuts = &cuts;
+  }
   hipError_t e;
   const bool cz = causal != 0;
   switch (dtype) {
@@ -1411,7 +1596,7 @@ int fa_fwd_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t 
   int cus = 0;
   const int st = device_cus(&cus);
   if (st != FA_OK) return st;
-  SplitPlan pl;
+  StreamPlan pl;
   size_t ws = 0;
   make_plan(B * H, (Nq + kBM - 1) / kBM, Nk, D, dtype, causal != 0, cus, pl, ws);
   *bytes = ws;
@@ -1436,7 +1621,7 @@ int fa_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse, 
   int cus = 0;
   st = device_cus(&cus);
   if (st != FA_OK) return st;
-  SplitPlan pl;
+  StreamPlan pl;
   size_t need = 0;
   if (!make_plan(sh.BH, sh.nqt, Nk, D, dtype, causal != 0, cus, pl, need))
     return run(q, k, v, o, lse, Nq, Nk, D, scale, causal, dtype, sh, nullptr, nullptr,
