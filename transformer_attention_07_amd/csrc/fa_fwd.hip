@@ -569,43 +569,55 @@ struct Pipe {
   // block (with pin); after each MFMA the wave issues the LDS reads two
   // MFMA pairs ahead and one slice of the softmax of this block (on sin,
   // into pout), so the VALU work runs while the MFMA pipe is busy.  Slices:
-  //   0-1   row maximum of the block
+  //   0-1   row maximum of the block (a tree of 3-input maxima)
   //   2     half-wave exchange, lazy move of the exponent reference, alpha
-  //   3-10  p = 2^(c*s - m) for two elements, their fp32 sum, their rounding
-  //         to T (one packed word of the P.V operand) and its sum
-  //   11    l, lr
+  //   3-13  p = 2^(c*s - m) for two elements per slice, pipelined over four
+  //         stages (exponent, 2^x, fp32 sum and rounding to T into one packed
+  //         word of the P.V operand, sum of the rounded pair)
+  //   14    l, lr
   // The reference moves per lane, only when the block's maximum exceeds it
   // by more than kLazy (both half-waves of a query take the same decision);
   // acc is then scaled by alpha after the block (a rare, wave-uniform
   // branch).  O is normalised by lr, the sum of p exactly as rounded for
-  // P.V, so the weights applied to V sum to one; L uses l.  MASKED: s may
-  // hold -inf, and the exponent is clamped so a hidden key gives p = 0 even
-  // when c == 0 (where -inf * c is NaN).
-  template <bool MASKED>
+  // P.V, so the weights applied to V sum to one; L uses l.  Hidden keys hold
+  // s = -inf and give p = 2^-inf = 0: c > 0 always (the host never passes
+  // 0), and a row that has not seen a key yet shifts by 0 instead of
+  // -(-inf).  One code path serves masked and unmasked blocks, so the
+  // accumulators stay in the same registers from block to block.
   __device__ __forceinline__ void block_step(const lds_char *kp, const lds_char *vp,
                                              f32x16 &sin, f32x16 &sout,
                                              const frag (&pin)[2], frag (&pout)[2]) {
-    constexpr int NCHUNK = 12;
+    constexpr int NCHUNK = 15;
     frag kf[QF], vf[NPV];
-    float mx = 0.f, nm = 0.f, alpha = 1.f, psum = 0.f, rsum = 0.f;
+    float mx = 0.f, nm = 0.f, alpha = 1.f;
+    float m3[5];               // partial maxima
+    float ea[2], pb[2];        // pair in flight: exponents, then p
+    uint32_t wq = 0;           // packed pair waiting for its rounded sum
+    float psa = 0.f, psb = 0.f, rsa = 0.f, rsb = 0.f;  // two partial sums each
     bool need = false;
     u32x4 pw[2];  // p rounded to T, packed in pairs (the two P.V operands)
     sout = f32x16{};
 
+    // Softmax slices.  The wave issues in order, so a slice holds only
+    // instructions that do not wait on each other: the row maximum is a
+    // tree, and the sixteen elements go through four stages (exponent,
+    // 2^x, fp32 sums and rounding, rounded sum) one pair per slice, each
+    // stage one slice behind the previous.
     auto chunk = [&](int ch) {
       // Each slice ends with an empty asm that uses its results: the values
       // must exist at that point, so the compiler cannot sink the slice out
       // of its MFMA slot (e.g. past the rescale branch, towards its use).
       if (ch == 0) {
-        mx = fmaxf(sin[0], sin[1]);
 #pragma unroll
-        for (int r = 2; r < 8; ++r) mx = fmaxf(mx, sin[r]);
-        asm volatile("" ::"v"(mx));
+        for (int i = 0; i < 5; ++i)
+          m3[i] = fmaxf(fmaxf(sin[3 * i], sin[3 * i + 1]), sin[3 * i + 2]);
+        asm volatile("" ::"v"(m3[0]), "v"(m3[1]), "v"(m3[2]), "v"(m3[3]), "v"(m3[4]));
       } else if (ch == 1) {
-#pragma unroll
-        for (int r = 8; r < 16; ++r) mx = fmaxf(mx, sin[r]);
-        asm volatile("" ::"v"(mx));
+        m3[0] = fmaxf(fmaxf(m3[0], m3[1]), m3[2]);
+        m3[3] = fmaxf(fmaxf(m3[3], m3[4]), sin[15]);
+        asm volatile("" ::"v"(m3[0]), "v"(m3[3]));
       } else if (ch == 2) {
+        mx = fmaxf(m3[0], m3[3]);
         const u32x2 sw = __builtin_amdgcn_permlane32_swap(
             __builtin_bit_cast(uint32_t, mx), __builtin_bit_cast(uint32_t, mx), false, false);
         mx = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
@@ -616,26 +628,36 @@ struct Pipe {
         // a fully masked first block must not turn l into NaN)
         alpha = need ? __builtin_amdgcn_exp2f(m_use - m_new) : 1.f;
         m_use = m_new;
-        nm = -m_new;
+        nm = m_new == -INFINITY ? 0.f : -m_new;
         asm volatile("" ::"v"(alpha), "v"(nm));
-      } else if (ch <= 10) {
-        const int w = ch - 3;  // packed word: elements 2w, 2w+1
-        float e0 = __builtin_fmaf(sin[2 * w], c, nm);
-        float e1 = __builtin_fmaf(sin[2 * w + 1], c, nm);
-        if (MASKED) {  // NaN or -inf -> 2^-3e38 = 0
-          e0 = fmaxf(e0, -3.0e38f);
-          e1 = fmaxf(e1, -3.0e38f);
+      } else if (ch <= 13) {
+        const int k = ch - 3;  // stage A on pair k, B on k-1, C on k-2, D on k-3
+        if (k >= 3 && k - 3 < 8) {  // D: sum of the rounded pair
+          if ((k - 3) & 1)
+            rsb = Mfma16<T>::pair_sum(wq, rsb);
+          else
+            rsa = Mfma16<T>::pair_sum(wq, rsa);
         }
-        const float p0 = __builtin_amdgcn_exp2f(e0);
-        const float p1 = __builtin_amdgcn_exp2f(e1);
-        psum += p0 + p1;
-        const uint32_t word = Mfma16<T>::pack2(p0, p1);
-        pw[w / 4][w % 4] = word;
-        rsum = Mfma16<T>::pair_sum(word, rsum);
-        asm volatile("" ::"v"(word), "v"(psum), "v"(rsum));
+        if (k >= 2 && k - 2 < 8) {  // C: fp32 sums, rounding to T
+          const int w = k - 2;
+          psa += pb[0];
+          psb += pb[1];
+          wq = Mfma16<T>::pack2(pb[0], pb[1]);
+          pw[w / 4][w % 4] = wq;
+        }
+        if (k >= 1 && k - 1 < 8) {  // B: p = 2^x
+          pb[0] = __builtin_amdgcn_exp2f(ea[0]);
+          pb[1] = __builtin_amdgcn_exp2f(ea[1]);
+        }
+        if (k < 8) {  // A: exponents of elements 2k, 2k+1
+          ea[0] = __builtin_fmaf(sin[2 * k], c, nm);
+          ea[1] = __builtin_fmaf(sin[2 * k + 1], c, nm);
+        }
+        asm volatile("" ::"v"(ea[0]), "v"(ea[1]), "v"(pb[0]), "v"(pb[1]), "v"(wq), "v"(psa),
+                     "v"(psb), "v"(rsa), "v"(rsb));
       } else {
-        l = l * alpha + psum;
-        lr = lr * alpha + rsum;
+        l = l * alpha + (psa + psb);
+        lr = lr * alpha + (rsa + rsb);
         pout[0] = __builtin_bit_cast(frag, pw[0]);
         pout[1] = __builtin_bit_cast(frag, pw[1]);
         asm volatile("" ::"v"(l), "v"(lr));
@@ -689,12 +711,8 @@ struct Pipe {
     if (b <= lastb) {
       const int k0 = b * 32;
       const bool need_mask = (k0 + 32 > Nk) || (CAUSAL && k0 + 31 > qw);
-      if (need_mask) {
-        mask(sin, k0);
-        block_step<true>(kp, vp, sin, sout, pin, pout);
-      } else {
-        block_step<false>(kp, vp, sin, sout, pin, pout);
-      }
+      if (need_mask) mask(sin, k0);
+      block_step(kp, vp, sin, sout, pin, pout);
     } else if (STRIDE > 0 && b - STRIDE <= lastb) {
       pv(vp, pin);
     }
@@ -858,7 +876,8 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
   const int ntiles = it.kt1 - it.kt0;
   const int lastb = CAUSAL ? min(2 * it.kt1 - 1, s.qw / 32) : 2 * it.kt1 - 1;
 
-  // Q first (see pipe_run): the prologue wait covers it.
+  // Q first: its loads are the oldest in flight, so the prologue wait for
+  // the first K/V unit covers them too.
   u32x4 qraw[P::QF];
 #pragma unroll
   for (int f = 0; f < P::QF; ++f)
@@ -1351,8 +1370,10 @@ struct Launch {
 template <typename T, typename OT, int D, bool CAUSAL>
 hipError_t launch16(const Launch &a) {
   if constexpr (D >= 64) {
-    // c >= 0 here; a negative scale flips the sign of Q inside the kernel.
-    const float c = a.c < 0.f ? -a.c : a.c;
+    // c > 0 here: a negative scale flips the sign of Q inside the kernel,
+    // and scale 0 runs as the smallest normal scale (scores of at most
+    // 2^-126 * |q.k|, which round to 0 against any shift the softmax uses).
+    const float c = fmaxf(a.c < 0.f ? -a.c : a.c, 1.17549435e-38f);
     const int neg = a.c < 0.f ? 1 : 0;
     if (a.plan) {
       const StreamPlan &sp = *a.plan;
