@@ -664,9 +664,10 @@ struct Pipe {
       }
     };
 
-    // fragments for the first two MFMA pairs
+    // fragments are read PF MFMA pairs ahead
+    constexpr int PF = QF < 3 ? QF : 3;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < PF; ++i) {
       kf[i] = kfrag(kp, i);
       vf[i] = vfrag(vp, i);
     }
@@ -674,14 +675,14 @@ struct Pipe {
     for (int i = 0; i < QF; ++i) {
       // K.Q^T, then a slice of the softmax
       sout = Mfma16<T>::mma(kf[i], qf[i], sout);
-      if (i + 2 < QF) kf[i + 2] = kfrag(kp, i + 2);
+      if (i + PF < QF) kf[i + PF] = kfrag(kp, i + PF);
 #pragma unroll
       for (int ch = (2 * i) * NCHUNK / NSLOT; ch < (2 * i + 1) * NCHUNK / NSLOT; ++ch)
         chunk(ch);
       __builtin_amdgcn_sched_barrier(0);
       // P.V, then a slice of the softmax
       acc[i % NDB] = Mfma16<T>::mma(vf[i], pin[i / NDB], acc[i % NDB]);
-      if (i + 2 < NPV) vf[i + 2] = vfrag(vp, i + 2);
+      if (i + PF < NPV) vf[i + PF] = vfrag(vp, i + PF);
 #pragma unroll
       for (int ch = (2 * i + 1) * NCHUNK / NSLOT; ch < (2 * i + 2) * NCHUNK / NSLOT; ++ch)
         chunk(ch);
