@@ -42,8 +42,8 @@ def source_digest() -> str:
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; otherwise None."""
+    """HBM bytes per step (every kernel of one call) from committed rocprofv3
+    counter runs, if they were taken on the current kernel source; else None."""
     path = os.path.join(TRAFFIC_DIR, f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -51,7 +51,7 @@ def measured_traffic(workload: str):
         t = json.load(f)
     if t.get("source_sha256") != source_digest():
         return None
-    return t.get("bytes_per_launch")
+    return t.get("bytes_per_step")
 
 
 def cpu_baseline(w, target_s: float):
