@@ -91,7 +91,7 @@ enum fa_status {
  * (nothing enqueued), or FA_ERR_HIP with the runtime's message available
  * from fa_last_hip_error().  o and lse must not overlap q, k, v or each
  * other (checked on the host: FA_ERR_OVERLAP).  Each (batch, head) slice is
- * addressed with 32-bit byte offsets, so (Nq + 128) * D * 4 and
+ * addressed with 32-bit byte offsets, so (Nq + 256) * D * 4 and
  * (Nk + 64) * D * 4 must stay below 2^31 (FA_ERR_SHAPE otherwise), as must
  * B*H*ceil(Nq/128).
  */
@@ -118,7 +118,9 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
  * "FlashAttention-2实现与优化：高效注意力机制详解" §3.1, the incremental
  * update of (m, l, o_acc)).  Cutting the work along the sequence is the
  * sequence parallelism of page "FlashAttention技术演进全景图" §3.2.  The size
- * is 2 * G * 128 * (D + 4) * 4 bytes, G = min(compute units, units of work).
+ * is 2 * G * R * (D + 4) * 4 bytes, G = min(compute units, units of work),
+ * R the rows of a query tile in this schedule (128 for D = 128, 256 for
+ * D = 64).
  *
  * Returns FA_OK, FA_ERR_NULLPTR (bytes NULL), FA_ERR_SHAPE, FA_ERR_HEAD_DIM,
  * FA_ERR_DTYPE or FA_ERR_HIP (device query failed).

@@ -133,12 +133,12 @@ struct WorkItem {
   int q0;  // first query row of the workgroup
 };
 
-__device__ __forceinline__ WorkItem work_item(int BH, int nqt, bool causal) {
+__device__ __forceinline__ WorkItem work_item(int BH, int nqt, bool causal, int rows = kBM) {
   const int id = blockIdx.x;
   const int bh = id % BH;
   const int t = id / BH;
   const int qt = causal ? (nqt - 1 - t) : t;
-  return {bh, qt * kBM};
+  return {bh, qt * rows};
 }
 
 // Applies the scale (base-2 folded) and the masks to one S^T tile, in place.
@@ -757,17 +757,25 @@ __device__ __forceinline__ void epilogue_partial(const f32x16 (&acc)[D / 32], fl
 }
 
 // ---------------------------------------------------------------------------
-// Eight waves per workgroup, two per SIMD.  Waves w and w + 4 hold the same
-// 32 query rows (group w % 4, on the same SIMD) and split the key blocks by
-// parity: wave w takes the even 32-key blocks, wave w + 4 the odd ones, so
-// in every ring step each wave runs one block (soft-max of its block, K.Q^T
-// of its next block, P.V of its previous block) while its partner's
-// instruction stream fills the SIMD's idle issue slots.  At the end the
-// pair's running statistics and accumulators are combined through LDS with
-// the online-softmax rescaling (2^(m_i - M)), and the even wave writes O and
-// L (or the split part's partial result).
+// Eight waves per workgroup, two per SIMD, in one of two layouts:
+//
+// * PAIR = false (256 query rows, 32 per wave): every wave runs both 32-key
+//   blocks of each 64-key ring step, so the per-step costs (the barrier, the
+//   DMA issue, the loop) are shared by two blocks, and the two waves of a
+//   SIMD fill each other's idle issue slots.
+// * PAIR = true (128 query rows): waves w and w + 4 hold the same 32 rows
+//   (group w % 4, on the same SIMD) and split the key blocks by parity, one
+//   block per wave per step; at the end the pair's running statistics and
+//   accumulators are combined through LDS with the online-softmax rescaling
+//   (2^(m_i - M)) and the even wave writes O and L.  Twice as many
+//   workgroups for the same rows: used when query tiles are few.
 constexpr int kWaves8 = 8;
 constexpr int kThreads8 = kWave * kWaves8;
+
+template <bool PAIR>
+struct QRows {
+  static constexpr int value = PAIR ? 32 * kWaves8 / 2 : 32 * kWaves8;
+};
 
 // DMA of one ring unit (one K tile, one V tile): each tile's 16-byte-per-lane
 // load instructions are dealt to the eight waves round-robin, K in the first
@@ -826,7 +834,7 @@ struct Dma8 {
   }
 };
 
-template <typename T, typename OT, int D, bool CAUSAL>
+template <typename T, typename OT, int D, bool CAUSAL, bool PAIR>
 __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__restrict__ k,
                                           const T *__restrict__ v, OT *__restrict__ o,
                                           float *__restrict__ lse, float *__restrict__ ws,
@@ -837,6 +845,7 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
   typedef typename P::frag frag;
   typedef Dma8<T, D> DM;
   constexpr int UNIT = DM::PER_WAVE;
+  constexpr int QT = QRows<PAIR>::value;
   __shared__ __attribute__((aligned(16))) char ring_[DM::LDS_BYTES];
   lds_char *ring = (lds_char *)ring_;
   const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
@@ -848,8 +857,8 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qg = wave & 3;  // query group (32 rows)
-  const int h = wave >> 2;  // block parity
+  const int qg = PAIR ? (wave & 3) : wave;  // query group (32 rows)
+  const int h = PAIR ? (wave >> 2) : 0;     // block parity (PAIR)
   s.lane = tid & 63;
   s.wave = qg;
   s.l32 = s.lane & 31;
@@ -875,6 +884,7 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
 
   const int kt0 = it.kt0;
   const int ntiles = it.kt1 - it.kt0;
+  // last 32-key block (absolute index) this query group needs in this item
   const int lastb = CAUSAL ? min(2 * it.kt1 - 1, s.qw / 32) : 2 * it.kt1 - 1;
 
   // Q first: its loads are the oldest in flight, so the prologue wait for
@@ -884,17 +894,24 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
   for (int f = 0; f < P::QF; ++f)
     qraw[f] = load16_async(q_rs, ((uint32_t)s.my_q * D + 16 * f + 8 * s.g) * sizeof(T));
 
-  // The first step's P.V belongs to the block before the item (P = 0) and
-  // reads V stage 3 (both halves), which no load has written yet: clear it.
+  // The first P.V of a wave belongs to the block before the item (P = 0)
+  // and reads V stage 3 (rows 32..63, and with PAIR also rows 0..31), which
+  // no load has written yet: clear it so that 0 * stale LDS cannot give NaN.
+  // Everything else the kernel reads was written by a load (rows past Nk by
+  // the bounds check, as zero).
   {
-    constexpr int Z0 = L::V_OFF + 3 * L::V_BYTES;
-    constexpr int ZN = L::V_BYTES / 16;
+    constexpr int Z0 = L::V_OFF + 3 * L::V_BYTES + (PAIR ? 0 : 32 * L::SV * 16);
+    constexpr int ZN = (PAIR ? 64 : 32) * L::SV;  // 16-byte chunks
     for (int i = tid; i < ZN; i += kThreads8)
       *(__attribute__((address_space(3))) u32x4 *)(ring + Z0 + i * 16) = u32x4{};
   }
 
-  // Units as in pipe_run: 0..2 in the prologue, unit r+3 = (K(r+3), V(r+2))
-  // in step r; unit j >= 1 only when j <= ntiles.
+  // Issue units: unit 0 = (K0,V0), 1 = (K1,V1), 2 = (K2,V2) in the
+  // prologue, then step r issues unit r+3 = (K(r+3), V(r+2)) (relative
+  // tiles; tile j lives in ring stage j % 4).  Unit j >= 1 is issued only
+  // when j <= ntiles: nothing is fetched past the item except one K tile
+  // whose scores are never used.  Every wave issues the same number of loads
+  // per unit, so "the youngest unit may be in flight" is one vmcnt value.
   dm.issue(k_rs, v_rs, kt0, 0, kt0, 0);
   dm.issue(k_rs, v_rs, kt0 + 1, 1, kt0 + 1, 1);
   if (ntiles >= 2) {
@@ -919,30 +936,58 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
   s.P1[1] = frag{};
   s.qk(s.kptr(ring, 0, h), s.S0);
 
-  // Step r: this wave's block b = 2(kt0 + r) + h.  It reads K tile r+1
-  // (half h, for the K.Q^T of block b+2) and V tile r-1 (half h, for the
-  // P.V of block b-2).  K(r+1) was requested in step r-2 and V(r-1) in step
-  // r-3 (or the prologue); unit r+2 may still be in flight.  Step r's
-  // request of unit r+3 overwrites K(r-1) and V(r-2), last read in steps
-  // r-2 and r-1.  Two steps per iteration: S and P alternate registers.
-  auto step = [&](int r, auto odd) {
-    ring_barrier_sel<UNIT>(r + 2 <= ntiles);
-    if (r + 3 <= ntiles)
-      dm.issue(k_rs, v_rs, kt0 + r + 3, (r + 3) & (kStages - 1), kt0 + r + 2,
-               (r + 2) & (kStages - 1));
-    const int b = 2 * (kt0 + r) + h;
-    s.template block<decltype(odd)::value, 0>(ring, b, lastb, (r + kStages - 1) & (kStages - 1),
-                                              h, (r + 1) & (kStages - 1), h);
-  };
-  for (int r = 0; r < ntiles; r += 2) {
-    step(r, std::false_type{});
-    if (r + 1 < ntiles) step(r + 1, std::true_type{});
-  }
-  // Drain: P.V of this wave's last block.  The last step's wait covered
-  // every unit issued (units <= ntiles), and no unit overwrites the V tiles
-  // of the item's last four steps, so that block's V is still in the ring.
-  // Its P sits in P0 or P1 by the parity of the step that made it.
-  {
+  if constexpr (!PAIR) {
+    // Step r reads K tiles r, r+1 and V tiles r-1, r (relative):
+    //   block 2r  : P.V(V tile r-1, rows 32..63), K.Q^T(K tile r, rows 32..63)
+    //   block 2r+1: P.V(V tile r, rows 0..31),    K.Q^T(K tile r+1, rows 0..31)
+    // K(r+1) and V(r) belong to units <= r+1, issued at least two steps
+    // earlier; unit r+2 (issued in step r-1, if at all) may still be in
+    // flight.  Step r requests unit r+3: K(r+3) into the stage of K(r-1) and
+    // V(r+2) into the stage of V(r-2), both last read in step r-1.  Every
+    // wave runs every step so that the loads and barriers line up.
+    for (int r = 0; r < ntiles; ++r) {
+      ring_barrier_sel<UNIT>(r + 2 <= ntiles);
+      if (r + 3 <= ntiles)
+        dm.issue(k_rs, v_rs, kt0 + r + 3, (r + 3) & (kStages - 1), kt0 + r + 2,
+                 (r + 2) & (kStages - 1));
+      const int st0 = r & (kStages - 1);
+      const int stm = (r + kStages - 1) & (kStages - 1);
+      const int st1 = (r + 1) & (kStages - 1);
+      const int b = 2 * (kt0 + r);
+      s.template block<false, 0>(ring, b, lastb, stm, 1, st0, 1);
+      s.template block<true, 0>(ring, b + 1, lastb, st0, 0, st1, 0);
+    }
+    // Drain: P.V of the wave's last block (its P sits in P0 for an even
+    // block, P1 for an odd one).  The last step's wait covered every unit
+    // issued (units <= ntiles), and no unit overwrites the V tiles of the
+    // item's last four steps, where a wave's last block always lies.
+    if (lastb >= 2 * kt0) {
+      const int rl = (lastb >> 1) - kt0;
+      frag pl[2];
+      pl[0] = (lastb & 1) ? s.P1[0] : s.P0[0];
+      pl[1] = (lastb & 1) ? s.P1[1] : s.P0[1];
+      s.pv(s.vptr(ring, rl & (kStages - 1), lastb & 1), pl);
+    }
+  } else {
+    // Step r: this wave's block b = 2(kt0 + r) + h.  It reads K tile r+1
+    // (half h, for the K.Q^T of block b+2) and V tile r-1 (half h, for the
+    // P.V of block b-2); loads and stage reuse as above.  Two steps per
+    // iteration: S and P alternate registers from step to step.
+    auto step = [&](int r, auto odd) {
+      ring_barrier_sel<UNIT>(r + 2 <= ntiles);
+      if (r + 3 <= ntiles)
+        dm.issue(k_rs, v_rs, kt0 + r + 3, (r + 3) & (kStages - 1), kt0 + r + 2,
+                 (r + 2) & (kStages - 1));
+      const int b = 2 * (kt0 + r) + h;
+      s.template block<decltype(odd)::value, 0>(ring, b, lastb, (r + kStages - 1) & (kStages - 1),
+                                                h, (r + 1) & (kStages - 1), h);
+    };
+    for (int r = 0; r < ntiles; r += 2) {
+      step(r, std::false_type{});
+      if (r + 1 < ntiles) step(r + 1, std::true_type{});
+    }
+    // Drain: P.V of this wave's last block, made in step rl: its P sits in
+    // P0 or P1 by the parity of rl.
     const int mylast = lastb - ((lastb - h) & 1);  // last block of parity h
     if (mylast >= 2 * kt0 + h) {
       const int rl = mylast / 2 - kt0;
@@ -953,78 +998,83 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
     }
   }
   wait_vmcnt<0>();  // no DMA may outlive the ring
-
-  // Combine the pair: the odd wave hands (m, l, lr, acc) to the even one.
   ring_barrier<0>();  // every wave is done with the ring
-  constexpr int NR = P::NDB * 4;  // f32x4 registers of acc per lane
-  lds_char *xch = ring + (uint32_t)qg * (NR + 1) * kWave * 16;
-  if (h == 1) {
+
+  float M = s.m_use, l = s.l, lr = s.lr;
+  if constexpr (PAIR) {
+    // Combine the pair: the odd wave hands (m, l, lr, acc) to the even one.
+    constexpr int NR = P::NDB * 4;  // f32x4 registers of acc per lane
+    lds_char *xch = ring + (uint32_t)qg * (NR + 1) * kWave * 16;
+    if (h == 1) {
 #pragma unroll
-    for (int db = 0; db < P::NDB; ++db)
+      for (int db = 0; db < P::NDB; ++db)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 x = {s.acc[db][4 * r4], s.acc[db][4 * r4 + 1], s.acc[db][4 * r4 + 2],
-                         s.acc[db][4 * r4 + 3]};
-        *(__attribute__((address_space(3))) f32x4 *)(xch + ((db * 4 + r4) * kWave + s.lane) * 16) = x;
-      }
-    const f32x4 st = {s.m_use, s.l, s.lr, 0.f};
-    *(__attribute__((address_space(3))) f32x4 *)(xch + (NR * kWave + s.lane) * 16) = st;
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 x = {s.acc[db][4 * r4], s.acc[db][4 * r4 + 1], s.acc[db][4 * r4 + 2],
+                           s.acc[db][4 * r4 + 3]};
+          *(__attribute__((address_space(3))) f32x4 *)(xch + ((db * 4 + r4) * kWave + s.lane) * 16) = x;
+        }
+      const f32x4 st = {s.m_use, s.l, s.lr, 0.f};
+      *(__attribute__((address_space(3))) f32x4 *)(xch + (NR * kWave + s.lane) * 16) = st;
+    }
+    ring_barrier<0>();
+    if (h == 0) {
+      const f32x4 st =
+          *(const __attribute__((address_space(3))) f32x4 *)(xch + (NR * kWave + s.lane) * 16);
+      // A wave that saw no key of a row (its blocks lie past the row under
+      // the causal mask, or the item starts there) has m = -inf, l = 0,
+      // acc = 0 and weight 0; when neither wave saw one the row's partial is
+      // empty (l = 0).
+      M = fmaxf(s.m_use, st[0]);
+      const float a0 = s.m_use == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s.m_use - M);
+      const float a1 = st[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st[0] - M);
+      l = s.l * a0 + st[1] * a1;
+      lr = s.lr * a0 + st[2] * a1;
+#pragma unroll
+      for (int db = 0; db < P::NDB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 x = *(const __attribute__((address_space(3))) f32x4 *)(
+              xch + ((db * 4 + r4) * kWave + s.lane) * 16);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            s.acc[db][4 * r4 + e] = s.acc[db][4 * r4 + e] * a0 + x[e] * a1;
+        }
+    }
+    // The ring is free for the workgroup's next item once every read of the
+    // exchange area is done.
+    ring_barrier<0>();
+    if (h == 1) return;
   }
-  ring_barrier<0>();
-  f32x4 st = {0.f, 0.f, 0.f, 0.f};
-  if (h == 0) st = *(const __attribute__((address_space(3))) f32x4 *)(xch + (NR * kWave + s.lane) * 16);
-  // A wave that saw no key of a row (its blocks lie past the row under the
-  // causal mask, or the item starts there) has m = -inf, l = 0, acc = 0 and
-  // weight 0; when neither wave saw one the row's partial is empty (l = 0).
-  const float M = fmaxf(s.m_use, st[0]);
-  const float a0 = s.m_use == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s.m_use - M);
-  const float a1 = st[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st[0] - M);
-  const float l = s.l * a0 + st[1] * a1;
-  const float lr = s.lr * a0 + st[2] * a1;
-  if (h == 0) {
-#pragma unroll
-    for (int db = 0; db < P::NDB; ++db)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 x = *(const __attribute__((address_space(3))) f32x4 *)(
-            xch + ((db * 4 + r4) * kWave + s.lane) * 16);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          s.acc[db][4 * r4 + e] = s.acc[db][4 * r4 + e] * a0 + x[e] * a1;
-      }
-  }
-  // The ring is free for the workgroup's next item once every read of the
-  // exchange area is done.
-  ring_barrier<0>();
-  if (h == 1) return;
 
   if (it.slot < 0) {
     epilogue<D, OT>(s.acc, M, l, o, lse, it.bh, Nq, s.my_q, s.g, lr);
   } else {
-    float *ws_o = ws + (size_t)it.slot * kBM * D;
-    float *ws_s = ws + (size_t)nslots * kBM * D + (size_t)it.slot * kBM * 4;
+    float *ws_o = ws + (size_t)it.slot * QT * D;
+    float *ws_s = ws + (size_t)nslots * QT * D + (size_t)it.slot * QT * 4;
     epilogue_partial<D>(s.acc, M, l, lr, ws_o, ws_s, s.my_q - it.q0, s.g);
   }
 }
 
-template <typename T, typename OT, int D, bool CAUSAL>
+template <typename T, typename OT, int D, bool CAUSAL, bool PAIR>
 __global__ __launch_bounds__(kThreads8) void fa_fwd_pipe8(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     OT *__restrict__ o, float *__restrict__ lse, int Nq, int Nk, int BH, int nqt,
     float c, int negate) {
-  const WorkItem wi = work_item(BH, nqt, CAUSAL);
-  const int kend = CAUSAL ? min(Nk, wi.q0 + kBM) : Nk;
+  constexpr int QT = QRows<PAIR>::value;
+  const WorkItem wi = work_item(BH, nqt, CAUSAL, QT);
+  const int kend = CAUSAL ? min(Nk, wi.q0 + QT) : Nk;
   const PipeItem it = {wi.bh, wi.q0, 0, (kend + kBN - 1) / kBN, -1};
-  pipe8_run<T, OT, D, CAUSAL>(q, k, v, o, lse, nullptr, Nq, Nk, c, negate, it, 0);
+  pipe8_run<T, OT, D, CAUSAL, PAIR>(q, k, v, o, lse, nullptr, Nq, Nk, c, negate, it, 0);
 }
 
 // ---------------------------------------------------------------------------
 // Stream-K schedule (persistent workgroups).  The work of a call is laid out
-// as one sequence of units, a unit being one 64-key tile of one 128-row query
-// tile: head by head, and within a head the query tiles in zigzag order
-// 0, nqt-1, 1, nqt-2, ... (under the causal mask tile t needs
-// min(2t+2, nkt) key tiles, so neighbours in this order pair short and long
-// tiles).  Chunk c of G holds units [b(c), b(c+1)) with b(c) = floor(c*T/G);
+// as one sequence of units, a unit being one 64-key tile of one query tile of
+// 64*tu rows (128 with the pair-split layout, 256 without): head by head,
+// and within a head the query tiles in zigzag order 0, nqt-1, 1, nqt-2, ...
+// (under the causal mask tile t needs min(tu(t+1), nkt) key tiles, so
+// neighbours in this order pair short and long tiles).  Chunk c of G holds units [b(c), b(c+1)) with b(c) = floor(c*T/G);
 // each workgroup runs one chunk, so every CU gets the same number of units.
 // A chunk is a list of pieces (a query tile's key range, or part of it); a
 // piece that covers its whole tile writes O and L, any other writes a
@@ -1036,37 +1086,43 @@ struct StreamPlan {
   long long cq;        // T / G
   int cr;              // T % G
   int G;               // chunks = workgroups, 1 <= G <= min(T, 65535)
-  int nqt, nkt;        // query tiles (128 rows), key tiles (64 keys)
+  int nqt, nkt;        // query tiles (64*tu rows), key tiles (64 keys)
+  int tu;              // key tiles per query tile on the causal diagonal: 2 or 4
 };
 
+// Layout of the stream schedule's kernel: D = 128 runs 128-row tiles
+// (pair-split), D = 64, whose blocks are half as long, 256-row tiles, which
+// share the per-step costs between two blocks.
+constexpr bool stream_pair(int D) { return D == 128; }
+
 // Key tiles of query tile t.
-__host__ __device__ inline int tile_w(int t, int nkt, bool causal) {
-  return causal ? (2 * t + 2 < nkt ? 2 * t + 2 : nkt) : nkt;
+__host__ __device__ inline int tile_w(int t, int nkt, int tu, bool causal) {
+  return causal ? (tu * (t + 1) < nkt ? tu * (t + 1) : nkt) : nkt;
 }
 
 // Units of query tiles 0..t-1.
-__host__ __device__ inline long long prefix_nat(int t, int nkt, bool causal) {
+__host__ __device__ inline long long prefix_nat(int t, int nkt, int tu, bool causal) {
   if (!causal) return (long long)t * nkt;
-  const int a = nkt / 2;  // tiles i < a have 2i+2 <= nkt keys tiles
-  if (t <= a) return (long long)t * (t + 1);
-  return (long long)a * (a + 1) + (long long)(t - a) * nkt;
+  const int a = nkt / tu;  // tiles i < a have tu*(i+1) <= nkt key tiles
+  if (t <= a) return (long long)tu * t * (t + 1) / 2;
+  return (long long)tu * a * (a + 1) / 2 + (long long)(t - a) * nkt;
 }
 
 // Query tile at zigzag position o, and units of positions 0..o-1.
 __host__ __device__ inline int zz_tile(int o, int nqt) {
   return (o & 1) ? nqt - 1 - (o >> 1) : (o >> 1);
 }
-__host__ __device__ inline long long zz_prefix(int o, int nqt, int nkt, bool causal) {
-  return prefix_nat((o + 1) >> 1, nkt, causal) +
-         (prefix_nat(nqt, nkt, causal) - prefix_nat(nqt - (o >> 1), nkt, causal));
+__host__ __device__ inline long long zz_prefix(int o, int nqt, int nkt, int tu, bool causal) {
+  return prefix_nat((o + 1) >> 1, nkt, tu, causal) +
+         (prefix_nat(nqt, nkt, tu, causal) - prefix_nat(nqt - (o >> 1), nkt, tu, causal));
 }
 
 // Zigzag position of the tile holding head-relative unit r (0 <= r < per_head).
-__host__ __device__ inline int zz_find(long long r, int nqt, int nkt, bool causal) {
+__host__ __device__ inline int zz_find(long long r, int nqt, int nkt, int tu, bool causal) {
   int lo = 0, hi = nqt - 1;  // zz_prefix(lo) <= r always holds
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (zz_prefix(mid, nqt, nkt, causal) <= r)
+    if (zz_prefix(mid, nqt, nkt, tu, causal) <= r)
       lo = mid;
     else
       hi = mid - 1;
@@ -1086,7 +1142,7 @@ __device__ __forceinline__ int chunk_of(int g, int G) {
   return (G % 8 == 0) ? (g % 8) * (G / 8) + g / 8 : g;
 }
 
-template <typename T, typename OT, int D, bool CAUSAL>
+template <typename T, typename OT, int D, bool CAUSAL, bool PAIR>
 __global__ __launch_bounds__(kThreads8) void fa_fwd_stream(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     OT *__restrict__ o, float *__restrict__ lse, float *__restrict__ ws, int Nq, int Nk,
@@ -1097,20 +1153,21 @@ __global__ __launch_bounds__(kThreads8) void fa_fwd_stream(
   // position of the chunk's first unit: head, zigzag tile position, key tile
   int bh = (int)(u0 / sp.per_head);
   const long long r0 = u0 - (long long)bh * sp.per_head;
-  int zo = zz_find(r0, sp.nqt, sp.nkt, CAUSAL);
-  int kt0 = (int)(r0 - zz_prefix(zo, sp.nqt, sp.nkt, CAUSAL));
+  constexpr int TU = QRows<PAIR>::value / kBN;
+  int zo = zz_find(r0, sp.nqt, sp.nkt, TU, CAUSAL);
+  int kt0 = (int)(r0 - zz_prefix(zo, sp.nqt, sp.nkt, TU, CAUSAL));
   bool first = true;
   while (left > 0) {
     const int t = zz_tile(zo, sp.nqt);
-    const int w = tile_w(t, sp.nkt, CAUSAL);
+    const int w = tile_w(t, sp.nkt, TU, CAUSAL);
     const int kt1 = left < (long long)(w - kt0) ? kt0 + (int)left : w;
     PipeItem it;
     it.bh = bh;
-    it.q0 = t * kBM;
+    it.q0 = t * QRows<PAIR>::value;
     it.kt0 = kt0;
     it.kt1 = kt1;
     it.slot = (kt0 == 0 && kt1 == w) ? -1 : 2 * ch + (first ? 0 : 1);
-    pipe8_run<T, OT, D, CAUSAL>(q, k, v, o, lse, ws, Nq, Nk, c, negate, it, 2 * sp.G);
+    pipe8_run<T, OT, D, CAUSAL, PAIR>(q, k, v, o, lse, ws, Nq, Nk, c, negate, it, 2 * sp.G);
     left -= kt1 - kt0;
     first = false;
     kt0 = 0;  // the next piece starts a tile
@@ -1129,39 +1186,41 @@ struct CutList {
   uint16_t j[kMaxChunks - 1];
 };
 
-// Combines the pieces of the cut query tiles, kMergeSplit workgroups per
-// tile, with a_i = 2^(m_i - M), M = max_i m_i:
+// Combines the pieces of the cut query tiles, one workgroup per kMergeRows
+// rows of a tile, with a_i = 2^(m_i - M), M = max_i m_i:
 // O = sum_i a_i lr_i O_i / sum_i a_i lr_i, L = ln2 * (M + log2 sum_i a_i l_i).
 // The tile's pieces: chunk j-1 (its first piece when it starts at the tile,
 // else its last), then every chunk c >= j that starts inside the tile (its
 // first piece).  Each thread owns one 4-wide column slice of NR rows and
 // loads two pieces per round trip.
-constexpr int kMergeSplit = 8;
+constexpr int kMergeRows = 16;
 
-template <typename OT, int D, bool CAUSAL>
+template <typename OT, int D, bool CAUSAL, int QT>
 __global__ __launch_bounds__(kThreads) void fa_merge_stream(const float *__restrict__ ws,
                                                             OT *__restrict__ o,
                                                             float *__restrict__ lse, int Nq,
                                                             StreamPlan sp, CutList cuts) {
   constexpr int C4 = D / 4;           // float4 per row
   constexpr int RPP = kThreads / C4;  // rows per pass of the workgroup
-  constexpr int ROWS = kBM / kMergeSplit;
+  constexpr int TU = QT / kBN;
+  constexpr int SPLIT = QT / kMergeRows;
+  constexpr int ROWS = kMergeRows;
   constexpr int NR = ROWS / RPP;      // rows per thread
   static_assert(NR >= 1 && ROWS % RPP == 0, "merge tiling");
-  const int j = cuts.j[blockIdx.x / kMergeSplit];
-  const int rbase = (blockIdx.x % kMergeSplit) * ROWS;
+  const int j = cuts.j[blockIdx.x / SPLIT];
+  const int rbase = (blockIdx.x % SPLIT) * ROWS;
   const long long bj = chunk_start(sp, j);
   const int bh = (int)(bj / sp.per_head);
   const long long base = (long long)bh * sp.per_head;
-  const int zo = zz_find(bj - base, sp.nqt, sp.nkt, CAUSAL);
-  const long long s0 = base + zz_prefix(zo, sp.nqt, sp.nkt, CAUSAL);  // tile's first unit
+  const int zo = zz_find(bj - base, sp.nqt, sp.nkt, TU, CAUSAL);
+  const long long s0 = base + zz_prefix(zo, sp.nqt, sp.nkt, TU, CAUSAL);  // tile's first unit
   const long long bprev = chunk_start(sp, j - 1);
   const int t = zz_tile(zo, sp.nqt);
-  const long long s1 = s0 + tile_w(t, sp.nkt, CAUSAL);
+  const long long s1 = s0 + tile_w(t, sp.nkt, TU, CAUSAL);
   const int c4 = threadIdx.x % C4;
   const int r0 = rbase + threadIdx.x / C4;
   const int nslots = 2 * sp.G;
-  const float *ws_s = ws + (size_t)nslots * kBM * D;
+  const float *ws_s = ws + (size_t)nslots * QT * D;
   float M[NR], ls[NR], lrs[NR];
   f32x4 acc[NR];
 #pragma unroll
@@ -1183,7 +1242,7 @@ __global__ __launch_bounds__(kThreads) void fa_merge_stream(const float *__restr
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
         if (sl[u] < 0) continue;
-        const size_t e = (size_t)sl[u] * kBM + r0 + i * RPP;
+        const size_t e = (size_t)sl[u] * QT + r0 + i * RPP;
         st[u][i] = *reinterpret_cast<const f32x4 *>(ws_s + e * 4);
         x[u][i] = *reinterpret_cast<const f32x4 *>(ws + e * D + 4 * c4);
       }
@@ -1204,7 +1263,7 @@ __global__ __launch_bounds__(kThreads) void fa_merge_stream(const float *__restr
   }
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
-    const int row = t * kBM + r0 + i * RPP;
+    const int row = t * QT + r0 + i * RPP;
     if (row < Nq) {
       store4<OT>(o + ((size_t)bh * Nq + row) * D + 4 * c4, acc[i] * (1.0f / lrs[i]));
       if (c4 == 0) lse[(size_t)bh * Nq + row] = (M[i] + log2f(ls[i])) * 0.69314718055994531f;
@@ -1361,7 +1420,7 @@ struct Launch {
   void *o;
   float *lse;
   float *ws;
-  int Nq, Nk, BH, nqt;
+  int Nq, Nk, BH, nqt, nqtg;  // query tiles of kBM rows and of the 8-wave grid's rows
   float c;
   hipStream_t stream;
   const StreamPlan *plan;  // non-null: stream-K schedule (pipelined kernel only)
@@ -1378,21 +1437,23 @@ hipError_t launch16(const Launch &a) {
     const int neg = a.c < 0.f ? 1 : 0;
     if (a.plan) {
       const StreamPlan &sp = *a.plan;
-      hipLaunchKernelGGL((fa_fwd_stream<T, OT, D, CAUSAL>), dim3((unsigned)sp.G),
+      constexpr bool PAIR = stream_pair(D);
+      hipLaunchKernelGGL((fa_fwd_stream<T, OT, D, CAUSAL, PAIR>), dim3((unsigned)sp.G),
                          dim3(kThreads8), 0, a.stream, (const T *)a.q, (const T *)a.k,
                          (const T *)a.v, (OT *)a.o, a.lse, a.ws, a.Nq, a.Nk, c, neg, sp);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       if (a.cuts && a.cuts->n > 0) {
-        hipLaunchKernelGGL((fa_merge_stream<OT, D, CAUSAL>),
-                           dim3((unsigned)(a.cuts->n * kMergeSplit)),
+        hipLaunchKernelGGL((fa_merge_stream<OT, D, CAUSAL, QRows<PAIR>::value>),
+                           dim3((unsigned)(a.cuts->n * (QRows<PAIR>::value / kMergeRows))),
                            dim3(kThreads), 0, a.stream, (const float *)a.ws, (OT *)a.o,
                            a.lse, a.Nq, sp, *a.cuts);
       }
     } else {
-      hipLaunchKernelGGL((fa_fwd_pipe8<T, OT, D, CAUSAL>), dim3((unsigned)(a.BH * a.nqt)),
-                         dim3(kThreads8), 0, a.stream, (const T *)a.q, (const T *)a.k,
-                         (const T *)a.v, (OT *)a.o, a.lse, a.Nq, a.Nk, a.BH, a.nqt, c, neg);
+      hipLaunchKernelGGL((fa_fwd_pipe8<T, OT, D, CAUSAL, false>),
+                         dim3((unsigned)(a.BH * a.nqtg)), dim3(kThreads8), 0, a.stream,
+                         (const T *)a.q, (const T *)a.k, (const T *)a.v, (OT *)a.o, a.lse,
+                         a.Nq, a.Nk, a.BH, a.nqtg, c, neg);
     }
   } else {
     hipLaunchKernelGGL((fa_fwd_mfma16<T, OT, D, CAUSAL>), dim3((unsigned)(a.BH * a.nqt)),
@@ -1460,7 +1521,7 @@ int validate(const void *q, const void *k, const void *v, const void *o, const f
   // Per-head slices are addressed with 32-bit byte offsets (plus slack past
   // the end for ragged rows); the grid is one-dimensional.
   const int64_t lim = (int64_t)1 << 31;
-  if (Nq > lim / (D * 4) - kBM || Nk > lim / (D * 4) - 5 * kBN) return FA_ERR_SHAPE;
+  if (Nq > lim / (D * 4) - QRows<false>::value || Nk > lim / (D * 4) - 5 * kBN) return FA_ERR_SHAPE;
   if (B > lim || H > lim || B * H > lim) return FA_ERR_SHAPE;
   sh.BH = B * H;
   sh.nqt = (Nq + kBM - 1) / kBM;
@@ -1498,26 +1559,30 @@ int device_cus(int *cus) {
 }
 
 // Stream-K schedule of the pipelined kernel (16-bit inputs, D >= 64): one
-// chunk per compute unit.  With four or more query tiles per compute unit
-// the longest-first grid of fa_fwd already keeps every unit busy to the
+// chunk per compute unit.  With four or more 128-row query tiles per compute
+// unit the longest-first grid of fa_fwd already keeps every unit busy to the
 // end, and a chunk would hold many pieces, each paying its own prologue: the
 // call then takes that grid.  Returns false for the paths that take no
 // workspace.
-bool make_plan(int64_t BH, int64_t nqt, int64_t Nk, int64_t D, int dtype, bool causal,
+bool make_plan(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, int dtype, bool causal,
                int cus, StreamPlan &sp, size_t &ws_bytes) {
   ws_bytes = 0;
   if (dtype == FA_F32 || D < 64 || cus < 1) return false;
-  if (BH * nqt >= 4 * (int64_t)cus) return false;
+  const int64_t pair_rows = QRows<true>::value;
+  if (BH * ((Nq + pair_rows - 1) / pair_rows) >= 4 * (int64_t)cus) return false;
+  const int64_t qt = stream_pair((int)D) ? pair_rows : QRows<false>::value;
   const int nkt = (int)((Nk + kBN - 1) / kBN);
-  sp.nqt = (int)nqt;
+  const int nqt = (int)((Nq + qt - 1) / qt);
+  sp.tu = (int)(qt / kBN);
+  sp.nqt = nqt;
   sp.nkt = nkt;
-  sp.per_head = prefix_nat((int)nqt, nkt, causal);
+  sp.per_head = prefix_nat(nqt, nkt, sp.tu, causal);
   sp.T = BH * sp.per_head;
   const int gmax = cus < kMaxChunks ? cus : kMaxChunks;
   sp.G = (int)(sp.T < gmax ? sp.T : gmax);
   sp.cq = sp.T / sp.G;
   sp.cr = (int)(sp.T % sp.G);
-  ws_bytes = (size_t)2 * sp.G * kBM * (size_t)(D + 4) * 4;
+  ws_bytes = (size_t)2 * sp.G * qt * (size_t)(D + 4) * 4;
   return true;
 }
 
@@ -1530,8 +1595,8 @@ void make_cuts(const StreamPlan &sp, bool causal, CutList &cl) {
     const long long bj = chunk_start(sp, j);
     const long long bh = bj / sp.per_head;
     const long long base = bh * sp.per_head;
-    const int zo = zz_find(bj - base, sp.nqt, sp.nkt, causal);
-    const long long s0 = base + zz_prefix(zo, sp.nqt, sp.nkt, causal);
+    const int zo = zz_find(bj - base, sp.nqt, sp.nkt, sp.tu, causal);
+    const long long s0 = base + zz_prefix(zo, sp.nqt, sp.nkt, sp.tu, causal);
     if (s0 == bj || chunk_start(sp, j - 1) > s0) continue;
     cl.j[cl.n++] = (uint16_t)j;
   }
@@ -1551,6 +1616,7 @@ int run(const void *q, const void *k, const void *v, void *o, float *lse, int64_
   a.Nk = (int)Nk;
   a.BH = (int)sh.BH;
   a.nqt = (int)sh.nqt;
+  a.nqtg = (int)((Nq + QRows<false>::value - 1) / QRows<false>::value);
   a.c = scale * 1.4426950408889634f;
   a.stream = (hipStream_t)stream;
   a.plan = plan;
@@ -1620,7 +1686,7 @@ int fa_fwd_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t 
   if (st != FA_OK) return st;
   StreamPlan pl;
   size_t ws = 0;
-  make_plan(B * H, (Nq + kBM - 1) / kBM, Nk, D, dtype, causal != 0, cus, pl, ws);
+  make_plan(B * H, Nq, Nk, D, dtype, causal != 0, cus, pl, ws);
   *bytes = ws;
   return FA_OK;
 }
@@ -1645,7 +1711,7 @@ int fa_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse, 
   if (st != FA_OK) return st;
   StreamPlan pl;
   size_t need = 0;
-  if (!make_plan(sh.BH, sh.nqt, Nk, D, dtype, causal != 0, cus, pl, need))
+  if (!make_plan(sh.BH, Nq, Nk, D, dtype, causal != 0, cus, pl, need))
     return run(q, k, v, o, lse, Nq, Nk, D, scale, causal, dtype, sh, nullptr, nullptr,
                stream);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
