@@ -1,0 +1,123 @@
+// Host check of the stream-K schedule of fa_fwd_ws (make_plan, ChunkWalk,
+// CutTile, make_cuts of csrc/stream_plan.h, the code the kernels and the
+// host planner run): for many shapes and
+// compute-unit counts, every key tile of every query tile is covered by
+// exactly one piece, pieces that do not cover their whole tile write to
+// distinct workspace slots, those tiles are exactly the cut list, and the
+// merge's enumeration of each cut tile yields exactly its pieces, whose key
+// ranges partition the tile.  Prints "ok <plans checked>" or the first
+// failure; exit status 0 on success.
+#include "../../transformer_attention_07_amd/csrc/stream_plan.h"
+
+#include <cstdio>
+#include <map>
+#include <set>
+#include <tuple>
+#include <vector>
+
+using namespace fa_sched;
+
+namespace {
+
+struct Piece {
+  int ch, kt0, kt1, slot;
+};
+
+int check(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, bool causal, int cus, int lead) {
+  StreamPlan sp;
+  size_t ws = 0;
+  if (!make_plan(BH, Nq, Nk, D, FA_BF16, causal, cus, sp, ws)) return 0;
+  if (lead >= 0) {  // the same plan with another lead
+    sp.lead = lead;
+    sp.per_head = prefix_nat(sp.nqt, sp.nkt, sp.tu, causal) + (long long)sp.lead * sp.nqt;
+    sp.T = BH * sp.per_head;
+    const int gmax = cus < kMaxChunks ? cus : kMaxChunks;
+    sp.G = (int)(sp.T < gmax ? sp.T : gmax);
+    sp.cq = sp.T / sp.G;
+    sp.cr = (int)(sp.T % sp.G);
+  }
+  const int qt = sp.tu * kKeys;
+  auto fail = [&](const char *what, long long a, long long b) {
+    printf("FAIL %s (%lld, %lld): BH=%lld Nq=%lld Nk=%lld D=%lld causal=%d cus=%d lead=%d G=%d\n",
+           what, a, b, (long long)BH, (long long)Nq, (long long)Nk, (long long)D, (int)causal,
+           cus, sp.lead, sp.G);
+    return -1;
+  };
+  if (sp.nqt != (int)((Nq + qt - 1) / qt)) return fail("nqt", sp.nqt, qt);
+  if (ws != (size_t)2 * sp.G * qt * (size_t)(D + 4) * 4 && lead < 0) return fail("ws", (long long)ws, 0);
+  std::map<std::pair<int, int>, std::vector<Piece>> tiles;  // (bh, t) -> pieces
+  std::set<int> slots;
+  for (int ch = 0; ch < sp.G; ++ch) {
+    ChunkWalk cw;
+    cw.init(sp, ch, causal);
+    PipeItem it;
+    int t;
+    while (cw.next(sp, causal, it, t)) {
+      if (it.bh < 0 || it.bh >= BH || t < 0 || t >= sp.nqt) return fail("tile", it.bh, t);
+      if (it.slot >= 0) {
+        if (it.slot != 2 * ch && it.slot != 2 * ch + 1) return fail("slot owner", it.slot, ch);
+        if (!slots.insert(it.slot).second) return fail("slot reused", it.slot, ch);
+      }
+      tiles[{it.bh, t}].push_back({ch, it.kt0, it.kt1, it.slot});
+    }
+  }
+  std::set<std::pair<int, int>> partial;
+  for (int bh = 0; bh < BH; ++bh)
+    for (int t = 0; t < sp.nqt; ++t) {
+      const int w = tile_w(t, sp.nkt, sp.tu, causal);
+      auto itr = tiles.find({bh, t});
+      if (itr == tiles.end()) return fail("tile missing", bh, t);
+      std::vector<int> cover(w, 0);
+      for (const Piece &p : itr->second) {
+        if (p.kt0 < 0 || p.kt1 > w || p.kt0 >= p.kt1) return fail("range", p.kt0, p.kt1);
+        for (int x = p.kt0; x < p.kt1; ++x) cover[x]++;
+        if ((p.slot < 0) != (p.kt0 == 0 && p.kt1 == w)) return fail("full/slot", p.kt0, p.slot);
+      }
+      for (int x = 0; x < w; ++x)
+        if (cover[x] != 1) return fail("coverage", t, x);
+      if (itr->second.size() > 1) partial.insert({bh, t});
+      else if (itr->second[0].slot >= 0) return fail("lone partial", bh, t);
+    }
+  CutList cl;
+  make_cuts(sp, causal, cl);
+  std::set<std::pair<int, int>> listed;
+  for (int i = 0; i < cl.n; ++i) {
+    CutTile ct;
+    ct.init(sp, cl.j[i], causal);
+    if (!ct.cut) return fail("cut flag", cl.j[i], 0);
+    if (!listed.insert({ct.bh, ct.t}).second) return fail("cut listed twice", ct.bh, ct.t);
+    std::set<int> want;
+    for (const Piece &p : tiles[{ct.bh, ct.t}]) want.insert(p.slot);
+    std::set<int> got;
+    for (int cc = ct.j - 1;; ++cc) {
+      const int s = ct.slot(sp, cc);
+      if (s < 0) break;
+      got.insert(s);
+    }
+    if (got != want) return fail("merge pieces", ct.bh, ct.t);
+  }
+  if (listed != partial) return fail("cut set", (long long)listed.size(), (long long)partial.size());
+  return 1;
+}
+
+}  // namespace
+
+int main() {
+  int n = 0;
+  const int64_t Ns[] = {1, 33, 64, 127, 128, 129, 255, 256, 300, 1000, 2048, 3000, 4096, 8192};
+  const int cuss[] = {1, 3, 8, 80, 256, 304, 1024};
+  const int leads[] = {-1, 0, 1, 5, 17};
+  for (int64_t BH : {1, 2, 3, 8})
+    for (int64_t Nq : Ns)
+      for (int64_t Nk : {(int64_t)1, (int64_t)63, (int64_t)500, (int64_t)4096, Nq})
+        for (int64_t D : {64, 128})
+          for (int causal = 0; causal < 2; ++causal)
+            for (int cus : cuss)
+              for (int lead : leads) {
+                const int r = check(BH, Nq, Nk, D, causal != 0, cus, lead);
+                if (r < 0) return 1;
+                n += r;
+              }
+  printf("ok %d\n", n);
+  return 0;
+}

@@ -44,8 +44,11 @@
 #include <string.h>
 
 #include "fa.h"
+#include "stream_plan.h"
 
 namespace {
+
+using namespace fa_sched;
 
 constexpr int kWave = 64;
 constexpr int kWaves = 4;
@@ -720,14 +723,6 @@ struct Pipe {
   }
 };
 
-// The work of one workgroup: query rows [q0, q0 + 128) of head bh against
-// key tiles [kt0, kt1) (64 keys each).  slot < 0: the item covers every key
-// the rows see and writes O and L; slot >= 0: the item is one part of a
-// split key range and writes a partial result to workspace slot `slot`.
-struct PipeItem {
-  int bh, q0, kt0, kt1, slot;
-};
-
 // Partial result of one split part, per row: O_p = acc / lr (fp32, D values),
 // and the statistics (m, l, lr, 0) as one 16-byte record, m being the base-2
 // exponent reference.  A row that saw no
@@ -776,6 +771,9 @@ template <bool PAIR>
 struct QRows {
   static constexpr int value = PAIR ? 32 * kWaves8 / 2 : 32 * kWaves8;
 };
+static_assert(QRows<true>::value == kPairRows && QRows<false>::value == kGridRows &&
+                  kBN == kKeys,
+              "tile shapes of the stream schedule");
 
 // DMA of one ring unit (one K tile, one V tile): each tile's 16-byte-per-lane
 // load instructions are dealt to the eight waves round-robin, K in the first
@@ -1068,73 +1066,6 @@ __global__ __launch_bounds__(kThreads8) void fa_fwd_pipe8(
   pipe8_run<T, OT, D, CAUSAL, PAIR>(q, k, v, o, lse, nullptr, Nq, Nk, c, negate, it, 0);
 }
 
-// ---------------------------------------------------------------------------
-// Stream-K schedule (persistent workgroups).  The work of a call is laid out
-// as one sequence of units, a unit being one 64-key tile of one query tile of
-// 64*tu rows (128 with the pair-split layout, 256 without): head by head,
-// and within a head the query tiles in zigzag order 0, nqt-1, 1, nqt-2, ...
-// (under the causal mask tile t needs min(tu(t+1), nkt) key tiles, so
-// neighbours in this order pair short and long tiles).  Chunk c of G holds units [b(c), b(c+1)) with b(c) = floor(c*T/G);
-// each workgroup runs one chunk, so every CU gets the same number of units.
-// A chunk is a list of pieces (a query tile's key range, or part of it); a
-// piece that covers its whole tile writes O and L, any other writes a
-// partial result to workspace slot 2c (the chunk's first piece) or 2c + 1
-// (its last), and fa_merge_stream combines the pieces of each cut tile.
-struct StreamPlan {
-  long long T;         // units in the call
-  long long per_head;  // units per head
-  long long cq;        // T / G
-  int cr;              // T % G
-  int G;               // chunks = workgroups, 1 <= G <= min(T, 65535)
-  int nqt, nkt;        // query tiles (64*tu rows), key tiles (64 keys)
-  int tu;              // key tiles per query tile on the causal diagonal: 2 or 4
-};
-
-// Layout of the stream schedule's kernel: D = 128 runs 128-row tiles
-// (pair-split), D = 64, whose blocks are half as long, 256-row tiles, which
-// share the per-step costs between two blocks.
-constexpr bool stream_pair(int D) { return D == 128; }
-
-// Key tiles of query tile t.
-__host__ __device__ inline int tile_w(int t, int nkt, int tu, bool causal) {
-  return causal ? (tu * (t + 1) < nkt ? tu * (t + 1) : nkt) : nkt;
-}
-
-// Units of query tiles 0..t-1.
-__host__ __device__ inline long long prefix_nat(int t, int nkt, int tu, bool causal) {
-  if (!causal) return (long long)t * nkt;
-  const int a = nkt / tu;  // tiles i < a have tu*(i+1) <= nkt key tiles
-  if (t <= a) return (long long)tu * t * (t + 1) / 2;
-  return (long long)tu * a * (a + 1) / 2 + (long long)(t - a) * nkt;
-}
-
-// Query tile at zigzag position o, and units of positions 0..o-1.
-__host__ __device__ inline int zz_tile(int o, int nqt) {
-  return (o & 1) ? nqt - 1 - (o >> 1) : (o >> 1);
-}
-__host__ __device__ inline long long zz_prefix(int o, int nqt, int nkt, int tu, bool causal) {
-  return prefix_nat((o + 1) >> 1, nkt, tu, causal) +
-         (prefix_nat(nqt, nkt, tu, causal) - prefix_nat(nqt - (o >> 1), nkt, tu, causal));
-}
-
-// Zigzag position of the tile holding head-relative unit r (0 <= r < per_head).
-__host__ __device__ inline int zz_find(long long r, int nqt, int nkt, int tu, bool causal) {
-  int lo = 0, hi = nqt - 1;  // zz_prefix(lo) <= r always holds
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (zz_prefix(mid, nqt, nkt, tu, causal) <= r)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  return lo;
-}
-
-// floor(c * T / G), without 64-bit division (c * cr < G^2 < 2^32).
-__host__ __device__ inline long long chunk_start(const StreamPlan &sp, int c) {
-  return (long long)c * sp.cq + (long long)((uint32_t)c * (uint32_t)sp.cr / (uint32_t)sp.G);
-}
-
 // Chunk run by workgroup g: consecutive chunks go to one XCD (workgroups are
 // dealt to the 8 XCDs round robin), so an XCD's workgroups share heads and
 // their K/V in its L2.
@@ -1147,52 +1078,21 @@ __global__ __launch_bounds__(kThreads8) void fa_fwd_stream(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     OT *__restrict__ o, float *__restrict__ lse, float *__restrict__ ws, int Nq, int Nk,
     float c, int negate, StreamPlan sp) {
-  const int ch = chunk_of(blockIdx.x, sp.G);
-  const long long u0 = chunk_start(sp, ch);
-  long long left = chunk_start(sp, ch + 1) - u0;
-  // position of the chunk's first unit: head, zigzag tile position, key tile
-  int bh = (int)(u0 / sp.per_head);
-  const long long r0 = u0 - (long long)bh * sp.per_head;
-  constexpr int TU = QRows<PAIR>::value / kBN;
-  int zo = zz_find(r0, sp.nqt, sp.nkt, TU, CAUSAL);
-  int kt0 = (int)(r0 - zz_prefix(zo, sp.nqt, sp.nkt, TU, CAUSAL));
-  bool first = true;
-  while (left > 0) {
-    const int t = zz_tile(zo, sp.nqt);
-    const int w = tile_w(t, sp.nkt, TU, CAUSAL);
-    const int kt1 = left < (long long)(w - kt0) ? kt0 + (int)left : w;
-    PipeItem it;
-    it.bh = bh;
+  ChunkWalk cw;
+  cw.init(sp, chunk_of(blockIdx.x, sp.G), CAUSAL);
+  PipeItem it;
+  int t;
+  while (cw.next(sp, CAUSAL, it, t)) {
     it.q0 = t * QRows<PAIR>::value;
-    it.kt0 = kt0;
-    it.kt1 = kt1;
-    it.slot = (kt0 == 0 && kt1 == w) ? -1 : 2 * ch + (first ? 0 : 1);
     pipe8_run<T, OT, D, CAUSAL, PAIR>(q, k, v, o, lse, ws, Nq, Nk, c, negate, it, 2 * sp.G);
-    left -= kt1 - kt0;
-    first = false;
-    kt0 = 0;  // the next piece starts a tile
-    if (++zo == sp.nqt) {
-      zo = 0;
-      ++bh;
-    }
   }
 }
 
-// Cut query tiles of a stream-K schedule, named by the first chunk boundary
-// j that falls strictly inside each (host-computed).
-constexpr int kMaxChunks = 1024;
-struct CutList {
-  int n;
-  uint16_t j[kMaxChunks - 1];
-};
-
-// Combines the pieces of the cut query tiles, one workgroup per kMergeRows
-// rows of a tile, with a_i = 2^(m_i - M), M = max_i m_i:
+// Combines the pieces of the cut query tiles (CutTile), one workgroup per
+// kMergeRows rows of a tile, with a_i = 2^(m_i - M), M = max_i m_i:
 // O = sum_i a_i lr_i O_i / sum_i a_i lr_i, L = ln2 * (M + log2 sum_i a_i l_i).
-// The tile's pieces: chunk j-1 (its first piece when it starts at the tile,
-// else its last), then every chunk c >= j that starts inside the tile (its
-// first piece).  Each thread owns one 4-wide column slice of NR rows and
-// loads two pieces per round trip.
+// Each thread owns one 4-wide column slice of NR rows and loads two pieces
+// per round trip.
 constexpr int kMergeRows = 16;
 
 template <typename OT, int D, bool CAUSAL, int QT>
@@ -1202,21 +1102,14 @@ __global__ __launch_bounds__(kThreads) void fa_merge_stream(const float *__restr
                                                             StreamPlan sp, CutList cuts) {
   constexpr int C4 = D / 4;           // float4 per row
   constexpr int RPP = kThreads / C4;  // rows per pass of the workgroup
-  constexpr int TU = QT / kBN;
   constexpr int SPLIT = QT / kMergeRows;
   constexpr int ROWS = kMergeRows;
   constexpr int NR = ROWS / RPP;      // rows per thread
   static_assert(NR >= 1 && ROWS % RPP == 0, "merge tiling");
-  const int j = cuts.j[blockIdx.x / SPLIT];
+  CutTile ct;
+  ct.init(sp, cuts.j[blockIdx.x / SPLIT], CAUSAL);
+  const int j = ct.j, bh = ct.bh, t = ct.t;
   const int rbase = (blockIdx.x % SPLIT) * ROWS;
-  const long long bj = chunk_start(sp, j);
-  const int bh = (int)(bj / sp.per_head);
-  const long long base = (long long)bh * sp.per_head;
-  const int zo = zz_find(bj - base, sp.nqt, sp.nkt, TU, CAUSAL);
-  const long long s0 = base + zz_prefix(zo, sp.nqt, sp.nkt, TU, CAUSAL);  // tile's first unit
-  const long long bprev = chunk_start(sp, j - 1);
-  const int t = zz_tile(zo, sp.nqt);
-  const long long s1 = s0 + tile_w(t, sp.nkt, TU, CAUSAL);
   const int c4 = threadIdx.x % C4;
   const int r0 = rbase + threadIdx.x / C4;
   const int nslots = 2 * sp.G;
@@ -1229,12 +1122,8 @@ __global__ __launch_bounds__(kThreads) void fa_merge_stream(const float *__restr
     ls[i] = lrs[i] = 0.f;
     acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  auto piece_slot = [&](int cc) {  // -1 past the tile's last piece
-    if (cc >= sp.G || (cc >= j && chunk_start(sp, cc) >= s1)) return -1;
-    return (cc == j - 1 && bprev != s0) ? 2 * cc + 1 : 2 * cc;
-  };
   for (int cc = j - 1;; cc += 2) {
-    const int sl[2] = {piece_slot(cc), piece_slot(cc + 1)};
+    const int sl[2] = {ct.slot(sp, cc), ct.slot(sp, cc + 1)};
     if (sl[0] < 0) break;
     f32x4 st[2][NR], x[2][NR];
 #pragma unroll
@@ -1556,50 +1445,6 @@ int device_cus(int *cus) {
   if (dev >= 0 && dev < 64) __atomic_store_n(&cache[dev], n, __ATOMIC_RELAXED);
   *cus = n;
   return FA_OK;
-}
-
-// Stream-K schedule of the pipelined kernel (16-bit inputs, D >= 64): one
-// chunk per compute unit.  With four or more 128-row query tiles per compute
-// unit the longest-first grid of fa_fwd already keeps every unit busy to the
-// end, and a chunk would hold many pieces, each paying its own prologue: the
-// call then takes that grid.  Returns false for the paths that take no
-// workspace.
-bool make_plan(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, int dtype, bool causal,
-               int cus, StreamPlan &sp, size_t &ws_bytes) {
-  ws_bytes = 0;
-  if (dtype == FA_F32 || D < 64 || cus < 1) return false;
-  const int64_t pair_rows = QRows<true>::value;
-  if (BH * ((Nq + pair_rows - 1) / pair_rows) >= 4 * (int64_t)cus) return false;
-  const int64_t qt = stream_pair((int)D) ? pair_rows : QRows<false>::value;
-  const int nkt = (int)((Nk + kBN - 1) / kBN);
-  const int nqt = (int)((Nq + qt - 1) / qt);
-  sp.tu = (int)(qt / kBN);
-  sp.nqt = nqt;
-  sp.nkt = nkt;
-  sp.per_head = prefix_nat(nqt, nkt, sp.tu, causal);
-  sp.T = BH * sp.per_head;
-  const int gmax = cus < kMaxChunks ? cus : kMaxChunks;
-  sp.G = (int)(sp.T < gmax ? sp.T : gmax);
-  sp.cq = sp.T / sp.G;
-  sp.cr = (int)(sp.T % sp.G);
-  ws_bytes = (size_t)2 * sp.G * qt * (size_t)(D + 4) * 4;
-  return true;
-}
-
-// The cut tiles of a schedule: boundary j (1 <= j < G) names the tile that
-// holds unit b(j) when b(j) is not that tile's first unit and no earlier
-// boundary lies inside it.
-void make_cuts(const StreamPlan &sp, bool causal, CutList &cl) {
-  cl.n = 0;
-  for (int j = 1; j < sp.G; ++j) {
-    const long long bj = chunk_start(sp, j);
-    const long long bh = bj / sp.per_head;
-    const long long base = bh * sp.per_head;
-    const int zo = zz_find(bj - base, sp.nqt, sp.nkt, sp.tu, causal);
-    const long long s0 = base + zz_prefix(zo, sp.nqt, sp.nkt, sp.tu, causal);
-    if (s0 == bj || chunk_start(sp, j - 1) > s0) continue;
-    cl.j[cl.n++] = (uint16_t)j;
-  }
 }
 
 int run(const void *q, const void *k, const void *v, void *o, float *lse, int64_t Nq,

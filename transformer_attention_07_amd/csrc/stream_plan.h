@@ -1,0 +1,247 @@
+// Stream-K schedule of fa_fwd_ws: host and device code shared by the
+// kernels of fa_fwd.hip, the host planner and the host check of the
+// schedule (plain C++ when not compiled as HIP).
+//
+// Splitting the key range of one query tile over workgroups and combining
+// the parts with the online-softmax rescaling is the sequence parallelism of
+// page "FlashAttention技术演进全景图" §3.2, with the update rule of page
+// "FlashAttention-2实现与优化：高效注意力机制详解" §3.1.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fa.h"
+
+#if defined(__HIP__)
+#define FA_HD __host__ __device__
+#else
+#define FA_HD
+#endif
+
+namespace fa_sched {
+
+constexpr int kKeys = 64;        // keys per key tile (a unit)
+constexpr int kPairRows = 128;   // query rows of a tile, pair-split layout
+constexpr int kGridRows = 256;   // query rows of a tile, 256-row layout
+
+// The work of one workgroup: query rows [q0, q0 + rows) of head bh against
+// key tiles [kt0, kt1) (64 keys each).  slot < 0: the item covers every key
+// the rows see and writes O and L; slot >= 0: the item is one part of a
+// split key range and writes a partial result to workspace slot `slot`.
+struct PipeItem {
+  int bh, q0, kt0, kt1, slot;
+};
+
+// Stream-K schedule (persistent workgroups).  The work of a call is laid out
+// as one sequence of units, a unit being one 64-key tile of one query tile of
+// 64*tu rows (128 with the pair-split layout, 256 without): head by head,
+// and within a head the query tiles in zigzag order 0, nqt-1, 1, nqt-2, ...
+// (under the causal mask tile t needs min(tu(t+1), nkt) key tiles, so
+// neighbours in this order pair short and long tiles).  Each tile is preceded
+// by `lead` units that hold no work: they stand for the fixed cost of a
+// piece (loading Q and the first K/V tiles, writing the result), so that
+// chunks balance time rather than key tiles.  Chunk c of G holds units
+// [b(c), b(c+1)) with b(c) = floor(c*T/G); each workgroup runs one chunk.
+// A chunk is a list of pieces (a query tile's key range, or part of it); a
+// piece that covers its whole tile writes O and L, any other writes a
+// partial result to workspace slot 2c (the chunk's first piece) or 2c + 1
+// (its last), and fa_merge_stream combines the pieces of each cut tile.
+struct StreamPlan {
+  long long T;         // units in the call
+  long long per_head;  // units per head
+  long long cq;        // T / G
+  int cr;              // T % G
+  int G;               // chunks = workgroups, 1 <= G <= min(T, 65535)
+  int nqt, nkt;        // query tiles (64*tu rows), key tiles (64 keys)
+  int tu;              // key tiles per query tile on the causal diagonal: 2 or 4
+  int lead;            // empty units before each tile
+};
+
+// Layout of the stream schedule's kernel: D = 128 runs 128-row tiles
+// (pair-split), D = 64, whose blocks are half as long, 256-row tiles, which
+// share the per-step costs between two blocks.
+constexpr bool stream_pair(int D) { return D == 128; }
+
+// Lead units of a tile: about a piece's fixed cost (loading Q and the first
+// K/V tiles, the end-of-piece barriers and stores) in key tiles of its
+// layout; timed per piece on MI355X at about 14k cycles for D = 128 against
+// 2.3k per key tile, 7.5k against 3k for D = 64.  Throughput is flat within
+// a few units of these values; 0 (no lead) loses up to 20% on small causal
+// problems.
+constexpr int stream_lead(int D) { return D == 128 ? 5 : 6; }
+
+// Key tiles of query tile t.
+FA_HD inline int tile_w(int t, int nkt, int tu, bool causal) {
+  return causal ? (tu * (t + 1) < nkt ? tu * (t + 1) : nkt) : nkt;
+}
+
+// Units of query tiles 0..t-1.
+FA_HD inline long long prefix_nat(int t, int nkt, int tu, bool causal) {
+  if (!causal) return (long long)t * nkt;
+  const int a = nkt / tu;  // tiles i < a have tu*(i+1) <= nkt key tiles
+  if (t <= a) return (long long)tu * t * (t + 1) / 2;
+  return (long long)tu * a * (a + 1) / 2 + (long long)(t - a) * nkt;
+}
+
+// Query tile at zigzag position o, and units of positions 0..o-1 (their key
+// tiles and lead units).
+FA_HD inline int zz_tile(int o, int nqt) {
+  return (o & 1) ? nqt - 1 - (o >> 1) : (o >> 1);
+}
+FA_HD inline long long zz_prefix(int o, int nqt, int nkt, int tu, int lead,
+                                               bool causal) {
+  return prefix_nat((o + 1) >> 1, nkt, tu, causal) +
+         (prefix_nat(nqt, nkt, tu, causal) - prefix_nat(nqt - (o >> 1), nkt, tu, causal)) +
+         (long long)lead * o;
+}
+
+// Zigzag position of the tile holding head-relative unit r (0 <= r < per_head).
+FA_HD inline int zz_find(long long r, int nqt, int nkt, int tu, int lead,
+                                       bool causal) {
+  int lo = 0, hi = nqt - 1;  // zz_prefix(lo) <= r always holds
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (zz_prefix(mid, nqt, nkt, tu, lead, causal) <= r)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+// floor(c * T / G), without 64-bit division (c * cr < G^2 < 2^32).
+FA_HD inline long long chunk_start(const StreamPlan &sp, int c) {
+  return (long long)c * sp.cq + (long long)((uint32_t)c * (uint32_t)sp.cr / (uint32_t)sp.G);
+}
+
+// The pieces of chunk ch, in order: next() yields each piece that holds key
+// tiles (a chunk may also cover lead units only) as a PipeItem with query
+// tile index t (rows t*64*tu ...).
+struct ChunkWalk {
+  long long left;  // units of the chunk not walked yet
+  int ch, bh, zo, u;
+  bool first;
+
+  FA_HD void init(const StreamPlan &sp, int chunk, bool causal) {
+    ch = chunk;
+    const long long u0 = chunk_start(sp, ch);
+    left = chunk_start(sp, ch + 1) - u0;
+    // position of the chunk's first unit: head, zigzag tile position, unit
+    // within the tile's lead units and key tiles
+    bh = (int)(u0 / sp.per_head);
+    const long long r0 = u0 - (long long)bh * sp.per_head;
+    zo = zz_find(r0, sp.nqt, sp.nkt, sp.tu, sp.lead, causal);
+    u = (int)(r0 - zz_prefix(zo, sp.nqt, sp.nkt, sp.tu, sp.lead, causal));
+    first = true;
+  }
+
+  FA_HD bool next(const StreamPlan &sp, bool causal, PipeItem &it, int &t) {
+    const int E = sp.lead;
+    while (left > 0) {
+      t = zz_tile(zo, sp.nqt);
+      const int w = tile_w(t, sp.nkt, sp.tu, causal);
+      const int u1 = left < (long long)(E + w - u) ? u + (int)left : E + w;
+      const int kt0 = u > E ? u - E : 0;
+      const int kt1 = u1 > E ? u1 - E : 0;
+      left -= u1 - u;
+      u = 0;  // the next piece starts a tile
+      const int bh_t = bh;
+      if (++zo == sp.nqt) {
+        zo = 0;
+        ++bh;
+      }
+      if (kt1 > kt0) {
+        it.bh = bh_t;
+        it.kt0 = kt0;
+        it.kt1 = kt1;
+        it.slot = (kt0 == 0 && kt1 == w) ? -1 : 2 * ch + (first ? 0 : 1);
+        first = false;
+        return true;
+      }
+    }
+    return false;
+  }
+};
+
+// The query tile holding the first unit of chunk j, and whether boundary j
+// cuts it (lies after its first key tile, with no earlier boundary doing
+// so).  Its pieces: chunk j-1 (its first piece when it starts at the tile
+// or in its lead units, else its last), then every chunk c >= j that starts
+// before the tile's end (its first piece).
+struct CutTile {
+  long long sl0, s0, s1;  // the tile's lead units, first key tile, end
+  long long bprev;        // first unit of chunk j-1
+  int bh, t, j;
+  bool cut;
+
+  FA_HD void init(const StreamPlan &sp, int jj, bool causal) {
+    j = jj;
+    const long long bj = chunk_start(sp, j);
+    bh = (int)(bj / sp.per_head);
+    const long long base = (long long)bh * sp.per_head;
+    const int zo = zz_find(bj - base, sp.nqt, sp.nkt, sp.tu, sp.lead, causal);
+    t = zz_tile(zo, sp.nqt);
+    sl0 = base + zz_prefix(zo, sp.nqt, sp.nkt, sp.tu, sp.lead, causal);
+    s0 = sl0 + sp.lead;
+    s1 = s0 + tile_w(t, sp.nkt, sp.tu, causal);
+    bprev = chunk_start(sp, j - 1);
+    cut = bj > s0 && bprev <= s0;
+  }
+  // Workspace slot of the tile's piece in chunk cc (cc = j-1, j, j+1, ...),
+  // -1 past its last piece.
+  FA_HD int slot(const StreamPlan &sp, int cc) const {
+    if (cc >= sp.G || (cc >= j && chunk_start(sp, cc) >= s1)) return -1;
+    return (cc == j - 1 && bprev < sl0) ? 2 * cc + 1 : 2 * cc;
+  }
+};
+
+// Cut query tiles of a stream-K schedule, named by the first chunk boundary
+// j that falls strictly inside each (host-computed).
+constexpr int kMaxChunks = 1024;
+struct CutList {
+  int n;
+  uint16_t j[kMaxChunks - 1];
+};
+
+// Stream-K schedule of the pipelined kernel (16-bit inputs, D >= 64): one
+// chunk per compute unit.  With four or more 128-row query tiles per compute
+// unit the longest-first grid of fa_fwd already keeps every unit busy to the
+// end, and a chunk would hold many pieces, each paying its own prologue: the
+// call then takes that grid.  Returns false for the paths that take no
+// workspace.
+inline bool make_plan(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, int dtype, bool causal,
+               int cus, StreamPlan &sp, size_t &ws_bytes) {
+  ws_bytes = 0;
+  if (dtype == FA_F32 || D < 64 || cus < 1) return false;
+  const int64_t pair_rows = kPairRows;
+  if (BH * ((Nq + pair_rows - 1) / pair_rows) >= 4 * (int64_t)cus) return false;
+  const int64_t qt = stream_pair((int)D) ? pair_rows : kGridRows;
+  const int nkt = (int)((Nk + kKeys - 1) / kKeys);
+  const int nqt = (int)((Nq + qt - 1) / qt);
+  sp.tu = (int)(qt / kKeys);
+  sp.nqt = nqt;
+  sp.nkt = nkt;
+  sp.lead = stream_lead((int)D);
+  sp.per_head = prefix_nat(nqt, nkt, sp.tu, causal) + (long long)sp.lead * nqt;
+  sp.T = BH * sp.per_head;
+  const int gmax = cus < kMaxChunks ? cus : kMaxChunks;
+  sp.G = (int)(sp.T < gmax ? sp.T : gmax);
+  sp.cq = sp.T / sp.G;
+  sp.cr = (int)(sp.T % sp.G);
+  ws_bytes = (size_t)2 * sp.G * qt * (size_t)(D + 4) * 4;
+  return true;
+}
+
+// The cut tiles of a schedule (CutTile::cut for j = 1 .. G-1).
+inline void make_cuts(const StreamPlan &sp, bool causal, CutList &cl) {
+  cl.n = 0;
+  for (int j = 1; j < sp.G; ++j) {
+    CutTile ct;
+    ct.init(sp, j, causal);
+    if (ct.cut) cl.j[cl.n++] = (uint16_t)j;
+  }
+}
+
+
+}  // namespace fa_sched
