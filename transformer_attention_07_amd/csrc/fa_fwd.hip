@@ -412,34 +412,38 @@ __device__ __forceinline__ u32x2 read_tr16(const lds_char *p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
-// s_waitcnt vmcnt(N) (gfx9 encoding); with LGKM0 also lgkmcnt(0).
+// s_waitcnt vmcnt(N) lgkmcnt(L) (gfx9 encoding; L = 15: no LDS wait).
+template <int N, int L = 15>
+__device__ __forceinline__ void wait_counts() {
+  static_assert(N >= 0 && N < 64 && L >= 0 && L < 16, "counter range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (L << 8));
+}
 template <int N, bool LGKM0 = false>
 __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) |
-                             (LGKM0 ? 0 : (0xF << 8)));
+  wait_counts<N, LGKM0 ? 0 : 15>();
 }
 
 // Workgroup barrier for the DMA ring.  Waits until at most N of this wave's
-// buffer loads are in flight and all of its LDS reads have returned, then
-// meets the other waves.  No memory fence: a workgroup fence would wait for
-// every load in flight (vmcnt(0)) and drain the ring.  The empty asm
-// statements keep the compiler from moving LDS accesses across.
-template <int N>
+// buffer loads are in flight and all of its LDS reads but the L youngest
+// have returned (LDS accesses of a wave complete in order), then meets the
+// other waves.  No memory fence: a workgroup fence would wait for every
+// load in flight (vmcnt(0)) and drain the ring.  The empty asm statements
+// keep the compiler from moving LDS accesses across.
+template <int N, int L = 0>
 __device__ __forceinline__ void ring_barrier() {
-  wait_vmcnt<N, true>();
+  wait_counts<N, L>();
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
 // Ring wait with one per-wave load count for every wave.
-template <int N>
+template <int N, int L = 0>
 __device__ __forceinline__ void ring_barrier_sel(bool one) {
   if (one)
-    ring_barrier<N>();
+    ring_barrier<N, L>();
   else
-    ring_barrier<0>();
+    ring_barrier<0, L>();
 }
 
 // 16-byte buffer load into registers, as asm: the compiler does not count it
@@ -511,6 +515,10 @@ struct Pipe {
   f32x16 acc[NDB];
   f32x16 S0, S1;      // S^T blocks (alternate between the two blocks of a tile)
   frag P0[2], P1[2];  // P blocks rounded to T (alternate likewise)
+  // First K and V fragments of the wave's next block, read during the tail
+  // of the current one (blocks chained with PRE)
+  static constexpr int PF = QF < 3 ? QF : 3;
+  frag kpre[PF], vpre[PF];
   float m_use;
   float l;   // half-wave sum of p (fp32): gives L
   float lr;  // half-wave sum of p as rounded to T for P.V: normalises O
@@ -587,11 +595,18 @@ struct Pipe {
   // 0), and a row that has not seen a key yet shifts by 0 instead of
   // -(-inf).  One code path serves masked and unmasked blocks, so the
   // accumulators stay in the same registers from block to block.
+  // PRE: the first PF fragments of this block were read ahead into kpre
+  // and vpre, and this block reads those of the next one (kpn, vpn) in its
+  // last MFMA slots.
+  template <bool PRE = false>
   __device__ __forceinline__ void block_step(const lds_char *kp, const lds_char *vp,
                                              f32x16 &sin, f32x16 &sout,
-                                             const frag (&pin)[2], frag (&pout)[2]) {
+                                             const frag (&pin)[2], frag (&pout)[2],
+                                             const lds_char *kpn = nullptr,
+                                             const lds_char *vpn = nullptr) {
     constexpr int NCHUNK = 15;
     frag kf[QF], vf[NPV];
+    static_assert(NPV == QF, "one K.Q^T and one P.V per slot pair");
     float mx = 0.f, nm = 0.f, alpha = 1.f;
     float m3[5];               // partial maxima
     float ea[2], pb[2];        // pair in flight: exponents, then p
@@ -668,24 +683,29 @@ struct Pipe {
     };
 
     // fragments are read PF MFMA pairs ahead
-    constexpr int PF = QF < 3 ? QF : 3;
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-      kf[i] = kfrag(kp, i);
-      vf[i] = vfrag(vp, i);
+      kf[i] = PRE ? kpre[i] : kfrag(kp, i);
+      vf[i] = PRE ? vpre[i] : vfrag(vp, i);
     }
 #pragma unroll
     for (int i = 0; i < QF; ++i) {
       // K.Q^T, then a slice of the softmax
       sout = Mfma16<T>::mma(kf[i], qf[i], sout);
-      if (i + PF < QF) kf[i + PF] = kfrag(kp, i + PF);
+      if (i + PF < QF)
+        kf[i + PF] = kfrag(kp, i + PF);
+      else if (PRE)
+        kpre[i + PF - QF] = kfrag(kpn, i + PF - QF);
 #pragma unroll
       for (int ch = (2 * i) * NCHUNK / NSLOT; ch < (2 * i + 1) * NCHUNK / NSLOT; ++ch)
         chunk(ch);
       __builtin_amdgcn_sched_barrier(0);
       // P.V, then a slice of the softmax
       acc[i % NDB] = Mfma16<T>::mma(vf[i], pin[i / NDB], acc[i % NDB]);
-      if (i + PF < NPV) vf[i + PF] = vfrag(vp, i + PF);
+      if (i + PF < NPV)
+        vf[i + PF] = vfrag(vp, i + PF);
+      else if (PRE)
+        vpre[i + PF - NPV] = vfrag(vpn, i + PF - NPV);
 #pragma unroll
       for (int ch = (2 * i + 1) * NCHUNK / NSLOT; ch < (2 * i + 2) * NCHUNK / NSLOT; ++ch)
         chunk(ch);
@@ -719,6 +739,35 @@ struct Pipe {
       block_step(kp, vp, sin, sout, pin, pout);
     } else if (STRIDE > 0 && b - STRIDE <= lastb) {
       pv(vp, pin);
+    }
+  }
+  // The same for blocks chained by read-ahead (every block of the wave, no
+  // drain): the first fragments of this block are in kpre/vpre, and those of
+  // the next block (stages and halves given) are read during this one.  A
+  // block past lastb (causal) does nothing; every later one is past it too.
+  template <bool ODD>
+  __device__ __forceinline__ void block_pre(const lds_char *ring, int b, int lastb, int vst,
+                                            int vhalf, int kst, int khalf, int vst_n,
+                                            int vhalf_n, int kst_n, int khalf_n) {
+    f32x16 &sin = ODD ? S1 : S0;
+    f32x16 &sout = ODD ? S0 : S1;
+    frag(&pin)[2] = ODD ? P0 : P1;
+    frag(&pout)[2] = ODD ? P1 : P0;
+    if (b <= lastb) {
+      const int k0 = b * 32;
+      const bool need_mask = (k0 + 32 > Nk) || (CAUSAL && k0 + 31 > qw);
+      if (need_mask) mask(sin, k0);
+      block_step<true>(kptr(ring, kst, khalf), vptr(ring, vst, vhalf), sin, sout, pin, pout,
+                       kptr(ring, kst_n, khalf_n), vptr(ring, vst_n, vhalf_n));
+    }
+  }
+  // Reads the first fragments of a block ahead (the first of a chain).
+  __device__ __forceinline__ void read_ahead(const lds_char *ring, int vst, int vhalf, int kst,
+                                             int khalf) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      kpre[i] = kfrag(kptr(ring, kst, khalf), i);
+      vpre[i] = vfrag(vptr(ring, vst, vhalf), i);
     }
   }
 };
@@ -943,8 +992,17 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
     // flight.  Step r requests unit r+3: K(r+3) into the stage of K(r-1) and
     // V(r+2) into the stage of V(r-2), both last read in step r-1.  Every
     // wave runs every step so that the loads and barriers line up.
+    //
+    // Each block reads the first fragments of the next one during its last
+    // MFMAs (both tiles are in LDS by then: block 2r+1 reads K(r+1), V(r),
+    // and block 2r+2 of the next step the other halves of the same tiles),
+    // so a block never starts on a fresh LDS round trip.  Those reads are
+    // the wave's youngest LDS accesses at the next barrier, which lets them
+    // stay in flight: they touch neither stage the next unit overwrites.
+    constexpr int RA = 3 * P::PF;  // LDS reads of one read-ahead
+    s.read_ahead(ring, kStages - 1, 1, 0, 1);
     for (int r = 0; r < ntiles; ++r) {
-      ring_barrier_sel<UNIT>(r + 2 <= ntiles);
+      ring_barrier_sel<UNIT, RA>(r + 2 <= ntiles);
       if (r + 3 <= ntiles)
         dm.issue(k_rs, v_rs, kt0 + r + 3, (r + 3) & (kStages - 1), kt0 + r + 2,
                  (r + 2) & (kStages - 1));
@@ -952,8 +1010,8 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
       const int stm = (r + kStages - 1) & (kStages - 1);
       const int st1 = (r + 1) & (kStages - 1);
       const int b = 2 * (kt0 + r);
-      s.template block<false, 0>(ring, b, lastb, stm, 1, st0, 1);
-      s.template block<true, 0>(ring, b + 1, lastb, st0, 0, st1, 0);
+      s.template block_pre<false>(ring, b, lastb, stm, 1, st0, 1, st0, 0, st1, 0);
+      s.template block_pre<true>(ring, b + 1, lastb, st0, 0, st1, 0, st0, 1, st1, 1);
     }
     // Drain: P.V of the wave's last block (its P sits in P0 for an even
     // block, P1 for an odd one).  The last step's wait covered every unit
