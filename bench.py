@@ -32,13 +32,17 @@ METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak (B8 N4096 D128 causal)"
 # MI355X published dense peaks (TFLOP/s).
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
 HBM_GBPS = 8000.0
-SOURCE = os.path.join(ROOT, "transformer_attention_07_amd", "csrc", "fa_fwd.hip")
+CSRC = os.path.join(ROOT, "transformer_attention_07_amd", "csrc")
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
 def source_digest() -> str:
-    with open(SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 over the kernel sources (csrc/*, in name order)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload: str):
