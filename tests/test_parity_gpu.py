@@ -239,6 +239,10 @@ SPLIT = [
     (1, 1, 3000, 1000, 128),
     (2, 1, 1500, 1700, 64),
     (1, 3, 777, 4100, 128),
+    # D = 128 with at least one 256-row tile per compute unit: the schedule
+    # takes 256-row tiles (on a 256-CU device)
+    (20, 13, 300, 700, 128),
+    (2, 65, 512, 1000, 128),
 ]
 
 

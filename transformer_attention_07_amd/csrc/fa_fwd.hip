@@ -1384,18 +1384,28 @@ hipError_t launch16(const Launch &a) {
     const int neg = a.c < 0.f ? 1 : 0;
     if (a.plan) {
       const StreamPlan &sp = *a.plan;
-      constexpr bool PAIR = stream_pair(D);
-      hipLaunchKernelGGL((fa_fwd_stream<T, OT, D, CAUSAL, PAIR>), dim3((unsigned)sp.G),
-                         dim3(kThreads8), 0, a.stream, (const T *)a.q, (const T *)a.k,
-                         (const T *)a.v, (OT *)a.o, a.lse, a.ws, a.Nq, a.Nk, c, neg, sp);
-      hipError_t e = hipGetLastError();
+      // the plan's tile height selects the layout (pair-split: 128 rows)
+      auto go = [&](auto pair) -> hipError_t {
+        constexpr bool PAIR = decltype(pair)::value;
+        hipLaunchKernelGGL((fa_fwd_stream<T, OT, D, CAUSAL, PAIR>), dim3((unsigned)sp.G),
+                           dim3(kThreads8), 0, a.stream, (const T *)a.q, (const T *)a.k,
+                           (const T *)a.v, (OT *)a.o, a.lse, a.ws, a.Nq, a.Nk, c, neg, sp);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        if (a.cuts && a.cuts->n > 0) {
+          hipLaunchKernelGGL((fa_merge_stream<OT, D, CAUSAL, QRows<PAIR>::value>),
+                             dim3((unsigned)(a.cuts->n * (QRows<PAIR>::value / kMergeRows))),
+                             dim3(kThreads), 0, a.stream, (const float *)a.ws, (OT *)a.o,
+                             a.lse, a.Nq, sp, *a.cuts);
+        }
+        return hipSuccess;
+      };
+      hipError_t e;
+      if constexpr (D == 128)
+        e = sp.tu == kPairRows / kKeys ? go(std::true_type{}) : go(std::false_type{});
+      else
+        e = go(std::false_type{});
       if (e != hipSuccess) return e;
-      if (a.cuts && a.cuts->n > 0) {
-        hipLaunchKernelGGL((fa_merge_stream<OT, D, CAUSAL, QRows<PAIR>::value>),
-                           dim3((unsigned)(a.cuts->n * (QRows<PAIR>::value / kMergeRows))),
-                           dim3(kThreads), 0, a.stream, (const float *)a.ws, (OT *)a.o,
-                           a.lse, a.Nq, sp, *a.cuts);
-      }
     } else {
       hipLaunchKernelGGL((fa_fwd_pipe8<T, OT, D, CAUSAL, false>),
                          dim3((unsigned)(a.BH * a.nqtg)), dim3(kThreads8), 0, a.stream,

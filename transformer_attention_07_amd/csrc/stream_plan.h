@@ -58,18 +58,24 @@ struct StreamPlan {
   int lead;            // empty units before each tile
 };
 
-// Layout of the stream schedule's kernel: D = 128 runs 128-row tiles
-// (pair-split), D = 64, whose blocks are half as long, 256-row tiles, which
-// share the per-step costs between two blocks.
-constexpr bool stream_pair(int D) { return D == 128; }
+// Layout of the stream schedule's kernel: 256-row tiles (every wave runs
+// both blocks of a step) unless D = 128 and there are fewer 256-row tiles
+// than compute units, where the pair-split 128-row layout, twice as many
+// workgroups per row, balances better (measured on MI355X: 256-row +6% at
+// one tile per CU, pair-split +5% at half a tile per CU and +15% at an
+// eighth).  D = 64 always takes 256-row tiles: its blocks are half as long,
+// so sharing the per-step costs between two blocks matters more.
+inline bool stream_pair(int64_t BH, int64_t Nq, int64_t D, int cus) {
+  return D == 128 && BH * ((Nq + kGridRows - 1) / kGridRows) < (int64_t)cus;
+}
 
 // Lead units of a tile: about a piece's fixed cost (loading Q and the first
 // K/V tiles, the end-of-piece barriers and stores) in key tiles of its
 // layout; timed per piece on MI355X at about 14k cycles for D = 128 against
-// 2.3k per key tile, 7.5k against 3k for D = 64.  Throughput is flat within
-// a few units of these values; 0 (no lead) loses up to 20% on small causal
-// problems.
-constexpr int stream_lead(int D) { return D == 128 ? 5 : 6; }
+// 2.3k per 128-row key tile (4.5k per 256-row one), 7.5k against 3k for
+// D = 64.  Throughput is flat within a few units of these values; 0 (no
+// lead) loses up to 20% on small causal problems.
+constexpr int stream_lead(int D, bool pair) { return D == 128 ? (pair ? 5 : 4) : 6; }
 
 // Key tiles of query tile t.
 FA_HD inline int tile_w(int t, int nkt, int tu, bool causal) {
@@ -216,13 +222,14 @@ inline bool make_plan(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, int dtype, 
   if (dtype == FA_F32 || D < 64 || cus < 1) return false;
   const int64_t pair_rows = kPairRows;
   if (BH * ((Nq + pair_rows - 1) / pair_rows) >= 4 * (int64_t)cus) return false;
-  const int64_t qt = stream_pair((int)D) ? pair_rows : kGridRows;
+  const bool pair = stream_pair(BH, Nq, D, cus);
+  const int64_t qt = pair ? pair_rows : kGridRows;
   const int nkt = (int)((Nk + kKeys - 1) / kKeys);
   const int nqt = (int)((Nq + qt - 1) / qt);
   sp.tu = (int)(qt / kKeys);
   sp.nqt = nqt;
   sp.nkt = nkt;
-  sp.lead = stream_lead((int)D);
+  sp.lead = stream_lead((int)D, pair);
   sp.per_head = prefix_nat(nqt, nkt, sp.tu, causal) + (long long)sp.lead * nqt;
   sp.T = BH * sp.per_head;
   const int gmax = cus < kMaxChunks ? cus : kMaxChunks;
