@@ -1,6 +1,6 @@
 // Host check of the stream-K schedule of fa_fwd_ws (make_plan, ChunkWalk,
 // CutTile, make_cuts of csrc/stream_plan.h, the code the kernels and the
-// host planner run): for many shapes and
+// host planner run): for many shapes, lead and tail units and
 // compute-unit counts, every key tile of every query tile is covered by
 // exactly one piece, pieces that do not cover their whole tile write to
 // distinct workspace slots, those tiles are exactly the cut list, and the
@@ -23,13 +23,16 @@ struct Piece {
   int ch, kt0, kt1, slot;
 };
 
-int check(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, bool causal, int cus, int lead) {
+int check(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, bool causal, int cus, int lead,
+          int tail) {
   StreamPlan sp;
   size_t ws = 0;
   if (!make_plan(BH, Nq, Nk, D, FA_BF16, causal, cus, sp, ws)) return 0;
-  if (lead >= 0) {  // the same plan with another lead
+  if (lead >= 0) {  // the same plan with other lead and tail units
     sp.lead = lead;
-    sp.per_head = prefix_nat(sp.nqt, sp.nkt, sp.tu, causal) + (long long)sp.lead * sp.nqt;
+    sp.tail = tail;
+    sp.per_head =
+        prefix_nat(sp.nqt, sp.nkt, sp.tu, causal) + (long long)(sp.lead + sp.tail) * sp.nqt;
     sp.T = BH * sp.per_head;
     const int gmax = cus < kMaxChunks ? cus : kMaxChunks;
     sp.G = (int)(sp.T < gmax ? sp.T : gmax);
@@ -38,9 +41,10 @@ int check(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, bool causal, int cus, i
   }
   const int qt = sp.tu * kKeys;
   auto fail = [&](const char *what, long long a, long long b) {
-    printf("FAIL %s (%lld, %lld): BH=%lld Nq=%lld Nk=%lld D=%lld causal=%d cus=%d lead=%d G=%d\n",
+    printf("FAIL %s (%lld, %lld): BH=%lld Nq=%lld Nk=%lld D=%lld causal=%d cus=%d lead=%d "
+           "tail=%d G=%d\n",
            what, a, b, (long long)BH, (long long)Nq, (long long)Nk, (long long)D, (int)causal,
-           cus, sp.lead, sp.G);
+           cus, sp.lead, sp.tail, sp.G);
     return -1;
   };
   if (sp.nqt != (int)((Nq + qt - 1) / qt)) return fail("nqt", sp.nqt, qt);
@@ -106,15 +110,15 @@ int main() {
   int n = 0;
   const int64_t Ns[] = {1, 33, 64, 127, 128, 129, 255, 256, 300, 1000, 2048, 3000, 4096, 8192};
   const int cuss[] = {1, 3, 8, 80, 256, 304, 1024};
-  const int leads[] = {-1, 0, 1, 5, 17};
+  const int leads[][2] = {{-1, 0}, {0, 0}, {1, 0}, {5, 0}, {17, 0}, {0, 3}, {5, 2}, {6, 9}};
   for (int64_t BH : {1, 2, 3, 8})
     for (int64_t Nq : Ns)
       for (int64_t Nk : {(int64_t)1, (int64_t)63, (int64_t)500, (int64_t)4096, Nq})
         for (int64_t D : {64, 128})
           for (int causal = 0; causal < 2; ++causal)
             for (int cus : cuss)
-              for (int lead : leads) {
-                const int r = check(BH, Nq, Nk, D, causal != 0, cus, lead);
+              for (const auto &lt : leads) {
+                const int r = check(BH, Nq, Nk, D, causal != 0, cus, lt[0], lt[1]);
                 if (r < 0) return 1;
                 n += r;
               }

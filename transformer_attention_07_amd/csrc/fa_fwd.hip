@@ -1147,11 +1147,15 @@ __global__ __launch_bounds__(kThreads8) void fa_fwd_stream(
 }
 
 // Combines the pieces of the cut query tiles (CutTile), one workgroup per
-// kMergeRows rows of a tile, with a_i = 2^(m_i - M), M = max_i m_i:
+// merge_rows<D>() rows of a tile, with a_i = 2^(m_i - M), M = max_i m_i:
 // O = sum_i a_i lr_i O_i / sum_i a_i lr_i, L = ln2 * (M + log2 sum_i a_i l_i).
 // Each thread owns one 4-wide column slice of NR rows and loads two pieces
 // per round trip.
-constexpr int kMergeRows = 16;
+// (16 rows at D = 128, 64 at D = 64: measured fastest on MI355X; the
+// workgroup's fixed cost of locating the tile weighs against fewer loads
+// in flight per thread)
+template <int D>
+constexpr int merge_rows() { return D == 128 ? 16 : 64; }
 
 template <typename OT, int D, bool CAUSAL, int QT>
 __global__ __launch_bounds__(kThreads) void fa_merge_stream(const float *__restrict__ ws,
@@ -1160,8 +1164,8 @@ __global__ __launch_bounds__(kThreads) void fa_merge_stream(const float *__restr
                                                             StreamPlan sp, CutList cuts) {
   constexpr int C4 = D / 4;           // float4 per row
   constexpr int RPP = kThreads / C4;  // rows per pass of the workgroup
-  constexpr int SPLIT = QT / kMergeRows;
-  constexpr int ROWS = kMergeRows;
+  constexpr int SPLIT = QT / merge_rows<D>();
+  constexpr int ROWS = merge_rows<D>();
   constexpr int NR = ROWS / RPP;      // rows per thread
   static_assert(NR >= 1 && ROWS % RPP == 0, "merge tiling");
   CutTile ct;
@@ -1394,7 +1398,7 @@ hipError_t launch16(const Launch &a) {
         if (e != hipSuccess) return e;
         if (a.cuts && a.cuts->n > 0) {
           hipLaunchKernelGGL((fa_merge_stream<OT, D, CAUSAL, QRows<PAIR>::value>),
-                             dim3((unsigned)(a.cuts->n * (QRows<PAIR>::value / kMergeRows))),
+                             dim3((unsigned)(a.cuts->n * (QRows<PAIR>::value / merge_rows<D>()))),
                              dim3(kThreads), 0, a.stream, (const float *)a.ws, (OT *)a.o,
                              a.lse, a.Nq, sp, *a.cuts);
         }

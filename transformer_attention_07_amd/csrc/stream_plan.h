@@ -56,6 +56,7 @@ struct StreamPlan {
   int nqt, nkt;        // query tiles (64*tu rows), key tiles (64 keys)
   int tu;              // key tiles per query tile on the causal diagonal: 2 or 4
   int lead;            // empty units before each tile
+  int tail;            // empty units after each tile
 };
 
 // Layout of the stream schedule's kernel: 256-row tiles (every wave runs
@@ -76,6 +77,14 @@ inline bool stream_pair(int64_t BH, int64_t Nq, int64_t D, int cus) {
 // D = 64.  Throughput is flat within a few units of these values; 0 (no
 // lead) loses up to 20% on small causal problems.
 constexpr int stream_lead(int D, bool pair) { return D == 128 ? (pair ? 5 : 4) : 6; }
+// Tail units of a causal tile: the extra cost of its diagonal key tiles
+// (the last tu, partly masked; a wave whose rows end early waits for the
+// others at each of them).  A per-workgroup timing fit at the headline
+// shape (time = 1.8k + 2.2k per key tile + 14.4k per piece + 3.7k per
+// diagonal key tile, cycles) suggested lead 3 and tail 4 for the pair-split
+// layout; measured, that was within noise of lead 5 and tail 0 and 3%
+// slower on B4 N2048, so no tail is used.
+constexpr int stream_tail(int, bool) { return 0; }
 
 // Key tiles of query tile t.
 FA_HD inline int tile_w(int t, int nkt, int tu, bool causal) {
@@ -137,8 +146,8 @@ struct ChunkWalk {
     // within the tile's lead units and key tiles
     bh = (int)(u0 / sp.per_head);
     const long long r0 = u0 - (long long)bh * sp.per_head;
-    zo = zz_find(r0, sp.nqt, sp.nkt, sp.tu, sp.lead, causal);
-    u = (int)(r0 - zz_prefix(zo, sp.nqt, sp.nkt, sp.tu, sp.lead, causal));
+    zo = zz_find(r0, sp.nqt, sp.nkt, sp.tu, sp.lead + sp.tail, causal);
+    u = (int)(r0 - zz_prefix(zo, sp.nqt, sp.nkt, sp.tu, sp.lead + sp.tail, causal));
     first = true;
   }
 
@@ -147,9 +156,10 @@ struct ChunkWalk {
     while (left > 0) {
       t = zz_tile(zo, sp.nqt);
       const int w = tile_w(t, sp.nkt, sp.tu, causal);
-      const int u1 = left < (long long)(E + w - u) ? u + (int)left : E + w;
-      const int kt0 = u > E ? u - E : 0;
-      const int kt1 = u1 > E ? u1 - E : 0;
+      const int span = E + w + sp.tail;
+      const int u1 = left < (long long)(span - u) ? u + (int)left : span;
+      const int kt0 = u <= E ? 0 : (u - E < w ? u - E : w);
+      const int kt1 = u1 <= E ? 0 : (u1 - E < w ? u1 - E : w);
       left -= u1 - u;
       u = 0;  // the next piece starts a tile
       const int bh_t = bh;
@@ -172,9 +182,10 @@ struct ChunkWalk {
 
 // The query tile holding the first unit of chunk j, and whether boundary j
 // cuts it (lies after its first key tile, with no earlier boundary doing
-// so).  Its pieces: chunk j-1 (its first piece when it starts at the tile
-// or in its lead units, else its last), then every chunk c >= j that starts
-// before the tile's end (its first piece).
+// so).  Its pieces: chunk j-1 (its first piece when it starts at the tile,
+// in its lead units or in the previous tile's tail units, else its last),
+// then every chunk c >= j that starts before the tile's last key tile ends
+// (its first piece).
 struct CutTile {
   long long sl0, s0, s1;  // the tile's lead units, first key tile, end
   long long bprev;        // first unit of chunk j-1
@@ -186,19 +197,22 @@ struct CutTile {
     const long long bj = chunk_start(sp, j);
     bh = (int)(bj / sp.per_head);
     const long long base = (long long)bh * sp.per_head;
-    const int zo = zz_find(bj - base, sp.nqt, sp.nkt, sp.tu, sp.lead, causal);
+    const int zo = zz_find(bj - base, sp.nqt, sp.nkt, sp.tu, sp.lead + sp.tail, causal);
     t = zz_tile(zo, sp.nqt);
-    sl0 = base + zz_prefix(zo, sp.nqt, sp.nkt, sp.tu, sp.lead, causal);
+    sl0 = base + zz_prefix(zo, sp.nqt, sp.nkt, sp.tu, sp.lead + sp.tail, causal);
     s0 = sl0 + sp.lead;
     s1 = s0 + tile_w(t, sp.nkt, sp.tu, causal);
     bprev = chunk_start(sp, j - 1);
-    cut = bj > s0 && bprev <= s0;
+    cut = bj > s0 && bj < s1 && bprev <= s0;
   }
   // Workspace slot of the tile's piece in chunk cc (cc = j-1, j, j+1, ...),
   // -1 past its last piece.
   FA_HD int slot(const StreamPlan &sp, int cc) const {
     if (cc >= sp.G || (cc >= j && chunk_start(sp, cc) >= s1)) return -1;
-    return (cc == j - 1 && bprev < sl0) ? 2 * cc + 1 : 2 * cc;
+    // chunk j-1 holds key tiles of an earlier tile (this one is then its
+    // last piece) iff it starts before the end of the previous tile's key
+    // tiles, tail units before this tile's lead
+    return (cc == j - 1 && bprev < sl0 - sp.tail) ? 2 * cc + 1 : 2 * cc;
   }
 };
 
@@ -230,7 +244,8 @@ inline bool make_plan(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, int dtype, 
   sp.nqt = nqt;
   sp.nkt = nkt;
   sp.lead = stream_lead((int)D, pair);
-  sp.per_head = prefix_nat(nqt, nkt, sp.tu, causal) + (long long)sp.lead * nqt;
+  sp.tail = causal ? stream_tail((int)D, pair) : 0;
+  sp.per_head = prefix_nat(nqt, nkt, sp.tu, causal) + (long long)(sp.lead + sp.tail) * nqt;
   sp.T = BH * sp.per_head;
   const int gmax = cus < kMaxChunks ? cus : kMaxChunks;
   sp.G = (int)(sp.T < gmax ? sp.T : gmax);
