@@ -207,6 +207,54 @@ template <> __device__ __forceinline__ void store4<_Float16>(_Float16 *dst, f32x
 
 // Writes O = acc / lo (rows < Nq) and L = ln2 * (m + log2 l).  l and lo are
 // half-wave partial sums; lo is the normaliser of O (by default l itself).
+// Four values in a storage type, as the raw register words a store takes.
+template <typename OT> struct Pack4;
+template <> struct Pack4<float> {
+  typedef u32x4 type;
+  static __device__ __forceinline__ type pack(f32x4 v) { return __builtin_bit_cast(u32x4, v); }
+};
+template <> struct Pack4<__bf16> {
+  typedef u32x2 type;
+  static __device__ __forceinline__ type pack(f32x4 v) {
+    return __builtin_bit_cast(u32x2, __builtin_convertvector(v, bf16x4));
+  }
+};
+template <> struct Pack4<_Float16> {
+  typedef u32x2 type;
+  static __device__ __forceinline__ type pack(f32x4 v) {
+    return __builtin_bit_cast(u32x2, __builtin_convertvector(v, f16x4));
+  }
+};
+
+// Stores a lane's row values (acc * inv) from registers that nothing
+// overwrites afterwards: every value is computed before the first store.
+// Computing each store's data into the same few registers made each one
+// wait until the previous store had read its data, which under load from
+// other waves serialised the stores.
+template <typename OT, int NDB>
+__device__ __forceinline__ void store_row(const f32x16 (&acc)[NDB], float inv, OT *orow, int g,
+                                          int dlim) {
+  typedef typename Pack4<OT>::type PT;
+  PT pk[NDB * 4];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 v = {acc[db][4 * r4 + 0] * inv, acc[db][4 * r4 + 1] * inv,
+                       acc[db][4 * r4 + 2] * inv, acc[db][4 * r4 + 3] * inv};
+      pk[db * 4 + r4] = Pack4<OT>::pack(v);
+    }
+#pragma unroll
+  for (int i = 0; i < NDB * 4; ++i) asm volatile("" : "+v"(pk[i]));
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d = db * 32 + 8 * r4 + 4 * g;
+      if (d < dlim) *reinterpret_cast<PT *>(orow + d) = pk[db * 4 + r4];
+    }
+}
+
 template <int D, typename OT>
 __device__ __forceinline__ void epilogue(const f32x16 (&acc)[(D < 32 ? 32 : D) / 32],
                                          float m, float l, OT *o, float *lse, int bh,
@@ -216,18 +264,7 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[(D < 32 ? 32 : D) /
   if (my_q >= Nq) return;
   const float inv = 1.0f / lot;
   OT *orow = o + ((size_t)bh * Nq + my_q) * D;
-#pragma unroll
-  for (int db = 0; db < (D < 32 ? 32 : D) / 32; ++db) {
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int d = db * 32 + 8 * r4 + 4 * g;
-      if (D >= 32 || d < D) {
-        f32x4 v = {acc[db][4 * r4 + 0] * inv, acc[db][4 * r4 + 1] * inv,
-                   acc[db][4 * r4 + 2] * inv, acc[db][4 * r4 + 3] * inv};
-        store4<OT>(orow + d, v);
-      }
-    }
-  }
+  store_row<OT, (D < 32 ? 32 : D) / 32>(acc, inv, orow, g, D);
   if (g == 0) lse[(size_t)bh * Nq + my_q] = (m + log2f(lt)) * 0.69314718055994531f;
 }
 
@@ -783,17 +820,7 @@ __device__ __forceinline__ void epilogue_partial(const f32x16 (&acc)[D / 32], fl
   const float lt = l + __shfl_xor(l, 32);
   const float lrt = lr + __shfl_xor(lr, 32);
   const float inv = lrt > 0.f ? 1.0f / lrt : 0.f;
-  float *orow = ws_o + (size_t)row * D;
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int d = db * 32 + 8 * r4 + 4 * g;
-      const f32x4 x = {acc[db][4 * r4 + 0] * inv, acc[db][4 * r4 + 1] * inv,
-                       acc[db][4 * r4 + 2] * inv, acc[db][4 * r4 + 3] * inv};
-      *reinterpret_cast<f32x4 *>(orow + d) = x;
-    }
-  }
+  store_row<float, D / 32>(acc, inv, ws_o + (size_t)row * D, g, D);
   if (g == 0) {
     const f32x4 st = {lrt > 0.f ? m : -INFINITY, lt, lrt, 0.f};
     *reinterpret_cast<f32x4 *>(ws_s + row * 4) = st;
