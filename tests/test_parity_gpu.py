@@ -317,3 +317,50 @@ def test_split_repeat_is_deterministic():
     a = run_gpu(q, k, v, True, torch.bfloat16, 0.1)
     b = run_gpu(q, k, v, True, torch.bfloat16, 0.1)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("shape", [(8, 1, 1024, 1024, 128, 1), (2, 3, 700, 900, 64, 0),
+                                   (4, 64, 512, 512, 128, 1)],
+                         ids=["stream-d128", "stream-d64", "grid-d128"])
+def test_graph_capture_replays_match_eager(shape):
+    """Both kernels of fa_fwd_ws are plain launches on the caller's stream (no
+    allocation, no memset), so a HIP graph captured around the call replays
+    it: every replay, with eager work on the same buffers in between, gives
+    the eager result bit for bit."""
+    B, H, Nq, Nk, D, causal = shape
+    q, k, v = (t.to(DEV) for t in gen_qkv(B, H, Nq, Nk, D, seed=B * H + Nq, dtype="bf16"))
+    code = fa.FA_BF16
+    nb = _ws_bytes(B, H, Nq, Nk, D, causal, code)
+    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=DEV)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=DEV)
+    scale = 1.0 / math.sqrt(D)
+
+    def call():
+        st = fa.fa_fwd_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                          lse.data_ptr(), B, H, Nq, Nk, D, scale, causal, code,
+                          ws.data_ptr(), nb, torch.cuda.current_stream().cuda_stream)
+        assert st == fa.FA_OK, fa.fa_status_str(st)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    want_o, want_l = o.clone(), lse.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for i in range(3):
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        ws.fill_(i)  # stale partials and counters must not leak into a replay
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, want_o), f"replay {i}: O differs from the eager call"
+        assert torch.equal(lse, want_l), f"replay {i}: L differs from the eager call"
+        call()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(o, want_o) and torch.equal(lse, want_l)
