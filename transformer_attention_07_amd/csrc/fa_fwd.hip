@@ -755,12 +755,10 @@ struct Pipe {
   }
 
   // Block b of this wave (its tile-local half and ring stages given): full
-  // step, masked step (causal diagonal / key tail), the drain (P.V of the
-  // wave's last block) or nothing.
-  // STRIDE: distance between this wave's consecutive blocks (1 when a wave
-  // takes every block, 2 when two waves share a query group by block parity).
-  // STRIDE 0: no drain here (the caller runs it after the ring loop).
-  template <bool ODD, int STRIDE = 1>
+  // step, masked step (causal diagonal / key tail), or nothing past the
+  // wave's last block (the caller runs the drain, the P.V of that last
+  // block, after the ring loop).
+  template <bool ODD>
   __device__ __forceinline__ void block(const lds_char *ring, int b, int lastb,
                                         int vst, int vhalf, int kst, int khalf) {
     f32x16 &sin = ODD ? S1 : S0;
@@ -774,8 +772,6 @@ struct Pipe {
       const bool need_mask = (k0 + 32 > Nk) || (CAUSAL && k0 + 31 > qw);
       if (need_mask) mask(sin, k0);
       block_step(kp, vp, sin, sout, pin, pout);
-    } else if (STRIDE > 0 && b - STRIDE <= lastb) {
-      pv(vp, pin);
     }
   }
   // The same for blocks chained by read-ahead (every block of the wave, no
@@ -1062,7 +1058,7 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
         dm.issue(k_rs, v_rs, kt0 + r + 3, (r + 3) & (kStages - 1), kt0 + r + 2,
                  (r + 2) & (kStages - 1));
       const int b = 2 * (kt0 + r) + h;
-      s.template block<decltype(odd)::value, 0>(ring, b, lastb, (r + kStages - 1) & (kStages - 1),
+      s.template block<decltype(odd)::value>(ring, b, lastb, (r + kStages - 1) & (kStages - 1),
                                                 h, (r + 1) & (kStages - 1), h);
     };
     for (int r = 0; r < ntiles; r += 2) {
