@@ -102,7 +102,7 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
 /*
  * fa_fwd_workspace_size -- device scratch bytes that fa_fwd_ws needs for
  * this problem on the current device (written to *bytes; 0 when fa_fwd_ws
- * takes the same path as fa_fwd: fp32 inputs, D < 64, or at least four
+ * takes the same path as fa_fwd: fp32 inputs, D = 16, or at least four
  * query tiles of 128 rows per compute unit, where one workgroup per tile
  * already keeps every unit busy).
  *
@@ -119,8 +119,8 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
  * update of (m, l, o_acc)).  Cutting the work along the sequence is the
  * sequence parallelism of page "FlashAttention技术演进全景图" §3.2.  The size
  * is 2 * G * R * (D + 4) * 4 bytes, G = min(compute units, units of work),
- * R the rows of a query tile in this schedule (128 for D = 128, 256 for
- * D = 64).
+ * R the rows of a query tile in this schedule (256, or 128 at D = 128
+ * when there are fewer 256-row tiles than compute units).
  *
  * Returns FA_OK, FA_ERR_NULLPTR (bytes NULL), FA_ERR_SHAPE, FA_ERR_HEAD_DIM,
  * FA_ERR_DTYPE or FA_ERR_HIP (device query failed).

@@ -243,6 +243,9 @@ SPLIT = [
     # takes 256-row tiles (on a 256-CU device)
     (20, 13, 300, 700, 128),
     (2, 65, 512, 1000, 128),
+    # D = 32: the same schedule on 256-row tiles
+    (1, 2, 1000, 3000, 32),
+    (3, 1, 1500, 1500, 32),
 ]
 
 
@@ -268,7 +271,7 @@ def test_split_workspace_contract():
     assert need > 0
     assert need == _ws_bytes(B, H, Nq, Nk, D, 1, fa.FA_BF16_OF32)
     assert _ws_bytes(B, H, Nq, Nk, D, 1, fa.FA_F32) == 0
-    assert _ws_bytes(B, H, Nq, Nk, 32, 1, fa.FA_BF16) == 0
+    assert _ws_bytes(B, H, Nq, Nk, 16, 1, fa.FA_BF16) == 0
     cus = torch.cuda.get_device_properties(DEV).multi_processor_count
     assert _ws_bytes(4 * cus, 1, 128, 128, D, 1, fa.FA_BF16) == 0  # many tiles
     ws = torch.empty(need, dtype=torch.uint8, device=DEV)
@@ -280,9 +283,9 @@ def test_split_workspace_contract():
     assert fa.fa_fwd_ws(*args, ws.data_ptr() + 8, need - 8, sp) == fa.FA_ERR_ALIGN
     assert fa.fa_fwd_ws(*args, o.data_ptr(), need, sp) == fa.FA_ERR_OVERLAP
     assert fa.fa_fwd_ws(*args, ws.data_ptr(), need, sp) == fa.FA_OK
-    # a path without a schedule (D < 64) runs without scratch
+    # a path without a schedule (D = 16) runs without scratch
     small = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-             1, 1, 64, 64, 32, 0.1, 1, fa.FA_BF16)
+             1, 1, 64, 64, 16, 0.1, 1, fa.FA_BF16)
     assert fa.fa_fwd_ws(*small, None, 0, sp) == fa.FA_OK
     torch.cuda.synchronize()
 

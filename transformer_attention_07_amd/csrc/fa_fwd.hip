@@ -495,8 +495,8 @@ __device__ __forceinline__ u32x4 load16_async(u32x4 rs, uint32_t voff) {
 template <typename T, int D>
 struct PipeLayout {
   static constexpr int C = D / 8;                     // 16-byte chunks per row
-  static constexpr int SK = D == 128 ? 17 : 9;        // K row stride (slots)
-  static constexpr int SV = D == 128 ? 20 : 12;       // V row stride (slots)
+  static constexpr int SK = D == 128 ? 17 : (D == 64 ? 9 : 5);   // K row stride (slots)
+  static constexpr int SV = D == 128 ? 20 : (D == 64 ? 12 : 6);  // V row stride (slots)
   static constexpr int K_BYTES = kBN * SK * 16;
   static constexpr int V_BYTES = kBN * SV * 16;
   static constexpr int K_INS = kBN * SK / kWave;      // DMA instructions per K tile
@@ -1403,7 +1403,7 @@ struct Launch {
 
 template <typename T, typename OT, int D, bool CAUSAL>
 hipError_t launch16(const Launch &a) {
-  if constexpr (D >= 64) {
+  if constexpr (D >= 32) {
     // c > 0 here: a negative scale flips the sign of Q inside the kernel,
     // and scale 0 runs as the smallest normal scale (scores of at most
     // 2^-126 * |q.k|, which round to 0 against any shift the softmax uses).

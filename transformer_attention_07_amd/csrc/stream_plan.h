@@ -64,8 +64,8 @@ struct StreamPlan {
 // than compute units, where the pair-split 128-row layout, twice as many
 // workgroups per row, balances better (measured on MI355X: 256-row +6% at
 // one tile per CU, pair-split +5% at half a tile per CU and +15% at an
-// eighth).  D = 64 always takes 256-row tiles: its blocks are half as long,
-// so sharing the per-step costs between two blocks matters more.
+// eighth).  D = 64 and 32 always take 256-row tiles: their blocks are
+// shorter, so sharing the per-step costs between two blocks matters more.
 inline bool stream_pair(int64_t BH, int64_t Nq, int64_t D, int cus) {
   return D == 128 && BH * ((Nq + kGridRows - 1) / kGridRows) < (int64_t)cus;
 }
@@ -224,7 +224,7 @@ struct CutList {
   uint16_t j[kMaxChunks - 1];
 };
 
-// Stream-K schedule of the pipelined kernel (16-bit inputs, D >= 64): one
+// Stream-K schedule of the pipelined kernel (16-bit inputs, D >= 32): one
 // chunk per compute unit.  With four or more 128-row query tiles per compute
 // unit the longest-first grid of fa_fwd already keeps every unit busy to the
 // end, and a chunk would hold many pieces, each paying its own prologue: the
@@ -233,7 +233,7 @@ struct CutList {
 inline bool make_plan(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, int dtype, bool causal,
                int cus, StreamPlan &sp, size_t &ws_bytes) {
   ws_bytes = 0;
-  if (dtype == FA_F32 || D < 64 || cus < 1) return false;
+  if (dtype == FA_F32 || D < 32 || cus < 1) return false;
   const int64_t pair_rows = kPairRows;
   if (BH * ((Nq + pair_rows - 1) / pair_rows) >= 4 * (int64_t)cus) return false;
   const bool pair = stream_pair(BH, Nq, D, cus);
