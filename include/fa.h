@@ -102,7 +102,7 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
 /*
  * fa_fwd_workspace_size -- device scratch bytes that fa_fwd_ws needs for
  * this problem on the current device (written to *bytes; 0 when fa_fwd_ws
- * takes the same path as fa_fwd: fp32 inputs, D = 16, or at least four
+ * takes the same path as fa_fwd: fp32 inputs, or at least four
  * query tiles of 128 rows per compute unit, where one workgroup per tile
  * already keeps every unit busy).
  *

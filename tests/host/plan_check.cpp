@@ -114,7 +114,7 @@ int main() {
   for (int64_t BH : {1, 2, 3, 8})
     for (int64_t Nq : Ns)
       for (int64_t Nk : {(int64_t)1, (int64_t)63, (int64_t)500, (int64_t)4096, Nq})
-        for (int64_t D : {32, 64, 128})
+        for (int64_t D : {16, 32, 64, 128})
           for (int causal = 0; causal < 2; ++causal)
             for (int cus : cuss)
               for (const auto &lt : leads) {

@@ -243,9 +243,10 @@ SPLIT = [
     # takes 256-row tiles (on a 256-CU device)
     (20, 13, 300, 700, 128),
     (2, 65, 512, 1000, 128),
-    # D = 32: the same schedule on 256-row tiles
+    # D = 32 and 16: the same schedule on 256-row tiles
     (1, 2, 1000, 3000, 32),
     (3, 1, 1500, 1500, 32),
+    (2, 1, 1300, 2100, 16),
 ]
 
 
@@ -271,7 +272,7 @@ def test_split_workspace_contract():
     assert need > 0
     assert need == _ws_bytes(B, H, Nq, Nk, D, 1, fa.FA_BF16_OF32)
     assert _ws_bytes(B, H, Nq, Nk, D, 1, fa.FA_F32) == 0
-    assert _ws_bytes(B, H, Nq, Nk, 16, 1, fa.FA_BF16) == 0
+    assert _ws_bytes(B, H, Nq, Nk, 16, 1, fa.FA_F32) == 0
     cus = torch.cuda.get_device_properties(DEV).multi_processor_count
     assert _ws_bytes(4 * cus, 1, 128, 128, D, 1, fa.FA_BF16) == 0  # many tiles
     ws = torch.empty(need, dtype=torch.uint8, device=DEV)
@@ -283,9 +284,12 @@ def test_split_workspace_contract():
     assert fa.fa_fwd_ws(*args, ws.data_ptr() + 8, need - 8, sp) == fa.FA_ERR_ALIGN
     assert fa.fa_fwd_ws(*args, o.data_ptr(), need, sp) == fa.FA_ERR_OVERLAP
     assert fa.fa_fwd_ws(*args, ws.data_ptr(), need, sp) == fa.FA_OK
-    # a path without a schedule (D = 16) runs without scratch
-    small = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-             1, 1, 64, 64, 16, 0.1, 1, fa.FA_BF16)
+    # a path without a schedule (fp32 inputs) runs without scratch
+    q32, k32, v32 = (t.to(DEV) for t in gen_qkv(1, 1, 64, 64, 16, seed=2, dtype="f32"))
+    o32 = torch.empty_like(q32)
+    l32 = torch.empty(q32.shape[:-1], dtype=torch.float32, device=DEV)
+    small = (q32.data_ptr(), k32.data_ptr(), v32.data_ptr(), o32.data_ptr(), l32.data_ptr(),
+             1, 1, 64, 64, 16, 0.1, 1, fa.FA_F32)
     assert fa.fa_fwd_ws(*small, None, 0, sp) == fa.FA_OK
     torch.cuda.synchronize()
 

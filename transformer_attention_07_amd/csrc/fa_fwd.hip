@@ -269,154 +269,21 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[(D < 32 ? 32 : D) /
 }
 
 // ---------------------------------------------------------------------------
-// bf16 / fp16 inputs.
-template <typename T, typename OT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void fa_fwd_mfma16(
-    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-    OT *__restrict__ o, float *__restrict__ lse, int Nq, int Nk, int BH, int nqt,
-    float c) {
-  typedef typename Mfma16<T>::frag frag;
-  constexpr int KS = D + 8;                // K row stride in LDS (elements)
-  constexpr int DV = D < 32 ? 32 : D;      // V^T rows (MFMA M-blocks are 32)
-  constexpr int VS = kBN + 4;              // V^T row stride in LDS (elements)
-  constexpr int K_ELEMS = kBN * KS;
-  constexpr int V_ELEMS = DV * VS;
-  constexpr int BUF = K_ELEMS + V_ELEMS;
-  constexpr int CPR = D / 8;               // 16-byte chunks per K/V row
-  constexpr int NCH = kBN * CPR;           // chunks per tile
-  constexpr int LPT = (NCH + kThreads - 1) / kThreads;
-  constexpr int QF = D / 16;               // Q fragments (MFMA k-steps over D)
-  constexpr int NDB = DV / 32;             // O^T M-blocks
-
-  __shared__ __attribute__((aligned(16))) T smem[2 * BUF];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int l32 = lane & 31;
-  const int g = lane >> 5;
-
-  const WorkItem wi = work_item(BH, nqt, CAUSAL);
-  const int qw = wi.q0 + wave * 32;
-  const int my_q = qw + l32;
-
-  const size_t qoff = (size_t)wi.bh * Nq * D;
-  const size_t koff = (size_t)wi.bh * Nk * D;
-  const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(q + qoff, (uint32_t)Nq * D * sizeof(T));
-  const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(k + koff, (uint32_t)Nk * D * sizeof(T));
-  const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(v + koff, (uint32_t)Nk * D * sizeof(T));
-
-  // Q^T fragments stay in registers for the whole key loop.
-  frag qf[QF];
-#pragma unroll
-  for (int f = 0; f < QF; ++f) {
-    const uint32_t off = ((uint32_t)my_q * D + 16 * f + 8 * g) * sizeof(T);
-    qf[f] = __builtin_bit_cast(frag, load16(q_rs, off));
-  }
-
-  u32x4 kreg[LPT], vreg[LPT];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int ch = tid + i * kThreads;
-      if (NCH % kThreads == 0 || ch < NCH) {
-        const int row = ch / CPR;
-        const int col = (ch % CPR) * 8;
-        const uint32_t off = ((uint32_t)(kt * kBN + row) * D + col) * sizeof(T);
-        kreg[i] = load16(k_rs, off);
-        vreg[i] = load16(v_rs, off);
-      }
-    }
-  };
-  auto swrite = [&](int buf) {
-    T *Ks = smem + buf * BUF;
-    T *Vt = Ks + K_ELEMS;
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int ch = tid + i * kThreads;
-      if (NCH % kThreads == 0 || ch < NCH) {
-        const int row = ch / CPR;
-        const int col = (ch % CPR) * 8;
-        *reinterpret_cast<u32x4 *>(Ks + row * KS + col) = kreg[i];
-        const frag ve = __builtin_bit_cast(frag, vreg[i]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) Vt[(col + e) * VS + row] = ve[e];
-      }
-    }
-  };
-
-  f32x16 acc[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
-  float m = -INFINITY, l = 0.f;
-
-  const int kend = CAUSAL ? min(Nk, wi.q0 + kBM) : Nk;
-  const int nkt = (kend + kBN - 1) / kBN;
-
-  gload(0);
-  swrite(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < nkt; ++kt) {
-    if (kt + 1 < nkt) gload(kt + 1);
-    const int k0 = kt * kBN;
-    const bool active = !CAUSAL || (k0 <= qw + 31);
-    if (active) {
-      const T *Ks = smem + (kt & 1) * BUF;
-      const T *Vt = Ks + K_ELEMS;
-      f32x16 s[kBN / 32];
-#pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb) {
-        s[kb] = f32x16{};
-#pragma unroll
-        for (int f = 0; f < QF; ++f) {
-          const frag a =
-              *reinterpret_cast<const frag *>(Ks + (kb * 32 + l32) * KS + 16 * f + 8 * g);
-          s[kb] = Mfma16<T>::mma(a, qf[f], s[kb]);
-        }
-      }
-      const bool need_mask = (k0 + kBN > Nk) || (CAUSAL && k0 + kBN - 1 > qw);
-      scale_and_mask<CAUSAL>(s, c, k0, Nk, my_q, g, need_mask);
-      const float alpha = online_softmax(s, m, l);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
-#pragma unroll
-      for (int st = 0; st < kBN / 16; ++st) {
-        const int kb = st >> 1;
-        const int h = st & 1;
-        const f32x8 pv = {s[kb][8 * h + 0], s[kb][8 * h + 1], s[kb][8 * h + 2],
-                          s[kb][8 * h + 3], s[kb][8 * h + 4], s[kb][8 * h + 5],
-                          s[kb][8 * h + 6], s[kb][8 * h + 7]};
-        const frag pf = __builtin_convertvector(pv, frag);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const T *vp = Vt + (db * 32 + l32) * VS + st * 16 + 4 * g;
-          const u32x2 lo = *reinterpret_cast<const u32x2 *>(vp);
-          const u32x2 hi = *reinterpret_cast<const u32x2 *>(vp + 8);
-          const u32x4 raw = {lo[0], lo[1], hi[0], hi[1]};
-          acc[db] = Mfma16<T>::mma(__builtin_bit_cast(frag, raw), pf, acc[db]);
-        }
-      }
-    }
-    if (kt + 1 < nkt) swrite((kt + 1) & 1);
-    __syncthreads();
-  }
-
-  epilogue<D, OT>(acc, m, l, o, lse, wi.bh, Nq, my_q, g);
-}
-
-// ---------------------------------------------------------------------------
-// Pipelined kernel for 16-bit inputs with D = 64 or 128.
+// Pipelined kernel for 16-bit inputs (D = 16, 32, 64, 128).
 //
-// Same arithmetic and register layouts as fa_fwd_mfma16; what differs:
+//   * Products are transposed: S^T = K.Q^T on v_mfma_f32_32x32x16 (bf16 or
+//     fp16, fp32 accumulation) puts one query per lane (lane l holds query
+//     l % 32, 16 of its 32 scores per block, half-wave l / 32 the other
+//     rows), so row reductions are in-lane plus one exchange; P^T, rounded
+//     to the input type, is the B operand of O^T = V^T.P^T directly, with no
+//     trip through LDS.
 //   * K and V tiles (64 keys) go global -> LDS directly (buffer_load ... lds,
 //     16 bytes per lane, written lane-linearly) into a K ring and a V ring of
 //     four stages each; nothing passes through VGPRs.  Tile t+3 of K and
 //     tile t+2 of V are requested while tile t is computed on.
-//   * Rows are padded in LDS: K rows to 17 16-byte slots (9 for D=64) so the
-//     16 rows read by one ds_read_b128 pass start on distinct bank groups; V
-//     rows to 20 slots (12 for D=64), where the transpose reads below are
-//     fastest.  Padding slots are loaded from an out-of-range offset (zero, no
+//   * Rows are padded in LDS (PipeLayout): K rows so that the 16 rows read by
+//     one ds_read_b128 pass start on distinct bank groups; V rows where the
+//     transpose reads below are fastest.  Padding slots are loaded from an out-of-range offset (zero, no
 //     memory traffic).  With fixed strides every fragment address is a
 //     per-lane base plus an immediate.
 //   * V^T fragments come from ds_read_b64_tr_b16: within each 16-lane group,
@@ -495,8 +362,11 @@ __device__ __forceinline__ u32x4 load16_async(u32x4 rs, uint32_t voff) {
 template <typename T, int D>
 struct PipeLayout {
   static constexpr int C = D / 8;                     // 16-byte chunks per row
-  static constexpr int SK = D == 128 ? 17 : (D == 64 ? 9 : 5);   // K row stride (slots)
-  static constexpr int SV = D == 128 ? 20 : (D == 64 ? 12 : 6);  // V row stride (slots)
+  // K and V row strides (16-byte slots): padded against bank conflicts; at
+  // D = 16 the V row holds 4 slots so that the P.V fragments' upper 16
+  // head-dim columns read the zeroed padding
+  static constexpr int SK = D == 128 ? 17 : (D == 64 ? 9 : (D == 32 ? 5 : 3));
+  static constexpr int SV = D == 128 ? 20 : (D == 64 ? 12 : (D == 32 ? 6 : 4));
   static constexpr int K_BYTES = kBN * SK * 16;
   static constexpr int V_BYTES = kBN * SV * 16;
   static constexpr int K_INS = kBN * SK / kWave;      // DMA instructions per K tile
@@ -540,10 +410,12 @@ struct Pipe {
   typedef typename Mfma16<T>::frag frag;
   typedef PipeLayout<T, D> L;
   static constexpr int QF = D / 16;    // K.Q^T MFMAs per 32-key block
-  static constexpr int NDB = D / 32;
+  // O^T blocks of 32 head-dim rows (at D = 16 the upper 16 rows read zero
+  // padding of V and are never stored)
+  static constexpr int NDB = (D + 31) / 32;
   static constexpr int NPV = 2 * NDB;  // P.V MFMAs per 32-key block
-  static_assert(QF == NPV, "slots pair one K.Q^T with one P.V MFMA");
-  static constexpr int NSLOT = QF + NPV;
+  // MFMA slots of a block: slot i holds K.Q^T i (i < QF) and P.V i (i < NPV)
+  static constexpr int NSL = QF > NPV ? QF : NPV;
 
   int lane, wave, l32, g, qw, my_q, Nk;
   float c;
@@ -554,8 +426,9 @@ struct Pipe {
   frag P0[2], P1[2];  // P blocks rounded to T (alternate likewise)
   // First K and V fragments of the wave's next block, read during the tail
   // of the current one (blocks chained with PRE)
-  static constexpr int PF = QF < 3 ? QF : 3;
-  frag kpre[PF], vpre[PF];
+  static constexpr int PFK = QF < 3 ? QF : 3;   // K fragments read ahead
+  static constexpr int PFV = NPV < 3 ? NPV : 3;  // V fragments read ahead
+  frag kpre[PFK], vpre[PFV];
   float m_use;
   float l;   // half-wave sum of p (fp32): gives L
   float lr;  // half-wave sum of p as rounded to T for P.V: normalises O
@@ -632,7 +505,7 @@ struct Pipe {
   // 0), and a row that has not seen a key yet shifts by 0 instead of
   // -(-inf).  One code path serves masked and unmasked blocks, so the
   // accumulators stay in the same registers from block to block.
-  // PRE: the first PF fragments of this block were read ahead into kpre
+  // PRE: the first PFK / PFV fragments of this block were read ahead into kpre
   // and vpre, and this block reads those of the next one (kpn, vpn) in its
   // last MFMA slots.
   template <bool PRE = false>
@@ -643,7 +516,6 @@ struct Pipe {
                                              const lds_char *vpn = nullptr) {
     constexpr int NCHUNK = 15;
     frag kf[QF], vf[NPV];
-    static_assert(NPV == QF, "one K.Q^T and one P.V per slot pair");
     float mx = 0.f, nm = 0.f, alpha = 1.f;
     float m3[5];               // partial maxima
     float ea[2], pb[2];        // pair in flight: exponents, then p
@@ -719,33 +591,36 @@ struct Pipe {
       }
     };
 
-    // fragments are read PF MFMA pairs ahead
+    // fragments are read up to three MFMA slots ahead
 #pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      kf[i] = PRE ? kpre[i] : kfrag(kp, i);
-      vf[i] = PRE ? vpre[i] : vfrag(vp, i);
+    for (int i = 0; i < (PFK > PFV ? PFK : PFV); ++i) {
+      if (i < PFK) kf[i] = PRE ? kpre[i] : kfrag(kp, i);
+      if (i < PFV) vf[i] = PRE ? vpre[i] : vfrag(vp, i);
     }
+    constexpr int NH = 2 * NSL;  // half-slots, each followed by softmax slices
 #pragma unroll
-    for (int i = 0; i < QF; ++i) {
+    for (int i = 0; i < NSL; ++i) {
       // K.Q^T, then a slice of the softmax
-      sout = Mfma16<T>::mma(kf[i], qf[i], sout);
-      if (i + PF < QF)
-        kf[i + PF] = kfrag(kp, i + PF);
-      else if (PRE)
-        kpre[i + PF - QF] = kfrag(kpn, i + PF - QF);
+      if (i < QF) {
+        sout = Mfma16<T>::mma(kf[i], qf[i], sout);
+        if (i + PFK < QF)
+          kf[i + PFK] = kfrag(kp, i + PFK);
+        else if (PRE)
+          kpre[i + PFK - QF] = kfrag(kpn, i + PFK - QF);
+      }
 #pragma unroll
-      for (int ch = (2 * i) * NCHUNK / NSLOT; ch < (2 * i + 1) * NCHUNK / NSLOT; ++ch)
-        chunk(ch);
+      for (int ch = (2 * i) * NCHUNK / NH; ch < (2 * i + 1) * NCHUNK / NH; ++ch) chunk(ch);
       __builtin_amdgcn_sched_barrier(0);
       // P.V, then a slice of the softmax
-      acc[i % NDB] = Mfma16<T>::mma(vf[i], pin[i / NDB], acc[i % NDB]);
-      if (i + PF < NPV)
-        vf[i + PF] = vfrag(vp, i + PF);
-      else if (PRE)
-        vpre[i + PF - NPV] = vfrag(vpn, i + PF - NPV);
+      if (i < NPV) {
+        acc[i % NDB] = Mfma16<T>::mma(vf[i], pin[i / NDB], acc[i % NDB]);
+        if (i + PFV < NPV)
+          vf[i + PFV] = vfrag(vp, i + PFV);
+        else if (PRE)
+          vpre[i + PFV - NPV] = vfrag(vpn, i + PFV - NPV);
+      }
 #pragma unroll
-      for (int ch = (2 * i + 1) * NCHUNK / NSLOT; ch < (2 * i + 2) * NCHUNK / NSLOT; ++ch)
-        chunk(ch);
+      for (int ch = (2 * i + 1) * NCHUNK / NH; ch < (2 * i + 2) * NCHUNK / NH; ++ch) chunk(ch);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
@@ -798,9 +673,9 @@ struct Pipe {
   __device__ __forceinline__ void read_ahead(const lds_char *ring, int vst, int vhalf, int kst,
                                              int khalf) {
 #pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      kpre[i] = kfrag(kptr(ring, kst, khalf), i);
-      vpre[i] = vfrag(vptr(ring, vst, vhalf), i);
+    for (int i = 0; i < (PFK > PFV ? PFK : PFV); ++i) {
+      if (i < PFK) kpre[i] = kfrag(kptr(ring, kst, khalf), i);
+      if (i < PFV) vpre[i] = vfrag(vptr(ring, vst, vhalf), i);
     }
   }
 };
@@ -810,13 +685,13 @@ struct Pipe {
 // exponent reference.  A row that saw no
 // key in this part has l = lr = 0, m = -inf and O_p = 0.
 template <int D>
-__device__ __forceinline__ void epilogue_partial(const f32x16 (&acc)[D / 32], float m,
+__device__ __forceinline__ void epilogue_partial(const f32x16 (&acc)[(D + 31) / 32], float m,
                                                  float l, float lr, float *ws_o,
                                                  float *ws_s, int row, int g) {
   const float lt = l + __shfl_xor(l, 32);
   const float lrt = lr + __shfl_xor(lr, 32);
   const float inv = lrt > 0.f ? 1.0f / lrt : 0.f;
-  store_row<float, D / 32>(acc, inv, ws_o + (size_t)row * D, g, D);
+  store_row<float, (D + 31) / 32>(acc, inv, ws_o + (size_t)row * D, g, D);
   if (g == 0) {
     const f32x4 st = {lrt > 0.f ? m : -INFINITY, lt, lrt, 0.f};
     *reinterpret_cast<f32x4 *>(ws_s + row * 4) = st;
@@ -1022,7 +897,7 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
     // so a block never starts on a fresh LDS round trip.  Those reads are
     // the wave's youngest LDS accesses at the next barrier, which lets them
     // stay in flight: they touch neither stage the next unit overwrites.
-    constexpr int RA = 3 * P::PF;  // LDS reads of one read-ahead
+    constexpr int RA = P::PFK + 2 * P::PFV;  // LDS reads of one read-ahead
     s.read_ahead(ring, kStages - 1, 1, 0, 1);
     for (int r = 0; r < ntiles; ++r) {
       ring_barrier_sel<UNIT, RA>(r + 2 <= ntiles);
@@ -1403,46 +1278,40 @@ struct Launch {
 
 template <typename T, typename OT, int D, bool CAUSAL>
 hipError_t launch16(const Launch &a) {
-  if constexpr (D >= 32) {
-    // c > 0 here: a negative scale flips the sign of Q inside the kernel,
-    // and scale 0 runs as the smallest normal scale (scores of at most
-    // 2^-126 * |q.k|, which round to 0 against any shift the softmax uses).
-    const float c = fmaxf(a.c < 0.f ? -a.c : a.c, 1.17549435e-38f);
-    const int neg = a.c < 0.f ? 1 : 0;
-    if (a.plan) {
-      const StreamPlan &sp = *a.plan;
-      // the plan's tile height selects the layout (pair-split: 128 rows)
-      auto go = [&](auto pair) -> hipError_t {
-        constexpr bool PAIR = decltype(pair)::value;
-        hipLaunchKernelGGL((fa_fwd_stream<T, OT, D, CAUSAL, PAIR>), dim3((unsigned)sp.G),
-                           dim3(kThreads8), 0, a.stream, (const T *)a.q, (const T *)a.k,
-                           (const T *)a.v, (OT *)a.o, a.lse, a.ws, a.Nq, a.Nk, c, neg, sp);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        if (a.cuts && a.cuts->n > 0) {
-          hipLaunchKernelGGL((fa_merge_stream<OT, D, CAUSAL, QRows<PAIR>::value>),
-                             dim3((unsigned)(a.cuts->n * (QRows<PAIR>::value / merge_rows<D>()))),
-                             dim3(kThreads), 0, a.stream, (const float *)a.ws, (OT *)a.o,
-                             a.lse, a.Nq, sp, *a.cuts);
-        }
-        return hipSuccess;
-      };
-      hipError_t e;
-      if constexpr (D == 128)
-        e = sp.tu == kPairRows / kKeys ? go(std::true_type{}) : go(std::false_type{});
-      else
-        e = go(std::false_type{});
+  // c > 0 here: a negative scale flips the sign of Q inside the kernel,
+  // and scale 0 runs as the smallest normal scale (scores of at most
+  // 2^-126 * |q.k|, which round to 0 against any shift the softmax uses).
+  const float c = fmaxf(a.c < 0.f ? -a.c : a.c, 1.17549435e-38f);
+  const int neg = a.c < 0.f ? 1 : 0;
+  if (a.plan) {
+    const StreamPlan &sp = *a.plan;
+    // the plan's tile height selects the layout (pair-split: 128 rows)
+    auto go = [&](auto pair) -> hipError_t {
+      constexpr bool PAIR = decltype(pair)::value;
+      hipLaunchKernelGGL((fa_fwd_stream<T, OT, D, CAUSAL, PAIR>), dim3((unsigned)sp.G),
+                         dim3(kThreads8), 0, a.stream, (const T *)a.q, (const T *)a.k,
+                         (const T *)a.v, (OT *)a.o, a.lse, a.ws, a.Nq, a.Nk, c, neg, sp);
+      hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-    } else {
-      hipLaunchKernelGGL((fa_fwd_pipe8<T, OT, D, CAUSAL, false>),
-                         dim3((unsigned)(a.BH * a.nqtg)), dim3(kThreads8), 0, a.stream,
-                         (const T *)a.q, (const T *)a.k, (const T *)a.v, (OT *)a.o, a.lse,
-                         a.Nq, a.Nk, a.BH, a.nqtg, c, neg);
-    }
+      if (a.cuts && a.cuts->n > 0) {
+        hipLaunchKernelGGL((fa_merge_stream<OT, D, CAUSAL, QRows<PAIR>::value>),
+                           dim3((unsigned)(a.cuts->n * (QRows<PAIR>::value / merge_rows<D>()))),
+                           dim3(kThreads), 0, a.stream, (const float *)a.ws, (OT *)a.o,
+                           a.lse, a.Nq, sp, *a.cuts);
+      }
+      return hipSuccess;
+    };
+    hipError_t e;
+    if constexpr (D == 128)
+      e = sp.tu == kPairRows / kKeys ? go(std::true_type{}) : go(std::false_type{});
+    else
+      e = go(std::false_type{});
+    if (e != hipSuccess) return e;
   } else {
-    hipLaunchKernelGGL((fa_fwd_mfma16<T, OT, D, CAUSAL>), dim3((unsigned)(a.BH * a.nqt)),
-                       dim3(kThreads), 0, a.stream, (const T *)a.q, (const T *)a.k,
-                       (const T *)a.v, (OT *)a.o, a.lse, a.Nq, a.Nk, a.BH, a.nqt, a.c);
+    hipLaunchKernelGGL((fa_fwd_pipe8<T, OT, D, CAUSAL, false>),
+                       dim3((unsigned)(a.BH * a.nqtg)), dim3(kThreads8), 0, a.stream,
+                       (const T *)a.q, (const T *)a.k, (const T *)a.v, (OT *)a.o, a.lse,
+                       a.Nq, a.Nk, a.BH, a.nqtg, c, neg);
   }
   return hipGetLastError();
 }

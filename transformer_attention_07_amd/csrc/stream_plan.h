@@ -224,7 +224,7 @@ struct CutList {
   uint16_t j[kMaxChunks - 1];
 };
 
-// Stream-K schedule of the pipelined kernel (16-bit inputs, D >= 32): one
+// Stream-K schedule of the pipelined kernel (16-bit inputs): one
 // chunk per compute unit.  With four or more 128-row query tiles per compute
 // unit the longest-first grid of fa_fwd already keeps every unit busy to the
 // end, and a chunk would hold many pieces, each paying its own prologue: the
@@ -233,7 +233,7 @@ struct CutList {
 inline bool make_plan(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, int dtype, bool causal,
                int cus, StreamPlan &sp, size_t &ws_bytes) {
   ws_bytes = 0;
-  if (dtype == FA_F32 || D < 32 || cus < 1) return false;
+  if (dtype == FA_F32 || cus < 1) return false;
   const int64_t pair_rows = kPairRows;
   if (BH * ((Nq + pair_rows - 1) / pair_rows) >= 4 * (int64_t)cus) return false;
   const bool pair = stream_pair(BH, Nq, D, cus);
