@@ -31,6 +31,9 @@ if ROOT not in sys.path:
 METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak (B8 N4096 D128 causal)"
 # MI355X published dense peaks (TFLOP/s).
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+# Transcendental rate for the exp roofline of small head dims: v_exp_f32 at
+# a quarter of the 64-lane VALU rate, 16 per clock per CU (256 CUs, 2.4 GHz).
+EXP_PEAK_T = 16 * 256 * 2.4e9 / 1e12
 HBM_GBPS = 8000.0
 CSRC = os.path.join(ROOT, "transformer_attention_07_amd", "csrc")
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
@@ -225,6 +228,13 @@ def main() -> int:
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count},
     }
+    if w.D <= 64:
+        # one exp per visible score (half of them when causal): at small head
+        # dims the softmax's transcendentals, not the MFMAs, bound the kernel
+        exps = w.B * w.H * w.N * w.N / (2 if w.causal else 1)
+        rate = exps / (kernel_ms * 1e-3) / 1e12
+        line["exp_roofline"] = {"achieved": round(rate, 3), "peak": round(EXP_PEAK_T, 3),
+                                "unit": "Texp/s", "frac": round(rate / EXP_PEAK_T, 4)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line), flush=True)
