@@ -1288,6 +1288,9 @@ hipError_t launch16(const Launch &a) {
     // the plan's tile height selects the layout (pair-split: 128 rows)
     auto go = [&](auto pair) -> hipError_t {
       constexpr bool PAIR = decltype(pair)::value;
+      // the workspace slots and tile indices of the plan are in units of the
+      // kernel's tile height: never launch with another
+      if (sp.tu * kKeys != QRows<PAIR>::value) return hipErrorInvalidValue;
       hipLaunchKernelGGL((fa_fwd_stream<T, OT, D, CAUSAL, PAIR>), dim3((unsigned)sp.G),
                          dim3(kThreads8), 0, a.stream, (const T *)a.q, (const T *)a.k,
                          (const T *)a.v, (OT *)a.o, a.lse, a.ws, a.Nq, a.Nk, c, neg, sp);
