@@ -85,9 +85,12 @@ def cpu_baseline(w, target_s: float):
     oracle.attention(qn, kn, vn, scale, w.causal, rows=probe, lib=lib)
     t_probe = time.perf_counter() - t0
     est_full = t_probe * work_total / float(visible(probe))
+    reps = 1
     if est_full <= target_s:
-        rows, desc = None, f"all {total} rows of the workload"
-        work = work_total
+        # the whole workload fits the time budget: repeat it to fill the budget
+        reps = int(max(1, min(50, target_s / max(est_full, 1e-9))))
+        rows, desc = None, f"all {total} rows of the workload, {reps} passes"
+        work = work_total * reps
     else:
         n = int(max(64, min(total, 64 * target_s / max(t_probe, 1e-9))))
         rows = sample_rows(total, n, 8).numpy()
@@ -95,7 +98,8 @@ def cpu_baseline(w, target_s: float):
         desc = (f"{n} of {total} rows drawn uniformly (seed 8); time scaled to the "
                 f"whole workload by the count of visible keys")
     t0 = time.perf_counter()
-    oracle.attention(qn, kn, vn, scale, w.causal, rows=rows, lib=lib)
+    for _ in range(reps):
+        oracle.attention(qn, kn, vn, scale, w.causal, rows=rows, lib=lib)
     elapsed = time.perf_counter() - t0
     t_full = elapsed * work_total / work
     return {
@@ -105,7 +109,7 @@ def cpu_baseline(w, target_s: float):
         "kind": "oracle",
         "sample": desc,
         "seconds": round(elapsed, 3),
-        "seconds_full_workload": round(t_full, 3),
+        "seconds_full_workload": round(t_full, 6),
     }
 
 
@@ -131,8 +135,8 @@ def main() -> int:
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the forward pass shards over batch*heads with no exchange; see the "
-              "design notes)", file=sys.stderr)
+              "(sharded over batch*heads, each GPU would run this same "
+              "single-GPU path with no exchange)", file=sys.stderr)
         return 2
 
     import torch
@@ -184,16 +188,23 @@ def main() -> int:
                                f"{fa.fa_last_hip_error()}")
     torch.cuda.synchronize(dev)
 
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    # events at five evenly spaced points of the timed steps as well (no
+    # synchronisation between them) give the spread of the per-step time
+    groups = min(5, args.steps)
+    marks = sorted({args.steps * g // groups for g in range(groups + 1)})
+    evs = {m: torch.cuda.Event(enable_timing=True) for m in marks}
+    ev0, ev1 = evs[0], evs[args.steps]
     t0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
         call(*argv)
+        if i + 1 in evs and i + 1 != args.steps:
+            evs[i + 1].record(stream)
     ev1.record(stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
     kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    group_ms = sorted(evs[a].elapsed_time(evs[b]) / (b - a) for a, b in zip(marks, marks[1:]))
 
     ms_per_step = wall * 1e3 / args.steps
     flops = w.flops()
@@ -224,7 +235,10 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(name),
-                     "kernel_ms": round(kernel_ms, 5)},
+                     "kernel_ms": round(kernel_ms, 5),
+                     "group_ms": {"groups": len(group_ms),
+                                  "median": round(group_ms[len(group_ms) // 2], 5),
+                                  "min": round(group_ms[0], 5), "max": round(group_ms[-1], 5)}},
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count},
     }
