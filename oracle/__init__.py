@@ -11,6 +11,12 @@ Functions (all fp64, numpy in / numpy out):
   attention_online(q, k, v, scale, causal, bq, bk) -> (o, lse)
       the pages' tiled online-softmax recurrence ("FlashAttention-2实现与优化"
       §3.1), used only to show that it reaches the two-pass result.
+  attention_bwd(q, k, v, do, scale, causal, qrows=None, krows=None,
+                magnitudes=False) -> (dq, dk, dv[, bq, bk, bv])
+      gradients of the forward pass for an upstream gradient do of O, by the
+      chain rule (the pages fix no formula for the backward pass; it is the
+      derivative of the definition above), plus optional magnitude sums that
+      bound rounding effects.
   threads() -> int   OpenMP threads the oracle uses.
 
 Parity status: pinned by tests/test_oracle_pins.py (closed forms, invariants,
@@ -53,6 +59,12 @@ def _bind(path: str):
     lib.fa_oracle_online.restype = ctypes.c_int
     lib.fa_oracle_online.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64, i64,
                                      ctypes.c_double, ctypes.c_int, i64, i64]
+    lib.fa_oracle_attention_bwd.restype = ctypes.c_int
+    lib.fa_oracle_attention_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, dp,
+                                            i64, i64, i64, i64, i64,
+                                            ctypes.c_double, ctypes.c_int,
+                                            ctypes.POINTER(i64), i64,
+                                            ctypes.POINTER(i64), i64]
     lib.fa_oracle_threads.restype = ctypes.c_int
     lib.fa_oracle_threads.argtypes = []
     return lib
@@ -134,6 +146,51 @@ def attention_online(q, k, v, scale: float, causal: bool, bq: int, bk: int, lib=
     if squeeze:
         return o[:, 0], lse[:, 0]
     return o, lse
+
+
+def _rowlist(rows):
+    if rows is None:
+        return None, None, 0
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    return r, r.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), r.size
+
+
+def attention_bwd(q, k, v, do, scale: float, causal: bool, qrows=None, krows=None,
+                  magnitudes: bool = False, lib=None):
+    """fp64 gradients (dq, dk, dv) of the forward pass for upstream gradient do.
+
+    q, do [B,(H,)Nq,D]; k, v [B,(H,)Nk,D].  With ``qrows`` (flat query rows
+    (b*H + h)*Nq + i) dq is [len(qrows), D]; with ``krows`` (flat key rows
+    (b*H + h)*Nk + j) dk and dv are [len(krows), D].  With ``magnitudes`` the
+    absolute-value sums (bq, bk, bv) of the same shapes follow.
+    """
+    lib = lib or load()
+    squeeze = np.asarray(q).ndim == 3
+    q4, k4, v4, g4 = _as4d(q), _as4d(k), _as4d(v), _as4d(do)
+    B, H, Nq, D = q4.shape
+    Nk = k4.shape[2]
+    if k4.shape != (B, H, Nk, D) or v4.shape != (B, H, Nk, D) or g4.shape != q4.shape:
+        raise ValueError("q/k/v/do shapes disagree")
+    qa, qp, nq = _rowlist(qrows)
+    ka, kp, nk = _rowlist(krows)
+    qshape = (B, H, Nq, D) if qa is None else (nq, D)
+    kshape = (B, H, Nk, D) if ka is None else (nk, D)
+    dq, dk, dv = np.empty(qshape), np.empty(kshape), np.empty(kshape)
+    if magnitudes:
+        bq, bk, bv = np.empty(qshape), np.empty(kshape), np.empty(kshape)
+        mp = (_ptr(bq), _ptr(bk), _ptr(bv))
+    else:
+        mp = (None, None, None)
+    st = lib.fa_oracle_attention_bwd(_ptr(q4), _ptr(k4), _ptr(v4), _ptr(g4),
+                                     _ptr(dq), _ptr(dk), _ptr(dv), *mp,
+                                     B, H, Nq, Nk, D, float(scale), int(bool(causal)),
+                                     qp, nq, kp, nk)
+    if st != 0:
+        raise RuntimeError(f"oracle failed with status {st}")
+    out = [dq, dk, dv] + ([bq, bk, bv] if magnitudes else [])
+    if squeeze:
+        out = [a[:, 0] if a.ndim == 4 else a for a in out]
+    return tuple(out)
 
 
 def threads(lib=None) -> int:

@@ -243,3 +243,214 @@ int fa_oracle_online(const double *q, const double *k, const double *v,
     }
     return failed ? ORACLE_ENOMEM : ORACLE_OK;
 }
+
+/*
+ * Gradients of the attention forward pass, the plain chain rule in double
+ * precision.  Page "解释FlashAttention的显存优化原理" §一.2(2) (and page
+ * "FlashAttention技术演进全景图" §2.2, item 3) describe the backward pass as
+ * recomputing the forward quantities instead of storing them; page
+ * "FlashAttention-2实现与优化：高效注意力机制详解" §3.1 keeps q, k, v, o and L
+ * for it and lists the backward pass among its extensions (§7).  The pages
+ * print no formula for it, so this routine is the derivative of the
+ * definition in fa_oracle_attention, with the upstream gradient dO of O:
+ *
+ *     P_ij  = exp(s_ij - m_i) / l_i            (the softmax of row i)
+ *     dV_j  = sum_i P_ij dO_i
+ *     dP_ij = <dO_i, v_j>
+ *     D_i   = sum_j P_ij dP_ij                 (softmax Jacobian, row term)
+ *     dS_ij = P_ij (dP_ij - D_i)
+ *     dQ_i  = scale * sum_j dS_ij k_j
+ *     dK_j  = scale * sum_i dS_ij q_i
+ *
+ * with sums over the visible pairs only (same key set as the forward).
+ * Optional "magnitude" outputs bq, bk, bv (same shapes as dq, dk, dv, may be
+ * NULL) hold the same sums taken over absolute values,
+ *
+ *     bv_j = sum_i P_ij |dO_i|
+ *     bq_i = scale * sum_j (|dS_ij| + P_ij E_i) |k_j|
+ *     bk_j = scale * sum_i (|dS_ij| + P_ij E_i) |q_i|,   E_i = sum_d |dO_id O_id|
+ *
+ * which bound the effect of rounding one factor of every product (and the
+ * row term D_i through O) to a short floating-point type; tests derive their
+ * tolerances from them.
+ *
+ * qrows / krows optionally restrict dq (and bq) to a list of flat query rows
+ * (b*H + h)*Nq + i and dk, dv (and bk, bv) to flat key rows (b*H + h)*Nk + j;
+ * the outputs are then [nq, D] / [nk, D] in list order.  Row statistics are
+ * always computed for every row, since a key's gradient needs all of them.
+ */
+int fa_oracle_attention_bwd(const double *q, const double *k, const double *v,
+                            const double *dout,
+                            double *dq, double *dk, double *dv,
+                            double *bq, double *bk, double *bv,
+                            int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+                            double scale, int causal,
+                            const int64_t *qrows, int64_t nq,
+                            const int64_t *krows, int64_t nk)
+{
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || bad_shape(B, H, Nq, Nk, D))
+        return ORACLE_EINVAL;
+    const int64_t totq = B * H * Nq, totk = B * H * Nk;
+    if (qrows)
+        for (int64_t t = 0; t < nq; ++t)
+            if (qrows[t] < 0 || qrows[t] >= totq)
+                return ORACLE_EINVAL;
+    if (krows)
+        for (int64_t t = 0; t < nk; ++t)
+            if (krows[t] < 0 || krows[t] >= totk)
+                return ORACLE_EINVAL;
+    const int64_t cq = qrows ? nq : totq;
+    const int64_t ck = krows ? nk : totk;
+    const int magn = bq && bk && bv;
+
+    /* per-row statistics: max m, normaliser l, row term D, and E */
+    double *m = (double *)malloc((size_t)totq * sizeof(double));
+    double *l = (double *)malloc((size_t)totq * sizeof(double));
+    double *rd = (double *)malloc((size_t)totq * sizeof(double));
+    double *re = (double *)malloc((size_t)totq * sizeof(double));
+    if (!m || !l || !rd || !re) {
+        free(m);
+        free(l);
+        free(rd);
+        free(re);
+        return ORACLE_ENOMEM;
+    }
+    int failed = 0;
+
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)Nk * sizeof(double));
+        double *o = (double *)malloc((size_t)D * sizeof(double));
+        if (!s || !o) {
+#pragma omp atomic write
+            failed = 1;
+        }
+        /* pass 1, every query row: scores, m, l, then P, dP, D_i and E_i */
+#pragma omp for schedule(dynamic, 8)
+        for (int64_t r = 0; r < totq; ++r) {
+            if (!s || !o)
+                continue;
+            const int64_t bh = r / Nq, i = r % Nq;
+            const double *qi = q + r * D, *gi = dout + r * D;
+            const double *kb = k + bh * Nk * D, *vb = v + bh * Nk * D;
+            const int64_t n = valid_keys(i, Nk, causal);
+            double mx = -INFINITY;
+            for (int64_t j = 0; j < n; ++j) {
+                double dot = 0.0;
+                for (int64_t d = 0; d < D; ++d)
+                    dot += qi[d] * kb[j * D + d];
+                s[j] = scale * dot;
+                if (s[j] > mx)
+                    mx = s[j];
+            }
+            double sum = 0.0;
+            for (int64_t j = 0; j < n; ++j)
+                sum += exp(s[j] - mx);
+            double acc = 0.0;
+            for (int64_t d = 0; d < D; ++d)
+                o[d] = 0.0;
+            for (int64_t j = 0; j < n; ++j) {
+                const double p = exp(s[j] - mx) / sum;
+                double dp = 0.0;
+                for (int64_t d = 0; d < D; ++d) {
+                    dp += gi[d] * vb[j * D + d];
+                    o[d] += p * vb[j * D + d];
+                }
+                acc += p * dp;
+            }
+            double e = 0.0;
+            for (int64_t d = 0; d < D; ++d)
+                e += fabs(gi[d] * o[d]);
+            m[r] = mx;
+            l[r] = sum;
+            rd[r] = acc;
+            re[r] = e;
+        }
+        /* implicit barrier: every row's statistics are ready */
+
+        /* pass 2, the requested query rows: dQ_i */
+#pragma omp for schedule(dynamic, 8)
+        for (int64_t t = 0; t < cq; ++t) {
+            const int64_t r = qrows ? qrows[t] : t;
+            const int64_t bh = r / Nq, i = r % Nq;
+            const double *qi = q + r * D, *gi = dout + r * D;
+            const double *kb = k + bh * Nk * D, *vb = v + bh * Nk * D;
+            const int64_t n = valid_keys(i, Nk, causal);
+            double *gq = dq + t * D;
+            double *mq = magn ? bq + t * D : NULL;
+            for (int64_t d = 0; d < D; ++d) {
+                gq[d] = 0.0;
+                if (mq)
+                    mq[d] = 0.0;
+            }
+            for (int64_t j = 0; j < n; ++j) {
+                double dot = 0.0, dp = 0.0;
+                for (int64_t d = 0; d < D; ++d) {
+                    dot += qi[d] * kb[j * D + d];
+                    dp += gi[d] * vb[j * D + d];
+                }
+                const double p = exp(scale * dot - m[r]) / l[r];
+                const double ds = p * (dp - rd[r]);
+                const double w = fabs(ds) + p * re[r];
+                for (int64_t d = 0; d < D; ++d) {
+                    gq[d] += ds * kb[j * D + d];
+                    if (mq)
+                        mq[d] += w * fabs(kb[j * D + d]);
+                }
+            }
+            for (int64_t d = 0; d < D; ++d) {
+                gq[d] *= scale;
+                if (mq)
+                    mq[d] *= fabs(scale);
+            }
+        }
+
+        /* pass 3, the requested key rows: dK_j and dV_j */
+#pragma omp for schedule(dynamic, 8)
+        for (int64_t t = 0; t < ck; ++t) {
+            const int64_t c = krows ? krows[t] : t;
+            const int64_t bh = c / Nk, j = c % Nk;
+            const double *kj = k + c * D, *vj = v + c * D;
+            double *gk = dk + t * D, *gv = dv + t * D;
+            double *mk = magn ? bk + t * D : NULL, *mv = magn ? bv + t * D : NULL;
+            for (int64_t d = 0; d < D; ++d) {
+                gk[d] = gv[d] = 0.0;
+                if (magn)
+                    mk[d] = mv[d] = 0.0;
+            }
+            /* rows that see key j: all rows, or i >= j when causal */
+            for (int64_t i = causal ? j : 0; i < Nq; ++i) {
+                const int64_t r = bh * Nq + i;
+                const double *qi = q + r * D, *gi = dout + r * D;
+                double dot = 0.0, dp = 0.0;
+                for (int64_t d = 0; d < D; ++d) {
+                    dot += qi[d] * kj[d];
+                    dp += gi[d] * vj[d];
+                }
+                const double p = exp(scale * dot - m[r]) / l[r];
+                const double ds = p * (dp - rd[r]);
+                const double w = fabs(ds) + p * re[r];
+                for (int64_t d = 0; d < D; ++d) {
+                    gv[d] += p * gi[d];
+                    gk[d] += ds * qi[d];
+                    if (magn) {
+                        mv[d] += p * fabs(gi[d]);
+                        mk[d] += w * fabs(qi[d]);
+                    }
+                }
+            }
+            for (int64_t d = 0; d < D; ++d) {
+                gk[d] *= scale;
+                if (magn)
+                    mk[d] *= fabs(scale);
+            }
+        }
+        free(s);
+        free(o);
+    }
+    free(m);
+    free(l);
+    free(rd);
+    free(re);
+    return failed ? ORACLE_ENOMEM : ORACLE_OK;
+}

@@ -9,6 +9,7 @@ import pytest
 
 import oracle
 from pins import ALL_PINS
+from pins_bwd import ALL_BWD_PINS
 
 MUTATIONS = {
     "drop_scale": ("w[j] = scale * dot;", "w[j] = dot;"),
@@ -28,6 +29,29 @@ MUTATIONS = {
     "online_alpha_not_applied_to_acc": ("ar[d] = alpha * ar[d] + pv;", "ar[d] = ar[d] + pv;"),
     "online_alpha_not_applied_to_l": ("l[r] = alpha * l[r] + psum;", "l[r] = l[r] + psum;"),
     "online_mask_direction": ("if (causal && !(i >= j))", "if (causal && !(i <= j))"),
+}
+
+
+_DS_Q = ("const double ds = p * (dp - rd[r]);\n                const double w = fabs(ds) + "
+         "p * re[r];\n                for (int64_t d = 0; d < D; ++d) {\n                    gq")
+_DS_K = _DS_Q[:-2] + "gv"
+
+# Planted mistakes in the backward pass (fa_oracle_attention_bwd).
+BWD_MUTATIONS = {
+    "bwd_row_term_without_p": ("acc += p * dp;", "acc += dp;"),
+    "bwd_dv_without_p": ("gv[d] += p * gi[d];", "gv[d] += gi[d];"),
+    "bwd_dk_uses_do": ("gk[d] += ds * qi[d];", "gk[d] += ds * gi[d];"),
+    "bwd_dq_uses_v": ("gq[d] += ds * kb[j * D + d];", "gq[d] += ds * vb[j * D + d];"),
+    "bwd_dkdv_mask_off_by_one": ("for (int64_t i = causal ? j : 0; i < Nq; ++i)",
+                                 "for (int64_t i = causal ? j + 1 : 0; i < Nq; ++i)"),
+    "bwd_dq_without_scale": ("gq[d] *= scale;", "gq[d] *= 1.0;"),
+    "bwd_dk_without_scale": ("gk[d] *= scale;", "gk[d] *= 1.0;"),
+    "bwd_transposed_v_in_row_term": ("dp += gi[d] * vb[j * D + d];\n                    o[d]",
+                                     "dp += gi[d] * vb[d * Nk + j];\n                    o[d]"),
+    "bwd_dq_row_term_sign": (_DS_Q, _DS_Q.replace("(dp - rd[r])", "(dp + rd[r])")),
+    "bwd_dk_row_term_dropped": (_DS_K, _DS_K.replace("(dp - rd[r])", "dp")),
+    "bwd_normaliser_squared": ("sum += exp(s[j] - mx);", "sum += exp(2 * (s[j] - mx));"),
+    "bwd_dk_score_uses_v": ("dot += qi[d] * kj[d];", "dot += qi[d] * vj[d];"),
 }
 
 
@@ -55,8 +79,21 @@ def test_mutation_is_caught(tmp_path, name):
     assert failures, f"no pin caught the planted mistake {name!r}"
 
 
+@pytest.mark.parametrize("name", sorted(BWD_MUTATIONS))
+def test_bwd_mutation_is_caught(tmp_path, name):
+    old, new = BWD_MUTATIONS[name]
+    lib = _mutated_lib(tmp_path, name, old, new)
+    failures = []
+    for pin in ALL_BWD_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, RuntimeError, FloatingPointError) as e:
+            failures.append((pin.__name__, str(e)[:80]))
+    assert failures, f"no backward pin caught the planted mistake {name!r}"
+
+
 def test_unmutated_source_passes_every_pin(tmp_path):
     lib = _mutated_lib(tmp_path, "identity", "int fa_oracle_threads(void)",
                        "int fa_oracle_threads(void)")
-    for pin in ALL_PINS:
+    for pin in ALL_PINS + ALL_BWD_PINS:
         pin(lib)

@@ -12,6 +12,10 @@ Workload shapes follow the sweep on the page "FlashAttention-2实现与优化：
 dataset; i.i.d. Gaussian tensors of those shapes stand in for real
 activations.
 
+The backward pass also needs an upstream gradient dO of O: ``gen_grad_out``
+draws it the same way (i.i.d. N(0,1), its own seed, rounded to the storage
+dtype).
+
 Generation recipe (fixed, so every consumer sees identical values):
   * one ``torch.Generator`` on the CPU, ``manual_seed(seed)``;
   * draw q, then k, then v, each ``randn([B, H, N, D])`` in fp32;
@@ -29,6 +33,7 @@ import torch
 __all__ = [
     "Workload",
     "gen_qkv",
+    "gen_grad_out",
     "sample_rows",
     "WORKLOADS",
     "workload",
@@ -88,6 +93,19 @@ def gen_qkv(B: int, H: int, Nq: int, Nk: int, D: int, seed: int,
         v.mul_(std)
     t = _DTYPES[dtype]
     return q.to(t).contiguous(), k.to(t).contiguous(), v.to(t).contiguous()
+
+
+def gen_grad_out(B: int, H: int, Nq: int, D: int, seed: int, dtype: str = "bf16"
+                 ) -> torch.Tensor:
+    """Upstream gradient dO [B,H,Nq,D] for the backward pass: i.i.d. N(0,1) in
+    fp32 from its own CPU generator (seeded with ``seed``), rounded to
+    ``dtype``."""
+    if dtype not in _DTYPES:
+        raise ValueError(f"unknown dtype {dtype!r}")
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    do = torch.randn((B, H, Nq, D), generator=g, dtype=torch.float32)
+    return do.to(_DTYPES[dtype]).contiguous()
 
 
 def gen_workload(w: Workload):
