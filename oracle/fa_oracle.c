@@ -268,11 +268,15 @@ int fa_oracle_online(const double *q, const double *k, const double *v,
  *
  *     bv_j = sum_i P_ij |dO_i|
  *     bq_i = scale * sum_j (|dS_ij| + P_ij E_i) |k_j|
- *     bk_j = scale * sum_i (|dS_ij| + P_ij E_i) |q_i|,   E_i = sum_d |dO_id O_id|
+ *     bk_j = scale * sum_i (|dS_ij| + P_ij E_i) |q_i|,
+ *     E_i  = sum_d |dO_id| sum_j P_ij |v_jd|
  *
- * which bound the effect of rounding one factor of every product (and the
- * row term D_i through O) to a short floating-point type; tests derive their
- * tolerances from them.
+ * which bound the effect of rounding one factor of every product to a short
+ * floating-point type.  E_i bounds the row term's sensitivity to its O: a
+ * GPU forms D_i as <dO_i, O_i> from the forward's stored O, whose error from
+ * rounding P is at most a unit roundoff times sum_j P_ij |v_jd| per element
+ * (which also covers rounding O itself, since |O_id| is no larger).  Tests
+ * derive their tolerances from these sums.
  *
  * qrows / krows optionally restrict dq (and bq) to a list of flat query rows
  * (b*H + h)*Nq + i and dk, dv (and bk, bv) to flat key rows (b*H + h)*Nk + j;
@@ -303,7 +307,8 @@ int fa_oracle_attention_bwd(const double *q, const double *k, const double *v,
     const int64_t ck = krows ? nk : totk;
     const int magn = bq && bk && bv;
 
-    /* per-row statistics: max m, normaliser l, row term D, and E */
+    /* per-row statistics: max m, normaliser l, row term D, and E
+       (o below holds sum_j P_ij |v_j|, the magnitude of row i of O) */
     double *m = (double *)malloc((size_t)totq * sizeof(double));
     double *l = (double *)malloc((size_t)totq * sizeof(double));
     double *rd = (double *)malloc((size_t)totq * sizeof(double));
@@ -354,13 +359,13 @@ int fa_oracle_attention_bwd(const double *q, const double *k, const double *v,
                 double dp = 0.0;
                 for (int64_t d = 0; d < D; ++d) {
                     dp += gi[d] * vb[j * D + d];
-                    o[d] += p * vb[j * D + d];
+                    o[d] += p * fabs(vb[j * D + d]);
                 }
                 acc += p * dp;
             }
             double e = 0.0;
             for (int64_t d = 0; d < D; ++d)
-                e += fabs(gi[d] * o[d]);
+                e += fabs(gi[d]) * o[d];
             m[r] = mx;
             l[r] = sum;
             rd[r] = acc;

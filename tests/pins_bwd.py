@@ -189,7 +189,7 @@ def pin_bwd_magnitudes(lib):
         dp = np.einsum("bhid,bhjd->bhij", g, v)
         o = np.einsum("bhij,bhjd->bhid", p, v)
         rowterm = (g * o).sum(-1, keepdims=True)
-        e = np.abs(g * o).sum(-1, keepdims=True)
+        e = (np.abs(g) * np.einsum("bhij,bhjd->bhid", p, np.abs(v))).sum(-1, keepdims=True)
         w = np.abs(p * (dp - rowterm)) + p * e
         _close(bv, np.einsum("bhij,bhid->bhjd", p, np.abs(g)), 1e-12, "bV definition")
         _close(bq, scale * np.einsum("bhij,bhjd->bhid", w, np.abs(k)), 1e-12,
