@@ -1,5 +1,6 @@
 /*
- * fa.h -- C ABI of the MI355X (gfx950) FlashAttention-2 forward library.
+ * fa.h -- C ABI of the MI355X (gfx950) FlashAttention-2 library: the
+ * forward pass (fa_fwd, fa_fwd_ws) and its backward pass (fa_bwd).
  *
  * The operation (page "FlashAttention-2实现与优化：高效注意力机制详解",
  * §3.1 PyTorch forward and §3.2 Triton forward; page
@@ -149,6 +150,60 @@ int fa_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse,
               int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
               float scale, int causal, int dtype, void *workspace,
               size_t workspace_bytes, void *stream);
+
+/*
+ * fa_bwd_workspace_size -- device scratch bytes that fa_bwd needs (written
+ * to *bytes): B * H * Nq * 4, one fp32 row term per query row.
+ *
+ * Returns FA_OK, FA_ERR_NULLPTR (bytes NULL), FA_ERR_SHAPE, FA_ERR_HEAD_DIM
+ * or FA_ERR_DTYPE, with the rules of fa_bwd.
+ */
+int fa_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                          int64_t D, int causal, int dtype, size_t *bytes);
+
+/*
+ * fa_bwd -- enqueue the backward pass of fa_fwd on `stream`: the gradients
+ * dq, dk, dv of sum(dout * O) for the upstream gradient dout of O.
+ *
+ * The pages describe the backward pass as recomputing the attention
+ * probabilities block by block from the saved logsumexp instead of storing
+ * them (page "解释FlashAttention的显存优化原理" §一.2(2); page
+ * "FlashAttention-2实现与优化：高效注意力机制详解" §3.1 saves q, k, v, o and L
+ * for it, §7 lists it as the next step).  With P_ij = exp(scale <q_i, k_j>
+ * - L_i) over the visible pairs (the forward's mask rule):
+ *
+ *     dv_j = sum_i P_ij dout_i
+ *     dS_ij = P_ij (<dout_i, v_j> - <dout_i, o_i>)
+ *     dq_i = scale sum_j dS_ij k_j,     dk_j = scale sum_i dS_ij q_i
+ *
+ *   q, k, v    the forward's inputs, [B,H,Nq,D] / [B,H,Nk,D], 16-bit
+ *   o          the forward's output O, [B,H,Nq,D], same 16-bit type
+ *   lse        the forward's L, [B,H,Nq] fp32
+ *   dout       upstream gradient of O, [B,H,Nq,D], same 16-bit type
+ *   dq         [B,H,Nq,D] (written); dk, dv [B,H,Nk,D] (written)
+ *   B .. causal  as fa_fwd; D must be 32, 64 or 128
+ *   dtype      FA_BF16 / FA_F16: every tensor in that type (gradients
+ *              rounded once, at the end); FA_BF16_OF32 / FA_F16_OF32: the
+ *              same inputs, gradients stored in fp32.  FA_F32 is not
+ *              supported here (FA_ERR_DTYPE).
+ *   workspace  device pointer, 16-byte aligned, at least
+ *              fa_bwd_workspace_size bytes (overwritten)
+ *   stream     a hipStream_t (NULL = the default stream)
+ *
+ * Products are formed from 16-bit operands with fp32 accumulation; P and dS
+ * are rounded to the input type before they multiply dout, q and k.  Every
+ * gradient element is written by exactly one workgroup, with plain stores:
+ * results are deterministic.  Returns FA_OK once enqueued, a validation
+ * error (nothing enqueued: FA_ERR_NULLPTR, FA_ERR_SHAPE, FA_ERR_HEAD_DIM,
+ * FA_ERR_DTYPE, FA_ERR_SCALE, FA_ERR_ALIGN, FA_ERR_WORKSPACE, or
+ * FA_ERR_OVERLAP when dq, dk, dv or the workspace overlap an input or each
+ * other), or FA_ERR_HIP.  The library allocates nothing.
+ */
+int fa_bwd(const void *q, const void *k, const void *v, const void *o,
+           const float *lse, const void *dout, void *dq, void *dk, void *dv,
+           int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+           float scale, int causal, int dtype, void *workspace,
+           size_t workspace_bytes, void *stream);
 
 /* Static description of a status code; never NULL. */
 const char *fa_status_str(int status);

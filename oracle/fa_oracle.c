@@ -281,7 +281,8 @@ int fa_oracle_online(const double *q, const double *k, const double *v,
  * qrows / krows optionally restrict dq (and bq) to a list of flat query rows
  * (b*H + h)*Nq + i and dk, dv (and bk, bv) to flat key rows (b*H + h)*Nk + j;
  * the outputs are then [nq, D] / [nk, D] in list order.  Row statistics are
- * always computed for every row, since a key's gradient needs all of them.
+ * computed for every row of each (b, h) slice that holds a requested row,
+ * since a key's gradient needs all of them.
  */
 int fa_oracle_attention_bwd(const double *q, const double *k, const double *v,
                             const double *dout,
@@ -320,6 +321,24 @@ int fa_oracle_attention_bwd(const double *q, const double *k, const double *v,
         free(re);
         return ORACLE_ENOMEM;
     }
+    /* slices (b, h) that hold a requested row: only their statistics are
+       needed */
+    unsigned char *need = (unsigned char *)calloc((size_t)(B * H), 1);
+    if (!need) {
+        free(m);
+        free(l);
+        free(rd);
+        free(re);
+        return ORACLE_ENOMEM;
+    }
+    if (!qrows || !krows)
+        memset(need, 1, (size_t)(B * H));
+    else {
+        for (int64_t t = 0; t < nq; ++t)
+            need[qrows[t] / Nq] = 1;
+        for (int64_t t = 0; t < nk; ++t)
+            need[krows[t] / Nk] = 1;
+    }
     int failed = 0;
 
 #pragma omp parallel
@@ -333,7 +352,7 @@ int fa_oracle_attention_bwd(const double *q, const double *k, const double *v,
         /* pass 1, every query row: scores, m, l, then P, dP, D_i and E_i */
 #pragma omp for schedule(dynamic, 8)
         for (int64_t r = 0; r < totq; ++r) {
-            if (!s || !o)
+            if (!s || !o || !need[r / Nq])
                 continue;
             const int64_t bh = r / Nq, i = r % Nq;
             const double *qi = q + r * D, *gi = dout + r * D;
@@ -453,6 +472,7 @@ int fa_oracle_attention_bwd(const double *q, const double *k, const double *v,
         free(s);
         free(o);
     }
+    free(need);
     free(m);
     free(l);
     free(rd);

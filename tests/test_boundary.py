@@ -152,3 +152,44 @@ def test_workspace_size_null_output():
     lib = fa.library()
     assert lib.fa_fwd_workspace_size(1, 1, 64, 64, 64, 0, fa.FA_BF16, None) == \
         fa.FA_ERR_NULLPTR
+
+
+# --- fa_bwd: every validation error precedes device work -------------------
+DO, DQ, DK, DV, WS = 0x60000000, 0x70000000, 0x80000000, 0x90000000, 0xA0000000
+
+
+def call_bwd(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, do=DO, dq=DQ, dk=DK, dv=DV, B=2, H=3, Nq=100,
+             Nk=90, D=64, scale=0.125, causal=1, dtype=fa.FA_BF16, ws=WS, ws_bytes=1 << 20,
+             stream=None)
+    a.update(kw)
+    return fa.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                     a["dv"], a["B"], a["H"], a["Nq"], a["Nk"], a["D"], a["scale"],
+                     a["causal"], a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("arg", ["q", "k", "v", "o", "lse", "do", "dq", "dk", "dv"])
+def test_bwd_null_pointers(arg):
+    assert call_bwd(**{arg: None}) == fa.FA_ERR_NULLPTR
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"B": 0}, "FA_ERR_SHAPE"), ({"Nq": 0}, "FA_ERR_SHAPE"), ({"Nk": -1}, "FA_ERR_SHAPE"),
+    ({"D": 16}, "FA_ERR_HEAD_DIM"), ({"D": 96}, "FA_ERR_HEAD_DIM"),
+    ({"dtype": 0}, "FA_ERR_DTYPE"), ({"dtype": 5}, "FA_ERR_DTYPE"),
+    ({"scale": math.inf}, "FA_ERR_SCALE"), ({"scale": math.nan}, "FA_ERR_SCALE"),
+    ({"dq": DQ + 8}, "FA_ERR_ALIGN"), ({"do": DO + 2}, "FA_ERR_ALIGN"),
+    ({"lse": L + 2}, "FA_ERR_ALIGN"), ({"ws": WS + 4}, "FA_ERR_ALIGN"),
+    ({"ws": None}, "FA_ERR_WORKSPACE"), ({"ws_bytes": 2 * 3 * 100 * 4 - 1}, "FA_ERR_WORKSPACE"),
+    ({"dq": Q}, "FA_ERR_OVERLAP"), ({"dk": DV}, "FA_ERR_OVERLAP"),
+    ({"ws": L}, "FA_ERR_OVERLAP"), ({"dv": O + 1024}, "FA_ERR_OVERLAP"),
+])
+def test_bwd_validation(kw, status):
+    assert call_bwd(**kw) == getattr(fa, status)
+
+
+def test_bwd_workspace_size():
+    st, n = fa.fa_bwd_workspace_size(2, 3, 100, 90, 64, 1, fa.FA_BF16)
+    assert (st, n) == (fa.FA_OK, 2 * 3 * 100 * 4)
+    assert fa.fa_bwd_workspace_size(2, 3, 100, 90, 16, 1, fa.FA_BF16)[0] == fa.FA_ERR_HEAD_DIM
+    assert fa.fa_bwd_workspace_size(2, 3, 100, 90, 64, 1, fa.FA_F32)[0] == fa.FA_ERR_DTYPE

@@ -1,7 +1,7 @@
-"""Python binding of libfa.so, the MI355X FlashAttention-2 forward library.
+"""Python binding of libfa.so, the MI355X FlashAttention-2 library.
 
-The binding marshals arguments only: every step of the forward pass runs in
-the HIP kernels of libfa.so (csrc/fa_fwd.hip).  PyTorch is used to allocate
+The binding marshals arguments only: every step of the forward and backward
+passes runs in the HIP kernels of libfa.so (csrc/fa_fwd.hip, csrc/fa_bwd.hip).  PyTorch is used to allocate
 the outputs and to name the current HIP stream.  There is no fallback: if
 libfa.so is missing or fails to load, every call raises.
 
@@ -11,6 +11,10 @@ C-ABI mirrors (same names and meaning as include/fa.h):
     fa_fwd_workspace_size(B, H, Nq, Nk, D, causal, dtype) -> (status, bytes)
     fa_fwd_ws(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Nq, Nk, D, scale,
               causal, dtype, ws_ptr, ws_bytes, stream) -> status
+    fa_bwd_workspace_size(B, H, Nq, Nk, D, causal, dtype) -> (status, bytes)
+    fa_bwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_ptr,
+           B, H, Nq, Nk, D, scale, causal, dtype, ws_ptr, ws_bytes, stream)
+        -> status
     fa_status_str(status) -> str
     fa_last_hip_error() -> str
     fa_version() -> int
@@ -18,6 +22,8 @@ Tensor convenience:
     fwd(q, k, v, causal=False, scale=None, out_dtype=None, split=True)
         -> (o, lse); split=True runs fa_fwd_ws with a workspace from torch's
         allocator, split=False runs fa_fwd
+    bwd(q, k, v, o, lse, do, causal=False, scale=None, grad_dtype=None)
+        -> (dq, dk, dv) through fa_bwd
 """
 from __future__ import annotations
 
@@ -31,8 +37,8 @@ __all__ = [
     "FA_OK", "FA_ERR_NULLPTR", "FA_ERR_SHAPE", "FA_ERR_HEAD_DIM", "FA_ERR_DTYPE",
     "FA_ERR_SCALE", "FA_ERR_ALIGN", "FA_ERR_HIP", "FA_ERR_OVERLAP", "FA_ERR_WORKSPACE",
     "LIBRARY", "EXPORTS", "library", "fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws",
-    "fa_status_str", "fa_last_hip_error",
-    "fa_version", "fwd", "FaError",
+    "fa_bwd_workspace_size", "fa_bwd", "fa_status_str", "fa_last_hip_error",
+    "fa_version", "fwd", "bwd", "FaError",
 ]
 
 LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
@@ -42,8 +48,8 @@ FA_F32, FA_BF16, FA_BF16_OF32, FA_F16, FA_F16_OF32 = 0, 1, 2, 3, 4
  FA_ERR_ALIGN, FA_ERR_HIP, FA_ERR_OVERLAP, FA_ERR_WORKSPACE) = range(10)
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws", "fa_status_str",
-           "fa_last_hip_error", "fa_version")
+EXPORTS = ("fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws", "fa_bwd_workspace_size",
+           "fa_bwd", "fa_status_str", "fa_last_hip_error", "fa_version")
 
 _lib = None
 
@@ -74,6 +80,13 @@ def library() -> ctypes.CDLL:
     lib.fa_fwd_ws.restype = ctypes.c_int
     lib.fa_fwd_ws.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
                               ctypes.c_int, ctypes.c_int, vp, ctypes.c_size_t, vp]
+    lib.fa_bwd_workspace_size.restype = ctypes.c_int
+    lib.fa_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int,
+                                          ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+    lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                           ctypes.c_float, ctypes.c_int, ctypes.c_int, vp, ctypes.c_size_t,
+                           vp]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_status_str.argtypes = [ctypes.c_int]
     lib.fa_last_hip_error.restype = ctypes.c_char_p
@@ -103,6 +116,22 @@ def fa_fwd_ws(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, dtype, ws, ws_byt
     """Raw C call; pointers are integers (device addresses) or None."""
     return int(library().fa_fwd_ws(q, k, v, o, lse, B, H, Nq, Nk, D, float(scale),
                                    int(causal), int(dtype), ws, int(ws_bytes), stream))
+
+
+def fa_bwd_workspace_size(B, H, Nq, Nk, D, causal, dtype) -> Tuple[int, int]:
+    """Raw C call; returns (status, workspace bytes)."""
+    n = ctypes.c_size_t(0)
+    st = int(library().fa_bwd_workspace_size(B, H, Nq, Nk, D, int(causal), int(dtype),
+                                             ctypes.byref(n)))
+    return st, int(n.value)
+
+
+def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, B, H, Nq, Nk, D, scale, causal, dtype, ws,
+           ws_bytes, stream) -> int:
+    """Raw C call; pointers are integers (device addresses) or None."""
+    return int(library().fa_bwd(q, k, v, o, lse, do, dq, dk, dv, B, H, Nq, Nk, D,
+                                float(scale), int(causal), int(dtype), ws, int(ws_bytes),
+                                stream))
 
 
 def fa_status_str(status: int) -> str:
@@ -201,3 +230,65 @@ def fwd(q, k, v, causal: bool = False, scale: Optional[float] = None,
             msg += ": " + fa_last_hip_error()
         raise FaError(st, msg)
     return o, lse
+
+
+def bwd(q, k, v, o, lse, do, causal: bool = False, scale: Optional[float] = None,
+        grad_dtype=None, out=None, stream=None
+        ) -> Tuple["torch.Tensor", "torch.Tensor", "torch.Tensor"]:
+    """Attention backward on device tensors (fa_bwd).
+
+    q, o, do: [B,Nq,D] or [B,H,Nq,D]; k, v: [B,Nk,D] or [B,H,Nk,D]; all of
+    one 16-bit dtype (bf16 or fp16), same device, contiguous; lse fp32 shaped
+    like q[..., 0] (the forward's outputs o and lse).  Returns (dq, dk, dv)
+    shaped like q, k, v in ``grad_dtype`` (default: the input dtype; fp32
+    keeps the gradients unrounded).  ``scale`` defaults to 1/sqrt(D) and
+    must equal the forward's.  The row-term workspace comes from torch's
+    allocator.
+    """
+    import torch
+
+    t = (q, k, v, o, do)
+    if q.dim() not in (3, 4) or any(x.dim() != q.dim() for x in t):
+        raise ValueError("q, k, v, o, do must all be [B,N,D] or all [B,H,N,D]")
+    three = q.dim() == 3
+    q4, k4 = (x.unsqueeze(1) if three else x for x in (q, k))
+    B, H, Nq, D = q4.shape
+    Nk = k4.shape[2]
+    if (tuple(k.shape) != tuple(v.shape) or tuple(o.shape) != tuple(q.shape)
+            or tuple(do.shape) != tuple(q.shape) or tuple(k4.shape) != (B, H, Nk, D)):
+        raise ValueError("shape mismatch among q, k, v, o, do")
+    if tuple(lse.shape) != tuple(q.shape[:-1]) or lse.dtype != torch.float32:
+        raise ValueError("lse must be fp32 shaped like q[..., 0]")
+    if not all(x.dtype == q.dtype for x in t):
+        raise ValueError("q, k, v, o, do must share a dtype")
+    if not all(x.is_cuda and x.device == q.device for x in t + (lse,)):
+        raise ValueError("all tensors must be on the same GPU device")
+    if not all(x.is_contiguous() for x in t + (lse,)):
+        raise ValueError("all tensors must be contiguous")
+    grad_dtype = q.dtype if grad_dtype is None else grad_dtype
+    code = _dtype_code(torch, q.dtype, grad_dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        dq = torch.empty(q.shape, dtype=grad_dtype, device=q.device)
+        dk = torch.empty(k.shape, dtype=grad_dtype, device=q.device)
+        dv = torch.empty(v.shape, dtype=grad_dtype, device=q.device)
+    else:
+        dq, dk, dv = out
+    own_stream = stream is None
+    if own_stream:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st, nbytes = fa_bwd_workspace_size(B, H, Nq, Nk, D, causal, code)
+    if st == FA_OK:
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+        if not own_stream:
+            ws.record_stream(torch.cuda.ExternalStream(stream, device=q.device))
+        st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                    do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Nq,
+                    Nk, D, scale, causal, code, ws.data_ptr(), nbytes, stream)
+    if st != FA_OK:
+        msg = fa_status_str(st)
+        if st == FA_ERR_HIP:
+            msg += ": " + fa_last_hip_error()
+        raise FaError(st, msg)
+    return dq, dk, dv

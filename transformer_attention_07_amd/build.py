@@ -14,7 +14,13 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", "fa_fwd.hip")]
+# (source, extra flags): each source is compiled on its own, then linked
+SOURCES = [
+    # keep MFMA accumulators in VGPRs: the softmax and the rescale read them
+    (os.path.join(PKG, "csrc", "fa_fwd.hip"), ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
+    # the backward kernels keep their dK/dV/dQ accumulators in AGPRs
+    (os.path.join(PKG, "csrc", "fa_bwd.hip"), []),
+]
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libfa.so")
 ARCH = "gfx950"
@@ -26,23 +32,30 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # keep MFMA accumulators in VGPRs: the softmax and the rescale read them
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 
-def build(out: str = LIBRARY, extra=(), verbose: bool = False) -> str:
-    tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra, f"-I{INCLUDE}", "-o", tmp, *SOURCES]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed ({res.returncode})")
+
+
+def build(out: str = LIBRARY, extra=(), verbose: bool = False) -> str:
+    tmp = out + ".tmp"
+    objs = []
+    for src, flags in SOURCES:
+        obj = out + "." + os.path.splitext(os.path.basename(src))[0] + ".o"
+        _run([HIPCC, *FLAGS, *flags, *extra, f"-I{INCLUDE}", "-c", "-o", obj, src], verbose)
+        objs.append(obj)
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+    for obj in objs:
+        os.remove(obj)
     os.replace(tmp, out)
     return out
 

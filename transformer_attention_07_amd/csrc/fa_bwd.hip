@@ -1,0 +1,621 @@
+// fa_bwd.hip -- FlashAttention-2 backward pass for MI355X (gfx950, CDNA4).
+//
+// The method: the forward pass keeps only O and the per-row logsumexp L
+// (page "FlashAttention-2实现与优化：高效注意力机制详解", §3.1, which saves
+// q, k, v, o and L for the backward pass and lists it under §7); the
+// backward pass recomputes the attention probabilities block by block from
+// L instead of reading a stored N x N matrix (page "解释FlashAttention的显存
+// 优化原理", §一.2(2), recomputation).  With the upstream gradient dO:
+//
+//     P_ij  = exp(scale <q_i, k_j> - L_i)      (visible pairs, else 0)
+//     dV_j  = sum_i P_ij dO_i
+//     dP_ij = <dO_i, v_j>
+//     Dl_i  = <dO_i, O_i>                      (= sum_j P_ij dP_ij)
+//     dS_ij = P_ij (dP_ij - Dl_i)
+//     dQ_i  = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i
+//
+// Three kernels, enqueued in order on the caller's stream:
+//   * fa_bwd_prep: Dl_i = <dO_i, O_i> in fp32 into the workspace.
+//   * fa_bwd_dkdv: one workgroup per (batch*head, 128 keys), 32 keys per
+//     wave held in VGPRs as MFMA B operands; it streams 32-query blocks of Q
+//     and dO through LDS (double-buffered) and accumulates dV^T and dK^T.
+//   * fa_bwd_dq: one workgroup per (batch*head, 128 queries), 32 queries per
+//     wave held in VGPRs; it streams 32-key blocks of K and V through LDS
+//     and accumulates dQ^T.
+// Recomputing S and dP in both kernels (instead of fp32 atomics on dQ)
+// keeps every result deterministic and every store plain.
+//
+// gfx950 mapping (v_mfma_f32_32x32x16_{bf16,f16}, fp32 accumulation):
+//   * dK/dV kernel: S = Q K^T and dP = dO V^T with lane l owning key l%32;
+//     the accumulator registers of S and dS, rounded to the input type, are
+//     directly the B operands of dV^T += dO^T P and dK^T += Q^T dS (the
+//     contraction index, queries, is permuted identically on both sides), so
+//     P never leaves registers.  dO^T and Q^T fragments come from
+//     ds_read_b64_tr_b16 (lane L of a 16-lane group receives four
+//     consecutive rows of column d0 + L).
+//   * dQ kernel: S^T = K Q^T and dP^T = V dO^T with lane l owning query l%32
+//     (so L_i and Dl_i are per-lane scalars); dQ^T += K^T dS^T with K^T from
+//     the same transpose read.
+//   * Causal: a wave skips (wave-uniformly) every block in which no pair is
+//     visible; blocks on the diagonal and past Nq / Nk are masked by setting
+//     P to 0.  Rows past Nq get L = +inf (P = 0), rows past Nk read as zero
+//     and are never stored.
+//   * Exponentials in base 2: P = 2^(c <q, k> - L log2 e), c = scale log2 e;
+//     the scale of dQ and dK is applied once, in fp32, at the store.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "fa.h"
+
+// Records the runtime's text for fa_last_hip_error (defined with the
+// forward pass's host code) and returns FA_ERR_HIP.
+int fa_internal_hip_fail(hipError_t e);
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kWaves = 4;
+constexpr int kThreads = kWave * kWaves;
+constexpr int kOwn = 32;                // keys / queries owned by one wave
+constexpr int kTile = kOwn * kWaves;    // keys / queries per workgroup
+constexpr int kBlk = 32;                // rows per block streamed through LDS
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) float lds_float;
+
+template <typename T> struct Mma;
+
+template <> struct Mma<__bf16> {
+  typedef bf16x8 frag;
+  static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // (a, b) rounded to nearest-even bf16, a in the low half.
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    const f32x2 x = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+  }
+  static __device__ __forceinline__ f32x2 unpack2(uint32_t x) {
+    return __builtin_convertvector(__builtin_bit_cast(bf16x2, x), f32x2);
+  }
+};
+
+template <> struct Mma<_Float16> {
+  typedef f16x8 frag;
+  static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    const f32x2 x = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2));
+  }
+  static __device__ __forceinline__ f32x2 unpack2(uint32_t x) {
+    return __builtin_convertvector(__builtin_bit_cast(f16x2, x), f32x2);
+  }
+};
+
+// LDS image of one block of kBlk rows of a [N, D] 16-bit tensor, row-major.
+// The row stride (in bytes) is 16 * odd, so the 16 rows of one ds_read_b128
+// pass start on distinct 16-byte bank groups, and the four rows of one
+// ds_read_b64_tr_b16 group land on disjoint 32-byte ranges.
+template <int D> struct Blk {
+  static constexpr int STRIDE = D == 128 ? 304 : D == 64 ? 208 : 112;
+  static constexpr int BYTES = kBlk * STRIDE;
+};
+
+// Register staging of one block: global -> VGPRs -> LDS, 16 bytes a piece.
+template <int D> struct Stage {
+  static constexpr int CPR = D / 8;  // 16-byte pieces per row
+  static constexpr int PIECES = kBlk * CPR;
+  static constexpr int N = (PIECES + kThreads - 1) / kThreads;
+  u32x4 r[N];
+
+  // rows row0 .. row0+kBlk-1 of a slice with nrows rows; missing rows are 0
+  __device__ __forceinline__ void load(const void *slice, int row0, int nrows, int tid) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      const int c = tid + n * kThreads;
+      r[n] = u32x4{0u, 0u, 0u, 0u};
+      if (c < PIECES) {
+        const int row = row0 + c / CPR;
+        if (row < nrows)
+          r[n] = *(const u32x4 *)((const char *)slice + (size_t)row * (D * 2) + (c % CPR) * 16);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(lds_char *dst, int tid) const {
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      const int c = tid + n * kThreads;
+      if (c < PIECES)
+        *(lds_u32x4 *)(dst + (c / CPR) * Blk<D>::STRIDE + (c % CPR) * 16) = r[n];
+    }
+  }
+};
+
+__device__ __forceinline__ u32x2 read_tr16(const lds_char *p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p);
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// A operand (32 x 16, rows = head-dim columns d0 .. d0+31 of the block,
+// contraction = 16 block rows r0 ..) read transposed from a row-major LDS
+// block.  Contraction slot e of half-wave g holds block row
+// r0 + 8*(e/4) + 4*g + e%4, the row order of a 32x32 accumulator's
+// registers 8*t' .. 8*t'+7, so the matching B operand is those registers.
+template <typename T, int D>
+__device__ __forceinline__ typename Mma<T>::frag tr_frag(const lds_char *blk, int r0, int d0,
+                                                       int lane) {
+  const int s = lane & 15, g16 = (lane >> 4) & 1, g = lane >> 5;
+  const lds_char *p =
+      blk + (r0 + 4 * g + (s >> 2)) * Blk<D>::STRIDE + (d0 + 16 * g16 + 4 * (s & 3)) * 2;
+  const u32x2 lo = read_tr16(p);
+  const u32x2 hi = read_tr16(p + 8 * Blk<D>::STRIDE);
+  const u32x4 raw = {lo[0], lo[1], hi[0], hi[1]};
+  return __builtin_bit_cast(typename Mma<T>::frag, raw);
+}
+
+// A operand read row-wise: lane l holds block row l%32, columns
+// d0 + 8*(l/32) .. +7.
+template <typename T, int D>
+__device__ __forceinline__ typename Mma<T>::frag row_frag(const lds_char *blk, int d0,
+                                                        int lane) {
+  const lds_char *p = blk + (lane & 31) * Blk<D>::STRIDE + (d0 + 8 * (lane >> 5)) * 2;
+  return __builtin_bit_cast(typename Mma<T>::frag, *(const lds_u32x4 *)p);
+}
+
+// Registers 8t' .. 8t'+7 of an accumulator, rounded to T, as a B operand.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag pack_b(const float *x) {
+  const u32x4 raw = {Mma<T>::pack2(x[0], x[1]), Mma<T>::pack2(x[2], x[3]),
+                     Mma<T>::pack2(x[4], x[5]), Mma<T>::pack2(x[6], x[7])};
+  return __builtin_bit_cast(typename Mma<T>::frag, raw);
+}
+
+// Row `row` (or zeros past nrows) of a [N, D] slice: 16 bytes at column d0.
+template <typename T, int D>
+__device__ __forceinline__ typename Mma<T>::frag glob_frag(const T *slice, int row, int nrows,
+                                                         int d0) {
+  u32x4 raw = {0u, 0u, 0u, 0u};
+  if (row < nrows) raw = *(const u32x4 *)(slice + (size_t)row * D + d0);
+  return __builtin_bit_cast(typename Mma<T>::frag, raw);
+}
+
+template <typename OT> __device__ __forceinline__ void store4(OT *dst, f32x4 x);
+template <> __device__ __forceinline__ void store4<float>(float *dst, f32x4 x) {
+  *(f32x4 *)dst = x;
+}
+template <> __device__ __forceinline__ void store4<__bf16>(__bf16 *dst, f32x4 x) {
+  const u32x2 w = {Mma<__bf16>::pack2(x[0], x[1]), Mma<__bf16>::pack2(x[2], x[3])};
+  *(u32x2 *)dst = w;
+}
+template <> __device__ __forceinline__ void store4<_Float16>(_Float16 *dst, f32x4 x) {
+  const u32x2 w = {Mma<_Float16>::pack2(x[0], x[1]), Mma<_Float16>::pack2(x[2], x[3])};
+  *(u32x2 *)dst = w;
+}
+
+// Stores a 32 x 32 accumulator holding rows d = d0 + 8(r/4) + 4g + r%4 of a
+// transposed gradient for the lane's row `row` of the [N, D] output, times
+// `mul`.
+template <typename OT, int D>
+__device__ __forceinline__ void store_t(OT *slice, int row, int d0, int g, const f32x16 &acc,
+                                        float mul) {
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) {
+    const f32x4 x = {acc[4 * r4] * mul, acc[4 * r4 + 1] * mul, acc[4 * r4 + 2] * mul,
+                     acc[4 * r4 + 3] * mul};
+    store4<OT>(slice + (size_t)row * D + d0 + 8 * r4 + 4 * g, x);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dl_i = <dO_i, O_i>, fp32, one row per D/8 lanes.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void fa_bwd_prep(const T *__restrict__ o,
+                                                        const T *__restrict__ dout,
+                                                        float *__restrict__ dl, int64_t rows) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = kThreads / LPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int part = threadIdx.x % LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 a = *(const u32x4 *)(o + row * D + part * 8);
+    const u32x4 b = *(const u32x4 *)(dout + row * D + part * 8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const f32x2 x = Mma<T>::unpack2(a[w]), y = Mma<T>::unpack2(b[w]);
+      acc = fmaf(x[0], y[0], acc);
+      acc = fmaf(x[1], y[1], acc);
+    }
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (part == 0 && row < rows) dl[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// dK and dV: one workgroup per (batch*head, 128 keys).
+template <typename T, typename OT, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void fa_bwd_dkdv(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    const T *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dl,
+    OT *__restrict__ dk, OT *__restrict__ dv, int Nq, int Nk, int BH, float c, float scale) {
+  using M = Mma<T>;
+  typedef typename M::frag frag;
+  constexpr int KF = D / 16;  // MFMA steps along D
+  constexpr int NC = D / 32;  // 32-row chunks of dK^T / dV^T
+  constexpr int BB = Blk<D>::BYTES;
+  // [buffer][Q, dO] blocks, then [buffer] L*log2(e) and Dl of the block's rows
+  __shared__ __attribute__((aligned(16))) char smem_raw[4 * BB + 4 * kBlk * 4];
+  lds_char *smem = (lds_char *)smem_raw;
+  lds_float *stats = (lds_float *)(smem + 4 * BB);
+
+  const int bh = blockIdx.x % BH;
+  const int kt = blockIdx.x / BH;  // causal: the lowest keys see the most queries: first
+  const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
+  const int g = lane >> 5, col = lane & 31;
+  const int key0 = kt * kTile + w * kOwn;
+  const int myk = key0 + col;
+  const T *qs = q + (size_t)bh * Nq * D;
+  const T *dos = dout + (size_t)bh * Nq * D;
+  const T *ks = k + (size_t)bh * Nk * D;
+  const T *vs = v + (size_t)bh * Nk * D;
+  const float *ls = lse + (size_t)bh * Nq;
+  const float *ds_ = dl + (size_t)bh * Nq;
+
+  frag kf[KF], vf[KF];
+#pragma unroll
+  for (int t = 0; t < KF; ++t) {
+    kf[t] = glob_frag<T, D>(ks, myk, Nk, 16 * t + 8 * g);
+    vf[t] = glob_frag<T, D>(vs, myk, Nk, 16 * t + 8 * g);
+  }
+  f32x16 dva[NC], dka[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) {
+    dva[cc] = f32x16{};
+    dka[cc] = f32x16{};
+  }
+
+  // queries before the tile's first key see none of its keys
+  const int qstart = CAUSAL ? kt * kTile : 0;
+  const int nblk = qstart < Nq ? (Nq - qstart + kBlk - 1) / kBlk : 0;
+
+  Stage<D> sq, sdo;
+  float stat = 0.f;
+  auto gload = [&](int b) {
+    const int row0 = qstart + b * kBlk;
+    sq.load(qs, row0, Nq, tid);
+    sdo.load(dos, row0, Nq, tid);
+    if (tid < kBlk) {
+      const int r = row0 + tid;
+      stat = r < Nq ? ls[r] * kLog2e : INFINITY;  // P = 0 on rows past Nq
+    } else if (tid < 2 * kBlk) {
+      const int r = row0 + tid - kBlk;
+      stat = r < Nq ? ds_[r] : 0.f;
+    }
+  };
+  auto sstore = [&](int buf) {
+    sq.store(smem + buf * 2 * BB, tid);
+    sdo.store(smem + buf * 2 * BB + BB, tid);
+    if (tid < 2 * kBlk) stats[buf * 2 * kBlk + tid] = stat;
+  };
+
+  if (nblk > 0) {
+    gload(0);
+    sstore(0);
+  }
+  __syncthreads();
+  for (int b = 0; b < nblk; ++b) {
+    const int cur = b & 1;
+    if (b + 1 < nblk) gload(b + 1);
+    const int i0 = qstart + b * kBlk;
+    // wave-uniform: does any query of this block see a key of this wave?
+    if (!CAUSAL || i0 + kBlk - 1 >= key0) {
+      const lds_char *qb = smem + cur * 2 * BB;
+      const lds_char *db = qb + BB;
+      const lds_float *l2 = stats + cur * 2 * kBlk;
+      const lds_float *dd = l2 + kBlk;
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int t = 0; t < KF; ++t) {
+        s = M::mma(row_frag<T, D>(qb, 16 * t, lane), kf[t], s);
+        dp = M::mma(row_frag<T, D>(db, 16 * t, lane), vf[t], dp);
+      }
+      float p[16], dsv[16];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int ib = 8 * r4 + 4 * g;  // block row of register 4*r4
+        const f32x4 lv = *(const __attribute__((address_space(3))) f32x4 *)(l2 + ib);
+        const f32x4 dv4 = *(const __attribute__((address_space(3))) f32x4 *)(dd + ib);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e;
+          float pr = exp2f(fmaf(s[r], c, -lv[e]));
+          if (CAUSAL && myk > i0 + ib + e) pr = 0.f;
+          p[r] = pr;
+          dsv[r] = pr * (dp[r] - dv4[e]);
+        }
+      }
+#pragma unroll
+      for (int tp = 0; tp < 2; ++tp) {
+        const frag pb = pack_b<T>(p + 8 * tp);
+        const frag sb = pack_b<T>(dsv + 8 * tp);
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+          dva[cc] = M::mma(tr_frag<T, D>(db, 16 * tp, 32 * cc, lane), pb, dva[cc]);
+          dka[cc] = M::mma(tr_frag<T, D>(qb, 16 * tp, 32 * cc, lane), sb, dka[cc]);
+        }
+      }
+    }
+    if (b + 1 < nblk) sstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  if (myk < Nk) {
+    OT *dks = dk + (size_t)bh * Nk * D;
+    OT *dvs = dv + (size_t)bh * Nk * D;
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      store_t<OT, D>(dvs, myk, 32 * cc, g, dva[cc], 1.f);
+      store_t<OT, D>(dks, myk, 32 * cc, g, dka[cc], scale);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per (batch*head, 128 queries).
+template <typename T, typename OT, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void fa_bwd_dq(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    const T *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dl,
+    OT *__restrict__ dq, int Nq, int Nk, int BH, int nqt, float c, float scale) {
+  using M = Mma<T>;
+  typedef typename M::frag frag;
+  constexpr int KF = D / 16;
+  constexpr int NC = D / 32;
+  constexpr int BB = Blk<D>::BYTES;
+  // [buffer][K, V] blocks
+  __shared__ __attribute__((aligned(16))) char smem_raw[4 * BB];
+  lds_char *smem = (lds_char *)smem_raw;
+
+  const int bh = blockIdx.x % BH;
+  // causal: the last query tiles see the most keys: first
+  const int qt = CAUSAL ? nqt - 1 - (int)(blockIdx.x / BH) : (int)(blockIdx.x / BH);
+  const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
+  const int g = lane >> 5, col = lane & 31;
+  const int qw0 = qt * kTile + w * kOwn;
+  const int myq = qw0 + col;
+  const T *qs = q + (size_t)bh * Nq * D;
+  const T *dos = dout + (size_t)bh * Nq * D;
+  const T *ks = k + (size_t)bh * Nk * D;
+  const T *vs = v + (size_t)bh * Nk * D;
+
+  frag qf[KF], df[KF];
+#pragma unroll
+  for (int t = 0; t < KF; ++t) {
+    qf[t] = glob_frag<T, D>(qs, myq, Nq, 16 * t + 8 * g);
+    df[t] = glob_frag<T, D>(dos, myq, Nq, 16 * t + 8 * g);
+  }
+  const float l2 = myq < Nq ? lse[(size_t)bh * Nq + myq] * kLog2e : INFINITY;
+  const float dd = myq < Nq ? dl[(size_t)bh * Nq + myq] : 0.f;
+  f32x16 dqa[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) dqa[cc] = f32x16{};
+
+  // keys past the tile's last query are hidden from all its rows
+  const int kend = CAUSAL ? min(Nk, qt * kTile + kTile) : Nk;
+  const int nblk = (kend + kBlk - 1) / kBlk;
+
+  Stage<D> sk, sv;
+  auto gload = [&](int b) {
+    sk.load(ks, b * kBlk, Nk, tid);
+    sv.load(vs, b * kBlk, Nk, tid);
+  };
+  auto sstore = [&](int buf) {
+    sk.store(smem + buf * 2 * BB, tid);
+    sv.store(smem + buf * 2 * BB + BB, tid);
+  };
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int b = 0; b < nblk; ++b) {
+    const int cur = b & 1;
+    if (b + 1 < nblk) gload(b + 1);
+    const int j0 = b * kBlk;
+    // wave-uniform: does any key of this block reach a query of this wave?
+    if (!CAUSAL || j0 <= qw0 + kOwn - 1) {
+      const lds_char *kb = smem + cur * 2 * BB;
+      const lds_char *vb = kb + BB;
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int t = 0; t < KF; ++t) {
+        s = M::mma(row_frag<T, D>(kb, 16 * t, lane), qf[t], s);
+        dp = M::mma(row_frag<T, D>(vb, 16 * t, lane), df[t], dp);
+      }
+      float dsv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = j0 + 8 * (r >> 2) + 4 * g + (r & 3);
+        float pr = exp2f(fmaf(s[r], c, -l2));
+        if (j >= Nk || (CAUSAL && j > myq)) pr = 0.f;
+        dsv[r] = pr * (dp[r] - dd);
+      }
+#pragma unroll
+      for (int tp = 0; tp < 2; ++tp) {
+        const frag sb = pack_b<T>(dsv + 8 * tp);
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc)
+          dqa[cc] = M::mma(tr_frag<T, D>(kb, 16 * tp, 32 * cc, lane), sb, dqa[cc]);
+      }
+    }
+    if (b + 1 < nblk) sstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  if (myq < Nq) {
+    OT *dqs = dq + (size_t)bh * Nq * D;
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) store_t<OT, D>(dqs, myq, 32 * cc, g, dqa[cc], scale);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+
+struct BwdArgs {
+  const void *q, *k, *v, *o, *dout;
+  const float *lse;
+  void *dq, *dk, *dv;
+  float *dl;
+  int Nq, Nk, BH;
+  float scale;
+  hipStream_t stream;
+};
+
+template <typename T, typename OT, int D, bool CAUSAL>
+hipError_t launch_bwd(const BwdArgs &a) {
+  const float c = a.scale * kLog2e;
+  const int64_t rows = (int64_t)a.BH * a.Nq;
+  constexpr int RPB = kThreads / (D / 8);
+  hipLaunchKernelGGL((fa_bwd_prep<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)),
+                     dim3(kThreads), 0, a.stream, (const T *)a.o, (const T *)a.dout, a.dl,
+                     rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nkt = (a.Nk + kTile - 1) / kTile;
+  const int nqt = (a.Nq + kTile - 1) / kTile;
+  hipLaunchKernelGGL((fa_bwd_dkdv<T, OT, D, CAUSAL>), dim3((unsigned)(a.BH * nkt)),
+                     dim3(kThreads), 0, a.stream, (const T *)a.q, (const T *)a.k,
+                     (const T *)a.v, (const T *)a.dout, a.lse, (const float *)a.dl,
+                     (OT *)a.dk, (OT *)a.dv, a.Nq, a.Nk, a.BH, c, a.scale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((fa_bwd_dq<T, OT, D, CAUSAL>), dim3((unsigned)(a.BH * nqt)),
+                     dim3(kThreads), 0, a.stream, (const T *)a.q, (const T *)a.k,
+                     (const T *)a.v, (const T *)a.dout, a.lse, (const float *)a.dl,
+                     (OT *)a.dq, a.Nq, a.Nk, a.BH, nqt, c, a.scale);
+  return hipGetLastError();
+}
+
+template <typename T, typename OT>
+hipError_t dispatch_bwd(const BwdArgs &a, int D, bool causal) {
+  switch (D) {
+    case 32: return causal ? launch_bwd<T, OT, 32, true>(a) : launch_bwd<T, OT, 32, false>(a);
+    case 64: return causal ? launch_bwd<T, OT, 64, true>(a) : launch_bwd<T, OT, 64, false>(a);
+    default:
+      return causal ? launch_bwd<T, OT, 128, true>(a) : launch_bwd<T, OT, 128, false>(a);
+  }
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+int check_shape(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int dtype) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
+  if (D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  if (dtype != FA_BF16 && dtype != FA_BF16_OF32 && dtype != FA_F16 && dtype != FA_F16_OF32)
+    return FA_ERR_DTYPE;
+  const int64_t lim = (int64_t)1 << 31;
+  // per-slice byte offsets (fp32 gradients at most 4 bytes an element) fit in
+  // 32 bits; grids are one-dimensional
+  if (Nq > lim / (D * 4) - kTile || Nk > lim / (D * 4) - kTile) return FA_ERR_SHAPE;
+  if (B > lim || H > lim || B * H > lim / ((Nq > Nk ? Nq : Nk) / kTile + 1)) return FA_ERR_SHAPE;
+  if (B * H * Nq > lim) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+                          int causal, int dtype, size_t *bytes) {
+  (void)causal;
+  if (!bytes) return FA_ERR_NULLPTR;
+  *bytes = 0;
+  const int st = check_shape(B, H, Nq, Nk, D, dtype);
+  if (st != FA_OK) return st;
+  *bytes = (size_t)(B * H * Nq) * sizeof(float);
+  return FA_OK;
+}
+
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+           const void *dout, void *dq, void *dk, void *dv, int64_t B, int64_t H, int64_t Nq,
+           int64_t Nk, int64_t D, float scale, int causal, int dtype, void *workspace,
+           size_t workspace_bytes, void *stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULLPTR;
+  int st = check_shape(B, H, Nq, Nk, D, dtype);
+  if (st != FA_OK) return st;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout |
+       (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv) & 15u)
+    return FA_ERR_ALIGN;
+  if (((uintptr_t)lse & 3u) || ((uintptr_t)workspace & 15u)) return FA_ERR_ALIGN;
+  const int64_t BH = B * H;
+  const size_t gsz = (dtype == FA_BF16_OF32 || dtype == FA_F16_OF32) ? 4 : 2;
+  const size_t qb = (size_t)(BH * Nq * D) * 2, kb = (size_t)(BH * Nk * D) * 2;
+  const size_t lb = (size_t)(BH * Nq) * 4;
+  const size_t dqb = (size_t)(BH * Nq * D) * gsz, dkb = (size_t)(BH * Nk * D) * gsz;
+  const size_t need = lb;
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  // written buffers against every buffer of the call
+  const void *outs[4] = {dq, dk, dv, workspace};
+  const size_t osz[4] = {dqb, dkb, dkb, need};
+  const void *ins[6] = {q, k, v, o, dout, lse};
+  const size_t isz[6] = {qb, kb, kb, qb, qb, lb};
+  for (int x = 0; x < 4; ++x) {
+    for (int y = 0; y < 6; ++y)
+      if (overlaps(outs[x], osz[x], ins[y], isz[y])) return FA_ERR_OVERLAP;
+    for (int y = x + 1; y < 4; ++y)
+      if (overlaps(outs[x], osz[x], outs[y], osz[y])) return FA_ERR_OVERLAP;
+  }
+  BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dl = (float *)workspace;
+  a.Nq = (int)Nq;
+  a.Nk = (int)Nk;
+  a.BH = (int)BH;
+  a.scale = scale;
+  a.stream = (hipStream_t)stream;
+  const bool cz = causal != 0;
+  hipError_t e;
+  switch (dtype) {
+    case FA_BF16: e = dispatch_bwd<__bf16, __bf16>(a, (int)D, cz); break;
+    case FA_BF16_OF32: e = dispatch_bwd<__bf16, float>(a, (int)D, cz); break;
+    case FA_F16: e = dispatch_bwd<_Float16, _Float16>(a, (int)D, cz); break;
+    default: e = dispatch_bwd<_Float16, float>(a, (int)D, cz); break;
+  }
+  if (e != hipSuccess) return fa_internal_hip_fail(e);
+  return FA_OK;
+}
+
+}  // extern "C"

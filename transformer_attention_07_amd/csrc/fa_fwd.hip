@@ -1453,9 +1453,14 @@ int run(const void *q, const void *k, const void *v, void *o, float *lse, int64_
 
 }  // namespace
 
+// Shared with the backward pass's host code (same library, hidden symbol).
+__attribute__((visibility("hidden"))) int fa_internal_hip_fail(hipError_t e) {
+  return hip_fail(e);
+}
+
 extern "C" {
 
-int fa_version(void) { return 200; }
+int fa_version(void) { return 300; }
 
 const char *fa_status_str(int s) {
   switch (s) {
