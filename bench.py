@@ -3,6 +3,9 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
+--pass bwd times fa_bwd instead (the backward pass, fed by one forward
+call; a separate line, not the default).
+
 One step is one call of fa_fwd_ws (the whole forward pass: the attention
 kernel and, when the plan splits long query tiles, the kernel that combines
 the parts) over the workload's synthetic inputs, which are resident in
@@ -29,6 +32,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak (B8 N4096 D128 causal)"
+METRIC_BWD = "attention bwd TFLOP/s + % bf16 MFMA peak (2.5x fwd flops)"
 # MI355X published dense peaks (TFLOP/s).
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
 # Transcendental rate for the exp roofline of small head dims: v_exp_f32 at
@@ -113,6 +117,37 @@ def cpu_baseline(w, target_s: float):
     }
 
 
+def cpu_baseline_bwd(w, target_s: float):
+    """Time the fp64 oracle's backward pass on the host cores over the whole
+    workload (repeated to fill the time budget when it is short)."""
+    import oracle
+    from workloads import gen_grad_out, gen_workload
+
+    q, k, v = gen_workload(w)
+    g = gen_grad_out(w.B, w.H, w.N, w.D, seed=w.seed + 10000, dtype=w.dtype)
+    qn, kn, vn, gn = (t.double().numpy() for t in (q, k, v, g))
+    scale = 1.0 / math.sqrt(w.D)
+    lib = oracle.load()
+    t0 = time.perf_counter()
+    oracle.attention_bwd(qn, kn, vn, gn, scale, w.causal, lib=lib)
+    first = time.perf_counter() - t0
+    reps = int(max(0, min(20, target_s / max(first, 1e-9) - 1)))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle.attention_bwd(qn, kn, vn, gn, scale, w.causal, lib=lib)
+    elapsed = first + (time.perf_counter() - t0)
+    t_full = elapsed / (reps + 1)
+    return {
+        "value": 2.5 * w.flops() / t_full / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.threads(lib),
+        "kind": "oracle",
+        "sample": f"the whole workload's dQ, dK, dV, {reps + 1} passes",
+        "seconds": round(elapsed, 3),
+        "seconds_full_workload": round(t_full, 6),
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -131,6 +166,11 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--entry", choices=("fa_fwd_ws", "fa_fwd"), default="fa_fwd_ws",
                     help="C entry point to time (default: fa_fwd_ws, with scratch)")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
+                    help="time the forward pass (default) or the backward pass "
+                         "(fa_bwd, fed by one forward call; flops counted as 2.5x "
+                         "the forward's: the five N x N contractions of the "
+                         "recomputing backward)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -172,6 +212,30 @@ def main() -> int:
         argv = argv + (sp,)
         call = lib.fa_fwd
 
+    bwd = args.which == "bwd"
+    if bwd:
+        from workloads import gen_grad_out
+
+        st = call(*argv)  # the forward pass whose O and L the backward consumes
+        if st != 0:
+            raise RuntimeError(f"forward failed: {fa.fa_status_str(st)}")
+        g = gen_grad_out(w.B, w.H, w.N, w.D, seed=w.seed + 10000, dtype=w.dtype).to(dev)
+        grad_dt = out_dt
+        bcode = fa._dtype_code(torch, in_dt, grad_dt)
+        dq = torch.empty(q.shape, dtype=grad_dt, device=dev)
+        dk = torch.empty(k.shape, dtype=grad_dt, device=dev)
+        dv = torch.empty(v.shape, dtype=grad_dt, device=dev)
+        st, ws_bytes = fa.fa_bwd_workspace_size(w.B, w.H, w.N, w.N, w.D, int(w.causal),
+                                                bcode)
+        if st != 0:
+            raise RuntimeError(f"fa_bwd_workspace_size failed: {fa.fa_status_str(st)}")
+        bws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        argv = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                g.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), w.B, w.H, w.N,
+                w.N, w.D, scale, int(w.causal), bcode, bws.data_ptr(), ws_bytes, sp)
+        call = lib.fa_bwd
+        args.entry = "fa_bwd"
+
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -207,7 +271,7 @@ def main() -> int:
     group_ms = sorted(evs[a].elapsed_time(evs[b]) / (b - a) for a, b in zip(marks, marks[1:]))
 
     ms_per_step = wall * 1e3 / args.steps
-    flops = w.flops()
+    flops = w.flops() * (2.5 if bwd else 1.0)
     value = flops / (ms_per_step * 1e-3) / 1e12
     dkey = "f32" if in_dt == torch.float32 else ("bf16" if in_dt == torch.bfloat16 else "f16")
     peak = PEAK_TFLOPS[dkey]
@@ -215,7 +279,7 @@ def main() -> int:
     props = torch.cuda.get_device_properties(dev)
 
     line = {
-        "metric": METRIC,
+        "metric": METRIC if not bwd else METRIC_BWD,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "pct_of_peak": round(100.0 * value / peak, 2),
@@ -234,7 +298,7 @@ def main() -> int:
                    "workspace_bytes": ws_bytes},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": measured_traffic(name),
+                     "traffic": None if bwd else measured_traffic(name),
                      "kernel_ms": round(kernel_ms, 5),
                      "group_ms": {"groups": len(group_ms),
                                   "median": round(group_ms[len(group_ms) // 2], 5),
@@ -242,7 +306,7 @@ def main() -> int:
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count},
     }
-    if w.D <= 64:
+    if w.D <= 64 and not bwd:
         # one exp per visible score (half of them when causal): at small head
         # dims the softmax's transcendentals, not the MFMAs, bound the kernel
         exps = w.B * w.H * w.N * w.N / (2 if w.causal else 1)
@@ -250,7 +314,8 @@ def main() -> int:
         line["exp_roofline"] = {"achieved": round(rate, 3), "peak": round(EXP_PEAK_T, 3),
                                 "unit": "Texp/s", "frac": round(rate / EXP_PEAK_T, 4)}
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        line["cpu_baseline"] = (cpu_baseline_bwd(w, args.cpu_seconds) if bwd
+                                else cpu_baseline(w, args.cpu_seconds))
     print(json.dumps(line), flush=True)
     return 0
 

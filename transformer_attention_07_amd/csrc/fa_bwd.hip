@@ -16,11 +16,12 @@
 //
 // Three kernels, enqueued in order on the caller's stream:
 //   * fa_bwd_prep: Dl_i = <dO_i, O_i> in fp32 into the workspace.
-//   * fa_bwd_dkdv: one workgroup per (batch*head, 128 keys), 32 keys per
-//     wave held in VGPRs as MFMA B operands; it streams 32-query blocks of Q
-//     and dO through LDS (double-buffered) and accumulates dV^T and dK^T.
-//   * fa_bwd_dq: one workgroup per (batch*head, 128 queries), 32 queries per
-//     wave held in VGPRs; it streams 32-key blocks of K and V through LDS
+//   * fa_bwd_dkdv: one workgroup per (batch*head, 64 keys), 32 keys per
+//     wave held in VGPRs as MFMA B operands; it streams 128-query blocks of
+//     Q and dO through LDS (double-buffered, each wave taking two 32-row
+//     quarters of a block) and accumulates dV^T and dK^T.
+//   * fa_bwd_dq: one workgroup per (batch*head, 64 queries), 32 queries per
+//     wave held in VGPRs; it streams 128-key blocks of K and V through LDS
 //     and accumulates dQ^T.
 // Recomputing S and dP in both kernels (instead of fp32 atomics on dQ)
 // keeps every result deterministic and every store plain.
@@ -60,9 +61,17 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWave * kWaves;
-constexpr int kOwn = 32;                // keys / queries owned by one wave
-constexpr int kTile = kOwn * kWaves;    // keys / queries per workgroup
-constexpr int kBlk = 32;                // rows per block streamed through LDS
+constexpr int kOwn = 32;  // keys / queries owned by one wave
+// Workgroups of four waves: two groups of 32 keys (or queries), and two
+// parities that split each streamed block between them, summed at the end.
+// 64 keys per workgroup make causal problems twice as many, finer
+// workgroups, issued longest first, so the compute units stay evenly loaded
+// (a wave has a SIMD to itself: its accumulators need more than 256
+// registers at D = 128).
+constexpr int kTile = 2 * kOwn;  // keys / queries per workgroup
+// Rows per block streamed through LDS: four 32-row quarters, two per wave,
+// so one quarter's MFMAs can run beside the other's exponentials.
+constexpr int kBlk = 128;
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -172,12 +181,13 @@ __device__ __forceinline__ typename Mma<T>::frag tr_frag(const lds_char *blk, in
   return __builtin_bit_cast(typename Mma<T>::frag, raw);
 }
 
-// A operand read row-wise: lane l holds block row l%32, columns
+// A operand read row-wise: lane l holds block row r0 + l%32, columns
 // d0 + 8*(l/32) .. +7.
 template <typename T, int D>
-__device__ __forceinline__ typename Mma<T>::frag row_frag(const lds_char *blk, int d0,
+__device__ __forceinline__ typename Mma<T>::frag row_frag(const lds_char *blk, int r0, int d0,
                                                         int lane) {
-  const lds_char *p = blk + (lane & 31) * Blk<D>::STRIDE + (d0 + 8 * (lane >> 5)) * 2;
+  const lds_char *p =
+      blk + (r0 + (lane & 31)) * Blk<D>::STRIDE + (d0 + 8 * (lane >> 5)) * 2;
   return __builtin_bit_cast(typename Mma<T>::frag, *(const lds_u32x4 *)p);
 }
 
@@ -252,7 +262,39 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_prep(const T *__restrict__ o,
 }
 
 // ---------------------------------------------------------------------------
-// dK and dV: one workgroup per (batch*head, 128 keys).
+// Sum of the two parity halves of a workgroup's accumulators: waves with
+// par = 1 leave theirs in LDS, waves with par = 0 add them.  `buf` must be
+// free (every wave past the last barrier of the main loop).
+template <int N>
+__device__ __forceinline__ void pair_sum(f32x16 (&acc)[N], lds_char *buf, int grp, int par,
+                                         int lane) {
+  typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+  lds_f32x4 *x = (lds_f32x4 *)(buf + grp * (N * 16 * 4 * kWave));
+  if (par == 1) {
+#pragma unroll
+    for (int n = 0; n < N; ++n)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        x[(n * 4 + r4) * kWave + lane] =
+            f32x4{acc[n][4 * r4], acc[n][4 * r4 + 1], acc[n][4 * r4 + 2], acc[n][4 * r4 + 3]};
+  }
+  __syncthreads();
+  if (par == 0) {
+#pragma unroll
+    for (int n = 0; n < N; ++n)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 y = x[(n * 4 + r4) * kWave + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[n][4 * r4 + e] += y[e];
+      }
+  }
+}
+
+// dK and dV: one workgroup per (batch*head, kTile keys).  Wave w owns keys
+// key0 + 32*(w & 1) .. +31 and, of every 128-query block, the 32-row
+// quarters par and par + 2 (par = w >> 1); the two parities are summed at
+// the end.
 template <typename T, typename OT, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
@@ -272,7 +314,8 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv(
   const int kt = blockIdx.x / BH;  // causal: the lowest keys see the most queries: first
   const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
   const int g = lane >> 5, col = lane & 31;
-  const int key0 = kt * kTile + w * kOwn;
+  const int grp = w & 1, par = w >> 1;
+  const int key0 = kt * kTile + grp * kOwn;
   const int myk = key0 + col;
   const T *qs = q + (size_t)bh * Nq * D;
   const T *dos = dout + (size_t)bh * Nq * D;
@@ -298,78 +341,98 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv(
   const int qstart = CAUSAL ? kt * kTile : 0;
   const int nblk = qstart < Nq ? (Nq - qstart + kBlk - 1) / kBlk : 0;
 
-  Stage<D> sq, sdo;
+  Stage<D> st;
   float stat = 0.f;
-  auto gload = [&](int b) {
-    const int row0 = qstart + b * kBlk;
-    sq.load(qs, row0, Nq, tid);
-    sdo.load(dos, row0, Nq, tid);
-    if (tid < kBlk) {
-      const int r = row0 + tid;
+  auto load_stat = [&](int row0) {
+    const int r = row0 + (tid & (kBlk - 1));
+    if (tid < kBlk)
       stat = r < Nq ? ls[r] * kLog2e : INFINITY;  // P = 0 on rows past Nq
-    } else if (tid < 2 * kBlk) {
-      const int r = row0 + tid - kBlk;
+    else
       stat = r < Nq ? ds_[r] : 0.f;
-    }
   };
-  auto sstore = [&](int buf) {
-    sq.store(smem + buf * 2 * BB, tid);
-    sdo.store(smem + buf * 2 * BB + BB, tid);
-    if (tid < 2 * kBlk) stats[buf * 2 * kBlk + tid] = stat;
-  };
+  auto qbuf = [&](int buf) { return smem + buf * 2 * BB; };
 
   if (nblk > 0) {
-    gload(0);
-    sstore(0);
+    st.load(qs, qstart, Nq, tid);
+    st.store(qbuf(0), tid);
+    st.load(dos, qstart, Nq, tid);
+    st.store(qbuf(0) + BB, tid);
+    load_stat(qstart);
+    stats[tid] = stat;
   }
   __syncthreads();
   for (int b = 0; b < nblk; ++b) {
     const int cur = b & 1;
-    if (b + 1 < nblk) gload(b + 1);
+    const bool nx = b + 1 < nblk;
     const int i0 = qstart + b * kBlk;
-    // wave-uniform: does any query of this block see a key of this wave?
-    if (!CAUSAL || i0 + kBlk - 1 >= key0) {
-      const lds_char *qb = smem + cur * 2 * BB;
-      const lds_char *db = qb + BB;
-      const lds_float *l2 = stats + cur * 2 * kBlk;
-      const lds_float *dd = l2 + kBlk;
-      f32x16 s = f32x16{}, dp = f32x16{};
+    if (nx) {
+      st.load(qs, i0 + kBlk, Nq, tid);
+      load_stat(i0 + kBlk);
+    }
+    // wave-uniform: does any of this wave's queries see one of its keys?
+    const bool live = !CAUSAL || i0 + kOwn * (par + 2) + kOwn - 1 >= key0;
+    const lds_char *qb = qbuf(cur);
+    const lds_char *db = qb + BB;
+    const lds_float *l2 = stats + cur * 2 * kBlk;
+    const lds_float *dd = l2 + kBlk;
+    f32x16 s[2], dp[2];
+    if (live) {
 #pragma unroll
-      for (int t = 0; t < KF; ++t) {
-        s = M::mma(row_frag<T, D>(qb, 16 * t, lane), kf[t], s);
-        dp = M::mma(row_frag<T, D>(db, 16 * t, lane), vf[t], dp);
-      }
-      float p[16], dsv[16];
+      for (int hf = 0; hf < 2; ++hf) {
+        const int r0 = kOwn * (par + 2 * hf);
+        s[hf] = f32x16{};
+        dp[hf] = f32x16{};
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int ib = 8 * r4 + 4 * g;  // block row of register 4*r4
-        const f32x4 lv = *(const __attribute__((address_space(3))) f32x4 *)(l2 + ib);
-        const f32x4 dv4 = *(const __attribute__((address_space(3))) f32x4 *)(dd + ib);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * r4 + e;
-          float pr = exp2f(fmaf(s[r], c, -lv[e]));
-          if (CAUSAL && myk > i0 + ib + e) pr = 0.f;
-          p[r] = pr;
-          dsv[r] = pr * (dp[r] - dv4[e]);
-        }
-      }
-#pragma unroll
-      for (int tp = 0; tp < 2; ++tp) {
-        const frag pb = pack_b<T>(p + 8 * tp);
-        const frag sb = pack_b<T>(dsv + 8 * tp);
-#pragma unroll
-        for (int cc = 0; cc < NC; ++cc) {
-          dva[cc] = M::mma(tr_frag<T, D>(db, 16 * tp, 32 * cc, lane), pb, dva[cc]);
-          dka[cc] = M::mma(tr_frag<T, D>(qb, 16 * tp, 32 * cc, lane), sb, dka[cc]);
+        for (int t = 0; t < KF; ++t) {
+          s[hf] = M::mma(row_frag<T, D>(qb, r0, 16 * t, lane), kf[t], s[hf]);
+          dp[hf] = M::mma(row_frag<T, D>(db, r0, 16 * t, lane), vf[t], dp[hf]);
         }
       }
     }
-    if (b + 1 < nblk) sstore(cur ^ 1);
+    if (nx) {
+      st.store(qbuf(cur ^ 1), tid);
+      stats[(cur ^ 1) * 2 * kBlk + tid] = stat;
+      st.load(dos, i0 + kBlk, Nq, tid);
+    }
+    if (live) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int r0 = kOwn * (par + 2 * hf);
+        float p[16], dsv[16];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int ib = r0 + 8 * r4 + 4 * g;  // block row of register 4*r4
+          const f32x4 lv = *(const __attribute__((address_space(3))) f32x4 *)(l2 + ib);
+          const f32x4 dv4 = *(const __attribute__((address_space(3))) f32x4 *)(dd + ib);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * r4 + e;
+            float pr = exp2f(fmaf(s[hf][r], c, -lv[e]));
+            if (CAUSAL && myk > i0 + ib + e) pr = 0.f;
+            p[r] = pr;
+            dsv[r] = pr * (dp[hf][r] - dv4[e]);
+          }
+        }
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) {
+          const frag pb = pack_b<T>(p + 8 * tp);
+          const frag sb = pack_b<T>(dsv + 8 * tp);
+#pragma unroll
+          for (int cc = 0; cc < NC; ++cc) {
+            dva[cc] = M::mma(tr_frag<T, D>(db, r0 + 16 * tp, 32 * cc, lane), pb, dva[cc]);
+            dka[cc] = M::mma(tr_frag<T, D>(qb, r0 + 16 * tp, 32 * cc, lane), sb, dka[cc]);
+          }
+        }
+      }
+    }
+    if (nx) st.store(qbuf(cur ^ 1) + BB, tid);
     __syncthreads();
   }
 
-  if (myk < Nk) {
+  pair_sum<NC>(dva, smem, grp, par, lane);
+  __syncthreads();
+  pair_sum<NC>(dka, smem, grp, par, lane);
+  if (par == 0 && myk < Nk) {
     OT *dks = dk + (size_t)bh * Nk * D;
     OT *dvs = dv + (size_t)bh * Nk * D;
 #pragma unroll
@@ -381,7 +444,9 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv(
 }
 
 // ---------------------------------------------------------------------------
-// dQ: one workgroup per (batch*head, 128 queries).
+// dQ: one workgroup per (batch*head, kTile queries).  Wave w owns queries
+// qw0 + 32*(w & 1) .. +31 and, of every 128-key block, the 32-key quarters
+// par and par + 2 (par = w >> 1); the two parities are summed at the end.
 template <typename T, typename OT, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void fa_bwd_dq(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
@@ -401,7 +466,8 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dq(
   const int qt = CAUSAL ? nqt - 1 - (int)(blockIdx.x / BH) : (int)(blockIdx.x / BH);
   const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
   const int g = lane >> 5, col = lane & 31;
-  const int qw0 = qt * kTile + w * kOwn;
+  const int grp = w & 1, par = w >> 1;
+  const int qw0 = qt * kTile + grp * kOwn;
   const int myq = qw0 + col;
   const T *qs = q + (size_t)bh * Nq * D;
   const T *dos = dout + (size_t)bh * Nq * D;
@@ -423,55 +489,68 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dq(
   // keys past the tile's last query are hidden from all its rows
   const int kend = CAUSAL ? min(Nk, qt * kTile + kTile) : Nk;
   const int nblk = (kend + kBlk - 1) / kBlk;
+  auto kbuf = [&](int buf) { return smem + buf * 2 * BB; };
 
-  Stage<D> sk, sv;
-  auto gload = [&](int b) {
-    sk.load(ks, b * kBlk, Nk, tid);
-    sv.load(vs, b * kBlk, Nk, tid);
-  };
-  auto sstore = [&](int buf) {
-    sk.store(smem + buf * 2 * BB, tid);
-    sv.store(smem + buf * 2 * BB + BB, tid);
-  };
-
-  gload(0);
-  sstore(0);
+  Stage<D> st;
+  st.load(ks, 0, Nk, tid);
+  st.store(kbuf(0), tid);
+  st.load(vs, 0, Nk, tid);
+  st.store(kbuf(0) + BB, tid);
   __syncthreads();
   for (int b = 0; b < nblk; ++b) {
     const int cur = b & 1;
-    if (b + 1 < nblk) gload(b + 1);
+    const bool nx = b + 1 < nblk;
     const int j0 = b * kBlk;
-    // wave-uniform: does any key of this block reach a query of this wave?
-    if (!CAUSAL || j0 <= qw0 + kOwn - 1) {
-      const lds_char *kb = smem + cur * 2 * BB;
-      const lds_char *vb = kb + BB;
-      f32x16 s = f32x16{}, dp = f32x16{};
+    if (nx) st.load(ks, j0 + kBlk, Nk, tid);
+    // wave-uniform: does any of this wave's keys reach one of its queries?
+    const bool live = !CAUSAL || j0 + kOwn * par <= qw0 + kOwn - 1;
+    const lds_char *kb = kbuf(cur);
+    const lds_char *vb = kb + BB;
+    f32x16 s[2], dp[2];
+    if (live) {
 #pragma unroll
-      for (int t = 0; t < KF; ++t) {
-        s = M::mma(row_frag<T, D>(kb, 16 * t, lane), qf[t], s);
-        dp = M::mma(row_frag<T, D>(vb, 16 * t, lane), df[t], dp);
-      }
-      float dsv[16];
+      for (int hf = 0; hf < 2; ++hf) {
+        const int r0 = kOwn * (par + 2 * hf);
+        s[hf] = f32x16{};
+        dp[hf] = f32x16{};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = j0 + 8 * (r >> 2) + 4 * g + (r & 3);
-        float pr = exp2f(fmaf(s[r], c, -l2));
-        if (j >= Nk || (CAUSAL && j > myq)) pr = 0.f;
-        dsv[r] = pr * (dp[r] - dd);
-      }
-#pragma unroll
-      for (int tp = 0; tp < 2; ++tp) {
-        const frag sb = pack_b<T>(dsv + 8 * tp);
-#pragma unroll
-        for (int cc = 0; cc < NC; ++cc)
-          dqa[cc] = M::mma(tr_frag<T, D>(kb, 16 * tp, 32 * cc, lane), sb, dqa[cc]);
+        for (int t = 0; t < KF; ++t) {
+          s[hf] = M::mma(row_frag<T, D>(kb, r0, 16 * t, lane), qf[t], s[hf]);
+          dp[hf] = M::mma(row_frag<T, D>(vb, r0, 16 * t, lane), df[t], dp[hf]);
+        }
       }
     }
-    if (b + 1 < nblk) sstore(cur ^ 1);
+    if (nx) {
+      st.store(kbuf(cur ^ 1), tid);
+      st.load(vs, j0 + kBlk, Nk, tid);
+    }
+    if (live) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int r0 = kOwn * (par + 2 * hf);
+        float dsv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = j0 + r0 + 8 * (r >> 2) + 4 * g + (r & 3);
+          float pr = exp2f(fmaf(s[hf][r], c, -l2));
+          if (j >= Nk || (CAUSAL && j > myq)) pr = 0.f;
+          dsv[r] = pr * (dp[hf][r] - dd);
+        }
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) {
+          const frag sb = pack_b<T>(dsv + 8 * tp);
+#pragma unroll
+          for (int cc = 0; cc < NC; ++cc)
+            dqa[cc] = M::mma(tr_frag<T, D>(kb, r0 + 16 * tp, 32 * cc, lane), sb, dqa[cc]);
+        }
+      }
+    }
+    if (nx) st.store(kbuf(cur ^ 1) + BB, tid);
     __syncthreads();
   }
 
-  if (myq < Nq) {
+  pair_sum<NC>(dqa, smem, grp, par, lane);
+  if (par == 0 && myq < Nq) {
     OT *dqs = dq + (size_t)bh * Nq * D;
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) store_t<OT, D>(dqs, myq, 32 * cc, g, dqa[cc], scale);
