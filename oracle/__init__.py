@@ -17,6 +17,13 @@ Functions (all fp64, numpy in / numpy out):
       chain rule (the pages fix no formula for the backward pass; it is the
       derivative of the definition above), plus optional magnitude sums that
       bound rounding effects.
+  attention_varlen(q, k, v, cu_q, cu_k, scale, causal) -> (o, lse)
+      variable-length batches ("FlashAttention-2实现与优化" §7, ragged input
+      sequences): q [H, Tq, D], k and v [H, Tk, D] hold S sequences packed
+      along the token axis, sequence s at rows cu_q[s] .. cu_q[s+1] (keys
+      cu_k[s] .. cu_k[s+1]); each sequence attends only to its own keys,
+      with the forward definition above applied per sequence.  A sequence
+      with queries but no keys gets O = 0 and L = -inf (the empty sum).
   threads() -> int   OpenMP threads the oracle uses.
 
 Parity status: pinned by tests/test_oracle_pins.py (closed forms, invariants,
@@ -191,6 +198,35 @@ def attention_bwd(q, k, v, do, scale: float, causal: bool, qrows=None, krows=Non
     if squeeze:
         out = [a[:, 0] if a.ndim == 4 else a for a in out]
     return tuple(out)
+
+
+def attention_varlen(q, k, v, cu_q, cu_k, scale: float, causal: bool, lib=None
+                     ) -> Tuple[np.ndarray, np.ndarray]:
+    """Variable-length attention in fp64: the two-pass definition applied to
+    each packed sequence on its own (q [H,Tq,D], k, v [H,Tk,D]; cu_q, cu_k
+    offsets of length S+1).  Returns o [H,Tq,D], lse [H,Tq]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    cu_q = [int(x) for x in cu_q]
+    cu_k = [int(x) for x in cu_k]
+    H, Tq, D = q.shape
+    if (k.shape[0] != H or v.shape != k.shape or k.shape[2] != D or len(cu_q) != len(cu_k)
+            or cu_q[0] != 0 or cu_k[0] != 0 or cu_q[-1] != Tq or cu_k[-1] != k.shape[1]
+            or any(b < a for a, b in zip(cu_q, cu_q[1:]))
+            or any(b < a for a, b in zip(cu_k, cu_k[1:]))):
+        raise ValueError("inconsistent varlen shapes or offsets")
+    o = np.zeros((H, Tq, D))
+    lse = np.full((H, Tq), -np.inf)
+    for s in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = cu_q[s], cu_q[s + 1], cu_k[s], cu_k[s + 1]
+        if q1 == q0 or k1 == k0:
+            continue  # no rows, or no keys: O = 0, L = -inf
+        so, sl = attention(q[None, :, q0:q1], k[None, :, k0:k1], v[None, :, k0:k1],
+                           scale, causal, lib=lib)
+        o[:, q0:q1] = so[0]
+        lse[:, q0:q1] = sl[0]
+    return o, lse
 
 
 def threads(lib=None) -> int:
