@@ -1,6 +1,7 @@
 /*
  * fa.h -- C ABI of the MI355X (gfx950) FlashAttention-2 library: the
- * forward pass (fa_fwd, fa_fwd_ws) and its backward pass (fa_bwd).
+ * forward pass (fa_fwd, fa_fwd_ws; fa_fwd_varlen for variable-length
+ * batches) and its backward pass (fa_bwd).
  *
  * The operation (page "FlashAttention-2实现与优化：高效注意力机制详解",
  * §3.1 PyTorch forward and §3.2 Triton forward; page
@@ -150,6 +151,44 @@ int fa_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse,
               int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
               float scale, int causal, int dtype, void *workspace,
               size_t workspace_bytes, void *stream);
+
+/*
+ * fa_fwd_varlen -- the forward pass over a variable-length batch (page
+ * "FlashAttention-2实现与优化：高效注意力机制详解" §7, ragged input sequences).
+ *
+ *   q          device pointer, [H, Tq, D] of the dtype's input type: S
+ *              sequences packed along the token axis, sequence s at rows
+ *              cu_seqlens_q[s] .. cu_seqlens_q[s+1] - 1 of every head
+ *   k, v       device pointers, [H, Tk, D]; sequence s at rows
+ *              cu_seqlens_k[s] .. cu_seqlens_k[s+1] - 1
+ *   o          device pointer, [H, Tq, D] of the dtype's output type (written)
+ *   lse        device pointer, [H, Tq] fp32 (written)
+ *   cu_seqlens_q, cu_seqlens_k
+ *              device pointers to S + 1 int32 offsets each, starting at 0,
+ *              non-decreasing, ending at Tq / Tk
+ *   S, H       number of sequences (>= 1) and heads (>= 1)
+ *   Tq, Tk     total query rows (>= 1) and key rows (>= 0)
+ *   max_seqlen_q  an upper bound of every query length (rows of a longer
+ *              sequence past this bound are not computed)
+ *   D, scale, causal   as fa_fwd; the causal rule applies within each
+ *              sequence: key j of a sequence is visible to its row i iff
+ *              j <= i (indices from the sequence's first row)
+ *   dtype      FA_BF16, FA_BF16_OF32, FA_F16 or FA_F16_OF32 (FA_F32 is not
+ *              supported here: FA_ERR_DTYPE)
+ *
+ * Each sequence attends only to its own keys; its rows get exactly what
+ * fa_fwd computes for that sequence alone.  A sequence with queries and no
+ * keys gets O = 0 and lse = -inf.  The offsets live in device memory and
+ * are read by the kernel, which clamps them to [0, Tq] / [0, Tk]: offsets
+ * that break the rules above give wrong rows but never an access outside
+ * the tensors.  Validation, ownership and error codes as fa_fwd (the
+ * offsets need 4-byte alignment).
+ */
+int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
+                  const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                  int64_t S, int64_t H, int64_t Tq, int64_t Tk,
+                  int64_t max_seqlen_q, int64_t D, float scale, int causal,
+                  int dtype, void *stream);
 
 /*
  * fa_bwd_workspace_size -- device scratch bytes that fa_bwd needs (written

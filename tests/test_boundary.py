@@ -193,3 +193,28 @@ def test_bwd_workspace_size():
     assert (st, n) == (fa.FA_OK, 2 * 3 * 100 * 4)
     assert fa.fa_bwd_workspace_size(2, 3, 100, 90, 16, 1, fa.FA_BF16)[0] == fa.FA_ERR_HEAD_DIM
     assert fa.fa_bwd_workspace_size(2, 3, 100, 90, 64, 1, fa.FA_F32)[0] == fa.FA_ERR_DTYPE
+
+
+# --- fa_fwd_varlen: validation precedes device work --------------------------
+CQ, CK = 0xB0000000, 0xC0000000
+
+
+def call_varlen(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, cq=CQ, ck=CK, S=3, H=2, Tq=500, Tk=400, mq=300,
+             D=64, scale=0.125, causal=1, dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return fa.fa_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"],
+                            a["S"], a["H"], a["Tq"], a["Tk"], a["mq"], a["D"], a["scale"],
+                            a["causal"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"q": None}, "FA_ERR_NULLPTR"), ({"cq": None}, "FA_ERR_NULLPTR"),
+    ({"ck": None}, "FA_ERR_NULLPTR"), ({"S": 0}, "FA_ERR_SHAPE"), ({"Tq": 0}, "FA_ERR_SHAPE"),
+    ({"Tk": -1}, "FA_ERR_SHAPE"), ({"mq": 0}, "FA_ERR_SHAPE"), ({"D": 48}, "FA_ERR_HEAD_DIM"),
+    ({"dtype": fa.FA_F32}, "FA_ERR_DTYPE"), ({"scale": math.nan}, "FA_ERR_SCALE"),
+    ({"o": O + 8}, "FA_ERR_ALIGN"), ({"cq": CQ + 2}, "FA_ERR_ALIGN"),
+    ({"o": Q}, "FA_ERR_OVERLAP"), ({"lse": CK}, "FA_ERR_OVERLAP"),
+])
+def test_varlen_validation(kw, status):
+    assert call_varlen(**kw) == getattr(fa, status)

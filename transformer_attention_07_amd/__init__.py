@@ -11,6 +11,8 @@ C-ABI mirrors (same names and meaning as include/fa.h):
     fa_fwd_workspace_size(B, H, Nq, Nk, D, causal, dtype) -> (status, bytes)
     fa_fwd_ws(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Nq, Nk, D, scale,
               causal, dtype, ws_ptr, ws_bytes, stream) -> status
+    fa_fwd_varlen(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, cu_q_ptr, cu_k_ptr, S, H,
+                  Tq, Tk, max_seqlen_q, D, scale, causal, dtype, stream) -> status
     fa_bwd_workspace_size(B, H, Nq, Nk, D, causal, dtype) -> (status, bytes)
     fa_bwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_ptr,
            B, H, Nq, Nk, D, scale, causal, dtype, ws_ptr, ws_bytes, stream)
@@ -22,6 +24,8 @@ Tensor convenience:
     fwd(q, k, v, causal=False, scale=None, out_dtype=None, split=True)
         -> (o, lse); split=True runs fa_fwd_ws with a workspace from torch's
         allocator, split=False runs fa_fwd
+    fwd_varlen(q, k, v, cu_q, cu_k, max_seqlen_q, causal=False, scale=None,
+               out_dtype=None) -> (o, lse) through fa_fwd_varlen
     bwd(q, k, v, o, lse, do, causal=False, scale=None, grad_dtype=None)
         -> (dq, dk, dv) through fa_bwd
 """
@@ -37,8 +41,8 @@ __all__ = [
     "FA_OK", "FA_ERR_NULLPTR", "FA_ERR_SHAPE", "FA_ERR_HEAD_DIM", "FA_ERR_DTYPE",
     "FA_ERR_SCALE", "FA_ERR_ALIGN", "FA_ERR_HIP", "FA_ERR_OVERLAP", "FA_ERR_WORKSPACE",
     "LIBRARY", "EXPORTS", "library", "fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws",
-    "fa_bwd_workspace_size", "fa_bwd", "fa_status_str", "fa_last_hip_error",
-    "fa_version", "fwd", "bwd", "FaError",
+    "fa_fwd_varlen", "fa_bwd_workspace_size", "fa_bwd", "fa_status_str",
+    "fa_last_hip_error", "fa_version", "fwd", "fwd_varlen", "bwd", "FaError",
 ]
 
 LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
@@ -48,8 +52,9 @@ FA_F32, FA_BF16, FA_BF16_OF32, FA_F16, FA_F16_OF32 = 0, 1, 2, 3, 4
  FA_ERR_ALIGN, FA_ERR_HIP, FA_ERR_OVERLAP, FA_ERR_WORKSPACE) = range(10)
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws", "fa_bwd_workspace_size",
-           "fa_bwd", "fa_status_str", "fa_last_hip_error", "fa_version")
+EXPORTS = ("fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws", "fa_fwd_varlen",
+           "fa_bwd_workspace_size", "fa_bwd", "fa_status_str", "fa_last_hip_error",
+           "fa_version")
 
 _lib = None
 
@@ -80,6 +85,9 @@ def library() -> ctypes.CDLL:
     lib.fa_fwd_ws.restype = ctypes.c_int
     lib.fa_fwd_ws.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
                               ctypes.c_int, ctypes.c_int, vp, ctypes.c_size_t, vp]
+    lib.fa_fwd_varlen.restype = ctypes.c_int
+    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                  ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
     lib.fa_bwd_workspace_size.restype = ctypes.c_int
     lib.fa_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int,
                                           ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
@@ -116,6 +124,14 @@ def fa_fwd_ws(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, dtype, ws, ws_byt
     """Raw C call; pointers are integers (device addresses) or None."""
     return int(library().fa_fwd_ws(q, k, v, o, lse, B, H, Nq, Nk, D, float(scale),
                                    int(causal), int(dtype), ws, int(ws_bytes), stream))
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, S, H, Tq, Tk, max_seqlen_q, D, scale, causal,
+                  dtype, stream) -> int:
+    """Raw C call; pointers are integers (device addresses) or None."""
+    return int(library().fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, S, H, Tq, Tk,
+                                       max_seqlen_q, D, float(scale), int(causal),
+                                       int(dtype), stream))
 
 
 def fa_bwd_workspace_size(B, H, Nq, Nk, D, causal, dtype) -> Tuple[int, int]:
@@ -292,3 +308,47 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, scale: Optional[float] = None
             msg += ": " + fa_last_hip_error()
         raise FaError(st, msg)
     return dq, dk, dv
+
+
+def fwd_varlen(q, k, v, cu_q, cu_k, max_seqlen_q: int, causal: bool = False,
+               scale: Optional[float] = None, out_dtype=None, stream=None
+               ) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """Variable-length attention forward (fa_fwd_varlen) on device tensors.
+
+    q: [H, Tq, D]; k, v: [H, Tk, D] (bf16 or fp16, contiguous, one device);
+    cu_q, cu_k: int32 device tensors of S + 1 offsets (0, ..., Tq / Tk).
+    Returns (o [H, Tq, D] in ``out_dtype``, lse [H, Tq] fp32).
+    """
+    import torch
+
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be [H, T, D]")
+    H, Tq, D = q.shape
+    Tk = k.shape[1]
+    if tuple(k.shape) != (H, Tk, D) or tuple(v.shape) != (H, Tk, D):
+        raise ValueError("shape mismatch among q, k, v")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    if cu_q.dtype != torch.int32 or cu_k.dtype != torch.int32 or cu_q.shape != cu_k.shape:
+        raise ValueError("cu_q, cu_k must be int32 tensors of equal length")
+    t = (q, k, v, cu_q, cu_k)
+    if not all(x.is_cuda and x.device == q.device and x.is_contiguous() for x in t):
+        raise ValueError("all tensors must be contiguous on the same GPU device")
+    S = cu_q.numel() - 1
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    code = _dtype_code(torch, q.dtype, out_dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    lse = torch.empty((H, Tq), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       cu_q.data_ptr(), cu_k.data_ptr(), S, H, Tq, Tk, int(max_seqlen_q), D,
+                       scale, causal, code, stream)
+    if st != FA_OK:
+        msg = fa_status_str(st)
+        if st == FA_ERR_HIP:
+            msg += ": " + fa_last_hip_error()
+        raise FaError(st, msg)
+    return o, lse

@@ -1022,6 +1022,48 @@ __global__ __launch_bounds__(kThreads8) void fa_fwd_pipe8(
   pipe8_run<T, OT, D, CAUSAL, PAIR>(q, k, v, o, lse, nullptr, Nq, Nk, c, negate, it, 0);
 }
 
+// Variable-length batches (page "FlashAttention-2实现与优化：高效注意力机制详解"
+// §7, ragged input sequences): S sequences packed along the token axis of
+// [H, T, D] tensors, sequence s at rows cu_q[s] .. cu_q[s+1] of every head
+// (keys cu_k[s] .. cu_k[s+1]), each attending only to its own keys.  One
+// workgroup per (tile rank, head, sequence), longest causal tiles first;
+// workgroups past their sequence's end return at once.  A sequence is one
+// slice for the pipelined kernel: its buffer resources end at the
+// sequence's last row, so no read crosses into a neighbour.  Offsets are
+// clamped to [0, T] (inconsistent offsets give wrong rows, never a read or
+// write outside the tensors).  A sequence with queries and no keys gets
+// O = 0 and L = -inf (the logarithm of an empty sum).
+template <typename T, typename OT, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads8) void fa_fwd_varlen(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    OT *__restrict__ o, float *__restrict__ lse, const int *__restrict__ cu_q,
+    const int *__restrict__ cu_k, int S, int H, int Tq, int Tk, int ntiles, float c,
+    int negate) {
+  constexpr int QT = QRows<false>::value;
+  const int id = blockIdx.x;
+  const int hs = id % (H * S);
+  const int t = id / (H * S);
+  const int h = hs / S, sq = hs % S;
+  const int qt = CAUSAL ? ntiles - 1 - t : t;
+  const int qa = max(0, min(cu_q[sq], Tq)), qb = max(qa, min(cu_q[sq + 1], Tq));
+  const int ka = max(0, min(cu_k[sq], Tk)), kb = max(ka, min(cu_k[sq + 1], Tk));
+  const int nq = qb - qa, nk = kb - ka;
+  const int q0 = qt * QT;
+  if (q0 >= nq) return;  // workgroup-uniform, before any barrier
+  const size_t qo = (size_t)h * Tq + qa, ko = (size_t)h * Tk + ka;
+  if (nk == 0) {
+    const int rows = min(QT, nq - q0);
+    for (int i = threadIdx.x; i < rows * D; i += kThreads8)
+      o[(qo + q0) * D + i] = (OT)0.f;
+    for (int i = threadIdx.x; i < rows; i += kThreads8) lse[qo + q0 + i] = -INFINITY;
+    return;
+  }
+  const int kend = CAUSAL ? min(nk, q0 + QT) : nk;
+  const PipeItem it = {0, q0, 0, (kend + kBN - 1) / kBN, -1};
+  pipe8_run<T, OT, D, CAUSAL, false>(q + qo * D, k + ko * D, v + ko * D, o + qo * D, lse + qo,
+                                     nullptr, nq, nk, c, negate, it, 0);
+}
+
 // Chunk run by workgroup g: consecutive chunks go to one XCD (workgroups are
 // dealt to the 8 XCDs round robin), so an XCD's workgroups share heads and
 // their K/V in its L2.
@@ -1451,6 +1493,40 @@ int run(const void *q, const void *k, const void *v, void *o, float *lse, int64_
   return FA_OK;
 }
 
+struct VarlenArgs {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  const int *cu_q, *cu_k;
+  int S, H, Tq, Tk, ntiles;
+  float c;
+  hipStream_t stream;
+};
+
+template <typename T, typename OT, int D, bool CAUSAL>
+hipError_t launch_varlen(const VarlenArgs &a) {
+  // as launch16: a negative scale flips Q's sign in the kernel, scale 0 runs
+  // as the smallest normal scale
+  const float c = fmaxf(a.c < 0.f ? -a.c : a.c, 1.17549435e-38f);
+  const int neg = a.c < 0.f ? 1 : 0;
+  hipLaunchKernelGGL((fa_fwd_varlen<T, OT, D, CAUSAL>),
+                     dim3((unsigned)(a.ntiles * a.H * a.S)), dim3(kThreads8), 0, a.stream,
+                     (const T *)a.q, (const T *)a.k, (const T *)a.v, (OT *)a.o, a.lse, a.cu_q,
+                     a.cu_k, a.S, a.H, a.Tq, a.Tk, a.ntiles, c, neg);
+  return hipGetLastError();
+}
+
+template <typename T, typename OT>
+hipError_t dispatch_varlen(const VarlenArgs &a, int D, bool causal) {
+  switch (D) {
+    case 16: return causal ? launch_varlen<T, OT, 16, true>(a) : launch_varlen<T, OT, 16, false>(a);
+    case 32: return causal ? launch_varlen<T, OT, 32, true>(a) : launch_varlen<T, OT, 32, false>(a);
+    case 64: return causal ? launch_varlen<T, OT, 64, true>(a) : launch_varlen<T, OT, 64, false>(a);
+    default:
+      return causal ? launch_varlen<T, OT, 128, true>(a) : launch_varlen<T, OT, 128, false>(a);
+  }
+}
+
 }  // namespace
 
 // Shared with the backward pass's host code (same library, hidden symbol).
@@ -1533,6 +1609,66 @@ int fa_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse, 
                stream);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
   return run(q, k, v, o, lse, Nq, Nk, D, scale, causal, dtype, sh, &pl, workspace, stream);
+}
+
+int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
+                  const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int64_t S,
+                  int64_t H, int64_t Tq, int64_t Tk, int64_t max_seqlen_q, int64_t D,
+                  float scale, int causal, int dtype, void *stream) {
+  if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k) return FA_ERR_NULLPTR;
+  if (S < 1 || H < 1 || Tq < 1 || Tk < 0 || max_seqlen_q < 1) return FA_ERR_SHAPE;
+  if (D != 16 && D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  if (dtype != FA_BF16 && dtype != FA_BF16_OF32 && dtype != FA_F16 && dtype != FA_F16_OF32)
+    return FA_ERR_DTYPE;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  const int64_t lim = (int64_t)1 << 31;
+  // a sequence is addressed like a (batch, head) slice of fa_fwd
+  if (Tq > lim / (D * 4) - QRows<false>::value || Tk > lim / (D * 4) - 5 * kBN)
+    return FA_ERR_SHAPE;
+  if (max_seqlen_q > Tq) max_seqlen_q = Tq;
+  const int64_t ntiles = (max_seqlen_q + QRows<false>::value - 1) / QRows<false>::value;
+  if (S > lim || H > lim || H * S > lim / ntiles || H * Tq > lim || H * Tk > lim)
+    return FA_ERR_SHAPE;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA_ERR_ALIGN;
+  if (((uintptr_t)lse | (uintptr_t)cu_seqlens_q | (uintptr_t)cu_seqlens_k) & 3u)
+    return FA_ERR_ALIGN;
+  const size_t out_size = (dtype == FA_BF16_OF32 || dtype == FA_F16_OF32) ? 4 : 2;
+  const size_t qb = (size_t)(H * Tq * D * 2), kb = (size_t)(H * Tk * D * 2);
+  const size_t ob = (size_t)(H * Tq * D) * out_size, lb = (size_t)(H * Tq * 4);
+  const size_t cb = (size_t)(S + 1) * 4;
+  const void *outs[2] = {o, lse};
+  const size_t osz[2] = {ob, lb};
+  const void *ins[5] = {q, k, v, cu_seqlens_q, cu_seqlens_k};
+  const size_t isz[5] = {qb, kb, kb, cb, cb};
+  for (int x = 0; x < 2; ++x)
+    for (int y = 0; y < 5; ++y)
+      if (overlaps(outs[x], osz[x], ins[y], isz[y])) return FA_ERR_OVERLAP;
+  if (overlaps(o, ob, lse, lb)) return FA_ERR_OVERLAP;
+  VarlenArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.S = (int)S;
+  a.H = (int)H;
+  a.Tq = (int)Tq;
+  a.Tk = (int)Tk;
+  a.ntiles = (int)ntiles;
+  a.c = scale * 1.4426950408889634f;
+  a.stream = (hipStream_t)stream;
+  const bool cz = causal != 0;
+  hipError_t e;
+  switch (dtype) {
+    case FA_BF16: e = dispatch_varlen<__bf16, __bf16>(a, (int)D, cz); break;
+    case FA_BF16_OF32: e = dispatch_varlen<__bf16, float>(a, (int)D, cz); break;
+    case FA_F16: e = dispatch_varlen<_Float16, _Float16>(a, (int)D, cz); break;
+    default: e = dispatch_varlen<_Float16, float>(a, (int)D, cz); break;
+  }
+  if (e != hipSuccess) return hip_fail(e);
+  return FA_OK;
 }
 
 }  // extern "C"

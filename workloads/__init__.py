@@ -34,6 +34,7 @@ __all__ = [
     "Workload",
     "gen_qkv",
     "gen_grad_out",
+    "varlen_lengths",
     "sample_rows",
     "WORKLOADS",
     "workload",
@@ -106,6 +107,19 @@ def gen_grad_out(B: int, H: int, Nq: int, D: int, seed: int, dtype: str = "bf16"
     g.manual_seed(int(seed))
     do = torch.randn((B, H, Nq, D), generator=g, dtype=torch.float32)
     return do.to(_DTYPES[dtype]).contiguous()
+
+
+def varlen_lengths(total: int, S: int, seed: int, min_len: int = 1) -> List[int]:
+    """``S`` sequence lengths >= ``min_len`` summing to ``total``: S - 1 cut
+    points drawn uniformly (seeded CPU generator) over the spare tokens."""
+    spare = total - S * min_len
+    if spare < 0:
+        raise ValueError("total too small for S sequences of min_len")
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    cuts = torch.randint(0, spare + 1, (S - 1,), generator=g).sort().values.tolist()
+    edges = [0] + cuts + [spare]
+    return [min_len + b - a for a, b in zip(edges, edges[1:])]
 
 
 def gen_workload(w: Workload):
