@@ -4,7 +4,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 --pass bwd times fa_bwd instead (the backward pass, fed by one forward
-call; a separate line, not the default).
+call), and --varlen S times fa_fwd_varlen on the workload's tokens cut into
+S sequences; both print separate lines, not the default one.
 
 One step is one call of fa_fwd_ws (the whole forward pass: the attention
 kernel and, when the plan splits long query tiles, the kernel that combines
@@ -166,6 +167,10 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--entry", choices=("fa_fwd_ws", "fa_fwd"), default="fa_fwd_ws",
                     help="C entry point to time (default: fa_fwd_ws, with scratch)")
+    ap.add_argument("--varlen", type=int, default=0, metavar="S",
+                    help="time fa_fwd_varlen instead: the workload's tokens (B*N, one "
+                         "head) cut into S sequences of seeded lengths (seed 77, at "
+                         "least 64 tokens each), flops summed per sequence")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward pass (default) or the backward pass "
                          "(fa_bwd, fed by one forward call; flops counted as 2.5x "
@@ -213,6 +218,22 @@ def main() -> int:
         call = lib.fa_fwd
 
     bwd = args.which == "bwd"
+    lens = None
+    if args.varlen:
+        from workloads import varlen_lengths
+
+        if w.H != 1 or bwd:
+            raise SystemExit("--varlen takes a single-head workload and the forward pass")
+        lens = varlen_lengths(w.B * w.N, args.varlen, seed=77, min_len=64)
+        cu = torch.tensor([0] + [sum(lens[:i + 1]) for i in range(len(lens))],
+                          dtype=torch.int32, device=dev)
+        T = w.B * w.N
+        argv = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                cu.data_ptr(), cu.data_ptr(), len(lens), 1, T, T, max(lens), w.D, scale,
+                int(w.causal), code, sp)
+        call = lib.fa_fwd_varlen
+        args.entry = "fa_fwd_varlen"
+        ws_bytes = 0
     if bwd:
         from workloads import gen_grad_out
 
@@ -272,6 +293,8 @@ def main() -> int:
 
     ms_per_step = wall * 1e3 / args.steps
     flops = w.flops() * (2.5 if bwd else 1.0)
+    if lens is not None:
+        flops = sum(4.0 * n * n * w.D / (2 if w.causal else 1) for n in lens)
     value = flops / (ms_per_step * 1e-3) / 1e12
     dkey = "f32" if in_dt == torch.float32 else ("bf16" if in_dt == torch.bfloat16 else "f16")
     peak = PEAK_TFLOPS[dkey]
@@ -295,10 +318,11 @@ def main() -> int:
         "config": {"workload": name, "B": w.B, "H": w.H, "Nq": w.N, "Nk": w.N, "D": w.D,
                    "causal": w.causal, "out": str(out_dt).replace("torch.", ""),
                    "flops_per_step": flops, "entry": args.entry,
+                   **({"varlen_lengths": lens} if lens is not None else {}),
                    "workspace_bytes": ws_bytes},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": None if bwd else measured_traffic(name),
+                     "traffic": None if (bwd or lens is not None) else measured_traffic(name),
                      "kernel_ms": round(kernel_ms, 5),
                      "group_ms": {"groups": len(group_ms),
                                   "median": round(group_ms[len(group_ms) // 2], 5),
@@ -313,7 +337,7 @@ def main() -> int:
         rate = exps / (kernel_ms * 1e-3) / 1e12
         line["exp_roofline"] = {"achieved": round(rate, 3), "peak": round(EXP_PEAK_T, 3),
                                 "unit": "Texp/s", "frac": round(rate / EXP_PEAK_T, 4)}
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and lens is None:
         line["cpu_baseline"] = (cpu_baseline_bwd(w, args.cpu_seconds) if bwd
                                 else cpu_baseline(w, args.cpu_seconds))
     print(json.dumps(line), flush=True)

@@ -2,8 +2,8 @@
 against the fp64 oracle (oracle.attention_varlen), with the forward's
 tolerances: fp32 O <= 1e-2 and L <= 1e-3 for 16-bit inputs, 16-bit O the
 exact rounding of the fp32 O and within 1e-2 plus half an ulp.  Each
-sequence must also be bit-identical to fa_fwd run on that sequence alone
-(the same per-tile kernel code)."""
+sequence must also be bit-identical to the same per-tile code run on that
+sequence alone (no cross-talk between packed sequences)."""
 import math
 
 import numpy as np
@@ -96,18 +96,28 @@ def compare(lq, lk, H, D, causal, seed, dtype="bf16", scale=None, rows=None, sol
     assert (np.abs(x16 - ro) <= 1e-2 + _half_ulp(ro, q.dtype)).all()
     assert torch.equal(l16.reshape(-1)[sel], l32.reshape(-1)[sel])
     if solo and rows is None:
-        # every sequence bit-identical to fa_fwd on that sequence alone
+        # every sequence bit-identical to the same computation on that
+        # sequence alone: fa_fwd's one-workgroup-per-tile grid (the same
+        # 256-row per-tile code), or at D = 128, where few packed tiles select
+        # the pair-split 128-row layout, fa_fwd_varlen with that one sequence
         for s in range(len(lq)):
             a, b, ka, kb = (int(x) for x in (cu_q[s], cu_q[s + 1], cu_k[s], cu_k[s + 1]))
             if b == a or kb == ka:
                 continue
-            so, sl = fa.fwd(q[None, :, a:b].contiguous().to(DEV),
-                            k[None, :, ka:kb].contiguous().to(DEV),
-                            v[None, :, ka:kb].contiguous().to(DEV), causal=causal, scale=scale,
-                            out_dtype=torch.float32, split=False)
-            torch.cuda.synchronize()
-            assert torch.equal(so[0].cpu(), o32[:, a:b]), f"sequence {s}: O differs from fa_fwd"
-            assert torch.equal(sl[0].cpu(), l32[:, a:b]), f"sequence {s}: L differs from fa_fwd"
+            qs = q[:, a:b].contiguous()
+            ks, vs = k[:, ka:kb].contiguous(), v[:, ka:kb].contiguous()
+            if D == 128:
+                one = torch.tensor([0, b - a], dtype=torch.int32)
+                onek = torch.tensor([0, kb - ka], dtype=torch.int32)
+                so, sl = run(qs, ks, vs, one, onek, b - a, causal, scale, torch.float32)
+            else:
+                so, sl = fa.fwd(qs[None].to(DEV), ks[None].to(DEV), vs[None].to(DEV),
+                                causal=causal, scale=scale, out_dtype=torch.float32,
+                                split=False)
+                torch.cuda.synchronize()
+                so, sl = so[0].cpu(), sl[0].cpu()
+            assert torch.equal(so, o32[:, a:b]), f"sequence {s}: O differs when run alone"
+            assert torch.equal(sl, l32[:, a:b]), f"sequence {s}: L differs when run alone"
 
 
 MIXED = [1, 31, 256, 257, 700, 64, 1000, 5]
