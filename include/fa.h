@@ -244,6 +244,29 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o,
            float scale, int causal, int dtype, void *workspace,
            size_t workspace_bytes, void *stream);
 
+/*
+ * fa_bwd_varlen -- fa_bwd over a variable-length batch laid out as for
+ * fa_fwd_varlen: q, o, dout, dq [H, Tq, D]; k, v, dk, dv [H, Tk, D]; lse
+ * [H, Tq]; sequence s at rows cu_seqlens_q[s] .. cu_seqlens_q[s+1] - 1 (keys
+ * cu_seqlens_k[s] .. cu_seqlens_k[s+1] - 1), offsets in device memory
+ * (S + 1 int32 each, 0 .. Tq / Tk, non-decreasing; the kernels clamp them
+ * to the tensors).  max_seqlen_q and max_seqlen_k bound every sequence's
+ * query and key count (rows of longer sequences past them are not
+ * computed).  Each sequence's gradients are exactly fa_bwd's for that
+ * sequence alone; keys that no query sees get dk = dv = 0, queries without
+ * keys get dq = 0.  The workspace needs H * Tq * 4 bytes (what
+ * fa_bwd_workspace_size reports for B = 1, Nq = Tq).  Other arguments,
+ * dtypes, head dims and status codes as fa_bwd (the offsets need 4-byte
+ * alignment).
+ */
+int fa_bwd_varlen(const void *q, const void *k, const void *v, const void *o,
+                  const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                  const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                  int64_t S, int64_t H, int64_t Tq, int64_t Tk,
+                  int64_t max_seqlen_q, int64_t max_seqlen_k, int64_t D,
+                  float scale, int causal, int dtype, void *workspace,
+                  size_t workspace_bytes, void *stream);
+
 /* Static description of a status code; never NULL. */
 const char *fa_status_str(int status);
 

@@ -24,6 +24,10 @@ Functions (all fp64, numpy in / numpy out):
       cu_k[s] .. cu_k[s+1]); each sequence attends only to its own keys,
       with the forward definition above applied per sequence.  A sequence
       with queries but no keys gets O = 0 and L = -inf (the empty sum).
+  attention_bwd_varlen(q, k, v, do, cu_q, cu_k, scale, causal)
+      -> (dq, dk, dv): the gradients of attention_varlen, attention_bwd
+      applied to each packed sequence (zero where a sequence has no queries
+      or no keys).
   threads() -> int   OpenMP threads the oracle uses.
 
 Parity status: pinned by tests/test_oracle_pins.py (closed forms, invariants,
@@ -227,6 +231,26 @@ def attention_varlen(q, k, v, cu_q, cu_k, scale: float, causal: bool, lib=None
         o[:, q0:q1] = so[0]
         lse[:, q0:q1] = sl[0]
     return o, lse
+
+
+def attention_bwd_varlen(q, k, v, do, cu_q, cu_k, scale: float, causal: bool, lib=None):
+    """fp64 gradients of attention_varlen for upstream gradient do [H,Tq,D]:
+    attention_bwd on each packed sequence on its own."""
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    cu_q = [int(x) for x in cu_q]
+    cu_k = [int(x) for x in cu_k]
+    H, Tq, D = q.shape
+    if do.shape != q.shape or cu_q[-1] != Tq or cu_k[-1] != k.shape[1] or len(cu_q) != len(cu_k):
+        raise ValueError("inconsistent varlen shapes or offsets")
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for s in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = cu_q[s], cu_q[s + 1], cu_k[s], cu_k[s + 1]
+        if q1 == q0 or k1 == k0:
+            continue
+        a, b, c = attention_bwd(q[None, :, q0:q1], k[None, :, k0:k1], v[None, :, k0:k1],
+                                do[None, :, q0:q1], scale, causal, lib=lib)
+        dq[:, q0:q1], dk[:, k0:k1], dv[:, k0:k1] = a[0], b[0], c[0]
+    return dq, dk, dv
 
 
 def threads(lib=None) -> int:

@@ -106,7 +106,49 @@ def pin_varlen_empty_sequences(lib):
     _close(o[:, cu_q[3]:], od[0], 0.0, "last sequence O")
 
 
+def pin_varlen_bwd_equal_lengths_is_dense(lib):
+    S, H, N, D = 3, 2, 9, 4
+    q, k, v, cu_q, cu_k = _packed(5, H, [N] * S, [N] * S, D)
+    g = np.random.default_rng(6).standard_normal(q.shape)
+    for causal in (False, True):
+        got = oracle.attention_bwd_varlen(q, k, v, g, cu_q, cu_k, 0.4, causal, lib=lib)
+        dense = [x.reshape(H, S, N, D).transpose(1, 0, 2, 3) for x in (q, k, v, g)]
+        ref = oracle.attention_bwd(*dense, 0.4, causal, lib=lib)
+        for a, b in zip(got, ref):
+            _close(a, b.transpose(1, 0, 2, 3).reshape(H, S * N, D), 0.0, "bwd equal lengths")
+
+
+def pin_varlen_bwd_finite_differences(lib):
+    """Gradients of sum(dO * O_varlen) against central differences."""
+    lq, lk, H, D, scale = [3, 0, 2, 4], [2, 3, 3, 0], 1, 2, 0.8
+    q, k, v, cu_q, cu_k = _packed(7, H, lq, lk, D)
+    g = np.random.default_rng(8).standard_normal(q.shape)
+    h = 1e-5
+    for causal in (False, True):
+        grads = oracle.attention_bwd_varlen(q, k, v, g, cu_q, cu_k, scale, causal, lib=lib)
+        base = {"q": q, "k": k, "v": v}
+
+        def loss(**kw):
+            a = dict(base)
+            a.update(kw)
+            o, _ = oracle.attention_varlen(a["q"], a["k"], a["v"], cu_q, cu_k, scale, causal,
+                                           lib=lib)
+            return float((o * g).sum())
+
+        for name, grad in zip(("q", "k", "v"), grads):
+            x = base[name]
+            num = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                num[idx] = (loss(**{name: xp}) - loss(**{name: xm})) / (2 * h)
+            _close(grad, num, 1e-7, f"varlen finite differences d{name}")
+
+
 ALL_VARLEN_PINS = [
+    pin_varlen_bwd_equal_lengths_is_dense,
+    pin_varlen_bwd_finite_differences,
     pin_varlen_equal_lengths_is_dense,
     pin_varlen_brute_force,
     pin_varlen_isolation,

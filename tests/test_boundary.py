@@ -218,3 +218,25 @@ def call_varlen(**kw):
 ])
 def test_varlen_validation(kw, status):
     assert call_varlen(**kw) == getattr(fa, status)
+
+
+def call_bwd_varlen(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, do=DO, dq=DQ, dk=DK, dv=DV, cq=CQ, ck=CK, S=3, H=2,
+             Tq=500, Tk=400, mq=300, mk=200, D=64, scale=0.125, causal=1, dtype=fa.FA_BF16,
+             ws=WS, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return fa.fa_bwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"],
+                            a["dk"], a["dv"], a["cq"], a["ck"], a["S"], a["H"], a["Tq"],
+                            a["Tk"], a["mq"], a["mk"], a["D"], a["scale"], a["causal"],
+                            a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"cq": None}, "FA_ERR_NULLPTR"), ({"dv": None}, "FA_ERR_NULLPTR"),
+    ({"S": 0}, "FA_ERR_SHAPE"), ({"Tq": 0}, "FA_ERR_SHAPE"), ({"mk": -1}, "FA_ERR_SHAPE"),
+    ({"D": 16}, "FA_ERR_HEAD_DIM"), ({"dtype": fa.FA_F32}, "FA_ERR_DTYPE"),
+    ({"scale": math.inf}, "FA_ERR_SCALE"), ({"ck": CK + 1}, "FA_ERR_ALIGN"),
+    ({"ws_bytes": 2 * 500 * 4 - 4}, "FA_ERR_WORKSPACE"), ({"dq": CQ}, "FA_ERR_OVERLAP"),
+])
+def test_bwd_varlen_validation(kw, status):
+    assert call_bwd_varlen(**kw) == getattr(fa, status)

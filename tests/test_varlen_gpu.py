@@ -163,3 +163,73 @@ def test_varlen_32k_tokens_sampled():
     lens = varlen_lengths(32768, 8, seed=77, min_len=64)
     rows = sample_rows(32768, 512, 7700).numpy()
     compare(lens, lens, 1, 128, True, seed=1800, rows=rows)
+
+
+# --- backward over variable-length batches (fa_bwd_varlen) ------------------
+def compare_bwd(lq, lk, H, D, causal, seed, dtype="bf16"):
+    """Gradients against the oracle (per sequence, with the backward's
+    derived bound 2u*b, u the input type's unit roundoff), 16-bit gradients
+    the exact rounding of the fp32 ones, and each sequence bit-identical to
+    fa_bwd on that sequence alone."""
+    from workloads import gen_grad_out
+
+    q, k, v, cu_q, cu_k = packed(lq, lk, H, D, seed, dtype)
+    g = gen_grad_out(1, H, sum(lq), D, seed=seed + 2, dtype=dtype)[0]
+    scale = 1.0 / math.sqrt(D)
+    maxq, maxk = max(max(lq), 1), max(lk)
+    _log(f"bwd S={len(lq)} H={H} D={D} causal={causal} Tq={sum(lq)} Tk={sum(lk)}")
+    qd, kd, vd, gd, cqd, ckd = (t.to(DEV) for t in (q, k, v, g, cu_q, cu_k))
+    o, lse = fa.fwd_varlen(qd, kd, vd, cqd, ckd, maxq, causal=causal, scale=scale)
+    g32 = fa.bwd_varlen(qd, kd, vd, o, lse, gd, cqd, ckd, maxq, maxk, causal=causal,
+                        scale=scale, grad_dtype=torch.float32)
+    g16 = fa.bwd_varlen(qd, kd, vd, o, lse, gd, cqd, ckd, maxq, maxk, causal=causal,
+                        scale=scale)
+    torch.cuda.synchronize()
+    g32 = [x.cpu() for x in g32]
+    g16 = [x.cpu() for x in g16]
+    u = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -11
+    qn, kn, vn, gn = (t.double().numpy() for t in (q, k, v, g))
+    cq, ck = cu_q.tolist(), cu_k.tolist()
+    for s in range(len(lq)):
+        a, b, ka, kb = cq[s], cq[s + 1], ck[s], ck[s + 1]
+        rows = (slice(a, b), slice(ka, kb), slice(ka, kb))
+        if b == a or kb == ka:
+            for n in range(3):
+                assert torch.all(g32[n][:, rows[n]] == 0), f"sequence {s}: expected zeros"
+            continue
+        ref = oracle.attention_bwd(qn[None, :, a:b], kn[None, :, ka:kb], vn[None, :, ka:kb],
+                                   gn[None, :, a:b], scale, causal, magnitudes=True)
+        for n, name in enumerate(("dQ", "dK", "dV")):
+            x = g32[n][:, rows[n]].double().numpy()
+            r, bd = ref[n][0], ref[n + 3][0]
+            bound = 2 * u * bd + 1e-6 * float(bd.max()) + 1e-30
+            ratio = float((np.abs(x - r) / bound).max())
+            assert ratio <= 1.0, f"sequence {s} {name}: error/bound {ratio:.3f}"
+            rnd = g32[n][:, rows[n]].to(q.dtype)
+            assert torch.equal(rnd, g16[n][:, rows[n]]), f"sequence {s} {name}: rounding"
+        # the same sequence through the dense entry point
+        so, sl = fa.fwd(qd[None, :, a:b].contiguous(), kd[None, :, ka:kb].contiguous(),
+                        vd[None, :, ka:kb].contiguous(), causal=causal, scale=scale)
+        one = fa.bwd(qd[None, :, a:b].contiguous(), kd[None, :, ka:kb].contiguous(),
+                     vd[None, :, ka:kb].contiguous(), o[None, :, a:b].contiguous(),
+                     lse[None, :, a:b].contiguous(), gd[None, :, a:b].contiguous(),
+                     causal=causal, scale=scale, grad_dtype=torch.float32)
+        torch.cuda.synchronize()
+        for n in range(3):
+            assert torch.equal(one[n][0].cpu(), g32[n][:, rows[n]]), \
+                f"sequence {s}: gradient {n} differs from fa_bwd on the sequence alone"
+
+
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_bwd_mixed_lengths(D, causal):
+    compare_bwd(MIXED, MIXED, 2, D, causal, seed=1900 + D)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_bwd_unequal_and_empty(causal):
+    compare_bwd([100, 0, 513, 40, 17], [7, 30, 200, 41, 0], 2, 128, causal, seed=2000)
+
+
+def test_varlen_bwd_fp16():
+    compare_bwd(MIXED, MIXED, 1, 64, True, seed=2100, dtype="f16")

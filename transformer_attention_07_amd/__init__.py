@@ -17,6 +17,9 @@ C-ABI mirrors (same names and meaning as include/fa.h):
     fa_bwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_ptr,
            B, H, Nq, Nk, D, scale, causal, dtype, ws_ptr, ws_bytes, stream)
         -> status
+    fa_bwd_varlen(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr,
+                  dv_ptr, cu_q_ptr, cu_k_ptr, S, H, Tq, Tk, max_q, max_k, D, scale,
+                  causal, dtype, ws_ptr, ws_bytes, stream) -> status
     fa_status_str(status) -> str
     fa_last_hip_error() -> str
     fa_version() -> int
@@ -28,6 +31,8 @@ Tensor convenience:
                out_dtype=None) -> (o, lse) through fa_fwd_varlen
     bwd(q, k, v, o, lse, do, causal=False, scale=None, grad_dtype=None)
         -> (dq, dk, dv) through fa_bwd
+    bwd_varlen(q, k, v, o, lse, do, cu_q, cu_k, max_q, max_k, causal=False,
+               scale=None, grad_dtype=None) -> (dq, dk, dv) through fa_bwd_varlen
 """
 from __future__ import annotations
 
@@ -41,8 +46,8 @@ __all__ = [
     "FA_OK", "FA_ERR_NULLPTR", "FA_ERR_SHAPE", "FA_ERR_HEAD_DIM", "FA_ERR_DTYPE",
     "FA_ERR_SCALE", "FA_ERR_ALIGN", "FA_ERR_HIP", "FA_ERR_OVERLAP", "FA_ERR_WORKSPACE",
     "LIBRARY", "EXPORTS", "library", "fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws",
-    "fa_fwd_varlen", "fa_bwd_workspace_size", "fa_bwd", "fa_status_str",
-    "fa_last_hip_error", "fa_version", "fwd", "fwd_varlen", "bwd", "FaError",
+    "fa_fwd_varlen", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_varlen", "fa_status_str",
+    "fa_last_hip_error", "fa_version", "fwd", "fwd_varlen", "bwd", "bwd_varlen", "FaError",
 ]
 
 LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
@@ -53,8 +58,8 @@ FA_F32, FA_BF16, FA_BF16_OF32, FA_F16, FA_F16_OF32 = 0, 1, 2, 3, 4
 
 # Every symbol include/fa.h declares.
 EXPORTS = ("fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws", "fa_fwd_varlen",
-           "fa_bwd_workspace_size", "fa_bwd", "fa_status_str", "fa_last_hip_error",
-           "fa_version")
+           "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_varlen", "fa_status_str",
+           "fa_last_hip_error", "fa_version")
 
 _lib = None
 
@@ -95,6 +100,10 @@ def library() -> ctypes.CDLL:
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                            ctypes.c_float, ctypes.c_int, ctypes.c_int, vp, ctypes.c_size_t,
                            vp]
+    lib.fa_bwd_varlen.restype = ctypes.c_int
+    lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64,
+                                  i64, i64, i64, i64, ctypes.c_float, ctypes.c_int,
+                                  ctypes.c_int, vp, ctypes.c_size_t, vp]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_status_str.argtypes = [ctypes.c_int]
     lib.fa_last_hip_error.restype = ctypes.c_char_p
@@ -148,6 +157,14 @@ def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, B, H, Nq, Nk, D, scale, causal, dtyp
     return int(library().fa_bwd(q, k, v, o, lse, do, dq, dk, dv, B, H, Nq, Nk, D,
                                 float(scale), int(causal), int(dtype), ws, int(ws_bytes),
                                 stream))
+
+
+def fa_bwd_varlen(q, k, v, o, lse, do, dq, dk, dv, cu_q, cu_k, S, H, Tq, Tk, max_q, max_k,
+                  D, scale, causal, dtype, ws, ws_bytes, stream) -> int:
+    """Raw C call; pointers are integers (device addresses) or None."""
+    return int(library().fa_bwd_varlen(q, k, v, o, lse, do, dq, dk, dv, cu_q, cu_k, S, H, Tq,
+                                       Tk, max_q, max_k, D, float(scale), int(causal),
+                                       int(dtype), ws, int(ws_bytes), stream))
 
 
 def fa_status_str(status: int) -> str:
@@ -352,3 +369,53 @@ def fwd_varlen(q, k, v, cu_q, cu_k, max_seqlen_q: int, causal: bool = False,
             msg += ": " + fa_last_hip_error()
         raise FaError(st, msg)
     return o, lse
+
+
+def bwd_varlen(q, k, v, o, lse, do, cu_q, cu_k, max_q: int, max_k: int,
+               causal: bool = False, scale: Optional[float] = None, grad_dtype=None,
+               stream=None):
+    """Variable-length attention backward (fa_bwd_varlen) on device tensors:
+    q, o, do [H, Tq, D]; k, v [H, Tk, D]; lse [H, Tq]; cu_q, cu_k int32
+    offsets.  Returns (dq, dk, dv) in ``grad_dtype`` (default: the input
+    dtype)."""
+    import torch
+
+    t = (q, k, v, o, do)
+    if any(x.dim() != 3 for x in t):
+        raise ValueError("q, k, v, o, do must be [H, T, D]")
+    H, Tq, D = q.shape
+    Tk = k.shape[1]
+    if (tuple(k.shape) != (H, Tk, D) or tuple(v.shape) != (H, Tk, D)
+            or tuple(o.shape) != tuple(q.shape) or tuple(do.shape) != tuple(q.shape)):
+        raise ValueError("shape mismatch among q, k, v, o, do")
+    if tuple(lse.shape) != (H, Tq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be fp32 [H, Tq]")
+    if not all(x.dtype == q.dtype for x in t):
+        raise ValueError("q, k, v, o, do must share a dtype")
+    if cu_q.dtype != torch.int32 or cu_k.dtype != torch.int32 or cu_q.shape != cu_k.shape:
+        raise ValueError("cu_q, cu_k must be int32 tensors of equal length")
+    allt = t + (lse, cu_q, cu_k)
+    if not all(x.is_cuda and x.device == q.device and x.is_contiguous() for x in allt):
+        raise ValueError("all tensors must be contiguous on the same GPU device")
+    S = cu_q.numel() - 1
+    grad_dtype = q.dtype if grad_dtype is None else grad_dtype
+    code = _dtype_code(torch, q.dtype, grad_dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = torch.empty(q.shape, dtype=grad_dtype, device=q.device)
+    dk = torch.empty(k.shape, dtype=grad_dtype, device=q.device)
+    dv = torch.empty(v.shape, dtype=grad_dtype, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    nbytes = H * Tq * 4
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    st = fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                       cu_q.data_ptr(), cu_k.data_ptr(), S, H, Tq, Tk, int(max_q), int(max_k),
+                       D, scale, causal, code, ws.data_ptr(), nbytes, stream)
+    if st != FA_OK:
+        msg = fa_status_str(st)
+        if st == FA_ERR_HIP:
+            msg += ": " + fa_last_hip_error()
+        raise FaError(st, msg)
+    return dq, dk, dv

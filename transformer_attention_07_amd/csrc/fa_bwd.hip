@@ -291,6 +291,43 @@ __device__ __forceinline__ void pair_sum(f32x16 (&acc)[N], lds_char *buf, int gr
   }
 }
 
+// The (batch*head) slice, or (head, sequence) slice of a variable-length
+// batch, that a workgroup works on, and its tile index.
+struct Slice {
+  size_t qrow, krow;  // first row of the slice in the [.., D] tensors
+  int Nq, Nk, tile;
+};
+
+// Dense: workgroup id = tile rank * BH + bh.  Variable length (cu_q != 0):
+// id = tile rank * (H*S) + h*S + s over [H, T, D] tensors, sequence s at
+// rows cu[s] .. cu[s+1] (offsets clamped to [0, T]).  `rank_to_tile`
+// reverses the rank order when `reverse` (ntiles tiles per slice).
+__device__ __forceinline__ Slice resolve(int BH, int Nq, int Nk, const int *cu_q,
+                                         const int *cu_k, int S, bool reverse, int ntiles) {
+  Slice sl;
+  const int id = blockIdx.x;
+  if (cu_q == nullptr) {
+    const int bh = id % BH, rank = id / BH;
+    sl.qrow = (size_t)bh * Nq;
+    sl.krow = (size_t)bh * Nk;
+    sl.Nq = Nq;
+    sl.Nk = Nk;
+    sl.tile = reverse ? ntiles - 1 - rank : rank;
+  } else {
+    // BH = H, Nq = Tq, Nk = Tk
+    const int hs = id % (BH * S), rank = id / (BH * S);
+    const int h = hs / S, sq = hs % S;
+    const int qa = max(0, min(cu_q[sq], Nq)), qb = max(qa, min(cu_q[sq + 1], Nq));
+    const int ka = max(0, min(cu_k[sq], Nk)), kb = max(ka, min(cu_k[sq + 1], Nk));
+    sl.qrow = (size_t)h * Nq + qa;
+    sl.krow = (size_t)h * Nk + ka;
+    sl.Nq = qb - qa;
+    sl.Nk = kb - ka;
+    sl.tile = reverse ? ntiles - 1 - rank : rank;
+  }
+  return sl;
+}
+
 // dK and dV: one workgroup per (batch*head, kTile keys).  Wave w owns keys
 // key0 + 32*(w & 1) .. +31 and, of every 128-query block, the 32-row
 // quarters par and par + 2 (par = w >> 1); the two parities are summed at
@@ -299,7 +336,8 @@ template <typename T, typename OT, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dl,
-    OT *__restrict__ dk, OT *__restrict__ dv, int Nq, int Nk, int BH, float c, float scale) {
+    OT *__restrict__ dk, OT *__restrict__ dv, int Nq, int Nk, int BH, float c, float scale,
+    const int *__restrict__ cu_q, const int *__restrict__ cu_k, int S) {
   using M = Mma<T>;
   typedef typename M::frag frag;
   constexpr int KF = D / 16;  // MFMA steps along D
@@ -310,19 +348,23 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv(
   lds_char *smem = (lds_char *)smem_raw;
   lds_float *stats = (lds_float *)(smem + 4 * BB);
 
-  const int bh = blockIdx.x % BH;
-  const int kt = blockIdx.x / BH;  // causal: the lowest keys see the most queries: first
+  // causal: the lowest keys see the most queries: first
+  const Slice sl = resolve(BH, Nq, Nk, cu_q, cu_k, S, false, 0);
+  Nq = sl.Nq;
+  Nk = sl.Nk;
+  const int kt = sl.tile;
+  if (kt * kTile >= Nk) return;  // past the slice's keys (workgroup-uniform)
   const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
   const int g = lane >> 5, col = lane & 31;
   const int grp = w & 1, par = w >> 1;
   const int key0 = kt * kTile + grp * kOwn;
   const int myk = key0 + col;
-  const T *qs = q + (size_t)bh * Nq * D;
-  const T *dos = dout + (size_t)bh * Nq * D;
-  const T *ks = k + (size_t)bh * Nk * D;
-  const T *vs = v + (size_t)bh * Nk * D;
-  const float *ls = lse + (size_t)bh * Nq;
-  const float *ds_ = dl + (size_t)bh * Nq;
+  const T *qs = q + sl.qrow * D;
+  const T *dos = dout + sl.qrow * D;
+  const T *ks = k + sl.krow * D;
+  const T *vs = v + sl.krow * D;
+  const float *ls = lse + sl.qrow;
+  const float *ds_ = dl + sl.qrow;
 
   frag kf[KF], vf[KF];
 #pragma unroll
@@ -433,8 +475,8 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv(
   __syncthreads();
   pair_sum<NC>(dka, smem, grp, par, lane);
   if (par == 0 && myk < Nk) {
-    OT *dks = dk + (size_t)bh * Nk * D;
-    OT *dvs = dv + (size_t)bh * Nk * D;
+    OT *dks = dk + sl.krow * D;
+    OT *dvs = dv + sl.krow * D;
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
       store_t<OT, D>(dvs, myk, 32 * cc, g, dva[cc], 1.f);
@@ -451,7 +493,8 @@ template <typename T, typename OT, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void fa_bwd_dq(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dl,
-    OT *__restrict__ dq, int Nq, int Nk, int BH, int nqt, float c, float scale) {
+    OT *__restrict__ dq, int Nq, int Nk, int BH, int nqt, float c, float scale,
+    const int *__restrict__ cu_q, const int *__restrict__ cu_k, int S) {
   using M = Mma<T>;
   typedef typename M::frag frag;
   constexpr int KF = D / 16;
@@ -461,18 +504,21 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dq(
   __shared__ __attribute__((aligned(16))) char smem_raw[4 * BB];
   lds_char *smem = (lds_char *)smem_raw;
 
-  const int bh = blockIdx.x % BH;
   // causal: the last query tiles see the most keys: first
-  const int qt = CAUSAL ? nqt - 1 - (int)(blockIdx.x / BH) : (int)(blockIdx.x / BH);
+  const Slice sl = resolve(BH, Nq, Nk, cu_q, cu_k, S, CAUSAL, nqt);
+  Nq = sl.Nq;
+  Nk = sl.Nk;
+  const int qt = sl.tile;
+  if (qt * kTile >= Nq) return;  // past the slice's queries (workgroup-uniform)
   const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
   const int g = lane >> 5, col = lane & 31;
   const int grp = w & 1, par = w >> 1;
   const int qw0 = qt * kTile + grp * kOwn;
   const int myq = qw0 + col;
-  const T *qs = q + (size_t)bh * Nq * D;
-  const T *dos = dout + (size_t)bh * Nq * D;
-  const T *ks = k + (size_t)bh * Nk * D;
-  const T *vs = v + (size_t)bh * Nk * D;
+  const T *qs = q + sl.qrow * D;
+  const T *dos = dout + sl.qrow * D;
+  const T *ks = k + sl.krow * D;
+  const T *vs = v + sl.krow * D;
 
   frag qf[KF], df[KF];
 #pragma unroll
@@ -480,8 +526,8 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dq(
     qf[t] = glob_frag<T, D>(qs, myq, Nq, 16 * t + 8 * g);
     df[t] = glob_frag<T, D>(dos, myq, Nq, 16 * t + 8 * g);
   }
-  const float l2 = myq < Nq ? lse[(size_t)bh * Nq + myq] * kLog2e : INFINITY;
-  const float dd = myq < Nq ? dl[(size_t)bh * Nq + myq] : 0.f;
+  const float l2 = myq < Nq ? lse[sl.qrow + myq] * kLog2e : INFINITY;
+  const float dd = myq < Nq ? dl[sl.qrow + myq] : 0.f;
   f32x16 dqa[NC];
 #pragma unroll
   for (int cc = 0; cc < NC; ++cc) dqa[cc] = f32x16{};
@@ -551,7 +597,7 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dq(
 
   pair_sum<NC>(dqa, smem, grp, par, lane);
   if (par == 0 && myq < Nq) {
-    OT *dqs = dq + (size_t)bh * Nq * D;
+    OT *dqs = dq + sl.qrow * D;
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) store_t<OT, D>(dqs, myq, 32 * cc, g, dqa[cc], scale);
   }
@@ -565,9 +611,12 @@ struct BwdArgs {
   const float *lse;
   void *dq, *dk, *dv;
   float *dl;
-  int Nq, Nk, BH;
+  int Nq, Nk, BH;  // variable length: Tq, Tk, H
   float scale;
   hipStream_t stream;
+  // variable length only (cu_q == nullptr otherwise)
+  const int *cu_q = nullptr, *cu_k = nullptr;
+  int S = 1, maxq = 0, maxk = 0;
 };
 
 template <typename T, typename OT, int D, bool CAUSAL>
@@ -580,18 +629,24 @@ hipError_t launch_bwd(const BwdArgs &a) {
                      rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nkt = (a.Nk + kTile - 1) / kTile;
-  const int nqt = (a.Nq + kTile - 1) / kTile;
-  hipLaunchKernelGGL((fa_bwd_dkdv<T, OT, D, CAUSAL>), dim3((unsigned)(a.BH * nkt)),
+  const bool vl = a.cu_q != nullptr;
+  // tiles per slice, and slices per tile rank
+  const int nkt = ((vl ? a.maxk : a.Nk) + kTile - 1) / kTile;
+  const int nqt = ((vl ? a.maxq : a.Nq) + kTile - 1) / kTile;
+  const int slices = vl ? a.BH * a.S : a.BH;
+  if (nkt > 0) {
+    hipLaunchKernelGGL((fa_bwd_dkdv<T, OT, D, CAUSAL>), dim3((unsigned)(slices * nkt)),
+                       dim3(kThreads), 0, a.stream, (const T *)a.q, (const T *)a.k,
+                       (const T *)a.v, (const T *)a.dout, a.lse, (const float *)a.dl,
+                       (OT *)a.dk, (OT *)a.dv, a.Nq, a.Nk, a.BH, c, a.scale, a.cu_q, a.cu_k,
+                       a.S);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((fa_bwd_dq<T, OT, D, CAUSAL>), dim3((unsigned)(slices * nqt)),
                      dim3(kThreads), 0, a.stream, (const T *)a.q, (const T *)a.k,
                      (const T *)a.v, (const T *)a.dout, a.lse, (const float *)a.dl,
-                     (OT *)a.dk, (OT *)a.dv, a.Nq, a.Nk, a.BH, c, a.scale);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa_bwd_dq<T, OT, D, CAUSAL>), dim3((unsigned)(a.BH * nqt)),
-                     dim3(kThreads), 0, a.stream, (const T *)a.q, (const T *)a.k,
-                     (const T *)a.v, (const T *)a.dout, a.lse, (const float *)a.dl,
-                     (OT *)a.dq, a.Nq, a.Nk, a.BH, nqt, c, a.scale);
+                     (OT *)a.dq, a.Nq, a.Nk, a.BH, nqt, c, a.scale, a.cu_q, a.cu_k, a.S);
   return hipGetLastError();
 }
 
@@ -685,6 +740,80 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const flo
   a.BH = (int)BH;
   a.scale = scale;
   a.stream = (hipStream_t)stream;
+  const bool cz = causal != 0;
+  hipError_t e;
+  switch (dtype) {
+    case FA_BF16: e = dispatch_bwd<__bf16, __bf16>(a, (int)D, cz); break;
+    case FA_BF16_OF32: e = dispatch_bwd<__bf16, float>(a, (int)D, cz); break;
+    case FA_F16: e = dispatch_bwd<_Float16, _Float16>(a, (int)D, cz); break;
+    default: e = dispatch_bwd<_Float16, float>(a, (int)D, cz); break;
+  }
+  if (e != hipSuccess) return fa_internal_hip_fail(e);
+  return FA_OK;
+}
+
+int fa_bwd_varlen(const void *q, const void *k, const void *v, const void *o,
+                  const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                  const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int64_t S,
+                  int64_t H, int64_t Tq, int64_t Tk, int64_t max_seqlen_q,
+                  int64_t max_seqlen_k, int64_t D, float scale, int causal, int dtype,
+                  void *workspace, size_t workspace_bytes, void *stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !cu_seqlens_q ||
+      !cu_seqlens_k)
+    return FA_ERR_NULLPTR;
+  if (S < 1 || H < 1 || Tq < 1 || Tk < 0 || max_seqlen_q < 1 || max_seqlen_k < 0)
+    return FA_ERR_SHAPE;
+  int st = check_shape(1, H, Tq, Tk > 0 ? Tk : 1, D, dtype);
+  if (st != FA_OK) return st;
+  if (max_seqlen_q > Tq) max_seqlen_q = Tq;
+  if (max_seqlen_k > Tk) max_seqlen_k = Tk;
+  const int64_t lim = (int64_t)1 << 31;
+  const int64_t tiles = (max_seqlen_q > max_seqlen_k ? max_seqlen_q : max_seqlen_k) / kTile + 1;
+  if (S > lim || H * S > lim / tiles) return FA_ERR_SHAPE;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout |
+       (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv) & 15u)
+    return FA_ERR_ALIGN;
+  if (((uintptr_t)lse | (uintptr_t)cu_seqlens_q | (uintptr_t)cu_seqlens_k) & 3u ||
+      ((uintptr_t)workspace & 15u))
+    return FA_ERR_ALIGN;
+  const size_t gsz = (dtype == FA_BF16_OF32 || dtype == FA_F16_OF32) ? 4 : 2;
+  const size_t qb = (size_t)(H * Tq * D) * 2, kb = (size_t)(H * Tk * D) * 2;
+  const size_t lb = (size_t)(H * Tq) * 4, cb = (size_t)(S + 1) * 4;
+  const size_t dqb = (size_t)(H * Tq * D) * gsz, dkb = (size_t)(H * Tk * D) * gsz;
+  const size_t need = lb;
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const void *outs[4] = {dq, dk, dv, workspace};
+  const size_t osz[4] = {dqb, dkb, dkb, need};
+  const void *ins[8] = {q, k, v, o, dout, lse, cu_seqlens_q, cu_seqlens_k};
+  const size_t isz[8] = {qb, kb, kb, qb, qb, lb, cb, cb};
+  for (int x = 0; x < 4; ++x) {
+    for (int y = 0; y < 8; ++y)
+      if (overlaps(outs[x], osz[x], ins[y], isz[y])) return FA_ERR_OVERLAP;
+    for (int y = x + 1; y < 4; ++y)
+      if (overlaps(outs[x], osz[x], outs[y], osz[y])) return FA_ERR_OVERLAP;
+  }
+  BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dl = (float *)workspace;
+  a.Nq = (int)Tq;
+  a.Nk = (int)Tk;
+  a.BH = (int)H;
+  a.scale = scale;
+  a.stream = (hipStream_t)stream;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.S = (int)S;
+  a.maxq = (int)max_seqlen_q;
+  a.maxk = (int)max_seqlen_k;
   const bool cz = causal != 0;
   hipError_t e;
   switch (dtype) {
