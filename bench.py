@@ -222,8 +222,8 @@ def main() -> int:
     if args.varlen:
         from workloads import varlen_lengths
 
-        if w.H != 1 or bwd:
-            raise SystemExit("--varlen takes a single-head workload and the forward pass")
+        if w.H != 1:
+            raise SystemExit("--varlen takes a single-head workload")
         lens = varlen_lengths(w.B * w.N, args.varlen, seed=77, min_len=64)
         cu = torch.tensor([0] + [sum(lens[:i + 1]) for i in range(len(lens))],
                           dtype=torch.int32, device=dev)
@@ -234,7 +234,24 @@ def main() -> int:
         call = lib.fa_fwd_varlen
         args.entry = "fa_fwd_varlen"
         ws_bytes = 0
-    if bwd:
+    if bwd and lens is not None:
+        from workloads import gen_grad_out
+
+        st = call(*argv)  # the forward pass whose O and L the backward consumes
+        if st != 0:
+            raise RuntimeError(f"forward failed: {fa.fa_status_str(st)}")
+        g = gen_grad_out(w.B, w.H, w.N, w.D, seed=w.seed + 10000, dtype=w.dtype).to(dev)
+        bcode = fa._dtype_code(torch, in_dt, out_dt)
+        dq, dk, dv = (torch.empty(x.shape, dtype=out_dt, device=dev) for x in (q, k, v))
+        ws_bytes = T * 4
+        bws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        argv = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                g.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cu.data_ptr(),
+                cu.data_ptr(), len(lens), 1, T, T, max(lens), max(lens), w.D, scale,
+                int(w.causal), bcode, bws.data_ptr(), ws_bytes, sp)
+        call = lib.fa_bwd_varlen
+        args.entry = "fa_bwd_varlen"
+    elif bwd:
         from workloads import gen_grad_out
 
         st = call(*argv)  # the forward pass whose O and L the backward consumes
@@ -295,6 +312,7 @@ def main() -> int:
     flops = w.flops() * (2.5 if bwd else 1.0)
     if lens is not None:
         flops = sum(4.0 * n * n * w.D / (2 if w.causal else 1) for n in lens)
+        flops *= 2.5 if bwd else 1.0
     value = flops / (ms_per_step * 1e-3) / 1e12
     dkey = "f32" if in_dt == torch.float32 else ("bf16" if in_dt == torch.bfloat16 else "f16")
     peak = PEAK_TFLOPS[dkey]

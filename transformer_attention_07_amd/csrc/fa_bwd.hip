@@ -299,7 +299,8 @@ struct Slice {
 };
 
 // Dense: workgroup id = tile rank * BH + bh.  Variable length (cu_q != 0):
-// id = tile rank * (H*S) + h*S + s over [H, T, D] tensors, sequence s at
+// id = tile rank * (H*S) + ((h*S + s - rank) mod H*S) over [H, T, D]
+// tensors, sequence s at
 // rows cu[s] .. cu[s+1] (offsets clamped to [0, T]).  `rank_to_tile`
 // reverses the rank order when `reverse` (ntiles tiles per slice).
 __device__ __forceinline__ Slice resolve(int BH, int Nq, int Nk, const int *cu_q,
@@ -314,8 +315,11 @@ __device__ __forceinline__ Slice resolve(int BH, int Nq, int Nk, const int *cu_q
     sl.Nk = Nk;
     sl.tile = reverse ? ntiles - 1 - rank : rank;
   } else {
-    // BH = H, Nq = Tq, Nk = Tk
-    const int hs = id % (BH * S), rank = id / (BH * S);
+    // BH = H, Nq = Tq, Nk = Tk.  The slice index is rotated by the rank so
+    // that one sequence's tiles are spread over the XCDs (workgroup ids are
+    // dealt to the 8 XCDs round robin; unrotated, H*S a multiple of 8 keeps
+    // every sequence on one XCD, and the longest sequence bounds the time)
+    const int rank = id / (BH * S), hs = (id % (BH * S) + rank) % (BH * S);
     const int h = hs / S, sq = hs % S;
     const int qa = max(0, min(cu_q[sq], Nq)), qb = max(qa, min(cu_q[sq + 1], Nq));
     const int ka = max(0, min(cu_k[sq], Nk)), kb = max(ka, min(cu_k[sq + 1], Nk));

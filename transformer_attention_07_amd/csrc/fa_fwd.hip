@@ -1042,8 +1042,12 @@ __global__ __launch_bounds__(kThreads8) void fa_fwd_varlen(
     int negate) {
   constexpr int QT = QRows<PAIR>::value;
   const int id = blockIdx.x;
-  const int hs = id % (H * S);
+  // rank-major (longest causal tiles first); the slice index is rotated by
+  // the rank so that one sequence's tiles are spread over the XCDs (the
+  // dispatcher deals workgroup ids to the 8 XCDs round robin: without the
+  // rotation, H*S a multiple of 8 would keep every sequence on one XCD)
   const int t = id / (H * S);
+  const int hs = (id % (H * S) + t) % (H * S);
   const int h = hs / S, sq = hs % S;
   const int qt = CAUSAL ? ntiles - 1 - t : t;
   const int qa = max(0, min(cu_q[sq], Tq)), qb = max(qa, min(cu_q[sq + 1], Tq));
