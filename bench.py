@@ -41,13 +41,15 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
 EXP_PEAK_T = 16 * 256 * 2.4e9 / 1e12
 HBM_GBPS = 8000.0
 CSRC = os.path.join(ROOT, "transformer_attention_07_amd", "csrc")
+FWD_SOURCES = ("fa_fwd.hip", "stream_plan.h")
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
 def source_digest() -> str:
-    """sha256 over the kernel sources (csrc/*, in name order)."""
+    """sha256 over the forward pass's kernel sources (in name order): the
+    traffic record is valid while these are unchanged."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in FWD_SOURCES:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
