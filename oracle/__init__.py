@@ -28,6 +28,10 @@ Functions (all fp64, numpy in / numpy out):
       -> (dq, dk, dv): the gradients of attention_varlen, attention_bwd
       applied to each packed sequence (zero where a sequence has no queries
       or no keys).
+  attention_masked(q, k, v, scale, causal, window, nglobal, rows=None)
+      -> (o, lse): attention under a local-window + global-token mask
+      ("FlashAttention-2实现与优化" §7 sparse attention; the pattern is this
+      package's reading, stated in fa_oracle.c).
   threads() -> int   OpenMP threads the oracle uses.
 
 Parity status: pinned by tests/test_oracle_pins.py (closed forms, invariants,
@@ -76,6 +80,10 @@ def _bind(path: str):
                                             ctypes.c_double, ctypes.c_int,
                                             ctypes.POINTER(i64), i64,
                                             ctypes.POINTER(i64), i64]
+    lib.fa_oracle_attention_masked.restype = ctypes.c_int
+    lib.fa_oracle_attention_masked.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64, i64,
+                                               ctypes.c_double, ctypes.c_int, i64, i64,
+                                               ctypes.POINTER(i64), i64]
     lib.fa_oracle_threads.restype = ctypes.c_int
     lib.fa_oracle_threads.argtypes = []
     return lib
@@ -251,6 +259,34 @@ def attention_bwd_varlen(q, k, v, do, cu_q, cu_k, scale: float, causal: bool, li
                                 do[None, :, q0:q1], scale, causal, lib=lib)
         dq[:, q0:q1], dk[:, k0:k1], dv[:, k0:k1] = a[0], b[0], c[0]
     return dq, dk, dv
+
+
+def attention_masked(q, k, v, scale: float, causal: bool, window: int, nglobal: int,
+                     rows=None, lib=None) -> Tuple[np.ndarray, np.ndarray]:
+    """fp64 attention over the keys a local window + global-token mask leaves
+    visible (see fa_oracle_attention_masked); shapes as attention()."""
+    lib = lib or load()
+    squeeze = np.asarray(q).ndim == 3
+    q4, k4, v4 = _as4d(q), _as4d(k), _as4d(v)
+    B, H, Nq, D = q4.shape
+    Nk = k4.shape[2]
+    if k4.shape != (B, H, Nk, D) or v4.shape != (B, H, Nk, D):
+        raise ValueError("q/k/v shapes disagree")
+    if rows is None:
+        o, lse = np.empty((B, H, Nq, D)), np.empty((B, H, Nq))
+        rp, nr = None, 0
+    else:
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        o, lse = np.empty((r.size, D)), np.empty((r.size,))
+        rp, nr = r.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), r.size
+    st = lib.fa_oracle_attention_masked(_ptr(q4), _ptr(k4), _ptr(v4), _ptr(o), _ptr(lse),
+                                        B, H, Nq, Nk, D, float(scale), int(bool(causal)),
+                                        int(window), int(nglobal), rp, nr)
+    if st != 0:
+        raise RuntimeError(f"oracle failed with status {st}")
+    if rows is None and squeeze:
+        return o[:, 0], lse[:, 0]
+    return o, lse
 
 
 def threads(lib=None) -> int:

@@ -479,3 +479,98 @@ int fa_oracle_attention_bwd(const double *q, const double *k, const double *v,
     free(re);
     return failed ? ORACLE_ENOMEM : ORACLE_OK;
 }
+
+/*
+ * Attention under a local-window + global-token mask, the plain definition
+ * in double precision.  Page "FlashAttention-2实现与优化：高效注意力机制详解"
+ * §7 names sparse attention combining local windows and global tokens as an
+ * extension, and page "解释FlashAttention的显存优化原理" §二 (case 2) uses
+ * local blocks plus global key points; neither defines the pattern, so this
+ * file reads it as: key j (j < Nk) is visible to query i iff
+ *
+ *     (causal ? 0 <= i - j < window : |i - j| < window)      local band
+ *  or (j < nglobal || i < nglobal) && (!causal || j <= i)     global tokens
+ *
+ * (indices from 0 in both sequences; window >= 1, nglobal >= 0).  Over the
+ * visible keys the row is the two-pass softmax of fa_oracle_attention.  A
+ * row with no visible key (possible only when Nq > Nk) gets O = 0 and
+ * L = -inf.  "rows" as in fa_oracle_attention.
+ */
+static int visible_masked(int64_t i, int64_t j, int causal, int64_t window, int64_t nglobal)
+{
+    const int64_t d = i - j;
+    const int local = causal ? (d >= 0 && d < window) : (d > -window && d < window);
+    const int global = (j < nglobal || i < nglobal) && (!causal || j <= i);
+    return local || global;
+}
+
+int fa_oracle_attention_masked(const double *q, const double *k, const double *v,
+                               double *o, double *lse,
+                               int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+                               double scale, int causal, int64_t window, int64_t nglobal,
+                               const int64_t *rows, int64_t nrows)
+{
+    if (!q || !k || !v || !o || !lse || bad_shape(B, H, Nq, Nk, D) || window < 1 ||
+        nglobal < 0)
+        return ORACLE_EINVAL;
+    const int64_t total = B * H * Nq;
+    const int64_t count = rows ? nrows : total;
+    if (rows)
+        for (int64_t t = 0; t < nrows; ++t)
+            if (rows[t] < 0 || rows[t] >= total)
+                return ORACLE_EINVAL;
+    int failed = 0;
+
+#pragma omp parallel
+    {
+        double *w = (double *)malloc((size_t)Nk * sizeof(double));
+        int64_t *idx = (int64_t *)malloc((size_t)Nk * sizeof(int64_t));
+        if (!w || !idx) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 8)
+        for (int64_t t = 0; t < count; ++t) {
+            if (!w || !idx)
+                continue;
+            const int64_t r = rows ? rows[t] : t;
+            const int64_t bh = r / Nq, i = r % Nq;
+            const double *qi = q + r * D;
+            const double *kb = k + bh * Nk * D, *vb = v + bh * Nk * D;
+            double *oi = o + t * D;
+            int64_t n = 0;
+            for (int64_t j = 0; j < Nk; ++j)
+                if (visible_masked(i, j, causal, window, nglobal))
+                    idx[n++] = j;
+            for (int64_t d = 0; d < D; ++d)
+                oi[d] = 0.0;
+            if (n == 0) {
+                lse[t] = -INFINITY;
+                continue;
+            }
+            double m = -INFINITY;
+            for (int64_t c = 0; c < n; ++c) {
+                double dot = 0.0;
+                for (int64_t d = 0; d < D; ++d)
+                    dot += qi[d] * kb[idx[c] * D + d];
+                w[c] = scale * dot;
+                if (w[c] > m)
+                    m = w[c];
+            }
+            double l = 0.0;
+            for (int64_t c = 0; c < n; ++c) {
+                w[c] = exp(w[c] - m);
+                l += w[c];
+            }
+            for (int64_t c = 0; c < n; ++c)
+                for (int64_t d = 0; d < D; ++d)
+                    oi[d] += w[c] * vb[idx[c] * D + d];
+            for (int64_t d = 0; d < D; ++d)
+                oi[d] /= l;
+            lse[t] = m + log(l);
+        }
+        free(w);
+        free(idx);
+    }
+    return failed ? ORACLE_ENOMEM : ORACLE_OK;
+}

@@ -1,0 +1,112 @@
+"""Pins of the oracle's local-window + global-token attention
+(oracle.attention_masked).  The pages name the pattern without defining it
+(page "FlashAttention-2实现与优化：高效注意力机制详解" §7); the reading is
+stated in fa_oracle.c.  Pins:
+
+  * a window covering every key and no global tokens reduces to the dense
+    oracle (causal and not); so does nglobal >= Nq, Nk;
+  * window 1 without global tokens leaves only the diagonal: O_i = v_i
+    exactly and L_i = scale <q_i, k_i>;
+  * a pure-Python brute force (math.fsum) over a visibility set written
+    independently, on tiny shapes, Nq != Nk both ways;
+  * keys a row cannot see do not matter: changing them leaves the row's
+    output bit-identical;
+  * rows with no visible key (Nq > Nk) get O = 0 and L = -inf.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+import oracle
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert np.isfinite(err) and err <= tol, f"{what}: max-abs error {err:.3e} > {tol:.1e}"
+
+
+def _qkv(seed, B, H, Nq, Nk, D):
+    r = np.random.default_rng(seed)
+    return (r.standard_normal((B, H, Nq, D)), r.standard_normal((B, H, Nk, D)),
+            r.standard_normal((B, H, Nk, D)))
+
+
+def pin_masked_reduces_to_dense(lib):
+    q, k, v = _qkv(1, 2, 2, 13, 11, 4)
+    for causal in (False, True):
+        ref = oracle.attention(q, k, v, 0.6, causal, lib=lib)
+        for window, ng in ((13, 0), (100, 3), (1, 13), (2, 50)):
+            got = oracle.attention_masked(q, k, v, 0.6, causal, window, ng, lib=lib)
+            _close(got[0], ref[0], 0.0, f"dense O (window {window}, global {ng})")
+            _close(got[1], ref[1], 0.0, f"dense L (window {window}, global {ng})")
+
+
+def pin_masked_diagonal_only(lib):
+    q, k, v = _qkv(2, 1, 2, 9, 9, 5)
+    for causal in (False, True):
+        o, l = oracle.attention_masked(q, k, v, 0.7, causal, 1, 0, lib=lib)
+        _close(o, v, 0.0, "window 1: O = V")
+        _close(l, 0.7 * np.einsum("bhnd,bhnd->bhn", q, k), 1e-12, "window 1: L = s_ii")
+
+
+def _visible(i, j, causal, window, ng):
+    if causal and j > i:
+        return False
+    if abs(i - j) < window:
+        return True
+    return j < ng or i < ng
+
+
+def pin_masked_brute_force(lib):
+    for (Nq, Nk, window, ng) in ((7, 7, 2, 1), (9, 5, 3, 2), (4, 10, 2, 0), (6, 6, 4, 6)):
+        q, k, v = _qkv(3 + Nq, 1, 1, Nq, Nk, 3)
+        for causal in (False, True):
+            o, l = oracle.attention_masked(q, k, v, 0.9, causal, window, ng, lib=lib)
+            for i in range(Nq):
+                keys = [j for j in range(Nk) if _visible(i, j, causal, window, ng)]
+                if not keys:
+                    assert np.all(o[0, 0, i] == 0) and np.isneginf(l[0, 0, i])
+                    continue
+                s = [0.9 * math.fsum(q[0, 0, i] * k[0, 0, j]) for j in keys]
+                m = max(s)
+                w = [math.exp(x - m) for x in s]
+                tot = math.fsum(w)
+                ref = [math.fsum(wj * v[0, 0, j, d] for wj, j in zip(w, keys)) / tot
+                       for d in range(3)]
+                _close(o[0, 0, i], ref, 1e-12, "brute force O")
+                _close([l[0, 0, i]], [m + math.log(tot)], 1e-12, "brute force L")
+
+
+def pin_masked_hidden_keys_do_not_matter(lib):
+    q, k, v = _qkv(4, 1, 1, 40, 40, 4)
+    window, ng = 5, 2
+    o, l = oracle.attention_masked(q, k, v, 0.5, True, window, ng, lib=lib)
+    k2, v2 = k.copy(), v.copy()
+    k2[..., 10:20, :] += 5.0   # hidden from rows 25.. (not global, out of window)
+    v2[..., 10:20, :] *= -3.0
+    o2, l2 = oracle.attention_masked(q, k2, v2, 0.5, True, window, ng, lib=lib)
+    assert np.array_equal(o[..., 25:, :], o2[..., 25:, :]), "hidden keys changed O"
+    assert np.array_equal(l[..., 25:], l2[..., 25:]), "hidden keys changed L"
+    assert not np.allclose(o[..., 12, :], o2[..., 12, :]), "visible keys must matter"
+
+
+def pin_masked_rows_without_keys(lib):
+    q, k, v = _qkv(5, 1, 1, 12, 4, 3)
+    o, l = oracle.attention_masked(q, k, v, 0.5, True, 3, 0, lib=lib)
+    # rows i >= Nk + window - 1 = 6 see no key (window [i-2, i] past Nk)
+    assert np.all(o[0, 0, 6:] == 0) and np.all(np.isneginf(l[0, 0, 6:]))
+    assert np.all(np.isfinite(l[0, 0, :6]))
+
+
+ALL_MASKED_PINS = [
+    pin_masked_reduces_to_dense,
+    pin_masked_diagonal_only,
+    pin_masked_brute_force,
+    pin_masked_hidden_keys_do_not_matter,
+    pin_masked_rows_without_keys,
+]
