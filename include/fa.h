@@ -1,7 +1,8 @@
 /*
  * fa.h -- C ABI of the MI355X (gfx950) FlashAttention-2 library: the
  * forward pass (fa_fwd, fa_fwd_ws; fa_fwd_varlen for variable-length
- * batches) and its backward pass (fa_bwd).
+ * batches, fa_fwd_masked for local-window + global-token masks) and its
+ * backward pass (fa_bwd, fa_bwd_varlen).
  *
  * The operation (page "FlashAttention-2实现与优化：高效注意力机制详解",
  * §3.1 PyTorch forward and §3.2 Triton forward; page
@@ -188,6 +189,38 @@ int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *l
                   const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
                   int64_t S, int64_t H, int64_t Tq, int64_t Tk,
                   int64_t max_seqlen_q, int64_t D, float scale, int causal,
+                  int dtype, void *stream);
+
+/*
+ * fa_fwd_masked -- the forward pass under a local-window + global-token
+ * mask (page "FlashAttention-2实现与优化：高效注意力机制详解" §7, sparse
+ * attention combining local windows and global tokens; the pages give no
+ * definition, so this library reads it as): key j (< Nk) is visible to
+ * query i iff
+ *
+ *     (causal ? 0 <= i - j < window : |i - j| < window)
+ *  or (j < nglobal || i < nglobal) && (!causal || j <= i)
+ *
+ * and each row is the softmax over its visible keys: O_i and L_i as fa_fwd
+ * computes them over that key set.  A row with no visible key (only when
+ * Nq > Nk) gets O = 0 and lse = -inf.  With window >= max(Nq, Nk) and
+ * nglobal = 0 this is fa_fwd's operation.
+ *
+ *   q, k, v, o, lse, B, H, Nq, Nk, scale, causal   as fa_fwd
+ *   D          32, 64 or 128
+ *   window     >= 1 (window 1 leaves the diagonal)
+ *   nglobal    >= 0: the first nglobal queries and keys are global tokens
+ *   dtype      FA_BF16, FA_BF16_OF32, FA_F16 or FA_F16_OF32 (FA_F32:
+ *              FA_ERR_DTYPE)
+ *
+ * Key blocks and 32-key quarters in which no pair is visible are never
+ * read or computed, so the work is proportional to the visible pairs
+ * (rounded up to 128 x 32 blocks).  Status codes as fa_fwd; window < 1 or
+ * nglobal < 0 is FA_ERR_SHAPE.
+ */
+int fa_fwd_masked(const void *q, const void *k, const void *v, void *o, float *lse,
+                  int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+                  float scale, int causal, int64_t window, int64_t nglobal,
                   int dtype, void *stream);
 
 /*

@@ -565,9 +565,10 @@ int fa_oracle_attention_masked(const double *q, const double *k, const double *v
             for (int64_t c = 0; c < n; ++c)
                 for (int64_t d = 0; d < D; ++d)
                     oi[d] += w[c] * vb[idx[c] * D + d];
+            const double inv = 1.0 / l;
             for (int64_t d = 0; d < D; ++d)
-                oi[d] /= l;
-            lse[t] = m + log(l);
+                oi[d] *= inv;
+            lse[t] = log(l) + m;
         }
         free(w);
         free(idx);

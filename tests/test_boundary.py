@@ -240,3 +240,23 @@ def call_bwd_varlen(**kw):
 ])
 def test_bwd_varlen_validation(kw, status):
     assert call_bwd_varlen(**kw) == getattr(fa, status)
+
+
+def call_masked(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, H=3, Nq=100, Nk=90, D=64, scale=0.125, causal=1,
+             window=16, nglobal=4, dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return fa.fa_fwd_masked(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"],
+                            a["Nk"], a["D"], a["scale"], a["causal"], a["window"],
+                            a["nglobal"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"lse": None}, "FA_ERR_NULLPTR"), ({"Nk": 0}, "FA_ERR_SHAPE"),
+    ({"window": 0}, "FA_ERR_SHAPE"), ({"nglobal": -1}, "FA_ERR_SHAPE"),
+    ({"D": 16}, "FA_ERR_HEAD_DIM"), ({"dtype": fa.FA_F32}, "FA_ERR_DTYPE"),
+    ({"scale": math.inf}, "FA_ERR_SCALE"), ({"v": V + 4}, "FA_ERR_ALIGN"),
+    ({"o": K}, "FA_ERR_OVERLAP"),
+])
+def test_masked_validation(kw, status):
+    assert call_masked(**kw) == getattr(fa, status)

@@ -13,6 +13,8 @@ C-ABI mirrors (same names and meaning as include/fa.h):
               causal, dtype, ws_ptr, ws_bytes, stream) -> status
     fa_fwd_varlen(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, cu_q_ptr, cu_k_ptr, S, H,
                   Tq, Tk, max_seqlen_q, D, scale, causal, dtype, stream) -> status
+    fa_fwd_masked(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Nq, Nk, D, scale,
+                  causal, window, nglobal, dtype, stream) -> status
     fa_bwd_workspace_size(B, H, Nq, Nk, D, causal, dtype) -> (status, bytes)
     fa_bwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_ptr,
            B, H, Nq, Nk, D, scale, causal, dtype, ws_ptr, ws_bytes, stream)
@@ -29,6 +31,8 @@ Tensor convenience:
         allocator, split=False runs fa_fwd
     fwd_varlen(q, k, v, cu_q, cu_k, max_seqlen_q, causal=False, scale=None,
                out_dtype=None) -> (o, lse) through fa_fwd_varlen
+    fwd_masked(q, k, v, window, nglobal=0, causal=False, scale=None,
+               out_dtype=None) -> (o, lse) through fa_fwd_masked
     bwd(q, k, v, o, lse, do, causal=False, scale=None, grad_dtype=None)
         -> (dq, dk, dv) through fa_bwd
     bwd_varlen(q, k, v, o, lse, do, cu_q, cu_k, max_q, max_k, causal=False,
@@ -46,8 +50,8 @@ __all__ = [
     "FA_OK", "FA_ERR_NULLPTR", "FA_ERR_SHAPE", "FA_ERR_HEAD_DIM", "FA_ERR_DTYPE",
     "FA_ERR_SCALE", "FA_ERR_ALIGN", "FA_ERR_HIP", "FA_ERR_OVERLAP", "FA_ERR_WORKSPACE",
     "LIBRARY", "EXPORTS", "library", "fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws",
-    "fa_fwd_varlen", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_varlen", "fa_status_str",
-    "fa_last_hip_error", "fa_version", "fwd", "fwd_varlen", "bwd", "bwd_varlen", "FaError",
+    "fa_fwd_varlen", "fa_fwd_masked", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_varlen", "fa_status_str",
+    "fa_last_hip_error", "fa_version", "fwd", "fwd_varlen", "fwd_masked", "bwd", "bwd_varlen", "FaError",
 ]
 
 LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
@@ -57,7 +61,7 @@ FA_F32, FA_BF16, FA_BF16_OF32, FA_F16, FA_F16_OF32 = 0, 1, 2, 3, 4
  FA_ERR_ALIGN, FA_ERR_HIP, FA_ERR_OVERLAP, FA_ERR_WORKSPACE) = range(10)
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws", "fa_fwd_varlen",
+EXPORTS = ("fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws", "fa_fwd_varlen", "fa_fwd_masked",
            "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_varlen", "fa_status_str",
            "fa_last_hip_error", "fa_version")
 
@@ -93,6 +97,9 @@ def library() -> ctypes.CDLL:
     lib.fa_fwd_varlen.restype = ctypes.c_int
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                   ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
+    lib.fa_fwd_masked.restype = ctypes.c_int
+    lib.fa_fwd_masked.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
+                                  ctypes.c_int, i64, i64, ctypes.c_int, vp]
     lib.fa_bwd_workspace_size.restype = ctypes.c_int
     lib.fa_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int,
                                           ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
@@ -141,6 +148,14 @@ def fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, S, H, Tq, Tk, max_seqlen_q, D, sc
     return int(library().fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, S, H, Tq, Tk,
                                        max_seqlen_q, D, float(scale), int(causal),
                                        int(dtype), stream))
+
+
+def fa_fwd_masked(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, window, nglobal, dtype,
+                  stream) -> int:
+    """Raw C call; pointers are integers (device addresses) or None."""
+    return int(library().fa_fwd_masked(q, k, v, o, lse, B, H, Nq, Nk, D, float(scale),
+                                       int(causal), int(window), int(nglobal), int(dtype),
+                                       stream))
 
 
 def fa_bwd_workspace_size(B, H, Nq, Nk, D, causal, dtype) -> Tuple[int, int]:
@@ -419,3 +434,39 @@ def bwd_varlen(q, k, v, o, lse, do, cu_q, cu_k, max_q: int, max_k: int,
             msg += ": " + fa_last_hip_error()
         raise FaError(st, msg)
     return dq, dk, dv
+
+
+def fwd_masked(q, k, v, window: int, nglobal: int = 0, causal: bool = False,
+               scale: Optional[float] = None, out_dtype=None, stream=None
+               ) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """Local-window + global-token attention forward (fa_fwd_masked) on
+    device tensors shaped as for fwd() (16-bit inputs)."""
+    import torch
+
+    if q.dim() not in (3, 4) or k.dim() != q.dim() or v.dim() != q.dim():
+        raise ValueError("q, k, v must all be [B,N,D] or all [B,H,N,D]")
+    q4, k4 = (x.unsqueeze(1) if q.dim() == 3 else x for x in (q, k))
+    B, H, Nq, D = q4.shape
+    Nk = k4.shape[2]
+    if tuple(k.shape) != tuple(v.shape) or tuple(k4.shape) != (B, H, Nk, D):
+        raise ValueError("shape mismatch among q, k, v")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    if not all(x.is_cuda and x.device == q.device and x.is_contiguous() for x in (q, k, v)):
+        raise ValueError("q, k, v must be contiguous on the same GPU device")
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    code = _dtype_code(torch, q.dtype, out_dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = fa_fwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       B, H, Nq, Nk, D, scale, causal, window, nglobal, code, stream)
+    if st != FA_OK:
+        msg = fa_status_str(st)
+        if st == FA_ERR_HIP:
+            msg += ": " + fa_last_hip_error()
+        raise FaError(st, msg)
+    return o, lse

@@ -20,6 +20,8 @@ SOURCES = [
     (os.path.join(PKG, "csrc", "fa_fwd.hip"), ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
     # the backward kernels keep their dK/dV/dQ accumulators in AGPRs
     (os.path.join(PKG, "csrc", "fa_bwd.hip"), []),
+    # local-window + global-token forward (same tile helpers as the backward)
+    (os.path.join(PKG, "csrc", "fa_masked.hip"), []),
 ]
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libfa.so")
