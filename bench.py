@@ -173,6 +173,10 @@ def main() -> int:
                     help="time fa_fwd_varlen instead: the workload's tokens (B*N, one "
                          "head) cut into S sequences of seeded lengths (seed 77, at "
                          "least 64 tokens each), flops summed per sequence")
+    ap.add_argument("--masked", default=None, metavar="W,G",
+                    help="time fa_fwd_masked instead: B=1 H=8 N=32768 D=128 causal bf16 "
+                         "under a local window W with G global tokens; flops counted "
+                         "over the visible pairs only (4*D each)")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward pass (default) or the backward pass "
                          "(fa_bwd, fed by one forward call; flops counted as 2.5x "
@@ -221,6 +225,31 @@ def main() -> int:
 
     bwd = args.which == "bwd"
     lens = None
+    masked = None
+    if args.masked:
+        import numpy as np
+        from workloads import gen_qkv
+
+        if bwd or args.varlen:
+            raise SystemExit("--masked times the forward pass alone")
+        W, G = (int(x) for x in args.masked.split(","))
+        MB, MH, MN, MD = 1, 8, 32768, 128
+        q, k, v = (t.to(dev) for t in gen_qkv(MB, MH, MN, MN, MD, seed=2601, dtype="bf16"))
+        o = torch.empty(q.shape, dtype=out_dt, device=dev)
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+        scale = 1.0 / math.sqrt(MD)
+        i = np.arange(MN, dtype=np.int64)
+        lo = np.maximum(0, i - W + 1)  # causal window [lo, i]
+        # visible keys of row i: all j <= i for a global row, else the window
+        # plus the global keys before it
+        per_row = np.where(i < G, i + 1, (i - lo + 1) + np.minimum(G, lo))
+        masked = {"window": W, "global": G, "visible_pairs": int(per_row.sum()) * MB * MH,
+                  "shape": [MB, MH, MN, MD]}
+        argv = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), MB, MH,
+                MN, MN, MD, scale, 1, W, G, code, sp)
+        call = lib.fa_fwd_masked
+        args.entry = "fa_fwd_masked"
+        ws_bytes = 0
     if args.varlen:
         from workloads import varlen_lengths
 
@@ -315,6 +344,8 @@ def main() -> int:
     if lens is not None:
         flops = sum(4.0 * n * n * w.D / (2 if w.causal else 1) for n in lens)
         flops *= 2.5 if bwd else 1.0
+    if masked is not None:
+        flops = 4.0 * masked["shape"][3] * masked["visible_pairs"]
     value = flops / (ms_per_step * 1e-3) / 1e12
     dkey = "f32" if in_dt == torch.float32 else ("bf16" if in_dt == torch.bfloat16 else "f16")
     peak = PEAK_TFLOPS[dkey]
@@ -339,10 +370,12 @@ def main() -> int:
                    "causal": w.causal, "out": str(out_dt).replace("torch.", ""),
                    "flops_per_step": flops, "entry": args.entry,
                    **({"varlen_lengths": lens} if lens is not None else {}),
+                   **({"masked": masked} if masked is not None else {}),
                    "workspace_bytes": ws_bytes},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": None if (bwd or lens is not None) else measured_traffic(name),
+                     "traffic": None if (bwd or lens is not None or masked is not None)
+        else measured_traffic(name),
                      "kernel_ms": round(kernel_ms, 5),
                      "group_ms": {"groups": len(group_ms),
                                   "median": round(group_ms[len(group_ms) // 2], 5),
@@ -350,14 +383,14 @@ def main() -> int:
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count},
     }
-    if w.D <= 64 and not bwd:
+    if w.D <= 64 and not bwd and masked is None:
         # one exp per visible score (half of them when causal): at small head
         # dims the softmax's transcendentals, not the MFMAs, bound the kernel
         exps = w.B * w.H * w.N * w.N / (2 if w.causal else 1)
         rate = exps / (kernel_ms * 1e-3) / 1e12
         line["exp_roofline"] = {"achieved": round(rate, 3), "peak": round(EXP_PEAK_T, 3),
                                 "unit": "Texp/s", "frac": round(rate / EXP_PEAK_T, 4)}
-    if not args.no_cpu_baseline and lens is None:
+    if not args.no_cpu_baseline and lens is None and masked is None:
         line["cpu_baseline"] = (cpu_baseline_bwd(w, args.cpu_seconds) if bwd
                                 else cpu_baseline(w, args.cpu_seconds))
     print(json.dumps(line), flush=True)
