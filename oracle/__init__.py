@@ -32,6 +32,9 @@ Functions (all fp64, numpy in / numpy out):
       -> (o, lse): attention under a local-window + global-token mask
       ("FlashAttention-2实现与优化" §7 sparse attention; the pattern is this
       package's reading, stated in fa_oracle.c).
+  attention_bwd_masked(q, k, v, do, scale, causal, window, nglobal)
+      -> (dq, dk, dv): the gradients of attention_masked (chain rule over the
+      visible pairs).
   threads() -> int   OpenMP threads the oracle uses.
 
 Parity status: pinned by tests/test_oracle_pins.py (closed forms, invariants,
@@ -84,6 +87,10 @@ def _bind(path: str):
     lib.fa_oracle_attention_masked.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64, i64,
                                                ctypes.c_double, ctypes.c_int, i64, i64,
                                                ctypes.POINTER(i64), i64]
+    lib.fa_oracle_attention_bwd_masked.restype = ctypes.c_int
+    lib.fa_oracle_attention_bwd_masked.argtypes = [dp, dp, dp, dp, dp, dp, dp, i64, i64, i64,
+                                                   i64, i64, ctypes.c_double, ctypes.c_int,
+                                                   i64, i64]
     lib.fa_oracle_threads.restype = ctypes.c_int
     lib.fa_oracle_threads.argtypes = []
     return lib
@@ -287,6 +294,27 @@ def attention_masked(q, k, v, scale: float, causal: bool, window: int, nglobal: 
     if rows is None and squeeze:
         return o[:, 0], lse[:, 0]
     return o, lse
+
+
+def attention_bwd_masked(q, k, v, do, scale: float, causal: bool, window: int, nglobal: int,
+                         lib=None):
+    """fp64 gradients of attention_masked for upstream gradient do."""
+    lib = lib or load()
+    squeeze = np.asarray(q).ndim == 3
+    q4, k4, v4, g4 = _as4d(q), _as4d(k), _as4d(v), _as4d(do)
+    B, H, Nq, D = q4.shape
+    Nk = k4.shape[2]
+    if k4.shape != (B, H, Nk, D) or v4.shape != (B, H, Nk, D) or g4.shape != q4.shape:
+        raise ValueError("q/k/v/do shapes disagree")
+    dq, dk, dv = np.empty(q4.shape), np.empty(k4.shape), np.empty(k4.shape)
+    st = lib.fa_oracle_attention_bwd_masked(_ptr(q4), _ptr(k4), _ptr(v4), _ptr(g4), _ptr(dq),
+                                            _ptr(dk), _ptr(dv), B, H, Nq, Nk, D, float(scale),
+                                            int(bool(causal)), int(window), int(nglobal))
+    if st != 0:
+        raise RuntimeError(f"oracle failed with status {st}")
+    if squeeze:
+        return dq[:, 0], dk[:, 0], dv[:, 0]
+    return dq, dk, dv
 
 
 def threads(lib=None) -> int:

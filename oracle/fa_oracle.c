@@ -575,3 +575,129 @@ int fa_oracle_attention_masked(const double *q, const double *k, const double *v
     }
     return failed ? ORACLE_ENOMEM : ORACLE_OK;
 }
+
+/*
+ * Gradients of fa_oracle_attention_masked (the local-window + global-token
+ * mask), the chain rule in double precision over the visible pairs only:
+ * with P_ij the softmax of row i over its visible keys,
+ *     dV_j = sum_i P_ij dO_i,  dP_ij = <dO_i, v_j>,  D_i = sum_j P_ij dP_ij,
+ *     dS_ij = P_ij (dP_ij - D_i),
+ *     dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i.
+ * Rows with no visible key contribute nothing (dQ_i = 0).  Full outputs
+ * only (no row lists).
+ */
+int fa_oracle_attention_bwd_masked(const double *q, const double *k, const double *v,
+                                   const double *dout, double *dq, double *dk, double *dv,
+                                   int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+                                   double scale, int causal, int64_t window, int64_t nglobal)
+{
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || bad_shape(B, H, Nq, Nk, D) ||
+        window < 1 || nglobal < 0)
+        return ORACLE_EINVAL;
+    const int64_t totq = B * H * Nq, totk = B * H * Nk;
+    double *m = (double *)malloc((size_t)totq * sizeof(double));
+    double *l = (double *)malloc((size_t)totq * sizeof(double));
+    double *rd = (double *)malloc((size_t)totq * sizeof(double));
+    if (!m || !l || !rd) {
+        free(m);
+        free(l);
+        free(rd);
+        return ORACLE_ENOMEM;
+    }
+
+#pragma omp parallel
+    {
+        /* every query row: max, normaliser and the row term D_i */
+#pragma omp for schedule(dynamic, 8)
+        for (int64_t r = 0; r < totq; ++r) {
+            const int64_t bh = r / Nq, i = r % Nq;
+            const double *qi = q + r * D, *gi = dout + r * D;
+            const double *kb = k + bh * Nk * D, *vb = v + bh * Nk * D;
+            double mx = -INFINITY;
+            for (int64_t j = 0; j < Nk; ++j) {
+                if (!visible_masked(i, j, causal, window, nglobal))
+                    continue;
+                double dot = 0.0;
+                for (int64_t d = 0; d < D; ++d)
+                    dot += qi[d] * kb[j * D + d];
+                if (scale * dot > mx)
+                    mx = scale * dot;
+            }
+            double sum = 0.0, acc = 0.0;
+            for (int64_t j = 0; j < Nk; ++j) {
+                if (!visible_masked(i, j, causal, window, nglobal))
+                    continue;
+                double dot = 0.0, dp = 0.0;
+                for (int64_t d = 0; d < D; ++d) {
+                    dot += qi[d] * kb[j * D + d];
+                    dp += gi[d] * vb[j * D + d];
+                }
+                const double e = exp(scale * dot - mx);
+                sum += e;
+                acc += e * dp;
+            }
+            m[r] = mx;
+            l[r] = sum;
+            rd[r] = sum > 0.0 ? acc / sum : 0.0;
+        }
+
+        /* dQ, row by row */
+#pragma omp for schedule(dynamic, 8)
+        for (int64_t r = 0; r < totq; ++r) {
+            const int64_t bh = r / Nq, i = r % Nq;
+            const double *qi = q + r * D, *gi = dout + r * D;
+            const double *kb = k + bh * Nk * D, *vb = v + bh * Nk * D;
+            double *aq = dq + r * D;
+            for (int64_t d = 0; d < D; ++d)
+                aq[d] = 0.0;
+            for (int64_t j = 0; j < Nk; ++j) {
+                if (!visible_masked(i, j, causal, window, nglobal))
+                    continue;
+                double dot = 0.0, dp = 0.0;
+                for (int64_t d = 0; d < D; ++d) {
+                    dot += qi[d] * kb[j * D + d];
+                    dp += gi[d] * vb[j * D + d];
+                }
+                const double p = exp(scale * dot - m[r]) / l[r];
+                const double ds = p * (dp - rd[r]);
+                for (int64_t d = 0; d < D; ++d)
+                    aq[d] += ds * kb[j * D + d];
+            }
+            for (int64_t d = 0; d < D; ++d)
+                aq[d] *= scale;
+        }
+
+        /* dK and dV, key by key */
+#pragma omp for schedule(dynamic, 8)
+        for (int64_t c = 0; c < totk; ++c) {
+            const int64_t bh = c / Nk, j = c % Nk;
+            const double *kc = k + c * D, *vc = v + c * D;
+            double *ak = dk + c * D, *av = dv + c * D;
+            for (int64_t d = 0; d < D; ++d)
+                ak[d] = av[d] = 0.0;
+            for (int64_t i = 0; i < Nq; ++i) {
+                if (!visible_masked(i, j, causal, window, nglobal))
+                    continue;
+                const int64_t r = bh * Nq + i;
+                const double *qi = q + r * D, *gi = dout + r * D;
+                double dot = 0.0, dp = 0.0;
+                for (int64_t d = 0; d < D; ++d) {
+                    dot += qi[d] * kc[d];
+                    dp += gi[d] * vc[d];
+                }
+                const double p = exp(scale * dot - m[r]) / l[r];
+                const double ds = p * (dp - rd[r]);
+                for (int64_t d = 0; d < D; ++d) {
+                    av[d] += p * gi[d];
+                    ak[d] += ds * qi[d];
+                }
+            }
+            for (int64_t d = 0; d < D; ++d)
+                ak[d] *= scale;
+        }
+    }
+    free(m);
+    free(l);
+    free(rd);
+    return ORACLE_OK;
+}

@@ -103,7 +103,58 @@ def pin_masked_rows_without_keys(lib):
     assert np.all(np.isfinite(l[0, 0, :6]))
 
 
+def pin_masked_bwd_reduces_to_dense(lib):
+    q, k, v = _qkv(6, 1, 2, 12, 9, 3)
+    g = np.random.default_rng(7).standard_normal(q.shape)
+    for causal in (False, True):
+        ref = oracle.attention_bwd(q, k, v, g, 0.5, causal, lib=lib)
+        got = oracle.attention_bwd_masked(q, k, v, g, 0.5, causal, 100, 0, lib=lib)
+        for a, b in zip(got, ref):
+            _close(a, b, 1e-12, "masked bwd reduces to dense")
+
+
+def pin_masked_bwd_diagonal(lib):
+    """window 1: each row sees only its own key, so dQ = dK = 0, dV_i = dO_i."""
+    q, k, v = _qkv(8, 1, 1, 7, 7, 4)
+    g = np.random.default_rng(9).standard_normal(q.shape)
+    for causal in (False, True):
+        dq, dk, dv = oracle.attention_bwd_masked(q, k, v, g, 0.8, causal, 1, 0, lib=lib)
+        _close(dq, np.zeros_like(dq), 1e-14, "diagonal dQ")
+        _close(dk, np.zeros_like(dk), 1e-14, "diagonal dK")
+        _close(dv, g, 1e-14, "diagonal dV")
+
+
+def pin_masked_bwd_finite_differences(lib):
+    h = 1e-5
+    for Nq, Nk, window, ng, causal in ((6, 6, 2, 1, True), (5, 7, 3, 2, False),
+                                       (7, 4, 2, 0, True)):
+        q, k, v = _qkv(10 + Nq, 1, 1, Nq, Nk, 2)
+        g = np.random.default_rng(11).standard_normal(q.shape)
+        grads = oracle.attention_bwd_masked(q, k, v, g, 0.7, causal, window, ng, lib=lib)
+        base = {"q": q, "k": k, "v": v}
+
+        def loss(**kw):
+            a = dict(base)
+            a.update(kw)
+            o, _ = oracle.attention_masked(a["q"], a["k"], a["v"], 0.7, causal, window, ng,
+                                           lib=lib)
+            return float((o * g).sum())
+
+        for name, grad in zip(("q", "k", "v"), grads):
+            x = base[name]
+            num = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                num[idx] = (loss(**{name: xp}) - loss(**{name: xm})) / (2 * h)
+            _close(grad, num, 1e-7, f"masked finite differences d{name}")
+
+
 ALL_MASKED_PINS = [
+    pin_masked_bwd_reduces_to_dense,
+    pin_masked_bwd_diagonal,
+    pin_masked_bwd_finite_differences,
     pin_masked_reduces_to_dense,
     pin_masked_diagonal_only,
     pin_masked_brute_force,
