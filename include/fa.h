@@ -2,7 +2,7 @@
  * fa.h -- C ABI of the MI355X (gfx950) FlashAttention-2 library: the
  * forward pass (fa_fwd, fa_fwd_ws; fa_fwd_varlen for variable-length
  * batches, fa_fwd_masked for local-window + global-token masks) and its
- * backward pass (fa_bwd, fa_bwd_varlen).
+ * backward pass (fa_bwd, fa_bwd_varlen, fa_bwd_masked).
  *
  * The operation (page "FlashAttention-2实现与优化：高效注意力机制详解",
  * §3.1 PyTorch forward and §3.2 Triton forward; page
@@ -276,6 +276,21 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o,
            int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
            float scale, int causal, int dtype, void *workspace,
            size_t workspace_bytes, void *stream);
+
+/*
+ * fa_bwd_masked -- fa_bwd under the local-window + global-token mask of
+ * fa_fwd_masked (same window, nglobal and causal rule; o and lse from
+ * fa_fwd_masked): the gradients of its O over the visible pairs.  Rows
+ * without a visible key get dq = 0; keys no row sees get dk = dv = 0.
+ * Query and key blocks without a visible pair are skipped.  Arguments,
+ * workspace, dtypes, head dims and status codes as fa_bwd; window < 1 or
+ * nglobal < 0 is FA_ERR_SHAPE.
+ */
+int fa_bwd_masked(const void *q, const void *k, const void *v, const void *o,
+                  const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                  int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+                  float scale, int causal, int64_t window, int64_t nglobal,
+                  int dtype, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * fa_bwd_varlen -- fa_bwd over a variable-length batch laid out as for

@@ -260,3 +260,21 @@ def call_masked(**kw):
 ])
 def test_masked_validation(kw, status):
     assert call_masked(**kw) == getattr(fa, status)
+
+
+def test_bwd_masked_validation():
+    def call(**kw):
+        a = dict(q=Q, k=K, v=V, o=O, lse=L, do=DO, dq=DQ, dk=DK, dv=DV, B=2, H=3, Nq=100,
+                 Nk=90, D=64, scale=0.125, causal=1, window=8, nglobal=2, dtype=fa.FA_BF16,
+                 ws=WS, ws_bytes=1 << 20, stream=None)
+        a.update(kw)
+        return fa.fa_bwd_masked(*(a[x] for x in ("q", "k", "v", "o", "lse", "do", "dq", "dk",
+                                                  "dv", "B", "H", "Nq", "Nk", "D", "scale",
+                                                  "causal", "window", "nglobal", "dtype",
+                                                  "ws", "ws_bytes", "stream")))
+    assert call(window=0) == fa.FA_ERR_SHAPE
+    assert call(nglobal=-1) == fa.FA_ERR_SHAPE
+    assert call(dk=None) == fa.FA_ERR_NULLPTR
+    assert call(D=16) == fa.FA_ERR_HEAD_DIM
+    assert call(dq=Q) == fa.FA_ERR_OVERLAP
+    assert call(ws=None) == fa.FA_ERR_WORKSPACE

@@ -19,6 +19,9 @@ C-ABI mirrors (same names and meaning as include/fa.h):
     fa_bwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_ptr,
            B, H, Nq, Nk, D, scale, causal, dtype, ws_ptr, ws_bytes, stream)
         -> status
+    fa_bwd_masked(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr,
+                  dv_ptr, B, H, Nq, Nk, D, scale, causal, window, nglobal, dtype,
+                  ws_ptr, ws_bytes, stream) -> status
     fa_bwd_varlen(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr,
                   dv_ptr, cu_q_ptr, cu_k_ptr, S, H, Tq, Tk, max_q, max_k, D, scale,
                   causal, dtype, ws_ptr, ws_bytes, stream) -> status
@@ -33,8 +36,9 @@ Tensor convenience:
                out_dtype=None) -> (o, lse) through fa_fwd_varlen
     fwd_masked(q, k, v, window, nglobal=0, causal=False, scale=None,
                out_dtype=None) -> (o, lse) through fa_fwd_masked
-    bwd(q, k, v, o, lse, do, causal=False, scale=None, grad_dtype=None)
-        -> (dq, dk, dv) through fa_bwd
+    bwd(q, k, v, o, lse, do, causal=False, scale=None, grad_dtype=None,
+        window=None, nglobal=0) -> (dq, dk, dv) through fa_bwd (fa_bwd_masked
+        when a window is given)
     bwd_varlen(q, k, v, o, lse, do, cu_q, cu_k, max_q, max_k, causal=False,
                scale=None, grad_dtype=None) -> (dq, dk, dv) through fa_bwd_varlen
 """
@@ -50,7 +54,7 @@ __all__ = [
     "FA_OK", "FA_ERR_NULLPTR", "FA_ERR_SHAPE", "FA_ERR_HEAD_DIM", "FA_ERR_DTYPE",
     "FA_ERR_SCALE", "FA_ERR_ALIGN", "FA_ERR_HIP", "FA_ERR_OVERLAP", "FA_ERR_WORKSPACE",
     "LIBRARY", "EXPORTS", "library", "fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws",
-    "fa_fwd_varlen", "fa_fwd_masked", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_varlen", "fa_status_str",
+    "fa_fwd_varlen", "fa_fwd_masked", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_varlen", "fa_bwd_masked", "fa_status_str",
     "fa_last_hip_error", "fa_version", "fwd", "fwd_varlen", "fwd_masked", "bwd", "bwd_varlen", "FaError",
 ]
 
@@ -62,8 +66,8 @@ FA_F32, FA_BF16, FA_BF16_OF32, FA_F16, FA_F16_OF32 = 0, 1, 2, 3, 4
 
 # Every symbol include/fa.h declares.
 EXPORTS = ("fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws", "fa_fwd_varlen", "fa_fwd_masked",
-           "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_varlen", "fa_status_str",
-           "fa_last_hip_error", "fa_version")
+           "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_varlen", "fa_bwd_masked",
+           "fa_status_str", "fa_last_hip_error", "fa_version")
 
 _lib = None
 
@@ -107,6 +111,10 @@ def library() -> ctypes.CDLL:
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                            ctypes.c_float, ctypes.c_int, ctypes.c_int, vp, ctypes.c_size_t,
                            vp]
+    lib.fa_bwd_masked.restype = ctypes.c_int
+    lib.fa_bwd_masked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                  ctypes.c_float, ctypes.c_int, i64, i64, ctypes.c_int, vp,
+                                  ctypes.c_size_t, vp]
     lib.fa_bwd_varlen.restype = ctypes.c_int
     lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64,
                                   i64, i64, i64, i64, ctypes.c_float, ctypes.c_int,
@@ -172,6 +180,14 @@ def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, B, H, Nq, Nk, D, scale, causal, dtyp
     return int(library().fa_bwd(q, k, v, o, lse, do, dq, dk, dv, B, H, Nq, Nk, D,
                                 float(scale), int(causal), int(dtype), ws, int(ws_bytes),
                                 stream))
+
+
+def fa_bwd_masked(q, k, v, o, lse, do, dq, dk, dv, B, H, Nq, Nk, D, scale, causal, window,
+                  nglobal, dtype, ws, ws_bytes, stream) -> int:
+    """Raw C call; pointers are integers (device addresses) or None."""
+    return int(library().fa_bwd_masked(q, k, v, o, lse, do, dq, dk, dv, B, H, Nq, Nk, D,
+                                       float(scale), int(causal), int(window), int(nglobal),
+                                       int(dtype), ws, int(ws_bytes), stream))
 
 
 def fa_bwd_varlen(q, k, v, o, lse, do, dq, dk, dv, cu_q, cu_k, S, H, Tq, Tk, max_q, max_k,
@@ -281,13 +297,15 @@ def fwd(q, k, v, causal: bool = False, scale: Optional[float] = None,
 
 
 def bwd(q, k, v, o, lse, do, causal: bool = False, scale: Optional[float] = None,
-        grad_dtype=None, out=None, stream=None
-        ) -> Tuple["torch.Tensor", "torch.Tensor", "torch.Tensor"]:
+        grad_dtype=None, out=None, stream=None, window: Optional[int] = None,
+        nglobal: int = 0) -> Tuple["torch.Tensor", "torch.Tensor", "torch.Tensor"]:
     """Attention backward on device tensors (fa_bwd).
 
     q, o, do: [B,Nq,D] or [B,H,Nq,D]; k, v: [B,Nk,D] or [B,H,Nk,D]; all of
     one 16-bit dtype (bf16 or fp16), same device, contiguous; lse fp32 shaped
-    like q[..., 0] (the forward's outputs o and lse).  Returns (dq, dk, dv)
+    like q[..., 0] (the forward's outputs o and lse; with ``window`` the
+    outputs of fwd_masked with the same window and ``nglobal``, and the
+    gradients are those of the masked pass).  Returns (dq, dk, dv)
     shaped like q, k, v in ``grad_dtype`` (default: the input dtype; fp32
     keeps the gradients unrounded).  ``scale`` defaults to 1/sqrt(D) and
     must equal the forward's.  The row-term workspace comes from torch's
@@ -331,9 +349,13 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, scale: Optional[float] = None
         ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
         if not own_stream:
             ws.record_stream(torch.cuda.ExternalStream(stream, device=q.device))
-        st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                    do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Nq,
-                    Nk, D, scale, causal, code, ws.data_ptr(), nbytes, stream)
+        ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Nq, Nk, D,
+                scale, causal)
+        if window is None:
+            st = fa_bwd(*ptrs, code, ws.data_ptr(), nbytes, stream)
+        else:
+            st = fa_bwd_masked(*ptrs, window, nglobal, code, ws.data_ptr(), nbytes, stream)
     if st != FA_OK:
         msg = fa_status_str(st)
         if st == FA_ERR_HIP:

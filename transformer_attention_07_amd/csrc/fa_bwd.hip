@@ -161,12 +161,15 @@ __device__ __forceinline__ Slice resolve(int BH, int Nq, int Nk, const int *cu_q
 // key0 + 32*(w & 1) .. +31 and, of every 128-query block, the 32-row
 // quarters par and par + 2 (par = w >> 1); the two parities are summed at
 // the end.
-template <typename T, typename OT, int D, bool CAUSAL>
+// MASKED: the local-window + global-token mask `mk` (CAUSAL is then false
+// and mk.causal carries the causal rule); query blocks, wave quarters and
+// pairs the mask hides are skipped or zeroed.
+template <typename T, typename OT, int D, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dl,
     OT *__restrict__ dk, OT *__restrict__ dv, int Nq, int Nk, int BH, float c, float scale,
-    const int *__restrict__ cu_q, const int *__restrict__ cu_k, int S) {
+    const int *__restrict__ cu_q, const int *__restrict__ cu_k, int S, Mask mk) {
   using M = Mma<T>;
   typedef typename M::frag frag;
   constexpr int KF = D / 16;  // MFMA steps along D
@@ -222,26 +225,43 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv(
       stat = r < Nq ? ds_[r] : 0.f;
   };
   auto qbuf = [&](int buf) { return smem + buf * 2 * BB; };
+  // next query block (from bb) in which some query sees a key of the tile
+  const int klo = kt * kTile, khi = min(klo + kTile, Nk) - 1;
+  auto next_blk = [&](int bb) {
+    if constexpr (MASKED)
+      while (bb < nblk &&
+             !mk.any(qstart + bb * kBlk, min(qstart + bb * kBlk + kBlk, Nq) - 1, klo, khi))
+        ++bb;
+    return bb;
+  };
 
-  if (nblk > 0) {
-    st.load(qs, qstart, Nq, tid);
+  int b = next_blk(0);
+  if (b < nblk) {
+    st.load(qs, qstart + b * kBlk, Nq, tid);
     st.store(qbuf(0), tid);
-    st.load(dos, qstart, Nq, tid);
+    st.load(dos, qstart + b * kBlk, Nq, tid);
     st.store(qbuf(0) + BB, tid);
-    load_stat(qstart);
+    load_stat(qstart + b * kBlk);
     stats[tid] = stat;
   }
   __syncthreads();
-  for (int b = 0; b < nblk; ++b) {
-    const int cur = b & 1;
-    const bool nx = b + 1 < nblk;
+  int cur = 0;
+  while (b < nblk) {
+    const int nb = next_blk(b + 1);
+    const bool nx = nb < nblk;
     const int i0 = qstart + b * kBlk;
+    const int in = qstart + nb * kBlk;
     if (nx) {
-      st.load(qs, i0 + kBlk, Nq, tid);
-      load_stat(i0 + kBlk);
+      st.load(qs, in, Nq, tid);
+      load_stat(in);
     }
     // wave-uniform: does any of this wave's queries see one of its keys?
-    const bool live = !CAUSAL || i0 + kOwn * (par + 2) + kOwn - 1 >= key0;
+    bool live;
+    if constexpr (MASKED)
+      live = mk.any(i0 + kOwn * par, min(i0 + kOwn * (par + 2) + kOwn, Nq) - 1, key0,
+                    min(key0 + kOwn, Nk) - 1);
+    else
+      live = !CAUSAL || i0 + kOwn * (par + 2) + kOwn - 1 >= key0;
     const lds_char *qb = qbuf(cur);
     const lds_char *db = qb + BB;
     const lds_float *l2 = stats + cur * 2 * kBlk;
@@ -263,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv(
     if (nx) {
       st.store(qbuf(cur ^ 1), tid);
       stats[(cur ^ 1) * 2 * kBlk + tid] = stat;
-      st.load(dos, i0 + kBlk, Nq, tid);
+      st.load(dos, in, Nq, tid);
     }
     if (live) {
 #pragma unroll
@@ -279,7 +299,11 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv(
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * r4 + e;
             float pr = exp2f(fmaf(s[hf][r], c, -lv[e]));
-            if (CAUSAL && myk > i0 + ib + e) pr = 0.f;
+            if constexpr (MASKED) {
+              if (!mk.visible(i0 + ib + e, myk)) pr = 0.f;
+            } else if (CAUSAL && myk > i0 + ib + e) {
+              pr = 0.f;
+            }
             p[r] = pr;
             dsv[r] = pr * (dp[hf][r] - dv4[e]);
           }
@@ -298,6 +322,8 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv(
     }
     if (nx) st.store(qbuf(cur ^ 1) + BB, tid);
     __syncthreads();
+    cur ^= 1;
+    b = nb;
   }
 
   pair_sum<NC>(dva, smem, grp, par, lane);
@@ -318,12 +344,12 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv(
 // dQ: one workgroup per (batch*head, kTile queries).  Wave w owns queries
 // qw0 + 32*(w & 1) .. +31 and, of every 128-key block, the 32-key quarters
 // par and par + 2 (par = w >> 1); the two parities are summed at the end.
-template <typename T, typename OT, int D, bool CAUSAL>
+template <typename T, typename OT, int D, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(kThreads) void fa_bwd_dq(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dl,
     OT *__restrict__ dq, int Nq, int Nk, int BH, int nqt, float c, float scale,
-    const int *__restrict__ cu_q, const int *__restrict__ cu_k, int S) {
+    const int *__restrict__ cu_q, const int *__restrict__ cu_k, int S, Mask mk) {
   using M = Mma<T>;
   typedef typename M::frag frag;
   constexpr int KF = D / 16;
@@ -365,20 +391,34 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dq(
   const int kend = CAUSAL ? min(Nk, qt * kTile + kTile) : Nk;
   const int nblk = (kend + kBlk - 1) / kBlk;
   auto kbuf = [&](int buf) { return smem + buf * 2 * BB; };
+  // next key block (from bb) holding a key that some query of the tile sees
+  const int qlo = qt * kTile, qhi = min(qlo + kTile, Nq) - 1;
+  auto next_blk = [&](int bb) {
+    if constexpr (MASKED)
+      while (bb < nblk && !mk.any(qlo, qhi, bb * kBlk, min(bb * kBlk + kBlk, Nk) - 1)) ++bb;
+    return bb;
+  };
 
   Stage<D> st;
-  st.load(ks, 0, Nk, tid);
+  int b = next_blk(0);
+  st.load(ks, b * kBlk, Nk, tid);
   st.store(kbuf(0), tid);
-  st.load(vs, 0, Nk, tid);
+  st.load(vs, b * kBlk, Nk, tid);
   st.store(kbuf(0) + BB, tid);
   __syncthreads();
-  for (int b = 0; b < nblk; ++b) {
-    const int cur = b & 1;
-    const bool nx = b + 1 < nblk;
+  int cur = 0;
+  while (b < nblk) {
+    const int nb = next_blk(b + 1);
+    const bool nx = nb < nblk;
     const int j0 = b * kBlk;
-    if (nx) st.load(ks, j0 + kBlk, Nk, tid);
+    if (nx) st.load(ks, nb * kBlk, Nk, tid);
     // wave-uniform: does any of this wave's keys reach one of its queries?
-    const bool live = !CAUSAL || j0 + kOwn * par <= qw0 + kOwn - 1;
+    bool live;
+    if constexpr (MASKED)
+      live = mk.any(qw0, min(qw0 + kOwn, Nq) - 1, j0 + kOwn * par,
+                    min(j0 + kOwn * (par + 2) + kOwn, Nk) - 1);
+    else
+      live = !CAUSAL || j0 + kOwn * par <= qw0 + kOwn - 1;
     const lds_char *kb = kbuf(cur);
     const lds_char *vb = kb + BB;
     f32x16 s[2], dp[2];
@@ -397,7 +437,7 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dq(
     }
     if (nx) {
       st.store(kbuf(cur ^ 1), tid);
-      st.load(vs, j0 + kBlk, Nk, tid);
+      st.load(vs, nb * kBlk, Nk, tid);
     }
     if (live) {
 #pragma unroll
@@ -408,7 +448,11 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dq(
         for (int r = 0; r < 16; ++r) {
           const int j = j0 + r0 + 8 * (r >> 2) + 4 * g + (r & 3);
           float pr = exp2f(fmaf(s[hf][r], c, -l2));
-          if (j >= Nk || (CAUSAL && j > myq)) pr = 0.f;
+          if constexpr (MASKED) {
+            if (j >= Nk || !mk.visible(myq, j)) pr = 0.f;
+          } else if (j >= Nk || (CAUSAL && j > myq)) {
+            pr = 0.f;
+          }
           dsv[r] = pr * (dp[hf][r] - dd);
         }
 #pragma unroll
@@ -422,6 +466,8 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dq(
     }
     if (nx) st.store(kbuf(cur ^ 1) + BB, tid);
     __syncthreads();
+    cur ^= 1;
+    b = nb;
   }
 
   pair_sum<NC>(dqa, smem, grp, par, lane);
@@ -446,9 +492,10 @@ struct BwdArgs {
   // variable length only (cu_q == nullptr otherwise)
   const int *cu_q = nullptr, *cu_k = nullptr;
   int S = 1, maxq = 0, maxk = 0;
+  Mask mk = {0, 1, 0};  // local-window + global-token mask (MASKED launches)
 };
 
-template <typename T, typename OT, int D, bool CAUSAL>
+template <typename T, typename OT, int D, bool CAUSAL, bool MASKED = false>
 hipError_t launch_bwd(const BwdArgs &a) {
   const float c = a.scale * kLog2e;
   const int64_t rows = (int64_t)a.BH * a.Nq;
@@ -464,19 +511,28 @@ hipError_t launch_bwd(const BwdArgs &a) {
   const int nqt = ((vl ? a.maxq : a.Nq) + kTile - 1) / kTile;
   const int slices = vl ? a.BH * a.S : a.BH;
   if (nkt > 0) {
-    hipLaunchKernelGGL((fa_bwd_dkdv<T, OT, D, CAUSAL>), dim3((unsigned)(slices * nkt)),
-                       dim3(kThreads), 0, a.stream, (const T *)a.q, (const T *)a.k,
-                       (const T *)a.v, (const T *)a.dout, a.lse, (const float *)a.dl,
-                       (OT *)a.dk, (OT *)a.dv, a.Nq, a.Nk, a.BH, c, a.scale, a.cu_q, a.cu_k,
-                       a.S);
+    hipLaunchKernelGGL((fa_bwd_dkdv<T, OT, D, CAUSAL, MASKED>),
+                       dim3((unsigned)(slices * nkt)), dim3(kThreads), 0, a.stream,
+                       (const T *)a.q, (const T *)a.k, (const T *)a.v, (const T *)a.dout,
+                       a.lse, (const float *)a.dl, (OT *)a.dk, (OT *)a.dv, a.Nq, a.Nk, a.BH, c,
+                       a.scale, a.cu_q, a.cu_k, a.S, a.mk);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((fa_bwd_dq<T, OT, D, CAUSAL>), dim3((unsigned)(slices * nqt)),
+  hipLaunchKernelGGL((fa_bwd_dq<T, OT, D, CAUSAL, MASKED>), dim3((unsigned)(slices * nqt)),
                      dim3(kThreads), 0, a.stream, (const T *)a.q, (const T *)a.k,
                      (const T *)a.v, (const T *)a.dout, a.lse, (const float *)a.dl,
-                     (OT *)a.dq, a.Nq, a.Nk, a.BH, nqt, c, a.scale, a.cu_q, a.cu_k, a.S);
+                     (OT *)a.dq, a.Nq, a.Nk, a.BH, nqt, c, a.scale, a.cu_q, a.cu_k, a.S, a.mk);
   return hipGetLastError();
+}
+
+template <typename T, typename OT>
+hipError_t dispatch_bwd_masked(const BwdArgs &a, int D) {
+  switch (D) {
+    case 32: return launch_bwd<T, OT, 32, false, true>(a);
+    case 64: return launch_bwd<T, OT, 64, false, true>(a);
+    default: return launch_bwd<T, OT, 128, false, true>(a);
+  }
 }
 
 template <typename T, typename OT>
@@ -523,10 +579,11 @@ int fa_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t 
   return FA_OK;
 }
 
-int fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
-           const void *dout, void *dq, void *dk, void *dv, int64_t B, int64_t H, int64_t Nq,
-           int64_t Nk, int64_t D, float scale, int causal, int dtype, void *workspace,
-           size_t workspace_bytes, void *stream) {
+static int bwd_dense(const void *q, const void *k, const void *v, const void *o,
+                     const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                     int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, float scale,
+                     int causal, int dtype, void *workspace, size_t workspace_bytes,
+                     void *stream, const Mask *mk) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULLPTR;
   int st = check_shape(B, H, Nq, Nk, D, dtype);
   if (st != FA_OK) return st;
@@ -571,14 +628,48 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const flo
   a.stream = (hipStream_t)stream;
   const bool cz = causal != 0;
   hipError_t e;
-  switch (dtype) {
-    case FA_BF16: e = dispatch_bwd<__bf16, __bf16>(a, (int)D, cz); break;
-    case FA_BF16_OF32: e = dispatch_bwd<__bf16, float>(a, (int)D, cz); break;
-    case FA_F16: e = dispatch_bwd<_Float16, _Float16>(a, (int)D, cz); break;
-    default: e = dispatch_bwd<_Float16, float>(a, (int)D, cz); break;
+  if (mk) {
+    a.mk = *mk;
+    switch (dtype) {
+      case FA_BF16: e = dispatch_bwd_masked<__bf16, __bf16>(a, (int)D); break;
+      case FA_BF16_OF32: e = dispatch_bwd_masked<__bf16, float>(a, (int)D); break;
+      case FA_F16: e = dispatch_bwd_masked<_Float16, _Float16>(a, (int)D); break;
+      default: e = dispatch_bwd_masked<_Float16, float>(a, (int)D); break;
+    }
+  } else {
+    switch (dtype) {
+      case FA_BF16: e = dispatch_bwd<__bf16, __bf16>(a, (int)D, cz); break;
+      case FA_BF16_OF32: e = dispatch_bwd<__bf16, float>(a, (int)D, cz); break;
+      case FA_F16: e = dispatch_bwd<_Float16, _Float16>(a, (int)D, cz); break;
+      default: e = dispatch_bwd<_Float16, float>(a, (int)D, cz); break;
+    }
   }
   if (e != hipSuccess) return fa_internal_hip_fail(e);
   return FA_OK;
+}
+
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+           const void *dout, void *dq, void *dk, void *dv, int64_t B, int64_t H, int64_t Nq,
+           int64_t Nk, int64_t D, float scale, int causal, int dtype, void *workspace,
+           size_t workspace_bytes, void *stream) {
+  return bwd_dense(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, D, scale, causal, dtype,
+                   workspace, workspace_bytes, stream, nullptr);
+}
+
+int fa_bwd_masked(const void *q, const void *k, const void *v, const void *o,
+                  const float *lse, const void *dout, void *dq, void *dk, void *dv, int64_t B,
+                  int64_t H, int64_t Nq, int64_t Nk, int64_t D, float scale, int causal,
+                  int64_t window, int64_t nglobal, int dtype, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULLPTR;
+  if (window < 1 || nglobal < 0) return FA_ERR_SHAPE;
+  const int64_t lim = (int64_t)1 << 31;
+  Mask mk;
+  mk.causal = causal != 0;
+  mk.window = (int)(window < lim ? window : lim - 1);
+  mk.nglobal = (int)(nglobal < lim ? nglobal : lim - 1);
+  return bwd_dense(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, D, scale, causal, dtype,
+                   workspace, workspace_bytes, stream, &mk);
 }
 
 int fa_bwd_varlen(const void *q, const void *k, const void *v, const void *o,

@@ -42,25 +42,6 @@ int fa_internal_hip_fail(hipError_t e);
 
 namespace {
 
-struct Mask {
-  int causal, window, nglobal;
-
-  __device__ __forceinline__ bool visible(int i, int j) const {
-    const int d = i - j;
-    const bool local = causal ? (d >= 0 && d < window) : (d > -window && d < window);
-    const bool global = (j < nglobal || i < nglobal) && (!causal || j <= i);
-    return local || global;
-  }
-  // Is some pair of queries [ilo, ihi] x keys [jlo, jhi] visible?
-  __device__ __forceinline__ bool any(int ilo, int ihi, int jlo, int jhi) const {
-    const bool gk = jlo < nglobal && (!causal || jlo <= ihi);
-    const bool gq = ilo < nglobal && (!causal || jlo <= min(ihi, nglobal - 1));
-    const bool local = causal ? (ihi - jlo >= 0 && ilo - jhi <= window - 1)
-                              : (ihi - jlo >= -(window - 1) && ilo - jhi <= window - 1);
-    return gk || gq || local;
-  }
-};
-
 constexpr int kQTile = kOwn * kWaves;  // 128 queries per workgroup
 
 template <typename T, typename OT, int D>

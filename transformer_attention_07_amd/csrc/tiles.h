@@ -191,6 +191,29 @@ __device__ __forceinline__ void store_t(OT *slice, int row, int d0, int g, const
   }
 }
 
+// Local-window + global-token visibility (the reading of the pages' sparse
+// attention used by fa_fwd_masked and fa_bwd_masked): key j is visible to
+// query i iff (causal ? 0 <= i - j < window : |i - j| < window) or
+// (j < nglobal || i < nglobal) && (!causal || j <= i).
+struct Mask {
+  int causal, window, nglobal;
+
+  __device__ __forceinline__ bool visible(int i, int j) const {
+    const int d = i - j;
+    const bool local = causal ? (d >= 0 && d < window) : (d > -window && d < window);
+    const bool global = (j < nglobal || i < nglobal) && (!causal || j <= i);
+    return local || global;
+  }
+  // Is some pair of queries [ilo, ihi] x keys [jlo, jhi] visible?
+  __device__ __forceinline__ bool any(int ilo, int ihi, int jlo, int jhi) const {
+    const bool gk = jlo < nglobal && (!causal || jlo <= ihi);
+    const bool gq = ilo < nglobal && (!causal || jlo <= min(ihi, nglobal - 1));
+    const bool local = causal ? (ihi - jlo >= 0 && ilo - jhi <= window - 1)
+                              : (ihi - jlo >= -(window - 1) && ilo - jhi <= window - 1);
+    return gk || gq || local;
+  }
+};
+
 }  // namespace
 
 #endif  // FA_TILES_H
