@@ -230,8 +230,8 @@ def main() -> int:
         import numpy as np
         from workloads import gen_qkv
 
-        if bwd or args.varlen:
-            raise SystemExit("--masked times the forward pass alone")
+        if args.varlen:
+            raise SystemExit("--masked and --varlen are separate modes")
         W, G = (int(x) for x in args.masked.split(","))
         MB, MH, MN, MD = 1, 8, 32768, 128
         q, k, v = (t.to(dev) for t in gen_qkv(MB, MH, MN, MN, MD, seed=2601, dtype="bf16"))
@@ -250,6 +250,21 @@ def main() -> int:
         call = lib.fa_fwd_masked
         args.entry = "fa_fwd_masked"
         ws_bytes = 0
+        if bwd:
+            from workloads import gen_grad_out
+
+            st = call(*argv)  # the masked forward whose O and L the backward consumes
+            if st != 0:
+                raise RuntimeError(f"forward failed: {fa.fa_status_str(st)}")
+            g = gen_grad_out(MB, MH, MN, MD, seed=2602, dtype="bf16").to(dev)
+            dq, dk, dv = (torch.empty(x.shape, dtype=out_dt, device=dev) for x in (q, k, v))
+            ws_bytes = MB * MH * MN * 4
+            bws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+            argv = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                    g.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), MB, MH, MN, MN,
+                    MD, scale, 1, W, G, code, bws.data_ptr(), ws_bytes, sp)
+            call = lib.fa_bwd_masked
+            args.entry = "fa_bwd_masked"
     if args.varlen:
         from workloads import varlen_lengths
 
@@ -265,7 +280,9 @@ def main() -> int:
         call = lib.fa_fwd_varlen
         args.entry = "fa_fwd_varlen"
         ws_bytes = 0
-    if bwd and lens is not None:
+    if masked is not None:
+        pass
+    elif bwd and lens is not None:
         from workloads import gen_grad_out
 
         st = call(*argv)  # the forward pass whose O and L the backward consumes
@@ -345,7 +362,7 @@ def main() -> int:
         flops = sum(4.0 * n * n * w.D / (2 if w.causal else 1) for n in lens)
         flops *= 2.5 if bwd else 1.0
     if masked is not None:
-        flops = 4.0 * masked["shape"][3] * masked["visible_pairs"]
+        flops = 4.0 * masked["shape"][3] * masked["visible_pairs"] * (2.5 if bwd else 1.0)
     value = flops / (ms_per_step * 1e-3) / 1e12
     dkey = "f32" if in_dt == torch.float32 else ("bf16" if in_dt == torch.bfloat16 else "f16")
     peak = PEAK_TFLOPS[dkey]
