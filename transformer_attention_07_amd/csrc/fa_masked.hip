@@ -19,7 +19,8 @@
 // gfx950 mapping: one workgroup of four waves per (batch*head, 128
 // queries); wave w owns 32 queries, one per lane column, with its Q
 // fragments in VGPRs as MFMA B operands.  K and V stream through LDS in
-// 128-key blocks (register staged, double buffered); per 32-key quarter
+// 64-key blocks (register staged, double buffered; two workgroups per
+// compute unit); per 32-key half
 // S^T = K Q^T (v_mfma_f32_32x32x16), the online softmax runs per lane (the
 // other half of a query's keys sits in lane l ^ 32), and P^T, rounded to
 // the input type, is directly the B operand of O^T += V^T P^T with V^T read
@@ -43,9 +44,14 @@ int fa_internal_hip_fail(hipError_t e);
 namespace {
 
 constexpr int kQTile = kOwn * kWaves;  // 128 queries per workgroup
+// Keys per LDS block: 64 (two 32-key quarters) keep a workgroup's double-
+// buffered K and V at 78 KB at D = 128, so two workgroups share a compute
+// unit (two waves per SIMD) and one's loads and softmax hide behind the
+// other's MFMAs.
+constexpr int kMBlk = 64;
 
 template <typename T, typename OT, int D>
-__global__ __launch_bounds__(kThreads) void fa_fwd_masked(
+__global__ __launch_bounds__(kThreads, 2) void fa_fwd_masked(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     OT *__restrict__ o, float *__restrict__ lse, int Nq, int Nk, int BH, int nqt, float c,
     Mask mk) {
@@ -53,7 +59,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_masked(
   typedef typename M::frag frag;
   constexpr int KF = D / 16;
   constexpr int NC = D / 32;
-  constexpr int BB = Blk<D>::BYTES;
+  constexpr int BB = kMBlk * Blk<D>::STRIDE;
   __shared__ __attribute__((aligned(16))) char smem_raw[4 * BB];  // [buffer][K, V]
   lds_char *smem = (lds_char *)smem_raw;
 
@@ -79,9 +85,9 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_masked(
   float m = -INFINITY;  // running maximum (base 2), equal in both half-waves
   float l = 0.f;        // this half-wave's share of the running sum
 
-  const int nblk = (Nk + kBlk - 1) / kBlk;
+  const int nblk = (Nk + kMBlk - 1) / kMBlk;
   auto live_block = [&](int b) {
-    return mk.any(q0, qlast, b * kBlk, min(b * kBlk + kBlk, Nk) - 1);
+    return mk.any(q0, qlast, b * kMBlk, min(b * kMBlk + kMBlk, Nk) - 1);
   };
   auto next_live = [&](int b) {
     while (b < nblk && !live_block(b)) ++b;
@@ -89,11 +95,11 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_masked(
   };
   auto kbuf = [&](int buf) { return smem + buf * 2 * BB; };
 
-  Stage<D> sk, sv;
+  Stage<D, kMBlk> sk, sv;
   int b = next_live(0);
   if (b < nblk) {
-    sk.load(ks, b * kBlk, Nk, tid);
-    sv.load(vs, b * kBlk, Nk, tid);
+    sk.load(ks, b * kMBlk, Nk, tid);
+    sv.load(vs, b * kMBlk, Nk, tid);
     sk.store(kbuf(0), tid);
     sv.store(kbuf(0) + BB, tid);
   }
@@ -102,15 +108,15 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_masked(
   while (b < nblk) {
     const int nb = next_live(b + 1);
     const bool nx = nb < nblk;
-    const int j0 = b * kBlk;
+    const int j0 = b * kMBlk;
     if (nx) {
-      sk.load(ks, nb * kBlk, Nk, tid);
-      sv.load(vs, nb * kBlk, Nk, tid);
+      sk.load(ks, nb * kMBlk, Nk, tid);
+      sv.load(vs, nb * kMBlk, Nk, tid);
     }
     const lds_char *kb = kbuf(cur);
     const lds_char *vb = kb + BB;
 #pragma unroll 1
-    for (int qq = 0; qq < kBlk / kOwn; ++qq) {
+    for (int qq = 0; qq < kMBlk / kOwn; ++qq) {
       const int jq = j0 + qq * kOwn;
       // wave-uniform: a visible pair among this wave's queries and the quarter's keys?
       if (jq >= Nk || wlast < qw0 || !mk.any(qw0, wlast, jq, min(jq + kOwn, Nk) - 1)) continue;

@@ -86,13 +86,13 @@ template <int D> struct Blk {
 };
 
 // Register staging of one block: global -> VGPRs -> LDS, 16 bytes a piece.
-template <int D> struct Stage {
+template <int D, int ROWS = kBlk> struct Stage {
   static constexpr int CPR = D / 8;  // 16-byte pieces per row
-  static constexpr int PIECES = kBlk * CPR;
+  static constexpr int PIECES = ROWS * CPR;
   static constexpr int N = (PIECES + kThreads - 1) / kThreads;
   u32x4 r[N];
 
-  // rows row0 .. row0+kBlk-1 of a slice with nrows rows; missing rows are 0
+  // rows row0 .. row0+ROWS-1 of a slice with nrows rows; missing rows are 0
   __device__ __forceinline__ void load(const void *slice, int row0, int nrows, int tid) {
 #pragma unroll
     for (int n = 0; n < N; ++n) {
