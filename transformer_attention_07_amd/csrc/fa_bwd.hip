@@ -60,6 +60,8 @@ int fa_internal_hip_fail(hipError_t e);
 
 namespace {
 
+constexpr int kQBlk = 64;  // keys per LDS block of the dQ kernel
+
 // ---------------------------------------------------------------------------
 // Dl_i = <dO_i, O_i>, fp32, one row per D/8 lanes.
 template <typename T, int D>
@@ -342,10 +344,12 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv(
 
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per (batch*head, kTile queries).  Wave w owns queries
-// qw0 + 32*(w & 1) .. +31 and, of every 128-key block, the 32-key quarters
-// par and par + 2 (par = w >> 1); the two parities are summed at the end.
+// qw0 + 32*(w & 1) .. +31 and, of every 64-key block, the 32-key half par
+// (par = w >> 1); the two parities are summed at the end.  The 64-key
+// blocks keep the LDS at 78 KB and the registers under 256 at D = 128, so
+// two workgroups share a compute unit (two waves per SIMD).
 template <typename T, typename OT, int D, bool CAUSAL, bool MASKED>
-__global__ __launch_bounds__(kThreads) void fa_bwd_dq(
+__global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dl,
     OT *__restrict__ dq, int Nq, int Nk, int BH, int nqt, float c, float scale,
@@ -354,7 +358,8 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dq(
   typedef typename M::frag frag;
   constexpr int KF = D / 16;
   constexpr int NC = D / 32;
-  constexpr int BB = Blk<D>::BYTES;
+  constexpr int BB = kQBlk * Blk<D>::STRIDE;
+  constexpr int NH = kQBlk / (2 * kOwn);  // quarters per wave and block
   // [buffer][K, V] blocks
   __shared__ __attribute__((aligned(16))) char smem_raw[4 * BB];
   lds_char *smem = (lds_char *)smem_raw;
@@ -389,42 +394,42 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dq(
 
   // keys past the tile's last query are hidden from all its rows
   const int kend = CAUSAL ? min(Nk, qt * kTile + kTile) : Nk;
-  const int nblk = (kend + kBlk - 1) / kBlk;
+  const int nblk = (kend + kQBlk - 1) / kQBlk;
   auto kbuf = [&](int buf) { return smem + buf * 2 * BB; };
   // next key block (from bb) holding a key that some query of the tile sees
   const int qlo = qt * kTile, qhi = min(qlo + kTile, Nq) - 1;
   auto next_blk = [&](int bb) {
     if constexpr (MASKED)
-      while (bb < nblk && !mk.any(qlo, qhi, bb * kBlk, min(bb * kBlk + kBlk, Nk) - 1)) ++bb;
+      while (bb < nblk && !mk.any(qlo, qhi, bb * kQBlk, min(bb * kQBlk + kQBlk, Nk) - 1)) ++bb;
     return bb;
   };
 
-  Stage<D> st;
+  Stage<D, kQBlk> st;
   int b = next_blk(0);
-  st.load(ks, b * kBlk, Nk, tid);
+  st.load(ks, b * kQBlk, Nk, tid);
   st.store(kbuf(0), tid);
-  st.load(vs, b * kBlk, Nk, tid);
+  st.load(vs, b * kQBlk, Nk, tid);
   st.store(kbuf(0) + BB, tid);
   __syncthreads();
   int cur = 0;
   while (b < nblk) {
     const int nb = next_blk(b + 1);
     const bool nx = nb < nblk;
-    const int j0 = b * kBlk;
-    if (nx) st.load(ks, nb * kBlk, Nk, tid);
+    const int j0 = b * kQBlk;
+    if (nx) st.load(ks, nb * kQBlk, Nk, tid);
     // wave-uniform: does any of this wave's keys reach one of its queries?
     bool live;
     if constexpr (MASKED)
       live = mk.any(qw0, min(qw0 + kOwn, Nq) - 1, j0 + kOwn * par,
-                    min(j0 + kOwn * (par + 2) + kOwn, Nk) - 1);
+                    min(j0 + kOwn * (par + 2 * (NH - 1)) + kOwn, Nk) - 1);
     else
       live = !CAUSAL || j0 + kOwn * par <= qw0 + kOwn - 1;
     const lds_char *kb = kbuf(cur);
     const lds_char *vb = kb + BB;
-    f32x16 s[2], dp[2];
+    f32x16 s[NH], dp[NH];
     if (live) {
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
+      for (int hf = 0; hf < NH; ++hf) {
         const int r0 = kOwn * (par + 2 * hf);
         s[hf] = f32x16{};
         dp[hf] = f32x16{};
@@ -437,11 +442,11 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dq(
     }
     if (nx) {
       st.store(kbuf(cur ^ 1), tid);
-      st.load(vs, nb * kBlk, Nk, tid);
+      st.load(vs, nb * kQBlk, Nk, tid);
     }
     if (live) {
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
+      for (int hf = 0; hf < NH; ++hf) {
         const int r0 = kOwn * (par + 2 * hf);
         float dsv[16];
 #pragma unroll
