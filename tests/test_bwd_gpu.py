@@ -181,3 +181,73 @@ def test_bwd_rejects_fp32_and_d16():
     with pytest.raises(fa.FaError) as e:
         fa.bwd(x, x, x, x, lse, x)  # fp32 inputs: not supported by the backward pass
     assert e.value.status == fa.FA_ERR_DTYPE
+
+
+@pytest.mark.parametrize("entry", ["bwd", "bwd_masked", "fwd_varlen", "fwd_masked"])
+def test_graph_capture_replays_match_eager(entry):
+    """fa_bwd, fa_bwd_masked, fa_fwd_varlen and fa_fwd_masked are plain
+    launches on the caller's stream (no allocation, no memset), so a HIP
+    graph captured around one call replays it: every replay, with eager work
+    between replays and stale outputs and workspace, gives the eager result
+    bit for bit."""
+    B, H, N, D = 2, 2, 333, 64
+    q, k, v, g = inputs(B, H, N, N, D, seed=903)
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, g))
+    scale = 0.125
+    o, lse = fa.fwd(qd, kd, vd, causal=True, scale=scale)
+    outs = [torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)]
+    ws = torch.empty(B * H * N * 4, dtype=torch.uint8, device=DEV)
+    cu = torch.tensor([0, 100, 333, 2 * N], dtype=torch.int32, device=DEV)
+    stream = lambda: torch.cuda.current_stream().cuda_stream  # noqa: E731
+    if entry in ("bwd", "bwd_masked"):
+        if entry == "bwd_masked":
+            o, lse = fa.fwd_masked(qd, kd, vd, 40, 5, causal=True, scale=scale)
+
+        def call():
+            base = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(),
+                    lse.data_ptr(), gd.data_ptr(), outs[0].data_ptr(), outs[1].data_ptr(),
+                    outs[2].data_ptr(), B, H, N, N, D, scale, 1)
+            if entry == "bwd":
+                st = fa.fa_bwd(*base, fa.FA_BF16, ws.data_ptr(), ws.numel(), stream())
+            else:
+                st = fa.fa_bwd_masked(*base, 40, 5, fa.FA_BF16, ws.data_ptr(), ws.numel(),
+                                      stream())
+            assert st == fa.FA_OK, fa.fa_status_str(st)
+    else:
+        outs = [torch.empty_like(qd), torch.empty(qd.shape[:-1], dtype=torch.float32,
+                                                  device=DEV)]
+
+        def call():
+            if entry == "fwd_varlen":
+                # q viewed as [2, 666, D]: two heads of 666 packed tokens, three sequences
+                st = fa.fa_fwd_varlen(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(),
+                                      outs[0].data_ptr(), outs[1].data_ptr(), cu.data_ptr(),
+                                      cu.data_ptr(), 3, B * H // 2, 2 * N, 2 * N, 333, D, scale,
+                                      1, fa.FA_BF16, stream())
+            else:
+                st = fa.fa_fwd_masked(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(),
+                                      outs[0].data_ptr(), outs[1].data_ptr(), B, H, N, N, D,
+                                      scale, 1, 40, 5, fa.FA_BF16, stream())
+            assert st == fa.FA_OK, fa.fa_status_str(st)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    want = [x.clone() for x in outs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for i in range(3):
+        for x in outs:
+            x.fill_(float("nan"))
+        ws.fill_(i)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for x, y in zip(outs, want):
+            assert torch.equal(x, y), f"replay {i} differs from the eager call"
+        call()
+        torch.cuda.synchronize()
