@@ -207,7 +207,7 @@ int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *l
  * nglobal = 0 this is fa_fwd's operation.
  *
  *   q, k, v, o, lse, B, H, Nq, Nk, scale, causal   as fa_fwd
- *   D          32, 64 or 128
+ *   D          16, 32, 64 or 128
  *   window     >= 1 (window 1 leaves the diagonal)
  *   nglobal    >= 0: the first nglobal queries and keys are global tokens
  *   dtype      FA_BF16, FA_BF16_OF32, FA_F16 or FA_F16_OF32 (FA_F32:
@@ -253,7 +253,7 @@ int fa_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk,
  *   lse        the forward's L, [B,H,Nq] fp32
  *   dout       upstream gradient of O, [B,H,Nq,D], same 16-bit type
  *   dq         [B,H,Nq,D] (written); dk, dv [B,H,Nk,D] (written)
- *   B .. causal  as fa_fwd; D must be 32, 64 or 128
+ *   B .. causal  as fa_fwd; D must be 16, 32, 64 or 128
  *   dtype      FA_BF16 / FA_F16: every tensor in that type (gradients
  *              rounded once, at the end); FA_BF16_OF32 / FA_F16_OF32: the
  *              same inputs, gradients stored in fp32.  FA_F32 is not

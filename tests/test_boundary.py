@@ -175,7 +175,7 @@ def test_bwd_null_pointers(arg):
 
 @pytest.mark.parametrize("kw,status", [
     ({"B": 0}, "FA_ERR_SHAPE"), ({"Nq": 0}, "FA_ERR_SHAPE"), ({"Nk": -1}, "FA_ERR_SHAPE"),
-    ({"D": 16}, "FA_ERR_HEAD_DIM"), ({"D": 96}, "FA_ERR_HEAD_DIM"),
+    ({"D": 8}, "FA_ERR_HEAD_DIM"), ({"D": 96}, "FA_ERR_HEAD_DIM"),
     ({"dtype": 0}, "FA_ERR_DTYPE"), ({"dtype": 5}, "FA_ERR_DTYPE"),
     ({"scale": math.inf}, "FA_ERR_SCALE"), ({"scale": math.nan}, "FA_ERR_SCALE"),
     ({"dq": DQ + 8}, "FA_ERR_ALIGN"), ({"do": DO + 2}, "FA_ERR_ALIGN"),
@@ -191,7 +191,7 @@ def test_bwd_validation(kw, status):
 def test_bwd_workspace_size():
     st, n = fa.fa_bwd_workspace_size(2, 3, 100, 90, 64, 1, fa.FA_BF16)
     assert (st, n) == (fa.FA_OK, 2 * 3 * 100 * 4)
-    assert fa.fa_bwd_workspace_size(2, 3, 100, 90, 16, 1, fa.FA_BF16)[0] == fa.FA_ERR_HEAD_DIM
+    assert fa.fa_bwd_workspace_size(2, 3, 100, 90, 48, 1, fa.FA_BF16)[0] == fa.FA_ERR_HEAD_DIM
     assert fa.fa_bwd_workspace_size(2, 3, 100, 90, 64, 1, fa.FA_F32)[0] == fa.FA_ERR_DTYPE
 
 
@@ -234,7 +234,7 @@ def call_bwd_varlen(**kw):
 @pytest.mark.parametrize("kw,status", [
     ({"cq": None}, "FA_ERR_NULLPTR"), ({"dv": None}, "FA_ERR_NULLPTR"),
     ({"S": 0}, "FA_ERR_SHAPE"), ({"Tq": 0}, "FA_ERR_SHAPE"), ({"mk": -1}, "FA_ERR_SHAPE"),
-    ({"D": 16}, "FA_ERR_HEAD_DIM"), ({"dtype": fa.FA_F32}, "FA_ERR_DTYPE"),
+    ({"D": 48}, "FA_ERR_HEAD_DIM"), ({"dtype": fa.FA_F32}, "FA_ERR_DTYPE"),
     ({"scale": math.inf}, "FA_ERR_SCALE"), ({"ck": CK + 1}, "FA_ERR_ALIGN"),
     ({"ws_bytes": 2 * 500 * 4 - 4}, "FA_ERR_WORKSPACE"), ({"dq": CQ}, "FA_ERR_OVERLAP"),
 ])
@@ -254,7 +254,7 @@ def call_masked(**kw):
 @pytest.mark.parametrize("kw,status", [
     ({"lse": None}, "FA_ERR_NULLPTR"), ({"Nk": 0}, "FA_ERR_SHAPE"),
     ({"window": 0}, "FA_ERR_SHAPE"), ({"nglobal": -1}, "FA_ERR_SHAPE"),
-    ({"D": 16}, "FA_ERR_HEAD_DIM"), ({"dtype": fa.FA_F32}, "FA_ERR_DTYPE"),
+    ({"D": 48}, "FA_ERR_HEAD_DIM"), ({"dtype": fa.FA_F32}, "FA_ERR_DTYPE"),
     ({"scale": math.inf}, "FA_ERR_SCALE"), ({"v": V + 4}, "FA_ERR_ALIGN"),
     ({"o": K}, "FA_ERR_OVERLAP"),
 ])
@@ -275,6 +275,6 @@ def test_bwd_masked_validation():
     assert call(window=0) == fa.FA_ERR_SHAPE
     assert call(nglobal=-1) == fa.FA_ERR_SHAPE
     assert call(dk=None) == fa.FA_ERR_NULLPTR
-    assert call(D=16) == fa.FA_ERR_HEAD_DIM
+    assert call(D=48) == fa.FA_ERR_HEAD_DIM
     assert call(dq=Q) == fa.FA_ERR_OVERLAP
     assert call(ws=None) == fa.FA_ERR_WORKSPACE

@@ -102,7 +102,7 @@ def inputs(B, H, Nq, Nk, D, seed, dtype=torch.bfloat16, q_mult=1.0, std=1.0):
     return q, k, v, g
 
 
-@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
 def test_bwd_ragged_tiles(D, causal, dtype):
@@ -171,8 +171,8 @@ def test_bwd_deterministic():
         assert np.array_equal(x, y)
 
 
-def test_bwd_rejects_fp32_and_d16():
-    q = torch.zeros(1, 1, 64, 16, device=DEV, dtype=torch.bfloat16)
+def test_bwd_rejects_fp32_and_odd_head_dims():
+    q = torch.zeros(1, 1, 64, 48, device=DEV, dtype=torch.bfloat16)
     lse = torch.zeros(1, 1, 64, device=DEV)
     with pytest.raises(fa.FaError) as e:
         fa.bwd(q, q, q, q, lse, q, causal=True)
@@ -181,6 +181,16 @@ def test_bwd_rejects_fp32_and_d16():
     with pytest.raises(fa.FaError) as e:
         fa.bwd(x, x, x, x, lse, x)  # fp32 inputs: not supported by the backward pass
     assert e.value.status == fa.FA_ERR_DTYPE
+
+
+def test_bwd_d16_sweep_shape_sampled():
+    """B8 N8192 D16 causal bf16 (a head dim of the pages' sweep): sampled rows."""
+    B, N, D = 8, 8192, 16
+    q, k, v, g = inputs(B, 1, N, N, D, seed=40)
+    qrows = sample_rows(B * N, 128, 6010).numpy()
+    krows = sample_rows(B * N, 128, 6011).numpy()
+    compare(q, k, v, g, True, 1.0 / math.sqrt(D), qrows=qrows, krows=krows,
+            what="D16 sampled")
 
 
 @pytest.mark.parametrize("entry", ["bwd", "bwd_masked", "fwd_varlen", "fwd_masked"])

@@ -67,7 +67,7 @@ def compare(B, H, Nq, Nk, D, causal, window, nglobal, seed, dtype="bf16", scale=
     assert (np.abs(x16 - ro) <= 1e-2 + _half_ulp(ro, q.dtype)).all()
 
 
-@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("window,nglobal", [(64, 0), (200, 16), (1, 0), (33, 130),
                                             (5000, 0)])
@@ -155,7 +155,7 @@ def compare_bwd(B, H, Nq, Nk, D, causal, window, nglobal, seed, dtype="bf16"):
         assert torch.equal(g32[n].to(q.dtype).cpu(), g16[n].cpu()), f"{name}: rounding"
 
 
-@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("window,nglobal", [(64, 0), (150, 16), (1, 0), (33, 200)])
 def test_masked_bwd_patterns(D, causal, window, nglobal):

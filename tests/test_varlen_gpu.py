@@ -220,7 +220,7 @@ def compare_bwd(lq, lk, H, D, causal, seed, dtype="bf16"):
                 f"sequence {s}: gradient {n} differs from fa_bwd on the sequence alone"
 
 
-@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_varlen_bwd_mixed_lengths(D, causal):
     compare_bwd(MIXED, MIXED, 2, D, causal, seed=1900 + D)

@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv(
   using M = Mma<T>;
   typedef typename M::frag frag;
   constexpr int KF = D / 16;  // MFMA steps along D
-  constexpr int NC = D / 32;  // 32-row chunks of dK^T / dV^T
+  constexpr int NC = chunks<D>();  // 32-row chunks of dK^T / dV^T
   constexpr int BB = Blk<D>::BYTES;
   // [buffer][Q, dO] blocks, then [buffer] L*log2(e) and Dl of the block's rows
   __shared__ __attribute__((aligned(16))) char smem_raw[4 * BB + 4 * kBlk * 4];
@@ -237,6 +237,8 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv(
     return bb;
   };
 
+  clear_padding<D>(smem, 4 * BB, tid);
+  if constexpr (D < 32) __syncthreads();
   int b = next_blk(0);
   if (b < nblk) {
     st.load(qs, qstart + b * kBlk, Nq, tid);
@@ -357,7 +359,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq(
   using M = Mma<T>;
   typedef typename M::frag frag;
   constexpr int KF = D / 16;
-  constexpr int NC = D / 32;
+  constexpr int NC = chunks<D>();
   constexpr int BB = kQBlk * Blk<D>::STRIDE;
   constexpr int NH = kQBlk / (2 * kOwn);  // quarters per wave and block
   // [buffer][K, V] blocks
@@ -405,6 +407,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq(
   };
 
   Stage<D, kQBlk> st;
+  clear_padding<D>(smem, 4 * BB, tid);
+  if constexpr (D < 32) __syncthreads();
   int b = next_blk(0);
   st.load(ks, b * kQBlk, Nk, tid);
   st.store(kbuf(0), tid);
@@ -534,6 +538,7 @@ hipError_t launch_bwd(const BwdArgs &a) {
 template <typename T, typename OT>
 hipError_t dispatch_bwd_masked(const BwdArgs &a, int D) {
   switch (D) {
+    case 16: return launch_bwd<T, OT, 16, false, true>(a);
     case 32: return launch_bwd<T, OT, 32, false, true>(a);
     case 64: return launch_bwd<T, OT, 64, false, true>(a);
     default: return launch_bwd<T, OT, 128, false, true>(a);
@@ -543,6 +548,7 @@ hipError_t dispatch_bwd_masked(const BwdArgs &a, int D) {
 template <typename T, typename OT>
 hipError_t dispatch_bwd(const BwdArgs &a, int D, bool causal) {
   switch (D) {
+    case 16: return causal ? launch_bwd<T, OT, 16, true>(a) : launch_bwd<T, OT, 16, false>(a);
     case 32: return causal ? launch_bwd<T, OT, 32, true>(a) : launch_bwd<T, OT, 32, false>(a);
     case 64: return causal ? launch_bwd<T, OT, 64, true>(a) : launch_bwd<T, OT, 64, false>(a);
     default:
@@ -557,7 +563,7 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 
 int check_shape(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int dtype) {
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
-  if (D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  if (D != 16 && D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
   if (dtype != FA_BF16 && dtype != FA_BF16_OF32 && dtype != FA_F16 && dtype != FA_F16_OF32)
     return FA_ERR_DTYPE;
   const int64_t lim = (int64_t)1 << 31;

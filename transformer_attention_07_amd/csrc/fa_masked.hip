@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_masked(
   using M = Mma<T>;
   typedef typename M::frag frag;
   constexpr int KF = D / 16;
-  constexpr int NC = D / 32;
+  constexpr int NC = chunks<D>();
   constexpr int BB = kMBlk * Blk<D>::STRIDE;
   __shared__ __attribute__((aligned(16))) char smem_raw[4 * BB];  // [buffer][K, V]
   lds_char *smem = (lds_char *)smem_raw;
@@ -96,6 +96,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_masked(
   auto kbuf = [&](int buf) { return smem + buf * 2 * BB; };
 
   Stage<D, kMBlk> sk, sv;
+  clear_padding<D>(smem, 4 * BB, tid);
+  if constexpr (D < 32) __syncthreads();
   int b = next_live(0);
   if (b < nblk) {
     sk.load(ks, b * kMBlk, Nk, tid);
@@ -194,6 +196,7 @@ hipError_t dispatch_masked(const void *q, const void *k, const void *v, void *o,
                            int Nq, int Nk, int BH, int D, float c, Mask mk,
                            hipStream_t stream) {
   switch (D) {
+    case 16: return launch_masked<T, OT, 16>(q, k, v, o, lse, Nq, Nk, BH, c, mk, stream);
     case 32: return launch_masked<T, OT, 32>(q, k, v, o, lse, Nq, Nk, BH, c, mk, stream);
     case 64: return launch_masked<T, OT, 64>(q, k, v, o, lse, Nq, Nk, BH, c, mk, stream);
     default: return launch_masked<T, OT, 128>(q, k, v, o, lse, Nq, Nk, BH, c, mk, stream);
@@ -214,7 +217,7 @@ int fa_fwd_masked(const void *q, const void *k, const void *v, void *o, float *l
                   int causal, int64_t window, int64_t nglobal, int dtype, void *stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULLPTR;
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || window < 1 || nglobal < 0) return FA_ERR_SHAPE;
-  if (D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  if (D != 16 && D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
   if (dtype != FA_BF16 && dtype != FA_BF16_OF32 && dtype != FA_F16 && dtype != FA_F16_OF32)
     return FA_ERR_DTYPE;
   if (!isfinite(scale)) return FA_ERR_SCALE;

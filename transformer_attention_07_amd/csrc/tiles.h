@@ -81,7 +81,7 @@ template <> struct Mma<_Float16> {
 // pass start on distinct 16-byte bank groups, and the four rows of one
 // ds_read_b64_tr_b16 group land on disjoint 32-byte ranges.
 template <int D> struct Blk {
-  static constexpr int STRIDE = D == 128 ? 304 : D == 64 ? 208 : 112;
+  static constexpr int STRIDE = D == 128 ? 304 : D == 64 ? 208 : 112;  // D <= 32: 112
   static constexpr int BYTES = kBlk * STRIDE;
 };
 
@@ -183,11 +183,27 @@ template <> __device__ __forceinline__ void store4<_Float16>(_Float16 *dst, f32x
 template <typename OT, int D>
 __device__ __forceinline__ void store_t(OT *slice, int row, int d0, int g, const f32x16 &acc,
                                         float mul) {
+  // D = 16: rows 16..31 of the single chunk came from zero padding; skipped
 #pragma unroll
-  for (int r4 = 0; r4 < 4; ++r4) {
+  for (int r4 = 0; r4 < (D < 32 ? 2 : 4); ++r4) {
     const f32x4 x = {acc[4 * r4] * mul, acc[4 * r4 + 1] * mul, acc[4 * r4 + 2] * mul,
                      acc[4 * r4 + 3] * mul};
     store4<OT>(slice + (size_t)row * D + d0 + 8 * r4 + 4 * g, x);
+  }
+}
+
+// 32-row output chunks along the head dimension (one, half padding, at D = 16)
+template <int D> constexpr int chunks() { return D < 32 ? 1 : D / 32; }
+
+// At D = 16 the LDS rows are 32 columns wide (the transposed reads of the
+// 32-row output MFMAs cover 32 columns) and columns 16..31 must read as zero;
+// the blocks never write them, so they are cleared once, before any block
+// is stored (the caller then synchronises).
+template <int D>
+__device__ __forceinline__ void clear_padding(lds_char *smem, int bytes, int tid) {
+  if constexpr (D < 32) {
+    for (int o = tid * 16; o < bytes; o += kThreads * 16)
+      *(lds_u32x4 *)(smem + o) = u32x4{0u, 0u, 0u, 0u};
   }
 }
 
