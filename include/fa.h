@@ -1,7 +1,8 @@
 /*
  * fa.h -- C ABI of the MI355X (gfx950) FlashAttention-2 library: the
  * forward pass (fa_fwd, fa_fwd_ws; fa_fwd_varlen for variable-length
- * batches, fa_fwd_masked for local-window + global-token masks) and its
+ * batches, fa_fwd_masked for local-window + global-token masks, fa_fwd_fp8
+ * for FP8 inputs) and its
  * backward pass (fa_bwd, fa_bwd_varlen, fa_bwd_masked).
  *
  * The operation (page "FlashAttention-2实现与优化：高效注意力机制详解",
@@ -222,6 +223,24 @@ int fa_fwd_masked(const void *q, const void *k, const void *v, void *o, float *l
                   int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
                   float scale, int causal, int64_t window, int64_t nglobal,
                   int dtype, void *stream);
+
+/*
+ * fa_fwd_fp8 -- the forward pass with FP8 inputs (page "FlashAttention技术
+ * 演进全景图" §5.3 names FP8 support; the pages give no rules, so this
+ * library reads it as): q, k, v hold OCP e4m3 values (one byte each,
+ * [B,H,N,D] contiguous) and the real inputs are those values times the
+ * per-tensor factors descale_q, descale_k, descale_v.  The result is fa_fwd's
+ * O and lse for the real inputs; O is bf16 (out_f32 = 0) or fp32 (out_f32 !=
+ * 0).  The score products run on FP8 MFMAs with fp32 sums (exact products);
+ * P.V runs in bf16 (V's e4m3 values widen exactly; P is rounded to bf16 as
+ * on the 16-bit path).  D must be 64 or 128.  Other arguments, ownership and
+ * status codes as fa_fwd (FA_ERR_SCALE also when a factor, or their product
+ * with scale, is not finite).
+ */
+int fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
+               int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, float scale,
+               float descale_q, float descale_k, float descale_v, int causal,
+               int out_f32, void *stream);
 
 /*
  * fa_bwd_workspace_size -- device scratch bytes that fa_bwd needs (written

@@ -24,7 +24,7 @@ def _header_text():
 
 def _declared_functions():
     text = re.sub(r"/\*.*?\*/", "", _header_text(), flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
 
 
 def _header_enums():
@@ -278,3 +278,20 @@ def test_bwd_masked_validation():
     assert call(D=48) == fa.FA_ERR_HEAD_DIM
     assert call(dq=Q) == fa.FA_ERR_OVERLAP
     assert call(ws=None) == fa.FA_ERR_WORKSPACE
+
+
+def test_fp8_validation():
+    def call(**kw):
+        a = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, H=3, Nq=100, Nk=90, D=128, scale=0.1, dq=0.01,
+                 dk=0.01, dv=0.01, causal=1, out_f32=0, stream=None)
+        a.update(kw)
+        return fa.fa_fwd_fp8(*(a[x] for x in ("q", "k", "v", "o", "lse", "B", "H", "Nq", "Nk",
+                                               "D", "scale", "dq", "dk", "dv", "causal",
+                                               "out_f32", "stream")))
+    assert call(q=None) == fa.FA_ERR_NULLPTR
+    assert call(Nq=0) == fa.FA_ERR_SHAPE
+    assert call(D=32) == fa.FA_ERR_HEAD_DIM
+    assert call(dk=math.inf) == fa.FA_ERR_SCALE
+    assert call(scale=3e38, dq=1e10) == fa.FA_ERR_SCALE
+    assert call(o=O + 4) == fa.FA_ERR_ALIGN
+    assert call(lse=Q) == fa.FA_ERR_OVERLAP

@@ -1,0 +1,77 @@
+"""GPU parity of the FP8 forward (fa_fwd_fp8, through the C ABI).  The
+operation is fa_fwd's on the dequantized inputs (e4m3 values times their
+per-tensor factors), so the oracle is the dense fp64 oracle applied to
+those real values, and the tolerance is the 16-bit path's: the products of
+e4m3 values are exact in fp32 and V widens exactly to bf16, leaving P's
+rounding to bf16 and fp32 sums: fp32 O <= 1e-2, L <= 1e-3; bf16 O the
+exact rounding of the fp32 O and within 1e-2 plus half an ulp."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_attention_07_amd as fa
+from workloads import gen_qkv_fp8, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fa.library()
+    oracle.load()
+
+
+def compare(B, H, Nq, Nk, D, causal, seed, rows=None, q_mult=1.0):
+    q8, k8, v8, (sq, sk, sv) = gen_qkv_fp8(B, H, Nq, Nk, D, seed, q_mult=q_mult)
+    scale = 1.0 / math.sqrt(D)
+    print(f"[fp8] B={B} H={H} Nq={Nq} Nk={Nk} D={D} causal={causal} "
+          f"rows={'all' if rows is None else len(rows)}", flush=True)
+    qd, kd, vd = q8.to(DEV), k8.to(DEV), v8.to(DEV)
+    o32, l32 = fa.fwd_fp8(qd, kd, vd, sq, sk, sv, causal=causal, scale=scale,
+                          out_dtype=torch.float32)
+    o16, l16 = fa.fwd_fp8(qd, kd, vd, sq, sk, sv, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    real = [t.double().numpy() * s for t, s in ((q8, sq), (k8, sk), (v8, sv))]
+    ro, rl = oracle.attention(*real, scale, causal, rows=rows)
+    sel = slice(None) if rows is None else torch.as_tensor(rows)
+    ro, rl = ro.reshape(-1, D), rl.reshape(-1)
+    g_o = o32.reshape(-1, D)[sel].double().cpu().numpy()
+    g_l = l32.reshape(-1)[sel].double().cpu().numpy()
+    err_o = float(np.abs(g_o - ro).max())
+    err_l = float(np.abs(g_l - rl).max())
+    print(f"[fp8]   fp32-O max-abs O {err_o:.3e} L {err_l:.3e}", flush=True)
+    assert err_o <= 1e-2 and err_l <= 1e-3
+    x16 = o16.reshape(-1, D)[sel].double().cpu().numpy()
+    assert np.array_equal(torch.from_numpy(g_o).to(torch.bfloat16).double().numpy(), x16)
+    mant = 7
+    e = np.floor(np.log2(np.maximum(np.abs(ro), 2.0 ** -14)))
+    assert (np.abs(x16 - ro) <= 1e-2 + 2.0 ** (e - mant - 1)).all()
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_ragged(D, causal):
+    compare(2, 2, 700, 700, D, causal, seed=3000 + D)
+
+
+@pytest.mark.parametrize("Nq,Nk", [(1, 1), (129, 400), (400, 129), (31, 33)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_shapes(Nq, Nk, causal):
+    compare(1, 2, Nq, Nk, 128, causal, seed=3100 + Nq)
+
+
+def test_fp8_large_logits():
+    compare(1, 2, 512, 512, 128, True, seed=3200, q_mult=8.0)
+
+
+def test_fp8_headline_shape_sampled():
+    """B8 N4096 D128 causal (the headline shape, FP8 inputs): 512 sampled rows."""
+    rows = sample_rows(8 * 4096, 512, 3300).numpy()
+    compare(8, 1, 4096, 4096, 128, True, seed=3, rows=rows)

@@ -15,6 +15,8 @@ C-ABI mirrors (same names and meaning as include/fa.h):
                   Tq, Tk, max_seqlen_q, D, scale, causal, dtype, stream) -> status
     fa_fwd_masked(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Nq, Nk, D, scale,
                   causal, window, nglobal, dtype, stream) -> status
+    fa_fwd_fp8(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Nq, Nk, D, scale,
+               descale_q, descale_k, descale_v, causal, out_f32, stream) -> status
     fa_bwd_workspace_size(B, H, Nq, Nk, D, causal, dtype) -> (status, bytes)
     fa_bwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_ptr,
            B, H, Nq, Nk, D, scale, causal, dtype, ws_ptr, ws_bytes, stream)
@@ -36,6 +38,8 @@ Tensor convenience:
                out_dtype=None) -> (o, lse) through fa_fwd_varlen
     fwd_masked(q, k, v, window, nglobal=0, causal=False, scale=None,
                out_dtype=None) -> (o, lse) through fa_fwd_masked
+    fwd_fp8(q8, k8, v8, descale_q, descale_k, descale_v, causal=False, scale=None,
+            out_dtype=None) -> (o, lse) through fa_fwd_fp8
     bwd(q, k, v, o, lse, do, causal=False, scale=None, grad_dtype=None,
         window=None, nglobal=0) -> (dq, dk, dv) through fa_bwd (fa_bwd_masked
         when a window is given)
@@ -54,8 +58,8 @@ __all__ = [
     "FA_OK", "FA_ERR_NULLPTR", "FA_ERR_SHAPE", "FA_ERR_HEAD_DIM", "FA_ERR_DTYPE",
     "FA_ERR_SCALE", "FA_ERR_ALIGN", "FA_ERR_HIP", "FA_ERR_OVERLAP", "FA_ERR_WORKSPACE",
     "LIBRARY", "EXPORTS", "library", "fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws",
-    "fa_fwd_varlen", "fa_fwd_masked", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_varlen", "fa_bwd_masked", "fa_status_str",
-    "fa_last_hip_error", "fa_version", "fwd", "fwd_varlen", "fwd_masked", "bwd", "bwd_varlen", "FaError",
+    "fa_fwd_varlen", "fa_fwd_masked", "fa_fwd_fp8", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_varlen", "fa_bwd_masked", "fa_status_str",
+    "fa_last_hip_error", "fa_version", "fwd", "fwd_varlen", "fwd_masked", "fwd_fp8", "bwd", "bwd_varlen", "FaError",
 ]
 
 LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
@@ -66,7 +70,8 @@ FA_F32, FA_BF16, FA_BF16_OF32, FA_F16, FA_F16_OF32 = 0, 1, 2, 3, 4
 
 # Every symbol include/fa.h declares.
 EXPORTS = ("fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws", "fa_fwd_varlen", "fa_fwd_masked",
-           "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_varlen", "fa_bwd_masked",
+           "fa_fwd_fp8",
+           "fa_fwd_fp8", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_varlen", "fa_bwd_masked",
            "fa_status_str", "fa_last_hip_error", "fa_version")
 
 _lib = None
@@ -104,6 +109,10 @@ def library() -> ctypes.CDLL:
     lib.fa_fwd_masked.restype = ctypes.c_int
     lib.fa_fwd_masked.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
                                   ctypes.c_int, i64, i64, ctypes.c_int, vp]
+    lib.fa_fwd_fp8.restype = ctypes.c_int
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
+                               ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_int,
+                               ctypes.c_int, vp]
     lib.fa_bwd_workspace_size.restype = ctypes.c_int
     lib.fa_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int,
                                           ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
@@ -164,6 +173,13 @@ def fa_fwd_masked(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, window, nglob
     return int(library().fa_fwd_masked(q, k, v, o, lse, B, H, Nq, Nk, D, float(scale),
                                        int(causal), int(window), int(nglobal), int(dtype),
                                        stream))
+
+
+def fa_fwd_fp8(q, k, v, o, lse, B, H, Nq, Nk, D, scale, dq, dk, dv, causal, out_f32,
+               stream) -> int:
+    """Raw C call; pointers are integers (device addresses) or None."""
+    return int(library().fa_fwd_fp8(q, k, v, o, lse, B, H, Nq, Nk, D, float(scale), float(dq),
+                                    float(dk), float(dv), int(causal), int(out_f32), stream))
 
 
 def fa_bwd_workspace_size(B, H, Nq, Nk, D, causal, dtype) -> Tuple[int, int]:
@@ -486,6 +502,45 @@ def fwd_masked(q, k, v, window: int, nglobal: int = 0, causal: bool = False,
         stream = torch.cuda.current_stream(q.device).cuda_stream
     st = fa_fwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                        B, H, Nq, Nk, D, scale, causal, window, nglobal, code, stream)
+    if st != FA_OK:
+        msg = fa_status_str(st)
+        if st == FA_ERR_HIP:
+            msg += ": " + fa_last_hip_error()
+        raise FaError(st, msg)
+    return o, lse
+
+
+def fwd_fp8(q, k, v, descale_q: float, descale_k: float, descale_v: float,
+            causal: bool = False, scale: Optional[float] = None, out_dtype=None, stream=None
+            ) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """FP8 attention forward (fa_fwd_fp8): q, k, v torch.float8_e4m3fn device
+    tensors [B,N,D] or [B,H,N,D] (real inputs = values x descale factors).
+    Returns (o in bf16 or fp32, lse fp32)."""
+    import torch
+
+    if q.dim() not in (3, 4) or k.dim() != q.dim() or v.dim() != q.dim():
+        raise ValueError("q, k, v must all be [B,N,D] or all [B,H,N,D]")
+    q4, k4 = (x.unsqueeze(1) if q.dim() == 3 else x for x in (q, k))
+    B, H, Nq, D = q4.shape
+    Nk = k4.shape[2]
+    if tuple(k.shape) != tuple(v.shape) or tuple(k4.shape) != (B, H, Nk, D):
+        raise ValueError("shape mismatch among q, k, v")
+    if not all(x.dtype == torch.float8_e4m3fn for x in (q, k, v)):
+        raise ValueError("q, k, v must be torch.float8_e4m3fn")
+    if not all(x.is_cuda and x.device == q.device and x.is_contiguous() for x in (q, k, v)):
+        raise ValueError("q, k, v must be contiguous on the same GPU device")
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out_dtype must be bfloat16 or float32")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H,
+                    Nq, Nk, D, scale, descale_q, descale_k, descale_v, causal,
+                    out_dtype == torch.float32, stream)
     if st != FA_OK:
         msg = fa_status_str(st)
         if st == FA_ERR_HIP:

@@ -22,6 +22,8 @@ SOURCES = [
     (os.path.join(PKG, "csrc", "fa_bwd.hip"), []),
     # local-window + global-token forward (same tile helpers as the backward)
     (os.path.join(PKG, "csrc", "fa_masked.hip"), []),
+    # FP8 (e4m3) forward
+    (os.path.join(PKG, "csrc", "fa_fp8.hip"), []),
 ]
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libfa.so")

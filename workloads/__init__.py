@@ -35,6 +35,7 @@ __all__ = [
     "gen_qkv",
     "gen_grad_out",
     "varlen_lengths",
+    "gen_qkv_fp8",
     "sample_rows",
     "WORKLOADS",
     "workload",
@@ -120,6 +121,22 @@ def varlen_lengths(total: int, S: int, seed: int, min_len: int = 1) -> List[int]
     cuts = torch.randint(0, spare + 1, (S - 1,), generator=g).sort().values.tolist()
     edges = [0] + cuts + [spare]
     return [min_len + b - a for a, b in zip(edges, edges[1:])]
+
+
+def gen_qkv_fp8(B: int, H: int, Nq: int, Nk: int, D: int, seed: int, q_mult: float = 1.0):
+    """FP8 inputs: the fp32 draws of gen_qkv (same recipe and seed), each
+    tensor divided by its own factor amax/448 and rounded to OCP e4m3
+    (torch.float8_e4m3fn, round to nearest even; 448 is e4m3's largest
+    finite value).  Returns (q8, k8, v8, (sq, sk, sv)); the real inputs are
+    q8 * sq etc."""
+    q, k, v = gen_qkv(B, H, Nq, Nk, D, seed, dtype="f32", q_mult=q_mult)
+    out, scales = [], []
+    for t in (q, k, v):
+        s = float(t.abs().max()) / 448.0
+        s = s if s > 0 else 1.0
+        out.append((t / s).to(torch.float8_e4m3fn).contiguous())
+        scales.append(s)
+    return out[0], out[1], out[2], tuple(scales)
 
 
 def gen_workload(w: Workload):
