@@ -177,6 +177,10 @@ def main() -> int:
                     help="time fa_fwd_masked instead: B=1 H=8 N=32768 D=128 causal bf16 "
                          "under a local window W with G global tokens; flops counted "
                          "over the visible pairs only (4*D each)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time fa_fwd_fp8 on the workload's shape with e4m3 inputs (scores on "
+                         "FP8 MFMA, P.V in bf16: roofline peak 1/(0.5/5000 + 0.5/2516.6) "
+                         "TFLOP/s)")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward pass (default) or the backward pass "
                          "(fa_bwd, fed by one forward call; flops counted as 2.5x "
@@ -280,7 +284,23 @@ def main() -> int:
         call = lib.fa_fwd_varlen
         args.entry = "fa_fwd_varlen"
         ws_bytes = 0
-    if masked is not None:
+    fp8 = None
+    if args.fp8:
+        from workloads import gen_qkv_fp8
+
+        if bwd or args.varlen or args.masked or w.dtype == "f32":
+            raise SystemExit("--fp8 times the forward pass of a 16-bit workload's shape")
+        q8, k8, v8, (sq, sk, sv) = gen_qkv_fp8(w.B, w.H, w.N, w.N, w.D, w.seed,
+                                               q_mult=w.q_mult)
+        q, k, v = q8.to(dev), k8.to(dev), v8.to(dev)
+        argv = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.H,
+                w.N, w.N, w.D, scale, sq, sk, sv, int(w.causal), int(out_dt == torch.float32),
+                sp)
+        call = lib.fa_fwd_fp8
+        args.entry = "fa_fwd_fp8"
+        ws_bytes = 0
+        fp8 = 1.0 / (0.5 / 5000.0 + 0.5 / PEAK_TFLOPS["bf16"])
+    if masked is not None or fp8 is not None:
         pass
     elif bwd and lens is not None:
         from workloads import gen_grad_out
@@ -365,7 +385,9 @@ def main() -> int:
         flops = 4.0 * masked["shape"][3] * masked["visible_pairs"] * (2.5 if bwd else 1.0)
     value = flops / (ms_per_step * 1e-3) / 1e12
     dkey = "f32" if in_dt == torch.float32 else ("bf16" if in_dt == torch.bfloat16 else "f16")
-    peak = PEAK_TFLOPS[dkey]
+    peak = PEAK_TFLOPS[dkey] if fp8 is None else round(fp8, 1)
+    if fp8 is not None:
+        dkey = "fp8e4m3+bf16"
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     props = torch.cuda.get_device_properties(dev)
 
@@ -391,7 +413,7 @@ def main() -> int:
                    "workspace_bytes": ws_bytes},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": None if (bwd or lens is not None or masked is not None)
+                     "traffic": None if (bwd or lens is not None or masked is not None or fp8 is not None)
         else measured_traffic(name),
                      "kernel_ms": round(kernel_ms, 5),
                      "group_ms": {"groups": len(group_ms),
@@ -407,7 +429,7 @@ def main() -> int:
         rate = exps / (kernel_ms * 1e-3) / 1e12
         line["exp_roofline"] = {"achieved": round(rate, 3), "peak": round(EXP_PEAK_T, 3),
                                 "unit": "Texp/s", "frac": round(rate / EXP_PEAK_T, 4)}
-    if not args.no_cpu_baseline and lens is None and masked is None:
+    if not args.no_cpu_baseline and lens is None and masked is None and fp8 is None:
         line["cpu_baseline"] = (cpu_baseline_bwd(w, args.cpu_seconds) if bwd
                                 else cpu_baseline(w, args.cpu_seconds))
     print(json.dumps(line), flush=True)
