@@ -43,6 +43,8 @@ int fa_internal_hip_fail(hipError_t e);
 
 namespace {
 
+constexpr float kLazy = 8.0f;  // base-2 slack of the lazy exponent reference
+
 constexpr int kQTile = kOwn * kWaves;  // 128 queries per workgroup
 // Keys per LDS block: 64 (two 32-key quarters) keep a workgroup's double-
 // buffered K and V at 78 KB at D = 128, so two workgroups share a compute
@@ -83,7 +85,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_masked(
 #pragma unroll
   for (int cc = 0; cc < NC; ++cc) acc[cc] = f32x16{};
   float m = -INFINITY;  // running maximum (base 2), equal in both half-waves
-  float l = 0.f;        // this half-wave's share of the running sum
+  float l = 0.f;   // this half-wave's share of the sum of p (fp32): gives L
+  float lr = 0.f;  // the same sum over p as rounded for P.V: normalises O        // this half-wave's share of the running sum
 
   const int nblk = (Nk + kMBlk - 1) / kMBlk;
   auto live_block = [&](int b) {
@@ -135,10 +138,23 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_masked(
         mx = fmaxf(mx, x);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx);
-      // a row with no visible key yet keeps the reference 0 (p = 0, alpha = 0)
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m - m_use);
+      // lazy reference: m moves only when a row's maximum exceeds it by more
+      // than kLazy (p stays below 2^kLazy), decided for the whole wave so the
+      // rescale of the accumulators is skipped together
+      const bool move = mx > m + kLazy;  // also true for the first visible key
+      if (__any(move)) {
+        const float m_new = move ? mx : m;
+        const float alpha = m == -INFINITY ? 0.f : exp2f(m - m_new);
+        l *= alpha;
+        lr *= alpha;
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[cc][r] *= alpha;
+        m = m_new;
+      }
+      // a row with no visible key yet keeps the reference 0 (p = 0)
+      const float m_use = m == -INFINITY ? 0.f : m;
       float p[16];
       float ps = 0.f;
 #pragma unroll
@@ -146,15 +162,13 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_masked(
         p[r] = exp2f(s[r] - m_use);
         ps += p[r];
       }
-      l = l * alpha + ps;
-      m = m_new;
-#pragma unroll
-      for (int cc = 0; cc < NC; ++cc)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[cc][r] *= alpha;
+      l += ps;
 #pragma unroll
       for (int tp = 0; tp < 2; ++tp) {
         const frag pb = pack_b<T>(p + 8 * tp);
+        const u32x4 pw = __builtin_bit_cast(u32x4, pb);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lr = Mma<T>::pair_sum(pw[e], lr);
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc)
           acc[cc] = M::mma(tr_frag<T, D>(vb, qq * kOwn + 16 * tp, 32 * cc, lane), pb, acc[cc]);
@@ -170,9 +184,13 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_masked(
   }
 
   const float lt = l + __shfl_xor(l, 32);
+  const float lrt = lr + __shfl_xor(lr, 32);
   if (myq < Nq) {
     OT *os = o + (size_t)bh * Nq * D;
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;  // no visible key: O = 0
+    // O is normalised by the rounded weights' sum, so the weights applied to
+    // V sum to one (a near one-hot row then reproduces its v); L uses the
+    // fp32 sum.  No visible key: O = 0
+    const float inv = lrt > 0.f ? 1.f / lrt : 0.f;
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) store_t<OT, D>(os, myq, 32 * cc, g, acc[cc], inv);
     if (g == 0)

@@ -60,6 +60,12 @@ template <> struct Mma<__bf16> {
   static __device__ __forceinline__ f32x2 unpack2(uint32_t x) {
     return __builtin_convertvector(__builtin_bit_cast(bf16x2, x), f32x2);
   }
+  // acc + x.lo + x.hi for a packed pair (v_dot2 with (1, 1)): sums values as
+  // rounded to bf16
+  static __device__ __forceinline__ float pair_sum(uint32_t x, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), one, acc, false);
+  }
 };
 
 template <> struct Mma<_Float16> {
@@ -73,6 +79,10 @@ template <> struct Mma<_Float16> {
   }
   static __device__ __forceinline__ f32x2 unpack2(uint32_t x) {
     return __builtin_convertvector(__builtin_bit_cast(f16x2, x), f32x2);
+  }
+  static __device__ __forceinline__ float pair_sum(uint32_t x, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), one, acc, false);
   }
 };
 
