@@ -75,3 +75,12 @@ def test_fp8_headline_shape_sampled():
     """B8 N4096 D128 causal (the headline shape, FP8 inputs): 512 sampled rows."""
     rows = sample_rows(8 * 4096, 512, 3300).numpy()
     compare(8, 1, 4096, 4096, 128, True, seed=3, rows=rows)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_many_tiles_sampled(causal):
+    """B1 H64 N1024 D128: 512 tiles of 128 rows, enough to fill every
+    workgroup slot, so the 128-row layout runs (smaller grids take the
+    pair-split 64-row layout): 512 sampled rows."""
+    rows = sample_rows(64 * 1024, 512, 3400 + int(causal)).numpy()
+    compare(1, 64, 1024, 1024, 128, causal, seed=3401, rows=rows)

@@ -70,11 +70,17 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t w) {
   return r;
 }
 
-template <typename OT, int D, bool CAUSAL>
+// PAIR: 64 queries per workgroup; waves w and w + 2 hold the same 32 queries
+// (group w & 1) and take alternate 32-key halves of each block, and merge
+// their states at the end (the online update applied to two partial
+// states).  Twice the workgroups for the same rows: for grids with fewer
+// 128-row tiles than workgroup slots, whose causal tiles are few and uneven.
+template <typename OT, int D, bool CAUSAL, bool PAIR>
 __global__ __launch_bounds__(kThreads, 2) void fa_fwd_fp8(
     const uint8_t *__restrict__ q, const uint8_t *__restrict__ k,
     const uint8_t *__restrict__ v, OT *__restrict__ o, float *__restrict__ lse, int Nq, int Nk,
     int BH, int nqt, float c, float dv) {
+  constexpr int QT = PAIR ? kQTile8 / 2 : kQTile8;  // queries per workgroup
   using M = Mma<__bf16>;
   typedef typename M::frag frag;
   constexpr int KF8 = D / 64;  // FP8 MFMAs along D for one 32x32 score block
@@ -90,8 +96,10 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_fp8(
   const int qt = CAUSAL ? nqt - 1 - (int)(blockIdx.x / BH) : (int)(blockIdx.x / BH);
   const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
   const int g = lane >> 5, col = lane & 31;
-  const int q0 = qt * kQTile8;
-  const int qw0 = q0 + w * kOwn;
+  const int grp = PAIR ? (w & 1) : w;  // query group
+  const int par = PAIR ? (w >> 1) : 0; // key-half parity (PAIR)
+  const int q0 = qt * QT;
+  const int qw0 = q0 + grp * kOwn;
   const int myq = qw0 + col;
   const uint8_t *qs = q + (size_t)bh * Nq * D;
   const uint8_t *ks = k + (size_t)bh * Nk * D;
@@ -155,7 +163,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_fp8(
     }
   };
 
-  const int kend = CAUSAL ? min(Nk, q0 + kQTile8) : Nk;
+  const int kend = CAUSAL ? min(Nk, q0 + QT) : Nk;
   const int nblk = (kend + kKBlk8 - 1) / kKBlk8;
   if (nblk > 0) {
     gload(0);
@@ -171,6 +179,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_fp8(
     const lds_char *vb = kb + KB;
 #pragma unroll
     for (int hq = 0; hq < kKBlk8 / kOwn; ++hq) {
+      if (PAIR && hq != par) continue;
       const int jq = j0 + hq * kOwn;
       // wave-uniform: keys past Nk, or (causal) past the wave's last query
       if (jq >= Nk || (CAUSAL && jq > qw0 + kOwn - 1)) continue;
@@ -230,6 +239,39 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_fp8(
     __syncthreads();
   }
 
+  if constexpr (PAIR) {
+    // merge the parity-1 wave's state into the parity-0 wave of each group
+    // (the K/V buffers are free: every wave is past the loop's last barrier)
+    typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+    lds_f32x4 *x = (lds_f32x4 *)(smem + grp * ((NC * 4 + 1) * kWave * 16));
+    if (par == 1) {
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          x[(cc * 4 + r4) * kWave + lane] = f32x4{acc[cc][4 * r4], acc[cc][4 * r4 + 1],
+                                                  acc[cc][4 * r4 + 2], acc[cc][4 * r4 + 3]};
+      x[NC * 4 * kWave + lane] = f32x4{m, l, lr, 0.f};
+    }
+    __syncthreads();
+    if (par == 1) return;
+    const f32x4 st = x[NC * 4 * kWave + lane];
+    const float mn = fmaxf(m, st[0]);
+    // a state with no key (m = -inf) weighs 0
+    const float a0 = m == -INFINITY ? 0.f : exp2f(m - mn);
+    const float a1 = st[0] == -INFINITY ? 0.f : exp2f(st[0] - mn);
+    l = l * a0 + st[1] * a1;
+    lr = lr * a0 + st[2] * a1;
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 y = x[(cc * 4 + r4) * kWave + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[cc][4 * r4 + e] = acc[cc][4 * r4 + e] * a0 + y[e] * a1;
+      }
+    m = mn;
+  }
   const float lt = l + __shfl_xor(l, 32);
   const float lrt = lr + __shfl_xor(lr, 32);
   if (myq < Nq) {
@@ -246,19 +288,40 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_fp8(
   }
 }
 
+template <typename OT, int D, bool CAUSAL, bool PAIR>
+hipError_t launch_fp8_1(const void *q, const void *k, const void *v, void *o, float *lse, int Nq,
+                        int Nk, int BH, float c, float dv, hipStream_t stream) {
+  constexpr int QT = PAIR ? kQTile8 / 2 : kQTile8;
+  const int nqt = (Nq + QT - 1) / QT;
+  hipLaunchKernelGGL((fa_fwd_fp8<OT, D, CAUSAL, PAIR>), dim3((unsigned)(BH * nqt)),
+                     dim3(kThreads), 0, stream, (const uint8_t *)q, (const uint8_t *)k,
+                     (const uint8_t *)v, (OT *)o, lse, Nq, Nk, BH, nqt, c, dv);
+  return hipGetLastError();
+}
+
 template <typename OT, int D>
 hipError_t launch_fp8(const void *q, const void *k, const void *v, void *o, float *lse, int Nq,
-                      int Nk, int BH, bool causal, float c, float dv, hipStream_t stream) {
-  const int nqt = (Nq + kQTile8 - 1) / kQTile8;
+                      int Nk, int BH, bool causal, bool pair, float c, float dv,
+                      hipStream_t stream) {
   if (causal)
-    hipLaunchKernelGGL((fa_fwd_fp8<OT, D, true>), dim3((unsigned)(BH * nqt)), dim3(kThreads), 0,
-                       stream, (const uint8_t *)q, (const uint8_t *)k, (const uint8_t *)v,
-                       (OT *)o, lse, Nq, Nk, BH, nqt, c, dv);
-  else
-    hipLaunchKernelGGL((fa_fwd_fp8<OT, D, false>), dim3((unsigned)(BH * nqt)), dim3(kThreads),
-                       0, stream, (const uint8_t *)q, (const uint8_t *)k, (const uint8_t *)v,
-                       (OT *)o, lse, Nq, Nk, BH, nqt, c, dv);
-  return hipGetLastError();
+    return pair ? launch_fp8_1<OT, D, true, true>(q, k, v, o, lse, Nq, Nk, BH, c, dv, stream)
+                : launch_fp8_1<OT, D, true, false>(q, k, v, o, lse, Nq, Nk, BH, c, dv, stream);
+  return pair ? launch_fp8_1<OT, D, false, true>(q, k, v, o, lse, Nq, Nk, BH, c, dv, stream)
+              : launch_fp8_1<OT, D, false, false>(q, k, v, o, lse, Nq, Nk, BH, c, dv, stream);
+}
+
+// Compute units of the current device, queried once per device (0 if the
+// query fails).
+int device_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  __atomic_store_n(&cache[dev], n, __ATOMIC_RELAXED);
+  return n;
 }
 
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
@@ -294,17 +357,21 @@ int fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
     return FA_ERR_OVERLAP;
   hipStream_t s = (hipStream_t)stream;
   const bool cz = causal != 0;
+  // pair-split 64-query workgroups when the 128-row tiles would leave
+  // workgroup slots (two per compute unit) empty
+  const int cus = device_cus();
+  const bool pair = cus > 0 && BH * ((Nq + kQTile8 - 1) / kQTile8) < 2 * (int64_t)cus;
   hipError_t e;
   if (out_f32)
-    e = D == 64 ? launch_fp8<float, 64>(q, k, v, o, lse, (int)Nq, (int)Nk, (int)BH, cz, c,
-                                        descale_v, s)
-                : launch_fp8<float, 128>(q, k, v, o, lse, (int)Nq, (int)Nk, (int)BH, cz, c,
-                                         descale_v, s);
+    e = D == 64 ? launch_fp8<float, 64>(q, k, v, o, lse, (int)Nq, (int)Nk, (int)BH, cz, pair,
+                                        c, descale_v, s)
+                : launch_fp8<float, 128>(q, k, v, o, lse, (int)Nq, (int)Nk, (int)BH, cz, pair,
+                                         c, descale_v, s);
   else
-    e = D == 64 ? launch_fp8<__bf16, 64>(q, k, v, o, lse, (int)Nq, (int)Nk, (int)BH, cz, c,
-                                         descale_v, s)
-                : launch_fp8<__bf16, 128>(q, k, v, o, lse, (int)Nq, (int)Nk, (int)BH, cz, c,
-                                          descale_v, s);
+    e = D == 64 ? launch_fp8<__bf16, 64>(q, k, v, o, lse, (int)Nq, (int)Nk, (int)BH, cz, pair,
+                                         c, descale_v, s)
+                : launch_fp8<__bf16, 128>(q, k, v, o, lse, (int)Nq, (int)Nk, (int)BH, cz, pair,
+                                          c, descale_v, s);
   if (e != hipSuccess) return fa_internal_hip_fail(e);
   return FA_OK;
 }
