@@ -151,6 +151,33 @@ def cpu_baseline_bwd(w, target_s: float):
     }
 
 
+def cpu_baseline_rows(run_rows, total_rows: int, flops_total: float, work_of, target_s: float,
+                      desc: str):
+    """Time an oracle on a uniform sample of its rows (64 first, to size the
+    sample for about target_s), scaled to the whole workload by the rows'
+    share of the work (work_of(rows) / work_of(all rows))."""
+    import numpy as np
+    import oracle
+    from workloads import sample_rows
+
+    probe = sample_rows(total_rows, min(64, total_rows), 7).numpy()
+    t0 = time.perf_counter()
+    run_rows(probe)
+    t_probe = time.perf_counter() - t0
+    n = int(max(64, min(total_rows, 64 * target_s / max(t_probe, 1e-9))))
+    rows = sample_rows(total_rows, n, 8).numpy()
+    t0 = time.perf_counter()
+    run_rows(rows)
+    elapsed = time.perf_counter() - t0
+    frac = work_of(rows) / work_of(np.arange(total_rows))
+    t_full = elapsed / frac
+    return {"value": flops_total / t_full / 1e12, "unit": "TFLOP/s",
+            "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{n} of {total_rows} rows drawn uniformly (seed 8), {desc}; time "
+                      f"scaled to the whole workload by the rows' share of the work",
+            "seconds": round(elapsed, 3), "seconds_full_workload": round(t_full, 6)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -429,9 +456,44 @@ def main() -> int:
         rate = exps / (kernel_ms * 1e-3) / 1e12
         line["exp_roofline"] = {"achieved": round(rate, 3), "peak": round(EXP_PEAK_T, 3),
                                 "unit": "Texp/s", "frac": round(rate / EXP_PEAK_T, 4)}
-    if not args.no_cpu_baseline and lens is None and masked is None and fp8 is None:
-        line["cpu_baseline"] = (cpu_baseline_bwd(w, args.cpu_seconds) if bwd
-                                else cpu_baseline(w, args.cpu_seconds))
+    if not args.no_cpu_baseline:
+        import numpy as np
+        import oracle
+
+        if bwd and (lens is not None or masked is not None or fp8 is not None):
+            pass  # the backward's oracle baseline is timed on the dense workload only
+        elif lens is not None:
+            # each packed sequence through the dense oracle, all of them
+            qn, kn, vn = (x.reshape(1, -1, w.D).double().cpu().numpy() for x in (q, k, v))
+            cu_h = [0] + [sum(lens[:i + 1]) for i in range(len(lens))]
+            t0 = time.perf_counter()
+            oracle.attention_varlen(qn, kn, vn, cu_h, cu_h, scale, w.causal)
+            el = time.perf_counter() - t0
+            line["cpu_baseline"] = {"value": flops / el / 1e12, "unit": "TFLOP/s",
+                                    "cores": oracle.threads(), "kind": "oracle",
+                                    "sample": "the whole varlen workload, once",
+                                    "seconds": round(el, 3)}
+        elif masked is not None:
+            MB, MH, MN, MD = masked["shape"]
+            qn, kn, vn = (x.double().cpu().numpy() for x in (q, k, v))
+            W, G = masked["window"], masked["global"]
+            i_all = np.arange(MN, dtype=np.int64)
+            lo = np.maximum(0, i_all - W + 1)
+            per_row = np.where(i_all < G, i_all + 1, (i_all - lo + 1) + np.minimum(G, lo))
+            line["cpu_baseline"] = cpu_baseline_rows(
+                lambda r: oracle.attention_masked(qn, kn, vn, scale, True, W, G, rows=r),
+                MB * MH * MN, flops, lambda r: float(per_row[np.asarray(r) % MN].sum()),
+                args.cpu_seconds, "masked oracle")
+        elif fp8 is not None:
+            real = [x.float().cpu().double().numpy() * f for x, f in ((q, sq), (k, sk), (v, sv))]
+            ii = lambda r: (np.asarray(r) % w.N) + 1 if w.causal else np.full(len(r), w.N)
+            line["cpu_baseline"] = cpu_baseline_rows(
+                lambda r: oracle.attention(*real, scale, w.causal, rows=r), w.rows, flops,
+                lambda r: float(ii(r).sum()), args.cpu_seconds,
+                "dense oracle on the dequantized inputs")
+        else:
+            line["cpu_baseline"] = (cpu_baseline_bwd(w, args.cpu_seconds) if bwd
+                                    else cpu_baseline(w, args.cpu_seconds))
     print(json.dumps(line), flush=True)
     return 0
 
