@@ -189,13 +189,23 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_fp8(
         s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
             k8_frag<D>(kb, hq * kOwn + col, 64 * t + 32 * g), qf[t], s, 0, 0, 0, 127, 0, 127);
       float mx = -INFINITY;
+      // wave-uniform: no key of the quarter past Nk or (causal) past the
+      // wave's first query: no per-score mask
+      if (jq + kOwn <= Nk && (!CAUSAL || jq + kOwn - 1 <= qw0)) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = jq + 8 * (r >> 2) + 4 * g + (r & 3);
-        const bool hid = j >= Nk || (CAUSAL && j > myq);
-        const float x = hid ? -INFINITY : s[r] * c;
-        s[r] = x;
-        mx = fmaxf(mx, x);
+        for (int r = 0; r < 16; ++r) {
+          s[r] *= c;
+          mx = fmaxf(mx, s[r]);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = jq + 8 * (r >> 2) + 4 * g + (r & 3);
+          const bool hid = j >= Nk || (CAUSAL && j > myq);
+          const float x = hid ? -INFINITY : s[r] * c;
+          s[r] = x;
+          mx = fmaxf(mx, x);
+        }
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       // lazy reference: m moves only when a row's maximum exceeds it by more

@@ -130,12 +130,23 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_masked(
       for (int t = 0; t < KF; ++t)
         s = M::mma(row_frag<T, D>(kb, qq * kOwn, 16 * t, lane), qf[t], s);
       float mx = -INFINITY;
+      // wave-uniform: every pair of the quarter visible (the common case
+      // inside the band): no per-score mask
+      if (jq + kOwn <= Nk && wlast == qw0 + kOwn - 1 &&
+          mk.all(qw0, wlast, jq, jq + kOwn - 1)) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = jq + 8 * (r >> 2) + 4 * g + (r & 3);
-        const float x = (j < Nk && mk.visible(myq, j)) ? s[r] * c : -INFINITY;
-        s[r] = x;
-        mx = fmaxf(mx, x);
+        for (int r = 0; r < 16; ++r) {
+          s[r] *= c;
+          mx = fmaxf(mx, s[r]);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = jq + 8 * (r >> 2) + 4 * g + (r & 3);
+          const float x = (j < Nk && mk.visible(myq, j)) ? s[r] * c : -INFINITY;
+          s[r] = x;
+          mx = fmaxf(mx, x);
+        }
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       // lazy reference: m moves only when a row's maximum exceeds it by more

@@ -238,6 +238,14 @@ struct Mask {
                               : (ihi - jlo >= -(window - 1) && ilo - jhi <= window - 1);
     return gk || gq || local;
   }
+  // Is every pair of queries [ilo, ihi] x keys [jlo, jhi] visible?  (A
+  // sufficient test: one part of the rule covers the whole range.)
+  __device__ __forceinline__ bool all(int ilo, int ihi, int jlo, int jhi) const {
+    const bool cz = !causal || jhi <= ilo;
+    const bool local = causal ? (ilo - jhi >= 0 && ihi - jlo <= window - 1)
+                              : (ihi - jlo <= window - 1 && jhi - ilo <= window - 1);
+    return local || ((jhi < nglobal || ihi < nglobal) && cz);
+  }
 };
 
 }  // namespace
