@@ -302,7 +302,7 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * r4 + e;
-            float pr = exp2f(fmaf(s[hf][r], c, -lv[e]));
+            float pr = __builtin_amdgcn_exp2f(fmaf(s[hf][r], c, -lv[e]));
             if constexpr (MASKED) {
               if (!mk.visible(i0 + ib + e, myk)) pr = 0.f;
             } else if (CAUSAL && myk > i0 + ib + e) {
@@ -456,7 +456,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = j0 + r0 + 8 * (r >> 2) + 4 * g + (r & 3);
-          float pr = exp2f(fmaf(s[hf][r], c, -l2));
+          float pr = __builtin_amdgcn_exp2f(fmaf(s[hf][r], c, -l2));
           if constexpr (MASKED) {
             if (j >= Nk || !mk.visible(myq, j)) pr = 0.f;
           } else if (j >= Nk || (CAUSAL && j > myq)) {

@@ -214,7 +214,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_fp8(
       const bool move = mx > m + kLazy;  // also true for the first visible key
       if (__any(move)) {
         const float m_new = move ? mx : m;
-        const float alpha = m == -INFINITY ? 0.f : exp2f(m - m_new);
+        const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_new);
         l *= alpha;
         lr *= alpha;
 #pragma unroll
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_fp8(
       float ps = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        p[r] = exp2f(s[r] - m_use);
+        p[r] = __builtin_amdgcn_exp2f(s[r] - m_use);
         ps += p[r];
       }
       l += ps;
@@ -268,8 +268,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_fp8(
     const f32x4 st = x[NC * 4 * kWave + lane];
     const float mn = fmaxf(m, st[0]);
     // a state with no key (m = -inf) weighs 0
-    const float a0 = m == -INFINITY ? 0.f : exp2f(m - mn);
-    const float a1 = st[0] == -INFINITY ? 0.f : exp2f(st[0] - mn);
+    const float a0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+    const float a1 = st[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st[0] - mn);
     l = l * a0 + st[1] * a1;
     lr = lr * a0 + st[2] * a1;
 #pragma unroll

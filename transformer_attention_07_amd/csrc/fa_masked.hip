@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_masked(
       const bool move = mx > m + kLazy;  // also true for the first visible key
       if (__any(move)) {
         const float m_new = move ? mx : m;
-        const float alpha = m == -INFINITY ? 0.f : exp2f(m - m_new);
+        const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_new);
         l *= alpha;
         lr *= alpha;
 #pragma unroll
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_masked(
       float ps = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        p[r] = exp2f(s[r] - m_use);
+        p[r] = __builtin_amdgcn_exp2f(s[r] - m_use);
         ps += p[r];
       }
       l += ps;
