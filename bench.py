@@ -418,8 +418,20 @@ def main() -> int:
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     props = torch.cuda.get_device_properties(dev)
 
+    metric = METRIC if not bwd else METRIC_BWD
+    shape = {"B": w.B, "H": w.H, "Nq": w.N, "Nk": w.N, "D": w.D, "causal": w.causal}
+    if masked is not None:
+        # the masked mode runs its own long-sequence shape, named as such
+        MB, MH, MN, MD = masked["shape"]
+        tag = f"B{MB} H{MH} N{MN} D{MD} causal, window {masked['window']}, " \
+              f"{masked['global']} global, visible pairs"
+        metric = (f"attention {'bwd' if bwd else 'fwd'} TFLOP/s + % bf16 MFMA peak "
+                  f"(masked {tag})")
+        name = (f"bf16_b{MB}_h{MH}_n{MN}_d{MD}_causal_w{masked['window']}"
+                f"_g{masked['global']}")
+        shape = {"B": MB, "H": MH, "Nq": MN, "Nk": MN, "D": MD, "causal": True}
     line = {
-        "metric": METRIC if not bwd else METRIC_BWD,
+        "metric": metric,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "pct_of_peak": round(100.0 * value / peak, 2),
@@ -432,8 +444,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": dkey,
         "data": "synthetic (seeded i.i.d. Gaussian q, k, v)",
-        "config": {"workload": name, "B": w.B, "H": w.H, "Nq": w.N, "Nk": w.N, "D": w.D,
-                   "causal": w.causal, "out": str(out_dt).replace("torch.", ""),
+        "config": {"workload": name, **shape, "out": str(out_dt).replace("torch.", ""),
                    "flops_per_step": flops, "entry": args.entry,
                    **({"varlen_lengths": lens} if lens is not None else {}),
                    **({"masked": masked} if masked is not None else {}),

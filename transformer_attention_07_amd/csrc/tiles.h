@@ -12,6 +12,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "mask.h"
+
 namespace {
 
 constexpr int kWave = 64;
@@ -216,37 +218,6 @@ __device__ __forceinline__ void clear_padding(lds_char *smem, int bytes, int tid
       *(lds_u32x4 *)(smem + o) = u32x4{0u, 0u, 0u, 0u};
   }
 }
-
-// Local-window + global-token visibility (the reading of the pages' sparse
-// attention used by fa_fwd_masked and fa_bwd_masked): key j is visible to
-// query i iff (causal ? 0 <= i - j < window : |i - j| < window) or
-// (j < nglobal || i < nglobal) && (!causal || j <= i).
-struct Mask {
-  int causal, window, nglobal;
-
-  __device__ __forceinline__ bool visible(int i, int j) const {
-    const int d = i - j;
-    const bool local = causal ? (d >= 0 && d < window) : (d > -window && d < window);
-    const bool global = (j < nglobal || i < nglobal) && (!causal || j <= i);
-    return local || global;
-  }
-  // Is some pair of queries [ilo, ihi] x keys [jlo, jhi] visible?
-  __device__ __forceinline__ bool any(int ilo, int ihi, int jlo, int jhi) const {
-    const bool gk = jlo < nglobal && (!causal || jlo <= ihi);
-    const bool gq = ilo < nglobal && (!causal || jlo <= min(ihi, nglobal - 1));
-    const bool local = causal ? (ihi - jlo >= 0 && ilo - jhi <= window - 1)
-                              : (ihi - jlo >= -(window - 1) && ilo - jhi <= window - 1);
-    return gk || gq || local;
-  }
-  // Is every pair of queries [ilo, ihi] x keys [jlo, jhi] visible?  (A
-  // sufficient test: one part of the rule covers the whole range.)
-  __device__ __forceinline__ bool all(int ilo, int ihi, int jlo, int jhi) const {
-    const bool cz = !causal || jhi <= ilo;
-    const bool local = causal ? (ilo - jhi >= 0 && ihi - jlo <= window - 1)
-                              : (ihi - jlo <= window - 1 && jhi - ilo <= window - 1);
-    return local || ((jhi < nglobal || ihi < nglobal) && cz);
-  }
-};
 
 }  // namespace
 
