@@ -200,6 +200,9 @@ def main() -> int:
                     help="time fa_fwd_varlen instead: the workload's tokens (B*N, one "
                          "head) cut into S sequences of seeded lengths (seed 77, at "
                          "least 64 tokens each), flops summed per sequence")
+    ap.add_argument("--split", action="store_true",
+                    help="with --varlen: time fa_fwd_varlen_ws (long tiles cut over their "
+                         "keys, caller-owned workspace) instead of fa_fwd_varlen")
     ap.add_argument("--masked", default=None, metavar="W,G",
                     help="time fa_fwd_masked instead: B=1 H=8 N=32768 D=128 causal bf16 "
                          "under a local window W with G global tokens; flops counted "
@@ -311,6 +314,15 @@ def main() -> int:
         call = lib.fa_fwd_varlen
         args.entry = "fa_fwd_varlen"
         ws_bytes = 0
+        if args.split and not bwd:
+            st, ws_bytes = fa.fa_fwd_varlen_workspace_size(len(lens), 1, T, T, max(lens),
+                                                           max(lens), w.D, int(w.causal), code)
+            if st != 0:
+                raise RuntimeError(f"fa_fwd_varlen_workspace_size: {fa.fa_status_str(st)}")
+            ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+            argv = argv[:12] + (max(lens),) + argv[12:16] + (ws.data_ptr(), ws_bytes, sp)
+            call = lib.fa_fwd_varlen_ws
+            args.entry = "fa_fwd_varlen_ws"
     fp8 = None
     if args.fp8:
         from workloads import gen_qkv_fp8

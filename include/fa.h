@@ -1,7 +1,7 @@
 /*
  * fa.h -- C ABI of the MI355X (gfx950) FlashAttention-2 library: the
- * forward pass (fa_fwd, fa_fwd_ws; fa_fwd_varlen for variable-length
- * batches, fa_fwd_masked for local-window + global-token masks, fa_fwd_fp8
+ * forward pass (fa_fwd, fa_fwd_ws; fa_fwd_varlen and fa_fwd_varlen_ws for
+ * variable-length batches, fa_fwd_masked for local-window + global-token masks, fa_fwd_fp8
  * for FP8 inputs) and its
  * backward pass (fa_bwd, fa_bwd_varlen, fa_bwd_masked).
  *
@@ -71,7 +71,7 @@ enum fa_status {
     FA_ERR_HIP = 7,      /* the HIP runtime refused the launch               */
     FA_ERR_OVERLAP = 8,  /* o, lse or workspace overlaps an input or another
                             output                                           */
-    FA_ERR_WORKSPACE = 9 /* workspace NULL or smaller than fa_fwd_ws needs   */
+    FA_ERR_WORKSPACE = 9 /* workspace NULL or smaller than the call needs     */
 };
 
 /*
@@ -191,6 +191,53 @@ int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *l
                   int64_t S, int64_t H, int64_t Tq, int64_t Tk,
                   int64_t max_seqlen_q, int64_t D, float scale, int causal,
                   int dtype, void *stream);
+
+/*
+ * fa_fwd_varlen_workspace_size -- device scratch bytes that fa_fwd_varlen_ws
+ * needs for this problem on the current device (written to *bytes; 0 when
+ * no query tile is split, and then fa_fwd_varlen_ws is fa_fwd_varlen).
+ *
+ * Arguments as fa_fwd_varlen, plus max_seqlen_k (>= 0), an estimate of the
+ * longest key length.  Together with max_seqlen_q it bounds the work of the
+ * call; a tile whose key range is longer than the call's share per compute
+ * unit is cut into several chunks (sequence parallelism, page
+ * "FlashAttention技术演进全景图" §3.2), each run by its own workgroup, whose
+ * partial results are combined with the online-softmax rescaling of page
+ * "FlashAttention-2实现与优化：高效注意力机制详解" §3.1 by a second kernel.
+ * Without the split one workgroup runs the longest sequence's last tile and
+ * bounds the call.  Returns FA_OK, or the shape / head-dim / dtype errors
+ * of fa_fwd_varlen, FA_ERR_NULLPTR (bytes NULL) or FA_ERR_HIP.
+ */
+int fa_fwd_varlen_workspace_size(int64_t S, int64_t H, int64_t Tq, int64_t Tk,
+                                 int64_t max_seqlen_q, int64_t max_seqlen_k,
+                                 int64_t D, int causal, int dtype, size_t *bytes);
+
+/*
+ * fa_fwd_varlen_ws -- fa_fwd_varlen with key-split tiles and caller-owned
+ * device scratch.
+ *
+ * Arguments as fa_fwd_varlen, plus
+ *   max_seqlen_k     as for fa_fwd_varlen_workspace_size; it steers the
+ *                    split only: every tile is computed whatever the real
+ *                    lengths (a tile gets at most a fixed number of chunks,
+ *                    which grow with its key range)
+ *   workspace        device pointer, 16-byte aligned, of at least the bytes
+ *                    fa_fwd_varlen_workspace_size reports for the same
+ *                    arguments, or NULL when it reports 0
+ *   workspace_bytes  its size in bytes
+ *
+ * Results as fa_fwd_varlen up to the order of the fp32 summation (split
+ * tiles add their chunks' partial sums in a different order).  Calls that
+ * share a workspace must be ordered on one stream.  Errors as fa_fwd_varlen,
+ * plus FA_ERR_WORKSPACE (workspace NULL or too small), FA_ERR_ALIGN and
+ * FA_ERR_OVERLAP for the workspace.
+ */
+int fa_fwd_varlen_ws(const void *q, const void *k, const void *v, void *o,
+                     float *lse, const int32_t *cu_seqlens_q,
+                     const int32_t *cu_seqlens_k, int64_t S, int64_t H, int64_t Tq,
+                     int64_t Tk, int64_t max_seqlen_q, int64_t max_seqlen_k,
+                     int64_t D, float scale, int causal, int dtype,
+                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * fa_fwd_masked -- the forward pass under a local-window + global-token

@@ -1,4 +1,5 @@
-"""GPU parity of variable-length batches (fa_fwd_varlen, through the C ABI)
+"""GPU parity of variable-length batches (fa_fwd_varlen, fa_fwd_varlen_ws
+with key-split tiles, through the C ABI)
 against the fp64 oracle (oracle.attention_varlen), with the forward's
 tolerances: fp32 O <= 1e-2 and L <= 1e-3 for 16-bit inputs, 16-bit O the
 exact rounding of the fp32 O and within 1e-2 plus half an ulp.  Each
@@ -46,21 +47,28 @@ def packed(lq, lk, H, D, seed, dtype="bf16"):
     return q[0], k[0], v[0], cu_q, cu_k
 
 
-def run(q, k, v, cu_q, cu_k, maxq, causal, scale, out_dtype):
+def run(q, k, v, cu_q, cu_k, maxq, causal, scale, out_dtype, maxk=None):
     o, lse = fa.fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu_q.to(DEV), cu_k.to(DEV), maxq,
-                           causal=causal, scale=scale, out_dtype=out_dtype)
+                           causal=causal, scale=scale, out_dtype=out_dtype, max_seqlen_k=maxk)
     torch.cuda.synchronize()
     return o.float().cpu(), lse.cpu()
 
 
-def compare(lq, lk, H, D, causal, seed, dtype="bf16", scale=None, rows=None, solo=True):
+def compare(lq, lk, H, D, causal, seed, dtype="bf16", scale=None, rows=None, solo=True,
+            maxk=None):
+    """maxk: run fa_fwd_varlen_ws with this max_seqlen_k (key-split tiles)."""
     q, k, v, cu_q, cu_k = packed(lq, lk, H, D, seed, dtype)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     maxq = max(lq) if max(lq) > 0 else 1
     _log(f"S={len(lq)} H={H} D={D} causal={causal} dtype={dtype} Tq={sum(lq)} Tk={sum(lk)} "
-         f"max_q={maxq} rows={'all' if rows is None else len(rows)}")
-    o32, l32 = run(q, k, v, cu_q, cu_k, maxq, causal, scale, torch.float32)
-    o16, l16 = run(q, k, v, cu_q, cu_k, maxq, causal, scale, q.dtype)
+         f"max_q={maxq} max_k={maxk} rows={'all' if rows is None else len(rows)}")
+    if maxk is not None:
+        st, nb = fa.fa_fwd_varlen_workspace_size(len(lq), H, sum(lq), sum(lk), maxq, maxk, D,
+                                                 causal, fa._dtype_code(torch, q.dtype, q.dtype))
+        assert st == 0 and nb > 0, "the split case must split"
+        solo = False  # split tiles sum their chunks in another order than fa_fwd
+    o32, l32 = run(q, k, v, cu_q, cu_k, maxq, causal, scale, torch.float32, maxk)
+    o16, l16 = run(q, k, v, cu_q, cu_k, maxq, causal, scale, q.dtype, maxk)
     qn, kn, vn = (t.double().numpy() for t in (q, k, v))
     if rows is None:
         ro, rl = oracle.attention_varlen(qn, kn, vn, cu_q.numpy(), cu_k.numpy(), scale, causal)
@@ -163,6 +171,63 @@ def test_varlen_32k_tokens_sampled():
     lens = varlen_lengths(32768, 8, seed=77, min_len=64)
     rows = sample_rows(32768, 512, 7700).numpy()
     compare(lens, lens, 1, 128, True, seed=1800, rows=rows)
+
+
+# --- key-split tiles (fa_fwd_varlen_ws) --------------------------------------
+# Lengths with long sequences next to short ones: tiles of the long ones span
+# more than eight 64-key tiles and are cut into 2-4 chunks; the rest run whole.
+SPLIT = [1, 2000, 31, 700, 1500, 64, 5]
+
+
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_split_mixed_lengths(D, causal):
+    compare(SPLIT, SPLIT, 2, D, causal, seed=2100 + D, maxk=max(SPLIT))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_split_unequal_and_empty(causal):
+    """Nq != Nk per sequence, a sequence without queries and one without keys."""
+    compare([100, 0, 1300, 40, 9], [7, 900, 2000, 0, 41], 2, 128, causal, seed=2200,
+            maxk=2000)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_split_pair_layout(causal):
+    """Long sequences on average (>= 2048 tokens): the pair-split 128-row
+    tiles, cut over their keys."""
+    compare([3000, 1200], [3000, 1200], 2, 128, causal, seed=2250, maxk=3000)
+
+
+def test_varlen_split_fp16_negative_scale():
+    compare(SPLIT, SPLIT, 1, 64, True, seed=2300, dtype="f16", scale=-0.2, maxk=max(SPLIT))
+
+
+def test_varlen_split_underestimated_keys():
+    """max_seqlen_k below the real longest key range: the chunks of a tile
+    grow (at most the planned count per tile) and every key is still seen."""
+    compare(SPLIT, SPLIT, 2, 128, True, seed=2400, maxk=700)
+    compare(SPLIT, SPLIT, 2, 128, False, seed=2401, maxk=700)
+
+
+def test_varlen_split_matches_unsplit_on_short_tiles():
+    """Tiles the plan leaves whole are computed exactly as fa_fwd_varlen does."""
+    q, k, v, cu_q, cu_k = packed(SPLIT, SPLIT, 1, 128, 2500)
+    a = run(q, k, v, cu_q, cu_k, 2000, True, 0.1, torch.float32)
+    b = run(q, k, v, cu_q, cu_k, 2000, True, 0.1, torch.float32, maxk=2000)
+    # the 64-row sequence (rows 4232 .. 4295) has one tile with one key tile
+    s = slice(int(cu_q[5]), int(cu_q[6]))
+    assert s.stop - s.start == 64
+    assert torch.equal(a[0][:, s], b[0][:, s]) and torch.equal(a[1][:, s], b[1][:, s])
+
+
+@pytest.mark.parametrize("S", [8, 32])
+def test_varlen_split_32k_tokens_sampled(S):
+    """The shapes bench.py --varlen S --split times (32768 tokens, D=128,
+    causal bf16): 512 sampled rows against the oracle."""
+    lens = varlen_lengths(32768, S, seed=77, min_len=64)
+    rows = sample_rows(32768, 512, 7800 + S).numpy()
+    compare(lens, lens, 1, 128, True, seed=1800 + S, rows=rows, maxk=max(lens))
 
 
 # --- backward over variable-length batches (fa_bwd_varlen) ------------------

@@ -13,6 +13,11 @@ C-ABI mirrors (same names and meaning as include/fa.h):
               causal, dtype, ws_ptr, ws_bytes, stream) -> status
     fa_fwd_varlen(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, cu_q_ptr, cu_k_ptr, S, H,
                   Tq, Tk, max_seqlen_q, D, scale, causal, dtype, stream) -> status
+    fa_fwd_varlen_workspace_size(S, H, Tq, Tk, max_seqlen_q, max_seqlen_k, D, causal,
+                  dtype) -> (status, bytes)
+    fa_fwd_varlen_ws(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, cu_q_ptr, cu_k_ptr, S, H, Tq,
+                  Tk, max_seqlen_q, max_seqlen_k, D, scale, causal, dtype, ws_ptr,
+                  ws_bytes, stream) -> status
     fa_fwd_masked(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Nq, Nk, D, scale,
                   causal, window, nglobal, dtype, stream) -> status
     fa_fwd_fp8(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Nq, Nk, D, scale,
@@ -58,7 +63,7 @@ __all__ = [
     "FA_OK", "FA_ERR_NULLPTR", "FA_ERR_SHAPE", "FA_ERR_HEAD_DIM", "FA_ERR_DTYPE",
     "FA_ERR_SCALE", "FA_ERR_ALIGN", "FA_ERR_HIP", "FA_ERR_OVERLAP", "FA_ERR_WORKSPACE",
     "LIBRARY", "EXPORTS", "library", "fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws",
-    "fa_fwd_varlen", "fa_fwd_masked", "fa_fwd_fp8", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_varlen", "fa_bwd_masked", "fa_status_str",
+    "fa_fwd_varlen", "fa_fwd_varlen_workspace_size", "fa_fwd_varlen_ws", "fa_fwd_masked", "fa_fwd_fp8", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_varlen", "fa_bwd_masked", "fa_status_str",
     "fa_last_hip_error", "fa_version", "fwd", "fwd_varlen", "fwd_masked", "fwd_fp8", "bwd", "bwd_varlen", "FaError",
 ]
 
@@ -69,9 +74,8 @@ FA_F32, FA_BF16, FA_BF16_OF32, FA_F16, FA_F16_OF32 = 0, 1, 2, 3, 4
  FA_ERR_ALIGN, FA_ERR_HIP, FA_ERR_OVERLAP, FA_ERR_WORKSPACE) = range(10)
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws", "fa_fwd_varlen", "fa_fwd_masked",
-           "fa_fwd_fp8",
-           "fa_fwd_fp8", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_varlen", "fa_bwd_masked",
+EXPORTS = ("fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws", "fa_fwd_varlen",
+           "fa_fwd_varlen_workspace_size", "fa_fwd_varlen_ws", "fa_fwd_masked", "fa_fwd_fp8", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_varlen", "fa_bwd_masked",
            "fa_status_str", "fa_last_hip_error", "fa_version")
 
 _lib = None
@@ -106,6 +110,13 @@ def library() -> ctypes.CDLL:
     lib.fa_fwd_varlen.restype = ctypes.c_int
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                   ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
+    lib.fa_fwd_varlen_workspace_size.restype = ctypes.c_int
+    lib.fa_fwd_varlen_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, i64, ctypes.c_int,
+                                                 ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+    lib.fa_fwd_varlen_ws.restype = ctypes.c_int
+    lib.fa_fwd_varlen_ws.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                     i64, ctypes.c_float, ctypes.c_int, ctypes.c_int, vp,
+                                     ctypes.c_size_t, vp]
     lib.fa_fwd_masked.restype = ctypes.c_int
     lib.fa_fwd_masked.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
                                   ctypes.c_int, i64, i64, ctypes.c_int, vp]
@@ -157,6 +168,24 @@ def fa_fwd_ws(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, dtype, ws, ws_byt
     """Raw C call; pointers are integers (device addresses) or None."""
     return int(library().fa_fwd_ws(q, k, v, o, lse, B, H, Nq, Nk, D, float(scale),
                                    int(causal), int(dtype), ws, int(ws_bytes), stream))
+
+
+def fa_fwd_varlen_workspace_size(S, H, Tq, Tk, max_seqlen_q, max_seqlen_k, D, causal,
+                                 dtype) -> Tuple[int, int]:
+    """Raw C call; returns (status, workspace bytes)."""
+    n = ctypes.c_size_t(0)
+    st = int(library().fa_fwd_varlen_workspace_size(S, H, Tq, Tk, max_seqlen_q, max_seqlen_k,
+                                                    D, int(causal), int(dtype),
+                                                    ctypes.byref(n)))
+    return st, int(n.value)
+
+
+def fa_fwd_varlen_ws(q, k, v, o, lse, cu_q, cu_k, S, H, Tq, Tk, max_seqlen_q, max_seqlen_k, D,
+                     scale, causal, dtype, ws, ws_bytes, stream) -> int:
+    """Raw C call; pointers are integers (device addresses) or None."""
+    return int(library().fa_fwd_varlen_ws(q, k, v, o, lse, cu_q, cu_k, S, H, Tq, Tk,
+                                          max_seqlen_q, max_seqlen_k, D, float(scale),
+                                          int(causal), int(dtype), ws, int(ws_bytes), stream))
 
 
 def fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, S, H, Tq, Tk, max_seqlen_q, D, scale, causal,
@@ -381,12 +410,15 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, scale: Optional[float] = None
 
 
 def fwd_varlen(q, k, v, cu_q, cu_k, max_seqlen_q: int, causal: bool = False,
-               scale: Optional[float] = None, out_dtype=None, stream=None
+               scale: Optional[float] = None, out_dtype=None, stream=None,
+               max_seqlen_k: Optional[int] = None
                ) -> Tuple["torch.Tensor", "torch.Tensor"]:
     """Variable-length attention forward (fa_fwd_varlen) on device tensors.
 
     q: [H, Tq, D]; k, v: [H, Tk, D] (bf16 or fp16, contiguous, one device);
     cu_q, cu_k: int32 device tensors of S + 1 offsets (0, ..., Tq / Tk).
+    With ``max_seqlen_k`` given, long tiles are split over their keys
+    (fa_fwd_varlen_ws, workspace allocated here).
     Returns (o [H, Tq, D] in ``out_dtype``, lse [H, Tq] fp32).
     """
     import torch
@@ -413,9 +445,19 @@ def fwd_varlen(q, k, v, cu_q, cu_k, max_seqlen_q: int, causal: bool = False,
     lse = torch.empty((H, Tq), dtype=torch.float32, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                       cu_q.data_ptr(), cu_k.data_ptr(), S, H, Tq, Tk, int(max_seqlen_q), D,
-                       scale, causal, code, stream)
+    if max_seqlen_k is None:
+        st = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                           lse.data_ptr(), cu_q.data_ptr(), cu_k.data_ptr(), S, H, Tq, Tk,
+                           int(max_seqlen_q), D, scale, causal, code, stream)
+    else:
+        st, nb = fa_fwd_varlen_workspace_size(S, H, Tq, Tk, int(max_seqlen_q),
+                                              int(max_seqlen_k), D, causal, code)
+        if st == FA_OK:
+            ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device)
+            st = fa_fwd_varlen_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  lse.data_ptr(), cu_q.data_ptr(), cu_k.data_ptr(), S, H, Tq,
+                                  Tk, int(max_seqlen_q), int(max_seqlen_k), D, scale, causal,
+                                  code, ws.data_ptr() if nb else None, nb, stream)
     if st != FA_OK:
         msg = fa_status_str(st)
         if st == FA_ERR_HIP:

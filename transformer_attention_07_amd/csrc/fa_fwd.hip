@@ -1034,14 +1034,39 @@ __global__ __launch_bounds__(kThreads8) void fa_fwd_pipe8(
 // write outside the tensors).  A sequence with queries and no keys gets
 // O = 0 and L = -inf (the logarithm of an empty sum).  PAIR selects the
 // pair-split 128-row layout (D = 128, few tiles) over the 256-row one.
+//
+// Split keys (NC > 1, the sequence parallelism of page "FlashAttention技术
+// 演进全景图" §3.2 applied per sequence): a tile whose key range spans more
+// than KC 64-key tiles is cut into chunks of KC, one workgroup each, which
+// write (m, l, lr) and the normalised accumulator to workspace slot
+// varlen_slot(...) for fa_merge_varlen; shorter tiles write O and L at once.
+// Without it the longest sequence's last tile, run by one workgroup, bounds
+// the whole call.
+__device__ __forceinline__ int varlen_slot(int h, int NT, int NC, int qa, int q0, int QT,
+                                           int sq, int chunk) {
+  // floor((qa + q0) / QT) + sq is distinct for every (sequence, tile) of a
+  // head: within a sequence consecutive tiles step it by one, and a later
+  // sequence starts past the earlier one's last row with a larger sq; it is
+  // below ceil(Tq / QT) + S = NT
+  return (h * NT + (qa + q0) / QT + sq) * NC + chunk;
+}
+
+// Chunks of a tile with nkt key tiles: ceil(nkt / KC), at most NC (the
+// chunks are then longer than KC, whatever the sequence lengths), each of
+// ceil(nkt / chunks) key tiles.
+__device__ __forceinline__ int varlen_chunks(int nkt, int NC, int KC) {
+  return min(NC, (nkt + KC - 1) / KC);
+}
+
 template <typename T, typename OT, int D, bool CAUSAL, bool PAIR>
 __global__ __launch_bounds__(kThreads8) void fa_fwd_varlen(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     OT *__restrict__ o, float *__restrict__ lse, const int *__restrict__ cu_q,
     const int *__restrict__ cu_k, int S, int H, int Tq, int Tk, int ntiles, float c,
-    int negate) {
+    int negate, float *__restrict__ ws, int NC, int KC, int NT) {
   constexpr int QT = QRows<PAIR>::value;
-  const int id = blockIdx.x;
+  const int chunk = blockIdx.x % NC;
+  const int id = blockIdx.x / NC;
   // rank-major (longest causal tiles first); the slice index is rotated by
   // the rank so that one sequence's tiles are spread over the XCDs (the
   // dispatcher deals workgroup ids to the 8 XCDs round robin: without the
@@ -1057,6 +1082,7 @@ __global__ __launch_bounds__(kThreads8) void fa_fwd_varlen(
   if (q0 >= nq) return;  // workgroup-uniform, before any barrier
   const size_t qo = (size_t)h * Tq + qa, ko = (size_t)h * Tk + ka;
   if (nk == 0) {
+    if (chunk != 0) return;
     const int rows = min(QT, nq - q0);
     for (int i = threadIdx.x; i < rows * D; i += kThreads8)
       o[(qo + q0) * D + i] = (OT)0.f;
@@ -1064,9 +1090,20 @@ __global__ __launch_bounds__(kThreads8) void fa_fwd_varlen(
     return;
   }
   const int kend = CAUSAL ? min(nk, q0 + QT) : nk;
-  const PipeItem it = {0, q0, 0, (kend + kBN - 1) / kBN, -1};
+  const int nkt = (kend + kBN - 1) / kBN;
+  PipeItem it = {0, q0, 0, nkt, -1};
+  const int nch = varlen_chunks(nkt, NC, KC);
+  if (nch > 1) {  // split: this workgroup's chunk of the key tiles
+    const int kc = (nkt + nch - 1) / nch;
+    it.kt0 = chunk * kc;
+    if (chunk >= nch || it.kt0 >= nkt) return;
+    it.kt1 = min(nkt, it.kt0 + kc);
+    it.slot = varlen_slot(h, NT, NC, qa, q0, QT, sq, chunk);
+  } else if (chunk != 0) {
+    return;
+  }
   pipe8_run<T, OT, D, CAUSAL, PAIR>(q + qo * D, k + ko * D, v + ko * D, o + qo * D, lse + qo,
-                                    nullptr, nq, nk, c, negate, it, 0);
+                                    ws, nq, nk, c, negate, it, H * NT * NC);
 }
 
 // Chunk run by workgroup g: consecutive chunks go to one XCD (workgroups are
@@ -1163,6 +1200,87 @@ __global__ __launch_bounds__(kThreads) void fa_merge_stream(const float *__restr
     if (row < Nq) {
       store4<OT>(o + ((size_t)bh * Nq + row) * D + 4 * c4, acc[i] * (1.0f / lrs[i]));
       if (c4 == 0) lse[(size_t)bh * Nq + row] = (M[i] + log2f(ls[i])) * 0.69314718055994531f;
+    }
+  }
+}
+
+// Combines the key chunks of the split tiles of fa_fwd_varlen, one workgroup
+// per merge_rows<D>() rows of every (tile rank, head, sequence); tiles that
+// were not split (or lie past their sequence's end) return at once.  Same
+// rescaling as fa_merge_stream.
+template <typename OT, int D, bool CAUSAL, int QT>
+__global__ __launch_bounds__(kThreads) void fa_merge_varlen(
+    const float *__restrict__ ws, OT *__restrict__ o, float *__restrict__ lse,
+    const int *__restrict__ cu_q, const int *__restrict__ cu_k, int S, int H, int Tq,
+    int Tk, int NC, int KC, int NT) {
+  constexpr int C4 = D / 4;
+  constexpr int RPP = kThreads / C4;
+  constexpr int SPLIT = QT / merge_rows<D>();
+  constexpr int ROWS = merge_rows<D>();
+  constexpr int NR = ROWS / RPP;
+  static_assert(NR >= 1 && ROWS % RPP == 0, "merge tiling");
+  const int id = blockIdx.x / SPLIT;
+  const int qt = id / (H * S), hs = id % (H * S);
+  const int h = hs / S, sq = hs % S;
+  const int qa = max(0, min(cu_q[sq], Tq)), qb = max(qa, min(cu_q[sq + 1], Tq));
+  const int ka = max(0, min(cu_k[sq], Tk)), kb = max(ka, min(cu_k[sq + 1], Tk));
+  const int nq = qb - qa, nk = kb - ka;
+  const int q0 = qt * QT;
+  if (q0 >= nq || nk == 0) return;
+  const int kend = CAUSAL ? min(nk, q0 + QT) : nk;
+  const int nkt = (kend + kBN - 1) / kBN;
+  const int nch = varlen_chunks(nkt, NC, KC);
+  if (nch <= 1) return;  // written by its only workgroup
+  const int nslots = H * NT * NC;
+  const float *ws_s = ws + (size_t)nslots * QT * D;
+  const int c4 = threadIdx.x % C4;
+  const int r0 = (blockIdx.x % SPLIT) * ROWS + threadIdx.x / C4;
+  float M[NR], ls[NR], lrs[NR];
+  f32x4 acc[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    M[i] = -INFINITY;
+    ls[i] = lrs[i] = 0.f;
+    acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // four chunks per round trip: their loads are issued before any is used
+  constexpr int U = 4;
+  for (int ch = 0; ch < nch; ch += U) {
+    f32x4 st[U][NR], x[U][NR];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (ch + u >= nch) break;
+      const size_t slot = (size_t)varlen_slot(h, NT, NC, qa, q0, QT, sq, ch + u);
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const size_t e = slot * QT + r0 + i * RPP;
+        st[u][i] = *reinterpret_cast<const f32x4 *>(ws_s + e * 4);
+        x[u][i] = *reinterpret_cast<const f32x4 *>(ws + e * D + 4 * c4);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (ch + u >= nch) break;
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        if (st[u][i][0] == -INFINITY) continue;  // no key of this row in the chunk
+        const float Mn = fmaxf(M[i], st[u][i][0]);
+        const float a_old = exp2f(M[i] - Mn);  // 0 while M = -inf
+        const float a = exp2f(st[u][i][0] - Mn);
+        ls[i] = ls[i] * a_old + a * st[u][i][1];
+        lrs[i] = lrs[i] * a_old + a * st[u][i][2];
+        acc[i] = acc[i] * a_old + (a * st[u][i][2]) * x[u][i];
+        M[i] = Mn;
+      }
+    }
+  }
+  const size_t base = (size_t)h * Tq + qa + q0;
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int r = r0 + i * RPP;
+    if (q0 + r < nq) {
+      store4<OT>(o + (base + r) * D + 4 * c4, acc[i] * (1.0f / lrs[i]));
+      if (c4 == 0) lse[base + r] = (M[i] + log2f(ls[i])) * 0.69314718055994531f;
     }
   }
 }
@@ -1506,6 +1624,8 @@ struct VarlenArgs {
   int S, H, Tq, Tk, maxq;
   bool pair;  // pair-split 128-row tiles (D = 128 only)
   float c;
+  float *ws;        // partial results of split tiles (NC > 1)
+  int NC, KC, NT;   // chunks per tile at most, 64-key tiles per chunk at least, tile ids per head
   hipStream_t stream;
 };
 
@@ -1520,9 +1640,17 @@ hipError_t launch_varlen(const VarlenArgs &a) {
     constexpr int QT = QRows<PAIR>::value;
     const int ntiles = (a.maxq + QT - 1) / QT;
     hipLaunchKernelGGL((fa_fwd_varlen<T, OT, D, CAUSAL, PAIR>),
-                       dim3((unsigned)(ntiles * a.H * a.S)), dim3(kThreads8), 0, a.stream,
-                       (const T *)a.q, (const T *)a.k, (const T *)a.v, (OT *)a.o, a.lse,
-                       a.cu_q, a.cu_k, a.S, a.H, a.Tq, a.Tk, ntiles, c, neg);
+                       dim3((unsigned)(ntiles * a.H * a.S * a.NC)), dim3(kThreads8), 0,
+                       a.stream, (const T *)a.q, (const T *)a.k, (const T *)a.v, (OT *)a.o,
+                       a.lse, a.cu_q, a.cu_k, a.S, a.H, a.Tq, a.Tk, ntiles, c, neg, a.ws,
+                       a.NC, a.KC, a.NT);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.NC == 1) return e;
+    constexpr int SPLIT = QT / merge_rows<D>();
+    hipLaunchKernelGGL((fa_merge_varlen<OT, D, CAUSAL, QT>),
+                       dim3((unsigned)(ntiles * a.H * a.S * SPLIT)), dim3(kThreads), 0,
+                       a.stream, (const float *)a.ws, (OT *)a.o, a.lse, a.cu_q, a.cu_k, a.S,
+                       a.H, a.Tq, a.Tk, a.NC, a.KC, a.NT);
     return hipGetLastError();
   };
   if constexpr (D == 128)
@@ -1541,6 +1669,148 @@ hipError_t dispatch_varlen(const VarlenArgs &a, int D, bool causal) {
       return causal ? launch_varlen<T, OT, 128, true>(a) : launch_varlen<T, OT, 128, false>(a);
   }
 }
+
+// Shape checks of the varlen entry points (before any pointer is looked at).
+int varlen_shape(int64_t S, int64_t H, int64_t Tq, int64_t Tk, int64_t max_seqlen_q,
+                 int64_t max_seqlen_k, int64_t D, int dtype) {
+  if (S < 1 || H < 1 || Tq < 1 || Tk < 0 || max_seqlen_q < 1 || max_seqlen_k < 0)
+    return FA_ERR_SHAPE;
+  if (D != 16 && D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  if (dtype != FA_BF16 && dtype != FA_BF16_OF32 && dtype != FA_F16 && dtype != FA_F16_OF32)
+    return FA_ERR_DTYPE;
+  const int64_t lim = (int64_t)1 << 31;
+  // a sequence is addressed like a (batch, head) slice of fa_fwd
+  if (Tq > lim / (D * 4) - QRows<false>::value || Tk > lim / (D * 4) - 5 * kBN)
+    return FA_ERR_SHAPE;
+  const int64_t mq = max_seqlen_q < Tq ? max_seqlen_q : Tq;
+  const int64_t ntiles = (mq + kPairRows - 1) / kPairRows;  // the finer tiling
+  if (S > lim || H > lim || H * S > lim / ntiles || H * Tq > lim || H * Tk > lim)
+    return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+// Tile layout and key split of a varlen call.  Layout: at D = 128 the
+// pair-split 128-row tiles when the packed rows make fewer 256-row tiles
+// than there are compute units (the stream schedule's rule) and sequences
+// are long on average (measured on 32768 tokens, causal, unsplit: 8
+// sequences +9% with pair-split, 32 sequences -15%: short sequences are
+// dominated by the fixed cost of a tile, which the finer tiles double).
+// Split (max_seqlen_k > 0): the work is at most Tq * max_seqlen_q / 2
+// (causal) or Tq * max_seqlen_k row-key pairs, in units of one tile's rows
+// by 64 keys; a chunk gets at least that divided by the compute units (and
+// at least kMinChunk units, against the fixed cost of a piece), and a tile
+// at most kMaxChunks chunks.  With one chunk per tile nothing is split.
+struct VarlenSplit {
+  bool pair;
+  int NC, KC, NT;
+  size_t bytes;
+};
+constexpr int kMinChunk = 8;
+constexpr int kMaxChunks = 16;
+
+int varlen_plan(int64_t S, int64_t H, int64_t Tq, int64_t Tk, int64_t max_seqlen_q,
+                int64_t max_seqlen_k, int64_t D, bool causal, VarlenSplit &sp) {
+  int cus = 0;
+  const int st = device_cus(&cus);
+  if (st != FA_OK) return st;
+  sp.pair = D == 128 && H * ((Tq + QRows<false>::value - 1) / QRows<false>::value) < cus &&
+            Tq / S >= 2048;
+  sp.NC = 1;
+  sp.KC = 1;
+  sp.NT = 1;
+  sp.bytes = 0;
+  if (max_seqlen_k < 1) return FA_OK;
+  const int64_t QT = sp.pair ? kPairRows : QRows<false>::value;
+  const int64_t mq = max_seqlen_q < Tq ? max_seqlen_q : Tq;
+  const int64_t mk = max_seqlen_k < Tk ? max_seqlen_k : Tk;
+  // key tiles of the longest tile
+  const int64_t kmax = causal ? (mk < (mq + QT - 1) / QT * QT ? mk : (mq + QT - 1) / QT * QT) : mk;
+  const int64_t nkt = (kmax + kBN - 1) / kBN;
+  const int64_t pairs = causal ? Tq * mq / 2 : Tq * mk;  // row-key pairs, at most
+  const int64_t units = H * (pairs / (QT * kBN) + 1);
+  int64_t kc = (units + cus - 1) / cus;
+  if (kc < kMinChunk) kc = kMinChunk;
+  int64_t nc = (nkt + kc - 1) / kc;
+  if (nc > kMaxChunks) nc = kMaxChunks;
+  if (nc < 2) return FA_OK;
+  const int64_t NT = (Tq + QT - 1) / QT + S;
+  if (H * NT * nc >= ((int64_t)1 << 31) / QT) return FA_OK;  // slot indices stay in int
+  sp.NC = (int)nc;
+  sp.KC = (int)kc;
+  sp.NT = (int)NT;
+  sp.bytes = (size_t)(H * NT * nc) * (size_t)QT * (size_t)(D + 4) * 4;
+  return FA_OK;
+}
+
+int varlen_entry(const void *q, const void *k, const void *v, void *o, float *lse,
+                 const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int64_t S,
+                 int64_t H, int64_t Tq, int64_t Tk, int64_t max_seqlen_q, int64_t max_seqlen_k,
+                 int64_t D, float scale, int causal, int dtype, void *workspace,
+                 size_t workspace_bytes, bool split, void *stream) {
+  if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k) return FA_ERR_NULLPTR;
+  int st = varlen_shape(S, H, Tq, Tk, max_seqlen_q, split ? max_seqlen_k : 0, D, dtype);
+  if (st != FA_OK) return st;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (max_seqlen_q > Tq) max_seqlen_q = Tq;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA_ERR_ALIGN;
+  if (((uintptr_t)lse | (uintptr_t)cu_seqlens_q | (uintptr_t)cu_seqlens_k) & 3u)
+    return FA_ERR_ALIGN;
+  const size_t out_size = (dtype == FA_BF16_OF32 || dtype == FA_F16_OF32) ? 4 : 2;
+  const size_t qb = (size_t)(H * Tq * D * 2), kb = (size_t)(H * Tk * D * 2);
+  const size_t ob = (size_t)(H * Tq * D) * out_size, lb = (size_t)(H * Tq * 4);
+  const size_t cb = (size_t)(S + 1) * 4;
+  const void *outs[3] = {o, lse, workspace};
+  size_t osz[3] = {ob, lb, 0};
+  const void *ins[5] = {q, k, v, cu_seqlens_q, cu_seqlens_k};
+  const size_t isz[5] = {qb, kb, kb, cb, cb};
+  for (int x = 0; x < 2; ++x)
+    for (int y = 0; y < 5; ++y)
+      if (overlaps(outs[x], osz[x], ins[y], isz[y])) return FA_ERR_OVERLAP;
+  if (overlaps(o, ob, lse, lb)) return FA_ERR_OVERLAP;
+  VarlenSplit sp;
+  st = varlen_plan(S, H, Tq, Tk, max_seqlen_q, split ? max_seqlen_k : 0, D, causal != 0, sp);
+  if (st != FA_OK) return st;
+  if (sp.bytes > 0) {
+    if (!workspace || workspace_bytes < sp.bytes) return FA_ERR_WORKSPACE;
+    if ((uintptr_t)workspace & 15u) return FA_ERR_ALIGN;
+    osz[2] = sp.bytes;
+    for (int y = 0; y < 5; ++y)
+      if (overlaps(workspace, sp.bytes, ins[y], isz[y])) return FA_ERR_OVERLAP;
+    for (int x = 0; x < 2; ++x)
+      if (overlaps(outs[x], osz[x], workspace, sp.bytes)) return FA_ERR_OVERLAP;
+  }
+  VarlenArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.S = (int)S;
+  a.H = (int)H;
+  a.Tq = (int)Tq;
+  a.Tk = (int)Tk;
+  a.maxq = (int)max_seqlen_q;
+  a.pair = sp.pair;
+  a.c = scale * 1.4426950408889634f;
+  a.ws = sp.bytes > 0 ? (float *)workspace : nullptr;
+  a.NC = sp.NC;
+  a.KC = sp.KC;
+  a.NT = sp.NT;
+  a.stream = (hipStream_t)stream;
+  const bool cz = causal != 0;
+  hipError_t e;
+  switch (dtype) {
+    case FA_BF16: e = dispatch_varlen<__bf16, __bf16>(a, (int)D, cz); break;
+    case FA_BF16_OF32: e = dispatch_varlen<__bf16, float>(a, (int)D, cz); break;
+    case FA_F16: e = dispatch_varlen<_Float16, _Float16>(a, (int)D, cz); break;
+    default: e = dispatch_varlen<_Float16, float>(a, (int)D, cz); break;
+  }
+  if (e != hipSuccess) return hip_fail(e);
+  return FA_OK;
+}
+
 
 }  // namespace
 
@@ -1564,7 +1834,7 @@ const char *fa_status_str(int s) {
     case FA_ERR_ALIGN: return "misaligned pointer (q, k, v, o, workspace need 16 bytes, lse 4)";
     case FA_ERR_HIP: return "HIP runtime error";
     case FA_ERR_OVERLAP: return "output or workspace buffers overlap each other or the inputs";
-    case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_fwd_workspace_size";
+    case FA_ERR_WORKSPACE: return "workspace missing or smaller than its workspace-size query reports";
     default: return "unknown status";
   }
 }
@@ -1630,70 +1900,32 @@ int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *l
                   const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int64_t S,
                   int64_t H, int64_t Tq, int64_t Tk, int64_t max_seqlen_q, int64_t D,
                   float scale, int causal, int dtype, void *stream) {
-  if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k) return FA_ERR_NULLPTR;
-  if (S < 1 || H < 1 || Tq < 1 || Tk < 0 || max_seqlen_q < 1) return FA_ERR_SHAPE;
-  if (D != 16 && D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
-  if (dtype != FA_BF16 && dtype != FA_BF16_OF32 && dtype != FA_F16 && dtype != FA_F16_OF32)
-    return FA_ERR_DTYPE;
-  if (!isfinite(scale)) return FA_ERR_SCALE;
-  const int64_t lim = (int64_t)1 << 31;
-  // a sequence is addressed like a (batch, head) slice of fa_fwd
-  if (Tq > lim / (D * 4) - QRows<false>::value || Tk > lim / (D * 4) - 5 * kBN)
-    return FA_ERR_SHAPE;
-  if (max_seqlen_q > Tq) max_seqlen_q = Tq;
-  const int64_t ntiles = (max_seqlen_q + kPairRows - 1) / kPairRows;  // the finer tiling
-  if (S > lim || H > lim || H * S > lim / ntiles || H * Tq > lim || H * Tk > lim)
-    return FA_ERR_SHAPE;
-  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA_ERR_ALIGN;
-  if (((uintptr_t)lse | (uintptr_t)cu_seqlens_q | (uintptr_t)cu_seqlens_k) & 3u)
-    return FA_ERR_ALIGN;
-  const size_t out_size = (dtype == FA_BF16_OF32 || dtype == FA_F16_OF32) ? 4 : 2;
-  const size_t qb = (size_t)(H * Tq * D * 2), kb = (size_t)(H * Tk * D * 2);
-  const size_t ob = (size_t)(H * Tq * D) * out_size, lb = (size_t)(H * Tq * 4);
-  const size_t cb = (size_t)(S + 1) * 4;
-  const void *outs[2] = {o, lse};
-  const size_t osz[2] = {ob, lb};
-  const void *ins[5] = {q, k, v, cu_seqlens_q, cu_seqlens_k};
-  const size_t isz[5] = {qb, kb, kb, cb, cb};
-  for (int x = 0; x < 2; ++x)
-    for (int y = 0; y < 5; ++y)
-      if (overlaps(outs[x], osz[x], ins[y], isz[y])) return FA_ERR_OVERLAP;
-  if (overlaps(o, ob, lse, lb)) return FA_ERR_OVERLAP;
-  VarlenArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
-  a.lse = lse;
-  a.cu_q = cu_seqlens_q;
-  a.cu_k = cu_seqlens_k;
-  a.S = (int)S;
-  a.H = (int)H;
-  a.Tq = (int)Tq;
-  a.Tk = (int)Tk;
-  a.maxq = (int)max_seqlen_q;
-  // at D = 128, the pair-split layout when the packed rows make fewer
-  // 256-row tiles than there are compute units (the stream schedule's rule)
-  // and sequences are long on average (measured on 32768 tokens, causal:
-  // 8 sequences +9% with pair-split, 32 sequences -15%: short sequences
-  // are dominated by the fixed cost of a tile, which the finer tiles double)
-  int cus = 0;
-  const int st = device_cus(&cus);
+  return varlen_entry(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, S, H, Tq, Tk, max_seqlen_q,
+                      0, D, scale, causal, dtype, nullptr, 0, false, stream);
+}
+
+int fa_fwd_varlen_workspace_size(int64_t S, int64_t H, int64_t Tq, int64_t Tk,
+                                 int64_t max_seqlen_q, int64_t max_seqlen_k, int64_t D,
+                                 int causal, int dtype, size_t *bytes) {
+  if (!bytes) return FA_ERR_NULLPTR;
+  *bytes = 0;
+  int st = varlen_shape(S, H, Tq, Tk, max_seqlen_q, max_seqlen_k, D, dtype);
   if (st != FA_OK) return st;
-  a.pair = D == 128 && H * ((Tq + QRows<false>::value - 1) / QRows<false>::value) < cus &&
-           Tq / S >= 2048;
-  a.c = scale * 1.4426950408889634f;
-  a.stream = (hipStream_t)stream;
-  const bool cz = causal != 0;
-  hipError_t e;
-  switch (dtype) {
-    case FA_BF16: e = dispatch_varlen<__bf16, __bf16>(a, (int)D, cz); break;
-    case FA_BF16_OF32: e = dispatch_varlen<__bf16, float>(a, (int)D, cz); break;
-    case FA_F16: e = dispatch_varlen<_Float16, _Float16>(a, (int)D, cz); break;
-    default: e = dispatch_varlen<_Float16, float>(a, (int)D, cz); break;
-  }
-  if (e != hipSuccess) return hip_fail(e);
+  VarlenSplit sp;
+  st = varlen_plan(S, H, Tq, Tk, max_seqlen_q, max_seqlen_k, D, causal != 0, sp);
+  if (st != FA_OK) return st;
+  *bytes = sp.bytes;
   return FA_OK;
+}
+
+int fa_fwd_varlen_ws(const void *q, const void *k, const void *v, void *o, float *lse,
+                     const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int64_t S,
+                     int64_t H, int64_t Tq, int64_t Tk, int64_t max_seqlen_q,
+                     int64_t max_seqlen_k, int64_t D, float scale, int causal, int dtype,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+  return varlen_entry(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, S, H, Tq, Tk, max_seqlen_q,
+                      max_seqlen_k, D, scale, causal, dtype, workspace, workspace_bytes, true,
+                      stream);
 }
 
 }  // extern "C"
