@@ -220,6 +220,39 @@ def test_varlen_validation(kw, status):
     assert call_varlen(**kw) == getattr(fa, status)
 
 
+def call_varlen_ws(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, cq=CQ, ck=CK, S=3, H=2, Tq=500, Tk=400, mq=300, mk=300,
+             D=64, scale=0.125, causal=1, dtype=fa.FA_BF16, ws=None, nb=0, stream=None)
+    a.update(kw)
+    return fa.fa_fwd_varlen_ws(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"],
+                               a["S"], a["H"], a["Tq"], a["Tk"], a["mq"], a["mk"], a["D"],
+                               a["scale"], a["causal"], a["dtype"], a["ws"], a["nb"],
+                               a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"q": None}, "FA_ERR_NULLPTR"), ({"ck": None}, "FA_ERR_NULLPTR"),
+    ({"S": 0}, "FA_ERR_SHAPE"), ({"mk": -1}, "FA_ERR_SHAPE"), ({"mq": 0}, "FA_ERR_SHAPE"),
+    ({"D": 8}, "FA_ERR_HEAD_DIM"), ({"dtype": fa.FA_F32}, "FA_ERR_DTYPE"),
+    ({"scale": math.inf}, "FA_ERR_SCALE"), ({"lse": L + 2}, "FA_ERR_ALIGN"),
+    ({"o": K}, "FA_ERR_OVERLAP"), ({"lse": O}, "FA_ERR_OVERLAP"),
+])
+def test_varlen_ws_validation(kw, status):
+    """fa_fwd_varlen_ws checks its arguments before it looks at the device."""
+    assert call_varlen_ws(**kw) == getattr(fa, status)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 1, 100, 100, 100, 100, 64, 1, 1), "FA_ERR_SHAPE"),
+    ((1, 1, 100, 100, 100, -1, 64, 1, 1), "FA_ERR_SHAPE"),
+    ((1, 1, 100, 100, 100, 100, 24, 1, 1), "FA_ERR_HEAD_DIM"),
+    ((1, 1, 100, 100, 100, 100, 64, 1, 0), "FA_ERR_DTYPE"),
+])
+def test_varlen_workspace_size_validation(args, status):
+    st, nb = fa.fa_fwd_varlen_workspace_size(*args)
+    assert st == getattr(fa, status) and nb == 0
+
+
 def call_bwd_varlen(**kw):
     a = dict(q=Q, k=K, v=V, o=O, lse=L, do=DO, dq=DQ, dk=DK, dv=DV, cq=CQ, ck=CK, S=3, H=2,
              Tq=500, Tk=400, mq=300, mk=200, D=64, scale=0.125, causal=1, dtype=fa.FA_BF16,
