@@ -206,8 +206,8 @@ def test_varlen_split_fp16_negative_scale():
 def test_varlen_split_underestimated_keys():
     """max_seqlen_k below the real longest key range: the chunks of a tile
     grow (at most the planned count per tile) and every key is still seen."""
-    compare(SPLIT, SPLIT, 2, 128, True, seed=2400, maxk=700)
-    compare(SPLIT, SPLIT, 2, 128, False, seed=2401, maxk=700)
+    compare(SPLIT, SPLIT, 2, 128, True, seed=2400, maxk=1500)
+    compare(SPLIT, SPLIT, 2, 128, False, seed=2401, maxk=1500)
 
 
 def test_varlen_split_matches_unsplit_on_short_tiles():
@@ -221,13 +221,29 @@ def test_varlen_split_matches_unsplit_on_short_tiles():
     assert torch.equal(a[0][:, s], b[0][:, s]) and torch.equal(a[1][:, s], b[1][:, s])
 
 
-@pytest.mark.parametrize("S", [8, 32])
-def test_varlen_split_32k_tokens_sampled(S):
-    """The shapes bench.py --varlen S --split times (32768 tokens, D=128,
-    causal bf16): 512 sampled rows against the oracle."""
-    lens = varlen_lengths(32768, S, seed=77, min_len=64)
-    rows = sample_rows(32768, 512, 7800 + S).numpy()
-    compare(lens, lens, 1, 128, True, seed=1800 + S, rows=rows, maxk=max(lens))
+def test_varlen_split_32k_tokens_sampled():
+    """The shape bench.py --varlen 32 --split times (32768 tokens in 32
+    sequences, D=128, causal bf16): 512 sampled rows against the oracle."""
+    lens = varlen_lengths(32768, 32, seed=77, min_len=64)
+    rows = sample_rows(32768, 512, 7832).numpy()
+    compare(lens, lens, 1, 128, True, seed=1832, rows=rows, maxk=max(lens))
+
+
+def test_varlen_split_one_long_sequence_sampled():
+    """One 16384-token sequence beside three short ones (pair-split tiles,
+    the longest cut into many chunks): 512 sampled rows."""
+    lens = [16384, 100, 1000, 3000]
+    rows = sample_rows(sum(lens), 512, 7900).numpy()
+    compare(lens, lens, 1, 128, True, seed=1900, rows=rows, maxk=max(lens))
+
+
+def test_varlen_split_not_taken_for_two_shares():
+    """32768 tokens in 8 sequences: the longest tile makes two shares, too few
+    to split (workspace 0; fa_fwd_varlen_ws is then fa_fwd_varlen)."""
+    lens = varlen_lengths(32768, 8, seed=77, min_len=64)
+    st, nb = fa.fa_fwd_varlen_workspace_size(8, 1, 32768, 32768, max(lens), max(lens), 128,
+                                             True, fa.FA_BF16)
+    assert st == 0 and nb == 0
 
 
 # --- backward over variable-length batches (fa_bwd_varlen) ------------------
