@@ -246,6 +246,53 @@ def test_varlen_split_not_taken_for_two_shares():
     assert st == 0 and nb == 0
 
 
+def test_varlen_split_graph_capture_replays_match_eager():
+    """Both kernels of fa_fwd_varlen_ws are plain launches on the caller's
+    stream (no allocation, no memset), so a HIP graph captured around the
+    call replays it: every replay, with eager work on the same buffers in
+    between and stale workspace contents, gives the eager result bit for
+    bit."""
+    lens = [3000, 700, 1, 1200, 64]
+    H, D, T = 2, 128, sum(lens)
+    q, k, v, cu_q, cu_k = (t.to(DEV) for t in packed(lens, lens, H, D, 3100))
+    st, nb = fa.fa_fwd_varlen_workspace_size(len(lens), H, T, T, max(lens), max(lens), D, True,
+                                             fa.FA_BF16)
+    assert st == fa.FA_OK and nb > 0
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=DEV)
+
+    def call():
+        r = fa.fa_fwd_varlen_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                lse.data_ptr(), cu_q.data_ptr(), cu_k.data_ptr(), len(lens), H,
+                                T, T, max(lens), max(lens), D, 0.125, True, fa.FA_BF16,
+                                ws.data_ptr(), nb, torch.cuda.current_stream().cuda_stream)
+        assert r == fa.FA_OK, fa.fa_status_str(r)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    want_o, want_l = o.clone(), lse.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for i in range(3):
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        ws.fill_(i + 1)  # stale partials must not leak into a replay
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, want_o), f"replay {i}: O differs from the eager call"
+        assert torch.equal(lse, want_l), f"replay {i}: L differs from the eager call"
+        call()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(o, want_o) and torch.equal(lse, want_l)
+
+
 # --- backward over variable-length batches (fa_bwd_varlen) ------------------
 def compare_bwd(lq, lk, H, D, causal, seed, dtype="bf16"):
     """Gradients against the oracle (per sequence, with the backward's
