@@ -366,8 +366,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq(
   __shared__ __attribute__((aligned(16))) char smem_raw[4 * BB];
   lds_char *smem = (lds_char *)smem_raw;
 
-  // causal: the last query tiles see the most keys: first
-  const Slice sl = resolve(BH, Nq, Nk, cu_q, cu_k, S, CAUSAL, nqt);
+  // causal (also a causal mask): the last query tiles see the most keys: first
+  const Slice sl = resolve(BH, Nq, Nk, cu_q, cu_k, S, CAUSAL || (MASKED && mk.causal), nqt);
   Nq = sl.Nq;
   Nk = sl.Nk;
   const int qt = sl.tile;

@@ -66,7 +66,9 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_masked(
   lds_char *smem = (lds_char *)smem_raw;
 
   const int bh = blockIdx.x % BH;
-  const int qt = blockIdx.x / BH;
+  // causal: later query tiles see more keys (up to the window): first
+  const int rank = blockIdx.x / BH;
+  const int qt = mk.causal ? nqt - 1 - rank : rank;
   const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
   const int g = lane >> 5, col = lane & 31;
   const int q0 = qt * kQTile;
