@@ -5,11 +5,14 @@
 // visible" (it is meant to be exact) and `all` never holds for a block with a
 // hidden pair; it also holds for every single visible pair and for every
 // block the local band or the global part covers on its own.  The block
-// sizes the kernels use (32, 64, 128) are checked on larger offsets.  Prints
+// sizes the kernels use (32, 64, 128) are checked on larger offsets, and the
+// band-only test (Mask::band) equals the rule wherever the global part is
+// out of play.  Prints
 // "ok <blocks checked>" or the first failure; exit status 0 on success.
 #include "../../transformer_attention_07_amd/csrc/mask.h"
 
 #include <cstdio>
+#include <initializer_list>
 
 namespace {
 
@@ -55,9 +58,38 @@ int check_block(const Mask &m, int ilo, int ihi, int jlo, int jhi) {
   return 0;
 }
 
+// The band test against the full rule where the global part is out of play
+// (i, j >= nglobal), over small windows and large offsets both ways.
+int check_band() {
+  const int windows[] = {1, 2, 3, 31, 32, 33, 512, 4096, 1 << 20, 1 << 22};
+  const int offs[] = {0, 1, 5, 100, 4095, 65536, (1 << 22) - 1};
+  for (int causal = 0; causal < 2; ++causal)
+    for (int w : windows)
+      for (int ng : {0, 7}) {
+        const Mask m{causal, w, ng};
+        for (int base : offs)
+          for (int a = 0; a < 40; ++a)
+            for (int b = 0; b < 40; ++b) {
+              const int i = ng + base + a, j = ng + b;
+              const int i2 = ng + a, j2 = ng + base + b;  // keys far ahead
+              for (int t = 0; t < 2; ++t) {
+                const int x = t ? i2 : i, y = t ? j2 : j;
+                ++checked;
+                if (m.band(x, y) != m.visible(x, y)) {
+                  std::printf("FAIL band causal=%d window=%d nglobal=%d i=%d j=%d\n", causal,
+                              w, ng, x, y);
+                  return 1;
+                }
+              }
+            }
+      }
+  return 0;
+}
+
 }  // namespace
 
 int main() {
+  if (check_band()) return 1;
   // Every block inside a 14 x 14 square, all small masks.
   const int n = 14;
   for (int causal = 0; causal < 2; ++causal)

@@ -141,6 +141,15 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_masked(
           s[r] *= c;
           mx = fmaxf(mx, s[r]);
         }
+      } else if (jq + kOwn <= Nk && qw0 >= mk.nglobal && jq >= mk.nglobal) {
+        // wave-uniform: no key tail and no global row or key: the band alone
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = jq + 8 * (r >> 2) + 4 * g + (r & 3);
+          const float x = mk.band(myq, j) ? s[r] * c : -INFINITY;
+          s[r] = x;
+          mx = fmaxf(mx, x);
+        }
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -267,7 +276,10 @@ int fa_fwd_masked(const void *q, const void *k, const void *v, void *o, float *l
     return FA_ERR_OVERLAP;
   Mask mk;
   mk.causal = causal != 0;
-  mk.window = (int)(window < lim ? window : lim - 1);
+  // a window of max(Nq, Nk) already covers every |i - j|; the clamp keeps
+  // the band test's unsigned arithmetic exact
+  const int64_t wmax = Nq > Nk ? Nq : Nk;
+  mk.window = (int)(window < wmax ? window : wmax);
   mk.nglobal = (int)(nglobal < lim ? nglobal : lim - 1);
   const float c = scale * kLog2e;
   hipStream_t s = (hipStream_t)stream;

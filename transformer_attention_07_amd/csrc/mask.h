@@ -33,6 +33,16 @@ struct Mask {
     const bool global = (j < nglobal || i < nglobal) && (!causal || j <= i);
     return local || global;
   }
+  // The band alone: visible(i, j) for i, j >= nglobal, where the global part
+  // is false.  One subtraction and one unsigned compare: i - j wraps to a
+  // large value when negative (causal), and |d| < window is d + window - 1
+  // in [0, 2 window - 2].  Exact while |i - j| + 3 window < 2^32 (callers
+  // clamp window to max(Nq, Nk)).
+  FA_MASK_FN bool band(int i, int j) const {
+    const unsigned d = (unsigned)(i - j);
+    return causal ? d < (unsigned)window
+                  : d + (unsigned)(window - 1) < 2u * (unsigned)window - 1u;
+  }
   // Is some pair of queries [ilo, ihi] x keys [jlo, jhi] visible?  Exact:
   // i - j takes every value in [ilo - jhi, ihi - jlo], so the band is hit iff
   // that interval meets it.  Global part: the lowest key jlo against the
