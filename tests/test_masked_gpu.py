@@ -76,6 +76,15 @@ def test_masked_patterns(D, causal, window, nglobal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("window", [2 ** 31 - 1, 2 ** 40])
+def test_masked_huge_window(window, causal):
+    """Windows far beyond max(Nq, Nk) (clamped by the library, which keeps
+    its band arithmetic exact) see every key the dense rule allows."""
+    compare(1, 2, 300, 500, 64, causal, window, 0, seed=2250 + causal)
+    compare(1, 1, 500, 300, 128, causal, window, 7, seed=2260 + causal)
+
+
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("Nq,Nk", [(500, 300), (300, 500), (1, 1), (129, 3)])
 def test_masked_unequal_lengths(Nq, Nk, causal):
     """Nq > Nk leaves rows without keys under a causal window."""
