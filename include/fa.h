@@ -170,8 +170,11 @@ int fa_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse,
  *              non-decreasing, ending at Tq / Tk
  *   S, H       number of sequences (>= 1) and heads (>= 1)
  *   Tq, Tk     total query rows (>= 1) and key rows (>= 0)
- *   max_seqlen_q  an upper bound of every query length (rows of a longer
- *              sequence past this bound are not computed)
+ *   max_seqlen_q  an upper bound of every query length.  A sequence longer
+ *              than it is computed up to the end of the query tile that
+ *              holds row max_seqlen_q - 1 (128 or 256 rows); its rows past
+ *              that tile get O = NaN and lse = NaN, so no row is left
+ *              unwritten
  *   D, scale, causal   as fa_fwd; the causal rule applies within each
  *              sequence: key j of a sequence is visible to its row i iff
  *              j <= i (indices from the sequence's first row)
@@ -365,8 +368,10 @@ int fa_bwd_masked(const void *q, const void *k, const void *v, const void *o,
  * cu_seqlens_k[s] .. cu_seqlens_k[s+1] - 1), offsets in device memory
  * (S + 1 int32 each, 0 .. Tq / Tk, non-decreasing; the kernels clamp them
  * to the tensors).  max_seqlen_q and max_seqlen_k bound every sequence's
- * query and key count (rows of longer sequences past them are not
- * computed).  Each sequence's gradients are exactly fa_bwd's for that
+ * query and key count: a longer sequence is computed up to the end of the
+ * 64-row tile that holds row max_seqlen_q - 1 (key max(max_seqlen_k, 1) - 1),
+ * and its dq rows (dk and dv rows) past that tile are set to NaN, so no row
+ * is left unwritten.  Each sequence's gradients are exactly fa_bwd's for that
  * sequence alone; keys that no query sees get dk = dv = 0, queries without
  * keys get dq = 0.  The workspace needs H * Tq * 4 bytes (what
  * fa_bwd_workspace_size reports for B = 1, Nq = Tq).  Other arguments,

@@ -32,9 +32,11 @@ Functions (all fp64, numpy in / numpy out):
       -> (o, lse): attention under a local-window + global-token mask
       ("FlashAttention-2实现与优化" §7 sparse attention; the pattern is this
       package's reading, stated in fa_oracle.c).
-  attention_bwd_masked(q, k, v, do, scale, causal, window, nglobal)
-      -> (dq, dk, dv): the gradients of attention_masked (chain rule over the
-      visible pairs).
+  attention_bwd_masked(q, k, v, do, scale, causal, window, nglobal,
+                       qrows=None, krows=None, magnitudes=False)
+      -> (dq, dk, dv[, bq, bk, bv]): the gradients of attention_masked (chain
+      rule over the visible pairs), with the row sampling and magnitude sums
+      of attention_bwd.
   threads() -> int   OpenMP threads the oracle uses.
 
 Parity status: pinned by tests/test_oracle_pins.py (closed forms, invariants,
@@ -88,9 +90,11 @@ def _bind(path: str):
                                                ctypes.c_double, ctypes.c_int, i64, i64,
                                                ctypes.POINTER(i64), i64]
     lib.fa_oracle_attention_bwd_masked.restype = ctypes.c_int
-    lib.fa_oracle_attention_bwd_masked.argtypes = [dp, dp, dp, dp, dp, dp, dp, i64, i64, i64,
-                                                   i64, i64, ctypes.c_double, ctypes.c_int,
-                                                   i64, i64]
+    lib.fa_oracle_attention_bwd_masked.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, dp,
+                                                   i64, i64, i64, i64, i64,
+                                                   ctypes.c_double, ctypes.c_int, i64, i64,
+                                                   ctypes.POINTER(i64), i64,
+                                                   ctypes.POINTER(i64), i64]
     lib.fa_oracle_threads.restype = ctypes.c_int
     lib.fa_oracle_threads.argtypes = []
     return lib
@@ -297,8 +301,10 @@ def attention_masked(q, k, v, scale: float, causal: bool, window: int, nglobal: 
 
 
 def attention_bwd_masked(q, k, v, do, scale: float, causal: bool, window: int, nglobal: int,
-                         lib=None):
-    """fp64 gradients of attention_masked for upstream gradient do."""
+                         qrows=None, krows=None, magnitudes: bool = False, lib=None):
+    """fp64 gradients of attention_masked for upstream gradient do; row
+    lists and magnitude sums as attention_bwd (every sum over the visible
+    pairs)."""
     lib = lib or load()
     squeeze = np.asarray(q).ndim == 3
     q4, k4, v4, g4 = _as4d(q), _as4d(k), _as4d(v), _as4d(do)
@@ -306,15 +312,26 @@ def attention_bwd_masked(q, k, v, do, scale: float, causal: bool, window: int, n
     Nk = k4.shape[2]
     if k4.shape != (B, H, Nk, D) or v4.shape != (B, H, Nk, D) or g4.shape != q4.shape:
         raise ValueError("q/k/v/do shapes disagree")
-    dq, dk, dv = np.empty(q4.shape), np.empty(k4.shape), np.empty(k4.shape)
+    qa, qp, nq = _rowlist(qrows)
+    ka, kp, nk = _rowlist(krows)
+    qshape = (B, H, Nq, D) if qa is None else (nq, D)
+    kshape = (B, H, Nk, D) if ka is None else (nk, D)
+    dq, dk, dv = np.empty(qshape), np.empty(kshape), np.empty(kshape)
+    if magnitudes:
+        bq, bk, bv = np.empty(qshape), np.empty(kshape), np.empty(kshape)
+        mp = (_ptr(bq), _ptr(bk), _ptr(bv))
+    else:
+        mp = (None, None, None)
     st = lib.fa_oracle_attention_bwd_masked(_ptr(q4), _ptr(k4), _ptr(v4), _ptr(g4), _ptr(dq),
-                                            _ptr(dk), _ptr(dv), B, H, Nq, Nk, D, float(scale),
-                                            int(bool(causal)), int(window), int(nglobal))
+                                            _ptr(dk), _ptr(dv), *mp, B, H, Nq, Nk, D,
+                                            float(scale), int(bool(causal)), int(window),
+                                            int(nglobal), qp, nq, kp, nk)
     if st != 0:
         raise RuntimeError(f"oracle failed with status {st}")
+    out = [dq, dk, dv] + ([bq, bk, bv] if magnitudes else [])
     if squeeze:
-        return dq[:, 0], dk[:, 0], dv[:, 0]
-    return dq, dk, dv
+        out = [a[:, 0] if a.ndim == 4 else a for a in out]
+    return tuple(out)
 
 
 def threads(lib=None) -> int:

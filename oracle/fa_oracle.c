@@ -565,10 +565,9 @@ int fa_oracle_attention_masked(const double *q, const double *k, const double *v
             for (int64_t c = 0; c < n; ++c)
                 for (int64_t d = 0; d < D; ++d)
                     oi[d] += w[c] * vb[idx[c] * D + d];
-            const double inv = 1.0 / l;
             for (int64_t d = 0; d < D; ++d)
-                oi[d] *= inv;
-            lse[t] = log(l) + m;
+                oi[d] /= l;
+            lse[t] = m + log(l);
         }
         free(w);
         free(idx);
@@ -583,33 +582,72 @@ int fa_oracle_attention_masked(const double *q, const double *k, const double *v
  *     dV_j = sum_i P_ij dO_i,  dP_ij = <dO_i, v_j>,  D_i = sum_j P_ij dP_ij,
  *     dS_ij = P_ij (dP_ij - D_i),
  *     dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i.
- * Rows with no visible key contribute nothing (dQ_i = 0).  Full outputs
- * only (no row lists).
+ * Rows with no visible key contribute nothing (dQ_i = 0).  The magnitude
+ * sums bq, bk, bv (may be NULL) and the row lists qrows / krows are those of
+ * fa_oracle_attention_bwd, with every sum over the visible pairs: they bound
+ * the effect of rounding one factor of every product, and the row lists
+ * restrict the outputs to sampled rows (statistics are computed for every
+ * row of each (b, h) slice that holds a requested row).
  */
 int fa_oracle_attention_bwd_masked(const double *q, const double *k, const double *v,
                                    const double *dout, double *dq, double *dk, double *dv,
+                                   double *bq, double *bk, double *bv,
                                    int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
-                                   double scale, int causal, int64_t window, int64_t nglobal)
+                                   double scale, int causal, int64_t window, int64_t nglobal,
+                                   const int64_t *qrows, int64_t nq,
+                                   const int64_t *krows, int64_t nk)
 {
     if (!q || !k || !v || !dout || !dq || !dk || !dv || bad_shape(B, H, Nq, Nk, D) ||
         window < 1 || nglobal < 0)
         return ORACLE_EINVAL;
     const int64_t totq = B * H * Nq, totk = B * H * Nk;
+    if (qrows)
+        for (int64_t t = 0; t < nq; ++t)
+            if (qrows[t] < 0 || qrows[t] >= totq)
+                return ORACLE_EINVAL;
+    if (krows)
+        for (int64_t t = 0; t < nk; ++t)
+            if (krows[t] < 0 || krows[t] >= totk)
+                return ORACLE_EINVAL;
+    const int64_t cq = qrows ? nq : totq;
+    const int64_t ck = krows ? nk : totk;
+    const int magn = bq && bk && bv;
     double *m = (double *)malloc((size_t)totq * sizeof(double));
     double *l = (double *)malloc((size_t)totq * sizeof(double));
     double *rd = (double *)malloc((size_t)totq * sizeof(double));
-    if (!m || !l || !rd) {
+    double *re = (double *)malloc((size_t)totq * sizeof(double));
+    unsigned char *need = (unsigned char *)calloc((size_t)(B * H), 1);
+    if (!m || !l || !rd || !re || !need) {
         free(m);
         free(l);
         free(rd);
+        free(re);
+        free(need);
         return ORACLE_ENOMEM;
     }
+    if (!qrows || !krows)
+        memset(need, 1, (size_t)(B * H));
+    else {
+        for (int64_t t = 0; t < nq; ++t)
+            need[qrows[t] / Nq] = 1;
+        for (int64_t t = 0; t < nk; ++t)
+            need[krows[t] / Nk] = 1;
+    }
+    int failed = 0;
 
 #pragma omp parallel
     {
-        /* every query row: max, normaliser and the row term D_i */
+        double *o = (double *)malloc((size_t)D * sizeof(double));
+        if (!o) {
+#pragma omp atomic write
+            failed = 1;
+        }
+        /* pass 1, every query row of the needed slices: max m, normaliser l,
+           row term D_i and E_i = sum_d |dO_id| sum_j P_ij |v_jd| */
 #pragma omp for schedule(dynamic, 8)
         for (int64_t r = 0; r < totq; ++r) {
+            if (!o || !need[r / Nq])
+                continue;
             const int64_t bh = r / Nq, i = r % Nq;
             const double *qi = q + r * D, *gi = dout + r * D;
             const double *kb = k + bh * Nk * D, *vb = v + bh * Nk * D;
@@ -623,8 +661,19 @@ int fa_oracle_attention_bwd_masked(const double *q, const double *k, const doubl
                 if (scale * dot > mx)
                     mx = scale * dot;
             }
-            double sum = 0.0, acc = 0.0;
+            double sum = 0.0;
             for (int64_t j = 0; j < Nk; ++j) {
+                if (!visible_masked(i, j, causal, window, nglobal))
+                    continue;
+                double dot = 0.0;
+                for (int64_t d = 0; d < D; ++d)
+                    dot += qi[d] * kb[j * D + d];
+                sum += exp(scale * dot - mx);
+            }
+            double acc = 0.0;
+            for (int64_t d = 0; d < D; ++d)
+                o[d] = 0.0;
+            for (int64_t j = 0; j < Nk && sum > 0.0; ++j) {
                 if (!visible_masked(i, j, causal, window, nglobal))
                     continue;
                 double dot = 0.0, dp = 0.0;
@@ -632,25 +681,36 @@ int fa_oracle_attention_bwd_masked(const double *q, const double *k, const doubl
                     dot += qi[d] * kb[j * D + d];
                     dp += gi[d] * vb[j * D + d];
                 }
-                const double e = exp(scale * dot - mx);
-                sum += e;
-                acc += e * dp;
+                const double p = exp(scale * dot - mx) / sum;
+                for (int64_t d = 0; d < D; ++d)
+                    o[d] += p * fabs(vb[j * D + d]);
+                acc += p * dp;
             }
+            double e = 0.0;
+            for (int64_t d = 0; d < D; ++d)
+                e += fabs(gi[d]) * o[d];
             m[r] = mx;
             l[r] = sum;
-            rd[r] = sum > 0.0 ? acc / sum : 0.0;
+            rd[r] = acc;
+            re[r] = e;
         }
+        /* implicit barrier: every needed row's statistics are ready */
 
-        /* dQ, row by row */
+        /* pass 2, the requested query rows: dQ_i (and bq_i) */
 #pragma omp for schedule(dynamic, 8)
-        for (int64_t r = 0; r < totq; ++r) {
+        for (int64_t t = 0; t < cq; ++t) {
+            const int64_t r = qrows ? qrows[t] : t;
             const int64_t bh = r / Nq, i = r % Nq;
             const double *qi = q + r * D, *gi = dout + r * D;
             const double *kb = k + bh * Nk * D, *vb = v + bh * Nk * D;
-            double *aq = dq + r * D;
-            for (int64_t d = 0; d < D; ++d)
+            double *aq = dq + t * D;
+            double *mq = magn ? bq + t * D : NULL;
+            for (int64_t d = 0; d < D; ++d) {
                 aq[d] = 0.0;
-            for (int64_t j = 0; j < Nk; ++j) {
+                if (mq)
+                    mq[d] = 0.0;
+            }
+            for (int64_t j = 0; j < Nk && l[r] > 0.0; ++j) {
                 if (!visible_masked(i, j, causal, window, nglobal))
                     continue;
                 double dot = 0.0, dp = 0.0;
@@ -660,21 +720,33 @@ int fa_oracle_attention_bwd_masked(const double *q, const double *k, const doubl
                 }
                 const double p = exp(scale * dot - m[r]) / l[r];
                 const double ds = p * (dp - rd[r]);
-                for (int64_t d = 0; d < D; ++d)
+                const double w = fabs(ds) + p * re[r];
+                for (int64_t d = 0; d < D; ++d) {
                     aq[d] += ds * kb[j * D + d];
+                    if (mq)
+                        mq[d] += w * fabs(kb[j * D + d]);
+                }
             }
-            for (int64_t d = 0; d < D; ++d)
+            for (int64_t d = 0; d < D; ++d) {
                 aq[d] *= scale;
+                if (mq)
+                    mq[d] *= fabs(scale);
+            }
         }
 
-        /* dK and dV, key by key */
+        /* pass 3, the requested key rows: dK_j and dV_j (and bk_j, bv_j) */
 #pragma omp for schedule(dynamic, 8)
-        for (int64_t c = 0; c < totk; ++c) {
+        for (int64_t t = 0; t < ck; ++t) {
+            const int64_t c = krows ? krows[t] : t;
             const int64_t bh = c / Nk, j = c % Nk;
             const double *kc = k + c * D, *vc = v + c * D;
-            double *ak = dk + c * D, *av = dv + c * D;
-            for (int64_t d = 0; d < D; ++d)
+            double *ak = dk + t * D, *av = dv + t * D;
+            double *mk = magn ? bk + t * D : NULL, *mv = magn ? bv + t * D : NULL;
+            for (int64_t d = 0; d < D; ++d) {
                 ak[d] = av[d] = 0.0;
+                if (magn)
+                    mk[d] = mv[d] = 0.0;
+            }
             for (int64_t i = 0; i < Nq; ++i) {
                 if (!visible_masked(i, j, causal, window, nglobal))
                     continue;
@@ -687,17 +759,28 @@ int fa_oracle_attention_bwd_masked(const double *q, const double *k, const doubl
                 }
                 const double p = exp(scale * dot - m[r]) / l[r];
                 const double ds = p * (dp - rd[r]);
+                const double w = fabs(ds) + p * re[r];
                 for (int64_t d = 0; d < D; ++d) {
                     av[d] += p * gi[d];
                     ak[d] += ds * qi[d];
+                    if (magn) {
+                        mv[d] += p * fabs(gi[d]);
+                        mk[d] += w * fabs(qi[d]);
+                    }
                 }
             }
-            for (int64_t d = 0; d < D; ++d)
+            for (int64_t d = 0; d < D; ++d) {
                 ak[d] *= scale;
+                if (magn)
+                    mk[d] *= fabs(scale);
+            }
         }
+        free(o);
     }
     free(m);
     free(l);
     free(rd);
-    return ORACLE_OK;
+    free(re);
+    free(need);
+    return failed ? ORACLE_ENOMEM : ORACLE_OK;
 }

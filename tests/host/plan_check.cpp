@@ -104,10 +104,55 @@ int check(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, bool causal, int cus, i
   return 1;
 }
 
+// Key chunks of a split variable-length tile (varlen_split): for every tile
+// length, chunk cap and minimum chunk length the kernels can meet, the
+// chunks [i*kc, min((i+1)*kc, nkt)) for i < count are non-empty and cover
+// the tile's key tiles exactly once, there are at most NC of them, and
+// wherever the earlier rule (count = min(NC, ceil(nkt / KC))) left no chunk
+// empty the count is unchanged.
+int check_varlen_split() {
+  int n = 0;
+  for (int NC = 1; NC <= 16; ++NC)
+    for (int KC = 1; KC <= 64; ++KC)
+      for (int nkt = 1; nkt <= 1024; ++nkt) {
+        int kc = 0;
+        const int nch = varlen_split(nkt, NC, KC, kc);
+        if (nch < 1 || nch > NC || kc < 1) {
+          printf("FAIL varlen_split count: nkt=%d NC=%d KC=%d -> %d chunks of %d\n", nkt, NC,
+                 KC, nch, kc);
+          return -1;
+        }
+        int covered = 0;
+        for (int i = 0; i < nch; ++i) {
+          const int a = i * kc, b = (a + kc < nkt) ? a + kc : nkt;
+          if (a != covered || b <= a) {
+            printf("FAIL varlen_split chunk %d: nkt=%d NC=%d KC=%d kc=%d\n", i, nkt, NC, KC,
+                   kc);
+            return -1;
+          }
+          covered = b;
+        }
+        if (covered != nkt) {
+          printf("FAIL varlen_split cover: nkt=%d NC=%d KC=%d\n", nkt, NC, KC);
+          return -1;
+        }
+        int old = (nkt + KC - 1) / KC;
+        if (old > NC) old = NC;
+        const int kold = (nkt + old - 1) / old;
+        if ((old - 1) * kold < nkt && old != nch) {
+          printf("FAIL varlen_split changed: nkt=%d NC=%d KC=%d\n", nkt, NC, KC);
+          return -1;
+        }
+        ++n;
+      }
+  return n;
+}
+
 }  // namespace
 
 int main() {
-  int n = 0;
+  int n = check_varlen_split();
+  if (n < 0) return 1;
   const int64_t Ns[] = {1, 33, 64, 127, 128, 129, 255, 256, 300, 1000, 2048, 3000, 4096, 8192};
   const int cuss[] = {1, 3, 8, 80, 256, 304, 1024};
   const int leads[][2] = {{-1, 0}, {0, 0}, {1, 0}, {5, 0}, {17, 0}, {0, 3}, {5, 2}, {6, 9}};

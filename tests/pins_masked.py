@@ -11,7 +11,11 @@ stated in fa_oracle.c.  Pins:
     independently, on tiny shapes, Nq != Nk both ways;
   * keys a row cannot see do not matter: changing them leaves the row's
     output bit-identical;
-  * rows with no visible key (Nq > Nk) get O = 0 and L = -inf.
+  * rows with no visible key (Nq > Nk) get O = 0 and L = -inf;
+  * backward: reduction to the dense backward (gradients and magnitude
+    sums), the diagonal window, central finite differences of the masked
+    forward, the magnitude sums against their definition written with numpy
+    on an independently built visibility matrix, and row sampling.
 """
 from __future__ import annotations
 
@@ -42,8 +46,8 @@ def pin_masked_reduces_to_dense(lib):
         ref = oracle.attention(q, k, v, 0.6, causal, lib=lib)
         for window, ng in ((13, 0), (100, 3), (1, 13), (2, 50)):
             got = oracle.attention_masked(q, k, v, 0.6, causal, window, ng, lib=lib)
-            _close(got[0], ref[0], 1e-13, f"dense O (window {window}, global {ng})")
-            _close(got[1], ref[1], 1e-13, f"dense L (window {window}, global {ng})")
+            _close(got[0], ref[0], 0.0, f"dense O (window {window}, global {ng})")
+            _close(got[1], ref[1], 0.0, f"dense L (window {window}, global {ng})")
 
 
 def pin_masked_diagonal_only(lib):
@@ -104,13 +108,81 @@ def pin_masked_rows_without_keys(lib):
 
 
 def pin_masked_bwd_reduces_to_dense(lib):
+    """A window covering every key: gradients and magnitude sums are the
+    dense oracle's."""
     q, k, v = _qkv(6, 1, 2, 12, 9, 3)
     g = np.random.default_rng(7).standard_normal(q.shape)
     for causal in (False, True):
-        ref = oracle.attention_bwd(q, k, v, g, 0.5, causal, lib=lib)
-        got = oracle.attention_bwd_masked(q, k, v, g, 0.5, causal, 100, 0, lib=lib)
+        ref = oracle.attention_bwd(q, k, v, g, 0.5, causal, magnitudes=True, lib=lib)
+        got = oracle.attention_bwd_masked(q, k, v, g, 0.5, causal, 100, 0, magnitudes=True,
+                                          lib=lib)
         for a, b in zip(got, ref):
             _close(a, b, 1e-12, "masked bwd reduces to dense")
+
+
+def _visible_matrix(Nq, Nk, causal, window, ng):
+    """The visibility matrix, written from the rule's two parts on index
+    grids (independently of the oracle's per-pair test)."""
+    i = np.arange(Nq)[:, None]
+    j = np.arange(Nk)[None, :]
+    band = (i - j >= 0) & (i - j < window) if causal else np.abs(i - j) < window
+    glob = (j < ng) | (i < ng)
+    if causal:
+        glob &= j <= i
+    return band | glob
+
+
+def pin_masked_bwd_magnitudes(lib):
+    """The magnitude sums bound the gradients and follow their definition
+    over the visible pairs (written here with numpy on the visibility matrix;
+    rows without a visible key contribute nothing)."""
+    B, H, Nq, Nk, D = 1, 2, 13, 9, 5
+    q, k, v = _qkv(50, B, H, Nq, Nk, D)
+    g = np.random.default_rng(51).standard_normal(q.shape)
+    scale = -0.7
+    for causal, window, ng in ((False, 3, 1), (True, 2, 2), (True, 4, 0), (False, 1, 0)):
+        dq, dk, dv, bq, bk, bv = oracle.attention_bwd_masked(q, k, v, g, scale, causal, window,
+                                                             ng, magnitudes=True, lib=lib)
+        for grad, bound, what in ((dq, bq, "Q"), (dk, bk, "K"), (dv, bv, "V")):
+            assert np.all(bound >= np.abs(grad) - 1e-12), f"b{what} below |d{what}|"
+        vis = _visible_matrix(Nq, Nk, causal, window, ng)
+        s = scale * np.einsum("bhid,bhjd->bhij", q, k)
+        s = np.where(vis, s, -np.inf)
+        mx = s.max(-1, keepdims=True)
+        mx = np.where(np.isfinite(mx), mx, 0.0)
+        e = np.where(vis, np.exp(s - mx), 0.0)
+        tot = e.sum(-1, keepdims=True)
+        p = np.divide(e, tot, out=np.zeros_like(e), where=tot > 0)
+        dp = np.einsum("bhid,bhjd->bhij", g, v)
+        o = np.einsum("bhij,bhjd->bhid", p, v)
+        rowterm = (g * o).sum(-1, keepdims=True)
+        ee = (np.abs(g) * np.einsum("bhij,bhjd->bhid", p, np.abs(v))).sum(-1, keepdims=True)
+        w = np.abs(p * (dp - rowterm)) + p * ee
+        _close(bv, np.einsum("bhij,bhid->bhjd", p, np.abs(g)), 1e-12, "masked bV definition")
+        _close(bq, abs(scale) * np.einsum("bhij,bhjd->bhid", w, np.abs(k)), 1e-12,
+               "masked bQ definition")
+        _close(bk, abs(scale) * np.einsum("bhij,bhid->bhjd", w, np.abs(q)), 1e-12,
+               "masked bK definition")
+        _close(dv, np.einsum("bhij,bhid->bhjd", p, g), 1e-12, "masked dV (numpy)")
+
+
+def pin_masked_bwd_row_sampling(lib):
+    """Sampled query and key rows equal the same rows of the full result,
+    gradients and magnitude sums alike."""
+    B, H, Nq, Nk, D = 2, 2, 15, 11, 3
+    q, k, v = _qkv(60, B, H, Nq, Nk, D)
+    g = np.random.default_rng(61).standard_normal(q.shape)
+    for causal, window, ng in ((False, 4, 2), (True, 3, 1)):
+        full = oracle.attention_bwd_masked(q, k, v, g, 0.4, causal, window, ng,
+                                           magnitudes=True, lib=lib)
+        qr = np.array([0, 7, B * H * Nq - 1, 33, 16])
+        kr = np.array([B * H * Nk - 1, 2, 0, 25])
+        part = oracle.attention_bwd_masked(q, k, v, g, 0.4, causal, window, ng, qrows=qr,
+                                           krows=kr, magnitudes=True, lib=lib)
+        _close(part[0], full[0].reshape(-1, D)[qr], 0.0, "sampled masked dQ")
+        _close(part[3], full[3].reshape(-1, D)[qr], 0.0, "sampled masked bQ")
+        for t in (1, 2, 4, 5):
+            _close(part[t], full[t].reshape(-1, D)[kr], 0.0, f"sampled masked key output {t}")
 
 
 def pin_masked_bwd_diagonal(lib):
@@ -153,6 +225,8 @@ def pin_masked_bwd_finite_differences(lib):
 
 ALL_MASKED_PINS = [
     pin_masked_bwd_reduces_to_dense,
+    pin_masked_bwd_magnitudes,
+    pin_masked_bwd_row_sampling,
     pin_masked_bwd_diagonal,
     pin_masked_bwd_finite_differences,
     pin_masked_reduces_to_dense,

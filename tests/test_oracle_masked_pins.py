@@ -1,5 +1,5 @@
 """CPU tests: the oracle's local-window + global-token attention against its
-pins, and planted mistakes in its visibility rule."""
+pins, and planted mistakes in its visibility rule and in its backward pass."""
 import pytest
 
 import oracle
@@ -21,6 +21,21 @@ MUTATIONS = {
     "global_keys_only": ("global = (j < nglobal || i < nglobal)", "global = (j < nglobal)"),
     "global_ignores_causal": ("&& (!causal || j <= i);", ";"),
     "one_sided_noncausal": ("(d > -window && d < window)", "(d >= 0 && d < window)"),
+    # the backward (fa_oracle_attention_bwd_masked)
+    "bwd_dv_without_p": ("av[d] += p * gi[d];", "av[d] += gi[d];"),
+    "bwd_dk_uses_do": ("ak[d] += ds * qi[d];", "ak[d] += ds * gi[d];"),
+    "bwd_dq_ignores_mask": (
+        "for (int64_t j = 0; j < Nk && l[r] > 0.0; ++j) {\n"
+        "                if (!visible_masked(i, j, causal, window, nglobal))\n"
+        "                    continue;",
+        "for (int64_t j = 0; j < Nk && l[r] > 0.0; ++j) {"),
+    "bwd_bk_without_row_term": (
+        "ak[d] += ds * qi[d];\n                    if (magn) {\n"
+        "                        mv[d] += p * fabs(gi[d]);\n"
+        "                        mk[d] += w * fabs(qi[d]);",
+        "ak[d] += ds * qi[d];\n                    if (magn) {\n"
+        "                        mv[d] += p * fabs(gi[d]);\n"
+        "                        mk[d] += fabs(ds) * fabs(qi[d]);"),
 }
 
 

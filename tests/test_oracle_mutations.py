@@ -11,12 +11,17 @@ import oracle
 from pins import ALL_PINS
 from pins_bwd import ALL_BWD_PINS
 
+# the end of fa_oracle_attention's row loop (the masked routine ends its
+# rows with the same two statements, then frees a second buffer)
+_DENSE_END = "\n        }\n        free(w);\n    }"
+
 MUTATIONS = {
     "drop_scale": ("w[j] = scale * dot;", "w[j] = dot;"),
     "diagonal_hidden": ("return (i + 1 < Nk) ? i + 1 : Nk;", "return (i < Nk) ? i : Nk;"),
-    "log2_lse": ("lse[t] = m + log(l);", "lse[t] = m + log2(l);"),
-    "lse_without_max": ("lse[t] = m + log(l);", "lse[t] = log(l);"),
-    "no_normalisation": ("oi[d] /= l;", "oi[d] /= 1.0;"),
+    "log2_lse": ("lse[t] = m + log(l);" + _DENSE_END, "lse[t] = m + log2(l);" + _DENSE_END),
+    "lse_without_max": ("lse[t] = m + log(l);" + _DENSE_END, "lse[t] = log(l);" + _DENSE_END),
+    "no_normalisation": ("oi[d] /= l;\n            lse[t] = m + log(l);" + _DENSE_END,
+                         "oi[d] /= 1.0;\n            lse[t] = m + log(l);" + _DENSE_END),
     "transposed_values": ("oi[d] += w[j] * vb[j * D + d];",
                           "oi[d] += w[j] * vb[d * Nk + j];"),
     "transposed_keys": ("dot += qi[d] * kb[j * D + d];\n                w[j]",
@@ -38,7 +43,7 @@ _DS_K = _DS_Q[:-2] + "gv"
 
 # Planted mistakes in the backward pass (fa_oracle_attention_bwd).
 BWD_MUTATIONS = {
-    "bwd_row_term_without_p": ("acc += p * dp;", "acc += dp;"),
+    "bwd_row_term_without_p": ("}\n                acc += p * dp;", "}\n                acc += dp;"),
     "bwd_dv_without_p": ("gv[d] += p * gi[d];", "gv[d] += gi[d];"),
     "bwd_dk_uses_do": ("gk[d] += ds * qi[d];", "gk[d] += ds * gi[d];"),
     "bwd_dq_uses_v": ("gq[d] += ds * kb[j * D + d];", "gq[d] += ds * vb[j * D + d];"),

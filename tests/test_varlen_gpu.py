@@ -361,3 +361,127 @@ def test_varlen_bwd_unequal_and_empty(causal):
 
 def test_varlen_bwd_fp16():
     compare_bwd(MIXED, MIXED, 1, 64, True, seed=2100, dtype="f16")
+
+
+def test_varlen_bwd_32k_tokens_sampled():
+    """The shape bench.py --varlen 8 --pass bwd times: 32768 tokens in 8
+    sequences of seeded lengths, one head, D=128, causal bf16.  Sampled query
+    rows (dQ) and key rows (dK, dV) of every sequence against the oracle's
+    backward on that sequence, with the backward's bound (2u times the
+    oracle's magnitude sums), and 16-bit gradients the rounding of the fp32
+    ones."""
+    from workloads import gen_grad_out
+
+    lens = varlen_lengths(32768, 8, seed=77, min_len=64)
+    D, T = 128, 32768
+    q, k, v, cu_q, cu_k = packed(lens, lens, 1, D, 3200)
+    g = gen_grad_out(1, 1, T, D, seed=3202, dtype="bf16")[0]
+    scale = 1.0 / math.sqrt(D)
+    _log(f"bwd sampled S=8 T={T} lens={lens}")
+    qd, kd, vd, gd, cqd, ckd = (t.to(DEV) for t in (q, k, v, g, cu_q, cu_k))
+    o, lse = fa.fwd_varlen(qd, kd, vd, cqd, ckd, max(lens), causal=True, scale=scale)
+    g32 = fa.bwd_varlen(qd, kd, vd, o, lse, gd, cqd, ckd, max(lens), max(lens), causal=True,
+                        scale=scale, grad_dtype=torch.float32)
+    g16 = fa.bwd_varlen(qd, kd, vd, o, lse, gd, cqd, ckd, max(lens), max(lens), causal=True,
+                        scale=scale)
+    torch.cuda.synchronize()
+    g32 = [x.cpu()[0] for x in g32]
+    g16 = [x.cpu()[0] for x in g16]
+    qn, kn, vn, gn = (t.double().numpy() for t in (q, k, v, g))
+    u = 2.0 ** -8
+    r = np.random.default_rng(3203)
+    cq = cu_q.tolist()
+    for s in range(8):
+        a, b = cq[s], cq[s + 1]
+        n = b - a
+        pick = np.unique(np.concatenate([r.integers(0, n, 32), [0, n - 1]]))
+        ref = oracle.attention_bwd(qn[None, :, a:b], kn[None, :, a:b], vn[None, :, a:b],
+                                   gn[None, :, a:b], scale, True, qrows=pick, krows=pick,
+                                   magnitudes=True)
+        for m, name in enumerate(("dQ", "dK", "dV")):
+            x = g32[m][a + pick].double().numpy()
+            bd = ref[m + 3]
+            bound = 2 * u * bd + 1e-6 * float(bd.max()) + 1e-30
+            ratio = float((np.abs(x - ref[m]) / bound).max())
+            assert ratio <= 1.0, f"sequence {s} {name}: error/bound {ratio:.3f}"
+            assert torch.equal(g32[m][a + pick].to(torch.bfloat16), g16[m][a + pick]), \
+                f"sequence {s} {name}: rounding"
+        _log(f"  sequence {s} ({n} tokens): {len(pick)} rows ok")
+
+
+def test_varlen_split_chunk_cap_leaves_no_chunk_empty():
+    """One 128-row sequence against 8256 keys, non-causal, with
+    max_seqlen_k = 8256: the split plan caps the tile at 16 chunks of 9 key
+    tiles, which cover its 129 key tiles with 15, so the 16th must neither
+    run nor be merged.  The workspace is filled with NaN bytes first, so a
+    merged empty chunk would show."""
+    lq, lk = [128], [8256]
+    H, D = 1, 128
+    q, k, v, cu_q, cu_k = (t.to(DEV) for t in packed(lq, lk, H, D, 3300))
+    code = fa._dtype_code(torch, q.dtype, torch.float32)
+    st, nb = fa.fa_fwd_varlen_workspace_size(1, H, 128, 8256, 128, 8256, D, False, code)
+    assert st == fa.FA_OK and nb > 0
+    ws = torch.full((nb,), 0xFF, dtype=torch.uint8, device=DEV)
+    o = torch.empty((H, 128, D), dtype=torch.float32, device=DEV)
+    lse = torch.empty((H, 128), dtype=torch.float32, device=DEV)
+    scale = 1.0 / math.sqrt(D)
+    st = fa.fa_fwd_varlen_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                             lse.data_ptr(), cu_q.data_ptr(), cu_k.data_ptr(), 1, H, 128, 8256,
+                             128, 8256, D, scale, False, code, ws.data_ptr(), nb,
+                             torch.cuda.current_stream().cuda_stream)
+    assert st == fa.FA_OK, fa.fa_status_str(st)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(q.cpu().double().numpy()[None], k.cpu().double().numpy()[None],
+                              v.cpu().double().numpy()[None], scale, False)
+    err_o = float(np.abs(o.cpu().double().numpy() - ro[0]).max())
+    err_l = float(np.abs(lse.cpu().double().numpy() - rl[0]).max())
+    _log(f"chunk cap: O {err_o:.3e} L {err_l:.3e}")
+    assert err_o <= 1e-2 and err_l <= 1e-3
+    # and the same through the Python binding
+    compare(lq, lk, H, D, False, seed=3300, maxk=8256)
+
+
+def test_varlen_rows_past_max_seqlen_q_are_nan():
+    """A sequence longer than max_seqlen_q: rows up to the end of the query
+    tile holding row max_seqlen_q - 1 (256-row tiles at D = 64) are computed
+    exactly, the rest get O = NaN and lse = NaN; the other sequence is
+    unaffected."""
+    lq, lk = [1000, 50], [1000, 50]
+    q, k, v, cu_q, cu_k = packed(lq, lk, 1, 64, 3400)
+    scale = 0.125
+    full = run(q, k, v, cu_q, cu_k, 1000, True, scale, torch.float32)
+    short = run(q, k, v, cu_q, cu_k, 100, True, scale, torch.float32)
+    assert torch.equal(short[0][:, :256], full[0][:, :256])
+    assert torch.equal(short[1][:, :256], full[1][:, :256])
+    assert torch.isnan(short[0][:, 256:1000]).all() and torch.isnan(short[1][:, 256:1000]).all()
+    assert torch.equal(short[0][:, 1000:], full[0][:, 1000:])
+    assert torch.equal(short[1][:, 1000:], full[1][:, 1000:])
+
+
+def test_varlen_bwd_rows_past_bounds_are_nan():
+    """Sequences longer than max_seqlen_q / max_seqlen_k in the backward:
+    dq rows past the 64-row tile holding row max_seqlen_q - 1, and dk, dv
+    rows past the tile holding key max_seqlen_k - 1, are NaN; every other row
+    equals the run with true bounds bit for bit."""
+    lq, lk = [300, 20], [400, 30]
+    H, D = 1, 64
+    q, k, v, cu_q, cu_k = (t.to(DEV) for t in packed(lq, lk, H, D, 3500))
+    from workloads import gen_grad_out
+
+    g = gen_grad_out(1, H, sum(lq), D, seed=3501, dtype="bf16")[0].to(DEV)
+    o, lse = fa.fwd_varlen(q, k, v, cu_q, cu_k, 300, causal=False, scale=0.125)
+    full = fa.bwd_varlen(q, k, v, o, lse, g, cu_q, cu_k, 300, 400, causal=False, scale=0.125,
+                         grad_dtype=torch.float32)
+    short = fa.bwd_varlen(q, k, v, o, lse, g, cu_q, cu_k, 100, 70, causal=False, scale=0.125,
+                          grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    full = [x.cpu() for x in full]
+    short = [x.cpu() for x in short]
+    # dq: rows 0..127 computed, 128..299 NaN, the second sequence (300..319) whole
+    assert torch.equal(short[0][:, :128], full[0][:, :128])
+    assert torch.isnan(short[0][:, 128:300]).all()
+    assert torch.equal(short[0][:, 300:], full[0][:, 300:])
+    for m in (1, 2):  # dk, dv: keys 0..127 computed, 128..399 NaN, 400..429 whole
+        assert torch.equal(short[m][:, :128], full[m][:, :128])
+        assert torch.isnan(short[m][:, 128:400]).all()
+        assert torch.equal(short[m][:, 400:], full[m][:, 400:])

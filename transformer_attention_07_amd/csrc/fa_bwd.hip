@@ -159,6 +159,15 @@ __device__ __forceinline__ Slice resolve(int BH, int Nq, int Nk, const int *cu_q
   return sl;
 }
 
+// Rows [from, n) of a [rows, D] slice set to NaN: the rows of a
+// variable-length sequence past the last tile its grid covers (the sequence
+// is longer than the caller's bound), so that no row is left unwritten.
+template <typename OT, int D>
+__device__ __forceinline__ void nan_rows(OT *base, int from, int n) {
+  const float nan = __builtin_nanf("");
+  for (int i = from * D + (int)threadIdx.x; i < n * D; i += kThreads) base[i] = (OT)nan;
+}
+
 // dK and dV: one workgroup per (batch*head, kTile keys).  Wave w owns keys
 // key0 + 32*(w & 1) .. +31 and, of every 128-query block, the 32-row
 // quarters par and par + 2 (par = w >> 1); the two parities are summed at
@@ -170,8 +179,8 @@ template <typename T, typename OT, int D, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dl,
-    OT *__restrict__ dk, OT *__restrict__ dv, int Nq, int Nk, int BH, float c, float scale,
-    const int *__restrict__ cu_q, const int *__restrict__ cu_k, int S, Mask mk) {
+    OT *__restrict__ dk, OT *__restrict__ dv, int Nq, int Nk, int BH, int nkt, float c,
+    float scale, const int *__restrict__ cu_q, const int *__restrict__ cu_k, int S, Mask mk) {
   using M = Mma<T>;
   typedef typename M::frag frag;
   constexpr int KF = D / 16;  // MFMA steps along D
@@ -187,6 +196,10 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv(
   Nq = sl.Nq;
   Nk = sl.Nk;
   const int kt = sl.tile;
+  if (kt == nkt - 1 && Nk > nkt * kTile) {  // longer than the grid (variable length)
+    nan_rows<OT, D>(dk + sl.krow * D, nkt * kTile, Nk);
+    nan_rows<OT, D>(dv + sl.krow * D, nkt * kTile, Nk);
+  }
   if (kt * kTile >= Nk) return;  // past the slice's keys (workgroup-uniform)
   const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
   const int g = lane >> 5, col = lane & 31;
@@ -371,6 +384,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq(
   Nq = sl.Nq;
   Nk = sl.Nk;
   const int qt = sl.tile;
+  if (qt == nqt - 1 && Nq > nqt * kTile)  // longer than the grid (variable length)
+    nan_rows<OT, D>(dq + sl.qrow * D, nqt * kTile, Nq);
   if (qt * kTile >= Nq) return;  // past the slice's queries (workgroup-uniform)
   const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
   const int g = lane >> 5, col = lane & 31;
@@ -516,15 +531,18 @@ hipError_t launch_bwd(const BwdArgs &a) {
   if (e != hipSuccess) return e;
   const bool vl = a.cu_q != nullptr;
   // tiles per slice, and slices per tile rank
-  const int nkt = ((vl ? a.maxk : a.Nk) + kTile - 1) / kTile;
+  // (a variable-length grid has at least one key tile per slice when there
+  // are keys, so that keys past a zero max_seqlen_k still get their NaN)
+  int nkt = ((vl ? a.maxk : a.Nk) + kTile - 1) / kTile;
+  if (vl && a.Nk > 0 && nkt < 1) nkt = 1;
   const int nqt = ((vl ? a.maxq : a.Nq) + kTile - 1) / kTile;
   const int slices = vl ? a.BH * a.S : a.BH;
   if (nkt > 0) {
     hipLaunchKernelGGL((fa_bwd_dkdv<T, OT, D, CAUSAL, MASKED>),
                        dim3((unsigned)(slices * nkt)), dim3(kThreads), 0, a.stream,
                        (const T *)a.q, (const T *)a.k, (const T *)a.v, (const T *)a.dout,
-                       a.lse, (const float *)a.dl, (OT *)a.dk, (OT *)a.dv, a.Nq, a.Nk, a.BH, c,
-                       a.scale, a.cu_q, a.cu_k, a.S, a.mk);
+                       a.lse, (const float *)a.dl, (OT *)a.dk, (OT *)a.dv, a.Nq, a.Nk, a.BH,
+                       nkt, c, a.scale, a.cu_q, a.cu_k, a.S, a.mk);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

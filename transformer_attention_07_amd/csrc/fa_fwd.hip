@@ -8,31 +8,29 @@
 // exp(m_old - m_new) and adds P V.  At the end it writes O = acc / l and the
 // per-row logsumexp L = m + ln l.  The score matrix lives only in registers.
 //
-// gfx950 mapping (one workgroup = 4 wave64s = 128 query rows, 32 per wave):
-//   * S^T = K Q^T on v_mfma_f32_32x32x16_{bf16,f16} (v_mfma_f32_32x32x2_f32
-//     for fp32 inputs).  Computing the transpose puts one query per lane
+// gfx950 mapping (16-bit inputs; fp32 inputs use fa_fwd_f32 further down):
+//   * Workgroups of eight wave64s, two per SIMD, each wave holding 32 query
+//     rows: 256 rows per workgroup, or 128 with the two waves of a SIMD
+//     splitting the key blocks of the same rows (pair-split layout, when
+//     query tiles are few); see pipe8_run.
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_{bf16,f16} puts one query per lane
 //     column: lane l owns query (l mod 32) and 16 of each 32-key block, so a
 //     row maximum or sum is a reduction inside the lane plus one exchange with
-//     lane l^32.
-//   * The S^T accumulator registers, rounded to the input type, are exactly
-//     the B operand of O^T += V^T P^T: no shuffle of P through LDS.
-//   * K tiles sit in LDS row-major (row stride padded by 16 bytes so eight
-//     consecutive rows start on distinct banks); V tiles are stored
-//     transposed (V^T, row stride padded by 8 bytes) so each lane reads 4
-//     consecutive keys of one head-dim column with one 8-byte LDS read.
-//   * K/V tiles are double-buffered: the global loads of tile j+1 are issued
-//     before the MFMAs of tile j and written to the other LDS buffer after
-//     them, so one barrier per tile suffices.
+//     lane l^32.  The S^T accumulator registers, rounded to the input type,
+//     are exactly the B operand of O^T += V^T P^T: no trip of P through LDS.
+//   * K and V tiles of 64 keys go global -> LDS directly (buffer_load ...
+//     lds) into four-stage rings, one barrier per tile; K rows are read with
+//     ds_read_b128, V^T fragments with ds_read_b64_tr_b16; row strides are
+//     padded so that neither read has bank conflicts.
 //   * Ragged tails: every global read goes through a buffer resource whose
 //     size is the (batch, head) slice, so rows past Nq / Nk read as zero;
-//     scores of keys >= Nk are set to -inf before the softmax, and rows >= Nq
-//     are never stored.
-//   * Causal: key tiles past a wave's last query are skipped by that wave;
-//     only tiles that straddle the diagonal (or the Nk tail) pay for masking.
-//     Workgroups are issued longest-first, and consecutive workgroup ids
-//     (which the dispatcher spreads over the 8 XCDs) take different heads so
-//     that one head's K/V stays within one XCD's L2 when B*H is a multiple
-//     of 8.
+//     scores of keys >= Nk are -inf, rows >= Nq are never stored.
+//   * Causal: blocks past a wave's last query are never visited; only the
+//     diagonal block (and a key tail) is masked.
+//   * Work distribution: fa_fwd runs one workgroup per query tile, longest
+//     causal tiles first; fa_fwd_ws runs a stream-K schedule (equal shares
+//     of (query tile, key tile) units per compute unit, cut tiles combined
+//     by fa_merge_stream) when query tiles are too few to balance.
 //   * The softmax works in base 2: c = scale*log2(e) is folded into the
 //     scores, p = 2^(c*s - m2), and L = ln2 * (m2 + log2 l).
 
@@ -44,6 +42,7 @@
 #include <string.h>
 
 #include "fa.h"
+#include "mma16.h"
 #include "stream_plan.h"
 
 namespace {
@@ -80,49 +79,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base,
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }
-
-// ---------------------------------------------------------------------------
-// 16-bit input types: one MFMA shape, two element types.
-template <typename T> struct Mfma16;
-
-template <> struct Mfma16<__bf16> {
-  typedef bf16x8 frag;
-  typedef bf16x4 quad;
-  static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-  // acc + x.lo + x.hi for a packed pair of bf16 (v_dot2c_f32_bf16 with (1,1)).
-  static __device__ __forceinline__ float pair_sum(uint32_t x, float acc) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), one, acc, false);
-  }
-  // (a, b) rounded to nearest-even bf16, a in the low half.
-  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const f32x2 x = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
-  }
-};
-
-template <> struct Mfma16<_Float16> {
-  typedef f16x8 frag;
-  typedef f16x4 quad;
-  static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ float pair_sum(uint32_t x, float acc) {
-    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), one, acc, false);
-  }
-  // (a, b) rounded to nearest-even fp16, a in the low half.
-  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
-    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-    const f32x2 x = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2));
-  }
-};
 
 // Key index (relative to its 32-key block) held by accumulator register r of
 // a lane in half-wave g, for the 32x32 MFMA output layout: row
@@ -407,7 +363,7 @@ __device__ __forceinline__ void dma16(u32x4 rs, uint32_t lds_addr, uint32_t voff
 
 template <typename T, typename OT, int D, bool CAUSAL>
 struct Pipe {
-  typedef typename Mfma16<T>::frag frag;
+  typedef typename Mma<T>::frag frag;
   typedef PipeLayout<T, D> L;
   static constexpr int QF = D / 16;    // K.Q^T MFMAs per 32-key block
   // O^T blocks of 32 head-dim rows (at D = 16 the upper 16 rows read zero
@@ -457,7 +413,7 @@ struct Pipe {
   __device__ __forceinline__ void qk(const lds_char *kp, f32x16 &sc) const {
     sc = f32x16{};
 #pragma unroll
-    for (int f = 0; f < QF; ++f) sc = Mfma16<T>::mma(kfrag(kp, f), qf[f], sc);
+    for (int f = 0; f < QF; ++f) sc = Mma<T>::mma(kfrag(kp, f), qf[f], sc);
   }
 
   // acc += V^T P^T of a 32-key block (no overlap; drain only).  Fragments
@@ -469,7 +425,7 @@ struct Pipe {
     vf[1] = vfrag(vp, 1);
 #pragma unroll
     for (int m = 0; m < NPV; ++m) {
-      acc[m % NDB] = Mfma16<T>::mma(vf[m], pin[m / NDB], acc[m % NDB]);
+      acc[m % NDB] = Mma<T>::mma(vf[m], pin[m / NDB], acc[m % NDB]);
       if (m + 2 < NPV) vf[m + 2] = vfrag(vp, m + 2);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -561,15 +517,15 @@ struct Pipe {
         const int k = ch - 3;  // stage A on pair k, B on k-1, C on k-2, D on k-3
         if (k >= 3 && k - 3 < 8) {  // D: sum of the rounded pair
           if ((k - 3) & 1)
-            rsb = Mfma16<T>::pair_sum(wq, rsb);
+            rsb = Mma<T>::pair_sum(wq, rsb);
           else
-            rsa = Mfma16<T>::pair_sum(wq, rsa);
+            rsa = Mma<T>::pair_sum(wq, rsa);
         }
         if (k >= 2 && k - 2 < 8) {  // C: fp32 sums, rounding to T
           const int w = k - 2;
           psa += pb[0];
           psb += pb[1];
-          wq = Mfma16<T>::pack2(pb[0], pb[1]);
+          wq = Mma<T>::pack2(pb[0], pb[1]);
           pw[w / 4][w % 4] = wq;
         }
         if (k >= 1 && k - 1 < 8) {  // B: p = 2^x
@@ -602,7 +558,7 @@ struct Pipe {
     for (int i = 0; i < NSL; ++i) {
       // K.Q^T, then a slice of the softmax
       if (i < QF) {
-        sout = Mfma16<T>::mma(kf[i], qf[i], sout);
+        sout = Mma<T>::mma(kf[i], qf[i], sout);
         if (i + PFK < QF)
           kf[i + PFK] = kfrag(kp, i + PFK);
         else if (PRE)
@@ -613,7 +569,7 @@ struct Pipe {
       __builtin_amdgcn_sched_barrier(0);
       // P.V, then a slice of the softmax
       if (i < NPV) {
-        acc[i % NDB] = Mfma16<T>::mma(vf[i], pin[i / NDB], acc[i % NDB]);
+        acc[i % NDB] = Mma<T>::mma(vf[i], pin[i / NDB], acc[i % NDB]);
         if (i + PFV < NPV)
           vf[i + PFV] = vfrag(vp, i + PFV);
         else if (PRE)
@@ -1051,13 +1007,6 @@ __device__ __forceinline__ int varlen_slot(int h, int NT, int NC, int qa, int q0
   return (h * NT + (qa + q0) / QT + sq) * NC + chunk;
 }
 
-// Chunks of a tile with nkt key tiles: ceil(nkt / KC), at most NC (the
-// chunks are then longer than KC, whatever the sequence lengths), each of
-// ceil(nkt / chunks) key tiles.
-__device__ __forceinline__ int varlen_chunks(int nkt, int NC, int KC) {
-  return min(NC, (nkt + KC - 1) / KC);
-}
-
 template <typename T, typename OT, int D, bool CAUSAL, bool PAIR>
 __global__ __launch_bounds__(kThreads8) void fa_fwd_varlen(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
@@ -1079,8 +1028,16 @@ __global__ __launch_bounds__(kThreads8) void fa_fwd_varlen(
   const int ka = max(0, min(cu_k[sq], Tk)), kb = max(ka, min(cu_k[sq + 1], Tk));
   const int nq = qb - qa, nk = kb - ka;
   const int q0 = qt * QT;
-  if (q0 >= nq) return;  // workgroup-uniform, before any barrier
   const size_t qo = (size_t)h * Tq + qa, ko = (size_t)h * Tk + ka;
+  if (qt == ntiles - 1 && chunk == 0 && nq > ntiles * QT) {
+    // rows past the last tile the grid covers (the sequence is longer than
+    // the caller's max_seqlen_q): defined as NaN rather than left unwritten
+    const float nan = __builtin_nanf("");
+    for (int i = ntiles * QT * D + threadIdx.x; i < nq * D; i += kThreads8)
+      o[qo * D + i] = (OT)nan;
+    for (int i = ntiles * QT + threadIdx.x; i < nq; i += kThreads8) lse[qo + i] = nan;
+  }
+  if (q0 >= nq) return;  // workgroup-uniform, before any barrier
   if (nk == 0) {
     if (chunk != 0) return;
     const int rows = min(QT, nq - q0);
@@ -1092,11 +1049,11 @@ __global__ __launch_bounds__(kThreads8) void fa_fwd_varlen(
   const int kend = CAUSAL ? min(nk, q0 + QT) : nk;
   const int nkt = (kend + kBN - 1) / kBN;
   PipeItem it = {0, q0, 0, nkt, -1};
-  const int nch = varlen_chunks(nkt, NC, KC);
+  int kc;
+  const int nch = varlen_split(nkt, NC, KC, kc);
   if (nch > 1) {  // split: this workgroup's chunk of the key tiles
-    const int kc = (nkt + nch - 1) / nch;
+    if (chunk >= nch) return;  // every chunk below nch holds key tiles
     it.kt0 = chunk * kc;
-    if (chunk >= nch || it.kt0 >= nkt) return;
     it.kt1 = min(nkt, it.kt0 + kc);
     it.slot = varlen_slot(h, NT, NC, qa, q0, QT, sq, chunk);
   } else if (chunk != 0) {
@@ -1229,7 +1186,8 @@ __global__ __launch_bounds__(kThreads) void fa_merge_varlen(
   if (q0 >= nq || nk == 0) return;
   const int kend = CAUSAL ? min(nk, q0 + QT) : nk;
   const int nkt = (kend + kBN - 1) / kBN;
-  const int nch = varlen_chunks(nkt, NC, KC);
+  int kc;
+  const int nch = varlen_split(nkt, NC, KC, kc);
   if (nch <= 1) return;  // written by its only workgroup
   const int nslots = H * NT * NC;
   const float *ws_s = ws + (size_t)nslots * QT * D;

@@ -255,6 +255,21 @@ inline bool make_plan(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, int dtype, 
   return true;
 }
 
+// Key chunks of a variable-length query tile with nkt (>= 1) key tiles when
+// a split allows at most NC chunks of at least KC key tiles: a chunk length
+// kc = ceil(nkt / min(NC, ceil(nkt / KC))) and ceil(nkt / kc) chunks (returned,
+// kc written).  Counting the chunks from kc rather than taking
+// min(NC, ceil(nkt / KC)) itself keeps every chunk non-empty: capping the
+// count at NC lengthens the chunks, and the rounded-up length can then cover
+// the tile in fewer of them (nkt = 129, NC = 16, KC = 8: kc = 9, 15 chunks).
+FA_HD inline int varlen_split(int nkt, int NC, int KC, int &kc) {
+  int n = (nkt + KC - 1) / KC;
+  if (n > NC) n = NC;
+  if (n < 1) n = 1;
+  kc = (nkt + n - 1) / n;
+  return (nkt + kc - 1) / kc;
+}
+
 // The cut tiles of a schedule (CutTile::cut for j = 1 .. G-1).
 inline void make_cuts(const StreamPlan &sp, bool causal, CutList &cl) {
   cl.n = 0;

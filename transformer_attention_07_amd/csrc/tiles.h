@@ -13,6 +13,7 @@
 #include <stdint.h>
 
 #include "mask.h"
+#include "mma16.h"
 
 namespace {
 
@@ -46,47 +47,6 @@ typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) float lds_float;
-
-template <typename T> struct Mma;
-
-template <> struct Mma<__bf16> {
-  typedef bf16x8 frag;
-  static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-  // (a, b) rounded to nearest-even bf16, a in the low half.
-  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
-    const f32x2 x = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
-  }
-  static __device__ __forceinline__ f32x2 unpack2(uint32_t x) {
-    return __builtin_convertvector(__builtin_bit_cast(bf16x2, x), f32x2);
-  }
-  // acc + x.lo + x.hi for a packed pair (v_dot2 with (1, 1)): sums values as
-  // rounded to bf16
-  static __device__ __forceinline__ float pair_sum(uint32_t x, float acc) {
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), one, acc, false);
-  }
-};
-
-template <> struct Mma<_Float16> {
-  typedef f16x8 frag;
-  static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
-    const f32x2 x = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2));
-  }
-  static __device__ __forceinline__ f32x2 unpack2(uint32_t x) {
-    return __builtin_convertvector(__builtin_bit_cast(f16x2, x), f32x2);
-  }
-  static __device__ __forceinline__ float pair_sum(uint32_t x, float acc) {
-    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), one, acc, false);
-  }
-};
 
 // LDS image of one block of kBlk rows of a [N, D] 16-bit tensor, row-major.
 // The row stride (in bytes) is 16 * odd, so the 16 rows of one ds_read_b128
