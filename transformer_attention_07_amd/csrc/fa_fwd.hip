@@ -161,8 +161,9 @@ template <> __device__ __forceinline__ void store4<_Float16>(_Float16 *dst, f32x
   *reinterpret_cast<f16x4 *>(dst) = __builtin_convertvector(v, f16x4);
 }
 
-// Writes O = acc / lo (rows < Nq) and L = ln2 * (m + log2 l).  l and lo are
-// half-wave partial sums; lo is the normaliser of O (by default l itself).
+// Writes O = acc / lo (rows < Nq) and L = ln2 * (m + log2 l).  l is a
+// half-wave partial sum; lo, the normaliser of O, is the row's whole sum (by
+// default l itself, both halves added).
 // Four values in a storage type, as the raw register words a store takes.
 template <typename OT> struct Pack4;
 template <> struct Pack4<float> {
@@ -216,7 +217,7 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[(D < 32 ? 32 : D) /
                                          float m, float l, OT *o, float *lse, int bh,
                                          int Nq, int my_q, int g, float lo = -1.f) {
   const float lt = l + __shfl_xor(l, 32);
-  const float lot = lo < 0.f ? lt : lo + __shfl_xor(lo, 32);
+  const float lot = lo < 0.f ? lt : lo;
   if (my_q >= Nq) return;
   const float inv = 1.0f / lot;
   OT *orow = o + ((size_t)bh * Nq + my_q) * D;
@@ -250,15 +251,24 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[(D < 32 ? 32 : D) /
 //     softmax of block b, so the MFMA pipe and the VALU work side by side.
 //     With 32-row waves the causal diagonal is exactly block qw/32 of each
 //     wave; it alone is masked, later blocks are skipped.
-//   * The running maximum used as the exponent reference only moves when some
-//     row's maximum exceeds it by more than kLazy (base-2 units; a
-//     wave-uniform decision), so the accumulator is rarely rescaled; p stays
-//     below 2^kLazy and O = acc / l is unchanged.
-//   * Half-wave maxima are exchanged with v_permlane32_swap.
+//   * No row maximum per block: each block is exponentiated against the
+//     current reference, and the reference moves (to the exact maximum, with
+//     the accumulator rescaled) only when a lane's p of the block sum past
+//     2^kLazy, or on a wave's first block; the check is one compare and a
+//     wave-uniform branch.  p stays at most 2^kLazy and O = acc / l is
+//     unchanged (the update rule of the online softmax with a reference that
+//     lags the maximum; the rescaling is exact).
+//   * Half-wave maxima (on a move) are exchanged with v_permlane32_swap.
 //   * A negative scale is applied by flipping the sign bits of the Q
 //     fragments once (exact), so the folded factor c is never negative.
 
 constexpr float kLazy = 8.0f;
+// A block whose p (16 per lane) sum to more than this moves the reference.
+constexpr float kSumMax = 256.0f;  // 2^kLazy
+// Two ones of type T packed in a word (the A operand of the rounded-sum MFMA).
+template <typename T> __device__ __forceinline__ constexpr uint32_t kOne2();
+template <> __device__ __forceinline__ constexpr uint32_t kOne2<__bf16>() { return 0x3f803f80u; }
+template <> __device__ __forceinline__ constexpr uint32_t kOne2<_Float16>() { return 0x3c003c00u; }
 constexpr uint32_t kOutOfRange = 0x40000000u;  // > any slice size (checked on the host)
 constexpr int kStages = 4;
 
@@ -385,9 +395,24 @@ struct Pipe {
   static constexpr int PFK = QF < 3 ? QF : 3;   // K fragments read ahead
   static constexpr int PFV = NPV < 3 ? NPV : 3;  // V fragments read ahead
   frag kpre[PFK], vpre[PFV];
-  float m_use;
+  float m_use;  // exponent reference (base 2), the same in both half-waves
+  float nm;     // -m_use, or 0 while m_use = -inf
   float l;   // half-wave sum of p (fp32): gives L
-  float lr;  // half-wave sum of p as rounded to T for P.V: normalises O
+  // Sums of p as rounded to T for P.V (they normalise O).  LRM (D < 128):
+  // accumulated by MFMA, lracc += ones . P^T, so every register of every lane
+  // holds its query's whole rounded sum (both half-waves' keys); otherwise a
+  // v_dot2 per rounded pair into lr, this half-wave's partial sum.  v_dot2
+  // runs on the matrix pipe and does not overlap the MFMAs (measured on
+  // MI355X: about 8 cycles each); two extra MFMAs per block cost about as
+  // much, and measured faster at D = 64, slower at D = 128.
+  static constexpr bool LRM = D < 128;
+  f32x16 lracc;
+  float lr;
+  // the row's whole rounded sum
+  __device__ __forceinline__ float lr_total() const {
+    return LRM ? lracc[0] : lr + __shfl_xor(lr, 32);
+  }
+  bool fresh;   // no block of the item seen yet (wave-uniform)
 
   __device__ __forceinline__ frag kfrag(const lds_char *kp, int f) const {
     return *(const __attribute__((address_space(3))) frag *)(kp + f * 32);
@@ -416,9 +441,10 @@ struct Pipe {
     for (int f = 0; f < QF; ++f) sc = Mma<T>::mma(kfrag(kp, f), qf[f], sc);
   }
 
-  // acc += V^T P^T of a 32-key block (no overlap; drain only).  Fragments
-  // are read two MFMAs ahead, as in block_step: this runs inside the ring
-  // loop, where the S and P registers of the pipeline are still live.
+  // acc += V^T P^T of a 32-key block, and its rounded sums into lracc (no
+  // overlap; drain only).  Fragments are read two MFMAs ahead, as in
+  // block_step: this runs inside the ring loop, where the S and P registers
+  // of the pipeline are still live.
   __device__ __forceinline__ void pv(const lds_char *vp, const frag (&pin)[2]) {
     frag vf[NPV];
     vf[0] = vfrag(vp, 0);
@@ -428,6 +454,10 @@ struct Pipe {
       acc[m % NDB] = Mma<T>::mma(vf[m], pin[m / NDB], acc[m % NDB]);
       if (m + 2 < NPV) vf[m + 2] = vfrag(vp, m + 2);
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if (LRM) {
+      lr_mma(pin[0]);
+      lr_mma(pin[1]);
     }
   }
 
@@ -441,81 +471,117 @@ struct Pipe {
     }
   }
 
+  // The softmax of one block (on s, scaled to base 2 by c) against the
+  // current reference nm = -m_use, straight-line: p = 2^(c*s + nm) rounded
+  // in pairs into pw, fp32 sum into *ps, rounded sum into *rs (without LRM).
+  __device__ __forceinline__ void softmax_block(const f32x16 &s, u32x4 (&pw)[2], float &ps,
+                                                float &rs) const {
+    float psa = 0.f, psb = 0.f, rsa = 0.f, rsb = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * w], c, nm));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * w + 1], c, nm));
+      psa += p0;
+      psb += p1;
+      const uint32_t wq = Mma<T>::pack2(p0, p1);
+      pw[w / 4][w % 4] = wq;
+      if (!LRM) {
+        if (w & 1)
+          rsb = Mma<T>::pair_sum(wq, rsb);
+        else
+          rsa = Mma<T>::pair_sum(wq, rsa);
+      }
+    }
+    ps = psa + psb;
+    rs = rsa + rsb;
+  }
+
+  // lracc += ones . P^T for the 16 keys of one P.V operand (rounded sums).
+  __device__ __forceinline__ void lr_mma(const frag &p) {
+    const frag ones = __builtin_bit_cast(frag, u32x4{kOne2<T>(), kOne2<T>(), kOne2<T>(), kOne2<T>()});
+    lracc = Mma<T>::mma(ones, p, lracc);
+  }
+
+  // Moves the exponent reference to the exact maximum of block s (and of
+  // the blocks before it) and rescales what was accumulated against the old
+  // reference: acc, l and lracc by alpha = 2^(m_old - m_new).  Both half-waves
+  // of a query take the same maximum (one exchange with lane l ^ 32).  A row
+  // that has seen no key keeps m_use = -inf and nm = 0 (hidden scores are
+  // -inf, so its p stay 0).
+  __device__ __forceinline__ void move_reference(const f32x16 &s) {
+    float m3[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) m3[i] = fmaxf(fmaxf(s[3 * i], s[3 * i + 1]), s[3 * i + 2]);
+    float mx = fmaxf(fmaxf(fmaxf(m3[0], m3[1]), fmaxf(m3[2], m3[3])), fmaxf(m3[4], s[15]));
+    const u32x2 sw = __builtin_amdgcn_permlane32_swap(
+        __builtin_bit_cast(uint32_t, mx), __builtin_bit_cast(uint32_t, mx), false, false);
+    mx = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
+    const float m_new = fmaxf(m_use, mx * c);  // -inf while no key is visible
+    // exactly 1 when the reference stays (also while it is still -inf)
+    const float alpha = m_new > m_use ? __builtin_amdgcn_exp2f(m_use - m_new) : 1.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+    l *= alpha;
+    if (LRM)
+      lracc *= alpha;
+    else
+      lr *= alpha;
+    m_use = m_new;
+    nm = m_new == -INFINITY ? 0.f : -m_new;
+  }
+
   // One 32-key block, software-pipelined by hand.  The MFMA stream
   // alternates K.Q^T of the next block (into sout) with P.V of the previous
-  // block (with pin); after each MFMA the wave issues the LDS reads two
-  // MFMA pairs ahead and one slice of the softmax of this block (on sin,
-  // into pout), so the VALU work runs while the MFMA pipe is busy.  Slices:
-  //   0-1   row maximum of the block (a tree of 3-input maxima)
-  //   2     half-wave exchange, lazy move of the exponent reference, alpha
-  //   3-13  p = 2^(c*s - m) for two elements per slice, pipelined over four
-  //         stages (exponent, 2^x, fp32 sum and rounding to T into one packed
-  //         word of the P.V operand, sum of the rounded pair)
-  //   14    l, lr
-  // The reference moves per lane, only when the block's maximum exceeds it
-  // by more than kLazy (both half-waves of a query take the same decision);
-  // acc is then scaled by alpha after the block (a rare, wave-uniform
-  // branch).  O is normalised by lr, the sum of p exactly as rounded for
-  // P.V, so the weights applied to V sum to one; L uses l.  Hidden keys hold
-  // s = -inf and give p = 2^-inf = 0: c > 0 always (the host never passes
-  // 0), and a row that has not seen a key yet shifts by 0 instead of
-  // -(-inf).  One code path serves masked and unmasked blocks, so the
+  // block (with pin); after each MFMA the wave issues the LDS reads three
+  // MFMA slots ahead and one slice of the softmax of this block (on sin,
+  // into pout), so the VALU work runs while the MFMA pipe is busy.  The
+  // slices take the sixteen elements through four stages (exponent, 2^x,
+  // fp32 sums and rounding to T into one packed word of the P.V operand,
+  // the rounded pair's sum by v_dot2 unless LRM), one pair per slice, each
+  // stage one slice behind the previous; the last slice checks the block.
+  // With LRM two more MFMAs add the previous block's rounded p to lracc
+  // (ones . P^T).
+  //
+  // The exponent reference is not moved block by block.  Each block is
+  // exponentiated against the current reference (p = 2^(c*s - m_use)), and
+  // only when some lane's p of the block sum to more than 2^kLazy (so some
+  // p may exceed 2^kLazy, or overflowed), or on the wave's first block of an
+  // item, does the wave take a rare, wave-uniform path: move the reference
+  // to the exact maximum (move_reference, which rescales acc, l and lr) and
+  // recompute the block.  So every p that reaches P.V or the sums is at most
+  // 2^kLazy, as with a reference that follows the maximum lazily, without a
+  // row maximum per block.  O is normalised by lr, the sum of p exactly as
+  // rounded for P.V (the weights applied to V sum to one); L uses l.  Hidden
+  // keys hold s = -inf and give p = 0 (c > 0 always: the host never passes
+  // 0).  One code path serves masked and unmasked blocks, so the
   // accumulators stay in the same registers from block to block.
-  // PRE: the first PFK / PFV fragments of this block were read ahead into kpre
-  // and vpre, and this block reads those of the next one (kpn, vpn) in its
-  // last MFMA slots.
+  // PRE: the first PFK / PFV fragments of this block were read ahead into
+  // kpre and vpre, and this block reads those of the next one (kpn, vpn) in
+  // its last MFMA slots.
   template <bool PRE = false>
   __device__ __forceinline__ void block_step(const lds_char *kp, const lds_char *vp,
                                              f32x16 &sin, f32x16 &sout,
                                              const frag (&pin)[2], frag (&pout)[2],
                                              const lds_char *kpn = nullptr,
                                              const lds_char *vpn = nullptr) {
-    constexpr int NCHUNK = 15;
+    constexpr int NCHUNK = LRM ? 11 : 12;
     frag kf[QF], vf[NPV];
-    float mx = 0.f, nm = 0.f, alpha = 1.f;
-    float m3[5];               // partial maxima
     float ea[2], pb[2];        // pair in flight: exponents, then p
     uint32_t wq = 0;           // packed pair waiting for its rounded sum
     float psa = 0.f, psb = 0.f, rsa = 0.f, rsb = 0.f;  // two partial sums each
-    bool need = false;
+    bool over = false;
     u32x4 pw[2];  // p rounded to T, packed in pairs (the two P.V operands)
     sout = f32x16{};
 
     // Softmax slices.  The wave issues in order, so a slice holds only
-    // instructions that do not wait on each other: the row maximum is a
-    // tree, and the sixteen elements go through four stages (exponent,
-    // 2^x, fp32 sums and rounding, rounded sum) one pair per slice, each
-    // stage one slice behind the previous.
+    // instructions that do not wait on each other.
     auto chunk = [&](int ch) {
       // Each slice ends with an empty asm that uses its results: the values
       // must exist at that point, so the compiler cannot sink the slice out
-      // of its MFMA slot (e.g. past the rescale branch, towards its use).
-      if (ch == 0) {
-#pragma unroll
-        for (int i = 0; i < 5; ++i)
-          m3[i] = fmaxf(fmaxf(sin[3 * i], sin[3 * i + 1]), sin[3 * i + 2]);
-        asm volatile("" ::"v"(m3[0]), "v"(m3[1]), "v"(m3[2]), "v"(m3[3]), "v"(m3[4]));
-      } else if (ch == 1) {
-        m3[0] = fmaxf(fmaxf(m3[0], m3[1]), m3[2]);
-        m3[3] = fmaxf(fmaxf(m3[3], m3[4]), sin[15]);
-        asm volatile("" ::"v"(m3[0]), "v"(m3[3]));
-      } else if (ch == 2) {
-        mx = fmaxf(m3[0], m3[3]);
-        const u32x2 sw = __builtin_amdgcn_permlane32_swap(
-            __builtin_bit_cast(uint32_t, mx), __builtin_bit_cast(uint32_t, mx), false, false);
-        mx = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
-        const float mt = mx * c;  // -inf or NaN when the row sees no key of this block
-        need = mt > m_use + kLazy;
-        const float m_new = need ? mt : m_use;
-        // exactly 1 when the reference stays (also while it is still -inf:
-        // a fully masked first block must not turn l into NaN)
-        alpha = need ? __builtin_amdgcn_exp2f(m_use - m_new) : 1.f;
-        m_use = m_new;
-        nm = m_new == -INFINITY ? 0.f : -m_new;
-        asm volatile("" ::"v"(alpha), "v"(nm));
-      } else if (ch <= 13) {
-        const int k = ch - 3;  // stage A on pair k, B on k-1, C on k-2, D on k-3
-        if (k >= 3 && k - 3 < 8) {  // D: sum of the rounded pair
+      // of its MFMA slot (e.g. past the branch, towards its use).
+      if (ch < NCHUNK - 1) {
+        const int k = ch;  // stage A on pair k, B on k-1, C on k-2, D on k-3
+        if (!LRM && k >= 3 && k - 3 < 8) {  // D: sum of the rounded pair
           if ((k - 3) & 1)
             rsb = Mma<T>::pair_sum(wq, rsb);
           else
@@ -539,11 +605,11 @@ struct Pipe {
         asm volatile("" ::"v"(ea[0]), "v"(ea[1]), "v"(pb[0]), "v"(pb[1]), "v"(wq), "v"(psa),
                      "v"(psb), "v"(rsa), "v"(rsb));
       } else {
-        l = l * alpha + (psa + psb);
-        lr = lr * alpha + (rsa + rsb);
-        pout[0] = __builtin_bit_cast(frag, pw[0]);
-        pout[1] = __builtin_bit_cast(frag, pw[1]);
-        asm volatile("" ::"v"(l), "v"(lr));
+        psa += psb;
+        rsa += rsb;
+        // a NaN sum (never from finite inputs) does not trigger
+        over = psa > kSumMax;
+        asm volatile("" ::"v"(psa), "v"(rsa));
       }
     };
 
@@ -575,14 +641,22 @@ struct Pipe {
         else if (PRE)
           vpre[i + PFV - NPV] = vfrag(vpn, i + PFV - NPV);
       }
+      // the previous block's rounded sums, spread over the block
+      if (LRM && (i == NSL / 4 || i == NSL / 2 + NSL / 4)) lr_mma(pin[i == NSL / 4 ? 0 : 1]);
 #pragma unroll
       for (int ch = (2 * i + 1) * NCHUNK / NH; ch < (2 * i + 2) * NCHUNK / NH; ++ch) chunk(ch);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+    if (fresh || __builtin_amdgcn_ballot_w64(over) != 0) {
+      // rare: the reference moves, and the block is exponentiated again
+      move_reference(sin);
+      softmax_block(sin, pw, psa, rsa);
+      fresh = false;
     }
+    l += psa;
+    if (!LRM) lr += rsa;
+    pout[0] = __builtin_bit_cast(frag, pw[0]);
+    pout[1] = __builtin_bit_cast(frag, pw[1]);
   }
 
   // Block b of this wave (its tile-local half and ring stages given): full
@@ -645,7 +719,7 @@ __device__ __forceinline__ void epilogue_partial(const f32x16 (&acc)[(D + 31) / 
                                                  float l, float lr, float *ws_o,
                                                  float *ws_s, int row, int g) {
   const float lt = l + __shfl_xor(l, 32);
-  const float lrt = lr + __shfl_xor(lr, 32);
+  const float lrt = lr;  // already the whole row's sum
   const float inv = lrt > 0.f ? 1.0f / lrt : 0.f;
   store_row<float, (D + 31) / 32>(acc, inv, ws_o + (size_t)row * D, g, D);
   if (g == 0) {
@@ -831,8 +905,11 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
 #pragma unroll
   for (int db = 0; db < P::NDB; ++db) s.acc[db] = f32x16{};
   s.m_use = -INFINITY;
+  s.nm = 0.f;
+  s.fresh = true;
   s.l = 0.f;
   s.lr = 0.f;
+  s.lracc = f32x16{};
   s.P1[0] = frag{};  // P.V of the block before the first adds nothing
   s.P1[1] = frag{};
   s.qk(s.kptr(ring, 0, h), s.S0);
@@ -910,7 +987,8 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
   wait_vmcnt<0>();  // no DMA may outlive the ring
   ring_barrier<0>();  // every wave is done with the ring
 
-  float M = s.m_use, l = s.l, lr = s.lr;
+  // lr: the row's whole rounded sum (every lane of a query holds it)
+  float M = s.m_use, l = s.l, lr = s.lr_total();
   if constexpr (PAIR) {
     // Combine the pair: the odd wave hands (m, l, lr, acc) to the even one.
     constexpr int NR = P::NDB * 4;  // f32x4 registers of acc per lane
@@ -924,7 +1002,7 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
                            s.acc[db][4 * r4 + 3]};
           *(__attribute__((address_space(3))) f32x4 *)(xch + ((db * 4 + r4) * kWave + s.lane) * 16) = x;
         }
-      const f32x4 st = {s.m_use, s.l, s.lr, 0.f};
+      const f32x4 st = {s.m_use, s.l, lr, 0.f};
       *(__attribute__((address_space(3))) f32x4 *)(xch + (NR * kWave + s.lane) * 16) = st;
     }
     ring_barrier<0>();
@@ -939,7 +1017,7 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
       const float a0 = s.m_use == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s.m_use - M);
       const float a1 = st[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st[0] - M);
       l = s.l * a0 + st[1] * a1;
-      lr = s.lr * a0 + st[2] * a1;
+      lr = lr * a0 + st[2] * a1;
 #pragma unroll
       for (int db = 0; db < P::NDB; ++db)
 #pragma unroll
