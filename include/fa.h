@@ -155,6 +155,29 @@ int fa_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse,
               size_t workspace_bytes, void *stream);
 
 /*
+ * fa_fwd_noalloc -- fa_fwd_ws without a workspace argument and without any
+ * allocation, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Arguments, results and errors as fa_fwd_ws; the stream-K schedule's
+ * partial results go to a scratch array inside the library, one copy per
+ * device (FA_NOALLOC_SCRATCH_BYTES, held until the process ends; its
+ * address is looked up on the first call on each device).  A plan that
+ * needs more scratch than that returns FA_ERR_WORKSPACE (on devices of up
+ * to 256 compute units no plan does).  The call enqueues the same kernels
+ * as fa_fwd_ws and allocates, frees and synchronises nothing.  Every call
+ * on one device shares that device's scratch: calls that may run at the
+ * same time on one device (different streams, or graphs replayed
+ * concurrently) race and must be ordered by the caller.  Nothing in the
+ * scratch needs to start at zero (every slot a combine reads was written
+ * by the same call).
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (72u * 1024u * 1024u)
+int fa_fwd_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                   int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+                   float scale, int causal, int dtype, void *stream);
+
+/*
  * fa_fwd_varlen -- the forward pass over a variable-length batch (page
  * "FlashAttention-2实现与优化：高效注意力机制详解" §7, ragged input sequences).
  *

@@ -63,18 +63,21 @@ __all__ = [
     "FA_OK", "FA_ERR_NULLPTR", "FA_ERR_SHAPE", "FA_ERR_HEAD_DIM", "FA_ERR_DTYPE",
     "FA_ERR_SCALE", "FA_ERR_ALIGN", "FA_ERR_HIP", "FA_ERR_OVERLAP", "FA_ERR_WORKSPACE",
     "LIBRARY", "EXPORTS", "library", "fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws",
-    "fa_fwd_varlen", "fa_fwd_varlen_workspace_size", "fa_fwd_varlen_ws", "fa_fwd_masked", "fa_fwd_fp8", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_varlen", "fa_bwd_masked", "fa_status_str",
+    "fa_fwd_noalloc", "fa_fwd_varlen", "fa_fwd_varlen_workspace_size", "fa_fwd_varlen_ws", "fa_fwd_masked", "fa_fwd_fp8", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_varlen", "fa_bwd_masked", "fa_status_str",
     "fa_last_hip_error", "fa_version", "fwd", "fwd_varlen", "fwd_masked", "fwd_fp8", "bwd", "bwd_varlen", "FaError",
 ]
 
 LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+# Scratch of fa_fwd_noalloc per device (include/fa.h)
+FA_NOALLOC_SCRATCH_BYTES = 72 * 1024 * 1024
 
 FA_F32, FA_BF16, FA_BF16_OF32, FA_F16, FA_F16_OF32 = 0, 1, 2, 3, 4
 (FA_OK, FA_ERR_NULLPTR, FA_ERR_SHAPE, FA_ERR_HEAD_DIM, FA_ERR_DTYPE, FA_ERR_SCALE,
  FA_ERR_ALIGN, FA_ERR_HIP, FA_ERR_OVERLAP, FA_ERR_WORKSPACE) = range(10)
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws", "fa_fwd_varlen",
+EXPORTS = ("fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws", "fa_fwd_noalloc", "fa_fwd_varlen",
            "fa_fwd_varlen_workspace_size", "fa_fwd_varlen_ws", "fa_fwd_masked", "fa_fwd_fp8", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_varlen", "fa_bwd_masked",
            "fa_status_str", "fa_last_hip_error", "fa_version")
 
@@ -107,6 +110,9 @@ def library() -> ctypes.CDLL:
     lib.fa_fwd_ws.restype = ctypes.c_int
     lib.fa_fwd_ws.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
                               ctypes.c_int, ctypes.c_int, vp, ctypes.c_size_t, vp]
+    lib.fa_fwd_noalloc.restype = ctypes.c_int
+    lib.fa_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
+                                   ctypes.c_int, ctypes.c_int, vp]
     lib.fa_fwd_varlen.restype = ctypes.c_int
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                   ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
@@ -168,6 +174,12 @@ def fa_fwd_ws(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, dtype, ws, ws_byt
     """Raw C call; pointers are integers (device addresses) or None."""
     return int(library().fa_fwd_ws(q, k, v, o, lse, B, H, Nq, Nk, D, float(scale),
                                    int(causal), int(dtype), ws, int(ws_bytes), stream))
+
+
+def fa_fwd_noalloc(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, dtype, stream) -> int:
+    """Raw C call; pointers are integers (device addresses) or None."""
+    return int(library().fa_fwd_noalloc(q, k, v, o, lse, B, H, Nq, Nk, D, float(scale),
+                                        int(causal), int(dtype), stream))
 
 
 def fa_fwd_varlen_workspace_size(S, H, Tq, Tk, max_seqlen_q, max_seqlen_k, D, causal,

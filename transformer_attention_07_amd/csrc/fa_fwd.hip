@@ -1861,6 +1861,42 @@ __attribute__((visibility("hidden"))) int fa_internal_hip_fail(hipError_t e) {
   return hip_fail(e);
 }
 
+// Scratch of fa_fwd_noalloc: the stream-K schedule's partial results, in a
+// file-scope device array (one copy per device, held until the process
+// ends) instead of caller memory.  FA_NOALLOC_SCRATCH_BYTES covers every
+// plan make_plan produces on a device of up to 256 compute units (the
+// largest, 2 * 256 chunks * 256 rows * (128 + 4) floats, is 66 MiB).
+static __device__ __align__(256) char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up once per
+// device (hipGetSymbolAddress, with that device current) and kept: in host
+// code the array's name is a host-side stand-in, never a device address.
+int noalloc_scratch(void **ptr) {
+  static void *cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev >= 0 && dev < 64) {
+    void *p = __atomic_load_n(&cache[dev], __ATOMIC_ACQUIRE);
+    if (p) {
+      *ptr = p;
+      return FA_OK;
+    }
+  }
+  void *p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return hip_fail(e);
+  if (!p) return hip_fail(hipErrorInvalidSymbol);
+  // the same address whichever thread looks it up first
+  if (dev >= 0 && dev < 64) __atomic_store_n(&cache[dev], p, __ATOMIC_RELEASE);
+  *ptr = p;
+  return FA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int fa_version(void) { return 300; }
@@ -1936,6 +1972,27 @@ int fa_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse, 
                stream);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
   return run(q, k, v, o, lse, Nq, Nk, D, scale, causal, dtype, sh, &pl, workspace, stream);
+}
+
+int fa_fwd_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                   int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, float scale,
+                   int causal, int dtype, void *stream) {
+  Shape sh;
+  int st = validate(q, k, v, o, lse, B, H, Nq, Nk, D, scale, dtype, sh);
+  if (st != FA_OK) return st;
+  int cus = 0;
+  st = device_cus(&cus);
+  if (st != FA_OK) return st;
+  StreamPlan pl;
+  size_t need = 0;
+  if (!make_plan(sh.BH, Nq, Nk, D, dtype, causal != 0, cus, pl, need))
+    return run(q, k, v, o, lse, Nq, Nk, D, scale, causal, dtype, sh, nullptr, nullptr,
+               stream);
+  if (need > (size_t)FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_WORKSPACE;
+  void *ws = nullptr;
+  st = noalloc_scratch(&ws);
+  if (st != FA_OK) return st;
+  return run(q, k, v, o, lse, Nq, Nk, D, scale, causal, dtype, sh, &pl, ws, stream);
 }
 
 int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
