@@ -36,9 +36,14 @@ METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak (B8 N4096 D128 causal)"
 METRIC_BWD = "attention bwd TFLOP/s + % bf16 MFMA peak (2.5x fwd flops)"
 # MI355X published dense peaks (TFLOP/s).
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
-# Transcendental rate for the exp roofline of small head dims: v_exp_f32 at
-# a quarter of the 64-lane VALU rate, 16 per clock per CU (256 CUs, 2.4 GHz).
-EXP_PEAK_T = 16 * 256 * 2.4e9 / 1e12
+# Transcendental rate for the exp roofline of small head dims: v_exp_f32
+# issues a wave64 every 8 cycles per SIMD on MI355X (measured with
+# independent chains, two waves per SIMD: half the 64-lane VALU rate), so 32
+# per clock per CU (256 CUs, 2.4 GHz).
+EXP_PEAK_T = 32 * 256 * 2.4e9 / 1e12
+# dense bf16/fp16 MFMA work per clock per CU (v_mfma_f32_32x32x16: 32768 flop
+# in 32 cycles on each of the 4 SIMDs): the peak derived from the device
+BF16_FLOP_PER_CLK_CU = 4096
 HBM_GBPS = 8000.0
 CSRC = os.path.join(ROOT, "transformer_attention_07_amd", "csrc")
 FWD_SOURCES = ("fa_fwd.hip", "stream_plan.h")
@@ -66,6 +71,92 @@ def measured_traffic(workload: str):
     if t.get("source_sha256") != source_digest():
         return None
     return t.get("bytes_per_step")
+
+
+def device_facts(torch, dev):
+    """What the box reports about itself: compute units, the maximum shader
+    clock (HIP device attribute, else the highest level the driver lists in
+    sysfs), the bf16 peak they give (CUs x 4096 flop/clk x clock), the ROCm
+    version and the host CPU."""
+    import ctypes
+    import glob
+
+    props = torch.cuda.get_device_properties(dev)
+    facts = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+             "cus": props.multi_processor_count}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        val = ctypes.c_int(0)
+        # hipDeviceAttributeMultiprocessorCount checks the enum numbering
+        # before hipDeviceAttributeClockRate (kHz) is trusted
+        if (hip.hipDeviceGetAttribute(ctypes.byref(val), 65, dev.index or 0) == 0
+                and val.value == props.multi_processor_count
+                and hip.hipDeviceGetAttribute(ctypes.byref(val), 7, dev.index or 0) == 0):
+            facts["max_sclk_mhz"] = val.value / 1000.0
+    except OSError:
+        pass
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                lv = f.read().split()
+        except OSError:
+            continue
+        facts["sclk_levels"] = " ".join(lv)
+        mhz = [float(x.lower().replace("mhz", "")) for x in lv if x.lower().endswith("mhz")]
+        if mhz and "max_sclk_mhz" not in facts:
+            facts["max_sclk_mhz"] = max(mhz)  # the highest clock level the driver lists
+        break
+    if "max_sclk_mhz" in facts:
+        facts["peak_bf16_derived_tflops"] = round(
+            facts["cus"] * BF16_FLOP_PER_CLK_CU * facts["max_sclk_mhz"] * 1e6 / 1e12, 1)
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            facts["rocm"] = f.read().strip()
+    except OSError:
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    facts["host_cpu"] = ln.split(":", 1)[1].strip()
+                    break
+        facts["host_threads"] = len(os.sched_getaffinity(0))
+    except OSError:
+        pass
+    return facts
+
+
+def cpu_baseline_one_core(w, rows_n: int = 256):
+    """The same oracle on ONE host thread over rows_n seeded sampled rows
+    (seed 9), its time scaled to the whole workload by the count of visible
+    keys (extrapolated)."""
+    import numpy as np
+    import oracle
+    from workloads import gen_workload, sample_rows
+
+    q, k, v = gen_workload(w)
+    qn, kn, vn = (t.double().numpy() for t in (q, k, v))
+    scale = 1.0 / math.sqrt(w.D)
+    lib = oracle.load()
+
+    def visible(rows):
+        i = rows % w.N
+        return float((i + 1).sum() if w.causal else len(rows) * w.N)
+
+    rows = sample_rows(w.rows, min(rows_n, w.rows), 9).numpy()
+    prev = oracle.set_threads(1, lib)
+    try:
+        t0 = time.perf_counter()
+        oracle.attention(qn, kn, vn, scale, w.causal, rows=rows, lib=lib)
+        el = time.perf_counter() - t0
+    finally:
+        oracle.set_threads(prev, lib)
+    t_full = el * visible(np.arange(w.rows)) / visible(rows)
+    return {"value": w.flops() / t_full / 1e12, "unit": "TFLOP/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{len(rows)} of {w.rows} rows drawn uniformly (seed 9) on one thread; "
+                      f"time extrapolated to the whole workload by the count of visible keys",
+            "seconds": round(el, 3), "seconds_full_workload_extrapolated": round(t_full, 3)}
 
 
 def cpu_baseline(w, target_s: float):
@@ -397,6 +488,7 @@ def main() -> int:
                                f"{fa.fa_last_hip_error()}")
     torch.cuda.synchronize(dev)
 
+    facts = device_facts(torch, dev)
     # events at five evenly spaced points of the timed steps as well (no
     # synchronisation between them) give the spread of the per-step time
     groups = min(5, args.steps)
@@ -428,7 +520,6 @@ def main() -> int:
     if fp8 is not None:
         dkey = "fp8e4m3+bf16"
     achieved = flops / (kernel_ms * 1e-3) / 1e12
-    props = torch.cuda.get_device_properties(dev)
 
     metric = METRIC if not bwd else METRIC_BWD
     shape = {"B": w.B, "H": w.H, "Nq": w.N, "Nk": w.N, "D": w.D, "causal": w.causal}
@@ -469,8 +560,7 @@ def main() -> int:
                      "group_ms": {"groups": len(group_ms),
                                   "median": round(group_ms[len(group_ms) // 2], 5),
                                   "min": round(group_ms[0], 5), "max": round(group_ms[-1], 5)}},
-        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
-                   "cus": props.multi_processor_count},
+        "device": facts,
     }
     if w.D <= 64 and not bwd and masked is None:
         # one exp per visible score (half of them when causal): at small head
@@ -517,6 +607,8 @@ def main() -> int:
         else:
             line["cpu_baseline"] = (cpu_baseline_bwd(w, args.cpu_seconds) if bwd
                                     else cpu_baseline(w, args.cpu_seconds))
+            if not bwd:
+                line["cpu_baseline_one_core"] = cpu_baseline_one_core(w)
     print(json.dumps(line), flush=True)
     return 0
 

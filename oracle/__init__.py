@@ -38,6 +38,7 @@ Functions (all fp64, numpy in / numpy out):
       rule over the visible pairs), with the row sampling and magnitude sums
       of attention_bwd.
   threads() -> int   OpenMP threads the oracle uses.
+  set_threads(n) -> int   sets them (the CPU baseline's one-core run).
 
 Parity status: pinned by tests/test_oracle_pins.py (closed forms, invariants,
 brute force, a library witness and hand-derived worked examples).
@@ -97,6 +98,8 @@ def _bind(path: str):
                                                    ctypes.POINTER(i64), i64]
     lib.fa_oracle_threads.restype = ctypes.c_int
     lib.fa_oracle_threads.argtypes = []
+    lib.fa_oracle_set_threads.restype = ctypes.c_int
+    lib.fa_oracle_set_threads.argtypes = [ctypes.c_int]
     return lib
 
 
@@ -336,3 +339,8 @@ def attention_bwd_masked(q, k, v, do, scale: float, causal: bool, window: int, n
 
 def threads(lib=None) -> int:
     return int((lib or load()).fa_oracle_threads())
+
+
+def set_threads(n: int, lib=None) -> int:
+    """OpenMP threads of later oracle calls; returns the previous setting."""
+    return int((lib or load()).fa_oracle_set_threads(int(n)))

@@ -51,6 +51,21 @@ int fa_oracle_threads(void)
 #endif
 }
 
+/* Sets the OpenMP threads of later parallel regions (no effect without
+   OpenMP); returns the previous setting. */
+int fa_oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    const int prev = omp_get_max_threads();
+    if (n >= 1)
+        omp_set_num_threads(n);
+    return prev;
+#else
+    (void)n;
+    return 1;
+#endif
+}
+
 static int bad_shape(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D)
 {
     return B < 1 || H < 1 || Nq < 1 || Nk < 1 || D < 1;

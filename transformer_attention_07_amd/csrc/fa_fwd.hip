@@ -807,6 +807,17 @@ struct Dma8 {
       dma16(isk ? k_rs : v_rs, lds, off);
     }
   }
+  // The K tile alone, or the V tile alone.
+  __device__ __forceinline__ void issue_k(u32x4 k_rs, int ktile, int kst) const {
+#pragma unroll
+    for (int j = 0; j < KJ; ++j)
+      dma16(k_rs, lbase[j] + (uint32_t)kst * lstride[j], src[j] + (uint32_t)ktile * L::TILE_GLOBAL);
+  }
+  __device__ __forceinline__ void issue_v(u32x4 v_rs, int vtile, int vst) const {
+#pragma unroll
+    for (int j = KJ; j < PER_WAVE; ++j)
+      dma16(v_rs, lbase[j] + (uint32_t)vst * lstride[j], src[j] + (uint32_t)vtile * L::TILE_GLOBAL);
+  }
 };
 
 template <typename T, typename OT, int D, bool CAUSAL, bool PAIR>
@@ -887,13 +898,22 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
   // when j <= ntiles: nothing is fetched past the item except one K tile
   // whose scores are never used.  Every wave issues the same number of loads
   // per unit, so "the youngest unit may be in flight" is one vmcnt value.
-  dm.issue(k_rs, v_rs, kt0, 0, kt0, 0);
-  dm.issue(k_rs, v_rs, kt0 + 1, 1, kt0 + 1, 1);
-  if (ntiles >= 2) {
-    dm.issue(k_rs, v_rs, kt0 + 2, 2, kt0 + 2, 2);
-    ring_barrier<2 * UNIT>();
+  if constexpr (!PAIR) {
+    dm.issue(k_rs, v_rs, kt0, 0, kt0, 0);
+    dm.issue(k_rs, v_rs, kt0 + 1, 1, kt0 + 1, 1);
+    if (ntiles >= 2) {
+      dm.issue(k_rs, v_rs, kt0 + 2, 2, kt0 + 2, 2);
+      ring_barrier<2 * UNIT>();
+    } else {
+      ring_barrier<UNIT>();
+    }
   } else {
-    ring_barrier<UNIT>();
+    // K tiles 0, 1, 2 and V tile 0; the loop's first barrier waits for all
+    // of them, the prologue's for Q, K0 and V0 (K1 and K2 may be in flight)
+    dm.issue(k_rs, v_rs, kt0, 0, kt0, 0);
+    dm.issue_k(k_rs, kt0 + 1, 1);
+    dm.issue_k(k_rs, kt0 + 2, 2);
+    ring_barrier<2 * DM::KJ>();
   }
 #pragma unroll
   for (int f = 0; f < P::QF; ++f) {
@@ -958,13 +978,23 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
   } else {
     // Step r: this wave's block b = 2(kt0 + r) + h.  It reads K tile r+1
     // (half h, for the K.Q^T of block b+2) and V tile r-1 (half h, for the
-    // P.V of block b-2); loads and stage reuse as above.  Two steps per
-    // iteration: S and P alternate registers from step to step.
+    // P.V of block b-2).  Steps run in pairs (r even, r+1) under one barrier,
+    // so that the barrier and the DMA issue serve two blocks per wave: the
+    // pair reads K tiles r+1, r+2 and V tiles r-1, r, all issued before the
+    // barrier, which waits for every load in flight; after it the wave
+    // issues K tiles r+3, r+4 and V tiles r+1, r+2 into the four stages that
+    // the pair does not read (their previous tiles were last read before
+    // the barrier).  K tiles up to ntiles (one past the item: scores that
+    // are never used) and V tiles below ntiles are fetched.  S and P
+    // alternate registers from step to step.
     auto step = [&](int r, auto odd) {
-      ring_barrier_sel<UNIT>(r + 2 <= ntiles);
-      if (r + 3 <= ntiles)
-        dm.issue(k_rs, v_rs, kt0 + r + 3, (r + 3) & (kStages - 1), kt0 + r + 2,
-                 (r + 2) & (kStages - 1));
+      if ((r & 1) == 0) {
+        ring_barrier<0>();
+        if (r + 3 <= ntiles) dm.issue_k(k_rs, kt0 + r + 3, (r + 3) & (kStages - 1));
+        if (r + 4 <= ntiles) dm.issue_k(k_rs, kt0 + r + 4, r & (kStages - 1));
+        if (r + 1 < ntiles) dm.issue_v(v_rs, kt0 + r + 1, (r + 1) & (kStages - 1));
+        if (r + 2 < ntiles) dm.issue_v(v_rs, kt0 + r + 2, (r + 2) & (kStages - 1));
+      }
       const int b = 2 * (kt0 + r) + h;
       s.template block<decltype(odd)::value>(ring, b, lastb, (r + kStages - 1) & (kStages - 1),
                                                 h, (r + 1) & (kStages - 1), h);
@@ -974,7 +1004,9 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
       if (r + 1 < ntiles) step(r + 1, std::true_type{});
     }
     // Drain: P.V of this wave's last block, made in step rl: its P sits in
-    // P0 or P1 by the parity of rl.
+    // P0 or P1 by the parity of rl.  Its V tile may have been issued after
+    // the last barrier: wait for every load first.
+    ring_barrier<0>();
     const int mylast = lastb - ((lastb - h) & 1);  // last block of parity h
     if (mylast >= 2 * kt0 + h) {
       const int rl = mylast / 2 - kt0;
