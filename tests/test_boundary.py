@@ -328,3 +328,36 @@ def test_fp8_validation():
     assert call(scale=3e38, dq=1e10) == fa.FA_ERR_SCALE
     assert call(o=O + 4) == fa.FA_ERR_ALIGN
     assert call(lse=Q) == fa.FA_ERR_OVERLAP
+
+
+# --- extreme sizes: rejected, with no overflow in the size arithmetic ------
+BIG = [1 << 31, 1 << 40, 1 << 62, (1 << 63) - 1]
+
+
+@pytest.mark.parametrize("big", BIG)
+@pytest.mark.parametrize("entry,field", [
+    (call, "B"), (call, "H"), (call, "Nq"), (call, "Nk"),
+    (call_ws, "B"), (call_ws, "H"), (call_ws, "Nq"), (call_ws, "Nk"),
+    (call_bwd, "B"), (call_bwd, "H"), (call_bwd, "Nq"), (call_bwd, "Nk"),
+    (call_varlen, "S"), (call_varlen, "H"), (call_varlen, "Tq"), (call_varlen, "Tk"),
+    (call_varlen_ws, "S"), (call_varlen_ws, "H"), (call_varlen_ws, "Tq"),
+    (call_varlen_ws, "Tk"),
+    (call_bwd_varlen, "S"), (call_bwd_varlen, "H"), (call_bwd_varlen, "Tq"),
+    (call_bwd_varlen, "Tk"),
+    (call_masked, "B"), (call_masked, "H"), (call_masked, "Nq"), (call_masked, "Nk"),
+], ids=lambda x: getattr(x, "__name__", x))
+def test_extreme_sizes_rejected(entry, field, big):
+    assert entry(**{field: big}) == fa.FA_ERR_SHAPE
+
+
+@pytest.mark.parametrize("big", BIG)
+@pytest.mark.parametrize("pos", [0, 1, 2, 3])
+def test_extreme_sizes_workspace_queries(pos, big):
+    a = [2, 3, 100, 90]
+    a[pos] = big
+    assert fa.fa_fwd_workspace_size(*a, 64, 1, fa.FA_BF16)[0] == fa.FA_ERR_SHAPE
+    assert fa.fa_bwd_workspace_size(*a, 64, 1, fa.FA_BF16)[0] == fa.FA_ERR_SHAPE
+    v = [3, 2, 500, 400]
+    v[pos] = big
+    assert fa.fa_fwd_varlen_workspace_size(*v, 300, 300, 64, 1, fa.FA_BF16)[0] == \
+        fa.FA_ERR_SHAPE

@@ -8,6 +8,7 @@ reports that it does not know the feature, which is harmless.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -50,14 +51,21 @@ def _run(cmd, verbose):
         raise RuntimeError(f"hipcc failed ({res.returncode})")
 
 
-def build(out: str = LIBRARY, extra=(), verbose: bool = False) -> str:
+def build(out: str = LIBRARY, extra=(), verbose: bool = False, link_extra=()) -> str:
+    """Compiles every source (in parallel) and links `out`.  `extra` goes to
+    each compile, `link_extra` to the link (e.g. host-only sanitizer
+    flags)."""
     tmp = out + ".tmp"
-    objs = []
+    jobs = []
     for src, flags in SOURCES:
         obj = out + "." + os.path.splitext(os.path.basename(src))[0] + ".o"
-        _run([HIPCC, *FLAGS, *flags, *extra, f"-I{INCLUDE}", "-c", "-o", obj, src], verbose)
-        objs.append(obj)
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+        jobs.append((obj, [HIPCC, *FLAGS, *flags, *extra, f"-I{INCLUDE}", "-c", "-o", obj, src]))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as pool:
+        for f in [pool.submit(_run, cmd, verbose) for _, cmd in jobs]:
+            f.result()
+    objs = [obj for obj, _ in jobs]
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_extra, "-o", tmp, *objs],
+         verbose)
     for obj in objs:
         os.remove(obj)
     os.replace(tmp, out)

@@ -1590,6 +1590,17 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// Per-head slices are addressed with 32-bit byte offsets (plus slack past
+// the end for ragged rows), and the grid is one-dimensional.  PRE: B, H,
+// Nq, Nk >= 1 and D in {16, 32, 64, 128}.  No product below can overflow:
+// each factor is bounded first.
+bool sizes_fit(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D) {
+  const int64_t lim = (int64_t)1 << 31;
+  if (Nq > lim / (D * 4) - QRows<false>::value || Nk > lim / (D * 4) - 5 * kBN) return false;
+  if (B > lim || H > lim || B * H > lim) return false;
+  return B * H * ((Nq + kBM - 1) / kBM) < lim;
+}
+
 // Sizes of the arguments of one call, filled by validate().
 struct Shape {
   int64_t BH, nqt;
@@ -1607,14 +1618,9 @@ int validate(const void *q, const void *k, const void *v, const void *o, const f
   const int64_t in_size = (dtype == FA_F32) ? 4 : 2;
   const int64_t out_size =
       (dtype == FA_F32 || dtype == FA_BF16_OF32 || dtype == FA_F16_OF32) ? 4 : 2;
-  // Per-head slices are addressed with 32-bit byte offsets (plus slack past
-  // the end for ragged rows); the grid is one-dimensional.
-  const int64_t lim = (int64_t)1 << 31;
-  if (Nq > lim / (D * 4) - QRows<false>::value || Nk > lim / (D * 4) - 5 * kBN) return FA_ERR_SHAPE;
-  if (B > lim || H > lim || B * H > lim) return FA_ERR_SHAPE;
+  if (!sizes_fit(B, H, Nq, Nk, D)) return FA_ERR_SHAPE;
   sh.BH = B * H;
   sh.nqt = (Nq + kBM - 1) / kBM;
-  if (sh.BH * sh.nqt >= lim) return FA_ERR_SHAPE;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA_ERR_ALIGN;
   if ((uintptr_t)lse & 3u) return FA_ERR_ALIGN;
   sh.qb = (size_t)(sh.BH * Nq * D * in_size);
@@ -1967,8 +1973,7 @@ int fa_fwd_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t 
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
   if (D != 16 && D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
   if (dtype < FA_F32 || dtype > FA_F16_OF32) return FA_ERR_DTYPE;
-  const int64_t lim = (int64_t)1 << 31;
-  if (B > lim || H > lim || B * H > lim) return FA_ERR_SHAPE;
+  if (!sizes_fit(B, H, Nq, Nk, D)) return FA_ERR_SHAPE;
   int cus = 0;
   const int st = device_cus(&cus);
   if (st != FA_OK) return st;
