@@ -124,7 +124,9 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
  * sequence parallelism of page "FlashAttention技术演进全景图" §3.2.  The size
  * is 2 * G * R * (D + 4) * 4 bytes, G = min(compute units, units of work),
  * R the rows of a query tile in this schedule (256, or 128 at D = 128
- * when there are fewer 256-row tiles than compute units).
+ * when there are fewer 256-row tiles than compute units and the work per
+ * compute unit is under 64 tiles of 128 x 64, or, non-causal, at most one
+ * 128-row tile per compute unit).
  *
  * Returns FA_OK, FA_ERR_NULLPTR (bytes NULL), FA_ERR_SHAPE, FA_ERR_HEAD_DIM,
  * FA_ERR_DTYPE or FA_ERR_HIP (device query failed).

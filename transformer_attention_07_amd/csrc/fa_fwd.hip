@@ -307,6 +307,18 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// ring_barrier<2n> for a wave-uniform n in 0..3: n = this wave's own count
+// of K-tile loads (waves differ when a tile's instructions do not divide
+// evenly over the eight).
+__device__ __forceinline__ void ring_barrier_k2(int n) {
+  switch (n) {
+    case 0: ring_barrier<0>(); break;
+    case 1: ring_barrier<2>(); break;
+    case 2: ring_barrier<4>(); break;
+    default: ring_barrier<6>(); break;
+  }
+}
+
 // Ring wait with one per-wave load count for every wave.
 template <int N, int L = 0>
 __device__ __forceinline__ void ring_barrier_sel(bool one) {
@@ -807,16 +819,32 @@ struct Dma8 {
       dma16(isk ? k_rs : v_rs, lds, off);
     }
   }
-  // The K tile alone, or the V tile alone.
+  // The K tile alone, or the V tile alone, without the padding loads: each
+  // wave issues only its own instructions of the tile (lstride = 0 marks a
+  // padding slot, wave-uniform), so the per-wave counts differ and only
+  // waits for every load (vmcnt(0)) or for a count taken from kloads() may
+  // follow.  Measured on MI355X: +1.4% at B8 N4096 D128 causal, +2.7%
+  // non-causal (the padding loads wrote 11 of the unit's 48 KB of LDS).
   __device__ __forceinline__ void issue_k(u32x4 k_rs, int ktile, int kst) const {
 #pragma unroll
     for (int j = 0; j < KJ; ++j)
-      dma16(k_rs, lbase[j] + (uint32_t)kst * lstride[j], src[j] + (uint32_t)ktile * L::TILE_GLOBAL);
+      if (lstride[j] != 0)
+        dma16(k_rs, lbase[j] + (uint32_t)kst * lstride[j],
+              src[j] + (uint32_t)ktile * L::TILE_GLOBAL);
   }
   __device__ __forceinline__ void issue_v(u32x4 v_rs, int vtile, int vst) const {
 #pragma unroll
     for (int j = KJ; j < PER_WAVE; ++j)
-      dma16(v_rs, lbase[j] + (uint32_t)vst * lstride[j], src[j] + (uint32_t)vtile * L::TILE_GLOBAL);
+      if (lstride[j] != 0)
+        dma16(v_rs, lbase[j] + (uint32_t)vst * lstride[j],
+              src[j] + (uint32_t)vtile * L::TILE_GLOBAL);
+  }
+  // This wave's instructions of one K tile (issue_k).
+  __device__ __forceinline__ int kloads() const {
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < KJ; ++j) n += lstride[j] != 0 ? 1 : 0;
+    return n;
   }
 };
 
@@ -909,11 +937,14 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
     }
   } else {
     // K tiles 0, 1, 2 and V tile 0; the loop's first barrier waits for all
-    // of them, the prologue's for Q, K0 and V0 (K1 and K2 may be in flight)
-    dm.issue(k_rs, v_rs, kt0, 0, kt0, 0);
+    // of them, the prologue's for Q, K0 and V0 (this wave's loads of K1 and
+    // K2 may be in flight)
+    dm.issue_k(k_rs, kt0, 0);
+    dm.issue_v(v_rs, kt0, 0);
     dm.issue_k(k_rs, kt0 + 1, 1);
     dm.issue_k(k_rs, kt0 + 2, 2);
-    ring_barrier<2 * DM::KJ>();
+    static_assert(DM::KJ <= 3, "ring_barrier_k2 range");
+    ring_barrier_k2(dm.kloads());
   }
 #pragma unroll
   for (int f = 0; f < P::QF; ++f) {

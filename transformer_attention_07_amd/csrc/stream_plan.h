@@ -59,17 +59,6 @@ struct StreamPlan {
   int tail;            // empty units after each tile
 };
 
-// Layout of the stream schedule's kernel: 256-row tiles (every wave runs
-// both blocks of a step) unless D = 128 and there are fewer 256-row tiles
-// than compute units, where the pair-split 128-row layout, twice as many
-// workgroups per row, balances better (measured on MI355X: 256-row +6% at
-// one tile per CU, pair-split +5% at half a tile per CU and +15% at an
-// eighth).  D = 64 and 32 always take 256-row tiles: their blocks are
-// shorter, so sharing the per-step costs between two blocks matters more.
-inline bool stream_pair(int64_t BH, int64_t Nq, int64_t D, int cus) {
-  return D == 128 && BH * ((Nq + kGridRows - 1) / kGridRows) < (int64_t)cus;
-}
-
 // Lead units of a tile: about a piece's fixed cost (loading Q and the first
 // K/V tiles, the end-of-piece barriers and stores) in key tiles of its
 // layout; timed per piece on MI355X at about 14k cycles for D = 128 against
@@ -97,6 +86,25 @@ FA_HD inline long long prefix_nat(int t, int nkt, int tu, bool causal) {
   const int a = nkt / tu;  // tiles i < a have tu*(i+1) <= nkt key tiles
   if (t <= a) return (long long)tu * t * (t + 1) / 2;
   return (long long)tu * a * (a + 1) / 2 + (long long)(t - a) * nkt;
+}
+
+// Layout of the stream schedule's kernel at D = 128: the pair-split 128-row
+// tiles when there are fewer 256-row tiles than compute units and each
+// compute unit's share is small (under 64 units of 128 rows by 64 keys), or
+// when a non-causal call has at most one 128-row tile per compute unit (no
+// tile is then cut); otherwise 256-row tiles, which move half the K/V bytes
+// into LDS per MFMA.  Measured on MI355X (B x N, D = 128, units per compute
+// unit), pair-split against 256-row: causal B8 N4096 (33) +2.6%, B4 N2048
+// (4) +17%, non-causal B8 N4096 (64) +9%; causal B1 N16384 (64) -1.4%, B4
+// N8192 (65) -0.5%, B2 N16384 (129) -5.6%, B1 N24576 (145) -8%, B1 N32768
+// (257) -7%.  D = 64 and 32 always take 256-row tiles: their blocks are
+// shorter, so sharing the per-step costs between two blocks matters more.
+inline bool stream_pair(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, bool causal, int cus) {
+  if (D != 128 || BH * ((Nq + kGridRows - 1) / kGridRows) >= (int64_t)cus) return false;
+  const int64_t nqt = (Nq + kPairRows - 1) / kPairRows;
+  const int nkt = (int)((Nk + kKeys - 1) / kKeys);
+  if (!causal && BH * nqt <= (int64_t)cus) return true;
+  return BH * prefix_nat((int)nqt, nkt, kPairRows / kKeys, causal) < 64LL * cus;
 }
 
 // Query tile at zigzag position o, and units of positions 0..o-1 (their key
@@ -236,7 +244,7 @@ inline bool make_plan(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, int dtype, 
   if (dtype == FA_F32 || cus < 1) return false;
   const int64_t pair_rows = kPairRows;
   if (BH * ((Nq + pair_rows - 1) / pair_rows) >= 4 * (int64_t)cus) return false;
-  const bool pair = stream_pair(BH, Nq, D, cus);
+  const bool pair = stream_pair(BH, Nq, Nk, D, causal, cus);
   const int64_t qt = pair ? pair_rows : kGridRows;
   const int nkt = (int)((Nk + kKeys - 1) / kKeys);
   const int nqt = (int)((Nq + qt - 1) / qt);
