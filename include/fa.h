@@ -122,7 +122,7 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
  * "FlashAttention-2实现与优化：高效注意力机制详解" §3.1, the incremental
  * update of (m, l, o_acc)).  Cutting the work along the sequence is the
  * sequence parallelism of page "FlashAttention技术演进全景图" §3.2.  The size
- * is 2 * G * R * (D + 4) * 4 bytes, G = min(compute units, units of work),
+ * is 2 * G * R * (D + 4) * 4 bytes, G = min(compute units, 256, units of work),
  * R the rows of a query tile in this schedule (256, or 128 at D = 128
  * when there are fewer 256-row tiles than compute units and the work per
  * compute unit is under 64 tiles of 128 x 64, or, non-causal, at most one

@@ -1,11 +1,13 @@
 // Host check of the stream-K schedule of fa_fwd_ws (make_plan, ChunkWalk,
-// CutTile, make_cuts of csrc/stream_plan.h, the code the kernels and the
+// CutTile, make_tables of csrc/stream_plan.h, the code the kernels and the
 // host planner run): for many shapes, lead and tail units and
 // compute-unit counts, every key tile of every query tile is covered by
 // exactly one piece, pieces that do not cover their whole tile write to
-// distinct workspace slots, those tiles are exactly the cut list, and the
+// distinct workspace slots, those tiles are exactly the cut list, the
 // merge's enumeration of each cut tile yields exactly its pieces, whose key
-// ranges partition the tile.  Prints "ok <plans checked>" or the first
+// ranges partition the tile, and the host tables the kernels read (chunk
+// starts, cut tiles with their slots) agree with ChunkWalk::init and
+// CutTile.  Prints "ok <plans checked>" or the first
 // failure; exit status 0 on success.
 #include "../../transformer_attention_07_amd/csrc/stream_plan.h"
 
@@ -49,11 +51,18 @@ int check(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, bool causal, int cus, i
   };
   if (sp.nqt != (int)((Nq + qt - 1) / qt)) return fail("nqt", sp.nqt, qt);
   if (ws != (size_t)2 * sp.G * qt * (size_t)(D + 4) * 4 && lead < 0) return fail("ws", (long long)ws, 0);
+  ChunkStarts cs;
+  CutList tab;
+  make_tables(sp, causal, cs, tab);
   std::map<std::pair<int, int>, std::vector<Piece>> tiles;  // (bh, t) -> pieces
   std::set<int> slots;
   for (int ch = 0; ch < sp.G; ++ch) {
     ChunkWalk cw;
     cw.init(sp, ch, causal);
+    ChunkWalk tw;  // the kernels' start, from the host table
+    tw.init_at(sp, ch, cs.w[2 * ch], cs.w[2 * ch + 1]);
+    if (tw.bh != cw.bh || tw.zo != cw.zo || tw.u != cw.u || tw.left != cw.left)
+      return fail("chunk start table", ch, tw.u);
     PipeItem it;
     int t;
     while (cw.next(sp, causal, it, t)) {
@@ -82,23 +91,36 @@ int check(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, bool causal, int cus, i
       if (itr->second.size() > 1) partial.insert({bh, t});
       else if (itr->second[0].slot >= 0) return fail("lone partial", bh, t);
     }
-  CutList cl;
-  make_cuts(sp, causal, cl);
-  std::set<std::pair<int, int>> listed;
-  for (int i = 0; i < cl.n; ++i) {
+  // The cut tiles by CutTile (every boundary j) against the host table,
+  // which lists the same tiles in boundary order with the same slots; both
+  // must give exactly the pieces of the walk.
+  std::vector<int> cut_js;
+  for (int j = 1; j < sp.G; ++j) {
     CutTile ct;
-    ct.init(sp, cl.j[i], causal);
-    if (!ct.cut) return fail("cut flag", cl.j[i], 0);
+    ct.init(sp, j, causal);
+    if (ct.cut) cut_js.push_back(j);
+  }
+  if ((int)cut_js.size() != tab.n) return fail("cut count", (long long)cut_js.size(), tab.n);
+  std::set<std::pair<int, int>> listed;
+  for (int i = 0; i < tab.n; ++i) {
+    CutTile ct;
+    ct.init(sp, cut_js[i], causal);
+    const uint32_t w0 = tab.w[2 * i], w1 = tab.w[2 * i + 1];
+    if ((int)(w0 & 0xffffu) != ct.bh || (int)(w0 >> 16) != ct.t || (int)(w1 & 0xffffu) != ct.j)
+      return fail("cut table entry", i, ct.j);
     if (!listed.insert({ct.bh, ct.t}).second) return fail("cut listed twice", ct.bh, ct.t);
     std::set<int> want;
     for (const Piece &p : tiles[{ct.bh, ct.t}]) want.insert(p.slot);
-    std::set<int> got;
+    std::set<int> got, got_tab;
     for (int cc = ct.j - 1;; ++cc) {
       const int s = ct.slot(sp, cc);
       if (s < 0) break;
       got.insert(s);
     }
+    for (int k = 0; k < cut_pieces(w1); ++k) got_tab.insert(cut_slot(w1, k));
     if (got != want) return fail("merge pieces", ct.bh, ct.t);
+    if (got_tab != want || (int)got_tab.size() != cut_pieces(w1))
+      return fail("merge pieces (table)", ct.bh, ct.t);
   }
   if (listed != partial) return fail("cut set", (long long)listed.size(), (long long)partial.size());
   return 1;

@@ -1219,9 +1219,10 @@ template <typename T, typename OT, int D, bool CAUSAL, bool PAIR>
 __global__ __launch_bounds__(kThreads8) void fa_fwd_stream(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     OT *__restrict__ o, float *__restrict__ lse, float *__restrict__ ws, int Nq, int Nk,
-    float c, int negate, StreamPlan sp) {
+    float c, int negate, StreamPlan sp, ChunkStarts cs) {
   ChunkWalk cw;
-  cw.init(sp, chunk_of(blockIdx.x, sp.G), CAUSAL);
+  const int ch = chunk_of(blockIdx.x, sp.G);
+  cw.init_at(sp, ch, cs.w[2 * ch], cs.w[2 * ch + 1]);
   PipeItem it;
   int t;
   while (cw.next(sp, CAUSAL, it, t)) {
@@ -1230,7 +1231,7 @@ __global__ __launch_bounds__(kThreads8) void fa_fwd_stream(
   }
 }
 
-// Combines the pieces of the cut query tiles (CutTile), one workgroup per
+// Combines the pieces of the cut query tiles (CutList), one workgroup per
 // merge_rows<D>() rows of a tile, with a_i = 2^(m_i - M), M = max_i m_i:
 // O = sum_i a_i lr_i O_i / sum_i a_i lr_i, L = ln2 * (M + log2 sum_i a_i l_i).
 // Each thread owns one 4-wide column slice of NR rows and loads two pieces
@@ -1252,9 +1253,10 @@ __global__ __launch_bounds__(kThreads) void fa_merge_stream(const float *__restr
   constexpr int ROWS = merge_rows<D>();
   constexpr int NR = ROWS / RPP;      // rows per thread
   static_assert(NR >= 1 && ROWS % RPP == 0, "merge tiling");
-  CutTile ct;
-  ct.init(sp, cuts.j[blockIdx.x / SPLIT], CAUSAL);
-  const int j = ct.j, bh = ct.bh, t = ct.t;
+  const uint32_t w0 = cuts.w[2 * (blockIdx.x / SPLIT)];
+  const uint32_t w1 = cuts.w[2 * (blockIdx.x / SPLIT) + 1];
+  const int bh = (int)(w0 & 0xffffu), t = (int)(w0 >> 16);
+  const int np = cut_pieces(w1);
   const int rbase = (blockIdx.x % SPLIT) * ROWS;
   const int c4 = threadIdx.x % C4;
   const int r0 = rbase + threadIdx.x / C4;
@@ -1268,9 +1270,8 @@ __global__ __launch_bounds__(kThreads) void fa_merge_stream(const float *__restr
     ls[i] = lrs[i] = 0.f;
     acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  for (int cc = j - 1;; cc += 2) {
-    const int sl[2] = {ct.slot(sp, cc), ct.slot(sp, cc + 1)};
-    if (sl[0] < 0) break;
+  for (int k = 0; k < np; k += 2) {
+    const int sl[2] = {cut_slot(w1, k), k + 1 < np ? cut_slot(w1, k + 1) : -1};
     f32x4 st[2][NR], x[2][NR];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -1540,8 +1541,9 @@ struct Launch {
   int Nq, Nk, BH, nqt, nqtg;  // query tiles of kBM rows and of the 8-wave grid's rows
   float c;
   hipStream_t stream;
-  const StreamPlan *plan;  // non-null: stream-K schedule (pipelined kernel only)
-  const CutList *cuts;     // the schedule's cut tiles
+  const StreamPlan *plan;      // non-null: stream-K schedule (pipelined kernel only)
+  const ChunkStarts *starts;  // the schedule's chunk starts
+  const CutList *cuts;        // the schedule's cut tiles
 };
 
 template <typename T, typename OT, int D, bool CAUSAL>
@@ -1561,7 +1563,8 @@ hipError_t launch16(const Launch &a) {
       if (sp.tu * kKeys != QRows<PAIR>::value) return hipErrorInvalidValue;
       hipLaunchKernelGGL((fa_fwd_stream<T, OT, D, CAUSAL, PAIR>), dim3((unsigned)sp.G),
                          dim3(kThreads8), 0, a.stream, (const T *)a.q, (const T *)a.k,
-                         (const T *)a.v, (OT *)a.o, a.lse, a.ws, a.Nq, a.Nk, c, neg, sp);
+                         (const T *)a.v, (OT *)a.o, a.lse, a.ws, a.Nq, a.Nk, c, neg, sp,
+                         *a.starts);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       if (a.cuts && a.cuts->n > 0) {
@@ -1706,10 +1709,13 @@ int run(const void *q, const void *k, const void *v, void *o, float *lse, int64_
   a.c = scale * 1.4426950408889634f;
   a.stream = (hipStream_t)stream;
   a.plan = plan;
+  ChunkStarts starts;
   CutList cuts;
+  a.starts = nullptr;
   a.cuts = nullptr;
   if (plan) {
-    make_cuts(*plan, causal != 0, cuts);
+    make_tables(*plan, causal != 0, starts, cuts);
+    a.starts = &starts;
     a.cuts = &cuts;
   }
   hipError_t e;

@@ -52,7 +52,7 @@ struct StreamPlan {
   long long per_head;  // units per head
   long long cq;        // T / G
   int cr;              // T % G
-  int G;               // chunks = workgroups, 1 <= G <= min(T, 65535)
+  int G;               // chunks = workgroups, 1 <= G <= min(T, kMaxChunks)
   int nqt, nkt;        // query tiles (64*tu rows), key tiles (64 keys)
   int tu;              // key tiles per query tile on the causal diagonal: 2 or 4
   int lead;            // empty units before each tile
@@ -158,6 +158,15 @@ struct ChunkWalk {
     u = (int)(r0 - zz_prefix(zo, sp.nqt, sp.nkt, sp.tu, sp.lead + sp.tail, causal));
     first = true;
   }
+  // The same start, read from the host's table (ChunkStarts).
+  FA_HD void init_at(const StreamPlan &sp, int chunk, uint32_t w0, uint32_t w1) {
+    ch = chunk;
+    left = chunk_start(sp, ch + 1) - chunk_start(sp, ch);
+    bh = (int)(w0 & 0xffffu);
+    zo = (int)(w0 >> 16);
+    u = (int)w1;
+    first = true;
+  }
 
   FA_HD bool next(const StreamPlan &sp, bool causal, PipeItem &it, int &t) {
     const int E = sp.lead;
@@ -224,13 +233,34 @@ struct CutTile {
   }
 };
 
-// Cut query tiles of a stream-K schedule, named by the first chunk boundary
-// j that falls strictly inside each (host-computed).
-constexpr int kMaxChunks = 1024;
+// At most this many chunks (workgroups) per call: the host's tables below
+// are kernel arguments.
+constexpr int kMaxChunks = 256;
+
+// Where each chunk's walk starts (ChunkWalk::init: head, zigzag position,
+// unit within the tile), and the cut tiles with their pieces (CutTile),
+// computed on the host in one pass over the unit sequence and passed to the
+// kernels as arguments: on the device, ChunkWalk::init costs a 64-bit
+// division and a binary search per workgroup (about 1.7 us at the
+// kernel's start, measured on MI355X), and CutTile::init the same per
+// combining workgroup.
+struct ChunkStarts {
+  uint32_t w[2 * kMaxChunks];  // chunk c: bh | zo << 16, u
+};
+// Cut i: w[2i] = bh | t << 16; w[2i+1] = j | pieces << 16 | odd << 31,
+// where j is the first chunk boundary strictly inside the tile's key tiles,
+// the pieces are those of chunks j-1, j, ..., j+pieces-2, with workspace
+// slots 2(j-1) + odd (odd: chunk j-1 holds key tiles of an earlier tile, so
+// this is its last piece) and 2c for c >= j (their first pieces).
 struct CutList {
   int n;
-  uint16_t j[kMaxChunks - 1];
+  uint32_t w[2 * (kMaxChunks - 1)];
 };
+FA_HD inline int cut_slot(uint32_t w1, int k) {
+  const int j = (int)(w1 & 0xffffu);
+  return k == 0 ? 2 * (j - 1) + (int)(w1 >> 31) : 2 * (j - 1 + k);
+}
+FA_HD inline int cut_pieces(uint32_t w1) { return (int)((w1 >> 16) & 0x7fffu); }
 
 // Stream-K schedule of the pipelined kernel (16-bit inputs): one
 // chunk per compute unit.  With four or more 128-row query tiles per compute
@@ -244,6 +274,8 @@ inline bool make_plan(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, int dtype, 
   if (dtype == FA_F32 || cus < 1) return false;
   const int64_t pair_rows = kPairRows;
   if (BH * ((Nq + pair_rows - 1) / pair_rows) >= 4 * (int64_t)cus) return false;
+  // the tables hold head and tile indices in 16 bits
+  if (BH > 0xffff || (Nq + pair_rows - 1) / pair_rows > 0xffff) return false;
   const bool pair = stream_pair(BH, Nq, Nk, D, causal, cus);
   const int64_t qt = pair ? pair_rows : kGridRows;
   const int nkt = (int)((Nk + kKeys - 1) / kKeys);
@@ -278,14 +310,40 @@ FA_HD inline int varlen_split(int nkt, int NC, int KC, int &kc) {
   return (nkt + kc - 1) / kc;
 }
 
-// The cut tiles of a schedule (CutTile::cut for j = 1 .. G-1).
-inline void make_cuts(const StreamPlan &sp, bool causal, CutList &cl) {
+// The tables of a plan, in one pass over its tiles (heads in order, each
+// head's tiles in zigzag order), with the chunk boundaries b(c) =
+// chunk_start(c) advancing alongside: chunk c starts in the tile whose units
+// [lead start, end of tail) hold b(c); a tile is cut iff some boundary j
+// lies strictly inside its key tiles (s0 < b(j) < s1), the first such j
+// naming it (as CutTile).  The same as ChunkWalk::init and CutTile for
+// every chunk and boundary (checked on the host over many plans).
+inline void make_tables(const StreamPlan &sp, bool causal, ChunkStarts &cs, CutList &cl) {
+  const long long BH = sp.T / sp.per_head;
+  int c = 0;   // next chunk start to place
+  int jj = 0;  // first boundary after the current tile's first key tile
+  long long base = 0;
   cl.n = 0;
-  for (int j = 1; j < sp.G; ++j) {
-    CutTile ct;
-    ct.init(sp, j, causal);
-    if (ct.cut) cl.j[cl.n++] = (uint16_t)j;
-  }
+  for (long long bh = 0; bh < BH; ++bh)
+    for (int zo = 0; zo < sp.nqt; ++zo) {
+      const int t = zz_tile(zo, sp.nqt);
+      const long long s0 = base + sp.lead;
+      const long long s1 = s0 + tile_w(t, sp.nkt, sp.tu, causal);
+      const long long end = s1 + sp.tail;
+      for (; c < sp.G && chunk_start(sp, c) < end; ++c) {
+        cs.w[2 * c] = (uint32_t)bh | ((uint32_t)zo << 16);
+        cs.w[2 * c + 1] = (uint32_t)(chunk_start(sp, c) - base);
+      }
+      while (jj < sp.G && chunk_start(sp, jj) <= s0) ++jj;
+      if (jj >= 1 && jj < sp.G && chunk_start(sp, jj) < s1) {
+        int pieces = 1;
+        for (int cc = jj; cc < sp.G && chunk_start(sp, cc) < s1; ++cc) ++pieces;
+        const bool odd = chunk_start(sp, jj - 1) < base - sp.tail;
+        cl.w[2 * cl.n] = (uint32_t)bh | ((uint32_t)t << 16);
+        cl.w[2 * cl.n + 1] = (uint32_t)jj | ((uint32_t)pieces << 16) | (odd ? 1u << 31 : 0u);
+        ++cl.n;
+      }
+      base = end;
+    }
 }
 
 
