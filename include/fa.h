@@ -289,10 +289,12 @@ int fa_fwd_varlen_ws(const void *q, const void *k, const void *v, void *o,
  *   dtype      FA_BF16, FA_BF16_OF32, FA_F16 or FA_F16_OF32 (FA_F32:
  *              FA_ERR_DTYPE)
  *
- * Key blocks and 32-key quarters in which no pair is visible are never
- * read or computed, so the work is proportional to the visible pairs
- * (rounded up to 128 x 32 blocks).  Status codes as fa_fwd; window < 1 or
- * nglobal < 0 is FA_ERR_SHAPE.
+ * It runs fa_fwd's pipelined kernel, one workgroup per 256-row query tile,
+ * over that tile's 64-key tiles that hold a visible pair: the global
+ * tokens' tiles, then the band's.  Scores of hidden pairs inside those tiles
+ * are masked, so the work is proportional to the visible pairs, rounded up
+ * to whole tiles.  Status codes as fa_fwd; window < 1 or nglobal < 0 is
+ * FA_ERR_SHAPE.
  */
 int fa_fwd_masked(const void *q, const void *k, const void *v, void *o, float *lse,
                   int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,

@@ -21,8 +21,6 @@ SOURCES = [
     (os.path.join(PKG, "csrc", "fa_fwd.hip"), ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
     # the backward kernels keep their dK/dV/dQ accumulators in AGPRs
     (os.path.join(PKG, "csrc", "fa_bwd.hip"), []),
-    # local-window + global-token forward (same tile helpers as the backward)
-    (os.path.join(PKG, "csrc", "fa_masked.hip"), []),
     # FP8 (e4m3) forward
     (os.path.join(PKG, "csrc", "fa_fp8.hip"), []),
 ]

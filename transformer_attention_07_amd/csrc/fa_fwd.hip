@@ -42,6 +42,7 @@
 #include <string.h>
 
 #include "fa.h"
+#include "mask.h"
 #include "mma16.h"
 #include "stream_plan.h"
 
@@ -219,7 +220,8 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[(D < 32 ? 32 : D) /
   const float lt = l + __shfl_xor(l, 32);
   const float lot = lo < 0.f ? lt : lo;
   if (my_q >= Nq) return;
-  const float inv = 1.0f / lot;
+  // a row that saw no key (possible under the window mask) stores O = 0
+  const float inv = lot > 0.f ? 1.0f / lot : 0.f;
   OT *orow = o + ((size_t)bh * Nq + my_q) * D;
   store_row<OT, (D < 32 ? 32 : D) / 32>(acc, inv, orow, g, D);
   if (g == 0) lse[(size_t)bh * Nq + my_q] = (m + log2f(lt)) * 0.69314718055994531f;
@@ -383,7 +385,15 @@ __device__ __forceinline__ void dma16(u32x4 rs, uint32_t lds_addr, uint32_t voff
                : "memory");
 }
 
-template <typename T, typename OT, int D, bool CAUSAL>
+// Key tiles of one query tile under the local-window + global-token mask, as
+// a list of two ranges: list entry v < n1 is key tile v (the global tokens'
+// tiles), later entries are band tiles b0 + (v - n1).  Without the mask, or
+// when the two ranges meet, the list is the identity (n1 = b0).
+struct KeyList {
+  int n1, b0;
+};
+
+template <typename T, typename OT, int D, bool CAUSAL, bool MASKED = false>
 struct Pipe {
   typedef typename Mma<T>::frag frag;
   typedef PipeLayout<T, D> L;
@@ -397,6 +407,21 @@ struct Pipe {
 
   int lane, wave, l32, g, qw, my_q, Nk;
   float c;
+  Mask mk;     // the window rule (MASKED)
+  KeyList kl;  // the item's key tiles (MASKED)
+  // Key tile of list entry v, and first key of list block b (32 keys).
+  __device__ __forceinline__ int kt_act(int v) const {
+    return MASKED ? (v < kl.n1 ? v : kl.b0 + (v - kl.n1)) : v;
+  }
+  __device__ __forceinline__ int key0(int b) const {
+    return MASKED ? kt_act(b >> 1) * kBN + (b & 1) * 32 : b * 32;
+  }
+  // Does list block b need the per-score mask (some pair hidden, or keys
+  // past Nk)?
+  __device__ __forceinline__ bool needs_mask(int k0) const {
+    if (MASKED) return k0 + 32 > Nk || !mk.all(qw, qw + 31, k0, k0 + 31);
+    return (k0 + 32 > Nk) || (CAUSAL && k0 + 31 > qw);
+  }
   uint32_t kbase, vbase;  // per-lane LDS byte addresses of fragment 0
   frag qf[QF];
   f32x16 acc[NDB];
@@ -478,7 +503,8 @@ struct Pipe {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = k0 + acc_row(r, g);
-      const bool hidden = (key >= Nk) || (CAUSAL && key > my_q);
+      const bool hidden =
+          MASKED ? (key >= Nk || !mk.visible(my_q, key)) : ((key >= Nk) || (CAUSAL && key > my_q));
       sc[r] = hidden ? -INFINITY : sc[r];
     }
   }
@@ -525,9 +551,19 @@ struct Pipe {
 #pragma unroll
     for (int i = 0; i < 5; ++i) m3[i] = fmaxf(fmaxf(s[3 * i], s[3 * i + 1]), s[3 * i + 2]);
     float mx = fmaxf(fmaxf(fmaxf(m3[0], m3[1]), fmaxf(m3[2], m3[3])), fmaxf(m3[4], s[15]));
-    const u32x2 sw = __builtin_amdgcn_permlane32_swap(
-        __builtin_bit_cast(uint32_t, mx), __builtin_bit_cast(uint32_t, mx), false, false);
-    mx = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
+    // v_permlane32_swap exchanges the upper half of its first register with
+    // the lower half of its second; with both holding mx, each lane finds
+    // its partner's maximum in one of the two results.  The results are
+    // copied to scalars before the bit casts: __builtin_bit_cast of an
+    // element of an ext_vector_type value reads element 0 whatever the index
+    // (seen with this compiler), which had reduced the maximum to the lower
+    // half's (a row whose keys of the block all sit in the upper half kept
+    // its reference at -inf).
+    const u32x2 sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mx),
+                                                      __builtin_bit_cast(uint32_t, mx), false,
+                                                      false);
+    const uint32_t sw0 = sw[0], sw1 = sw[1];
+    mx = fmaxf(__builtin_bit_cast(float, sw0), __builtin_bit_cast(float, sw1));
     const float m_new = fmaxf(m_use, mx * c);  // -inf while no key is visible
     // exactly 1 when the reference stays (also while it is still -inf)
     const float alpha = m_new > m_use ? __builtin_amdgcn_exp2f(m_use - m_new) : 1.f;
@@ -663,7 +699,9 @@ struct Pipe {
       // rare: the reference moves, and the block is exponentiated again
       move_reference(sin);
       softmax_block(sin, pw, psa, rsa);
-      fresh = false;
+      // under the window mask a block may hide every key of some row: the
+      // wave stays on this path until each of its rows has a reference
+      fresh = MASKED ? __builtin_amdgcn_ballot_w64(m_use == -INFINITY) != 0 : false;
     }
     l += psa;
     if (!LRM) lr += rsa;
@@ -685,9 +723,8 @@ struct Pipe {
     const lds_char *kp = kptr(ring, kst, khalf);
     const lds_char *vp = vptr(ring, vst, vhalf);
     if (b <= lastb) {
-      const int k0 = b * 32;
-      const bool need_mask = (k0 + 32 > Nk) || (CAUSAL && k0 + 31 > qw);
-      if (need_mask) mask(sin, k0);
+      const int k0 = key0(b);
+      if (needs_mask(k0)) mask(sin, k0);
       block_step(kp, vp, sin, sout, pin, pout);
     }
   }
@@ -704,9 +741,8 @@ struct Pipe {
     frag(&pin)[2] = ODD ? P0 : P1;
     frag(&pout)[2] = ODD ? P1 : P0;
     if (b <= lastb) {
-      const int k0 = b * 32;
-      const bool need_mask = (k0 + 32 > Nk) || (CAUSAL && k0 + 31 > qw);
-      if (need_mask) mask(sin, k0);
+      const int k0 = key0(b);
+      if (needs_mask(k0)) mask(sin, k0);
       block_step<true>(kptr(ring, kst, khalf), vptr(ring, vst, vhalf), sin, sout, pin, pout,
                        kptr(ring, kst_n, khalf_n), vptr(ring, vst_n, vhalf_n));
     }
@@ -852,13 +888,17 @@ struct Dma8 {
   }
 };
 
-template <typename T, typename OT, int D, bool CAUSAL, bool PAIR>
+// MASKED (256-row layout only): the item's key tiles are the list kl (its
+// kt0, kt1 index the list), scores follow the window rule mk.
+template <typename T, typename OT, int D, bool CAUSAL, bool PAIR, bool MASKED = false>
 __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__restrict__ k,
                                           const T *__restrict__ v, OT *__restrict__ o,
                                           float *__restrict__ lse, float *__restrict__ ws,
                                           int Nq, int Nk, float c, int negate,
-                                          const PipeItem it, int nslots) {
-  typedef Pipe<T, OT, D, CAUSAL> P;
+                                          const PipeItem it, int nslots, const Mask mk = Mask{},
+                                          const KeyList kl = KeyList{}) {
+  static_assert(!(MASKED && PAIR), "the window mask runs in the 256-row layout");
+  typedef Pipe<T, OT, D, CAUSAL, MASKED> P;
   typedef typename P::L L;
   typedef typename P::frag frag;
   typedef Dma8<T, D> DM;
@@ -892,6 +932,8 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
   }
   s.qw = it.q0 + qg * 32;
   s.my_q = s.qw + s.l32;
+  s.mk = mk;
+  s.kl = kl;
   const size_t qoff = (size_t)it.bh * Nq * D;
   const size_t koff = (size_t)it.bh * Nk * D;
   const u32x4 q_rs = raw_rsrc(q + qoff, (uint32_t)Nq * D * sizeof(T));
@@ -902,8 +944,28 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
 
   const int kt0 = it.kt0;
   const int ntiles = it.kt1 - it.kt0;
-  // last 32-key block (absolute index) this query group needs in this item
-  const int lastb = CAUSAL ? min(2 * it.kt1 - 1, s.qw / 32) : 2 * it.kt1 - 1;
+  // last 32-key block (absolute index; MASKED: index in the list) this
+  // query group needs in this item
+  int lastb = CAUSAL ? min(2 * it.kt1 - 1, s.qw / 32) : 2 * it.kt1 - 1;
+  if constexpr (MASKED && CAUSAL) {
+    // The group's last visible key is its diagonal, 0-3 key tiles before the
+    // end of the tile's list (which ends at the tile's last query): the
+    // drain after the loop finds its V tile still in the ring.  Without the
+    // causal rule every group runs to the end of the list (its blocks past
+    // its band are all hidden): a group's band may end four key tiles
+    // before the list does, or many more when the tile holds global queries,
+    // and its V tile would have left the ring by the drain.
+    const int lk = min(Nk - 1, s.qw + 31);
+    const int at = lk / kBN;
+    int vb;
+    if (at < kl.n1)
+      vb = 2 * at + ((lk >> 5) & 1);
+    else if (at >= kl.b0)
+      vb = 2 * (at - kl.b0 + kl.n1) + ((lk >> 5) & 1);
+    else
+      vb = 2 * kl.n1 - 1;  // in the gap between the ranges: the global tiles' last block
+    lastb = min(2 * it.kt1 - 1, vb);
+  }
 
   // Q first: its loads are the oldest in flight, so the prologue wait for
   // the first K/V unit covers them too.
@@ -931,10 +993,10 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
   // whose scores are never used.  Every wave issues the same number of loads
   // per unit, so "the youngest unit may be in flight" is one vmcnt value.
   if constexpr (!PAIR) {
-    dm.issue(k_rs, v_rs, kt0, 0, kt0, 0);
-    dm.issue(k_rs, v_rs, kt0 + 1, 1, kt0 + 1, 1);
+    dm.issue(k_rs, v_rs, s.kt_act(kt0), 0, s.kt_act(kt0), 0);
+    dm.issue(k_rs, v_rs, s.kt_act(kt0 + 1), 1, s.kt_act(kt0 + 1), 1);
     if (ntiles >= 2) {
-      dm.issue(k_rs, v_rs, kt0 + 2, 2, kt0 + 2, 2);
+      dm.issue(k_rs, v_rs, s.kt_act(kt0 + 2), 2, s.kt_act(kt0 + 2), 2);
       ring_barrier<2 * UNIT>();
     } else {
       ring_barrier<UNIT>();
@@ -990,8 +1052,8 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
     for (int r = 0; r < ntiles; ++r) {
       ring_barrier_sel<UNIT, RA>(r + 2 <= ntiles);
       if (r + 3 <= ntiles)
-        dm.issue(k_rs, v_rs, kt0 + r + 3, (r + 3) & (kStages - 1), kt0 + r + 2,
-                 (r + 2) & (kStages - 1));
+        dm.issue(k_rs, v_rs, s.kt_act(kt0 + r + 3), (r + 3) & (kStages - 1),
+                 s.kt_act(kt0 + r + 2), (r + 2) & (kStages - 1));
       const int st0 = r & (kStages - 1);
       const int stm = (r + kStages - 1) & (kStages - 1);
       const int st1 = (r + 1) & (kStages - 1);
@@ -1111,16 +1173,65 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
   }
 }
 
-template <typename T, typename OT, int D, bool CAUSAL, bool PAIR>
+// Key tiles of the query tile at rows [q0, q0 + QT) under the window rule
+// mk (window <= max(Nq, Nk) as clamped by the host, so nothing overflows):
+// the global tokens' key tiles (causal: keys j <= the tile's last query),
+// then the band's, [q0 - window + 1, last query (+ window - 1 non-causal)];
+// every key tile for a non-causal tile holding global queries.  *n is the
+// list's length (0: the tile sees no key).
+__device__ __forceinline__ KeyList key_list(const Mask &mk, int q0, int QT, int Nq, int Nk,
+                                            int *n) {
+  const int qlast = min(q0 + QT, Nq) - 1;
+  const int nkt = (Nk + kBN - 1) / kBN;
+  if (!mk.causal && q0 < mk.nglobal) {
+    *n = nkt;
+    return {nkt, nkt};
+  }
+  const int gend = mk.causal ? min(min(mk.nglobal, Nk), qlast + 1) : min(mk.nglobal, Nk);
+  const int n1 = (gend + kBN - 1) / kBN;
+  const int blo = max(0, q0 - mk.window + 1);
+  const int bhi = mk.causal ? min(Nk - 1, qlast) : min(Nk - 1, qlast + mk.window - 1);
+  if (blo > bhi) {  // no band key
+    *n = n1;
+    return {n1, n1};
+  }
+  const int b0 = blo / kBN, b1 = bhi / kBN + 1;
+  if (b0 <= n1) {  // the ranges meet: one range from tile 0
+    *n = max(n1, b1);
+    return {*n, *n};
+  }
+  *n = n1 + (b1 - b0);
+  return {n1, b0};
+}
+
+// One workgroup per (batch*head, query tile), longest causal tiles first.
+// MASKED: the tile's key tiles are its key_list under the window rule mk; a
+// tile that sees no key writes O = 0 and L = -inf.
+template <typename T, typename OT, int D, bool CAUSAL, bool PAIR, bool MASKED = false>
 __global__ __launch_bounds__(kThreads8) void fa_fwd_pipe8(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     OT *__restrict__ o, float *__restrict__ lse, int Nq, int Nk, int BH, int nqt,
-    float c, int negate) {
+    float c, int negate, Mask mk) {
   constexpr int QT = QRows<PAIR>::value;
   const WorkItem wi = work_item(BH, nqt, CAUSAL, QT);
-  const int kend = CAUSAL ? min(Nk, wi.q0 + QT) : Nk;
-  const PipeItem it = {wi.bh, wi.q0, 0, (kend + kBN - 1) / kBN, -1};
-  pipe8_run<T, OT, D, CAUSAL, PAIR>(q, k, v, o, lse, nullptr, Nq, Nk, c, negate, it, 0);
+  if constexpr (MASKED) {
+    int n;
+    const KeyList kl = key_list(mk, wi.q0, QT, Nq, Nk, &n);
+    if (n == 0) {
+      const int rows = min(QT, Nq - wi.q0);
+      const size_t r0 = (size_t)wi.bh * Nq + wi.q0;
+      for (int i = threadIdx.x; i < rows * D; i += kThreads8) o[r0 * D + i] = (OT)0.f;
+      for (int i = threadIdx.x; i < rows; i += kThreads8) lse[r0 + i] = -INFINITY;
+      return;
+    }
+    const PipeItem it = {wi.bh, wi.q0, 0, n, -1};
+    pipe8_run<T, OT, D, CAUSAL, PAIR, true>(q, k, v, o, lse, nullptr, Nq, Nk, c, negate, it, 0,
+                                            mk, kl);
+  } else {
+    const int kend = CAUSAL ? min(Nk, wi.q0 + QT) : Nk;
+    const PipeItem it = {wi.bh, wi.q0, 0, (kend + kBN - 1) / kBN, -1};
+    pipe8_run<T, OT, D, CAUSAL, PAIR>(q, k, v, o, lse, nullptr, Nq, Nk, c, negate, it, 0);
+  }
 }
 
 // Variable-length batches (page "FlashAttention-2实现与优化：高效注意力机制详解"
@@ -1544,6 +1655,8 @@ struct Launch {
   const StreamPlan *plan;      // non-null: stream-K schedule (pipelined kernel only)
   const ChunkStarts *starts;  // the schedule's chunk starts
   const CutList *cuts;        // the schedule's cut tiles
+  bool masked;                // the window rule mk (grid path only)
+  Mask mk;
 };
 
 template <typename T, typename OT, int D, bool CAUSAL>
@@ -1581,11 +1694,16 @@ hipError_t launch16(const Launch &a) {
     else
       e = go(std::false_type{});
     if (e != hipSuccess) return e;
+  } else if (a.masked) {
+    hipLaunchKernelGGL((fa_fwd_pipe8<T, OT, D, CAUSAL, false, true>),
+                       dim3((unsigned)(a.BH * a.nqtg)), dim3(kThreads8), 0, a.stream,
+                       (const T *)a.q, (const T *)a.k, (const T *)a.v, (OT *)a.o, a.lse,
+                       a.Nq, a.Nk, a.BH, a.nqtg, c, neg, a.mk);
   } else {
     hipLaunchKernelGGL((fa_fwd_pipe8<T, OT, D, CAUSAL, false>),
                        dim3((unsigned)(a.BH * a.nqtg)), dim3(kThreads8), 0, a.stream,
                        (const T *)a.q, (const T *)a.k, (const T *)a.v, (OT *)a.o, a.lse,
-                       a.Nq, a.Nk, a.BH, a.nqtg, c, neg);
+                       a.Nq, a.Nk, a.BH, a.nqtg, c, neg, Mask{});
   }
   return hipGetLastError();
 }
@@ -1693,8 +1811,10 @@ int device_cus(int *cus) {
 
 int run(const void *q, const void *k, const void *v, void *o, float *lse, int64_t Nq,
         int64_t Nk, int64_t D, float scale, int causal, int dtype, const Shape &sh,
-        const StreamPlan *plan, void *ws, void *stream) {
+        const StreamPlan *plan, void *ws, void *stream, const Mask *mk = nullptr) {
   Launch a;
+  a.masked = mk != nullptr;
+  a.mk = mk ? *mk : Mask{};
   a.q = q;
   a.k = k;
   a.v = v;
@@ -2005,6 +2125,28 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int
   const int st = validate(q, k, v, o, lse, B, H, Nq, Nk, D, scale, dtype, sh);
   if (st != FA_OK) return st;
   return run(q, k, v, o, lse, Nq, Nk, D, scale, causal, dtype, sh, nullptr, nullptr, stream);
+}
+
+// The local-window + global-token forward: validated as fa_fwd (16-bit
+// inputs only), the window clamped to max(Nq, Nk) (which already covers
+// every |i - j|, and keeps the rule's arithmetic in 32 bits), then one
+// workgroup per 256-row query tile of the pipelined kernel over that tile's
+// key-tile list (key_list).
+int fa_fwd_masked(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
+                  int64_t H, int64_t Nq, int64_t Nk, int64_t D, float scale, int causal,
+                  int64_t window, int64_t nglobal, int dtype, void *stream) {
+  Shape sh;
+  const int st = validate(q, k, v, o, lse, B, H, Nq, Nk, D, scale, dtype, sh);
+  if (st != FA_OK) return st;
+  if (window < 1 || nglobal < 0) return FA_ERR_SHAPE;
+  if (dtype == FA_F32) return FA_ERR_DTYPE;
+  const int64_t wmax = Nq > Nk ? Nq : Nk;
+  Mask mk;
+  mk.causal = causal != 0;
+  mk.window = (int)(window < wmax ? window : wmax);
+  mk.nglobal = (int)(nglobal < wmax ? nglobal : wmax);  // >= max(Nq, Nk): every token
+  return run(q, k, v, o, lse, Nq, Nk, D, scale, causal, dtype, sh, nullptr, nullptr, stream,
+             &mk);
 }
 
 int fa_fwd_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,

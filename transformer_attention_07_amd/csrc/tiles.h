@@ -1,5 +1,5 @@
-// tiles.h -- MFMA tile helpers shared by the backward kernels (fa_bwd.hip)
-// and the masked forward kernel (fa_masked.hip): v_mfma_f32_32x32x16 on
+// tiles.h -- MFMA tile helpers of the backward kernels (fa_bwd.hip) and the
+// FP8 forward (fa_fp8.hip): v_mfma_f32_32x32x16 on
 // 16-bit operands, LDS images of 128-row blocks, register-staged loads,
 // row-wise and transposed (ds_read_b64_tr_b16) A-operand fragments, and
 // stores of transposed 32x32 accumulators.  Each including file keeps its
