@@ -226,39 +226,50 @@ int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *l
  * no query tile is split, and then fa_fwd_varlen_ws is fa_fwd_varlen).
  *
  * Arguments as fa_fwd_varlen, plus max_seqlen_k (>= 0), an estimate of the
- * longest key length.  Together with max_seqlen_q it bounds the work of the
- * call; a tile whose key range is longer than the call's share per compute
- * unit is cut into several chunks (sequence parallelism, page
- * "FlashAttention技术演进全景图" §3.2), each run by its own workgroup, whose
- * partial results are combined with the online-softmax rescaling of page
- * "FlashAttention-2实现与优化：高效注意力机制详解" §3.1 by a second kernel.
- * Without the split one workgroup runs the longest sequence's last tile and
- * bounds the call.  Returns FA_OK, or the shape / head-dim / dtype errors
- * of fa_fwd_varlen, FA_ERR_NULLPTR (bytes NULL) or FA_ERR_HIP.
+ * longest key length; 0 asks for no split.  Two schedules split work over
+ * the keys (sequence parallelism, page "FlashAttention技术演进全景图"
+ * §3.2), and a second kernel combines the partial results with the
+ * online-softmax rescaling of page
+ * "FlashAttention-2实现与优化：高效注意力机制详解" §3.1:
+ *   - at most 512 (head, sequence) pairs (H * S <= 512): a stream
+ *     schedule.  G = min(compute units, 256) workgroups each take an equal
+ *     share of the call's (query tile, 64-key tile) units, counted from the
+ *     offsets in device memory, so the work is balanced whatever the
+ *     lengths; a query tile cut between two workgroups is combined by the
+ *     second kernel.  Workspace: 2 G partial tiles of 128 or 256 rows by
+ *     (D + 4) fp32, rounded up to 256 bytes, and 12 G bytes for the cuts.
+ *   - more pairs: a tile whose key range is longer than the call's share
+ *     per compute unit (bounded with max_seqlen_q and max_seqlen_k) is cut
+ *     into at most 16 chunks, each run by its own workgroup.
+ * Returns FA_OK, or the shape / head-dim / dtype errors of fa_fwd_varlen,
+ * FA_ERR_NULLPTR (bytes NULL) or FA_ERR_HIP.
  */
 int fa_fwd_varlen_workspace_size(int64_t S, int64_t H, int64_t Tq, int64_t Tk,
                                  int64_t max_seqlen_q, int64_t max_seqlen_k,
                                  int64_t D, int causal, int dtype, size_t *bytes);
 
 /*
- * fa_fwd_varlen_ws -- fa_fwd_varlen with key-split tiles and caller-owned
- * device scratch.
+ * fa_fwd_varlen_ws -- fa_fwd_varlen with work split over the keys and
+ * caller-owned device scratch.
  *
  * Arguments as fa_fwd_varlen, plus
- *   max_seqlen_k     as for fa_fwd_varlen_workspace_size; it steers the
- *                    split only: every tile is computed whatever the real
- *                    lengths (a tile gets at most a fixed number of chunks,
- *                    which grow with its key range)
+ *   max_seqlen_k     as for fa_fwd_varlen_workspace_size; with max_seqlen_q
+ *                    it steers the schedule only (which one, the tile
+ *                    height, the chunk sizes): every key is seen whatever
+ *                    the real lengths
  *   workspace        device pointer, 16-byte aligned, of at least the bytes
  *                    fa_fwd_varlen_workspace_size reports for the same
  *                    arguments, or NULL when it reports 0
  *   workspace_bytes  its size in bytes
  *
  * Results as fa_fwd_varlen up to the order of the fp32 summation (split
- * tiles add their chunks' partial sums in a different order).  Calls that
- * share a workspace must be ordered on one stream.  Errors as fa_fwd_varlen,
- * plus FA_ERR_WORKSPACE (workspace NULL or too small), FA_ERR_ALIGN and
- * FA_ERR_OVERLAP for the workspace.
+ * tiles add their chunks' partial sums in a different order), with one
+ * difference under the stream schedule (H * S <= 512): it walks the offsets
+ * themselves, so the rows of a sequence longer than max_seqlen_q are all
+ * computed instead of set to NaN.  Calls that share a workspace must be
+ * ordered on one stream.  Errors as fa_fwd_varlen, plus FA_ERR_WORKSPACE
+ * (workspace NULL or too small), FA_ERR_ALIGN and FA_ERR_OVERLAP for the
+ * workspace.
  */
 int fa_fwd_varlen_ws(const void *q, const void *k, const void *v, void *o,
                      float *lse, const int32_t *cu_seqlens_q,

@@ -1,5 +1,6 @@
-"""GPU parity of variable-length batches (fa_fwd_varlen, fa_fwd_varlen_ws
-with key-split tiles, through the C ABI)
+"""GPU parity of variable-length batches (fa_fwd_varlen, and fa_fwd_varlen_ws
+with its stream schedule over (head, sequence) pairs or, past 512 pairs,
+its key-split tiles; through the C ABI)
 against the fp64 oracle (oracle.attention_varlen), with the forward's
 tolerances: fp32 O <= 1e-2 and L <= 1e-3 for 16-bit inputs, 16-bit O the
 exact rounding of the fp32 O and within 1e-2 plus half an ulp.  Each
@@ -56,7 +57,8 @@ def run(q, k, v, cu_q, cu_k, maxq, causal, scale, out_dtype, maxk=None):
 
 def compare(lq, lk, H, D, causal, seed, dtype="bf16", scale=None, rows=None, solo=True,
             maxk=None):
-    """maxk: run fa_fwd_varlen_ws with this max_seqlen_k (key-split tiles)."""
+    """maxk: run fa_fwd_varlen_ws with this max_seqlen_k (the stream
+    schedule at H * S <= 512 pairs, key-split tiles above)."""
     q, k, v, cu_q, cu_k = packed(lq, lk, H, D, seed, dtype)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     maxq = max(lq) if max(lq) > 0 else 1
@@ -173,9 +175,10 @@ def test_varlen_32k_tokens_sampled():
     compare(lens, lens, 1, 128, True, seed=1800, rows=rows)
 
 
-# --- key-split tiles (fa_fwd_varlen_ws) --------------------------------------
-# Lengths with long sequences next to short ones: tiles of the long ones span
-# more than eight 64-key tiles and are cut into 2-4 chunks; the rest run whole.
+# --- work split over the keys (fa_fwd_varlen_ws) ------------------------------
+# Lengths with long sequences next to short ones.  At these head counts the
+# stream schedule runs: the call's units are dealt evenly over the compute
+# units, so the long sequences' tiles are cut between workgroups and merged.
 SPLIT = [1, 2000, 31, 700, 1500, 64, 5]
 
 
@@ -210,17 +213,6 @@ def test_varlen_split_underestimated_keys():
     compare(SPLIT, SPLIT, 2, 128, False, seed=2401, maxk=1500)
 
 
-def test_varlen_split_matches_unsplit_on_short_tiles():
-    """Tiles the plan leaves whole are computed exactly as fa_fwd_varlen does."""
-    q, k, v, cu_q, cu_k = packed(SPLIT, SPLIT, 1, 128, 2500)
-    a = run(q, k, v, cu_q, cu_k, 2000, True, 0.1, torch.float32)
-    b = run(q, k, v, cu_q, cu_k, 2000, True, 0.1, torch.float32, maxk=2000)
-    # the 64-row sequence (rows 4232 .. 4295) has one tile with one key tile
-    s = slice(int(cu_q[5]), int(cu_q[6]))
-    assert s.stop - s.start == 64
-    assert torch.equal(a[0][:, s], b[0][:, s]) and torch.equal(a[1][:, s], b[1][:, s])
-
-
 def test_varlen_split_32k_tokens_sampled():
     """The shape bench.py --varlen 32 --split times (32768 tokens in 32
     sequences, D=128, causal bf16): 512 sampled rows against the oracle."""
@@ -237,13 +229,37 @@ def test_varlen_split_one_long_sequence_sampled():
     compare(lens, lens, 1, 128, True, seed=1900, rows=rows, maxk=max(lens))
 
 
-def test_varlen_split_not_taken_for_two_shares():
-    """32768 tokens in 8 sequences: the longest tile makes two shares, too few
-    to split (workspace 0; fa_fwd_varlen_ws is then fa_fwd_varlen)."""
+def test_varlen_stream_8_sequences_and_many_heads():
+    """The stream schedule over (head, sequence) pairs: 8 sequences of the
+    32768-token mix (the shape bench.py --varlen 8 --split times), and 48
+    short sequences over 3 heads with empty ones between them (sampled
+    rows against the oracle)."""
     lens = varlen_lengths(32768, 8, seed=77, min_len=64)
     st, nb = fa.fa_fwd_varlen_workspace_size(8, 1, 32768, 32768, max(lens), max(lens), 128,
                                              True, fa.FA_BF16)
-    assert st == 0 and nb == 0
+    assert st == 0 and nb > 0
+    rows = sample_rows(32768, 384, 7700).numpy()
+    compare(lens, lens, 1, 128, True, seed=1700, rows=rows, maxk=max(lens))
+    r = np.random.default_rng(7701)
+    lq = [int(x) for x in r.integers(0, 300, 48)]
+    lk = [int(x) if i % 7 else 0 for i, x in enumerate(r.integers(0, 300, 48))]
+    lq[5] = 0
+    compare(lq, lk, 3, 64, False, seed=1710, maxk=max(lk))
+    compare(lq, lq, 3, 128, True, seed=1720, maxk=max(lq))
+
+
+def test_varlen_stream_computes_rows_past_max_seqlen_q():
+    """Under the stream schedule the offsets alone decide the work: with
+    max_seqlen_q and max_seqlen_k far below the real lengths every row is
+    still computed, bit-identical to the call with true bounds of the same
+    tile height (both below the pair-split bound here: D = 64)."""
+    lq, lk = [1000, 50, 700], [1000, 50, 900]
+    q, k, v, cu_q, cu_k = packed(lq, lk, 2, 64, 3450)
+    scale = 0.125
+    full = run(q, k, v, cu_q, cu_k, 1000, True, scale, torch.float32, maxk=1000)
+    short = run(q, k, v, cu_q, cu_k, 100, True, scale, torch.float32, maxk=60)
+    assert torch.isfinite(short[0]).all() and torch.isfinite(short[1]).all()
+    assert torch.equal(short[0], full[0]) and torch.equal(short[1], full[1])
 
 
 def test_varlen_split_graph_capture_replays_match_eager():

@@ -429,8 +429,9 @@ def fwd_varlen(q, k, v, cu_q, cu_k, max_seqlen_q: int, causal: bool = False,
 
     q: [H, Tq, D]; k, v: [H, Tk, D] (bf16 or fp16, contiguous, one device);
     cu_q, cu_k: int32 device tensors of S + 1 offsets (0, ..., Tq / Tk).
-    With ``max_seqlen_k`` given, long tiles are split over their keys
-    (fa_fwd_varlen_ws, workspace allocated here).
+    With ``max_seqlen_k`` given, the work is split over the keys
+    (fa_fwd_varlen_ws, workspace allocated here): a stream schedule over
+    the (head, sequence) pairs up to 512 of them, key-split tiles above.
     Returns (o [H, Tq, D] in ``out_dtype``, lse [H, Tq] fp32).
     """
     import torch

@@ -1326,6 +1326,235 @@ __device__ __forceinline__ int chunk_of(int g, int G) {
   return (G % 8 == 0) ? (g % 8) * (G / 8) + g / 8 : g;
 }
 
+// Rows of a cut tile per combining workgroup (16 rows at D = 128, 64 at
+// D = 64: measured fastest on MI355X; the workgroup's fixed cost of
+// locating the tile weighs against fewer loads in flight per thread).
+template <int D>
+constexpr int merge_rows() { return D == 128 ? 16 : 64; }
+
+// ---------------------------------------------------------------------------
+// Stream-K schedule for variable-length batches (the dense schedule's
+// balance, for packed sequences of any lengths).  The units are those of the
+// dense schedule, laid out (head, sequence) pair by pair (p = h * S + s),
+// each pair's query tiles in zigzag order with `lead` empty units before
+// each tile; chunk c of G' = min(G, T) holds units [c T / G', (c+1) T / G').
+// The offsets are in device memory, so every workgroup derives the plan
+// itself at its start: the units of each pair (from the offsets), their
+// prefix sums (in LDS), and by binary search where its chunk starts.  The
+// workgroup of chunk j also records whether boundary j cuts a tile (as
+// CutTile) in entry j of the workspace's cut table, which the combining
+// kernel reads; every entry is written by every call.
+constexpr int kVPairs = 512;  // (head, sequence) pairs: one per thread of the workgroup
+
+// Rows, keys and tiles of pair p (offsets clamped to [0, T]: any offsets
+// stay inside the tensors).
+struct VPair {
+  int h, s, qa, ka, nq, nk, ntiles, nkt;
+};
+__device__ __forceinline__ VPair vpair(const int *cu_q, const int *cu_k, int S, int Tq, int Tk,
+                                       int p, int QT) {
+  VPair r;
+  r.h = p / S;
+  r.s = p % S;
+  r.qa = max(0, min(cu_q[r.s], Tq));
+  const int qb = max(r.qa, min(cu_q[r.s + 1], Tq));
+  r.ka = max(0, min(cu_k[r.s], Tk));
+  const int kb = max(r.ka, min(cu_k[r.s + 1], Tk));
+  r.nq = qb - r.qa;
+  r.nk = kb - r.ka;
+  r.ntiles = (r.nq + QT - 1) / QT;
+  r.nkt = (r.nk + kBN - 1) / kBN;
+  return r;
+}
+__device__ __forceinline__ long long vpair_units(const VPair &v, int tu, int lead, bool causal) {
+  if (v.nq == 0 || v.nk == 0) return 0;
+  return prefix_nat(v.ntiles, v.nkt, tu, causal) + (long long)lead * v.ntiles;
+}
+
+template <typename T, typename OT, int D, bool CAUSAL, bool PAIR>
+__global__ __launch_bounds__(kThreads8) void fa_fwd_stream_varlen(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    OT *__restrict__ o, float *__restrict__ lse, float *__restrict__ ws,
+    const int *__restrict__ cu_q, const int *__restrict__ cu_k, int S, int H, int Tq, int Tk,
+    float c, int negate, uint32_t *__restrict__ cuts, int G) {
+  constexpr int QT = QRows<PAIR>::value;
+  constexpr int tu = QT / kBN;
+  constexpr int LEAD = stream_lead(D, PAIR);
+  static_assert(kThreads8 >= kVPairs, "one pair per thread");
+  __shared__ long long pre[kVPairs + 1];
+  const int NP = H * S;
+  const int tid = threadIdx.x;
+  // units of each pair, then their inclusive prefix sums
+  if (tid < NP) {
+    const VPair vp = vpair(cu_q, cu_k, S, Tq, Tk, tid, QT);
+    pre[tid + 1] = vpair_units(vp, tu, LEAD, CAUSAL);
+  }
+  if (tid == 0) pre[0] = 0;
+  __syncthreads();
+  for (int off = 1; off < NP; off <<= 1) {
+    const long long x = (tid < NP && tid >= off) ? pre[tid + 1 - off] : 0;
+    __syncthreads();
+    if (tid < NP) pre[tid + 1] += x;
+    __syncthreads();
+  }
+  const long long TT = pre[NP];
+  const int Ge = (int)(TT < G ? TT : G);
+  // sequences with queries and no keys (no units): O = 0, L = -inf, their
+  // pairs dealt to the workgroups
+  for (int p = blockIdx.x; p < NP; p += G) {
+    if (pre[p + 1] != pre[p]) continue;
+    const VPair vp = vpair(cu_q, cu_k, S, Tq, Tk, p, QT);
+    if (vp.nq == 0 || vp.nk != 0) continue;
+    const size_t r0 = (size_t)vp.h * Tq + vp.qa;
+    for (int i = tid; i < vp.nq * D; i += kThreads8) o[r0 * D + i] = (OT)0.f;
+    for (int i = tid; i < vp.nq; i += kThreads8) lse[r0 + i] = -INFINITY;
+  }
+  if ((int)blockIdx.x >= Ge) {  // workgroup-uniform, before any barrier below
+    if (tid == 0) cuts[3 * blockIdx.x + 2] = 0;  // boundary blockIdx.x: no cut
+    return;
+  }
+  const long long cq = TT / Ge;
+  const int cr = (int)(TT - cq * Ge);
+  // floor(c T / G'): c r < G'^2 <= 2^16
+  auto bnd = [&](int cc) { return (long long)cc * cq + (cc * cr) / Ge; };
+  // the pair holding unit b: the last p with pre[p] <= b (pairs without
+  // units have pre[p] = pre[p + 1] and are passed over)
+  auto find = [&](long long b) {
+    int lo = 0, hi = NP - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= b) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
+  const int ch = chunk_of(blockIdx.x, Ge);
+  const long long b0 = bnd(ch);
+  int p = find(b0);
+  VPair vp = vpair(cu_q, cu_k, S, Tq, Tk, p, QT);
+  const int zo0 = zz_find(b0 - pre[p], vp.ntiles, vp.nkt, tu, LEAD, CAUSAL);
+  const long long sl0 = pre[p] + zz_prefix(zo0, vp.ntiles, vp.nkt, tu, LEAD, CAUSAL);
+  int zo = zo0, u = (int)(b0 - sl0);
+  // boundary ch: does it cut the tile holding it (strictly inside its key
+  // tiles, the previous boundary at or before them)?
+  if (tid == 0) {
+    uint32_t w1 = 0, tt = 0;
+    if (ch >= 1) {
+      const int t = zz_tile(zo0, vp.ntiles);
+      const long long s0 = sl0 + LEAD, s1 = s0 + tile_w(t, vp.nkt, tu, CAUSAL);
+      const long long bp = bnd(ch - 1);
+      if (b0 > s0 && b0 < s1 && bp <= s0) {
+        int pieces = 1;
+        for (int cc = ch; cc < Ge && bnd(cc) < s1; ++cc) ++pieces;
+        // chunk ch-1 holds key tiles of an earlier tile: this is its last piece
+        w1 = (uint32_t)ch | ((uint32_t)pieces << 16) | (bp < sl0 ? 1u << 31 : 0u);
+        tt = (uint32_t)t;
+      }
+    }
+    cuts[3 * ch] = (uint32_t)p;
+    cuts[3 * ch + 1] = tt;
+    cuts[3 * ch + 2] = w1;
+  }
+  long long left = bnd(ch + 1) - b0;
+  bool first = true;
+  while (left > 0 && p < NP) {
+    if (vp.nq == 0 || vp.nk == 0) {  // a pair without units
+      vp = vpair(cu_q, cu_k, S, Tq, Tk, ++p < NP ? p : NP - 1, QT);
+      zo = 0;
+      continue;
+    }
+    const int t = zz_tile(zo, vp.ntiles);
+    const int w = tile_w(t, vp.nkt, tu, CAUSAL);
+    const int span = LEAD + w;
+    const int u1 = left < (long long)(span - u) ? u + (int)left : span;
+    const int kt0 = u <= LEAD ? 0 : (u - LEAD < w ? u - LEAD : w);
+    const int kt1 = u1 <= LEAD ? 0 : (u1 - LEAD < w ? u1 - LEAD : w);
+    left -= u1 - u;
+    u = 0;
+    const VPair cur = vp;
+    if (++zo == vp.ntiles) {
+      zo = 0;
+      if (++p < NP) vp = vpair(cu_q, cu_k, S, Tq, Tk, p, QT);
+    }
+    if (kt1 > kt0) {
+      PipeItem it = {0, t * QT, kt0, kt1, (kt0 == 0 && kt1 == w) ? -1 : 2 * ch + (first ? 0 : 1)};
+      first = false;
+      const size_t qo = (size_t)cur.h * Tq + cur.qa, ko = (size_t)cur.h * Tk + cur.ka;
+      pipe8_run<T, OT, D, CAUSAL, PAIR>(q + qo * D, k + ko * D, v + ko * D, o + qo * D,
+                                        lse + qo, ws, cur.nq, cur.nk, c, negate, it, 2 * G);
+    }
+  }
+}
+
+// Combines the pieces of the varlen stream schedule's cut tiles, as
+// fa_merge_stream: the workgroups of boundary j read entry j of the cut
+// table (written by the stream kernel) and stop unless it names a cut.
+template <typename OT, int D, int QT>
+__global__ __launch_bounds__(kThreads) void fa_merge_stream_varlen(
+    const float *__restrict__ ws, OT *__restrict__ o, float *__restrict__ lse,
+    const int *__restrict__ cu_q, const int *__restrict__ cu_k, int S, int Tq, int Tk,
+    const uint32_t *__restrict__ cuts, int G) {
+  constexpr int C4 = D / 4;
+  constexpr int RPP = kThreads / C4;
+  constexpr int SPLIT = QT / merge_rows<D>();
+  constexpr int ROWS = merge_rows<D>();
+  constexpr int NR = ROWS / RPP;
+  static_assert(NR >= 1 && ROWS % RPP == 0, "merge tiling");
+  const uint32_t *cut = cuts + 3 * (1 + blockIdx.x / SPLIT);  // boundary 1 + blockIdx / SPLIT
+  const uint32_t w1 = cut[2];
+  if (w1 == 0) return;  // not a cut
+  const int p = (int)cut[0], t = (int)cut[1];
+  const int np = cut_pieces(w1);
+  const VPair vp = vpair(cu_q, cu_k, S, Tq, Tk, p, QT);
+  const int rbase = (blockIdx.x % SPLIT) * ROWS;
+  const int c4 = threadIdx.x % C4;
+  const int r0 = rbase + threadIdx.x / C4;
+  const float *ws_s = ws + (size_t)2 * G * QT * D;
+  float M[NR], ls[NR], lrs[NR];
+  f32x4 acc[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    M[i] = -INFINITY;
+    ls[i] = lrs[i] = 0.f;
+    acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int kk = 0; kk < np; kk += 2) {
+    const int sl[2] = {cut_slot(w1, kk), kk + 1 < np ? cut_slot(w1, kk + 1) : -1};
+    f32x4 st[2][NR], x[2][NR];
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        if (sl[uu] < 0) continue;
+        const size_t e = (size_t)sl[uu] * QT + r0 + i * RPP;
+        st[uu][i] = *reinterpret_cast<const f32x4 *>(ws_s + e * 4);
+        x[uu][i] = *reinterpret_cast<const f32x4 *>(ws + e * D + 4 * c4);
+      }
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        if (sl[uu] < 0 || st[uu][i][0] == -INFINITY) continue;  // no key of this row
+        const float Mn = fmaxf(M[i], st[uu][i][0]);
+        const float a_old = exp2f(M[i] - Mn);  // 0 while M = -inf
+        const float a = exp2f(st[uu][i][0] - Mn);
+        ls[i] = ls[i] * a_old + a * st[uu][i][1];
+        lrs[i] = lrs[i] * a_old + a * st[uu][i][2];
+        acc[i] = acc[i] * a_old + (a * st[uu][i][2]) * x[uu][i];
+        M[i] = Mn;
+      }
+  }
+  const size_t base = (size_t)vp.h * Tq + vp.qa + (size_t)t * QT;
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int r = r0 + i * RPP;
+    if (t * QT + r < vp.nq) {
+      store4<OT>(o + (base + r) * D + 4 * c4, acc[i] * (1.0f / lrs[i]));
+      if (c4 == 0) lse[base + r] = (M[i] + log2f(ls[i])) * 0.69314718055994531f;
+    }
+  }
+}
+
+
 template <typename T, typename OT, int D, bool CAUSAL, bool PAIR>
 __global__ __launch_bounds__(kThreads8) void fa_fwd_stream(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
@@ -1347,11 +1576,6 @@ __global__ __launch_bounds__(kThreads8) void fa_fwd_stream(
 // O = sum_i a_i lr_i O_i / sum_i a_i lr_i, L = ln2 * (M + log2 sum_i a_i l_i).
 // Each thread owns one 4-wide column slice of NR rows and loads two pieces
 // per round trip.
-// (16 rows at D = 128, 64 at D = 64: measured fastest on MI355X; the
-// workgroup's fixed cost of locating the tile weighs against fewer loads
-// in flight per thread)
-template <int D>
-constexpr int merge_rows() { return D == 128 ? 16 : 64; }
 
 template <typename OT, int D, bool CAUSAL, int QT>
 __global__ __launch_bounds__(kThreads) void fa_merge_stream(const float *__restrict__ ws,
@@ -1861,6 +2085,8 @@ struct VarlenArgs {
   float c;
   float *ws;        // partial results of split tiles (NC > 1)
   int NC, KC, NT;   // chunks per tile at most, 64-key tiles per chunk at least, tile ids per head
+  int G;            // > 0: the stream schedule with G workgroups (plan at ws + plan_off)
+  size_t plan_off;
   hipStream_t stream;
 };
 
@@ -1873,6 +2099,21 @@ hipError_t launch_varlen(const VarlenArgs &a) {
   auto go = [&](auto pair) -> hipError_t {
     constexpr bool PAIR = decltype(pair)::value;
     constexpr int QT = QRows<PAIR>::value;
+    if (a.G > 0) {
+      uint32_t *cuts = (uint32_t *)((char *)a.ws + a.plan_off);
+      hipLaunchKernelGGL((fa_fwd_stream_varlen<T, OT, D, CAUSAL, PAIR>), dim3((unsigned)a.G),
+                         dim3(kThreads8), 0, a.stream, (const T *)a.q, (const T *)a.k,
+                         (const T *)a.v, (OT *)a.o, a.lse, a.ws, a.cu_q, a.cu_k, a.S, a.H,
+                         a.Tq, a.Tk, c, neg, cuts, a.G);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess || a.G < 2) return e;
+      constexpr int SPLIT = QT / merge_rows<D>();
+      hipLaunchKernelGGL((fa_merge_stream_varlen<OT, D, QT>),
+                         dim3((unsigned)((a.G - 1) * SPLIT)), dim3(kThreads), 0, a.stream,
+                         (const float *)a.ws, (OT *)a.o, a.lse, a.cu_q, a.cu_k, a.S, a.Tq,
+                         a.Tk, (const uint32_t *)cuts, a.G);
+      return hipGetLastError();
+    }
     const int ntiles = (a.maxq + QT - 1) / QT;
     hipLaunchKernelGGL((fa_fwd_varlen<T, OT, D, CAUSAL, PAIR>),
                        dim3((unsigned)(ntiles * a.H * a.S * a.NC)), dim3(kThreads8), 0,
@@ -1930,7 +2171,10 @@ int varlen_shape(int64_t S, int64_t H, int64_t Tq, int64_t Tk, int64_t max_seqle
 // are long on average (measured on 32768 tokens, causal, unsplit: 8
 // sequences +9% with pair-split, 32 sequences -15%: short sequences are
 // dominated by the fixed cost of a tile, which the finer tiles double).
-// Split (max_seqlen_k > 0): the work is at most Tq * max_seqlen_q / 2
+// Stream (max_seqlen_k > 0 and H * S <= kVPairs): the units of every
+// (head, sequence) pair, counted by each workgroup from the offsets, dealt
+// evenly over G workgroups; see the rule in varlen_plan.
+// Split (max_seqlen_k > 0, more pairs): the work is at most Tq * max_seqlen_q / 2
 // (causal) or Tq * max_seqlen_k row-key pairs, in units of one tile's rows
 // by 64 keys; a chunk gets at least that divided by the compute units (and
 // at least kMinChunk units, against the fixed cost of a piece), and a tile
@@ -1939,6 +2183,8 @@ int varlen_shape(int64_t S, int64_t H, int64_t Tq, int64_t Tk, int64_t max_seqle
 struct VarlenSplit {
   bool pair;
   int NC, KC, NT;
+  int G;            // > 0: stream schedule over G workgroups
+  size_t plan_off;  // its cut table in the workspace
   size_t bytes;
 };
 constexpr int kMinChunk = 8;
@@ -1955,8 +2201,30 @@ int varlen_plan(int64_t S, int64_t H, int64_t Tq, int64_t Tk, int64_t max_seqlen
   sp.NC = 1;
   sp.KC = 1;
   sp.NT = 1;
+  sp.G = 0;
+  sp.plan_off = 0;
   sp.bytes = 0;
   if (max_seqlen_k < 1) return FA_OK;
+  if (H * S <= kVPairs) {
+    // Stream schedule: one workgroup per compute unit (at most kMaxChunks,
+    // whose partials the workspace holds).  Pair-split tiles at D = 128 when
+    // the packed rows make fewer 256-row tiles than compute units and a
+    // compute unit's share of 128 x 64 units, bounded above by taking every
+    // sequence as long as the longest, stays under 64 (the dense rule's
+    // bound).  Measured on 32768 tokens, causal: 8 sequences of up to 10278
+    // tokens (bound 80) ran 8% faster on 256-row tiles, 32 (bound 26) tied,
+    // 128 (bound 9) ran 9% faster pair-split.
+    const int64_t mq = max_seqlen_q < Tq ? max_seqlen_q : Tq;
+    const int64_t mk = max_seqlen_k < Tk ? max_seqlen_k : Tk;
+    const int64_t share = H * (causal ? Tq * mq / 2 : Tq * mk) / (kPairRows * kBN);
+    sp.pair = D == 128 && H * ((Tq + QRows<false>::value - 1) / QRows<false>::value) < cus &&
+              share < 64LL * cus;
+    const int64_t QT = sp.pair ? kPairRows : QRows<false>::value;
+    sp.G = cus < fa_sched::kMaxChunks ? cus : fa_sched::kMaxChunks;
+    sp.plan_off = ((size_t)2 * sp.G * (size_t)QT * (size_t)(D + 4) * 4 + 255) / 256 * 256;
+    sp.bytes = sp.plan_off + (size_t)3 * 4 * sp.G;  // the cut table
+    return FA_OK;
+  }
   const int64_t QT = sp.pair ? kPairRows : QRows<false>::value;
   const int64_t mq = max_seqlen_q < Tq ? max_seqlen_q : Tq;
   const int64_t mk = max_seqlen_k < Tk ? max_seqlen_k : Tk;
@@ -2039,6 +2307,8 @@ int varlen_entry(const void *q, const void *k, const void *v, void *o, float *ls
   a.NC = sp.NC;
   a.KC = sp.KC;
   a.NT = sp.NT;
+  a.G = sp.G;
+  a.plan_off = sp.plan_off;
   a.stream = (hipStream_t)stream;
   const bool cz = causal != 0;
   hipError_t e;
