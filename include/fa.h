@@ -106,9 +106,10 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
 /*
  * fa_fwd_workspace_size -- device scratch bytes that fa_fwd_ws needs for
  * this problem on the current device (written to *bytes; 0 when fa_fwd_ws
- * takes the same path as fa_fwd: fp32 inputs, or at least four
- * query tiles of 128 rows per compute unit, where one workgroup per tile
- * already keeps every unit busy).
+ * takes the same path as fa_fwd: 16-bit inputs with at least four query
+ * tiles of 128 rows per compute unit, or fp32 inputs with at least one per
+ * compute unit, where one workgroup per tile already keeps every unit
+ * busy, or a single 64-key tile per query tile).
  *
  * One workgroup per query tile leaves compute units idle when tiles are
  * few or, under the causal mask, of very unequal length.  fa_fwd_ws instead
@@ -127,6 +128,12 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
  * when there are fewer 256-row tiles than compute units and the work per
  * compute unit is under 64 tiles of 128 x 64, or, non-causal, at most one
  * 128-row tile per compute unit).
+ *
+ * fp32 inputs take a simpler split: each 128-row query tile's keys are cut
+ * into n <= 4 chunks of KC 64-key tiles (KC the smallest length that keeps
+ * the workgroups within one per compute unit), each chunk run by its own
+ * workgroup and the chunks combined by a second kernel as above.  The size
+ * is then T * n * 128 * (D + 4) * 4 bytes for T query tiles.
  *
  * Returns FA_OK, FA_ERR_NULLPTR (bytes NULL), FA_ERR_SHAPE, FA_ERR_HEAD_DIM,
  * FA_ERR_DTYPE or FA_ERR_HIP (device query failed).

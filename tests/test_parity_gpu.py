@@ -262,8 +262,9 @@ def test_split_shapes(shape, causal, dtype):
 
 
 def test_split_workspace_contract():
-    """Missing or short scratch is refused before any launch; fp32 and small
-    head dims need none; the workspace size does not depend on O's type."""
+    """Missing or short scratch is refused before any launch; the workspace
+    size does not depend on O's type; fp32 inputs take scratch for their key
+    split only when query tiles are few, and none for a single key tile."""
     B, H, Nq, Nk, D = 1, 1, 2048, 2048, 128
     q, k, v = (t.to(DEV) for t in gen_qkv(B, H, Nq, Nk, D, seed=1, dtype="bf16"))
     o = torch.empty_like(q)
@@ -271,9 +272,10 @@ def test_split_workspace_contract():
     need = _ws_bytes(B, H, Nq, Nk, D, 1, fa.FA_BF16)
     assert need > 0
     assert need == _ws_bytes(B, H, Nq, Nk, D, 1, fa.FA_BF16_OF32)
-    assert _ws_bytes(B, H, Nq, Nk, D, 1, fa.FA_F32) == 0
-    assert _ws_bytes(B, H, Nq, Nk, 16, 1, fa.FA_F32) == 0
     cus = torch.cuda.get_device_properties(DEV).multi_processor_count
+    assert _ws_bytes(B, H, Nq, Nk, D, 1, fa.FA_F32) > 0
+    assert _ws_bytes(1, 1, 64, 64, 16, 1, fa.FA_F32) == 0  # one key tile
+    assert _ws_bytes(2 * cus, 1, 128, 2048, 64, 0, fa.FA_F32) == 0  # many query tiles
     assert _ws_bytes(4 * cus, 1, 128, 128, D, 1, fa.FA_BF16) == 0  # many tiles
     ws = torch.empty(need, dtype=torch.uint8, device=DEV)
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
@@ -284,7 +286,7 @@ def test_split_workspace_contract():
     assert fa.fa_fwd_ws(*args, ws.data_ptr() + 8, need - 8, sp) == fa.FA_ERR_ALIGN
     assert fa.fa_fwd_ws(*args, o.data_ptr(), need, sp) == fa.FA_ERR_OVERLAP
     assert fa.fa_fwd_ws(*args, ws.data_ptr(), need, sp) == fa.FA_OK
-    # a path without a schedule (fp32 inputs) runs without scratch
+    # a call that needs no scratch runs without it
     q32, k32, v32 = (t.to(DEV) for t in gen_qkv(1, 1, 64, 64, 16, seed=2, dtype="f32"))
     o32 = torch.empty_like(q32)
     l32 = torch.empty(q32.shape[:-1], dtype=torch.float32, device=DEV)
@@ -292,6 +294,29 @@ def test_split_workspace_contract():
              1, 1, 64, 64, 16, 0.1, 1, fa.FA_F32)
     assert fa.fa_fwd_ws(*small, None, 0, sp) == fa.FA_OK
     torch.cuda.synchronize()
+
+
+SPLIT32 = [
+    # (B, H, Nq, Nk, D): fp32 shapes whose query tiles leave compute units
+    # idle, so the fp32 kernel splits their keys
+    (1, 1, 1000, 1000, 64),
+    (2, 1, 300, 2100, 128),  # 128-row tiles with a 44-row tail
+    (1, 3, 129, 4000, 16),
+    (1, 1, 64, 640, 32),     # one query tile, ten key tiles
+    (3, 2, 700, 333, 64),    # a ragged last key tile
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SPLIT32, ids=lambda s: "x".join(map(str, s)))
+def test_split32_shapes(shape, causal):
+    """The fp32 kernel's key chunks and their merge against the oracle, at
+    the fp32 tolerances (every tile cut into at least two chunks when it has
+    more than one key tile; causal tiles get fewer chunks than long ones)."""
+    B, H, Nq, Nk, D = shape
+    assert _ws_bytes(B, H, Nq, Nk, D, causal, fa.FA_F32) > 0, "plan does not split"
+    q, k, v = gen_qkv(B, H, Nq, Nk, D, seed=sum(shape) % 991, dtype="f32")
+    compare(q, k, v, causal, 1.0 / math.sqrt(D), what=f"split32 {shape}")
 
 
 @pytest.mark.parametrize("causal", [False, True])

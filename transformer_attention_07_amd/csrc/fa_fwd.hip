@@ -134,13 +134,16 @@ __device__ __forceinline__ float online_softmax(f32x16 (&s)[kBN / 32], float &m,
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
   mx = fmaxf(mx, __shfl_xor(mx, 32));
   const float m_new = fmaxf(m, mx);
-  const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+  // a row that has seen no visible key yet (possible when the keys are
+  // split, a chunk starting past the row) keeps p = 0 and alpha = 0
+  const float mu = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = __builtin_amdgcn_exp2f(m - mu);
   float psum = 0.f;
 #pragma unroll
   for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(s[kb][r] - m_new);
+      const float p = __builtin_amdgcn_exp2f(s[kb][r] - mu);
       s[kb][r] = p;
       psum += p;
     }
@@ -1726,11 +1729,27 @@ __global__ __launch_bounds__(kThreads) void fa_merge_varlen(
 
 // ---------------------------------------------------------------------------
 // fp32 inputs: same structure on v_mfma_f32_32x32x2_f32 (true fp32 products).
+//
+// Key split (the sequence parallelism of page "FlashAttention技术演进全景图"
+// §3.2): with nsplit > 1, workgroup id handles query tile item id / nsplit
+// (longest first, as work_item) and its key tiles [c KC, (c+1) KC),
+// c = id % nsplit.  A tile whose keys fit one chunk is stored directly; the
+// chunks of a longer tile write partials (epilogue_partial) to slot id of
+// ws, which fa_merge_split32 combines.  A fp32 MFMA takes 64 cycles for its
+// 4096 flops, so one 32-row wave needs about 3.4 us per 64-key tile: without
+// the split, shapes with few query tiles leave most SIMDs idle while each
+// wave walks every key.
+__device__ __forceinline__ int split32_chunks(int q0, int Nk, int KC, bool causal) {
+  const int kend = causal ? min(Nk, q0 + kBM) : Nk;
+  const int nkt = (kend + kBN - 1) / kBN;
+  return (nkt + KC - 1) / KC;
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void fa_fwd_f32(
     const float *__restrict__ q, const float *__restrict__ k,
     const float *__restrict__ v, float *__restrict__ o, float *__restrict__ lse,
-    int Nq, int Nk, int BH, int nqt, float c) {
+    int Nq, int Nk, int BH, int nqt, float c, int KC, int nsplit, float *__restrict__ ws) {
   constexpr int KS = D + 1;            // K row stride (floats): 32 rows on 32 banks
   constexpr int VS = D;                // V row stride (floats)
   constexpr int K_ELEMS = kBN * KS;
@@ -1749,7 +1768,10 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32(
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
-  const WorkItem wi = work_item(BH, nqt, CAUSAL);
+  const int item = blockIdx.x / nsplit, chunk = blockIdx.x % nsplit;
+  const WorkItem wi = {item % BH, (CAUSAL ? nqt - 1 - item / BH : item / BH) * kBM};
+  const int nch = nsplit > 1 ? split32_chunks(wi.q0, Nk, KC, CAUSAL) : 1;
+  if (chunk >= nch) return;  // a short causal tile needs fewer chunks
   const int qw = wi.q0 + wave * 32;
   const int my_q = qw + l32;
 
@@ -1809,18 +1831,19 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32(
   float m = -INFINITY, l = 0.f;
 
   const int kend = CAUSAL ? min(Nk, wi.q0 + kBM) : Nk;
-  const int nkt = (kend + kBN - 1) / kBN;
+  const int kt0 = nch > 1 ? chunk * KC : 0;
+  const int nkt = nch > 1 ? min((kend + kBN - 1) / kBN, kt0 + KC) : (kend + kBN - 1) / kBN;
 
-  gload(0);
+  gload(kt0);
   swrite(0);
   __syncthreads();
 
-  for (int kt = 0; kt < nkt; ++kt) {
+  for (int kt = kt0; kt < nkt; ++kt) {
     if (kt + 1 < nkt) gload(kt + 1);
     const int k0 = kt * kBN;
     const bool active = !CAUSAL || (k0 <= qw + 31);
     if (active) {
-      const float *Ks = smem + (kt & 1) * BUF;
+      const float *Ks = smem + ((kt - kt0) & 1) * BUF;
       const float *Vs = Ks + K_ELEMS;
       f32x16 s[kBN / 32];
 #pragma unroll
@@ -1850,11 +1873,90 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32(
         }
       }
     }
-    if (kt + 1 < nkt) swrite((kt + 1) & 1);
+    if (kt + 1 < nkt) swrite((kt + 1 - kt0) & 1);
     __syncthreads();
   }
 
-  epilogue<D, float>(acc, m, l, o, lse, wi.bh, Nq, my_q, g);
+  if (nch == 1) {
+    epilogue<D, float>(acc, m, l, o, lse, wi.bh, Nq, my_q, g);
+  } else {
+    const int nslots = BH * nqt * nsplit;
+    const int row = my_q - wi.q0;
+    epilogue_partial<D>(acc, m, l, l + __shfl_xor(l, 32), ws + (size_t)blockIdx.x * kBM * D,
+                        ws + (size_t)nslots * kBM * D + (size_t)blockIdx.x * kBM * 4, row, g);
+  }
+}
+
+// Combines the key chunks of the fp32 kernel's split tiles (slots item *
+// nsplit + c), merge_rows<D>() rows per workgroup, with the rescaling of
+// fa_merge_varlen; tiles left whole return at once.
+template <int D>
+__global__ __launch_bounds__(kThreads) void fa_merge_split32(const float *__restrict__ ws,
+                                                             float *__restrict__ o,
+                                                             float *__restrict__ lse, int Nq,
+                                                             int Nk, int BH, int nqt, int KC,
+                                                             int nsplit, bool causal) {
+  constexpr int C4 = D / 4;
+  constexpr int RPP = kThreads / C4;
+  constexpr int ROWS = merge_rows<D>();
+  constexpr int SPLIT = kBM / ROWS;
+  constexpr int NR = ROWS / RPP;
+  static_assert(NR >= 1 && ROWS % RPP == 0, "merge tiling");
+  const int item = blockIdx.x / SPLIT;
+  const int bh = item % BH;
+  const int q0 = (causal ? nqt - 1 - item / BH : item / BH) * kBM;
+  const int nch = split32_chunks(q0, Nk, KC, causal);
+  if (nch <= 1) return;  // stored by its only workgroup
+  const int nslots = BH * nqt * nsplit;
+  const float *ws_s = ws + (size_t)nslots * kBM * D;
+  const int c4 = threadIdx.x % C4;
+  const int r0 = (blockIdx.x % SPLIT) * ROWS + threadIdx.x / C4;
+  float M[NR], ls[NR], lrs[NR];
+  f32x4 acc[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    M[i] = -INFINITY;
+    ls[i] = lrs[i] = 0.f;
+    acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  constexpr int U = 4;  // chunks per round trip
+  for (int ch = 0; ch < nch; ch += U) {
+    f32x4 st[U][NR], x[U][NR];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (ch + u >= nch) break;
+      const size_t slot = (size_t)item * nsplit + ch + u;
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const size_t e = slot * kBM + r0 + i * RPP;
+        st[u][i] = *reinterpret_cast<const f32x4 *>(ws_s + e * 4);
+        x[u][i] = *reinterpret_cast<const f32x4 *>(ws + e * D + 4 * c4);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (ch + u >= nch) break;
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        if (st[u][i][0] == -INFINITY) continue;  // no key of this row in the chunk
+        const float Mn = fmaxf(M[i], st[u][i][0]);
+        const float a_old = exp2f(M[i] - Mn);  // 0 while M = -inf
+        const float a = exp2f(st[u][i][0] - Mn);
+        ls[i] = ls[i] * a_old + a * st[u][i][1];
+        lrs[i] = lrs[i] * a_old + a * st[u][i][2];
+        acc[i] = acc[i] * a_old + (a * st[u][i][2]) * x[u][i];
+        M[i] = Mn;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int row = q0 + r0 + i * RPP;
+    if (row < Nq) {
+      store4<float>(o + ((size_t)bh * Nq + row) * D + 4 * c4, acc[i] * (1.0f / lrs[i]));
+      if (c4 == 0) lse[(size_t)bh * Nq + row] = (M[i] + log2f(ls[i])) * 0.69314718055994531f;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1877,6 +1979,7 @@ struct Launch {
   float c;
   hipStream_t stream;
   const StreamPlan *plan;      // non-null: stream-K schedule (pipelined kernel only)
+  int KC, nsplit;             // the fp32 kernel's key split (nsplit 1: none)
   const ChunkStarts *starts;  // the schedule's chunk starts
   const CutList *cuts;        // the schedule's cut tiles
   bool masked;                // the window rule mk (grid path only)
@@ -1934,10 +2037,16 @@ hipError_t launch16(const Launch &a) {
 
 template <int D, bool CAUSAL>
 hipError_t launch32(const Launch &a) {
-  const dim3 grid((unsigned)(a.BH * a.nqt)), block(kThreads);
+  const dim3 grid((unsigned)(a.BH * a.nqt * a.nsplit)), block(kThreads);
   hipLaunchKernelGGL((fa_fwd_f32<D, CAUSAL>), grid, block, 0, a.stream,
                      (const float *)a.q, (const float *)a.k, (const float *)a.v,
-                     (float *)a.o, a.lse, a.Nq, a.Nk, a.BH, a.nqt, a.c);
+                     (float *)a.o, a.lse, a.Nq, a.Nk, a.BH, a.nqt, a.c, a.KC, a.nsplit, a.ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.nsplit < 2) return e;
+  hipLaunchKernelGGL((fa_merge_split32<D>),
+                     dim3((unsigned)(a.BH * a.nqt * (kBM / merge_rows<D>()))), block, 0,
+                     a.stream, (const float *)a.ws, (float *)a.o, a.lse, a.Nq, a.Nk, a.BH,
+                     a.nqt, a.KC, a.nsplit, CAUSAL);
   return hipGetLastError();
 }
 
@@ -2033,10 +2142,62 @@ int device_cus(int *cus) {
   return FA_OK;
 }
 
+// Key split of the fp32 kernel (fa_fwd_f32): used when the query tiles
+// number fewer than the compute units.  The chunk length KC (64-key tiles)
+// is the smallest that keeps the workgroups within one per compute unit
+// (one round) and a tile within four chunks (which the combine reads in
+// one round trip).  Measured on B8 N1000 D64 fp32, against chunks of 1, 2,
+// 3 and 6 tiles: the 4-tile chunks this gives were fastest both causal and
+// not (31.7 and 33.9 us, 2.7x and 2.5x the unsplit grid); two workgroups
+// per compute unit gained nothing over one, and extra chunks per tile cost
+// more in the combine than the shorter chunks saved.  The workspace is at
+// most four slots of 128 rows * (D + 4) floats per compute unit.
+struct Split32 {
+  int KC = 0, nsplit = 1;
+};
+
+bool plan32(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, bool causal, int cus, Split32 &ks,
+            size_t &bytes) {
+  bytes = 0;
+  ks = Split32{};
+  const int64_t nqt = (Nq + kBM - 1) / kBM;
+  const int64_t units = BH * nqt;
+  if (cus < 1 || units >= cus) return false;
+  auto keys = [&](int64_t t) {  // 64-key tiles of query tile t
+    const int64_t kend = causal ? (Nk < (t + 1) * kBM ? Nk : (t + 1) * kBM) : Nk;
+    return (kend + kBN - 1) / kBN;
+  };
+  const int64_t longest = keys(nqt - 1);  // the last tile's range is the longest
+  int64_t kc = (longest + 3) / 4;
+  for (;; ++kc) {
+    int64_t wgs = 0;
+    for (int64_t t = 0; t < nqt; ++t) wgs += (keys(t) + kc - 1) / kc;
+    if (BH * wgs <= cus || kc >= longest) break;
+  }
+  const int64_t ns = (longest + kc - 1) / kc;
+  if (ns < 2) return false;
+  ks.KC = (int)kc;
+  ks.nsplit = (int)ns;
+  bytes = (size_t)units * (size_t)ns * kBM * (size_t)(D + 4) * 4;
+  return true;
+}
+
+// The workspace a call takes, if any: the stream-K schedule of the
+// pipelined kernel (16-bit inputs) or the fp32 kernel's key split.
+bool plan_ws(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, int dtype, bool causal, int cus,
+             StreamPlan &pl, Split32 &ks, size_t &bytes) {
+  ks = Split32{};
+  if (dtype == FA_F32) return plan32(BH, Nq, Nk, D, causal, cus, ks, bytes);
+  return make_plan(BH, Nq, Nk, D, dtype, causal, cus, pl, bytes);
+}
+
 int run(const void *q, const void *k, const void *v, void *o, float *lse, int64_t Nq,
         int64_t Nk, int64_t D, float scale, int causal, int dtype, const Shape &sh,
-        const StreamPlan *plan, void *ws, void *stream, const Mask *mk = nullptr) {
+        const StreamPlan *plan, void *ws, void *stream, const Mask *mk = nullptr,
+        const Split32 *ks = nullptr) {
   Launch a;
+  a.KC = ks ? ks->KC : 0;
+  a.nsplit = ks ? ks->nsplit : 1;
   a.masked = mk != nullptr;
   a.mk = mk ? *mk : Mask{};
   a.q = q;
@@ -2333,8 +2494,9 @@ __attribute__((visibility("hidden"))) int fa_internal_hip_fail(hipError_t e) {
 // Scratch of fa_fwd_noalloc: the stream-K schedule's partial results, in a
 // file-scope device array (one copy per device, held until the process
 // ends) instead of caller memory.  FA_NOALLOC_SCRATCH_BYTES covers every
-// plan make_plan produces on a device of up to 256 compute units (the
-// largest, 2 * 256 chunks * 256 rows * (128 + 4) floats, is 66 MiB).
+// plan make_plan and plan32 produce on a device of up to 256 compute units
+// (the largest, 2 * 256 chunks * 256 rows * (128 + 4) floats, or 4 * 256
+// fp32 slots of 128 rows, is 66 MiB).
 static __device__ __align__(256) char scratch[FA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
@@ -2431,8 +2593,9 @@ int fa_fwd_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t 
   const int st = device_cus(&cus);
   if (st != FA_OK) return st;
   StreamPlan pl;
+  Split32 ks;
   size_t ws = 0;
-  make_plan(B * H, Nq, Nk, D, dtype, causal != 0, cus, pl, ws);
+  plan_ws(B * H, Nq, Nk, D, dtype, causal != 0, cus, pl, ks, ws);
   *bytes = ws;
   return FA_OK;
 }
@@ -2456,12 +2619,14 @@ int fa_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse, 
   st = device_cus(&cus);
   if (st != FA_OK) return st;
   StreamPlan pl;
+  Split32 ks;
   size_t need = 0;
-  if (!make_plan(sh.BH, Nq, Nk, D, dtype, causal != 0, cus, pl, need))
+  if (!plan_ws(sh.BH, Nq, Nk, D, dtype, causal != 0, cus, pl, ks, need))
     return run(q, k, v, o, lse, Nq, Nk, D, scale, causal, dtype, sh, nullptr, nullptr,
                stream);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
-  return run(q, k, v, o, lse, Nq, Nk, D, scale, causal, dtype, sh, &pl, workspace, stream);
+  return run(q, k, v, o, lse, Nq, Nk, D, scale, causal, dtype, sh,
+             dtype == FA_F32 ? nullptr : &pl, workspace, stream, nullptr, &ks);
 }
 
 int fa_fwd_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
@@ -2474,15 +2639,17 @@ int fa_fwd_noalloc(const void *q, const void *k, const void *v, void *o, float *
   st = device_cus(&cus);
   if (st != FA_OK) return st;
   StreamPlan pl;
+  Split32 ks;
   size_t need = 0;
-  if (!make_plan(sh.BH, Nq, Nk, D, dtype, causal != 0, cus, pl, need))
+  if (!plan_ws(sh.BH, Nq, Nk, D, dtype, causal != 0, cus, pl, ks, need))
     return run(q, k, v, o, lse, Nq, Nk, D, scale, causal, dtype, sh, nullptr, nullptr,
                stream);
   if (need > (size_t)FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_WORKSPACE;
   void *ws = nullptr;
   st = noalloc_scratch(&ws);
   if (st != FA_OK) return st;
-  return run(q, k, v, o, lse, Nq, Nk, D, scale, causal, dtype, sh, &pl, ws, stream);
+  return run(q, k, v, o, lse, Nq, Nk, D, scale, causal, dtype, sh,
+             dtype == FA_F32 ? nullptr : &pl, ws, stream, nullptr, &ks);
 }
 
 int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
