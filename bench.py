@@ -298,8 +298,11 @@ def main() -> int:
                     help="time fa_fwd_masked instead: B=1 H=8 N=32768 D=128 causal bf16 "
                          "under a local window W with G global tokens; flops counted "
                          "over the visible pairs only (4*D each)")
+    ap.add_argument("--fp8-nows", action="store_true",
+                    help="with --fp8: time fa_fwd_fp8 (no workspace, the query-stationary "
+                         "kernel) instead of fa_fwd_fp8_ws")
     ap.add_argument("--fp8", action="store_true",
-                    help="time fa_fwd_fp8 on the workload's shape with e4m3 inputs (scores on "
+                    help="time fa_fwd_fp8_ws on the workload's shape with e4m3 inputs (scores on "
                          "FP8 MFMA, P.V in bf16: roofline peak 1/(0.5/5000 + 0.5/2516.6) "
                          "TFLOP/s)")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
@@ -424,11 +427,21 @@ def main() -> int:
                                                q_mult=w.q_mult)
         q, k, v = q8.to(dev), k8.to(dev), v8.to(dev)
         argv = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.H,
-                w.N, w.N, w.D, scale, sq, sk, sv, int(w.causal), int(out_dt == torch.float32),
-                sp)
-        call = lib.fa_fwd_fp8
-        args.entry = "fa_fwd_fp8"
-        ws_bytes = 0
+                w.N, w.N, w.D, scale, sq, sk, sv, int(w.causal), int(out_dt == torch.float32))
+        if args.fp8_nows:
+            argv = argv + (sp,)
+            call = lib.fa_fwd_fp8
+            args.entry = "fa_fwd_fp8"
+            ws_bytes = 0
+        else:
+            st, ws_bytes = fa.fa_fwd_fp8_workspace_size(w.B, w.H, w.N, w.N, w.D, int(w.causal),
+                                                        int(out_dt == torch.float32))
+            if st != 0:
+                raise RuntimeError(f"fa_fwd_fp8_workspace_size: {fa.fa_status_str(st)}")
+            ws8 = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+            argv = argv + (ws8.data_ptr(), ws_bytes, sp)
+            call = lib.fa_fwd_fp8_ws
+            args.entry = "fa_fwd_fp8_ws"
         fp8 = 1.0 / (0.5 / 5000.0 + 0.5 / PEAK_TFLOPS["bf16"])
     if masked is not None or fp8 is not None:
         pass

@@ -2,7 +2,7 @@
  * fa.h -- C ABI of the MI355X (gfx950) FlashAttention-2 library: the
  * forward pass (fa_fwd, fa_fwd_ws; fa_fwd_varlen and fa_fwd_varlen_ws for
  * variable-length batches, fa_fwd_masked for local-window + global-token masks, fa_fwd_fp8
- * for FP8 inputs) and its
+ * and fa_fwd_fp8_ws for FP8 inputs) and its
  * backward pass (fa_bwd, fa_bwd_varlen, fa_bwd_masked).
  *
  * The operation (page "FlashAttention-2实现与优化：高效注意力机制详解",
@@ -336,6 +336,38 @@ int fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
                int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, float scale,
                float descale_q, float descale_k, float descale_v, int causal,
                int out_f32, void *stream);
+
+/*
+ * fa_fwd_fp8_workspace_size -- device scratch bytes that fa_fwd_fp8_ws
+ * needs (written to *bytes): V widened to bf16 (B*H*Nk*D*2 bytes, rounded
+ * up to 256), plus, when the shape takes the stream-K schedule of fa_fwd_ws
+ * (same rule as for bf16 inputs), that schedule's partials.  Returns FA_OK,
+ * FA_ERR_NULLPTR (bytes NULL), FA_ERR_SHAPE, FA_ERR_HEAD_DIM (D not 64 or
+ * 128) or FA_ERR_HIP.
+ */
+int fa_fwd_fp8_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                              int64_t D, int causal, int out_f32, size_t *bytes);
+
+/*
+ * fa_fwd_fp8_ws -- fa_fwd_fp8 on the pipelined kernel of fa_fwd_ws, with
+ * caller-owned device scratch (FP8 support, page "FlashAttention技术演进全景图"
+ * §5.3; the work split of §3.2 there).  The score products K.Q^T run on the
+ * FP8 MFMA (e4m3 operands, fp32 sums: exact products) with q and k read as
+ * stored; V's e4m3 values are first widened exactly to bf16 into the
+ * workspace by a separate kernel, and P.V runs on the bf16 MFMA with P
+ * rounded to bf16 as on the 16-bit path; descale_v multiplies O in fp32 at
+ * the normalisation.  Arguments, results and errors as fa_fwd_fp8, plus
+ *   workspace        device pointer, 16-byte aligned, of at least the bytes
+ *                    fa_fwd_fp8_workspace_size reports for the same shape
+ *   workspace_bytes  its size in bytes
+ * and FA_ERR_WORKSPACE (workspace NULL or too small), FA_ERR_ALIGN and
+ * FA_ERR_OVERLAP for the workspace.  Calls that share a workspace must be
+ * ordered on one stream.
+ */
+int fa_fwd_fp8_ws(const void *q, const void *k, const void *v, void *o, float *lse,
+                  int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, float scale,
+                  float descale_q, float descale_k, float descale_v, int causal,
+                  int out_f32, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * fa_bwd_workspace_size -- device scratch bytes that fa_bwd needs (written

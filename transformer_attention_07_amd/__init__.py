@@ -44,7 +44,8 @@ Tensor convenience:
     fwd_masked(q, k, v, window, nglobal=0, causal=False, scale=None,
                out_dtype=None) -> (o, lse) through fa_fwd_masked
     fwd_fp8(q8, k8, v8, descale_q, descale_k, descale_v, causal=False, scale=None,
-            out_dtype=None) -> (o, lse) through fa_fwd_fp8
+            out_dtype=None, ws=True) -> (o, lse); ws=True runs fa_fwd_fp8_ws (the
+        pipelined kernel, workspace from torch's allocator), ws=False fa_fwd_fp8
     bwd(q, k, v, o, lse, do, causal=False, scale=None, grad_dtype=None,
         window=None, nglobal=0) -> (dq, dk, dv) through fa_bwd (fa_bwd_masked
         when a window is given)
@@ -63,7 +64,8 @@ __all__ = [
     "FA_OK", "FA_ERR_NULLPTR", "FA_ERR_SHAPE", "FA_ERR_HEAD_DIM", "FA_ERR_DTYPE",
     "FA_ERR_SCALE", "FA_ERR_ALIGN", "FA_ERR_HIP", "FA_ERR_OVERLAP", "FA_ERR_WORKSPACE",
     "LIBRARY", "EXPORTS", "library", "fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws",
-    "fa_fwd_noalloc", "fa_fwd_varlen", "fa_fwd_varlen_workspace_size", "fa_fwd_varlen_ws", "fa_fwd_masked", "fa_fwd_fp8", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_varlen", "fa_bwd_masked", "fa_status_str",
+    "fa_fwd_noalloc", "fa_fwd_varlen", "fa_fwd_varlen_workspace_size", "fa_fwd_varlen_ws", "fa_fwd_masked", "fa_fwd_fp8", "fa_fwd_fp8_workspace_size", "fa_fwd_fp8_ws",
+    "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_varlen", "fa_bwd_masked", "fa_status_str",
     "fa_last_hip_error", "fa_version", "fwd", "fwd_varlen", "fwd_masked", "fwd_fp8", "bwd", "bwd_varlen", "FaError",
 ]
 
@@ -78,7 +80,9 @@ FA_F32, FA_BF16, FA_BF16_OF32, FA_F16, FA_F16_OF32 = 0, 1, 2, 3, 4
 
 # Every symbol include/fa.h declares.
 EXPORTS = ("fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws", "fa_fwd_noalloc", "fa_fwd_varlen",
-           "fa_fwd_varlen_workspace_size", "fa_fwd_varlen_ws", "fa_fwd_masked", "fa_fwd_fp8", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_varlen", "fa_bwd_masked",
+           "fa_fwd_varlen_workspace_size", "fa_fwd_varlen_ws", "fa_fwd_masked", "fa_fwd_fp8",
+           "fa_fwd_fp8_workspace_size", "fa_fwd_fp8_ws", "fa_bwd_workspace_size", "fa_bwd",
+           "fa_bwd_varlen", "fa_bwd_masked",
            "fa_status_str", "fa_last_hip_error", "fa_version")
 
 _lib = None
@@ -130,6 +134,13 @@ def library() -> ctypes.CDLL:
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
                                ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_int,
                                ctypes.c_int, vp]
+    lib.fa_fwd_fp8_workspace_size.restype = ctypes.c_int
+    lib.fa_fwd_fp8_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int,
+                                              ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+    lib.fa_fwd_fp8_ws.restype = ctypes.c_int
+    lib.fa_fwd_fp8_ws.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
+                                  ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_int,
+                                  ctypes.c_int, vp, ctypes.c_size_t, vp]
     lib.fa_bwd_workspace_size.restype = ctypes.c_int
     lib.fa_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int,
                                           ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
@@ -221,6 +232,22 @@ def fa_fwd_fp8(q, k, v, o, lse, B, H, Nq, Nk, D, scale, dq, dk, dv, causal, out_
     """Raw C call; pointers are integers (device addresses) or None."""
     return int(library().fa_fwd_fp8(q, k, v, o, lse, B, H, Nq, Nk, D, float(scale), float(dq),
                                     float(dk), float(dv), int(causal), int(out_f32), stream))
+
+
+def fa_fwd_fp8_workspace_size(B, H, Nq, Nk, D, causal, out_f32) -> Tuple[int, int]:
+    """Raw C call; returns (status, workspace bytes)."""
+    n = ctypes.c_size_t(0)
+    st = int(library().fa_fwd_fp8_workspace_size(B, H, Nq, Nk, D, int(causal), int(out_f32),
+                                                 ctypes.byref(n)))
+    return st, int(n.value)
+
+
+def fa_fwd_fp8_ws(q, k, v, o, lse, B, H, Nq, Nk, D, scale, dq, dk, dv, causal, out_f32, ws,
+                  ws_bytes, stream) -> int:
+    """Raw C call; pointers are integers (device addresses) or None."""
+    return int(library().fa_fwd_fp8_ws(q, k, v, o, lse, B, H, Nq, Nk, D, float(scale),
+                                       float(dq), float(dk), float(dv), int(causal),
+                                       int(out_f32), ws, ws_bytes, stream))
 
 
 def fa_bwd_workspace_size(B, H, Nq, Nk, D, causal, dtype) -> Tuple[int, int]:
@@ -566,11 +593,12 @@ def fwd_masked(q, k, v, window: int, nglobal: int = 0, causal: bool = False,
 
 
 def fwd_fp8(q, k, v, descale_q: float, descale_k: float, descale_v: float,
-            causal: bool = False, scale: Optional[float] = None, out_dtype=None, stream=None
-            ) -> Tuple["torch.Tensor", "torch.Tensor"]:
-    """FP8 attention forward (fa_fwd_fp8): q, k, v torch.float8_e4m3fn device
-    tensors [B,N,D] or [B,H,N,D] (real inputs = values x descale factors).
-    Returns (o in bf16 or fp32, lse fp32)."""
+            causal: bool = False, scale: Optional[float] = None, out_dtype=None, stream=None,
+            ws: bool = True) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """FP8 attention forward: q, k, v torch.float8_e4m3fn device tensors
+    [B,N,D] or [B,H,N,D] (real inputs = values x descale factors).  ws=True
+    runs fa_fwd_fp8_ws (the pipelined kernel; workspace allocated here),
+    ws=False fa_fwd_fp8.  Returns (o in bf16 or fp32, lse fp32)."""
     import torch
 
     if q.dim() not in (3, 4) or k.dim() != q.dim() or v.dim() != q.dim():
@@ -593,9 +621,18 @@ def fwd_fp8(q, k, v, descale_q: float, descale_k: float, descale_v: float,
     lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H,
-                    Nq, Nk, D, scale, descale_q, descale_k, descale_v, causal,
-                    out_dtype == torch.float32, stream)
+    f32 = out_dtype == torch.float32
+    if ws:
+        st, nb = fa_fwd_fp8_workspace_size(B, H, Nq, Nk, D, causal, f32)
+        if st == FA_OK:
+            buf = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device)
+            st = fa_fwd_fp8_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                               lse.data_ptr(), B, H, Nq, Nk, D, scale, descale_q, descale_k,
+                               descale_v, causal, f32, buf.data_ptr(), nb, stream)
+    else:
+        st = fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                        B, H, Nq, Nk, D, scale, descale_q, descale_k, descale_v, causal, f32,
+                        stream)
     if st != FA_OK:
         msg = fa_status_str(st)
         if st == FA_ERR_HIP:

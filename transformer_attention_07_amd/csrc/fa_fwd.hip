@@ -219,12 +219,14 @@ __device__ __forceinline__ void store_row(const f32x16 (&acc)[NDB], float inv, O
 template <int D, typename OT>
 __device__ __forceinline__ void epilogue(const f32x16 (&acc)[(D < 32 ? 32 : D) / 32],
                                          float m, float l, OT *o, float *lse, int bh,
-                                         int Nq, int my_q, int g, float lo = -1.f) {
+                                         int Nq, int my_q, int g, float lo = -1.f,
+                                         float osc = 1.f) {
   const float lt = l + __shfl_xor(l, 32);
   const float lot = lo < 0.f ? lt : lo;
   if (my_q >= Nq) return;
-  // a row that saw no key (possible under the window mask) stores O = 0
-  const float inv = lot > 0.f ? 1.0f / lot : 0.f;
+  // a row that saw no key (possible under the window mask) stores O = 0;
+  // osc: a factor of O (1 except on the FP8 path)
+  const float inv = (lot > 0.f ? 1.0f / lot : 0.f) * osc;
   OT *orow = o + ((size_t)bh * Nq + my_q) * D;
   store_row<OT, (D < 32 ? 32 : D) / 32>(acc, inv, orow, g, D);
   if (g == 0) lse[(size_t)bh * Nq + my_q] = (m + log2f(lt)) * 0.69314718055994531f;
@@ -342,13 +344,15 @@ __device__ __forceinline__ u32x4 load16_async(u32x4 rs, uint32_t voff) {
   return r;
 }
 
-template <typename T, int D>
+template <typename T, int D, typename KT = T>
 struct PipeLayout {
-  static constexpr int C = D / 8;                     // 16-byte chunks per row
-  // K and V row strides (16-byte slots): padded against bank conflicts; at
+  static constexpr int C = D / 8;                     // 16-byte chunks per V row
+  static constexpr int KRB = D * (int)sizeof(KT);     // bytes of a K row in HBM
+  // K and V row strides (16-byte slots): padded against bank conflicts (a K
+  // row is its 16-byte chunks plus one, for 16-bit and 8-bit K alike); at
   // D = 16 the V row holds 4 slots so that the P.V fragments' upper 16
   // head-dim columns read the zeroed padding
-  static constexpr int SK = D == 128 ? 17 : (D == 64 ? 9 : (D == 32 ? 5 : 3));
+  static constexpr int SK = KRB / 16 + 1;
   static constexpr int SV = D == 128 ? 20 : (D == 64 ? 12 : (D == 32 ? 6 : 4));
   static constexpr int K_BYTES = kBN * SK * 16;
   static constexpr int V_BYTES = kBN * SV * 16;
@@ -356,18 +360,18 @@ struct PipeLayout {
   static constexpr int V_INS = kBN * SV / kWave;
   static constexpr int V_OFF = kStages * K_BYTES;     // V ring after the K ring
   static constexpr int LDS_BYTES = kStages * (K_BYTES + V_BYTES);
-  static constexpr uint32_t TILE_GLOBAL = kBN * D * sizeof(T);  // bytes per tile in HBM
+  static constexpr uint32_t K_TILE_GLOBAL = kBN * KRB;            // bytes per tile in HBM
+  static constexpr uint32_t V_TILE_GLOBAL = kBN * D * sizeof(T);
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
 // Per-lane byte offset (within the head's K or V slice, tile 0) of the chunk
 // that DMA instruction `ins` places in LDS slot ins*64 + lane.
-template <typename T, int D>
-__device__ __forceinline__ uint32_t dma_src(int ins, int lane, int stride) {
+__device__ __forceinline__ uint32_t dma_src(int ins, int lane, int stride, int row_bytes) {
   const int p = ins * kWave + lane;
   const int row = p / stride;
   const int col = p % stride;
-  return col < D / 8 ? (uint32_t)(row * D + col * 8) * sizeof(T) : kOutOfRange;
+  return col < row_bytes / 16 ? (uint32_t)(row * row_bytes + col * 16) : kOutOfRange;
 }
 
 // gfx9 buffer resource (raw, stride 0): base, num_records = bytes, word 3
@@ -396,11 +400,39 @@ struct KeyList {
   int n1, b0;
 };
 
-template <typename T, typename OT, int D, bool CAUSAL, bool MASKED = false>
+// The score product S^T = K Q^T on Q/K elements of type KT: the 16-bit
+// MFMA (16 head-dim entries per instruction), or for bytes holding OCP e4m3
+// values the scaled FP8 MFMA v_mfma_scale_f32_32x32x64_f8f6f4 with unit
+// block scales (E8M0 127 = 2^0; 64 entries per instruction).  KSTEP entries
+// per instruction, FB bytes of them per lane: lane l gives row l % 32 and
+// the entries [KSTEP/2 (l / 32), +KSTEP/2) of the step, for K (A) and Q
+// (B) alike, so the contraction pairs the same head-dim entries whatever
+// order the instruction uses within a lane's slots.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+template <typename KT> struct QKOp {
+  typedef typename Mma<KT>::frag frag;
+  static constexpr int KSTEP = 16;
+  static constexpr int FB = 16;
+  static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return Mma<KT>::mma(a, b, c);
+  }
+};
+template <> struct QKOp<uint8_t> {
+  typedef i32x8 frag;
+  static constexpr int KSTEP = 64;
+  static constexpr int FB = 32;
+  static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  }
+};
+
+template <typename T, typename OT, int D, bool CAUSAL, bool MASKED = false, typename KT = T>
 struct Pipe {
-  typedef typename Mma<T>::frag frag;
-  typedef PipeLayout<T, D> L;
-  static constexpr int QF = D / 16;    // K.Q^T MFMAs per 32-key block
+  typedef typename Mma<T>::frag frag;            // P.V operands
+  typedef QKOp<KT> QK;
+  typedef typename QK::frag kfrag_t;             // K.Q^T operands
+  typedef PipeLayout<T, D, KT> L;
+  static constexpr int QF = D / QK::KSTEP;       // K.Q^T MFMAs per 32-key block
   // O^T blocks of 32 head-dim rows (at D = 16 the upper 16 rows read zero
   // padding of V and are never stored)
   static constexpr int NDB = (D + 31) / 32;
@@ -426,7 +458,8 @@ struct Pipe {
     return (k0 + 32 > Nk) || (CAUSAL && k0 + 31 > qw);
   }
   uint32_t kbase, vbase;  // per-lane LDS byte addresses of fragment 0
-  frag qf[QF];
+  float osc;              // factor of O (the FP8 path's V descale; else 1)
+  kfrag_t qf[QF];
   f32x16 acc[NDB];
   f32x16 S0, S1;      // S^T blocks (alternate between the two blocks of a tile)
   frag P0[2], P1[2];  // P blocks rounded to T (alternate likewise)
@@ -434,7 +467,8 @@ struct Pipe {
   // of the current one (blocks chained with PRE)
   static constexpr int PFK = QF < 3 ? QF : 3;   // K fragments read ahead
   static constexpr int PFV = NPV < 3 ? NPV : 3;  // V fragments read ahead
-  frag kpre[PFK], vpre[PFV];
+  kfrag_t kpre[PFK];
+  frag vpre[PFV];
   float m_use;  // exponent reference (base 2), the same in both half-waves
   float nm;     // -m_use, or 0 while m_use = -inf
   float l;   // half-wave sum of p (fp32): gives L
@@ -454,8 +488,8 @@ struct Pipe {
   }
   bool fresh;   // no block of the item seen yet (wave-uniform)
 
-  __device__ __forceinline__ frag kfrag(const lds_char *kp, int f) const {
-    return *(const __attribute__((address_space(3))) frag *)(kp + f * 32);
+  __device__ __forceinline__ kfrag_t kfrag(const lds_char *kp, int f) const {
+    return *(const __attribute__((address_space(3))) kfrag_t *)(kp + f * 2 * QK::FB);
   }
   __device__ __forceinline__ frag vfrag(const lds_char *vp, int m) const {
     const int ks = m / NDB, db = m % NDB;
@@ -478,7 +512,7 @@ struct Pipe {
   __device__ __forceinline__ void qk(const lds_char *kp, f32x16 &sc) const {
     sc = f32x16{};
 #pragma unroll
-    for (int f = 0; f < QF; ++f) sc = Mma<T>::mma(kfrag(kp, f), qf[f], sc);
+    for (int f = 0; f < QF; ++f) sc = QK::mma(kfrag(kp, f), qf[f], sc);
   }
 
   // acc += V^T P^T of a 32-key block, and its rounded sums into lracc (no
@@ -616,7 +650,8 @@ struct Pipe {
                                              const lds_char *kpn = nullptr,
                                              const lds_char *vpn = nullptr) {
     constexpr int NCHUNK = LRM ? 11 : 12;
-    frag kf[QF], vf[NPV];
+    kfrag_t kf[QF];
+    frag vf[NPV];
     float ea[2], pb[2];        // pair in flight: exponents, then p
     uint32_t wq = 0;           // packed pair waiting for its rounded sum
     float psa = 0.f, psb = 0.f, rsa = 0.f, rsb = 0.f;  // two partial sums each
@@ -675,7 +710,7 @@ struct Pipe {
     for (int i = 0; i < NSL; ++i) {
       // K.Q^T, then a slice of the softmax
       if (i < QF) {
-        sout = Mma<T>::mma(kf[i], qf[i], sout);
+        sout = QK::mma(kf[i], qf[i], sout);
         if (i + PFK < QF)
           kf[i + PFK] = kfrag(kp, i + PFK);
         else if (PRE)
@@ -768,10 +803,12 @@ struct Pipe {
 template <int D>
 __device__ __forceinline__ void epilogue_partial(const f32x16 (&acc)[(D + 31) / 32], float m,
                                                  float l, float lr, float *ws_o,
-                                                 float *ws_s, int row, int g) {
+                                                 float *ws_s, int row, int g,
+                                                 float osc = 1.f) {
   const float lt = l + __shfl_xor(l, 32);
   const float lrt = lr;  // already the whole row's sum
-  const float inv = lrt > 0.f ? 1.0f / lrt : 0.f;
+  // O_p carries the factor osc: the combine is linear in the O_p
+  const float inv = (lrt > 0.f ? 1.0f / lrt : 0.f) * osc;
   store_row<float, (D + 31) / 32>(acc, inv, ws_o + (size_t)row * D, g, D);
   if (g == 0) {
     const f32x4 st = {lrt > 0.f ? m : -INFINITY, lt, lrt, 0.f};
@@ -815,9 +852,9 @@ static_assert(QRows<true>::value == kPairRows && QRows<false>::value == kGridRow
 // skipping it in the pair-split loop +1.7%; in the 256-row loop, where the
 // waits then need each wave's own count (a scalar branch per step), +-0 at
 // D = 128 and 1-5% slower at D = 16-64.
-template <typename T, int D>
+template <typename T, int D, typename KT = T>
 struct Dma8 {
-  typedef PipeLayout<T, D> L;
+  typedef PipeLayout<T, D, KT> L;
   static constexpr int KJ = (L::K_INS + kWaves8 - 1) / kWaves8;
   static constexpr int VJ = (L::V_INS + kWaves8 - 1) / kWaves8;
   static constexpr int PER_WAVE = KJ + VJ;
@@ -838,7 +875,7 @@ struct Dma8 {
       if (i < (isk ? L::K_INS : L::V_INS)) {
         lb = ring_addr + (isk ? 0u : (uint32_t)L::V_OFF) + (uint32_t)i * kWave * 16;
         ls = isk ? L::K_BYTES : L::V_BYTES;
-        src[j] = dma_src<T, D>(i, lane, isk ? L::SK : L::SV);
+        src[j] = dma_src(i, lane, isk ? L::SK : L::SV, isk ? L::KRB : D * (int)sizeof(T));
       } else {
         lb = ring_addr + SCRATCH;
         ls = 0;
@@ -858,7 +895,8 @@ struct Dma8 {
     for (int j = 0; j < PER_WAVE; ++j) {
       const bool isk = j < KJ;
       const uint32_t lds = lbase[j] + (uint32_t)(isk ? kst : vst) * lstride[j];
-      const uint32_t off = src[j] + (uint32_t)(isk ? ktile : vtile) * L::TILE_GLOBAL;
+      const uint32_t off =
+          src[j] + (isk ? (uint32_t)ktile * L::K_TILE_GLOBAL : (uint32_t)vtile * L::V_TILE_GLOBAL);
       dma16(isk ? k_rs : v_rs, lds, off);
     }
   }
@@ -873,14 +911,14 @@ struct Dma8 {
     for (int j = 0; j < KJ; ++j)
       if (lstride[j] != 0)
         dma16(k_rs, lbase[j] + (uint32_t)kst * lstride[j],
-              src[j] + (uint32_t)ktile * L::TILE_GLOBAL);
+              src[j] + (uint32_t)ktile * L::K_TILE_GLOBAL);
   }
   __device__ __forceinline__ void issue_v(u32x4 v_rs, int vtile, int vst) const {
 #pragma unroll
     for (int j = KJ; j < PER_WAVE; ++j)
       if (lstride[j] != 0)
         dma16(v_rs, lbase[j] + (uint32_t)vst * lstride[j],
-              src[j] + (uint32_t)vtile * L::TILE_GLOBAL);
+              src[j] + (uint32_t)vtile * L::V_TILE_GLOBAL);
   }
   // This wave's instructions of one K tile (issue_k).
   __device__ __forceinline__ int kloads() const {
@@ -893,18 +931,22 @@ struct Dma8 {
 
 // MASKED (256-row layout only): the item's key tiles are the list kl (its
 // kt0, kt1 index the list), scores follow the window rule mk.
-template <typename T, typename OT, int D, bool CAUSAL, bool PAIR, bool MASKED = false>
-__device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__restrict__ k,
+// KT: the Q and K element type (T, or bytes holding e4m3 values for the
+// FP8 score product); V is T.  osc multiplies O (the FP8 path's V descale).
+template <typename T, typename OT, int D, bool CAUSAL, bool PAIR, bool MASKED = false,
+          typename KT = T>
+__device__ __forceinline__ void pipe8_run(const KT *__restrict__ q, const KT *__restrict__ k,
                                           const T *__restrict__ v, OT *__restrict__ o,
                                           float *__restrict__ lse, float *__restrict__ ws,
                                           int Nq, int Nk, float c, int negate,
                                           const PipeItem it, int nslots, const Mask mk = Mask{},
-                                          const KeyList kl = KeyList{}) {
+                                          const KeyList kl = KeyList{}, float osc = 1.f) {
   static_assert(!(MASKED && PAIR), "the window mask runs in the 256-row layout");
-  typedef Pipe<T, OT, D, CAUSAL, MASKED> P;
+  typedef Pipe<T, OT, D, CAUSAL, MASKED, KT> P;
   typedef typename P::L L;
   typedef typename P::frag frag;
-  typedef Dma8<T, D> DM;
+  typedef Dma8<T, D, KT> DM;
+  constexpr int QPC = P::QK::FB / 16;  // 16-byte pieces of a K.Q^T operand per lane
   constexpr int UNIT = DM::PER_WAVE;
   constexpr int QT = QRows<PAIR>::value;
   __shared__ __attribute__((aligned(16))) char ring_[DM::LDS_BYTES];
@@ -926,7 +968,8 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
   s.g = s.lane >> 5;
   s.Nk = Nk;
   s.c = c;
-  s.kbase = (uint32_t)(s.l32 * L::SK + s.g) * 16;
+  s.kbase = (uint32_t)(s.l32 * L::SK * 16 + s.g * P::QK::FB);
+  s.osc = osc;
   {
     const int G = s.lane >> 4, s16 = s.lane & 15;
     const int row = 4 * (G >> 1) + (s16 >> 2);
@@ -939,8 +982,8 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
   s.kl = kl;
   const size_t qoff = (size_t)it.bh * Nq * D;
   const size_t koff = (size_t)it.bh * Nk * D;
-  const u32x4 q_rs = raw_rsrc(q + qoff, (uint32_t)Nq * D * sizeof(T));
-  const u32x4 k_rs = raw_rsrc(k + koff, (uint32_t)Nk * D * sizeof(T));
+  const u32x4 q_rs = raw_rsrc(q + qoff, (uint32_t)Nq * D * sizeof(KT));
+  const u32x4 k_rs = raw_rsrc(k + koff, (uint32_t)Nk * D * sizeof(KT));
   const u32x4 v_rs = raw_rsrc(v + koff, (uint32_t)Nk * D * sizeof(T));
   DM dm;
   dm.init(ring_addr, wave, s.lane);
@@ -972,10 +1015,13 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
 
   // Q first: its loads are the oldest in flight, so the prologue wait for
   // the first K/V unit covers them too.
-  u32x4 qraw[P::QF];
+  u32x4 qraw[P::QF * QPC];
 #pragma unroll
   for (int f = 0; f < P::QF; ++f)
-    qraw[f] = load16_async(q_rs, ((uint32_t)s.my_q * D + 16 * f + 8 * s.g) * sizeof(T));
+#pragma unroll
+    for (int j = 0; j < QPC; ++j)
+      qraw[f * QPC + j] =
+          load16_async(q_rs, (uint32_t)s.my_q * L::KRB + (2 * f + s.g) * P::QK::FB + 16 * j);
 
   // The first P.V of a wave belongs to the block before the item (P = 0)
   // and reads V stage 3 (rows 32..63, and with PAIR also rows 0..31), which
@@ -1015,11 +1061,23 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
     static_assert(DM::KJ <= 3, "ring_barrier_k2 range");
     ring_barrier_k2(dm.kloads());
   }
+  // a negative scale flips the sign bit of every Q element
+  constexpr uint32_t SIGN = sizeof(KT) == 1 ? 0x80808080u : 0x80008000u;
+#pragma unroll
+  for (int f = 0; f < P::QF * QPC; ++f) {
+    asm volatile("" : "+v"(qraw[f]));  // Q is read only after the wait above
+    if (negate) qraw[f] ^= u32x4{SIGN, SIGN, SIGN, SIGN};
+  }
 #pragma unroll
   for (int f = 0; f < P::QF; ++f) {
-    asm volatile("" : "+v"(qraw[f]));  // Q is read only after the wait above
-    if (negate) qraw[f] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
-    s.qf[f] = __builtin_bit_cast(frag, qraw[f]);
+    if constexpr (QPC == 1) {
+      s.qf[f] = __builtin_bit_cast(typename P::kfrag_t, qraw[f]);
+    } else {
+      const u32x4 a = qraw[2 * f], b = qraw[2 * f + 1];
+      const i32x8 x = {(int)a[0], (int)a[1], (int)a[2], (int)a[3],
+                       (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+      s.qf[f] = __builtin_bit_cast(typename P::kfrag_t, x);
+    }
   }
 
 #pragma unroll
@@ -1050,7 +1108,7 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
     // so a block never starts on a fresh LDS round trip.  Those reads are
     // the wave's youngest LDS accesses at the next barrier, which lets them
     // stay in flight: they touch neither stage the next unit overwrites.
-    constexpr int RA = P::PFK + 2 * P::PFV;  // LDS reads of one read-ahead
+    constexpr int RA = P::PFK * QPC + 2 * P::PFV;  // LDS reads of one read-ahead
     s.read_ahead(ring, kStages - 1, 1, 0, 1);
     for (int r = 0; r < ntiles; ++r) {
       ring_barrier_sel<UNIT, RA>(r + 2 <= ntiles);
@@ -1168,11 +1226,11 @@ __device__ __forceinline__ void pipe8_run(const T *__restrict__ q, const T *__re
   }
 
   if (it.slot < 0) {
-    epilogue<D, OT>(s.acc, M, l, o, lse, it.bh, Nq, s.my_q, s.g, lr);
+    epilogue<D, OT>(s.acc, M, l, o, lse, it.bh, Nq, s.my_q, s.g, lr, osc);
   } else {
     float *ws_o = ws + (size_t)it.slot * QT * D;
     float *ws_s = ws + (size_t)nslots * QT * D + (size_t)it.slot * QT * 4;
-    epilogue_partial<D>(s.acc, M, l, lr, ws_o, ws_s, s.my_q - it.q0, s.g);
+    epilogue_partial<D>(s.acc, M, l, lr, ws_o, ws_s, s.my_q - it.q0, s.g, osc);
   }
 }
 
@@ -1210,11 +1268,12 @@ __device__ __forceinline__ KeyList key_list(const Mask &mk, int q0, int QT, int 
 // One workgroup per (batch*head, query tile), longest causal tiles first.
 // MASKED: the tile's key tiles are its key_list under the window rule mk; a
 // tile that sees no key writes O = 0 and L = -inf.
-template <typename T, typename OT, int D, bool CAUSAL, bool PAIR, bool MASKED = false>
+template <typename T, typename OT, int D, bool CAUSAL, bool PAIR, bool MASKED = false,
+          typename KT = T>
 __global__ __launch_bounds__(kThreads8) void fa_fwd_pipe8(
-    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    const KT *__restrict__ q, const KT *__restrict__ k, const T *__restrict__ v,
     OT *__restrict__ o, float *__restrict__ lse, int Nq, int Nk, int BH, int nqt,
-    float c, int negate, Mask mk) {
+    float c, int negate, Mask mk, float osc) {
   constexpr int QT = QRows<PAIR>::value;
   const WorkItem wi = work_item(BH, nqt, CAUSAL, QT);
   if constexpr (MASKED) {
@@ -1233,7 +1292,8 @@ __global__ __launch_bounds__(kThreads8) void fa_fwd_pipe8(
   } else {
     const int kend = CAUSAL ? min(Nk, wi.q0 + QT) : Nk;
     const PipeItem it = {wi.bh, wi.q0, 0, (kend + kBN - 1) / kBN, -1};
-    pipe8_run<T, OT, D, CAUSAL, PAIR>(q, k, v, o, lse, nullptr, Nq, Nk, c, negate, it, 0);
+    pipe8_run<T, OT, D, CAUSAL, PAIR, false, KT>(q, k, v, o, lse, nullptr, Nq, Nk, c, negate,
+                                                 it, 0, Mask{}, KeyList{}, osc);
   }
 }
 
@@ -1558,11 +1618,11 @@ __global__ __launch_bounds__(kThreads) void fa_merge_stream_varlen(
 }
 
 
-template <typename T, typename OT, int D, bool CAUSAL, bool PAIR>
+template <typename T, typename OT, int D, bool CAUSAL, bool PAIR, typename KT = T>
 __global__ __launch_bounds__(kThreads8) void fa_fwd_stream(
-    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    const KT *__restrict__ q, const KT *__restrict__ k, const T *__restrict__ v,
     OT *__restrict__ o, float *__restrict__ lse, float *__restrict__ ws, int Nq, int Nk,
-    float c, int negate, StreamPlan sp, ChunkStarts cs) {
+    float c, int negate, StreamPlan sp, ChunkStarts cs, float osc) {
   ChunkWalk cw;
   const int ch = chunk_of(blockIdx.x, sp.G);
   cw.init_at(sp, ch, cs.w[2 * ch], cs.w[2 * ch + 1]);
@@ -1570,7 +1630,8 @@ __global__ __launch_bounds__(kThreads8) void fa_fwd_stream(
   int t;
   while (cw.next(sp, CAUSAL, it, t)) {
     it.q0 = t * QRows<PAIR>::value;
-    pipe8_run<T, OT, D, CAUSAL, PAIR>(q, k, v, o, lse, ws, Nq, Nk, c, negate, it, 2 * sp.G);
+    pipe8_run<T, OT, D, CAUSAL, PAIR, false, KT>(q, k, v, o, lse, ws, Nq, Nk, c, negate, it,
+                                                 2 * sp.G, Mask{}, KeyList{}, osc);
   }
 }
 
@@ -1960,6 +2021,28 @@ __global__ __launch_bounds__(kThreads) void fa_merge_split32(const float *__rest
 }
 
 // ---------------------------------------------------------------------------
+// FP8 inputs on the pipelined kernel (fa_fwd_fp8_ws): Q and K stay e4m3 and
+// meet on the FP8 MFMA; P.V runs on the bf16 MFMA, so V's e4m3 values are
+// first widened to bf16 (exactly: e4m3's 3 fraction bits and exponent range
+// fit in bf16) into the workspace by this pass, 16 values per thread.
+__global__ __launch_bounds__(256) void fa_fp8_widen(const u32x4 *__restrict__ src,
+                                                    u32x4 *__restrict__ dst, size_t n16) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n16) return;
+  const u32x4 w = src[i];
+  uint32_t x[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], false);  // bytes 0, 1
+    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w[j], true);   // bytes 2, 3
+    x[2 * j] = Mma<__bf16>::pack2(a[0], a[1]);
+    x[2 * j + 1] = Mma<__bf16>::pack2(b[0], b[1]);
+  }
+  dst[2 * i] = u32x4{x[0], x[1], x[2], x[3]};
+  dst[2 * i + 1] = u32x4{x[4], x[5], x[6], x[7]};
+}
+
+// ---------------------------------------------------------------------------
 // Host side.
 
 thread_local char g_hip_error[256] = "";
@@ -1980,13 +2063,14 @@ struct Launch {
   hipStream_t stream;
   const StreamPlan *plan;      // non-null: stream-K schedule (pipelined kernel only)
   int KC, nsplit;             // the fp32 kernel's key split (nsplit 1: none)
+  float osc;                  // factor of O (FP8: the V descale; else 1)
   const ChunkStarts *starts;  // the schedule's chunk starts
   const CutList *cuts;        // the schedule's cut tiles
   bool masked;                // the window rule mk (grid path only)
   Mask mk;
 };
 
-template <typename T, typename OT, int D, bool CAUSAL>
+template <typename T, typename OT, int D, bool CAUSAL, typename KT = T>
 hipError_t launch16(const Launch &a) {
   // c > 0 here: a negative scale flips the sign of Q inside the kernel,
   // and scale 0 runs as the smallest normal scale (scores of at most
@@ -2001,10 +2085,10 @@ hipError_t launch16(const Launch &a) {
       // the workspace slots and tile indices of the plan are in units of the
       // kernel's tile height: never launch with another
       if (sp.tu * kKeys != QRows<PAIR>::value) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((fa_fwd_stream<T, OT, D, CAUSAL, PAIR>), dim3((unsigned)sp.G),
-                         dim3(kThreads8), 0, a.stream, (const T *)a.q, (const T *)a.k,
+      hipLaunchKernelGGL((fa_fwd_stream<T, OT, D, CAUSAL, PAIR, KT>), dim3((unsigned)sp.G),
+                         dim3(kThreads8), 0, a.stream, (const KT *)a.q, (const KT *)a.k,
                          (const T *)a.v, (OT *)a.o, a.lse, a.ws, a.Nq, a.Nk, c, neg, sp,
-                         *a.starts);
+                         *a.starts, a.osc);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       if (a.cuts && a.cuts->n > 0) {
@@ -2022,15 +2106,18 @@ hipError_t launch16(const Launch &a) {
       e = go(std::false_type{});
     if (e != hipSuccess) return e;
   } else if (a.masked) {
-    hipLaunchKernelGGL((fa_fwd_pipe8<T, OT, D, CAUSAL, false, true>),
-                       dim3((unsigned)(a.BH * a.nqtg)), dim3(kThreads8), 0, a.stream,
-                       (const T *)a.q, (const T *)a.k, (const T *)a.v, (OT *)a.o, a.lse,
-                       a.Nq, a.Nk, a.BH, a.nqtg, c, neg, a.mk);
+    if constexpr (std::is_same<KT, T>::value)
+      hipLaunchKernelGGL((fa_fwd_pipe8<T, OT, D, CAUSAL, false, true>),
+                         dim3((unsigned)(a.BH * a.nqtg)), dim3(kThreads8), 0, a.stream,
+                         (const T *)a.q, (const T *)a.k, (const T *)a.v, (OT *)a.o, a.lse,
+                         a.Nq, a.Nk, a.BH, a.nqtg, c, neg, a.mk, 1.f);
+    else
+      return hipErrorInvalidValue;  // the window mask runs on 16-bit inputs only
   } else {
-    hipLaunchKernelGGL((fa_fwd_pipe8<T, OT, D, CAUSAL, false>),
+    hipLaunchKernelGGL((fa_fwd_pipe8<T, OT, D, CAUSAL, false, false, KT>),
                        dim3((unsigned)(a.BH * a.nqtg)), dim3(kThreads8), 0, a.stream,
-                       (const T *)a.q, (const T *)a.k, (const T *)a.v, (OT *)a.o, a.lse,
-                       a.Nq, a.Nk, a.BH, a.nqtg, c, neg, Mask{});
+                       (const KT *)a.q, (const KT *)a.k, (const T *)a.v, (OT *)a.o, a.lse,
+                       a.Nq, a.Nk, a.BH, a.nqtg, c, neg, Mask{}, a.osc);
   }
   return hipGetLastError();
 }
@@ -2196,6 +2283,7 @@ int run(const void *q, const void *k, const void *v, void *o, float *lse, int64_
         const StreamPlan *plan, void *ws, void *stream, const Mask *mk = nullptr,
         const Split32 *ks = nullptr) {
   Launch a;
+  a.osc = 1.f;
   a.KC = ks ? ks->KC : 0;
   a.nsplit = ks ? ks->nsplit : 1;
   a.masked = mk != nullptr;
@@ -2528,6 +2616,68 @@ int noalloc_scratch(void **ptr) {
 
 }  // namespace
 
+namespace {
+
+// Validation and plan of the FP8 entry points on the pipelined kernel:
+// fa_fwd_fp8's argument rules; the workspace holds V widened to bf16
+// (rounded up to 256 bytes), then the stream-K partials when the schedule
+// of the 16-bit path with the same shape takes one.
+struct Fp8Plan {
+  Shape sh;
+  StreamPlan pl;
+  bool stream = false;
+  size_t vbytes = 0, bytes = 0;
+  float c = 0.f;
+};
+
+int fp8_plan(const void *q, const void *k, const void *v, const void *o, const float *lse,
+             int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, float scale, float dq,
+             float dk, float dv, int causal, int out_f32, bool check_ptrs, Fp8Plan &fp) {
+  if (check_ptrs && (!q || !k || !v || !o || !lse)) return FA_ERR_NULLPTR;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
+  if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  if (!isfinite(scale) || !isfinite(dq) || !isfinite(dk) || !isfinite(dv)) return FA_ERR_SCALE;
+  fp.c = scale * dq * dk * 1.4426950408889634f;
+  if (!isfinite(fp.c)) return FA_ERR_SCALE;
+  if (!sizes_fit(B, H, Nq, Nk, D)) return FA_ERR_SHAPE;
+  fp.sh.BH = B * H;
+  fp.sh.nqt = (Nq + kBM - 1) / kBM;
+  fp.sh.qb = (size_t)(fp.sh.BH * Nq * D);
+  fp.sh.kb = (size_t)(fp.sh.BH * Nk * D);
+  fp.sh.ob = (size_t)(fp.sh.BH * Nq * D) * (out_f32 ? 4 : 2);
+  fp.sh.lb = (size_t)(fp.sh.BH * Nq) * 4;
+  if (check_ptrs) {
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA_ERR_ALIGN;
+    if ((uintptr_t)lse & 3u) return FA_ERR_ALIGN;
+    const Shape &sh = fp.sh;
+    if (overlaps(o, sh.ob, q, sh.qb) || overlaps(o, sh.ob, k, sh.kb) ||
+        overlaps(o, sh.ob, v, sh.kb) || overlaps(lse, sh.lb, q, sh.qb) ||
+        overlaps(lse, sh.lb, k, sh.kb) || overlaps(lse, sh.lb, v, sh.kb) ||
+        overlaps(o, sh.ob, lse, sh.lb))
+      return FA_ERR_OVERLAP;
+  }
+  int cus = 0;
+  const int st = device_cus(&cus);
+  if (st != FA_OK) return st;
+  size_t pbytes = 0;
+  fp.stream = make_plan(fp.sh.BH, Nq, Nk, D, out_f32 ? FA_BF16_OF32 : FA_BF16, causal != 0,
+                        cus, fp.pl, pbytes);
+  fp.vbytes = (fp.sh.kb * 2 + 255) / 256 * 256;
+  fp.bytes = fp.vbytes + (fp.stream ? pbytes : 0);
+  return FA_OK;
+}
+
+template <typename OT>
+hipError_t dispatch_fp8(const Launch &a, int D, bool causal) {
+  if (D == 64)
+    return causal ? launch16<__bf16, OT, 64, true, uint8_t>(a)
+                  : launch16<__bf16, OT, 64, false, uint8_t>(a);
+  return causal ? launch16<__bf16, OT, 128, true, uint8_t>(a)
+                : launch16<__bf16, OT, 128, false, uint8_t>(a);
+}
+
+}  // namespace
+
 extern "C" {
 
 int fa_version(void) { return 300; }
@@ -2627,6 +2777,74 @@ int fa_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse, 
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
   return run(q, k, v, o, lse, Nq, Nk, D, scale, causal, dtype, sh,
              dtype == FA_F32 ? nullptr : &pl, workspace, stream, nullptr, &ks);
+}
+
+int fa_fwd_fp8_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+                              int causal, int out_f32, size_t *bytes) {
+  if (!bytes) return FA_ERR_NULLPTR;
+  *bytes = 0;
+  Fp8Plan fp;
+  const int st = fp8_plan(nullptr, nullptr, nullptr, nullptr, nullptr, B, H, Nq, Nk, D, 1.f,
+                          1.f, 1.f, 1.f, causal, out_f32, false, fp);
+  if (st != FA_OK) return st;
+  *bytes = fp.bytes;
+  return FA_OK;
+}
+
+int fa_fwd_fp8_ws(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
+                  int64_t H, int64_t Nq, int64_t Nk, int64_t D, float scale, float descale_q,
+                  float descale_k, float descale_v, int causal, int out_f32, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+  Fp8Plan fp;
+  int st = fp8_plan(q, k, v, o, lse, B, H, Nq, Nk, D, scale, descale_q, descale_k, descale_v,
+                    causal, out_f32, true, fp);
+  if (st != FA_OK) return st;
+  if (!workspace || workspace_bytes < fp.bytes) return FA_ERR_WORKSPACE;
+  if ((uintptr_t)workspace & 15u) return FA_ERR_ALIGN;
+  const Shape &sh = fp.sh;
+  if (overlaps(workspace, fp.bytes, q, sh.qb) || overlaps(workspace, fp.bytes, k, sh.kb) ||
+      overlaps(workspace, fp.bytes, v, sh.kb) || overlaps(workspace, fp.bytes, o, sh.ob) ||
+      overlaps(workspace, fp.bytes, lse, sh.lb))
+    return FA_ERR_OVERLAP;
+  hipStream_t hs = (hipStream_t)stream;
+  const size_t n16 = sh.kb / 16;  // D is a multiple of 16
+  hipLaunchKernelGGL(fa_fp8_widen, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, hs,
+                     (const u32x4 *)v, (u32x4 *)workspace, n16);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e);
+  Launch a;
+  a.masked = false;
+  a.mk = Mask{};
+  a.q = q;
+  a.k = k;
+  a.v = workspace;
+  a.o = o;
+  a.lse = lse;
+  a.ws = (float *)((char *)workspace + fp.vbytes);
+  a.Nq = (int)Nq;
+  a.Nk = (int)Nk;
+  a.BH = (int)sh.BH;
+  a.nqt = (int)sh.nqt;
+  a.nqtg = (int)((Nq + QRows<false>::value - 1) / QRows<false>::value);
+  a.c = fp.c;
+  a.osc = descale_v;
+  a.KC = 0;
+  a.nsplit = 1;
+  a.stream = hs;
+  a.plan = fp.stream ? &fp.pl : nullptr;
+  ChunkStarts starts;
+  CutList cuts;
+  a.starts = nullptr;
+  a.cuts = nullptr;
+  if (fp.stream) {
+    make_tables(fp.pl, causal != 0, starts, cuts);
+    a.starts = &starts;
+    a.cuts = &cuts;
+  }
+  e = out_f32 ? dispatch_fp8<float>(a, (int)D, causal != 0)
+              : dispatch_fp8<__bf16>(a, (int)D, causal != 0);
+  if (e != hipSuccess) return hip_fail(e);
+  return FA_OK;
 }
 
 int fa_fwd_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
