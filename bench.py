@@ -73,6 +73,70 @@ def measured_traffic(workload: str):
     return t.get("bytes_per_step")
 
 
+def write_traffic(run_dir: str, workload: str = "bf16_b8_n4096_d128_causal") -> dict:
+    """Builds profiles/traffic_<workload>.json from two rocprofv3 counter runs
+    of this script on the workload (run_dir/fetch: --pmc FETCH_SIZE,
+    run_dir/write: --pmc WRITE_SIZE; both with --copy-probe-mib 256 and
+    --output-format csv).  Each counter, in KiB per dispatch, is scaled by
+    what it reads for the probe's plain copy of 256 MiB; the record is keyed
+    to the forward sources' digest, so bench.py ignores it once they change."""
+    import csv
+    import statistics
+
+    def read(kind, counter):
+        by = {}
+        with open(os.path.join(run_dir, kind, "run_counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    by.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return by
+
+    fetch, write = read("fetch", "FETCH_SIZE"), read("write", "WRITE_SIZE")
+    copy = [n for n in fetch if "copyBuffer" in n]
+    if not copy:
+        raise SystemExit("no copy kernel in the fetch run (run with --copy-probe-mib 256)")
+    copy_bytes = 256 * (1 << 20)
+    copy_f = fetch[copy[0]][0]
+    copy_w = write[[n for n in write if "copyBuffer" in n][0]][0]
+    ff, wf = copy_bytes / (copy_f * 1024), copy_bytes / (copy_w * 1024)
+    from workloads import WORKLOADS
+
+    w = WORKLOADS[workload]
+    out = {"workload": workload, "entry": "fa_fwd_ws (every kernel of one call)",
+           "source_sha256": source_digest(), "source_files": list(FWD_SOURCES), "kernels": {}}
+    total = 0.0
+    counts = {"fetch": {}, "write": {}}
+    for name in sorted(n for n in fetch if "fa_" in n):
+        fk, wk = fetch[name], write.get(name, [])
+        if not wk:
+            continue
+        b = statistics.mean(fk) * 1024 * ff + statistics.mean(wk) * 1024 * wf
+        out["kernels"][name] = {"fetch_kib_per_launch": round(statistics.mean(fk), 1),
+                                "write_kib_per_launch": round(statistics.mean(wk), 1),
+                                "bytes": int(b)}
+        counts["fetch"][name] = len(fk)
+        counts["write"][name] = len(wk)
+        total += b
+    out["calibration"] = {"copy_bytes": copy_bytes, "copy_fetch_kib": round(copy_f, 1),
+                          "copy_write_kib": round(copy_w, 1), "fetch_factor": round(ff, 5),
+                          "write_factor": round(wf, 5)}
+    out["bytes_per_step"] = int(total)
+    s_in = 4 if w.dtype == "f32" else 2
+    out["algorithmic_bytes_per_step"] = (3 * w.B * w.H * w.N * w.D * s_in
+                                         + w.B * w.H * w.N * (w.D * s_in + 4))
+    out["launches_counted"] = counts
+    out["commands"] = [
+        f"cd /tmp && rocprofv3 --pmc {c} -d <out>/{k} -o run --output-format csv -- python3 "
+        f"/root/repo/bench.py --workload {workload} --steps 20 --warmup 2 --no-cpu-baseline "
+        f"--copy-probe-mib 256" for c, k in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write"))]
+    out["commands"].append(f"python3 /root/repo/bench.py --write-traffic <out>")
+    path = os.path.join(TRAFFIC_DIR, f"traffic_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    return out
+
+
 def device_facts(torch, dev):
     """What the box reports about itself: compute units, the maximum shader
     clock (HIP device attribute, else the highest level the driver lists in
@@ -298,6 +362,9 @@ def main() -> int:
                     help="time fa_fwd_masked instead: B=1 H=8 N=32768 D=128 causal bf16 "
                          "under a local window W with G global tokens; flops counted "
                          "over the visible pairs only (4*D each)")
+    ap.add_argument("--write-traffic", default=None, metavar="DIR",
+                    help="write profiles/traffic_<workload>.json from the rocprofv3 "
+                         "FETCH_SIZE / WRITE_SIZE runs under DIR (no GPU work)")
     ap.add_argument("--fp8-nows", action="store_true",
                     help="with --fp8: time fa_fwd_fp8 (no workspace, the query-stationary "
                          "kernel) instead of fa_fwd_fp8_ws")
@@ -311,6 +378,14 @@ def main() -> int:
                          "the forward's: the five N x N contractions of the "
                          "recomputing backward)")
     args = ap.parse_args()
+
+    if args.write_traffic:
+        from workloads import HEADLINE
+
+        rec = write_traffic(args.write_traffic, args.workload or HEADLINE)
+        print(json.dumps({k: rec[k] for k in ("workload", "bytes_per_step",
+                                              "algorithmic_bytes_per_step")}))
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
