@@ -45,6 +45,7 @@
 //     the scale of dQ and dK is applied once, in fp32, at the store.
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 
 #include <math.h>
 #include <stdint.h>
@@ -55,6 +56,12 @@
 // Records the runtime's text for fa_last_hip_error (defined with the
 // forward pass's host code) and returns FA_ERR_HIP.
 int fa_internal_hip_fail(hipError_t e);
+// dQ on the forward's pipelined machinery (fa_fwd.hip): dense problems, D = 64
+// or 128; returns false for any other case, which the kernel below takes.
+bool fa_internal_bwd_dq8(const void *q, const void *k, const void *v, const void *dout,
+                         const float *lse, const float *dl, void *dq, int Nq, int Nk, int BH,
+                         int D, int dtype, bool causal, float c, float scale, void *stream,
+                         hipError_t *err);
 
 #include "tiles.h"
 
@@ -545,6 +552,16 @@ hipError_t launch_bwd(const BwdArgs &a) {
                        nkt, c, a.scale, a.cu_q, a.cu_k, a.S, a.mk);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  if constexpr (!MASKED && (D == 64 || D == 128)) {
+    if (!vl) {
+      constexpr bool of32 = std::is_same<OT, float>::value;
+      constexpr int code = std::is_same<T, __bf16>::value ? (of32 ? FA_BF16_OF32 : FA_BF16)
+                                                          : (of32 ? FA_F16_OF32 : FA_F16);
+      if (fa_internal_bwd_dq8(a.q, a.k, a.v, a.dout, a.lse, (const float *)a.dl, a.dq, a.Nq,
+                              a.Nk, a.BH, D, code, CAUSAL, c, a.scale, a.stream, &e))
+        return e;
+    }
   }
   hipLaunchKernelGGL((fa_bwd_dq<T, OT, D, CAUSAL, MASKED>), dim3((unsigned)(slices * nqt)),
                      dim3(kThreads), 0, a.stream, (const T *)a.q, (const T *)a.k,

@@ -852,9 +852,9 @@ static_assert(QRows<true>::value == kPairRows && QRows<false>::value == kGridRow
 // skipping it in the pair-split loop +1.7%; in the 256-row loop, where the
 // waits then need each wave's own count (a scalar branch per step), +-0 at
 // D = 128 and 1-5% slower at D = 16-64.
-template <typename T, int D, typename KT = T>
+template <typename T, int D, typename KT = T, typename LAY = PipeLayout<T, D, KT>>
 struct Dma8 {
-  typedef PipeLayout<T, D, KT> L;
+  typedef LAY L;
   static constexpr int KJ = (L::K_INS + kWaves8 - 1) / kWaves8;
   static constexpr int VJ = (L::V_INS + kWaves8 - 1) / kWaves8;
   static constexpr int PER_WAVE = KJ + VJ;
@@ -1295,6 +1295,196 @@ __global__ __launch_bounds__(kThreads8) void fa_fwd_pipe8(
     pipe8_run<T, OT, D, CAUSAL, PAIR, false, KT>(q, k, v, o, lse, nullptr, Nq, Nk, c, negate,
                                                  it, 0, Mask{}, KeyList{}, osc);
   }
+}
+
+// ---------------------------------------------------------------------------
+// dQ of the backward pass on the forward's pipelined machinery.  The
+// backward recomputes the probabilities from the saved logsumexp (page
+// "解释FlashAttention的显存优化原理" §一.2(2)); for a 128-row query tile,
+// with Q and dO held in registers like the forward's Q:
+//
+//     S^T  = K Q^T               (A: K rows from LDS, B: Q^T)
+//     dP^T = V dO^T              (A: V rows from LDS, B: dO^T)
+//     P = 2^(c s - L log2 e),  dS = P (dP - Dl)       (0 on hidden pairs)
+//     dQ^T += K^T dS^T            (A: K^T by ds_read_b64_tr_b16, B: dS^T rounded to T)
+//
+// so one lane owns one query (L and Dl are per-lane scalars) and dS never
+// leaves registers, as P in the forward.  K and V 64-key tiles stream through
+// a four-stage DMA ring (buffer_load ... lds); K is read both by rows and
+// transposed, so its row stride is the one that measured best for both in
+// the backward's LDS blocks (19 slots at D = 128, 13 at D = 64), V keeps the
+// forward's row stride.  Eight waves, two per SIMD: waves w and w + 4 hold
+// query group w % 4 (32 rows) and take the even and odd 32-key blocks; their
+// dQ^T partial sums are added through LDS at the end.  One workgroup per
+// query tile, longest first under the causal mask.
+template <typename T, int D>
+struct DqLayout {
+  static constexpr int KRB = D * (int)sizeof(T);
+  static constexpr int SK = D == 128 ? 19 : 13;  // K rows (read both ways), 16-byte slots
+  static constexpr int SV = KRB / 16 + 1;        // V rows (read by rows)
+  static constexpr int K_BYTES = kBN * SK * 16;
+  static constexpr int V_BYTES = kBN * SV * 16;
+  static constexpr int K_INS = kBN * SK / kWave;
+  static constexpr int V_INS = kBN * SV / kWave;
+  static constexpr int V_OFF = kStages * K_BYTES;
+  static constexpr int LDS_BYTES = kStages * (K_BYTES + V_BYTES);
+  static constexpr uint32_t K_TILE_GLOBAL = kBN * KRB;
+  static constexpr uint32_t V_TILE_GLOBAL = kBN * KRB;
+  static_assert(LDS_BYTES <= 150 * 1024, "LDS");
+};
+
+template <typename T, typename OT, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads8) void fa_bwd_dq8(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    const T *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dl,
+    OT *__restrict__ dq, int Nq, int Nk, int BH, int nqt, float c, float scale) {
+  typedef DqLayout<T, D> L;
+  typedef Dma8<T, D, T, L> DM;
+  typedef typename Mma<T>::frag frag;
+  constexpr int QF = D / 16;   // MFMAs of S^T and of dP^T per 32-key block
+  constexpr int NDB = D / 32;  // dQ^T blocks of 32 head-dim rows
+  constexpr int QT = 128;
+  __shared__ __attribute__((aligned(16))) char ring_[DM::LDS_BYTES];
+  lds_char *ring = (lds_char *)ring_;
+  const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
+
+  const WorkItem wi = work_item(BH, nqt, CAUSAL, QT);
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qg = wave & 3, h = wave >> 2;
+  const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int qw = wi.q0 + qg * 32;
+  const int my_q = qw + l32;
+  const uint32_t kbase = (uint32_t)(l32 * L::SK * 16 + g * 16);
+  const uint32_t vbase = (uint32_t)(L::V_OFF + l32 * L::SV * 16 + g * 16);
+  uint32_t tbase;
+  {
+    const int G = lane >> 4, s16 = lane & 15;
+    const int row = 4 * (G >> 1) + (s16 >> 2);
+    const int col = 16 * (G & 1) + 4 * (s16 & 3);
+    tbase = (uint32_t)(row * L::SK * 16 + col * 2);
+  }
+  const size_t qoff = (size_t)wi.bh * Nq * D;
+  const size_t koff = (size_t)wi.bh * Nk * D;
+  const u32x4 q_rs = raw_rsrc(q + qoff, (uint32_t)Nq * D * sizeof(T));
+  const u32x4 do_rs = raw_rsrc(dout + qoff, (uint32_t)Nq * D * sizeof(T));
+  const u32x4 k_rs = raw_rsrc(k + koff, (uint32_t)Nk * D * sizeof(T));
+  const u32x4 v_rs = raw_rsrc(v + koff, (uint32_t)Nk * D * sizeof(T));
+  DM dm;
+  dm.init(ring_addr, wave, lane);
+
+  // rows past Nq: L = +inf gives P = 0
+  const float l2 = my_q < Nq ? lse[(size_t)wi.bh * Nq + my_q] * 1.4426950408889634f : INFINITY;
+  const float dd = my_q < Nq ? dl[(size_t)wi.bh * Nq + my_q] : 0.f;
+  const int kend = CAUSAL ? min(Nk, wi.q0 + QT) : Nk;
+  const int ntiles = (kend + kBN - 1) / kBN;
+  // last 32-key block with a key this wave's queries see
+  const int lastb = CAUSAL ? min(2 * ntiles - 1, (qw + 31) / 32) : 2 * ntiles - 1;
+
+  u32x4 qraw[QF], draw[QF];
+#pragma unroll
+  for (int f = 0; f < QF; ++f) {
+    const uint32_t off = ((uint32_t)my_q * D + 16 * f + 8 * g) * sizeof(T);
+    qraw[f] = load16_async(q_rs, off);
+    draw[f] = load16_async(do_rs, off);
+  }
+  dm.issue(k_rs, v_rs, 0, 0, 0, 0);
+  if (ntiles > 1) dm.issue(k_rs, v_rs, 1, 1, 1, 1);
+  frag qf[QF], dof[QF];
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+
+  for (int r = 0; r < ntiles; ++r) {
+    if ((r & 1) == 0) {
+      // tiles r and r+1 have landed, and every wave is done with the stages
+      // of tiles r-2 and r-1, which tiles r+2 and r+3 now take
+      ring_barrier<0>();
+      if (r + 2 < ntiles) dm.issue(k_rs, v_rs, r + 2, (r + 2) & 3, r + 2, (r + 2) & 3);
+      if (r + 3 < ntiles) dm.issue(k_rs, v_rs, r + 3, (r + 3) & 3, r + 3, (r + 3) & 3);
+      if (r == 0) {
+#pragma unroll
+        for (int f = 0; f < QF; ++f) {
+          asm volatile("" : "+v"(qraw[f]), "+v"(draw[f]));  // read after the wait above
+          qf[f] = __builtin_bit_cast(frag, qraw[f]);
+          dof[f] = __builtin_bit_cast(frag, draw[f]);
+        }
+      }
+    }
+    const int b = 2 * r + h;
+    if (b > lastb) continue;  // wave-uniform; later blocks are past it too
+    const int st = r & 3;
+    const lds_char *kp = ring + st * L::K_BYTES + h * 32 * L::SK * 16;
+    const lds_char *vp = ring + st * L::V_BYTES + h * 32 * L::SV * 16;
+    f32x16 sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int f = 0; f < QF; ++f) {
+      const frag kf = *(const __attribute__((address_space(3))) frag *)(kp + kbase + f * 32);
+      const frag vf = *(const __attribute__((address_space(3))) frag *)(vp + vbase + f * 32);
+      sc = Mma<T>::mma(kf, qf[f], sc);
+      dp = Mma<T>::mma(vf, dof[f], dp);
+    }
+    const int k0 = 32 * b;
+    const bool need_mask = (k0 + 32 > Nk) || (CAUSAL && k0 + 31 > qw);
+    float ds[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], c, -l2));
+      if (need_mask) {
+        const int key = k0 + acc_row(e, g);
+        if (key >= Nk || (CAUSAL && key > my_q)) p = 0.f;
+      }
+      ds[e] = p * (dp[e] - dd);
+    }
+    frag dsb[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4 w = {Mma<T>::pack2(ds[8 * ks], ds[8 * ks + 1]),
+                       Mma<T>::pack2(ds[8 * ks + 2], ds[8 * ks + 3]),
+                       Mma<T>::pack2(ds[8 * ks + 4], ds[8 * ks + 5]),
+                       Mma<T>::pack2(ds[8 * ks + 6], ds[8 * ks + 7])};
+      dsb[ks] = __builtin_bit_cast(frag, w);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const lds_char *a0 = kp + tbase + ks * 16 * L::SK * 16 + db * 64;
+        const u32x2 lo = read_tr16(a0);
+        const u32x2 hi = read_tr16(a0 + 8 * L::SK * 16);
+        const u32x4 raw = {lo[0], lo[1], hi[0], hi[1]};
+        acc[db] = Mma<T>::mma(__builtin_bit_cast(frag, raw), dsb[ks], acc[db]);
+      }
+  }
+  wait_vmcnt<0>();    // no DMA may outlive the ring
+  ring_barrier<0>();  // every wave is done with the ring
+
+  // the odd wave of each group hands its partial sums to the even one
+  constexpr int NR = NDB * 4;
+  lds_char *xch = ring + (uint32_t)qg * NR * kWave * 16;
+  if (h == 1) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 x = {acc[db][4 * r4], acc[db][4 * r4 + 1], acc[db][4 * r4 + 2],
+                         acc[db][4 * r4 + 3]};
+        *(__attribute__((address_space(3))) f32x4 *)(xch + ((db * 4 + r4) * kWave + lane) * 16) = x;
+      }
+  }
+  ring_barrier<0>();
+  if (h == 1 || my_q >= Nq) return;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 x = *(const __attribute__((address_space(3))) f32x4 *)(
+          xch + ((db * 4 + r4) * kWave + lane) * 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[db][4 * r4 + e] += x[e];
+    }
+  store_row<OT, NDB>(acc, scale, dq + ((size_t)wi.bh * Nq + my_q) * D, g, D);
 }
 
 // Variable-length batches (page "FlashAttention-2实现与优化：高效注意力机制详解"
@@ -2577,6 +2767,62 @@ int varlen_entry(const void *q, const void *k, const void *v, void *o, float *ls
 // Shared with the backward pass's host code (same library, hidden symbol).
 __attribute__((visibility("hidden"))) int fa_internal_hip_fail(hipError_t e) {
   return hip_fail(e);
+}
+
+// dQ of fa_bwd on the pipelined kernel (fa_bwd_dq8), for dense problems at
+// D = 64 or 128 with 16-bit inputs; called by the backward's host code
+// after its row-term kernel.  Returns false for a case it does not take.
+namespace {
+template <typename T, typename OT, int D>
+hipError_t launch_dq8(const void *q, const void *k, const void *v, const void *dout,
+                      const float *lse, const float *dl, void *dq, int Nq, int Nk, int BH,
+                      bool causal, float c, float scale, hipStream_t s) {
+  const int nqt = (Nq + 127) / 128;
+  const dim3 grid((unsigned)(BH * nqt)), block(kThreads8);
+  if (causal)
+    hipLaunchKernelGGL((fa_bwd_dq8<T, OT, D, true>), grid, block, 0, s, (const T *)q,
+                       (const T *)k, (const T *)v, (const T *)dout, lse, dl, (OT *)dq, Nq, Nk,
+                       BH, nqt, c, scale);
+  else
+    hipLaunchKernelGGL((fa_bwd_dq8<T, OT, D, false>), grid, block, 0, s, (const T *)q,
+                       (const T *)k, (const T *)v, (const T *)dout, lse, dl, (OT *)dq, Nq, Nk,
+                       BH, nqt, c, scale);
+  return hipGetLastError();
+}
+template <typename T, typename OT>
+hipError_t dq8_d(int D, const void *q, const void *k, const void *v, const void *dout,
+                 const float *lse, const float *dl, void *dq, int Nq, int Nk, int BH,
+                 bool causal, float c, float scale, hipStream_t s) {
+  return D == 64 ? launch_dq8<T, OT, 64>(q, k, v, dout, lse, dl, dq, Nq, Nk, BH, causal, c,
+                                         scale, s)
+                 : launch_dq8<T, OT, 128>(q, k, v, dout, lse, dl, dq, Nq, Nk, BH, causal, c,
+                                          scale, s);
+}
+}  // namespace
+
+__attribute__((visibility("hidden"))) bool fa_internal_bwd_dq8(
+    const void *q, const void *k, const void *v, const void *dout, const float *lse,
+    const float *dl, void *dq, int Nq, int Nk, int BH, int D, int dtype, bool causal, float c,
+    float scale, void *stream, hipError_t *err) {
+  if (D != 64 && D != 128) return false;
+  hipStream_t s = (hipStream_t)stream;
+  switch (dtype) {
+    case FA_BF16:
+      *err = dq8_d<__bf16, __bf16>(D, q, k, v, dout, lse, dl, dq, Nq, Nk, BH, causal, c, scale, s);
+      return true;
+    case FA_BF16_OF32:
+      *err = dq8_d<__bf16, float>(D, q, k, v, dout, lse, dl, dq, Nq, Nk, BH, causal, c, scale, s);
+      return true;
+    case FA_F16:
+      *err = dq8_d<_Float16, _Float16>(D, q, k, v, dout, lse, dl, dq, Nq, Nk, BH, causal, c,
+                                       scale, s);
+      return true;
+    case FA_F16_OF32:
+      *err = dq8_d<_Float16, float>(D, q, k, v, dout, lse, dl, dq, Nq, Nk, BH, causal, c, scale,
+                                    s);
+      return true;
+    default: return false;
+  }
 }
 
 // Scratch of fa_fwd_noalloc: the stream-K schedule's partial results, in a
