@@ -189,8 +189,17 @@ def test_bwd_validation(kw, status):
 
 
 def test_bwd_workspace_size():
-    st, n = fa.fa_bwd_workspace_size(2, 3, 100, 90, 64, 1, fa.FA_BF16)
+    """The row terms (B*H*Nq fp32), plus at D = 64 and 128 the dQ partial
+    sums of the stream schedule past them (rounded up to 256 bytes): at most
+    two slots of 128 rows x D fp32 per chunk, 256 chunks.  The query needs no
+    device."""
+    st, n = fa.fa_bwd_workspace_size(2, 3, 100, 90, 32, 1, fa.FA_BF16)
     assert (st, n) == (fa.FA_OK, 2 * 3 * 100 * 4)
+    st, n = fa.fa_bwd_workspace_size(2, 3, 100, 90, 64, 1, fa.FA_BF16)
+    assert st == fa.FA_OK and n > 2 * 3 * 100 * 4 and (n - 2560) % (2 * 128 * 64 * 4) == 0
+    assert n - 2560 <= 2 * 256 * 128 * 64 * 4
+    # 512 or more query tiles of 128 rows: one workgroup per tile, row terms only
+    assert fa.fa_bwd_workspace_size(1, 32, 2048, 2048, 128, 1, fa.FA_BF16)[1] == 32 * 2048 * 4
     assert fa.fa_bwd_workspace_size(2, 3, 100, 90, 48, 1, fa.FA_BF16)[0] == fa.FA_ERR_HEAD_DIM
     assert fa.fa_bwd_workspace_size(2, 3, 100, 90, 64, 1, fa.FA_F32)[0] == fa.FA_ERR_DTYPE
 

@@ -171,6 +171,49 @@ def test_bwd_deterministic():
         assert np.array_equal(x, y)
 
 
+@pytest.mark.parametrize("shape", [(2, 2, 700, 700, 128), (8, 1, 1024, 1024, 64),
+                                   (1, 3, 300, 1300, 128)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_dq_stream_and_grid(shape, causal):
+    """dQ at D = 64 and 128 runs the stream-K schedule of 128-row tiles when
+    the workspace holds its partial sums (the size fa_bwd_workspace_size
+    reports) and one workgroup per tile when it holds only the row terms:
+    both against the oracle's bound, and within a few fp32 roundings of
+    each other (they add the key chunks in a different order); dK and dV are
+    the same kernel either way, bit for bit."""
+    B, H, Nq, Nk, D = shape
+    q, k, v, g = inputs(B, H, Nq, Nk, D, seed=950 + Nq)
+    scale = 1.0 / math.sqrt(D)
+    st, full = fa.fa_bwd_workspace_size(B, H, Nq, Nk, D, causal, fa.FA_BF16_OF32)
+    assert st == fa.FA_OK and full > B * H * Nq * 4, "no stream schedule for dQ"
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, g))
+    o, lse = fa.fwd(qd, kd, vd, causal=causal, scale=scale)
+    res = []
+    for nbytes in (full, B * H * Nq * 4):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+        grads = [torch.empty(t.shape, dtype=torch.float32, device=DEV) for t in (qd, kd, vd)]
+        st = fa.fa_bwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       gd.data_ptr(), *(t.data_ptr() for t in grads), B, H, Nq, Nk, D, scale,
+                       int(causal), fa.FA_BF16_OF32, ws.data_ptr(), nbytes,
+                       torch.cuda.current_stream().cuda_stream)
+        assert st == fa.FA_OK, fa.fa_status_str(st)
+        torch.cuda.synchronize()
+        res.append([t.double().cpu().numpy() for t in grads])
+    ref = oracle.attention_bwd(*(t.double().numpy() for t in (q, k, v, g)), scale, causal,
+                               magnitudes=True)
+    u = UNIT[q.dtype]
+    for which, grads in zip(("stream", "grid"), res):
+        for n, name in enumerate(("dQ", "dK", "dV")):
+            r, b = ref[n].reshape(-1, D), ref[n + 3].reshape(-1, D)
+            err = np.abs(grads[n].reshape(-1, D) - r)
+            ratio = float((err / (2 * u * b + 1e-6 * float(b.max()) + 1e-30)).max())
+            _log(f"  {which} {name}: max-abs {float(err.max()):.3e} worst error/bound {ratio:.3f}")
+            assert ratio <= 1.0, f"{which} {name}: error exceeds 2u*b ({ratio:.3f})"
+    assert np.array_equal(res[0][1], res[1][1]) and np.array_equal(res[0][2], res[1][2])
+    d = np.abs(res[0][0] - res[1][0])
+    assert float(d.max()) <= 1e-5 * max(1.0, float(np.abs(res[1][0]).max())), float(d.max())
+
+
 def test_bwd_rejects_fp32_and_odd_head_dims():
     q = torch.zeros(1, 1, 64, 48, device=DEV, dtype=torch.bfloat16)
     lse = torch.zeros(1, 1, 64, device=DEV)
@@ -193,7 +236,8 @@ def test_bwd_d16_sweep_shape_sampled():
             what="D16 sampled")
 
 
-@pytest.mark.parametrize("entry", ["bwd", "bwd_masked", "fwd_varlen", "fwd_masked"])
+@pytest.mark.parametrize("entry", ["bwd", "bwd_stream", "bwd_masked", "fwd_varlen",
+                                   "fwd_masked"])
 def test_graph_capture_replays_match_eager(entry):
     """fa_bwd, fa_bwd_masked, fa_fwd_varlen and fa_fwd_masked are plain
     launches on the caller's stream (no allocation, no memset), so a HIP
@@ -206,10 +250,14 @@ def test_graph_capture_replays_match_eager(entry):
     scale = 0.125
     o, lse = fa.fwd(qd, kd, vd, causal=True, scale=scale)
     outs = [torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)]
-    ws = torch.empty(B * H * N * 4, dtype=torch.uint8, device=DEV)
+    nws = B * H * N * 4
+    if entry == "bwd_stream":  # room for the stream schedule's dQ partial sums
+        nws = fa.fa_bwd_workspace_size(B, H, N, N, D, 1, fa.FA_BF16)[1]
+        assert nws > B * H * N * 4
+    ws = torch.empty(nws, dtype=torch.uint8, device=DEV)
     cu = torch.tensor([0, 100, 333, 2 * N], dtype=torch.int32, device=DEV)
     stream = lambda: torch.cuda.current_stream().cuda_stream  # noqa: E731
-    if entry in ("bwd", "bwd_masked"):
+    if entry in ("bwd", "bwd_stream", "bwd_masked"):
         if entry == "bwd_masked":
             o, lse = fa.fwd_masked(qd, kd, vd, 40, 5, causal=True, scale=scale)
 
@@ -217,7 +265,7 @@ def test_graph_capture_replays_match_eager(entry):
             base = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(),
                     lse.data_ptr(), gd.data_ptr(), outs[0].data_ptr(), outs[1].data_ptr(),
                     outs[2].data_ptr(), B, H, N, N, D, scale, 1)
-            if entry == "bwd":
+            if entry in ("bwd", "bwd_stream"):
                 st = fa.fa_bwd(*base, fa.FA_BF16, ws.data_ptr(), ws.numel(), stream())
             else:
                 st = fa.fa_bwd_masked(*base, 40, 5, fa.FA_BF16, ws.data_ptr(), ws.numel(),

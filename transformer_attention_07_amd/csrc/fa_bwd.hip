@@ -58,10 +58,13 @@
 int fa_internal_hip_fail(hipError_t e);
 // dQ on the forward's pipelined machinery (fa_fwd.hip): dense problems, D = 64
 // or 128; returns false for any other case, which the kernel below takes.
+// ws / ws_bytes: scratch for the stream schedule's partial sums (its size
+// from fa_internal_dq8_bytes; with less, one workgroup per query tile).
 bool fa_internal_bwd_dq8(const void *q, const void *k, const void *v, const void *dout,
                          const float *lse, const float *dl, void *dq, int Nq, int Nk, int BH,
-                         int D, int dtype, bool causal, float c, float scale, void *stream,
-                         hipError_t *err);
+                         int D, int dtype, bool causal, float c, float scale, void *ws,
+                         size_t ws_bytes, void *stream, hipError_t *err);
+size_t fa_internal_dq8_bytes(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, bool causal);
 
 #include "tiles.h"
 
@@ -524,6 +527,8 @@ struct BwdArgs {
   const int *cu_q = nullptr, *cu_k = nullptr;
   int S = 1, maxq = 0, maxk = 0;
   Mask mk = {0, 1, 0};  // local-window + global-token mask (MASKED launches)
+  void *dqws = nullptr;  // dQ partial sums of the stream schedule (dense only)
+  size_t dqws_bytes = 0;
 };
 
 template <typename T, typename OT, int D, bool CAUSAL, bool MASKED = false>
@@ -559,7 +564,8 @@ hipError_t launch_bwd(const BwdArgs &a) {
       constexpr int code = std::is_same<T, __bf16>::value ? (of32 ? FA_BF16_OF32 : FA_BF16)
                                                           : (of32 ? FA_F16_OF32 : FA_F16);
       if (fa_internal_bwd_dq8(a.q, a.k, a.v, a.dout, a.lse, (const float *)a.dl, a.dq, a.Nq,
-                              a.Nk, a.BH, D, code, CAUSAL, c, a.scale, a.stream, &e))
+                              a.Nk, a.BH, D, code, CAUSAL, c, a.scale, a.dqws, a.dqws_bytes,
+                              a.stream, &e))
         return e;
     }
   }
@@ -616,12 +622,13 @@ extern "C" {
 
 int fa_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
                           int causal, int dtype, size_t *bytes) {
-  (void)causal;
   if (!bytes) return FA_ERR_NULLPTR;
   *bytes = 0;
   const int st = check_shape(B, H, Nq, Nk, D, dtype);
   if (st != FA_OK) return st;
-  *bytes = (size_t)(B * H * Nq) * sizeof(float);
+  const size_t lb = (size_t)(B * H * Nq) * sizeof(float);
+  const size_t extra = fa_internal_dq8_bytes(B * H, Nq, Nk, D, causal != 0);
+  *bytes = extra ? (lb + 255) / 256 * 256 + extra : lb;
   return FA_OK;
 }
 
@@ -667,6 +674,14 @@ static int bwd_dense(const void *q, const void *k, const void *v, const void *o,
   a.dk = dk;
   a.dv = dv;
   a.dl = (float *)workspace;
+  {
+    // past the row terms (rounded up to 256 bytes): the dQ partial sums
+    const size_t off = (lb + 255) / 256 * 256;
+    if (!mk && workspace_bytes > off) {
+      a.dqws = (char *)workspace + off;
+      a.dqws_bytes = workspace_bytes - off;
+    }
+  }
   a.Nq = (int)Nq;
   a.Nk = (int)Nk;
   a.BH = (int)BH;

@@ -1297,196 +1297,6 @@ __global__ __launch_bounds__(kThreads8) void fa_fwd_pipe8(
   }
 }
 
-// ---------------------------------------------------------------------------
-// dQ of the backward pass on the forward's pipelined machinery.  The
-// backward recomputes the probabilities from the saved logsumexp (page
-// "解释FlashAttention的显存优化原理" §一.2(2)); for a 128-row query tile,
-// with Q and dO held in registers like the forward's Q:
-//
-//     S^T  = K Q^T               (A: K rows from LDS, B: Q^T)
-//     dP^T = V dO^T              (A: V rows from LDS, B: dO^T)
-//     P = 2^(c s - L log2 e),  dS = P (dP - Dl)       (0 on hidden pairs)
-//     dQ^T += K^T dS^T            (A: K^T by ds_read_b64_tr_b16, B: dS^T rounded to T)
-//
-// so one lane owns one query (L and Dl are per-lane scalars) and dS never
-// leaves registers, as P in the forward.  K and V 64-key tiles stream through
-// a four-stage DMA ring (buffer_load ... lds); K is read both by rows and
-// transposed, so its row stride is the one that measured best for both in
-// the backward's LDS blocks (19 slots at D = 128, 13 at D = 64), V keeps the
-// forward's row stride.  Eight waves, two per SIMD: waves w and w + 4 hold
-// query group w % 4 (32 rows) and take the even and odd 32-key blocks; their
-// dQ^T partial sums are added through LDS at the end.  One workgroup per
-// query tile, longest first under the causal mask.
-template <typename T, int D>
-struct DqLayout {
-  static constexpr int KRB = D * (int)sizeof(T);
-  static constexpr int SK = D == 128 ? 19 : 13;  // K rows (read both ways), 16-byte slots
-  static constexpr int SV = KRB / 16 + 1;        // V rows (read by rows)
-  static constexpr int K_BYTES = kBN * SK * 16;
-  static constexpr int V_BYTES = kBN * SV * 16;
-  static constexpr int K_INS = kBN * SK / kWave;
-  static constexpr int V_INS = kBN * SV / kWave;
-  static constexpr int V_OFF = kStages * K_BYTES;
-  static constexpr int LDS_BYTES = kStages * (K_BYTES + V_BYTES);
-  static constexpr uint32_t K_TILE_GLOBAL = kBN * KRB;
-  static constexpr uint32_t V_TILE_GLOBAL = kBN * KRB;
-  static_assert(LDS_BYTES <= 150 * 1024, "LDS");
-};
-
-template <typename T, typename OT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads8) void fa_bwd_dq8(
-    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-    const T *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dl,
-    OT *__restrict__ dq, int Nq, int Nk, int BH, int nqt, float c, float scale) {
-  typedef DqLayout<T, D> L;
-  typedef Dma8<T, D, T, L> DM;
-  typedef typename Mma<T>::frag frag;
-  constexpr int QF = D / 16;   // MFMAs of S^T and of dP^T per 32-key block
-  constexpr int NDB = D / 32;  // dQ^T blocks of 32 head-dim rows
-  constexpr int QT = 128;
-  __shared__ __attribute__((aligned(16))) char ring_[DM::LDS_BYTES];
-  lds_char *ring = (lds_char *)ring_;
-  const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
-
-  const WorkItem wi = work_item(BH, nqt, CAUSAL, QT);
-  int tid = threadIdx.x;
-  asm volatile("" : "+v"(tid));
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qg = wave & 3, h = wave >> 2;
-  const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
-  const int qw = wi.q0 + qg * 32;
-  const int my_q = qw + l32;
-  const uint32_t kbase = (uint32_t)(l32 * L::SK * 16 + g * 16);
-  const uint32_t vbase = (uint32_t)(L::V_OFF + l32 * L::SV * 16 + g * 16);
-  uint32_t tbase;
-  {
-    const int G = lane >> 4, s16 = lane & 15;
-    const int row = 4 * (G >> 1) + (s16 >> 2);
-    const int col = 16 * (G & 1) + 4 * (s16 & 3);
-    tbase = (uint32_t)(row * L::SK * 16 + col * 2);
-  }
-  const size_t qoff = (size_t)wi.bh * Nq * D;
-  const size_t koff = (size_t)wi.bh * Nk * D;
-  const u32x4 q_rs = raw_rsrc(q + qoff, (uint32_t)Nq * D * sizeof(T));
-  const u32x4 do_rs = raw_rsrc(dout + qoff, (uint32_t)Nq * D * sizeof(T));
-  const u32x4 k_rs = raw_rsrc(k + koff, (uint32_t)Nk * D * sizeof(T));
-  const u32x4 v_rs = raw_rsrc(v + koff, (uint32_t)Nk * D * sizeof(T));
-  DM dm;
-  dm.init(ring_addr, wave, lane);
-
-  // rows past Nq: L = +inf gives P = 0
-  const float l2 = my_q < Nq ? lse[(size_t)wi.bh * Nq + my_q] * 1.4426950408889634f : INFINITY;
-  const float dd = my_q < Nq ? dl[(size_t)wi.bh * Nq + my_q] : 0.f;
-  const int kend = CAUSAL ? min(Nk, wi.q0 + QT) : Nk;
-  const int ntiles = (kend + kBN - 1) / kBN;
-  // last 32-key block with a key this wave's queries see
-  const int lastb = CAUSAL ? min(2 * ntiles - 1, (qw + 31) / 32) : 2 * ntiles - 1;
-
-  u32x4 qraw[QF], draw[QF];
-#pragma unroll
-  for (int f = 0; f < QF; ++f) {
-    const uint32_t off = ((uint32_t)my_q * D + 16 * f + 8 * g) * sizeof(T);
-    qraw[f] = load16_async(q_rs, off);
-    draw[f] = load16_async(do_rs, off);
-  }
-  dm.issue(k_rs, v_rs, 0, 0, 0, 0);
-  if (ntiles > 1) dm.issue(k_rs, v_rs, 1, 1, 1, 1);
-  frag qf[QF], dof[QF];
-  f32x16 acc[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
-
-  for (int r = 0; r < ntiles; ++r) {
-    if ((r & 1) == 0) {
-      // tiles r and r+1 have landed, and every wave is done with the stages
-      // of tiles r-2 and r-1, which tiles r+2 and r+3 now take
-      ring_barrier<0>();
-      if (r + 2 < ntiles) dm.issue(k_rs, v_rs, r + 2, (r + 2) & 3, r + 2, (r + 2) & 3);
-      if (r + 3 < ntiles) dm.issue(k_rs, v_rs, r + 3, (r + 3) & 3, r + 3, (r + 3) & 3);
-      if (r == 0) {
-#pragma unroll
-        for (int f = 0; f < QF; ++f) {
-          asm volatile("" : "+v"(qraw[f]), "+v"(draw[f]));  // read after the wait above
-          qf[f] = __builtin_bit_cast(frag, qraw[f]);
-          dof[f] = __builtin_bit_cast(frag, draw[f]);
-        }
-      }
-    }
-    const int b = 2 * r + h;
-    if (b > lastb) continue;  // wave-uniform; later blocks are past it too
-    const int st = r & 3;
-    const lds_char *kp = ring + st * L::K_BYTES + h * 32 * L::SK * 16;
-    const lds_char *vp = ring + st * L::V_BYTES + h * 32 * L::SV * 16;
-    f32x16 sc = f32x16{}, dp = f32x16{};
-#pragma unroll
-    for (int f = 0; f < QF; ++f) {
-      const frag kf = *(const __attribute__((address_space(3))) frag *)(kp + kbase + f * 32);
-      const frag vf = *(const __attribute__((address_space(3))) frag *)(vp + vbase + f * 32);
-      sc = Mma<T>::mma(kf, qf[f], sc);
-      dp = Mma<T>::mma(vf, dof[f], dp);
-    }
-    const int k0 = 32 * b;
-    const bool need_mask = (k0 + 32 > Nk) || (CAUSAL && k0 + 31 > qw);
-    float ds[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], c, -l2));
-      if (need_mask) {
-        const int key = k0 + acc_row(e, g);
-        if (key >= Nk || (CAUSAL && key > my_q)) p = 0.f;
-      }
-      ds[e] = p * (dp[e] - dd);
-    }
-    frag dsb[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const u32x4 w = {Mma<T>::pack2(ds[8 * ks], ds[8 * ks + 1]),
-                       Mma<T>::pack2(ds[8 * ks + 2], ds[8 * ks + 3]),
-                       Mma<T>::pack2(ds[8 * ks + 4], ds[8 * ks + 5]),
-                       Mma<T>::pack2(ds[8 * ks + 6], ds[8 * ks + 7])};
-      dsb[ks] = __builtin_bit_cast(frag, w);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const lds_char *a0 = kp + tbase + ks * 16 * L::SK * 16 + db * 64;
-        const u32x2 lo = read_tr16(a0);
-        const u32x2 hi = read_tr16(a0 + 8 * L::SK * 16);
-        const u32x4 raw = {lo[0], lo[1], hi[0], hi[1]};
-        acc[db] = Mma<T>::mma(__builtin_bit_cast(frag, raw), dsb[ks], acc[db]);
-      }
-  }
-  wait_vmcnt<0>();    // no DMA may outlive the ring
-  ring_barrier<0>();  // every wave is done with the ring
-
-  // the odd wave of each group hands its partial sums to the even one
-  constexpr int NR = NDB * 4;
-  lds_char *xch = ring + (uint32_t)qg * NR * kWave * 16;
-  if (h == 1) {
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 x = {acc[db][4 * r4], acc[db][4 * r4 + 1], acc[db][4 * r4 + 2],
-                         acc[db][4 * r4 + 3]};
-        *(__attribute__((address_space(3))) f32x4 *)(xch + ((db * 4 + r4) * kWave + lane) * 16) = x;
-      }
-  }
-  ring_barrier<0>();
-  if (h == 1 || my_q >= Nq) return;
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const f32x4 x = *(const __attribute__((address_space(3))) f32x4 *)(
-          xch + ((db * 4 + r4) * kWave + lane) * 16);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[db][4 * r4 + e] += x[e];
-    }
-  store_row<OT, NDB>(acc, scale, dq + ((size_t)wi.bh * Nq + my_q) * D, g, D);
-}
-
 // Variable-length batches (page "FlashAttention-2实现与优化：高效注意力机制详解"
 // §7, ragged input sequences): S sequences packed along the token axis of
 // [H, T, D] tensors, sequence s at rows cu_q[s] .. cu_q[s+1] of every head
@@ -1584,6 +1394,286 @@ __device__ __forceinline__ int chunk_of(int g, int G) {
 // locating the tile weighs against fewer loads in flight per thread).
 template <int D>
 constexpr int merge_rows() { return D == 128 ? 16 : 64; }
+
+// ---------------------------------------------------------------------------
+// dQ of the backward pass on the forward's pipelined machinery.  The
+// backward recomputes the probabilities from the saved logsumexp (page
+// "解释FlashAttention的显存优化原理" §一.2(2)); for a 128-row query tile,
+// with Q and dO held in registers like the forward's Q:
+//
+//     S^T  = K Q^T               (A: K rows from LDS, B: Q^T)
+//     dP^T = V dO^T              (A: V rows from LDS, B: dO^T)
+//     P = 2^(c s - L log2 e),  dS = P (dP - Dl)       (0 on hidden pairs)
+//     dQ^T += K^T dS^T            (A: K^T by ds_read_b64_tr_b16, B: dS^T rounded to T)
+//
+// so one lane owns one query (L and Dl are per-lane scalars) and dS never
+// leaves registers, as P in the forward.  K and V 64-key tiles stream through
+// a four-stage DMA ring (buffer_load ... lds); K is read both by rows and
+// transposed, so its row stride is the one that measured best for both in
+// the backward's LDS blocks (19 slots at D = 128, 13 at D = 64), V keeps the
+// forward's row stride.  Eight waves, two per SIMD: waves w and w + 4 hold
+// query group w % 4 (32 rows) and take the even and odd 32-key blocks; their
+// dQ^T partial sums are added through LDS at the end.  One workgroup per
+// query tile, longest first under the causal mask.
+template <typename T, int D>
+struct DqLayout {
+  static constexpr int KRB = D * (int)sizeof(T);
+  static constexpr int SK = D == 128 ? 19 : 13;  // K rows (read both ways), 16-byte slots
+  static constexpr int SV = KRB / 16 + 1;        // V rows (read by rows)
+  static constexpr int K_BYTES = kBN * SK * 16;
+  static constexpr int V_BYTES = kBN * SV * 16;
+  static constexpr int K_INS = kBN * SK / kWave;
+  static constexpr int V_INS = kBN * SV / kWave;
+  static constexpr int V_OFF = kStages * K_BYTES;
+  static constexpr int LDS_BYTES = kStages * (K_BYTES + V_BYTES);
+  static constexpr uint32_t K_TILE_GLOBAL = kBN * KRB;
+  static constexpr uint32_t V_TILE_GLOBAL = kBN * KRB;
+  static_assert(LDS_BYTES <= 150 * 1024, "LDS");
+};
+
+// One item of the dQ kernel: key tiles [it.kt0, it.kt1) of the 128-row query
+// tile at it.q0 of slice it.bh.  With it.slot < 0 the item is the whole tile
+// and stores dQ (times scale, in OT); otherwise it writes its fp32 partial
+// sum to workspace slot it.slot (128 rows of D), which fa_merge_dq8 adds up.
+template <typename T, typename OT, int D, bool CAUSAL>
+__device__ __forceinline__ void dq8_run(const T *__restrict__ q, const T *__restrict__ k,
+                                        const T *__restrict__ v, const T *__restrict__ dout,
+                                        const float *__restrict__ lse,
+                                        const float *__restrict__ dl, OT *__restrict__ dq,
+                                        float *__restrict__ ws, int Nq, int Nk, float c,
+                                        float scale, const PipeItem it, bool reuse) {
+  typedef DqLayout<T, D> L;
+  typedef Dma8<T, D, T, L> DM;
+  typedef typename Mma<T>::frag frag;
+  constexpr int QF = D / 16;   // MFMAs of S^T and of dP^T per 32-key block
+  constexpr int NDB = D / 32;  // dQ^T blocks of 32 head-dim rows
+  constexpr int QT = 128;
+  __shared__ __attribute__((aligned(16))) char ring_[DM::LDS_BYTES];
+  lds_char *ring = (lds_char *)ring_;
+  const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
+
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qg = wave & 3, h = wave >> 2;
+  const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int qw = it.q0 + qg * 32;
+  const int my_q = qw + l32;
+  const uint32_t kbase = (uint32_t)(l32 * L::SK * 16 + g * 16);
+  const uint32_t vbase = (uint32_t)(L::V_OFF + l32 * L::SV * 16 + g * 16);
+  uint32_t tbase;
+  {
+    const int G = lane >> 4, s16 = lane & 15;
+    const int row = 4 * (G >> 1) + (s16 >> 2);
+    const int col = 16 * (G & 1) + 4 * (s16 & 3);
+    tbase = (uint32_t)(row * L::SK * 16 + col * 2);
+  }
+  const size_t qoff = (size_t)it.bh * Nq * D;
+  const size_t koff = (size_t)it.bh * Nk * D;
+  const u32x4 q_rs = raw_rsrc(q + qoff, (uint32_t)Nq * D * sizeof(T));
+  const u32x4 do_rs = raw_rsrc(dout + qoff, (uint32_t)Nq * D * sizeof(T));
+  const u32x4 k_rs = raw_rsrc(k + koff, (uint32_t)Nk * D * sizeof(T));
+  const u32x4 v_rs = raw_rsrc(v + koff, (uint32_t)Nk * D * sizeof(T));
+  DM dm;
+  dm.init(ring_addr, wave, lane);
+
+  // rows past Nq: L = +inf gives P = 0
+  const float l2 = my_q < Nq ? lse[(size_t)it.bh * Nq + my_q] * 1.4426950408889634f : INFINITY;
+  const float dd = my_q < Nq ? dl[(size_t)it.bh * Nq + my_q] : 0.f;
+  const int kt0 = it.kt0;
+  const int ntiles = it.kt1 - it.kt0;
+  // last 32-key block (absolute) with a key this wave's queries see
+  const int lastb = CAUSAL ? min(2 * it.kt1 - 1, (qw + 31) / 32) : 2 * it.kt1 - 1;
+
+  u32x4 qraw[QF], draw[QF];
+#pragma unroll
+  for (int f = 0; f < QF; ++f) {
+    const uint32_t off = ((uint32_t)my_q * D + 16 * f + 8 * g) * sizeof(T);
+    qraw[f] = load16_async(q_rs, off);
+    draw[f] = load16_async(do_rs, off);
+  }
+  dm.issue(k_rs, v_rs, kt0, 0, kt0, 0);
+  if (ntiles > 1) dm.issue(k_rs, v_rs, kt0 + 1, 1, kt0 + 1, 1);
+  frag qf[QF], dof[QF];
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+
+  for (int r = 0; r < ntiles; ++r) {
+    if ((r & 1) == 0) {
+      // tiles r and r+1 have landed, and every wave is done with the stages
+      // of tiles r-2 and r-1, which tiles r+2 and r+3 now take
+      ring_barrier<0>();
+      if (r + 2 < ntiles) dm.issue(k_rs, v_rs, kt0 + r + 2, (r + 2) & 3, kt0 + r + 2, (r + 2) & 3);
+      if (r + 3 < ntiles) dm.issue(k_rs, v_rs, kt0 + r + 3, (r + 3) & 3, kt0 + r + 3, (r + 3) & 3);
+      if (r == 0) {
+#pragma unroll
+        for (int f = 0; f < QF; ++f) {
+          asm volatile("" : "+v"(qraw[f]), "+v"(draw[f]));  // read after the wait above
+          qf[f] = __builtin_bit_cast(frag, qraw[f]);
+          dof[f] = __builtin_bit_cast(frag, draw[f]);
+        }
+      }
+    }
+    const int b = 2 * (kt0 + r) + h;
+    if (b > lastb) continue;  // wave-uniform; later blocks are past it too
+    const int st = r & 3;
+    const lds_char *kp = ring + st * L::K_BYTES + h * 32 * L::SK * 16;
+    const lds_char *vp = ring + st * L::V_BYTES + h * 32 * L::SV * 16;
+    f32x16 sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int f = 0; f < QF; ++f) {
+      const frag kf = *(const __attribute__((address_space(3))) frag *)(kp + kbase + f * 32);
+      const frag vf = *(const __attribute__((address_space(3))) frag *)(vp + vbase + f * 32);
+      sc = Mma<T>::mma(kf, qf[f], sc);
+      dp = Mma<T>::mma(vf, dof[f], dp);
+    }
+    const int k0 = 32 * b;
+    // wave-uniform, and taken as a branch (the compiler had turned the
+    // per-score test into selects on every block: +130 VALU per block)
+    const int need_mask =
+        __builtin_amdgcn_readfirstlane((k0 + 32 > Nk) || (CAUSAL && k0 + 31 > qw) ? 1 : 0);
+    float ds[16];
+    if (need_mask) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = k0 + acc_row(e, g);
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], c, -l2));
+        if (key >= Nk || (CAUSAL && key > my_q)) p = 0.f;
+        ds[e] = p * (dp[e] - dd);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        ds[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], c, -l2)) * (dp[e] - dd);
+    }
+    frag dsb[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4 w = {Mma<T>::pack2(ds[8 * ks], ds[8 * ks + 1]),
+                       Mma<T>::pack2(ds[8 * ks + 2], ds[8 * ks + 3]),
+                       Mma<T>::pack2(ds[8 * ks + 4], ds[8 * ks + 5]),
+                       Mma<T>::pack2(ds[8 * ks + 6], ds[8 * ks + 7])};
+      dsb[ks] = __builtin_bit_cast(frag, w);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const lds_char *a0 = kp + tbase + ks * 16 * L::SK * 16 + db * 64;
+        const u32x2 lo = read_tr16(a0);
+        const u32x2 hi = read_tr16(a0 + 8 * L::SK * 16);
+        const u32x4 raw = {lo[0], lo[1], hi[0], hi[1]};
+        acc[db] = Mma<T>::mma(__builtin_bit_cast(frag, raw), dsb[ks], acc[db]);
+      }
+  }
+  wait_vmcnt<0>();    // no DMA may outlive the ring
+  ring_barrier<0>();  // every wave is done with the ring
+
+  // the odd wave of each group hands its partial sums to the even one
+  constexpr int NR = NDB * 4;
+  lds_char *xch = ring + (uint32_t)qg * NR * kWave * 16;
+  if (h == 1) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 x = {acc[db][4 * r4], acc[db][4 * r4 + 1], acc[db][4 * r4 + 2],
+                         acc[db][4 * r4 + 3]};
+        *(__attribute__((address_space(3))) f32x4 *)(xch + ((db * 4 + r4) * kWave + lane) * 16) = x;
+      }
+  }
+  ring_barrier<0>();
+  if (h == 0) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 x = *(const __attribute__((address_space(3))) f32x4 *)(
+            xch + ((db * 4 + r4) * kWave + lane) * 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[db][4 * r4 + e] += x[e];
+      }
+    if (it.slot < 0) {
+      if (my_q < Nq) store_row<OT, NDB>(acc, scale, dq + ((size_t)it.bh * Nq + my_q) * D, g, D);
+    } else {
+      store_row<float, NDB>(acc, 1.f, ws + ((size_t)it.slot * QT + (my_q - it.q0)) * D, g, D);
+    }
+  }
+  // reuse: the ring (and the exchange area in it) is free for the
+  // workgroup's next item once every read of the exchange area is done (the
+  // stores need not be)
+  if (reuse) ring_barrier<63, 0>();
+}
+
+// One workgroup per 128-row query tile, longest first under the causal mask.
+// ws is never written here (every item is a whole tile); it is passed as an
+// argument because this compiler crashes on the constant null pointer that
+// the never-taken partial store would otherwise see.
+template <typename T, typename OT, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads8) void fa_bwd_dq8(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    const T *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dl,
+    OT *__restrict__ dq, float *__restrict__ ws, int Nq, int Nk, int BH, int nqt, float c,
+    float scale) {
+  const WorkItem wi = work_item(BH, nqt, CAUSAL, 128);
+  const int kend = CAUSAL ? min(Nk, wi.q0 + 128) : Nk;
+  const PipeItem it = {wi.bh, wi.q0, 0, (kend + kBN - 1) / kBN, -1};
+  dq8_run<T, OT, D, CAUSAL>(q, k, v, dout, lse, dl, dq, ws, Nq, Nk, c, scale, it, false);
+}
+
+// The stream-K schedule of the forward (128-row tiles): each workgroup walks
+// its chunk of (query tile, 64-key tile) units; cut tiles leave partial sums.
+template <typename T, typename OT, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads8) void fa_bwd_dq8_stream(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    const T *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dl,
+    OT *__restrict__ dq, float *__restrict__ ws, int Nq, int Nk, float c, float scale,
+    StreamPlan sp, ChunkStarts cs) {
+  ChunkWalk cw;
+  const int ch = chunk_of(blockIdx.x, sp.G);
+  cw.init_at(sp, ch, cs.w[2 * ch], cs.w[2 * ch + 1]);
+  PipeItem it;
+  int t;
+  while (cw.next(sp, CAUSAL, it, t)) {
+    it.q0 = t * 128;
+    dq8_run<T, OT, D, CAUSAL>(q, k, v, dout, lse, dl, dq, ws, Nq, Nk, c, scale, it, true);
+  }
+}
+
+// Sums the partial dQ of each cut tile's pieces (in piece order) and stores
+// scale times the sum: merge_rows<D>() rows of a tile per workgroup.
+template <typename OT, int D>
+__global__ __launch_bounds__(kThreads) void fa_merge_dq8(const float *__restrict__ ws,
+                                                         OT *__restrict__ dq, int Nq,
+                                                         float scale, CutList cuts) {
+  constexpr int C4 = D / 4;
+  constexpr int RPP = kThreads / C4;
+  constexpr int ROWS = merge_rows<D>();
+  constexpr int SPLIT = 128 / ROWS;
+  constexpr int NR = ROWS / RPP;
+  static_assert(NR >= 1 && ROWS % RPP == 0, "merge tiling");
+  const uint32_t w0 = cuts.w[2 * (blockIdx.x / SPLIT)];
+  const uint32_t w1 = cuts.w[2 * (blockIdx.x / SPLIT) + 1];
+  const int bh = (int)(w0 & 0xffffu), t = (int)(w0 >> 16);
+  const int np = cut_pieces(w1);
+  const int c4 = threadIdx.x % C4;
+  const int r0 = (blockIdx.x % SPLIT) * ROWS + threadIdx.x / C4;
+  f32x4 acc[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kk = 0; kk < np; ++kk) {
+    const size_t sl = (size_t)cut_slot(w1, kk);
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+      acc[i] += *reinterpret_cast<const f32x4 *>(ws + (sl * 128 + r0 + i * RPP) * D + 4 * c4);
+  }
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int row = t * 128 + r0 + i * RPP;
+    if (row < Nq) store4<OT>(dq + ((size_t)bh * Nq + row) * D + 4 * c4, acc[i] * scale);
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Stream-K schedule for variable-length batches (the dense schedule's
@@ -2771,55 +2861,102 @@ __attribute__((visibility("hidden"))) int fa_internal_hip_fail(hipError_t e) {
 
 // dQ of fa_bwd on the pipelined kernel (fa_bwd_dq8), for dense problems at
 // D = 64 or 128 with 16-bit inputs; called by the backward's host code
-// after its row-term kernel.  Returns false for a case it does not take.
+// after its row-term kernel.  With fewer than two 128-row query tiles per
+// compute unit, and a workspace that holds the plan's partials, it takes the
+// stream-K schedule of 128-row tiles (fa_bwd_dq8_stream, then fa_merge_dq8
+// for the cut tiles); otherwise one workgroup per tile.
 namespace {
-template <typename T, typename OT, int D>
+constexpr int kDqLead = 3;  // fixed cost of a piece, in 64-key tiles
+
+bool dq8_plan(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, bool causal, int cus,
+              StreamPlan &sp) {
+  if (D != 64 && D != 128) return false;
+  // from two tiles per compute unit on, the grid's longest-first rounds
+  // balance as well (measured: B8 N8192 D64 causal 481 us on the grid, 497
+  // on the stream schedule; B8 N4096 D128 causal 222 against 198)
+  if (BH * ((Nq + 127) / 128) >= 2LL * cus) return false;
+  return plan_rows(BH, Nq, Nk, 128, kDqLead, 0, causal, cus, sp);
+}
+
+template <typename T, typename OT, int D, bool CAUSAL>
 hipError_t launch_dq8(const void *q, const void *k, const void *v, const void *dout,
                       const float *lse, const float *dl, void *dq, int Nq, int Nk, int BH,
-                      bool causal, float c, float scale, hipStream_t s) {
+                      float c, float scale, const StreamPlan *sp, float *ws, hipStream_t s) {
+  if (sp) {
+    ChunkStarts cs;
+    CutList cuts;
+    make_tables(*sp, CAUSAL, cs, cuts);
+    hipLaunchKernelGGL((fa_bwd_dq8_stream<T, OT, D, CAUSAL>), dim3((unsigned)sp->G),
+                       dim3(kThreads8), 0, s, (const T *)q, (const T *)k, (const T *)v,
+                       (const T *)dout, lse, dl, (OT *)dq, ws, Nq, Nk, c, scale, *sp, cs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || cuts.n == 0) return e;
+    hipLaunchKernelGGL((fa_merge_dq8<OT, D>), dim3((unsigned)(cuts.n * (128 / merge_rows<D>()))),
+                       dim3(kThreads), 0, s, (const float *)ws, (OT *)dq, Nq, scale, cuts);
+    return hipGetLastError();
+  }
   const int nqt = (Nq + 127) / 128;
-  const dim3 grid((unsigned)(BH * nqt)), block(kThreads8);
-  if (causal)
-    hipLaunchKernelGGL((fa_bwd_dq8<T, OT, D, true>), grid, block, 0, s, (const T *)q,
-                       (const T *)k, (const T *)v, (const T *)dout, lse, dl, (OT *)dq, Nq, Nk,
-                       BH, nqt, c, scale);
-  else
-    hipLaunchKernelGGL((fa_bwd_dq8<T, OT, D, false>), grid, block, 0, s, (const T *)q,
-                       (const T *)k, (const T *)v, (const T *)dout, lse, dl, (OT *)dq, Nq, Nk,
-                       BH, nqt, c, scale);
+  hipLaunchKernelGGL((fa_bwd_dq8<T, OT, D, CAUSAL>), dim3((unsigned)(BH * nqt)),
+                     dim3(kThreads8), 0, s, (const T *)q, (const T *)k, (const T *)v,
+                     (const T *)dout, lse, dl, (OT *)dq, ws, Nq, Nk, BH, nqt, c, scale);
   return hipGetLastError();
 }
 template <typename T, typename OT>
-hipError_t dq8_d(int D, const void *q, const void *k, const void *v, const void *dout,
-                 const float *lse, const float *dl, void *dq, int Nq, int Nk, int BH,
-                 bool causal, float c, float scale, hipStream_t s) {
-  return D == 64 ? launch_dq8<T, OT, 64>(q, k, v, dout, lse, dl, dq, Nq, Nk, BH, causal, c,
-                                         scale, s)
-                 : launch_dq8<T, OT, 128>(q, k, v, dout, lse, dl, dq, Nq, Nk, BH, causal, c,
-                                          scale, s);
+hipError_t dq8_d(int D, bool causal, const void *q, const void *k, const void *v,
+                 const void *dout, const float *lse, const float *dl, void *dq, int Nq, int Nk,
+                 int BH, float c, float scale, const StreamPlan *sp, float *ws, hipStream_t s) {
+  if (D == 64)
+    return causal ? launch_dq8<T, OT, 64, true>(q, k, v, dout, lse, dl, dq, Nq, Nk, BH, c,
+                                                scale, sp, ws, s)
+                  : launch_dq8<T, OT, 64, false>(q, k, v, dout, lse, dl, dq, Nq, Nk, BH, c,
+                                                 scale, sp, ws, s);
+  return causal ? launch_dq8<T, OT, 128, true>(q, k, v, dout, lse, dl, dq, Nq, Nk, BH, c, scale,
+                                               sp, ws, s)
+                : launch_dq8<T, OT, 128, false>(q, k, v, dout, lse, dl, dq, Nq, Nk, BH, c,
+                                                scale, sp, ws, s);
 }
 }  // namespace
+
+// Bytes of dQ partials the stream schedule may need for this problem on a
+// device of up to 256 compute units (0 when it never runs), independent of
+// the device, so that the backward's workspace query needs no GPU.
+__attribute__((visibility("hidden"))) size_t fa_internal_dq8_bytes(int64_t BH, int64_t Nq,
+                                                                   int64_t Nk, int64_t D,
+                                                                   bool causal) {
+  StreamPlan sp;
+  if (!dq8_plan(BH, Nq, Nk, D, causal, fa_sched::kMaxChunks, sp)) return 0;
+  return (size_t)2 * sp.G * 128 * (size_t)D * 4;
+}
 
 __attribute__((visibility("hidden"))) bool fa_internal_bwd_dq8(
     const void *q, const void *k, const void *v, const void *dout, const float *lse,
     const float *dl, void *dq, int Nq, int Nk, int BH, int D, int dtype, bool causal, float c,
-    float scale, void *stream, hipError_t *err) {
+    float scale, void *ws, size_t ws_bytes, void *stream, hipError_t *err) {
   if (D != 64 && D != 128) return false;
   hipStream_t s = (hipStream_t)stream;
+  int cus = 0;
+  StreamPlan sp;
+  const StreamPlan *use = nullptr;
+  if (ws && device_cus(&cus) == FA_OK && dq8_plan(BH, Nq, Nk, D, causal, cus, sp) &&
+      ws_bytes >= (size_t)2 * sp.G * 128 * (size_t)D * 4)
+    use = &sp;
+  float *w = (float *)ws;
   switch (dtype) {
     case FA_BF16:
-      *err = dq8_d<__bf16, __bf16>(D, q, k, v, dout, lse, dl, dq, Nq, Nk, BH, causal, c, scale, s);
+      *err = dq8_d<__bf16, __bf16>(D, causal, q, k, v, dout, lse, dl, dq, Nq, Nk, BH, c, scale,
+                                   use, w, s);
       return true;
     case FA_BF16_OF32:
-      *err = dq8_d<__bf16, float>(D, q, k, v, dout, lse, dl, dq, Nq, Nk, BH, causal, c, scale, s);
+      *err = dq8_d<__bf16, float>(D, causal, q, k, v, dout, lse, dl, dq, Nq, Nk, BH, c, scale,
+                                  use, w, s);
       return true;
     case FA_F16:
-      *err = dq8_d<_Float16, _Float16>(D, q, k, v, dout, lse, dl, dq, Nq, Nk, BH, causal, c,
-                                       scale, s);
+      *err = dq8_d<_Float16, _Float16>(D, causal, q, k, v, dout, lse, dl, dq, Nq, Nk, BH, c,
+                                       scale, use, w, s);
       return true;
     case FA_F16_OF32:
-      *err = dq8_d<_Float16, float>(D, q, k, v, dout, lse, dl, dq, Nq, Nk, BH, causal, c, scale,
-                                    s);
+      *err = dq8_d<_Float16, float>(D, causal, q, k, v, dout, lse, dl, dq, Nq, Nk, BH, c,
+                                    scale, use, w, s);
       return true;
     default: return false;
   }

@@ -268,6 +268,28 @@ FA_HD inline int cut_pieces(uint32_t w1) { return (int)((w1 >> 16) & 0x7fffu); }
 // end, and a chunk would hold many pieces, each paying its own prologue: the
 // call then takes that grid.  Returns false for the paths that take no
 // workspace.
+// A plan over query tiles of qt rows (a multiple of kKeys) with `lead` and
+// `tail` units of fixed cost per tile, dealt to at most min(cus,
+// kMaxChunks) chunks; the tables limit BH and the query tiles to 16 bits.
+inline bool plan_rows(int64_t BH, int64_t Nq, int64_t Nk, int64_t qt, int lead, int tail,
+                      bool causal, int cus, StreamPlan &sp) {
+  if (cus < 1 || BH > 0xffff || (Nq + qt - 1) / qt > 0xffff) return false;
+  const int nkt = (int)((Nk + kKeys - 1) / kKeys);
+  const int nqt = (int)((Nq + qt - 1) / qt);
+  sp.tu = (int)(qt / kKeys);
+  sp.nqt = nqt;
+  sp.nkt = nkt;
+  sp.lead = lead;
+  sp.tail = tail;
+  sp.per_head = prefix_nat(nqt, nkt, sp.tu, causal) + (long long)(sp.lead + sp.tail) * nqt;
+  sp.T = BH * sp.per_head;
+  const int gmax = cus < kMaxChunks ? cus : kMaxChunks;
+  sp.G = (int)(sp.T < gmax ? sp.T : gmax);
+  sp.cq = sp.T / sp.G;
+  sp.cr = (int)(sp.T % sp.G);
+  return true;
+}
+
 inline bool make_plan(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, int dtype, bool causal,
                int cus, StreamPlan &sp, size_t &ws_bytes) {
   ws_bytes = 0;
@@ -278,19 +300,8 @@ inline bool make_plan(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, int dtype, 
   if (BH > 0xffff || (Nq + pair_rows - 1) / pair_rows > 0xffff) return false;
   const bool pair = stream_pair(BH, Nq, Nk, D, causal, cus);
   const int64_t qt = pair ? pair_rows : kGridRows;
-  const int nkt = (int)((Nk + kKeys - 1) / kKeys);
-  const int nqt = (int)((Nq + qt - 1) / qt);
-  sp.tu = (int)(qt / kKeys);
-  sp.nqt = nqt;
-  sp.nkt = nkt;
-  sp.lead = stream_lead((int)D, pair);
-  sp.tail = causal ? stream_tail((int)D, pair) : 0;
-  sp.per_head = prefix_nat(nqt, nkt, sp.tu, causal) + (long long)(sp.lead + sp.tail) * nqt;
-  sp.T = BH * sp.per_head;
-  const int gmax = cus < kMaxChunks ? cus : kMaxChunks;
-  sp.G = (int)(sp.T < gmax ? sp.T : gmax);
-  sp.cq = sp.T / sp.G;
-  sp.cr = (int)(sp.T % sp.G);
+  plan_rows(BH, Nq, Nk, qt, stream_lead((int)D, pair),
+            causal ? stream_tail((int)D, pair) : 0, causal, cus, sp);
   ws_bytes = (size_t)2 * sp.G * qt * (size_t)(D + 4) * 4;
   return true;
 }
