@@ -214,6 +214,17 @@ def test_bwd_dq_stream_and_grid(shape, causal):
     assert float(d.max()) <= 1e-5 * max(1.0, float(np.abs(res[1][0]).max())), float(d.max())
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_many_key_tiles(D, causal):
+    """B2 H128, Nq = 200 against Nk = 250: 512 tiles of 128 keys, so dK and
+    dV run one workgroup per 128-key tile of the pipelined kernel (Q, dO and
+    their row terms streamed through the DMA ring), ragged query and key
+    tails, every row against the oracle."""
+    q, k, v, g = inputs(2, 128, 200, 250, D, seed=970 + D)
+    compare(q, k, v, g, causal, 1.0 / math.sqrt(D), what="512 key tiles")
+
+
 def test_bwd_rejects_fp32_and_odd_head_dims():
     q = torch.zeros(1, 1, 64, 48, device=DEV, dtype=torch.bfloat16)
     lse = torch.zeros(1, 1, 64, device=DEV)

@@ -65,6 +65,11 @@ bool fa_internal_bwd_dq8(const void *q, const void *k, const void *v, const void
                          int D, int dtype, bool causal, float c, float scale, void *ws,
                          size_t ws_bytes, void *stream, hipError_t *err);
 size_t fa_internal_dq8_bytes(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, bool causal);
+// dK and dV on the same machinery (fa_fwd.hip), same cases; false otherwise.
+bool fa_internal_bwd_dkdv8(const void *q, const void *k, const void *v, const void *dout,
+                           const float *lse, const float *dl, void *dk, void *dv, int Nq, int Nk,
+                           int BH, int D, int dtype, bool causal, float c, float scale,
+                           void *stream, hipError_t *err);
 
 #include "tiles.h"
 
@@ -549,7 +554,19 @@ hipError_t launch_bwd(const BwdArgs &a) {
   if (vl && a.Nk > 0 && nkt < 1) nkt = 1;
   const int nqt = ((vl ? a.maxq : a.Nq) + kTile - 1) / kTile;
   const int slices = vl ? a.BH * a.S : a.BH;
-  if (nkt > 0) {
+  bool done_kv = false;
+  if constexpr (!MASKED && (D == 64 || D == 128)) {
+    if (!vl) {
+      constexpr bool of32 = std::is_same<OT, float>::value;
+      constexpr int code = std::is_same<T, __bf16>::value ? (of32 ? FA_BF16_OF32 : FA_BF16)
+                                                          : (of32 ? FA_F16_OF32 : FA_F16);
+      done_kv = fa_internal_bwd_dkdv8(a.q, a.k, a.v, a.dout, a.lse, (const float *)a.dl, a.dk,
+                                      a.dv, a.Nq, a.Nk, a.BH, D, code, CAUSAL, c, a.scale,
+                                      a.stream, &e);
+      if (done_kv && e != hipSuccess) return e;
+    }
+  }
+  if (nkt > 0 && !done_kv) {
     hipLaunchKernelGGL((fa_bwd_dkdv<T, OT, D, CAUSAL, MASKED>),
                        dim3((unsigned)(slices * nkt)), dim3(kThreads), 0, a.stream,
                        (const T *)a.q, (const T *)a.k, (const T *)a.v, (const T *)a.dout,

@@ -1676,6 +1676,271 @@ __global__ __launch_bounds__(kThreads) void fa_merge_dq8(const float *__restrict
 }
 
 // ---------------------------------------------------------------------------
+// dK and dV of the backward pass on the same machinery, the roles of keys and
+// queries swapped: a workgroup holds 128 keys (K and V fragments in registers
+// as the B operands of S = Q K^T and dP = dO V^T, one key per lane) and
+// streams 64-row tiles of Q and dO through the DMA ring, with each tile's L
+// and Dl; per 32-query block
+//
+//     P = 2^(c s - L log2 e),  dS = P (dP - Dl)          (0 on hidden pairs)
+//     dV^T += dO^T P,   dK^T += Q^T dS                     (A: dO^T, Q^T by
+//                                                          ds_read_b64_tr_b16)
+//
+// with P and dS from registers.  Waves w and w + 4 hold key group w % 4
+// (32 keys) and take the two 32-row halves of each query tile; their sums
+// are added through LDS at the end.  Q and dO are read both by rows and
+// transposed: both take the 19-slot stride at D = 128 (13 at D = 64).
+template <typename T, int D>
+struct DkvLayout {
+  static constexpr int KRB = D * (int)sizeof(T);
+  static constexpr int SK = D == 128 ? 19 : 13;  // Q rows
+  static constexpr int SV = SK;                  // dO rows
+  static constexpr int K_BYTES = kBN * SK * 16;
+  static constexpr int V_BYTES = kBN * SV * 16;
+  static constexpr int K_INS = kBN * SK / kWave;
+  static constexpr int V_INS = kBN * SV / kWave;
+  static constexpr int V_OFF = kStages * K_BYTES;
+  static constexpr int S_OFF = kStages * (K_BYTES + V_BYTES);  // L, Dl of each stage
+  static constexpr int S_BYTES = 2 * kBN * 4;
+  static constexpr int LDS_BYTES = S_OFF + kStages * S_BYTES;
+  static constexpr uint32_t K_TILE_GLOBAL = kBN * KRB;
+  static constexpr uint32_t V_TILE_GLOBAL = kBN * KRB;
+  static_assert(LDS_BYTES + kWave * 16 <= 160 * 1024, "LDS");
+};
+
+// One item: the 128 keys at it.q0 (the tile's first key) of slice it.bh,
+// query tiles (64 rows) [it.kt0, it.kt1).  it.slot < 0: the whole tile,
+// stores dK (times scale) and dV in OT; else fp32 partial sums of dK^T and
+// dV^T to workspace slot it.slot (128 keys of D each, dK then dV).
+template <typename T, typename OT, int D, bool CAUSAL>
+__device__ __forceinline__ void dkv8_run(const T *__restrict__ q, const T *__restrict__ k,
+                                         const T *__restrict__ v, const T *__restrict__ dout,
+                                         const float *__restrict__ lse,
+                                         const float *__restrict__ dl, OT *__restrict__ dk,
+                                         OT *__restrict__ dv, float *__restrict__ ws, int Nq,
+                                         int Nk, float c, float scale, const PipeItem it,
+                                         bool reuse) {
+  typedef DkvLayout<T, D> L;
+  typedef Dma8<T, D, T, L> DM;
+  typedef typename Mma<T>::frag frag;
+  constexpr int QF = D / 16;   // MFMAs of S and of dP per 32-query block
+  constexpr int NDB = D / 32;  // dK^T, dV^T blocks of 32 head-dim rows
+  constexpr int KT = 128;      // keys per workgroup
+  __shared__ __attribute__((aligned(16))) char ring_[DM::LDS_BYTES];
+  lds_char *ring = (lds_char *)ring_;
+  const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
+
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = wave & 3, h = wave >> 2;
+  const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int kw = it.q0 + kg * 32;  // this wave's first key
+  const int my_k = kw + l32;
+  const uint32_t rbase = (uint32_t)(l32 * L::SK * 16 + g * 16);  // row reads (Q, dO)
+  uint32_t tbase;                                                 // transposed reads
+  {
+    const int G = lane >> 4, s16 = lane & 15;
+    const int row = 4 * (G >> 1) + (s16 >> 2);
+    const int col = 16 * (G & 1) + 4 * (s16 & 3);
+    tbase = (uint32_t)(row * L::SK * 16 + col * 2);
+  }
+  const size_t qoff = (size_t)it.bh * Nq * D;
+  const size_t koff = (size_t)it.bh * Nk * D;
+  const u32x4 q_rs = raw_rsrc(q + qoff, (uint32_t)Nq * D * sizeof(T));
+  const u32x4 do_rs = raw_rsrc(dout + qoff, (uint32_t)Nq * D * sizeof(T));
+  const u32x4 k_rs = raw_rsrc(k + koff, (uint32_t)Nk * D * sizeof(T));
+  const u32x4 v_rs = raw_rsrc(v + koff, (uint32_t)Nk * D * sizeof(T));
+  const u32x4 l_rs = raw_rsrc(lse + (size_t)it.bh * Nq, (uint32_t)Nq * 4u);
+  const u32x4 d_rs = raw_rsrc(dl + (size_t)it.bh * Nq, (uint32_t)Nq * 4u);
+  DM dm;
+  dm.init(ring_addr, wave, lane);
+  // the L and Dl of query tile j into stage st: 16 lanes of wave 0 each
+  auto issue_stats = [&](int j, int st) {
+    if (wave == 0 && lane < 16) {
+      const uint32_t off = (uint32_t)(j * kBN + 4 * lane) * 4u;
+      const uint32_t lb = ring_addr + L::S_OFF + st * L::S_BYTES;
+      dma16(l_rs, lb, off);
+      dma16(d_rs, lb + kBN * 4, off);
+    }
+  };
+  auto issue = [&](int j, int st) {
+    dm.issue(q_rs, do_rs, j, st, j, st);
+    issue_stats(j, st);
+  };
+
+  const int qt0 = it.kt0;
+  const int ntiles = it.kt1 - it.kt0;
+
+  u32x4 kraw[QF], vraw[QF];
+#pragma unroll
+  for (int f = 0; f < QF; ++f) {
+    const uint32_t off = ((uint32_t)my_k * D + 16 * f + 8 * g) * sizeof(T);
+    kraw[f] = load16_async(k_rs, off);
+    vraw[f] = load16_async(v_rs, off);
+  }
+  issue(qt0, 0);
+  if (ntiles > 1) issue(qt0 + 1, 1);
+  frag kf[QF], vf[QF];
+  f32x16 dka[NDB], dva[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dka[db] = f32x16{};
+    dva[db] = f32x16{};
+  }
+
+  for (int r = 0; r < ntiles; ++r) {
+    if ((r & 1) == 0) {
+      ring_barrier<0>();
+      if (r + 2 < ntiles) issue(qt0 + r + 2, (r + 2) & 3);
+      if (r + 3 < ntiles) issue(qt0 + r + 3, (r + 3) & 3);
+      if (r == 0) {
+#pragma unroll
+        for (int f = 0; f < QF; ++f) {
+          asm volatile("" : "+v"(kraw[f]), "+v"(vraw[f]));  // read after the wait above
+          kf[f] = __builtin_bit_cast(frag, kraw[f]);
+          vf[f] = __builtin_bit_cast(frag, vraw[f]);
+        }
+      }
+    }
+    const int i0 = (qt0 + r) * kBN + 32 * h;  // this wave's first query of the tile
+    // wave-uniform: no query of the block sees a key of this wave
+    if (CAUSAL && i0 + 31 < kw) continue;
+    if (i0 >= Nq) continue;
+    const int st = r & 3;
+    const lds_char *qp = ring + st * L::K_BYTES + h * 32 * L::SK * 16;
+    const lds_char *dp_ = ring + L::V_OFF + st * L::V_BYTES + h * 32 * L::SV * 16;
+    const lds_char *sp = ring + L::S_OFF + st * L::S_BYTES + h * 32 * 4;
+    f32x16 sc = f32x16{}, dpv = f32x16{};
+#pragma unroll
+    for (int f = 0; f < QF; ++f) {
+      const frag qa = *(const __attribute__((address_space(3))) frag *)(qp + rbase + f * 32);
+      const frag da = *(const __attribute__((address_space(3))) frag *)(dp_ + rbase + f * 32);
+      sc = Mma<T>::mma(qa, kf[f], sc);
+      dpv = Mma<T>::mma(da, vf[f], dpv);
+    }
+    // rows of register 4 r4 + e: query i0 + 8 r4 + 4 g + e; the two 16-row
+    // halves (ks) are finished one after the other to keep registers low
+    const int need_mask = __builtin_amdgcn_readfirstlane(
+        (i0 + 32 > Nq) || (CAUSAL && kw + 31 > i0) ? 1 : 0);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      float p[8], ds[8];
+#pragma unroll
+      for (int hr = 0; hr < 2; ++hr) {
+        const int r4 = 2 * ks + hr;
+        const int ib = 8 * r4 + 4 * g;
+        const f32x4 lv = *(const __attribute__((address_space(3))) f32x4 *)(sp + ib * 4);
+        const f32x4 dv4 =
+            *(const __attribute__((address_space(3))) f32x4 *)(sp + kBN * 4 + ib * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int x = 4 * r4 + e;
+          float pr =
+              __builtin_amdgcn_exp2f(__builtin_fmaf(sc[x], c, -lv[e] * 1.4426950408889634f));
+          if (need_mask) {
+            const int qi = i0 + ib + e;
+            if (qi >= Nq || (CAUSAL && my_k > qi)) pr = 0.f;
+          }
+          p[4 * hr + e] = pr;
+          ds[4 * hr + e] = pr * (dpv[x] - dv4[e]);
+        }
+      }
+      const u32x4 pw = {Mma<T>::pack2(p[0], p[1]), Mma<T>::pack2(p[2], p[3]),
+                        Mma<T>::pack2(p[4], p[5]), Mma<T>::pack2(p[6], p[7])};
+      const u32x4 sw = {Mma<T>::pack2(ds[0], ds[1]), Mma<T>::pack2(ds[2], ds[3]),
+                        Mma<T>::pack2(ds[4], ds[5]), Mma<T>::pack2(ds[6], ds[7])};
+      const frag pb = __builtin_bit_cast(frag, pw), sb = __builtin_bit_cast(frag, sw);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const lds_char *a0 = dp_ + tbase + ks * 16 * L::SV * 16 + db * 64;
+        const u32x2 lo = read_tr16(a0), hi = read_tr16(a0 + 8 * L::SV * 16);
+        const u32x4 ra = {lo[0], lo[1], hi[0], hi[1]};
+        dva[db] = Mma<T>::mma(__builtin_bit_cast(frag, ra), pb, dva[db]);
+        const lds_char *b0 = qp + tbase + ks * 16 * L::SK * 16 + db * 64;
+        const u32x2 lo2 = read_tr16(b0), hi2 = read_tr16(b0 + 8 * L::SK * 16);
+        const u32x4 rb = {lo2[0], lo2[1], hi2[0], hi2[1]};
+        dka[db] = Mma<T>::mma(__builtin_bit_cast(frag, rb), sb, dka[db]);
+      }
+    }
+  }
+  wait_vmcnt<0>();    // no DMA may outlive the ring
+  ring_barrier<0>();  // every wave is done with the ring
+
+  // the odd wave of each group hands its sums to the even one
+  constexpr int NR = NDB * 4;
+  lds_char *xch = ring + (uint32_t)kg * 2 * NR * kWave * 16;
+  if (h == 1) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 x = {dka[db][4 * r4], dka[db][4 * r4 + 1], dka[db][4 * r4 + 2],
+                         dka[db][4 * r4 + 3]};
+        const f32x4 y = {dva[db][4 * r4], dva[db][4 * r4 + 1], dva[db][4 * r4 + 2],
+                         dva[db][4 * r4 + 3]};
+        *(__attribute__((address_space(3))) f32x4 *)(xch + ((db * 4 + r4) * kWave + lane) * 16) = x;
+        *(__attribute__((address_space(3))) f32x4 *)(xch + ((NR + db * 4 + r4) * kWave + lane) * 16) = y;
+      }
+  }
+  ring_barrier<0>();
+  if (h == 0) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 x = *(const __attribute__((address_space(3))) f32x4 *)(
+            xch + ((db * 4 + r4) * kWave + lane) * 16);
+        const f32x4 y = *(const __attribute__((address_space(3))) f32x4 *)(
+            xch + ((NR + db * 4 + r4) * kWave + lane) * 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dka[db][4 * r4 + e] += x[e];
+          dva[db][4 * r4 + e] += y[e];
+        }
+      }
+    if (it.slot < 0) {
+      if (my_k < Nk) {
+        store_row<OT, NDB>(dka, scale, dk + ((size_t)it.bh * Nk + my_k) * D, g, D);
+        store_row<OT, NDB>(dva, 1.f, dv + ((size_t)it.bh * Nk + my_k) * D, g, D);
+      }
+    } else {
+      float *w = ws + (size_t)it.slot * 2 * KT * D;
+      store_row<float, NDB>(dka, 1.f, w + (size_t)(my_k - it.q0) * D, g, D);
+      store_row<float, NDB>(dva, 1.f, w + (size_t)(KT + my_k - it.q0) * D, g, D);
+    }
+  }
+  if (reuse) ring_barrier<63, 0>();
+}
+
+// One workgroup per 128-key tile, lowest keys (the most queries) first
+// under the causal mask.
+template <typename T, typename OT, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads8) void fa_bwd_dkdv8(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    const T *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dl,
+    OT *__restrict__ dk, OT *__restrict__ dv, float *__restrict__ ws, int Nq, int Nk, int BH,
+    int nkt, float c, float scale) {
+  const int id = blockIdx.x;
+  const int bh = id % BH, t = id / BH;  // causal: t ascending = longest first
+  const int k0 = t * 128;
+  const int nq = (Nq + kBN - 1) / kBN;
+  const int qa = CAUSAL ? min(k0 / kBN, nq) : 0;  // first query tile with a visible key
+  const PipeItem it = {bh, k0, qa, nq, -1};
+  if (qa >= nq) {  // no query sees these keys: zero gradients
+    for (int i = threadIdx.x; i < 128 * D; i += kThreads8) {
+      const int key = k0 + i / D;
+      if (key < Nk) {
+        dk[((size_t)bh * Nk + key) * D + i % D] = (OT)0.f;
+        dv[((size_t)bh * Nk + key) * D + i % D] = (OT)0.f;
+      }
+    }
+    return;
+  }
+  dkv8_run<T, OT, D, CAUSAL>(q, k, v, dout, lse, dl, dk, dv, ws, Nq, Nk, c, scale, it, false);
+}
+
+// ---------------------------------------------------------------------------
 // Stream-K schedule for variable-length batches (the dense schedule's
 // balance, for packed sequences of any lengths).  The units are those of the
 // dense schedule, laid out (head, sequence) pair by pair (p = h * S + s),
@@ -2916,6 +3181,69 @@ hipError_t dq8_d(int D, bool causal, const void *q, const void *k, const void *v
                                                 scale, sp, ws, s);
 }
 }  // namespace
+
+// dK and dV of fa_bwd on the pipelined kernel (fa_bwd_dkdv8): dense problems
+// at D = 64 or 128 with 16-bit inputs, one workgroup per 128-key tile.
+namespace {
+template <typename T, typename OT, int D, bool CAUSAL>
+hipError_t launch_dkv8(const void *q, const void *k, const void *v, const void *dout,
+                       const float *lse, const float *dl, void *dk, void *dv, int Nq, int Nk,
+                       int BH, float c, float scale, hipStream_t s) {
+  const int nkt = (Nk + 127) / 128;
+  hipLaunchKernelGGL((fa_bwd_dkdv8<T, OT, D, CAUSAL>), dim3((unsigned)(BH * nkt)),
+                     dim3(kThreads8), 0, s, (const T *)q, (const T *)k, (const T *)v,
+                     (const T *)dout, lse, dl, (OT *)dk, (OT *)dv, (float *)nullptr, Nq, Nk, BH,
+                     nkt, c, scale);
+  return hipGetLastError();
+}
+template <typename T, typename OT>
+hipError_t dkv8_d(int D, bool causal, const void *q, const void *k, const void *v,
+                  const void *dout, const float *lse, const float *dl, void *dk, void *dv,
+                  int Nq, int Nk, int BH, float c, float scale, hipStream_t s) {
+  if (D == 64)
+    return causal ? launch_dkv8<T, OT, 64, true>(q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH, c,
+                                                 scale, s)
+                  : launch_dkv8<T, OT, 64, false>(q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH,
+                                                  c, scale, s);
+  return causal ? launch_dkv8<T, OT, 128, true>(q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH, c,
+                                                scale, s)
+                : launch_dkv8<T, OT, 128, false>(q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH, c,
+                                                 scale, s);
+}
+}  // namespace
+
+__attribute__((visibility("hidden"))) bool fa_internal_bwd_dkdv8(
+    const void *q, const void *k, const void *v, const void *dout, const float *lse,
+    const float *dl, void *dk, void *dv, int Nq, int Nk, int BH, int D, int dtype, bool causal,
+    float c, float scale, void *stream, hipError_t *err) {
+  if (D != 64 && D != 128) return false;
+  // one round of 128-key workgroups leaves the causal triangle unbalanced:
+  // from two tiles per compute unit on, longest-first rounds balance it
+  // (measured: B8 N4096 D128 causal, one tile per unit, 211 us against 201
+  // for the 64-key kernel; B1 H16 N8192 968 against 1278)
+  int cus = 0;
+  if (device_cus(&cus) != FA_OK || (int64_t)BH * ((Nk + 127) / 128) < 2LL * cus) return false;
+  hipStream_t s = (hipStream_t)stream;
+  switch (dtype) {
+    case FA_BF16:
+      *err = dkv8_d<__bf16, __bf16>(D, causal, q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH, c,
+                                    scale, s);
+      return true;
+    case FA_BF16_OF32:
+      *err = dkv8_d<__bf16, float>(D, causal, q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH, c,
+                                   scale, s);
+      return true;
+    case FA_F16:
+      *err = dkv8_d<_Float16, _Float16>(D, causal, q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH,
+                                        c, scale, s);
+      return true;
+    case FA_F16_OF32:
+      *err = dkv8_d<_Float16, float>(D, causal, q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH, c,
+                                     scale, s);
+      return true;
+    default: return false;
+  }
+}
 
 // Bytes of dQ partials the stream schedule may need for this problem on a
 // device of up to 256 compute units (0 when it never runs), independent of
