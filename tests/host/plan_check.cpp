@@ -1,6 +1,7 @@
 // Host check of the stream-K schedule of fa_fwd_ws (make_plan, ChunkWalk,
 // CutTile, make_tables of csrc/stream_plan.h, the code the kernels and the
-// host planner run): for many shapes, lead and tail units and
+// host planner run), and of the backward's plans of 128-row and 128-key
+// tiles (plan_rows): for many shapes, lead and tail units and
 // compute-unit counts, every key tile of every query tile is covered by
 // exactly one piece, pieces that do not cover their whole tile write to
 // distinct workspace slots, those tiles are exactly the cut list, the
@@ -25,11 +26,19 @@ struct Piece {
   int ch, kt0, kt1, slot;
 };
 
+// rows128: the plan of the backward's 128-row (dQ) or 128-key (dK/dV)
+// tiles, plan_rows with lead `lead` instead of make_plan's.
 int check(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, bool causal, int cus, int lead,
-          int tail) {
+          int tail, bool rows128 = false) {
   StreamPlan sp;
   size_t ws = 0;
-  if (!make_plan(BH, Nq, Nk, D, FA_BF16, causal, cus, sp, ws)) return 0;
+  if (rows128) {
+    if (!plan_rows(BH, Nq, Nk, 128, lead, 0, causal, cus, sp)) return 0;
+    lead = -1;
+    ws = (size_t)2 * sp.G * 128 * (size_t)(D + 4) * 4;
+  } else if (!make_plan(BH, Nq, Nk, D, FA_BF16, causal, cus, sp, ws)) {
+    return 0;
+  }
   if (lead >= 0) {  // the same plan with other lead and tail units
     sp.lead = lead;
     sp.tail = tail;
@@ -189,6 +198,16 @@ int main() {
                 if (r < 0) return 1;
                 n += r;
               }
+  for (int64_t BH : {1, 2, 3, 8, 40})
+    for (int64_t Nq : Ns)
+      for (int64_t Nk : {(int64_t)1, (int64_t)500, Nq})
+        for (int causal = 0; causal < 2; ++causal)
+          for (int cus : cuss)
+            for (int lead : {0, 3, 4}) {
+              const int r = check(BH, Nq, Nk, 128, causal != 0, cus, lead, 0, true);
+              if (r < 0) return 1;
+              n += r;
+            }
   printf("ok %d\n", n);
   return 0;
 }

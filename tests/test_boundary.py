@@ -189,15 +189,24 @@ def test_bwd_validation(kw, status):
 
 
 def test_bwd_workspace_size():
-    """The row terms (B*H*Nq fp32), plus at D = 64 and 128 the dQ partial
-    sums of the stream schedule past them (rounded up to 256 bytes): at most
-    two slots of 128 rows x D fp32 per chunk, 256 chunks.  The query needs no
-    device."""
+    """The row terms (B*H*Nq fp32), plus at D = 64 and 128 the partial sums
+    of the stream schedules past them (rounded up to 256 bytes): the larger
+    of dQ's (two slots of 128 rows x D fp32 per chunk) and dK/dV's (two
+    slots of 2 x 128 keys x D per chunk), at most 256 chunks.  The query
+    needs no device."""
     st, n = fa.fa_bwd_workspace_size(2, 3, 100, 90, 32, 1, fa.FA_BF16)
     assert (st, n) == (fa.FA_OK, 2 * 3 * 100 * 4)
+    # causal with Nq != Nk: the dQ schedule only
     st, n = fa.fa_bwd_workspace_size(2, 3, 100, 90, 64, 1, fa.FA_BF16)
     assert st == fa.FA_OK and n > 2 * 3 * 100 * 4 and (n - 2560) % (2 * 128 * 64 * 4) == 0
     assert n - 2560 <= 2 * 256 * 128 * 64 * 4
+    # causal, Nq = Nk = 256: dK/dV's plan has 6 heads x (2 + 4 key-tile
+    # units and 2 x 4 lead units) = 84 chunks, dQ's 6 x (6 + 2 x 3) = 72
+    st, n = fa.fa_bwd_workspace_size(2, 3, 256, 256, 64, 1, fa.FA_BF16)
+    assert (st, n) == (fa.FA_OK, 6 * 256 * 4 + 2 * 84 * 2 * 128 * 64 * 4)
+    # a workspace of that size is written in full: the part past the row
+    # terms counts in the overlap check
+    assert call_bwd(Nq=256, Nk=256, ws=DQ - 8192, ws_bytes=n) == fa.FA_ERR_OVERLAP
     # 512 or more query tiles of 128 rows: one workgroup per tile, row terms only
     assert fa.fa_bwd_workspace_size(1, 32, 2048, 2048, 128, 1, fa.FA_BF16)[1] == 32 * 2048 * 4
     assert fa.fa_bwd_workspace_size(2, 3, 100, 90, 48, 1, fa.FA_BF16)[0] == fa.FA_ERR_HEAD_DIM

@@ -177,10 +177,11 @@ def test_bwd_deterministic():
 def test_bwd_dq_stream_and_grid(shape, causal):
     """dQ at D = 64 and 128 runs the stream-K schedule of 128-row tiles when
     the workspace holds its partial sums (the size fa_bwd_workspace_size
-    reports) and one workgroup per tile when it holds only the row terms:
-    both against the oracle's bound, and within a few fp32 roundings of
-    each other (they add the key chunks in a different order); dK and dV are
-    the same kernel either way, bit for bit."""
+    reports) and one workgroup per tile when it holds only the row terms;
+    so do dK and dV where their schedule applies (non-causal, or causal with
+    Nq = Nk a multiple of 128), else both runs take the 64-key kernel: both
+    against the oracle's bound, and within a few fp32 roundings of each
+    other (the sums run in a different order)."""
     B, H, Nq, Nk, D = shape
     q, k, v, g = inputs(B, H, Nq, Nk, D, seed=950 + Nq)
     scale = 1.0 / math.sqrt(D)
@@ -209,9 +210,28 @@ def test_bwd_dq_stream_and_grid(shape, causal):
             ratio = float((err / (2 * u * b + 1e-6 * float(b.max()) + 1e-30)).max())
             _log(f"  {which} {name}: max-abs {float(err.max()):.3e} worst error/bound {ratio:.3f}")
             assert ratio <= 1.0, f"{which} {name}: error exceeds 2u*b ({ratio:.3f})"
-    assert np.array_equal(res[0][1], res[1][1]) and np.array_equal(res[0][2], res[1][2])
-    d = np.abs(res[0][0] - res[1][0])
-    assert float(d.max()) <= 1e-5 * max(1.0, float(np.abs(res[1][0]).max())), float(d.max())
+    for n in range(3):
+        d = np.abs(res[0][n] - res[1][n])
+        assert float(d.max()) <= 1e-5 * max(1.0, float(np.abs(res[1][n]).max())), float(d.max())
+    if causal and (Nq != Nk or Nq % 128):  # the same dK/dV kernel both times
+        assert np.array_equal(res[0][1], res[1][1]) and np.array_equal(res[0][2], res[1][2])
+
+
+@pytest.mark.parametrize("shape,causal", [
+    ((2, 3, 1024, 1024, 128), True),   # 48 tiles over 256 chunks: most cut many times
+    ((1, 1, 128, 128, 64), True),      # one tile, two pieces
+    ((1, 2, 640, 640, 64), True),
+    ((1, 2, 77, 333, 64), False),      # ragged keys and queries
+    ((3, 1, 500, 300, 128), False),
+])
+def test_bwd_dkv_stream_shapes(shape, causal):
+    """dK and dV on the stream-K schedule of 128-key tiles (fewer than two
+    per compute unit): key tiles split into pieces over query tiles, each
+    cut tile's partial sums added in piece order by the merge kernel; every
+    row against the oracle."""
+    B, H, Nq, Nk, D = shape
+    q, k, v, g = inputs(B, H, Nq, Nk, D, seed=990 + Nq + D)
+    compare(q, k, v, g, causal, 1.0 / math.sqrt(D), what="dK/dV stream")
 
 
 @pytest.mark.parametrize("D", [64, 128])

@@ -66,10 +66,13 @@ bool fa_internal_bwd_dq8(const void *q, const void *k, const void *v, const void
                          size_t ws_bytes, void *stream, hipError_t *err);
 size_t fa_internal_dq8_bytes(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, bool causal);
 // dK and dV on the same machinery (fa_fwd.hip), same cases; false otherwise.
+// Below two key tiles per compute unit it needs the stream schedule's
+// partial sums in ws (fa_internal_dkv8_bytes); without them, false.
 bool fa_internal_bwd_dkdv8(const void *q, const void *k, const void *v, const void *dout,
                            const float *lse, const float *dl, void *dk, void *dv, int Nq, int Nk,
-                           int BH, int D, int dtype, bool causal, float c, float scale,
-                           void *stream, hipError_t *err);
+                           int BH, int D, int dtype, bool causal, float c, float scale, void *ws,
+                           size_t ws_bytes, void *stream, hipError_t *err);
+size_t fa_internal_dkv8_bytes(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, bool causal);
 
 #include "tiles.h"
 
@@ -532,7 +535,9 @@ struct BwdArgs {
   const int *cu_q = nullptr, *cu_k = nullptr;
   int S = 1, maxq = 0, maxk = 0;
   Mask mk = {0, 1, 0};  // local-window + global-token mask (MASKED launches)
-  void *dqws = nullptr;  // dQ partial sums of the stream schedule (dense only)
+  // partial sums of the stream schedules of dK/dV, then of dQ (dense only;
+  // the kernels run one after the other, so they share it)
+  void *dqws = nullptr;
   size_t dqws_bytes = 0;
 };
 
@@ -562,7 +567,7 @@ hipError_t launch_bwd(const BwdArgs &a) {
                                                           : (of32 ? FA_F16_OF32 : FA_F16);
       done_kv = fa_internal_bwd_dkdv8(a.q, a.k, a.v, a.dout, a.lse, (const float *)a.dl, a.dk,
                                       a.dv, a.Nq, a.Nk, a.BH, D, code, CAUSAL, c, a.scale,
-                                      a.stream, &e);
+                                      a.dqws, a.dqws_bytes, a.stream, &e);
       if (done_kv && e != hipSuccess) return e;
     }
   }
@@ -633,6 +638,14 @@ int check_shape(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int dty
   return FA_OK;
 }
 
+// Partial sums of the stream schedules past the row terms: the larger of
+// the dK/dV and the dQ needs (the two never hold data at once).
+size_t stream_bytes(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, bool causal) {
+  const size_t a = fa_internal_dq8_bytes(BH, Nq, Nk, D, causal);
+  const size_t b = fa_internal_dkv8_bytes(BH, Nq, Nk, D, causal);
+  return a > b ? a : b;
+}
+
 }  // namespace
 
 extern "C" {
@@ -644,7 +657,7 @@ int fa_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t 
   const int st = check_shape(B, H, Nq, Nk, D, dtype);
   if (st != FA_OK) return st;
   const size_t lb = (size_t)(B * H * Nq) * sizeof(float);
-  const size_t extra = fa_internal_dq8_bytes(B * H, Nq, Nk, D, causal != 0);
+  const size_t extra = stream_bytes(B * H, Nq, Nk, D, causal != 0);
   *bytes = extra ? (lb + 255) / 256 * 256 + extra : lb;
   return FA_OK;
 }
@@ -669,9 +682,14 @@ static int bwd_dense(const void *q, const void *k, const void *v, const void *o,
   const size_t dqb = (size_t)(BH * Nq * D) * gsz, dkb = (size_t)(BH * Nk * D) * gsz;
   const size_t need = lb;
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  // past the row terms (rounded up to 256 bytes): the stream schedules'
+  // partial sums, used when the workspace holds them
+  const size_t off = (lb + 255) / 256 * 256;
+  const size_t extra = mk ? 0 : stream_bytes(BH, Nq, Nk, D, causal != 0);
+  const size_t used = extra && workspace_bytes >= off + extra ? off + extra : need;
   // written buffers against every buffer of the call
   const void *outs[4] = {dq, dk, dv, workspace};
-  const size_t osz[4] = {dqb, dkb, dkb, need};
+  const size_t osz[4] = {dqb, dkb, dkb, used};
   const void *ins[6] = {q, k, v, o, dout, lse};
   const size_t isz[6] = {qb, kb, kb, qb, qb, lb};
   for (int x = 0; x < 4; ++x) {
@@ -691,13 +709,9 @@ static int bwd_dense(const void *q, const void *k, const void *v, const void *o,
   a.dk = dk;
   a.dv = dv;
   a.dl = (float *)workspace;
-  {
-    // past the row terms (rounded up to 256 bytes): the dQ partial sums
-    const size_t off = (lb + 255) / 256 * 256;
-    if (!mk && workspace_bytes > off) {
-      a.dqws = (char *)workspace + off;
-      a.dqws_bytes = workspace_bytes - off;
-    }
+  if (used > need) {
+    a.dqws = (char *)workspace + off;
+    a.dqws_bytes = extra;
   }
   a.Nq = (int)Nq;
   a.Nk = (int)Nk;

@@ -1940,6 +1940,76 @@ __global__ __launch_bounds__(kThreads8) void fa_bwd_dkdv8(
   dkv8_run<T, OT, D, CAUSAL>(q, k, v, dout, lse, dl, dk, dv, ws, Nq, Nk, c, scale, it, false);
 }
 
+// The stream-K schedule of the forward applied to key tiles: the plan's
+// "query tiles" are 128-key tiles and its units the 64-row query tiles each
+// one meets.  Under the causal mask key tile t meets query tiles 2t .. n-1,
+// the forward's triangle read backwards (plan tile t' = nkt - 1 - t holds
+// 2(t' + 1) units) when Nq = Nk is a multiple of 128, the only causal case
+// the host gives this kernel.
+template <typename T, typename OT, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads8) void fa_bwd_dkdv8_stream(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    const T *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dl,
+    OT *__restrict__ dk, OT *__restrict__ dv, float *__restrict__ ws, int Nq, int Nk, float c,
+    float scale, StreamPlan sp, ChunkStarts cs) {
+  ChunkWalk cw;
+  const int ch = chunk_of(blockIdx.x, sp.G);
+  cw.init_at(sp, ch, cs.w[2 * ch], cs.w[2 * ch + 1]);
+  PipeItem it;
+  int t;
+  while (cw.next(sp, CAUSAL, it, t)) {
+    const int kt = CAUSAL ? sp.nqt - 1 - t : t;  // the key tile
+    const int base = CAUSAL ? 2 * kt : 0;          // its first query tile
+    it.q0 = kt * 128;
+    it.kt0 += base;
+    it.kt1 += base;
+    dkv8_run<T, OT, D, CAUSAL>(q, k, v, dout, lse, dl, dk, dv, ws, Nq, Nk, c, scale, it, true);
+  }
+}
+
+// Sums the partial dK^T and dV^T of each cut key tile's pieces (in piece
+// order) and stores scale times the dK sum and the dV sum.
+template <typename OT, int D>
+__global__ __launch_bounds__(kThreads) void fa_merge_dkv8(const float *__restrict__ ws,
+                                                          OT *__restrict__ dk,
+                                                          OT *__restrict__ dv, int Nk,
+                                                          float scale, int nkt, bool causal,
+                                                          CutList cuts) {
+  constexpr int C4 = D / 4;
+  constexpr int RPP = kThreads / C4;
+  constexpr int ROWS = merge_rows<D>();
+  constexpr int SPLIT = 128 / ROWS;
+  constexpr int NR = ROWS / RPP;
+  static_assert(NR >= 1 && ROWS % RPP == 0, "merge tiling");
+  const uint32_t w0 = cuts.w[2 * (blockIdx.x / SPLIT)];
+  const uint32_t w1 = cuts.w[2 * (blockIdx.x / SPLIT) + 1];
+  const int bh = (int)(w0 & 0xffffu), tp = (int)(w0 >> 16);
+  const int kt = causal ? nkt - 1 - tp : tp;
+  const int np = cut_pieces(w1);
+  const int c4 = threadIdx.x % C4;
+  const int r0 = (blockIdx.x % SPLIT) * ROWS + threadIdx.x / C4;
+  f32x4 ak[NR], av[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) ak[i] = av[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kk = 0; kk < np; ++kk) {
+    const float *w = ws + (size_t)cut_slot(w1, kk) * 2 * 128 * D;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const size_t e = (size_t)(r0 + i * RPP) * D + 4 * c4;
+      ak[i] += *reinterpret_cast<const f32x4 *>(w + e);
+      av[i] += *reinterpret_cast<const f32x4 *>(w + 128 * D + e);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int key = kt * 128 + r0 + i * RPP;
+    if (key < Nk) {
+      store4<OT>(dk + ((size_t)bh * Nk + key) * D + 4 * c4, ak[i] * scale);
+      store4<OT>(dv + ((size_t)bh * Nk + key) * D + 4 * c4, av[i]);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Stream-K schedule for variable-length batches (the dense schedule's
 // balance, for packed sequences of any lengths).  The units are those of the
@@ -3185,10 +3255,38 @@ hipError_t dq8_d(int D, bool causal, const void *q, const void *k, const void *v
 // dK and dV of fa_bwd on the pipelined kernel (fa_bwd_dkdv8): dense problems
 // at D = 64 or 128 with 16-bit inputs, one workgroup per 128-key tile.
 namespace {
+constexpr int kKvLead = 4;  // fixed cost of a piece, in 64-row query tiles
+
+// Stream schedule of fa_bwd_dkdv8_stream: fewer than two 128-key tiles per
+// compute unit, and under the causal mask Nq = Nk, a multiple of 128.
+bool dkv8_plan(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, bool causal, int cus,
+               StreamPlan &sp) {
+  if (D != 64 && D != 128) return false;
+  if (BH * ((Nk + 127) / 128) >= 2LL * cus) return false;
+  if (causal && (Nq != Nk || Nk % 128 != 0)) return false;
+  return plan_rows(BH, Nk, Nq, 128, kKvLead, 0, causal, cus, sp);
+}
+
 template <typename T, typename OT, int D, bool CAUSAL>
 hipError_t launch_dkv8(const void *q, const void *k, const void *v, const void *dout,
                        const float *lse, const float *dl, void *dk, void *dv, int Nq, int Nk,
-                       int BH, float c, float scale, hipStream_t s) {
+                       int BH, float c, float scale, const StreamPlan *sp, float *ws,
+                       hipStream_t s) {
+  if (sp) {
+    ChunkStarts cs;
+    CutList cuts;
+    make_tables(*sp, CAUSAL, cs, cuts);
+    hipLaunchKernelGGL((fa_bwd_dkdv8_stream<T, OT, D, CAUSAL>), dim3((unsigned)sp->G),
+                       dim3(kThreads8), 0, s, (const T *)q, (const T *)k, (const T *)v,
+                       (const T *)dout, lse, dl, (OT *)dk, (OT *)dv, ws, Nq, Nk, c, scale, *sp,
+                       cs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || cuts.n == 0) return e;
+    hipLaunchKernelGGL((fa_merge_dkv8<OT, D>),
+                       dim3((unsigned)(cuts.n * (128 / merge_rows<D>()))), dim3(kThreads), 0, s,
+                       (const float *)ws, (OT *)dk, (OT *)dv, Nk, scale, sp->nqt, CAUSAL, cuts);
+    return hipGetLastError();
+  }
   const int nkt = (Nk + 127) / 128;
   hipLaunchKernelGGL((fa_bwd_dkdv8<T, OT, D, CAUSAL>), dim3((unsigned)(BH * nkt)),
                      dim3(kThreads8), 0, s, (const T *)q, (const T *)k, (const T *)v,
@@ -3199,47 +3297,59 @@ hipError_t launch_dkv8(const void *q, const void *k, const void *v, const void *
 template <typename T, typename OT>
 hipError_t dkv8_d(int D, bool causal, const void *q, const void *k, const void *v,
                   const void *dout, const float *lse, const float *dl, void *dk, void *dv,
-                  int Nq, int Nk, int BH, float c, float scale, hipStream_t s) {
+                  int Nq, int Nk, int BH, float c, float scale, const StreamPlan *sp, float *ws,
+                  hipStream_t s) {
   if (D == 64)
     return causal ? launch_dkv8<T, OT, 64, true>(q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH, c,
-                                                 scale, s)
+                                                 scale, sp, ws, s)
                   : launch_dkv8<T, OT, 64, false>(q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH,
-                                                  c, scale, s);
+                                                  c, scale, sp, ws, s);
   return causal ? launch_dkv8<T, OT, 128, true>(q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH, c,
-                                                scale, s)
+                                                scale, sp, ws, s)
                 : launch_dkv8<T, OT, 128, false>(q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH, c,
-                                                 scale, s);
+                                                 scale, sp, ws, s);
 }
 }  // namespace
 
 __attribute__((visibility("hidden"))) bool fa_internal_bwd_dkdv8(
     const void *q, const void *k, const void *v, const void *dout, const float *lse,
     const float *dl, void *dk, void *dv, int Nq, int Nk, int BH, int D, int dtype, bool causal,
-    float c, float scale, void *stream, hipError_t *err) {
+    float c, float scale, void *ws, size_t ws_bytes, void *stream, hipError_t *err) {
   if (D != 64 && D != 128) return false;
-  // one round of 128-key workgroups leaves the causal triangle unbalanced:
+  // One round of 128-key workgroups leaves the causal triangle unbalanced:
   // from two tiles per compute unit on, longest-first rounds balance it
   // (measured: B8 N4096 D128 causal, one tile per unit, 211 us against 201
-  // for the 64-key kernel; B1 H16 N8192 968 against 1278)
+  // for the 64-key kernel; B1 H16 N8192 968 against 1278); below that the
+  // stream schedule, when the workspace holds its partials; else the
+  // 64-key kernel.
   int cus = 0;
-  if (device_cus(&cus) != FA_OK || (int64_t)BH * ((Nk + 127) / 128) < 2LL * cus) return false;
+  if (device_cus(&cus) != FA_OK) return false;
+  StreamPlan sp;
+  const StreamPlan *use = nullptr;
+  if ((int64_t)BH * ((Nk + 127) / 128) < 2LL * cus) {
+    if (!ws || !dkv8_plan(BH, Nq, Nk, D, causal, cus, sp) ||
+        ws_bytes < (size_t)2 * sp.G * 2 * 128 * (size_t)D * 4)
+      return false;
+    use = &sp;
+  }
+  float *w = (float *)ws;
   hipStream_t s = (hipStream_t)stream;
   switch (dtype) {
     case FA_BF16:
       *err = dkv8_d<__bf16, __bf16>(D, causal, q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH, c,
-                                    scale, s);
+                                    scale, use, w, s);
       return true;
     case FA_BF16_OF32:
       *err = dkv8_d<__bf16, float>(D, causal, q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH, c,
-                                   scale, s);
+                                   scale, use, w, s);
       return true;
     case FA_F16:
       *err = dkv8_d<_Float16, _Float16>(D, causal, q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH,
-                                        c, scale, s);
+                                        c, scale, use, w, s);
       return true;
     case FA_F16_OF32:
       *err = dkv8_d<_Float16, float>(D, causal, q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH, c,
-                                     scale, s);
+                                     scale, use, w, s);
       return true;
     default: return false;
   }
@@ -3254,6 +3364,17 @@ __attribute__((visibility("hidden"))) size_t fa_internal_dq8_bytes(int64_t BH, i
   StreamPlan sp;
   if (!dq8_plan(BH, Nq, Nk, D, causal, fa_sched::kMaxChunks, sp)) return 0;
   return (size_t)2 * sp.G * 128 * (size_t)D * 4;
+}
+
+// Bytes of dK/dV partials the stream schedule may need (as
+// fa_internal_dq8_bytes: for a device of up to 256 compute units, 0 when
+// it never runs).
+__attribute__((visibility("hidden"))) size_t fa_internal_dkv8_bytes(int64_t BH, int64_t Nq,
+                                                                    int64_t Nk, int64_t D,
+                                                                    bool causal) {
+  StreamPlan sp;
+  if (!dkv8_plan(BH, Nq, Nk, D, causal, fa_sched::kMaxChunks, sp)) return 0;
+  return (size_t)2 * sp.G * 2 * 128 * (size_t)D * 4;
 }
 
 __attribute__((visibility("hidden"))) bool fa_internal_bwd_dq8(
