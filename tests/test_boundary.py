@@ -200,10 +200,12 @@ def test_bwd_workspace_size():
     st, n = fa.fa_bwd_workspace_size(2, 3, 100, 90, 64, 1, fa.FA_BF16)
     assert st == fa.FA_OK and n > 2 * 3 * 100 * 4 and (n - 2560) % (2 * 128 * 64 * 4) == 0
     assert n - 2560 <= 2 * 256 * 128 * 64 * 4
-    # causal, Nq = Nk = 256: dK/dV's plan has 6 heads x (2 + 4 key-tile
-    # units and 2 x 4 lead units) = 84 chunks, dQ's 6 x (6 + 2 x 3) = 72
+    # causal, Nq = Nk = 256: dK/dV's plan has 6 heads x (2 + 4 query-tile
+    # units and 2 x 2 lead units) = 60 chunks (two slots of 2 x 128 x 64
+    # floats each), dQ's 6 x (2 + 4 key-tile units and 2 x 3 lead units) =
+    # 72 chunks (two slots of 128 x 64 floats)
     st, n = fa.fa_bwd_workspace_size(2, 3, 256, 256, 64, 1, fa.FA_BF16)
-    assert (st, n) == (fa.FA_OK, 6 * 256 * 4 + 2 * 84 * 2 * 128 * 64 * 4)
+    assert (st, n) == (fa.FA_OK, 6 * 256 * 4 + 2 * 60 * 2 * 128 * 64 * 4)
     # a workspace of that size is written in full: the part past the row
     # terms counts in the overlap check
     assert call_bwd(Nq=256, Nk=256, ws=DQ - 8192, ws_bytes=n) == fa.FA_ERR_OVERLAP

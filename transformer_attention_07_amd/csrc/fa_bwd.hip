@@ -58,11 +58,12 @@
 int fa_internal_hip_fail(hipError_t e);
 // dQ on the forward's pipelined machinery (fa_fwd.hip): dense problems, D = 64
 // or 128; returns false for any other case, which the kernel below takes.
+// It forms Dl from O and dO itself and writes it to dl (no fa_bwd_prep).
 // ws / ws_bytes: scratch for the stream schedule's partial sums (its size
 // from fa_internal_dq8_bytes; with less, one workgroup per query tile).
-bool fa_internal_bwd_dq8(const void *q, const void *k, const void *v, const void *dout,
-                         const float *lse, const float *dl, void *dq, int Nq, int Nk, int BH,
-                         int D, int dtype, bool causal, float c, float scale, void *ws,
+bool fa_internal_bwd_dq8(const void *q, const void *k, const void *v, const void *o,
+                         const void *dout, const float *lse, float *dl, void *dq, int Nq, int Nk,
+                         int BH, int D, int dtype, bool causal, float c, float scale, void *ws,
                          size_t ws_bytes, void *stream, hipError_t *err);
 size_t fa_internal_dq8_bytes(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, bool causal);
 // dK and dV on the same machinery (fa_fwd.hip), same cases; false otherwise.
@@ -544,14 +545,32 @@ struct BwdArgs {
 template <typename T, typename OT, int D, bool CAUSAL, bool MASKED = false>
 hipError_t launch_bwd(const BwdArgs &a) {
   const float c = a.scale * kLog2e;
-  const int64_t rows = (int64_t)a.BH * a.Nq;
-  constexpr int RPB = kThreads / (D / 8);
-  hipLaunchKernelGGL((fa_bwd_prep<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)),
-                     dim3(kThreads), 0, a.stream, (const T *)a.o, (const T *)a.dout, a.dl,
-                     rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const bool vl = a.cu_q != nullptr;
+  hipError_t e = hipSuccess;
+  // Dense problems at D = 64 and 128: dQ first, on the pipelined kernel,
+  // which also writes Dl; otherwise the row terms come from fa_bwd_prep and
+  // dQ from fa_bwd_dq after dK/dV.
+  bool done_q = false;
+  if constexpr (!MASKED && (D == 64 || D == 128)) {
+    if (!vl) {
+      constexpr bool of32 = std::is_same<OT, float>::value;
+      constexpr int code = std::is_same<T, __bf16>::value ? (of32 ? FA_BF16_OF32 : FA_BF16)
+                                                          : (of32 ? FA_F16_OF32 : FA_F16);
+      done_q = fa_internal_bwd_dq8(a.q, a.k, a.v, a.o, a.dout, a.lse, a.dl, a.dq, a.Nq, a.Nk,
+                                   a.BH, D, code, CAUSAL, c, a.scale, a.dqws, a.dqws_bytes,
+                                   a.stream, &e);
+      if (done_q && e != hipSuccess) return e;
+    }
+  }
+  if (!done_q) {
+    const int64_t rows = (int64_t)a.BH * a.Nq;
+    constexpr int RPB = kThreads / (D / 8);
+    hipLaunchKernelGGL((fa_bwd_prep<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)),
+                       dim3(kThreads), 0, a.stream, (const T *)a.o, (const T *)a.dout, a.dl,
+                       rows);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   // tiles per slice, and slices per tile rank
   // (a variable-length grid has at least one key tile per slice when there
   // are keys, so that keys past a zero max_seqlen_k still get their NaN)
@@ -580,17 +599,7 @@ hipError_t launch_bwd(const BwdArgs &a) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if constexpr (!MASKED && (D == 64 || D == 128)) {
-    if (!vl) {
-      constexpr bool of32 = std::is_same<OT, float>::value;
-      constexpr int code = std::is_same<T, __bf16>::value ? (of32 ? FA_BF16_OF32 : FA_BF16)
-                                                          : (of32 ? FA_F16_OF32 : FA_F16);
-      if (fa_internal_bwd_dq8(a.q, a.k, a.v, a.dout, a.lse, (const float *)a.dl, a.dq, a.Nq,
-                              a.Nk, a.BH, D, code, CAUSAL, c, a.scale, a.dqws, a.dqws_bytes,
-                              a.stream, &e))
-        return e;
-    }
-  }
+  if (done_q) return hipSuccess;
   hipLaunchKernelGGL((fa_bwd_dq<T, OT, D, CAUSAL, MASKED>), dim3((unsigned)(slices * nqt)),
                      dim3(kThreads), 0, a.stream, (const T *)a.q, (const T *)a.k,
                      (const T *)a.v, (const T *)a.dout, a.lse, (const float *)a.dl,

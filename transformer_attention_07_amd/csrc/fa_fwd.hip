@@ -1435,13 +1435,19 @@ struct DqLayout {
 // tile at it.q0 of slice it.bh.  With it.slot < 0 the item is the whole tile
 // and stores dQ (times scale, in OT); otherwise it writes its fp32 partial
 // sum to workspace slot it.slot (128 rows of D), which fa_merge_dq8 adds up.
+//
+// Dl_i = <dO_i, O_i> is formed here from O and dO (each lane holds half of
+// its query's row of both, the other half in lane l ^ 32), and the piece
+// that starts at the tile's first key tile stores it to dl for the dK/dV
+// pass, which runs after this one.
 template <typename T, typename OT, int D, bool CAUSAL>
 __device__ __forceinline__ void dq8_run(const T *__restrict__ q, const T *__restrict__ k,
-                                        const T *__restrict__ v, const T *__restrict__ dout,
-                                        const float *__restrict__ lse,
-                                        const float *__restrict__ dl, OT *__restrict__ dq,
-                                        float *__restrict__ ws, int Nq, int Nk, float c,
-                                        float scale, const PipeItem it, bool reuse) {
+                                        const T *__restrict__ v, const T *__restrict__ o,
+                                        const T *__restrict__ dout,
+                                        const float *__restrict__ lse, float *__restrict__ dl,
+                                        OT *__restrict__ dq, float *__restrict__ ws, int Nq,
+                                        int Nk, float c, float scale, const PipeItem it,
+                                        bool reuse) {
   typedef DqLayout<T, D> L;
   typedef Dma8<T, D, T, L> DM;
   typedef typename Mma<T>::frag frag;
@@ -1472,6 +1478,7 @@ __device__ __forceinline__ void dq8_run(const T *__restrict__ q, const T *__rest
   const size_t koff = (size_t)it.bh * Nk * D;
   const u32x4 q_rs = raw_rsrc(q + qoff, (uint32_t)Nq * D * sizeof(T));
   const u32x4 do_rs = raw_rsrc(dout + qoff, (uint32_t)Nq * D * sizeof(T));
+  const u32x4 o_rs = raw_rsrc(o + qoff, (uint32_t)Nq * D * sizeof(T));
   const u32x4 k_rs = raw_rsrc(k + koff, (uint32_t)Nk * D * sizeof(T));
   const u32x4 v_rs = raw_rsrc(v + koff, (uint32_t)Nk * D * sizeof(T));
   DM dm;
@@ -1479,18 +1486,19 @@ __device__ __forceinline__ void dq8_run(const T *__restrict__ q, const T *__rest
 
   // rows past Nq: L = +inf gives P = 0
   const float l2 = my_q < Nq ? lse[(size_t)it.bh * Nq + my_q] * 1.4426950408889634f : INFINITY;
-  const float dd = my_q < Nq ? dl[(size_t)it.bh * Nq + my_q] : 0.f;
+  float dd = 0.f;  // Dl of this lane's query (0 past Nq: O and dO read as zero)
   const int kt0 = it.kt0;
   const int ntiles = it.kt1 - it.kt0;
   // last 32-key block (absolute) with a key this wave's queries see
   const int lastb = CAUSAL ? min(2 * it.kt1 - 1, (qw + 31) / 32) : 2 * it.kt1 - 1;
 
-  u32x4 qraw[QF], draw[QF];
+  u32x4 qraw[QF], draw[QF], oraw[QF];
 #pragma unroll
   for (int f = 0; f < QF; ++f) {
     const uint32_t off = ((uint32_t)my_q * D + 16 * f + 8 * g) * sizeof(T);
     qraw[f] = load16_async(q_rs, off);
     draw[f] = load16_async(do_rs, off);
+    oraw[f] = load16_async(o_rs, off);
   }
   dm.issue(k_rs, v_rs, kt0, 0, kt0, 0);
   if (ntiles > 1) dm.issue(k_rs, v_rs, kt0 + 1, 1, kt0 + 1, 1);
@@ -1507,12 +1515,22 @@ __device__ __forceinline__ void dq8_run(const T *__restrict__ q, const T *__rest
       if (r + 2 < ntiles) dm.issue(k_rs, v_rs, kt0 + r + 2, (r + 2) & 3, kt0 + r + 2, (r + 2) & 3);
       if (r + 3 < ntiles) dm.issue(k_rs, v_rs, kt0 + r + 3, (r + 3) & 3, kt0 + r + 3, (r + 3) & 3);
       if (r == 0) {
+        float part = 0.f;
 #pragma unroll
         for (int f = 0; f < QF; ++f) {
-          asm volatile("" : "+v"(qraw[f]), "+v"(draw[f]));  // read after the wait above
+          // read after the wait above
+          asm volatile("" : "+v"(qraw[f]), "+v"(draw[f]), "+v"(oraw[f]));
           qf[f] = __builtin_bit_cast(frag, qraw[f]);
           dof[f] = __builtin_bit_cast(frag, draw[f]);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const f32x2 x = Mma<T>::unpack2(draw[f][w]), y = Mma<T>::unpack2(oraw[f][w]);
+            part = __builtin_fmaf(x[0], y[0], part);
+            part = __builtin_fmaf(x[1], y[1], part);
+          }
         }
+        dd = part + __shfl_xor(part, 32);
+        if (it.kt0 == 0 && h == 0 && g == 0 && my_q < Nq) dl[(size_t)it.bh * Nq + my_q] = dd;
       }
     }
     const int b = 2 * (kt0 + r) + h;
@@ -1613,13 +1631,13 @@ __device__ __forceinline__ void dq8_run(const T *__restrict__ q, const T *__rest
 template <typename T, typename OT, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads8) void fa_bwd_dq8(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-    const T *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dl,
-    OT *__restrict__ dq, float *__restrict__ ws, int Nq, int Nk, int BH, int nqt, float c,
-    float scale) {
+    const T *__restrict__ o, const T *__restrict__ dout, const float *__restrict__ lse,
+    float *__restrict__ dl, OT *__restrict__ dq, float *__restrict__ ws, int Nq, int Nk, int BH,
+    int nqt, float c, float scale) {
   const WorkItem wi = work_item(BH, nqt, CAUSAL, 128);
   const int kend = CAUSAL ? min(Nk, wi.q0 + 128) : Nk;
   const PipeItem it = {wi.bh, wi.q0, 0, (kend + kBN - 1) / kBN, -1};
-  dq8_run<T, OT, D, CAUSAL>(q, k, v, dout, lse, dl, dq, ws, Nq, Nk, c, scale, it, false);
+  dq8_run<T, OT, D, CAUSAL>(q, k, v, o, dout, lse, dl, dq, ws, Nq, Nk, c, scale, it, false);
 }
 
 // The stream-K schedule of the forward (128-row tiles): each workgroup walks
@@ -1627,9 +1645,9 @@ __global__ __launch_bounds__(kThreads8) void fa_bwd_dq8(
 template <typename T, typename OT, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads8) void fa_bwd_dq8_stream(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-    const T *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dl,
-    OT *__restrict__ dq, float *__restrict__ ws, int Nq, int Nk, float c, float scale,
-    StreamPlan sp, ChunkStarts cs) {
+    const T *__restrict__ o, const T *__restrict__ dout, const float *__restrict__ lse,
+    float *__restrict__ dl, OT *__restrict__ dq, float *__restrict__ ws, int Nq, int Nk,
+    float c, float scale, StreamPlan sp, ChunkStarts cs) {
   ChunkWalk cw;
   const int ch = chunk_of(blockIdx.x, sp.G);
   cw.init_at(sp, ch, cs.w[2 * ch], cs.w[2 * ch + 1]);
@@ -1637,7 +1655,7 @@ __global__ __launch_bounds__(kThreads8) void fa_bwd_dq8_stream(
   int t;
   while (cw.next(sp, CAUSAL, it, t)) {
     it.q0 = t * 128;
-    dq8_run<T, OT, D, CAUSAL>(q, k, v, dout, lse, dl, dq, ws, Nq, Nk, c, scale, it, true);
+    dq8_run<T, OT, D, CAUSAL>(q, k, v, o, dout, lse, dl, dq, ws, Nq, Nk, c, scale, it, true);
   }
 }
 
@@ -3214,8 +3232,9 @@ bool dq8_plan(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, bool causal, int cu
 }
 
 template <typename T, typename OT, int D, bool CAUSAL>
-hipError_t launch_dq8(const void *q, const void *k, const void *v, const void *dout,
-                      const float *lse, const float *dl, void *dq, int Nq, int Nk, int BH,
+hipError_t launch_dq8(const void *q, const void *k, const void *v, const void *o,
+                      const void *dout, const float *lse, float *dl, void *dq, int Nq, int Nk,
+                      int BH,
                       float c, float scale, const StreamPlan *sp, float *ws, hipStream_t s) {
   if (sp) {
     ChunkStarts cs;
@@ -3223,7 +3242,7 @@ hipError_t launch_dq8(const void *q, const void *k, const void *v, const void *d
     make_tables(*sp, CAUSAL, cs, cuts);
     hipLaunchKernelGGL((fa_bwd_dq8_stream<T, OT, D, CAUSAL>), dim3((unsigned)sp->G),
                        dim3(kThreads8), 0, s, (const T *)q, (const T *)k, (const T *)v,
-                       (const T *)dout, lse, dl, (OT *)dq, ws, Nq, Nk, c, scale, *sp, cs);
+                       (const T *)o, (const T *)dout, lse, dl, (OT *)dq, ws, Nq, Nk, c, scale, *sp, cs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || cuts.n == 0) return e;
     hipLaunchKernelGGL((fa_merge_dq8<OT, D>), dim3((unsigned)(cuts.n * (128 / merge_rows<D>()))),
@@ -3233,21 +3252,22 @@ hipError_t launch_dq8(const void *q, const void *k, const void *v, const void *d
   const int nqt = (Nq + 127) / 128;
   hipLaunchKernelGGL((fa_bwd_dq8<T, OT, D, CAUSAL>), dim3((unsigned)(BH * nqt)),
                      dim3(kThreads8), 0, s, (const T *)q, (const T *)k, (const T *)v,
-                     (const T *)dout, lse, dl, (OT *)dq, ws, Nq, Nk, BH, nqt, c, scale);
+                     (const T *)o, (const T *)dout, lse, dl, (OT *)dq, ws, Nq, Nk, BH, nqt, c, scale);
   return hipGetLastError();
 }
 template <typename T, typename OT>
 hipError_t dq8_d(int D, bool causal, const void *q, const void *k, const void *v,
-                 const void *dout, const float *lse, const float *dl, void *dq, int Nq, int Nk,
+                 const void *o, const void *dout, const float *lse, float *dl, void *dq, int Nq,
+                 int Nk,
                  int BH, float c, float scale, const StreamPlan *sp, float *ws, hipStream_t s) {
   if (D == 64)
-    return causal ? launch_dq8<T, OT, 64, true>(q, k, v, dout, lse, dl, dq, Nq, Nk, BH, c,
+    return causal ? launch_dq8<T, OT, 64, true>(q, k, v, o, dout, lse, dl, dq, Nq, Nk, BH, c,
                                                 scale, sp, ws, s)
-                  : launch_dq8<T, OT, 64, false>(q, k, v, dout, lse, dl, dq, Nq, Nk, BH, c,
+                  : launch_dq8<T, OT, 64, false>(q, k, v, o, dout, lse, dl, dq, Nq, Nk, BH, c,
                                                  scale, sp, ws, s);
-  return causal ? launch_dq8<T, OT, 128, true>(q, k, v, dout, lse, dl, dq, Nq, Nk, BH, c, scale,
+  return causal ? launch_dq8<T, OT, 128, true>(q, k, v, o, dout, lse, dl, dq, Nq, Nk, BH, c, scale,
                                                sp, ws, s)
-                : launch_dq8<T, OT, 128, false>(q, k, v, dout, lse, dl, dq, Nq, Nk, BH, c,
+                : launch_dq8<T, OT, 128, false>(q, k, v, o, dout, lse, dl, dq, Nq, Nk, BH, c,
                                                 scale, sp, ws, s);
 }
 }  // namespace
@@ -3255,7 +3275,11 @@ hipError_t dq8_d(int D, bool causal, const void *q, const void *k, const void *v
 // dK and dV of fa_bwd on the pipelined kernel (fa_bwd_dkdv8): dense problems
 // at D = 64 or 128 with 16-bit inputs, one workgroup per 128-key tile.
 namespace {
-constexpr int kKvLead = 4;  // fixed cost of a piece, in 64-row query tiles
+// Fixed cost of a piece, in 64-row query tiles.  Measured on MI355X
+// (causal B8 N4096 D128, B16 N2048 D128, B8 N4096 D64, B2 H8 N2048 D128;
+// non-causal B1 H8 N4096 D128) against lead 4: lead 2 gained 1-3% on every
+// causal shape and lost 1% on the non-causal one, 6 and 9 the reverse.
+constexpr int kKvLead(bool causal) { return causal ? 2 : 6; }
 
 // Stream schedule of fa_bwd_dkdv8_stream: fewer than two 128-key tiles per
 // compute unit, and under the causal mask Nq = Nk, a multiple of 128.
@@ -3264,7 +3288,7 @@ bool dkv8_plan(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, bool causal, int c
   if (D != 64 && D != 128) return false;
   if (BH * ((Nk + 127) / 128) >= 2LL * cus) return false;
   if (causal && (Nq != Nk || Nk % 128 != 0)) return false;
-  return plan_rows(BH, Nk, Nq, 128, kKvLead, 0, causal, cus, sp);
+  return plan_rows(BH, Nk, Nq, 128, kKvLead(causal), 0, causal, cus, sp);
 }
 
 template <typename T, typename OT, int D, bool CAUSAL>
@@ -3378,9 +3402,9 @@ __attribute__((visibility("hidden"))) size_t fa_internal_dkv8_bytes(int64_t BH, 
 }
 
 __attribute__((visibility("hidden"))) bool fa_internal_bwd_dq8(
-    const void *q, const void *k, const void *v, const void *dout, const float *lse,
-    const float *dl, void *dq, int Nq, int Nk, int BH, int D, int dtype, bool causal, float c,
-    float scale, void *ws, size_t ws_bytes, void *stream, hipError_t *err) {
+    const void *q, const void *k, const void *v, const void *o, const void *dout,
+    const float *lse, float *dl, void *dq, int Nq, int Nk, int BH, int D, int dtype, bool causal,
+    float c, float scale, void *ws, size_t ws_bytes, void *stream, hipError_t *err) {
   if (D != 64 && D != 128) return false;
   hipStream_t s = (hipStream_t)stream;
   int cus = 0;
@@ -3392,19 +3416,19 @@ __attribute__((visibility("hidden"))) bool fa_internal_bwd_dq8(
   float *w = (float *)ws;
   switch (dtype) {
     case FA_BF16:
-      *err = dq8_d<__bf16, __bf16>(D, causal, q, k, v, dout, lse, dl, dq, Nq, Nk, BH, c, scale,
+      *err = dq8_d<__bf16, __bf16>(D, causal, q, k, v, o, dout, lse, dl, dq, Nq, Nk, BH, c, scale,
                                    use, w, s);
       return true;
     case FA_BF16_OF32:
-      *err = dq8_d<__bf16, float>(D, causal, q, k, v, dout, lse, dl, dq, Nq, Nk, BH, c, scale,
+      *err = dq8_d<__bf16, float>(D, causal, q, k, v, o, dout, lse, dl, dq, Nq, Nk, BH, c, scale,
                                   use, w, s);
       return true;
     case FA_F16:
-      *err = dq8_d<_Float16, _Float16>(D, causal, q, k, v, dout, lse, dl, dq, Nq, Nk, BH, c,
+      *err = dq8_d<_Float16, _Float16>(D, causal, q, k, v, o, dout, lse, dl, dq, Nq, Nk, BH, c,
                                        scale, use, w, s);
       return true;
     case FA_F16_OF32:
-      *err = dq8_d<_Float16, float>(D, causal, q, k, v, dout, lse, dl, dq, Nq, Nk, BH, c,
+      *err = dq8_d<_Float16, float>(D, causal, q, k, v, o, dout, lse, dl, dq, Nq, Nk, BH, c,
                                     scale, use, w, s);
       return true;
     default: return false;
