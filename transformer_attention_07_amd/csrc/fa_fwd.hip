@@ -1807,24 +1807,33 @@ __device__ __forceinline__ void dkv8_run(const T *__restrict__ q, const T *__res
     dva[db] = f32x16{};
   }
 
-  for (int r = 0; r < ntiles; ++r) {
-    if ((r & 1) == 0) {
-      ring_barrier<0>();
-      if (r + 2 < ntiles) issue(qt0 + r + 2, (r + 2) & 3);
-      if (r + 3 < ntiles) issue(qt0 + r + 3, (r + 3) & 3);
-      if (r == 0) {
+  // even steps: tiles r and r+1 have landed, and every wave is done with
+  // the stages of tiles r-2 and r-1, which tiles r+2 and r+3 now take
+  auto ring_step = [&](int r) {
+    ring_barrier<0>();
+    if (r + 2 < ntiles) issue(qt0 + r + 2, (r + 2) & 3);
+    if (r + 3 < ntiles) issue(qt0 + r + 3, (r + 3) & 3);
+  };
+  ring_step(0);
 #pragma unroll
-        for (int f = 0; f < QF; ++f) {
-          asm volatile("" : "+v"(kraw[f]), "+v"(vraw[f]));  // read after the wait above
-          kf[f] = __builtin_bit_cast(frag, kraw[f]);
-          vf[f] = __builtin_bit_cast(frag, vraw[f]);
-        }
-      }
-    }
+  for (int f = 0; f < QF; ++f) {
+    asm volatile("" : "+v"(kraw[f]), "+v"(vraw[f]));  // read after the wait above
+    kf[f] = __builtin_bit_cast(frag, kraw[f]);
+    vf[f] = __builtin_bit_cast(frag, vraw[f]);
+  }
+
+  const int mk4 = my_k - 4 * g;
+  // Step r: query tile qt0 + r, this wave's 32 rows (i0 .. i0 + 31).  Blocks
+  // with no visible pair are skipped; every other step takes the causal test
+  // (two instructions a score).  Rows past Nq need no mask: their Q, dO, L
+  // and Dl read as zero, so P = 1 there and dS = 0, and both meet zero rows
+  // of dO and Q in dV and dK.
+  auto step = [&](int r) {
+    if (r > 0 && (r & 1) == 0) ring_step(r);
     const int i0 = (qt0 + r) * kBN + 32 * h;  // this wave's first query of the tile
     // wave-uniform: no query of the block sees a key of this wave
-    if (CAUSAL && i0 + 31 < kw) continue;
-    if (i0 >= Nq) continue;
+    if (CAUSAL && i0 + 31 < kw) return;
+    if (i0 >= Nq) return;
     const int st = r & 3;
     const lds_char *qp = ring + st * L::K_BYTES + h * 32 * L::SK * 16;
     const lds_char *dp_ = ring + L::V_OFF + st * L::V_BYTES + h * 32 * L::SV * 16;
@@ -1839,8 +1848,6 @@ __device__ __forceinline__ void dkv8_run(const T *__restrict__ q, const T *__res
     }
     // rows of register 4 r4 + e: query i0 + 8 r4 + 4 g + e; the two 16-row
     // halves (ks) are finished one after the other to keep registers low
-    const int need_mask = __builtin_amdgcn_readfirstlane(
-        (i0 + 32 > Nq) || (CAUSAL && kw + 31 > i0) ? 1 : 0);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       float p[8], ds[8];
@@ -1854,12 +1861,12 @@ __device__ __forceinline__ void dkv8_run(const T *__restrict__ q, const T *__res
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int x = 4 * r4 + e;
-          float pr =
-              __builtin_amdgcn_exp2f(__builtin_fmaf(sc[x], c, -lv[e] * 1.4426950408889634f));
-          if (need_mask) {
-            const int qi = i0 + ib + e;
-            if (qi >= Nq || (CAUSAL && my_k > qi)) pr = 0.f;
-          }
+          float pr = __builtin_amdgcn_exp2f(
+              __builtin_fmaf(sc[x], c, -lv[e] * 1.4426950408889634f));
+          // query i0 + 8 r4 + e + 4g against key my_k: the wave-uniform
+          // part of the query index against a per-lane constant
+          if constexpr (CAUSAL)
+            if (mk4 > i0 + 8 * r4 + e) pr = 0.f;
           p[4 * hr + e] = pr;
           ds[4 * hr + e] = pr * (dpv[x] - dv4[e]);
         }
@@ -1881,7 +1888,10 @@ __device__ __forceinline__ void dkv8_run(const T *__restrict__ q, const T *__res
         dka[db] = Mma<T>::mma(__builtin_bit_cast(frag, rb), sb, dka[db]);
       }
     }
-  }
+  };
+  // One loop: the masked steps run apart from the others (two more copies
+  // of the step) made the compiler spill K and V fragments.
+  for (int r = 0; r < ntiles; ++r) step(r);
   wait_vmcnt<0>();    // no DMA may outlive the ring
   ring_barrier<0>();  // every wave is done with the ring
 
