@@ -370,8 +370,16 @@ int fa_fwd_fp8_ws(const void *q, const void *k, const void *v, void *o, float *l
                   int out_f32, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * fa_bwd_workspace_size -- device scratch bytes that fa_bwd needs (written
- * to *bytes): B * H * Nq * 4, one fp32 row term per query row.
+ * fa_bwd_workspace_size -- device scratch bytes for fa_bwd (written to
+ * *bytes): B * H * Nq * 4, one fp32 row term per query row; at D = 64 and
+ * 128, when a stream-K schedule may run (fewer than two 128-row query tiles,
+ * or 128-key tiles, per compute unit), that rounded up to 256 bytes plus the
+ * larger of the two schedules' partial sums: for dQ two slots of 128 x D
+ * fp32 per chunk, for dK/dV two slots of 2 x 128 x D fp32 per chunk, at most
+ * 256 chunks (the figure covers every device of up to 256 compute units).
+ * fa_bwd needs only the row terms; with less than this size it runs one
+ * workgroup per tile instead of the stream schedule (same results within
+ * fp32 rounding of the sums' order).  The query needs no device.
  *
  * Returns FA_OK, FA_ERR_NULLPTR (bytes NULL), FA_ERR_SHAPE, FA_ERR_HEAD_DIM
  * or FA_ERR_DTYPE, with the rules of fa_bwd.
@@ -404,14 +412,17 @@ int fa_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk,
  *              rounded once, at the end); FA_BF16_OF32 / FA_F16_OF32: the
  *              same inputs, gradients stored in fp32.  FA_F32 is not
  *              supported here (FA_ERR_DTYPE).
- *   workspace  device pointer, 16-byte aligned, at least
- *              fa_bwd_workspace_size bytes (overwritten)
+ *   workspace  device pointer, 16-byte aligned, at least B * H * Nq * 4
+ *              bytes; fa_bwd_workspace_size bytes let the stream-K
+ *              schedules run (overwritten, as far as the call uses it)
  *   stream     a hipStream_t (NULL = the default stream)
  *
  * Products are formed from 16-bit operands with fp32 accumulation; P and dS
  * are rounded to the input type before they multiply dout, q and k.  Every
- * gradient element is written by exactly one workgroup, with plain stores:
- * results are deterministic.  Returns FA_OK once enqueued, a validation
+ * gradient element is written by exactly one workgroup, with plain stores
+ * (a tile split by a stream-K schedule leaves fp32 partial sums in the
+ * workspace, added in a fixed order by a second kernel): results are
+ * deterministic.  Returns FA_OK once enqueued, a validation
  * error (nothing enqueued: FA_ERR_NULLPTR, FA_ERR_SHAPE, FA_ERR_HEAD_DIM,
  * FA_ERR_DTYPE, FA_ERR_SCALE, FA_ERR_ALIGN, FA_ERR_WORKSPACE, or
  * FA_ERR_OVERLAP when dq, dk, dv or the workspace overlap an input or each
@@ -450,8 +461,8 @@ int fa_bwd_masked(const void *q, const void *k, const void *v, const void *o,
  * and its dq rows (dk and dv rows) past that tile are set to NaN, so no row
  * is left unwritten.  Each sequence's gradients are exactly fa_bwd's for that
  * sequence alone; keys that no query sees get dk = dv = 0, queries without
- * keys get dq = 0.  The workspace needs H * Tq * 4 bytes (what
- * fa_bwd_workspace_size reports for B = 1, Nq = Tq).  Other arguments,
+ * keys get dq = 0.  The workspace needs H * Tq * 4 bytes (the row terms of
+ * fa_bwd_workspace_size for B = 1, Nq = Tq).  Other arguments,
  * dtypes, head dims and status codes as fa_bwd (the offsets need 4-byte
  * alignment).
  */

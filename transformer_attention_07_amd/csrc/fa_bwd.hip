@@ -14,7 +14,12 @@
 //     dS_ij = P_ij (dP_ij - Dl_i)
 //     dQ_i  = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i
 //
-// Three kernels, enqueued in order on the caller's stream:
+// Dense problems at D = 64 and 128 run on the forward's pipelined machinery
+// (fa_fwd.hip: fa_bwd_dq8 / fa_bwd_dq8_stream, then fa_bwd_dkdv8 /
+// fa_bwd_dkdv8_stream, with their merge kernels when a stream-K schedule
+// splits tiles); the dQ kernel there forms Dl itself.  Every other case
+// (head dims 16 and 32, the masked and variable-length passes) runs the
+// three kernels of this file, enqueued in order on the caller's stream:
 //   * fa_bwd_prep: Dl_i = <dO_i, O_i> in fp32 into the workspace.
 //   * fa_bwd_dkdv: one workgroup per (batch*head, 64 keys), 32 keys per
 //     wave held in VGPRs as MFMA B operands; it streams 128-query blocks of
@@ -23,7 +28,7 @@
 //   * fa_bwd_dq: one workgroup per (batch*head, 64 queries), 32 queries per
 //     wave held in VGPRs; it streams 128-key blocks of K and V through LDS
 //     and accumulates dQ^T.
-// Recomputing S and dP in both kernels (instead of fp32 atomics on dQ)
+// Recomputing S and dP for dQ and for dK/dV (instead of fp32 atomics on dQ)
 // keeps every result deterministic and every store plain.
 //
 // gfx950 mapping (v_mfma_f32_32x32x16_{bf16,f16}, fp32 accumulation):
