@@ -313,8 +313,11 @@ def test_varlen_split_graph_capture_replays_match_eager():
 def compare_bwd(lq, lk, H, D, causal, seed, dtype="bf16"):
     """Gradients against the oracle (per sequence, with the backward's
     derived bound 2u*b, u the input type's unit roundoff), 16-bit gradients
-    the exact rounding of the fp32 ones, and each sequence bit-identical to
-    fa_bwd on that sequence alone."""
+    the exact rounding of the fp32 ones, and each sequence matching fa_bwd on
+    that sequence alone: bit for bit at D = 16 and 32, where both run the same
+    kernels; at D = 64 and 128 fa_bwd runs the pipelined kernels (other tile
+    shapes and summation orders, and P and dS can round to the neighbouring
+    16-bit value), so there within u*b, half of each side's own bound."""
     from workloads import gen_grad_out
 
     q, k, v, cu_q, cu_k = packed(lq, lk, H, D, seed, dtype)
@@ -360,8 +363,15 @@ def compare_bwd(lq, lk, H, D, causal, seed, dtype="bf16"):
                      causal=causal, scale=scale, grad_dtype=torch.float32)
         torch.cuda.synchronize()
         for n in range(3):
-            assert torch.equal(one[n][0].cpu(), g32[n][:, rows[n]]), \
-                f"sequence {s}: gradient {n} differs from fa_bwd on the sequence alone"
+            if D <= 32:
+                assert torch.equal(one[n][0].cpu(), g32[n][:, rows[n]]), \
+                    f"sequence {s}: gradient {n} differs from fa_bwd on the sequence alone"
+            else:
+                bd = ref[n + 3][0]
+                d = np.abs(one[n][0].cpu().double().numpy() - g32[n][:, rows[n]].double().numpy())
+                lim = u * bd + 1e-6 * float(bd.max()) + 1e-30
+                assert (d <= lim).all(), \
+                    f"sequence {s}: gradient {n} differs from fa_bwd on the sequence alone"
 
 
 @pytest.mark.parametrize("D", [16, 32, 64, 128])
