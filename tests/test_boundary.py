@@ -381,3 +381,15 @@ def test_extreme_sizes_workspace_queries(pos, big):
     v[pos] = big
     assert fa.fa_fwd_varlen_workspace_size(*v, 300, 300, 64, 1, fa.FA_BF16)[0] == \
         fa.FA_ERR_SHAPE
+
+
+def test_debug_library_exports_the_same_symbols_and_its_check():
+    """libfa_debug.so (the build with ring-barrier checks, include/fa_debug.h)
+    exports every symbol of include/fa.h plus fa_debug_barrier_faults, which
+    the release library does not."""
+    dbg = fa.debug_library()
+    for name in _declared_functions():
+        assert hasattr(dbg, name), f"libfa_debug.so does not export {name}"
+    assert hasattr(dbg, "fa_debug_barrier_faults")
+    assert not hasattr(fa.library(), "fa_debug_barrier_faults")
+    assert dbg.fa_debug_barrier_faults(None, 0) == fa.FA_ERR_NULLPTR

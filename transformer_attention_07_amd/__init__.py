@@ -63,13 +63,14 @@ __all__ = [
     "FA_F32", "FA_BF16", "FA_BF16_OF32", "FA_F16", "FA_F16_OF32",
     "FA_OK", "FA_ERR_NULLPTR", "FA_ERR_SHAPE", "FA_ERR_HEAD_DIM", "FA_ERR_DTYPE",
     "FA_ERR_SCALE", "FA_ERR_ALIGN", "FA_ERR_HIP", "FA_ERR_OVERLAP", "FA_ERR_WORKSPACE",
-    "LIBRARY", "EXPORTS", "library", "fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws",
+    "LIBRARY", "DEBUG_LIBRARY", "EXPORTS", "library", "debug_library", "fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws",
     "fa_fwd_noalloc", "fa_fwd_varlen", "fa_fwd_varlen_workspace_size", "fa_fwd_varlen_ws", "fa_fwd_masked", "fa_fwd_fp8", "fa_fwd_fp8_workspace_size", "fa_fwd_fp8_ws",
     "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_varlen", "fa_bwd_masked", "fa_status_str",
     "fa_last_hip_error", "fa_version", "fwd", "fwd_varlen", "fwd_masked", "fwd_fp8", "bwd", "bwd_varlen", "FaError",
 ]
 
 LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+DEBUG_LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_debug.so")
 
 # Scratch of fa_fwd_noalloc per device (include/fa.h)
 FA_NOALLOC_SCRATCH_BYTES = 72 * 1024 * 1024
@@ -97,13 +98,28 @@ class FaError(RuntimeError):
 def library() -> ctypes.CDLL:
     """Load libfa.so (raises if it has not been built)."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIBRARY):
+    if _lib is None:
+        _lib = _bind(LIBRARY)
+    return _lib
+
+
+def debug_library() -> ctypes.CDLL:
+    """Load libfa_debug.so, the build with ring-barrier checks
+    (include/fa_debug.h), with the same prototypes plus
+    fa_debug_barrier_faults.  The wrappers below use it in place of libfa.so
+    while ``_lib`` is set to it."""
+    lib = _bind(DEBUG_LIBRARY)
+    lib.fa_debug_barrier_faults.restype = ctypes.c_int
+    lib.fa_debug_barrier_faults.argtypes = [ctypes.POINTER(ctypes.c_uint), ctypes.c_int]
+    return lib
+
+
+def _bind(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
         raise RuntimeError(
-            f"{LIBRARY} is missing: build it with `python -m "
+            f"{path} is missing: build it with `python -m "
             "transformer_attention_07_amd.build` (or __graft_entry__.build())")
-    lib = ctypes.CDLL(LIBRARY)
+    lib = ctypes.CDLL(path)
     i64, vp = ctypes.c_int64, ctypes.c_void_p
     lib.fa_fwd.restype = ctypes.c_int
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
@@ -162,7 +178,6 @@ def library() -> ctypes.CDLL:
     lib.fa_last_hip_error.argtypes = []
     lib.fa_version.restype = ctypes.c_int
     lib.fa_version.argtypes = []
-    _lib = lib
     return lib
 
 

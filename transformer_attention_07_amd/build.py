@@ -26,6 +26,9 @@ SOURCES = [
 ]
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libfa.so")
+# the same sources with the ring-barrier checks compiled in (include/fa_debug.h)
+DEBUG_LIBRARY = os.path.join(PKG, "libfa_debug.so")
+DEBUG_FLAGS = ("-DFA_DEBUG_BARRIERS=1",)
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -70,5 +73,15 @@ def build(out: str = LIBRARY, extra=(), verbose: bool = False, link_extra=()) ->
     return out
 
 
+def build_all(verbose: bool = False) -> None:
+    """The release library and the debug one, side by side."""
+    with concurrent.futures.ThreadPoolExecutor(max_workers=2) as pool:
+        jobs = [pool.submit(build, LIBRARY, (), verbose),
+                pool.submit(build, DEBUG_LIBRARY, DEBUG_FLAGS, verbose)]
+        for f in jobs:
+            f.result()
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    build_all(verbose=True)
+    print(LIBRARY, DEBUG_LIBRARY)

@@ -295,6 +295,49 @@ __device__ __forceinline__ void wait_counts() {
   static_assert(N >= 0 && N < 64 && L >= 0 && L < 16, "counter range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (L << 8));
 }
+
+// Debug builds (compiled with -DFA_DEBUG_BARRIERS=1, libfa_debug.so): every
+// ring barrier also checks that all waves of the workgroup have passed as
+// many ring barriers as this one.  The DMA ring's stage accounting assumes
+// that they do; a wave that skipped or added a barrier would otherwise let a
+// load overwrite a stage still being read, silently.  Each wave counts its
+// barriers in its own LDS slot, raised before the barrier; after it, another
+// wave's count may be one ahead (raised for the next barrier, which cannot
+// complete without this wave) but never behind or further ahead.  A mismatch
+// adds one to a device counter that fa_debug_barrier_faults reads
+// (include/fa_debug.h).  Release builds compile none of it.
+#ifndef FA_DEBUG_BARRIERS
+#define FA_DEBUG_BARRIERS 0
+#endif
+#if FA_DEBUG_BARRIERS
+__device__ unsigned int fa_dbg_faults;
+__device__ __forceinline__ __attribute__((address_space(3))) unsigned int *dbg_slots() {
+  __shared__ unsigned int slots[16];
+  return (__attribute__((address_space(3))) unsigned int *)slots;
+}
+// at the start of every kernel that uses ring barriers
+__device__ __forceinline__ void dbg_begin() {
+  if (threadIdx.x < 16) dbg_slots()[threadIdx.x] = 0u;
+  __syncthreads();
+}
+__device__ __forceinline__ void dbg_pre() {
+  if ((threadIdx.x & 63) == 0) dbg_slots()[threadIdx.x >> 6] += 1u;
+  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (0x7 << 4) | (0 << 8));  // lgkmcnt(0)
+}
+__device__ __forceinline__ void dbg_post() {
+  const int lane = threadIdx.x & 63, nw = (int)(blockDim.x >> 6);
+  const unsigned int mine = dbg_slots()[threadIdx.x >> 6];
+  bool bad = false;
+  if (lane < nw) {
+    const unsigned int d = dbg_slots()[lane] - mine;
+    bad = d > 1u;
+  }
+  if (__ballot(bad) != 0ull && lane == 0) atomicAdd(&fa_dbg_faults, 1u);
+}
+#define FA_DBG_BEGIN() dbg_begin()
+#else
+#define FA_DBG_BEGIN() ((void)0)
+#endif
 template <int N, bool LGKM0 = false>
 __device__ __forceinline__ void wait_vmcnt() {
   wait_counts<N, LGKM0 ? 0 : 15>();
@@ -308,10 +351,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 // keep the compiler from moving LDS accesses across.
 template <int N, int L = 0>
 __device__ __forceinline__ void ring_barrier() {
+#if FA_DEBUG_BARRIERS
+  dbg_pre();
+#endif
   wait_counts<N, L>();
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+#if FA_DEBUG_BARRIERS
+  dbg_post();
+#endif
 }
 
 // ring_barrier<2n> for a wave-uniform n in 0..3: n = this wave's own count
@@ -1274,6 +1323,7 @@ __global__ __launch_bounds__(kThreads8) void fa_fwd_pipe8(
     const KT *__restrict__ q, const KT *__restrict__ k, const T *__restrict__ v,
     OT *__restrict__ o, float *__restrict__ lse, int Nq, int Nk, int BH, int nqt,
     float c, int negate, Mask mk, float osc) {
+  FA_DBG_BEGIN();
   constexpr int QT = QRows<PAIR>::value;
   const WorkItem wi = work_item(BH, nqt, CAUSAL, QT);
   if constexpr (MASKED) {
@@ -1332,6 +1382,7 @@ __global__ __launch_bounds__(kThreads8) void fa_fwd_varlen(
     OT *__restrict__ o, float *__restrict__ lse, const int *__restrict__ cu_q,
     const int *__restrict__ cu_k, int S, int H, int Tq, int Tk, int ntiles, float c,
     int negate, float *__restrict__ ws, int NC, int KC, int NT) {
+  FA_DBG_BEGIN();
   constexpr int QT = QRows<PAIR>::value;
   const int chunk = blockIdx.x % NC;
   const int id = blockIdx.x / NC;
@@ -1634,6 +1685,7 @@ __global__ __launch_bounds__(kThreads8) void fa_bwd_dq8(
     const T *__restrict__ o, const T *__restrict__ dout, const float *__restrict__ lse,
     float *__restrict__ dl, OT *__restrict__ dq, float *__restrict__ ws, int Nq, int Nk, int BH,
     int nqt, float c, float scale) {
+  FA_DBG_BEGIN();
   const WorkItem wi = work_item(BH, nqt, CAUSAL, 128);
   const int kend = CAUSAL ? min(Nk, wi.q0 + 128) : Nk;
   const PipeItem it = {wi.bh, wi.q0, 0, (kend + kBN - 1) / kBN, -1};
@@ -1648,6 +1700,7 @@ __global__ __launch_bounds__(kThreads8) void fa_bwd_dq8_stream(
     const T *__restrict__ o, const T *__restrict__ dout, const float *__restrict__ lse,
     float *__restrict__ dl, OT *__restrict__ dq, float *__restrict__ ws, int Nq, int Nk,
     float c, float scale, StreamPlan sp, ChunkStarts cs) {
+  FA_DBG_BEGIN();
   ChunkWalk cw;
   const int ch = chunk_of(blockIdx.x, sp.G);
   cw.init_at(sp, ch, cs.w[2 * ch], cs.w[2 * ch + 1]);
@@ -1949,6 +2002,7 @@ __global__ __launch_bounds__(kThreads8) void fa_bwd_dkdv8(
     const T *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dl,
     OT *__restrict__ dk, OT *__restrict__ dv, float *__restrict__ ws, int Nq, int Nk, int BH,
     int nkt, float c, float scale) {
+  FA_DBG_BEGIN();
   const int id = blockIdx.x;
   const int bh = id % BH, t = id / BH;  // causal: t ascending = longest first
   const int k0 = t * 128;
@@ -1980,6 +2034,7 @@ __global__ __launch_bounds__(kThreads8) void fa_bwd_dkdv8_stream(
     const T *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dl,
     OT *__restrict__ dk, OT *__restrict__ dv, float *__restrict__ ws, int Nq, int Nk, float c,
     float scale, StreamPlan sp, ChunkStarts cs) {
+  FA_DBG_BEGIN();
   ChunkWalk cw;
   const int ch = chunk_of(blockIdx.x, sp.G);
   cw.init_at(sp, ch, cs.w[2 * ch], cs.w[2 * ch + 1]);
@@ -2083,6 +2138,7 @@ __global__ __launch_bounds__(kThreads8) void fa_fwd_stream_varlen(
     OT *__restrict__ o, float *__restrict__ lse, float *__restrict__ ws,
     const int *__restrict__ cu_q, const int *__restrict__ cu_k, int S, int H, int Tq, int Tk,
     float c, int negate, uint32_t *__restrict__ cuts, int G) {
+  FA_DBG_BEGIN();
   constexpr int QT = QRows<PAIR>::value;
   constexpr int tu = QT / kBN;
   constexpr int LEAD = stream_lead(D, PAIR);
@@ -2266,6 +2322,7 @@ __global__ __launch_bounds__(kThreads8) void fa_fwd_stream(
     const KT *__restrict__ q, const KT *__restrict__ k, const T *__restrict__ v,
     OT *__restrict__ o, float *__restrict__ lse, float *__restrict__ ws, int Nq, int Nk,
     float c, int negate, StreamPlan sp, ChunkStarts cs, float osc) {
+  FA_DBG_BEGIN();
   ChunkWalk cw;
   const int ch = chunk_of(blockIdx.x, sp.G);
   cw.init_at(sp, ch, cs.w[2 * ch], cs.w[2 * ch + 1]);
@@ -3547,6 +3604,23 @@ hipError_t dispatch_fp8(const Launch &a, int D, bool causal) {
 extern "C" {
 
 int fa_version(void) { return 300; }
+
+#if FA_DEBUG_BARRIERS
+// include/fa_debug.h: ring-barrier mismatches counted on the current device.
+int fa_debug_barrier_faults(unsigned int *count, int reset) {
+  if (!count) return FA_ERR_NULLPTR;
+  hipError_t e = hipMemcpyFromSymbol(count, HIP_SYMBOL(fa_dbg_faults), sizeof(unsigned int), 0,
+                                     hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fa_internal_hip_fail(e);
+  if (reset) {
+    const unsigned int zero = 0u;
+    e = hipMemcpyToSymbol(HIP_SYMBOL(fa_dbg_faults), &zero, sizeof(zero), 0,
+                          hipMemcpyHostToDevice);
+    if (e != hipSuccess) return fa_internal_hip_fail(e);
+  }
+  return FA_OK;
+}
+#endif
 
 const char *fa_status_str(int s) {
   switch (s) {
