@@ -192,9 +192,10 @@ template <> struct Pack4<_Float16> {
 // Computing each store's data into the same few registers made each one
 // wait until the previous store had read its data, which under load from
 // other waves serialised the stores.
+// Column blocks [cb, ce) of the row (wave-uniform bounds).
 template <typename OT, int NDB>
 __device__ __forceinline__ void store_row(const f32x16 (&acc)[NDB], float inv, OT *orow, int g,
-                                          int dlim) {
+                                          int dlim, int cb = 0, int ce = NDB) {
   typedef typename Pack4<OT>::type PT;
   PT pk[NDB * 4];
 #pragma unroll
@@ -212,7 +213,7 @@ __device__ __forceinline__ void store_row(const f32x16 (&acc)[NDB], float inv, O
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int d = db * 32 + 8 * r4 + 4 * g;
-      if (d < dlim) *reinterpret_cast<PT *>(orow + d) = pk[db * 4 + r4];
+      if (db >= cb && db < ce && d < dlim) *reinterpret_cast<PT *>(orow + d) = pk[db * 4 + r4];
     }
 }
 
@@ -220,7 +221,8 @@ template <int D, typename OT>
 __device__ __forceinline__ void epilogue(const f32x16 (&acc)[(D < 32 ? 32 : D) / 32],
                                          float m, float l, OT *o, float *lse, int bh,
                                          int Nq, int my_q, int g, float lo = -1.f,
-                                         float osc = 1.f) {
+                                         float osc = 1.f, int cb = 0,
+                                         int ce = (D < 32 ? 32 : D) / 32, bool stats = true) {
   const float lt = l + __shfl_xor(l, 32);
   const float lot = lo < 0.f ? lt : lo;
   if (my_q >= Nq) return;
@@ -228,8 +230,8 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[(D < 32 ? 32 : D) /
   // osc: a factor of O (1 except on the FP8 path)
   const float inv = (lot > 0.f ? 1.0f / lot : 0.f) * osc;
   OT *orow = o + ((size_t)bh * Nq + my_q) * D;
-  store_row<OT, (D < 32 ? 32 : D) / 32>(acc, inv, orow, g, D);
-  if (g == 0) lse[(size_t)bh * Nq + my_q] = (m + log2f(lt)) * 0.69314718055994531f;
+  store_row<OT, (D < 32 ? 32 : D) / 32>(acc, inv, orow, g, D, cb, ce);
+  if (stats && g == 0) lse[(size_t)bh * Nq + my_q] = (m + log2f(lt)) * 0.69314718055994531f;
 }
 
 // ---------------------------------------------------------------------------
@@ -853,13 +855,14 @@ template <int D>
 __device__ __forceinline__ void epilogue_partial(const f32x16 (&acc)[(D + 31) / 32], float m,
                                                  float l, float lr, float *ws_o,
                                                  float *ws_s, int row, int g,
-                                                 float osc = 1.f) {
+                                                 float osc = 1.f, int cb = 0,
+                                                 int ce = (D + 31) / 32, bool stats = true) {
   const float lt = l + __shfl_xor(l, 32);
   const float lrt = lr;  // already the whole row's sum
   // O_p carries the factor osc: the combine is linear in the O_p
   const float inv = (lrt > 0.f ? 1.0f / lrt : 0.f) * osc;
-  store_row<float, (D + 31) / 32>(acc, inv, ws_o + (size_t)row * D, g, D);
-  if (g == 0) {
+  store_row<float, (D + 31) / 32>(acc, inv, ws_o + (size_t)row * D, g, D, cb, ce);
+  if (stats && g == 0) {
     const f32x4 st = {lrt > 0.f ? m : -INFINITY, lt, lrt, 0.f};
     *reinterpret_cast<f32x4 *>(ws_s + row * 4) = st;
   }
@@ -1228,58 +1231,94 @@ __device__ __forceinline__ void pipe8_run(const KT *__restrict__ q, const KT *__
 
   // lr: the row's whole rounded sum (every lane of a query holds it)
   float M = s.m_use, l = s.l, lr = s.lr_total();
+  // PAIR: each wave of the pair stores half of the head-dim columns (blocks
+  // [cb, cb + NDB / 2)); otherwise one wave stores them all.
+  int cb = 0, ce = P::NDB;
   if constexpr (PAIR) {
-    // Combine the pair: the odd wave hands (m, l, lr, acc) to the even one.
-    constexpr int NR = P::NDB * 4;  // f32x4 registers of acc per lane
-    lds_char *xch = ring + (uint32_t)qg * (NR + 1) * kWave * 16;
-    if (h == 1) {
+    // Combine the pair, each wave the half of the columns it stores: a wave
+    // hands the partner's half of acc and its (m, l, lr) over, and rescales
+    // its own half with the partner's (the online-softmax update applied to
+    // two partial states).
+    static_assert(P::NDB % 2 == 0, "pair split of the columns");
+    constexpr int HB = P::NDB / 2;                 // column blocks per wave
+    constexpr int XW = (HB * 4 + 1) * kWave * 16;  // bytes one wave hands over
+    lds_char *xw = ring + (uint32_t)(2 * qg + h) * XW;      // written by this wave
+    lds_char *xr = ring + (uint32_t)(2 * qg + 1 - h) * XW;  // written by the partner
+    cb = h * HB;
+    ce = cb + HB;
+    // the partner's blocks (static indices: acc stays in registers)
+    auto hand = [&](const int ob) {
 #pragma unroll
-      for (int db = 0; db < P::NDB; ++db)
+      for (int j = 0; j < HB; ++j)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4 x = {s.acc[db][4 * r4], s.acc[db][4 * r4 + 1], s.acc[db][4 * r4 + 2],
-                           s.acc[db][4 * r4 + 3]};
-          *(__attribute__((address_space(3))) f32x4 *)(xch + ((db * 4 + r4) * kWave + s.lane) * 16) = x;
+          const f32x4 x = {s.acc[ob + j][4 * r4], s.acc[ob + j][4 * r4 + 1],
+                           s.acc[ob + j][4 * r4 + 2], s.acc[ob + j][4 * r4 + 3]};
+          *(__attribute__((address_space(3))) f32x4 *)(xw + ((j * 4 + r4) * kWave + s.lane) * 16) = x;
         }
+    };
+    if (h == 0)
+      hand(HB);
+    else
+      hand(0);
+    {
       const f32x4 st = {s.m_use, s.l, lr, 0.f};
-      *(__attribute__((address_space(3))) f32x4 *)(xch + (NR * kWave + s.lane) * 16) = st;
+      *(__attribute__((address_space(3))) f32x4 *)(xw + (HB * 4 * kWave + s.lane) * 16) = st;
     }
     ring_barrier<0>();
+    const f32x4 st =
+        *(const __attribute__((address_space(3))) f32x4 *)(xr + (HB * 4 * kWave + s.lane) * 16);
+    // A wave that saw no key of a row (its blocks lie past the row under the
+    // causal mask, or the item starts there) has m = -inf, l = 0, acc = 0
+    // and weight 0; when neither wave saw one the row's partial is empty
+    // (l = 0).  Both waves form M, l and lr, and their halves of acc, by
+    // the same expressions with the even wave's terms first, so that the two
+    // agree bit for bit.
+    M = fmaxf(s.m_use, st[0]);
+    const float a0 = s.m_use == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s.m_use - M);
+    const float a1 = st[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st[0] - M);
+    f32x4 x[HB][4];
+#pragma unroll
+    for (int j = 0; j < HB; ++j)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        x[j][r4] = *(const __attribute__((address_space(3))) f32x4 *)(
+            xr + ((j * 4 + r4) * kWave + s.lane) * 16);
     if (h == 0) {
-      const f32x4 st =
-          *(const __attribute__((address_space(3))) f32x4 *)(xch + (NR * kWave + s.lane) * 16);
-      // A wave that saw no key of a row (its blocks lie past the row under
-      // the causal mask, or the item starts there) has m = -inf, l = 0,
-      // acc = 0 and weight 0; when neither wave saw one the row's partial is
-      // empty (l = 0).
-      M = fmaxf(s.m_use, st[0]);
-      const float a0 = s.m_use == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s.m_use - M);
-      const float a1 = st[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st[0] - M);
-      l = s.l * a0 + st[1] * a1;
-      lr = lr * a0 + st[2] * a1;
+      l = __builtin_fmaf(s.l, a0, st[1] * a1);
+      lr = __builtin_fmaf(lr, a0, st[2] * a1);
 #pragma unroll
-      for (int db = 0; db < P::NDB; ++db)
+      for (int j = 0; j < HB; ++j)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4 x = *(const __attribute__((address_space(3))) f32x4 *)(
-              xch + ((db * 4 + r4) * kWave + s.lane) * 16);
+        for (int r4 = 0; r4 < 4; ++r4)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            s.acc[db][4 * r4 + e] = s.acc[db][4 * r4 + e] * a0 + x[e] * a1;
-        }
+            s.acc[j][4 * r4 + e] =
+                __builtin_fmaf(s.acc[j][4 * r4 + e], a0, x[j][r4][e] * a1);
+    } else {
+      l = __builtin_fmaf(st[1], a1, s.l * a0);
+      lr = __builtin_fmaf(st[2], a1, lr * a0);
+#pragma unroll
+      for (int j = 0; j < HB; ++j)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            s.acc[HB + j][4 * r4 + e] =
+                __builtin_fmaf(x[j][r4][e], a1, s.acc[HB + j][4 * r4 + e] * a0);
     }
     // The ring is free for the workgroup's next item once every read of the
     // exchange area is done.
     ring_barrier<0>();
-    if (h == 1) return;
   }
 
+  const bool stats = !PAIR || h == 0;  // the wave that writes L (or the record)
   if (it.slot < 0) {
-    epilogue<D, OT>(s.acc, M, l, o, lse, it.bh, Nq, s.my_q, s.g, lr, osc);
+    epilogue<D, OT>(s.acc, M, l, o, lse, it.bh, Nq, s.my_q, s.g, lr, osc, cb, ce, stats);
   } else {
     float *ws_o = ws + (size_t)it.slot * QT * D;
     float *ws_s = ws + (size_t)nslots * QT * D + (size_t)it.slot * QT * 4;
-    epilogue_partial<D>(s.acc, M, l, lr, ws_o, ws_s, s.my_q - it.q0, s.g, osc);
+    epilogue_partial<D>(s.acc, M, l, lr, ws_o, ws_s, s.my_q - it.q0, s.g, osc, cb, ce, stats);
   }
 }
 
