@@ -2180,7 +2180,7 @@ __global__ __launch_bounds__(kThreads8) void fa_fwd_stream_varlen(
   FA_DBG_BEGIN();
   constexpr int QT = QRows<PAIR>::value;
   constexpr int tu = QT / kBN;
-  constexpr int LEAD = stream_lead(D, PAIR);
+  constexpr int LEAD = varlen_lead(D, PAIR);
   static_assert(kThreads8 >= kVPairs, "one pair per thread");
   __shared__ long long pre[kVPairs + 1];
   const int NP = H * S;

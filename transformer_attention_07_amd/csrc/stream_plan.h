@@ -66,6 +66,12 @@ struct StreamPlan {
 // D = 64.  Throughput is flat within a few units of these values; 0 (no
 // lead) loses up to 20% on small causal problems.
 constexpr int stream_lead(int D, bool pair) { return D == 128 ? (pair ? 5 : 4) : 6; }
+// The same for the variable-length schedule, whose tiles are shorter (a
+// sequence's last tile is often partly empty, and more pieces per chunk end
+// early): measured with the pair-split layout on 32768 tokens in 32 (8)
+// sequences, D = 128 causal, lead 7 against 5: 47.9 -> 45.3 us (93.7 ->
+// 92.1); 9: 45.9 (92.3); 3: 52.8 (93.0).
+constexpr int varlen_lead(int D, bool pair) { return pair ? 7 : stream_lead(D, pair); }
 // Tail units of a causal tile: the extra cost of its diagonal key tiles
 // (the last tu, partly masked; a wave whose rows end early waits for the
 // others at each of them).  A per-workgroup timing fit at the headline
