@@ -66,10 +66,12 @@ int fa_internal_hip_fail(hipError_t e);
 // It forms Dl from O and dO itself and writes it to dl (no fa_bwd_prep).
 // ws / ws_bytes: scratch for the stream schedule's partial sums (its size
 // from fa_internal_dq8_bytes; with less, one workgroup per query tile).
+// mask3: the local-window + global-token rule as {causal, window, nglobal}
+// (one workgroup per tile over its key list), or null.
 bool fa_internal_bwd_dq8(const void *q, const void *k, const void *v, const void *o,
                          const void *dout, const float *lse, float *dl, void *dq, int Nq, int Nk,
                          int BH, int D, int dtype, bool causal, float c, float scale, void *ws,
-                         size_t ws_bytes, void *stream, hipError_t *err);
+                         size_t ws_bytes, const int *mask3, void *stream, hipError_t *err);
 size_t fa_internal_dq8_bytes(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, bool causal);
 // dK and dV on the same machinery (fa_fwd.hip), same cases; false otherwise.
 // Below two key tiles per compute unit it needs the stream schedule's
@@ -552,18 +554,19 @@ hipError_t launch_bwd(const BwdArgs &a) {
   const float c = a.scale * kLog2e;
   const bool vl = a.cu_q != nullptr;
   hipError_t e = hipSuccess;
-  // Dense problems at D = 64 and 128: dQ first, on the pipelined kernel,
-  // which also writes Dl; otherwise the row terms come from fa_bwd_prep and
-  // dQ from fa_bwd_dq after dK/dV.
+  // Dense and masked problems at D = 64 and 128: dQ first, on the pipelined
+  // kernel, which also writes Dl; otherwise the row terms come from
+  // fa_bwd_prep and dQ from fa_bwd_dq after dK/dV.
   bool done_q = false;
-  if constexpr (!MASKED && (D == 64 || D == 128)) {
+  if constexpr (D == 64 || D == 128) {
     if (!vl) {
       constexpr bool of32 = std::is_same<OT, float>::value;
       constexpr int code = std::is_same<T, __bf16>::value ? (of32 ? FA_BF16_OF32 : FA_BF16)
                                                           : (of32 ? FA_F16_OF32 : FA_F16);
+      const int mask3[3] = {a.mk.causal, a.mk.window, a.mk.nglobal};
       done_q = fa_internal_bwd_dq8(a.q, a.k, a.v, a.o, a.dout, a.lse, a.dl, a.dq, a.Nq, a.Nk,
                                    a.BH, D, code, CAUSAL, c, a.scale, a.dqws, a.dqws_bytes,
-                                   a.stream, &e);
+                                   MASKED ? mask3 : nullptr, a.stream, &e);
       if (done_q && e != hipSuccess) return e;
     }
   }

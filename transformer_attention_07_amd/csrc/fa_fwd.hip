@@ -1530,14 +1530,20 @@ struct DqLayout {
 // its query's row of both, the other half in lane l ^ 32), and the piece
 // that starts at the tile's first key tile stores it to dl for the dK/dV
 // pass, which runs after this one.
-template <typename T, typename OT, int D, bool CAUSAL>
+//
+// MASKED: the local-window + global-token rule mk; the tile's key tiles are
+// the list kl (its entries [kt0, kt1) are list indices), a block with no
+// visible pair is skipped and the others test each score against the rule
+// where some pair of the block is hidden.
+template <typename T, typename OT, int D, bool CAUSAL, bool MASKED = false>
 __device__ __forceinline__ void dq8_run(const T *__restrict__ q, const T *__restrict__ k,
                                         const T *__restrict__ v, const T *__restrict__ o,
                                         const T *__restrict__ dout,
                                         const float *__restrict__ lse, float *__restrict__ dl,
                                         OT *__restrict__ dq, float *__restrict__ ws, int Nq,
                                         int Nk, float c, float scale, const PipeItem it,
-                                        bool reuse) {
+                                        bool reuse, const Mask mk = Mask{},
+                                        const KeyList kl = KeyList{}) {
   typedef DqLayout<T, D> L;
   typedef Dma8<T, D, T, L> DM;
   typedef typename Mma<T>::frag frag;
@@ -1579,8 +1585,11 @@ __device__ __forceinline__ void dq8_run(const T *__restrict__ q, const T *__rest
   float dd = 0.f;  // Dl of this lane's query (0 past Nq: O and dO read as zero)
   const int kt0 = it.kt0;
   const int ntiles = it.kt1 - it.kt0;
-  // last 32-key block (absolute) with a key this wave's queries see
-  const int lastb = CAUSAL ? min(2 * it.kt1 - 1, (qw + 31) / 32) : 2 * it.kt1 - 1;
+  // key tile of entry v (MASKED: of the list)
+  auto kt_act = [&](int v) { return MASKED ? (v < kl.n1 ? v : kl.b0 + (v - kl.n1)) : v; };
+  // last 32-key block (absolute; MASKED: in list order, the list's last)
+  // with a key this wave's queries may see
+  const int lastb = (CAUSAL && !MASKED) ? min(2 * it.kt1 - 1, (qw + 31) / 32) : 2 * it.kt1 - 1;
 
   u32x4 qraw[QF], draw[QF], oraw[QF];
 #pragma unroll
@@ -1590,8 +1599,8 @@ __device__ __forceinline__ void dq8_run(const T *__restrict__ q, const T *__rest
     draw[f] = load16_async(do_rs, off);
     oraw[f] = load16_async(o_rs, off);
   }
-  dm.issue(k_rs, v_rs, kt0, 0, kt0, 0);
-  if (ntiles > 1) dm.issue(k_rs, v_rs, kt0 + 1, 1, kt0 + 1, 1);
+  dm.issue(k_rs, v_rs, kt_act(kt0), 0, kt_act(kt0), 0);
+  if (ntiles > 1) dm.issue(k_rs, v_rs, kt_act(kt0 + 1), 1, kt_act(kt0 + 1), 1);
   frag qf[QF], dof[QF];
   f32x16 acc[NDB];
 #pragma unroll
@@ -1602,8 +1611,10 @@ __device__ __forceinline__ void dq8_run(const T *__restrict__ q, const T *__rest
       // tiles r and r+1 have landed, and every wave is done with the stages
       // of tiles r-2 and r-1, which tiles r+2 and r+3 now take
       ring_barrier<0>();
-      if (r + 2 < ntiles) dm.issue(k_rs, v_rs, kt0 + r + 2, (r + 2) & 3, kt0 + r + 2, (r + 2) & 3);
-      if (r + 3 < ntiles) dm.issue(k_rs, v_rs, kt0 + r + 3, (r + 3) & 3, kt0 + r + 3, (r + 3) & 3);
+      if (r + 2 < ntiles)
+        dm.issue(k_rs, v_rs, kt_act(kt0 + r + 2), (r + 2) & 3, kt_act(kt0 + r + 2), (r + 2) & 3);
+      if (r + 3 < ntiles)
+        dm.issue(k_rs, v_rs, kt_act(kt0 + r + 3), (r + 3) & 3, kt_act(kt0 + r + 3), (r + 3) & 3);
       if (r == 0) {
         float part = 0.f;
 #pragma unroll
@@ -1625,6 +1636,8 @@ __device__ __forceinline__ void dq8_run(const T *__restrict__ q, const T *__rest
     }
     const int b = 2 * (kt0 + r) + h;
     if (b > lastb) continue;  // wave-uniform; later blocks are past it too
+    const int k0 = MASKED ? kt_act(b >> 1) * kBN + (b & 1) * 32 : 32 * b;
+    if (MASKED && !mk.any(qw, qw + 31, k0, k0 + 31)) continue;  // wave-uniform
     const int st = r & 3;
     const lds_char *kp = ring + st * L::K_BYTES + h * 32 * L::SK * 16;
     const lds_char *vp = ring + st * L::V_BYTES + h * 32 * L::SV * 16;
@@ -1636,18 +1649,20 @@ __device__ __forceinline__ void dq8_run(const T *__restrict__ q, const T *__rest
       sc = Mma<T>::mma(kf, qf[f], sc);
       dp = Mma<T>::mma(vf, dof[f], dp);
     }
-    const int k0 = 32 * b;
     // wave-uniform, and taken as a branch (the compiler had turned the
     // per-score test into selects on every block: +130 VALU per block)
-    const int need_mask =
-        __builtin_amdgcn_readfirstlane((k0 + 32 > Nk) || (CAUSAL && k0 + 31 > qw) ? 1 : 0);
+    const int need_mask = __builtin_amdgcn_readfirstlane(
+        (k0 + 32 > Nk) ||
+                (MASKED ? !mk.all(qw, qw + 31, k0, k0 + 31) : (CAUSAL && k0 + 31 > qw))
+            ? 1
+            : 0);
     float ds[16];
     if (need_mask) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = k0 + acc_row(e, g);
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], c, -l2));
-        if (key >= Nk || (CAUSAL && key > my_q)) p = 0.f;
+        if (key >= Nk || (MASKED ? !mk.visible(my_q, key) : (CAUSAL && key > my_q))) p = 0.f;
         ds[e] = p * (dp[e] - dd);
       }
     } else {
@@ -1718,17 +1733,35 @@ __device__ __forceinline__ void dq8_run(const T *__restrict__ q, const T *__rest
 // ws is never written here (every item is a whole tile); it is passed as an
 // argument because this compiler crashes on the constant null pointer that
 // the never-taken partial store would otherwise see.
-template <typename T, typename OT, int D, bool CAUSAL>
+//
+// MASKED: the tile walks its key_list under the rule mk; a tile that sees no
+// key gets dQ = 0 and Dl = 0 (nothing reads the Dl of such rows).
+template <typename T, typename OT, int D, bool CAUSAL, bool MASKED = false>
 __global__ __launch_bounds__(kThreads8) void fa_bwd_dq8(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ o, const T *__restrict__ dout, const float *__restrict__ lse,
     float *__restrict__ dl, OT *__restrict__ dq, float *__restrict__ ws, int Nq, int Nk, int BH,
-    int nqt, float c, float scale) {
+    int nqt, float c, float scale, Mask mk) {
   FA_DBG_BEGIN();
   const WorkItem wi = work_item(BH, nqt, CAUSAL, 128);
-  const int kend = CAUSAL ? min(Nk, wi.q0 + 128) : Nk;
-  const PipeItem it = {wi.bh, wi.q0, 0, (kend + kBN - 1) / kBN, -1};
-  dq8_run<T, OT, D, CAUSAL>(q, k, v, o, dout, lse, dl, dq, ws, Nq, Nk, c, scale, it, false);
+  if constexpr (MASKED) {
+    int n;
+    const KeyList kl = key_list(mk, wi.q0, 128, Nq, Nk, &n);
+    if (n == 0) {
+      const int rows = min(128, Nq - wi.q0);
+      const size_t r0 = (size_t)wi.bh * Nq + wi.q0;
+      for (int i = threadIdx.x; i < rows * D; i += kThreads8) dq[r0 * D + i] = (OT)0.f;
+      for (int i = threadIdx.x; i < rows; i += kThreads8) dl[r0 + i] = 0.f;
+      return;
+    }
+    const PipeItem it = {wi.bh, wi.q0, 0, n, -1};
+    dq8_run<T, OT, D, CAUSAL, true>(q, k, v, o, dout, lse, dl, dq, ws, Nq, Nk, c, scale, it,
+                                    false, mk, kl);
+  } else {
+    const int kend = CAUSAL ? min(Nk, wi.q0 + 128) : Nk;
+    const PipeItem it = {wi.bh, wi.q0, 0, (kend + kBN - 1) / kBN, -1};
+    dq8_run<T, OT, D, CAUSAL>(q, k, v, o, dout, lse, dl, dq, ws, Nq, Nk, c, scale, it, false);
+  }
 }
 
 // The stream-K schedule of the forward (128-row tiles): each workgroup walks
@@ -3340,8 +3373,16 @@ bool dq8_plan(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, bool causal, int cu
 template <typename T, typename OT, int D, bool CAUSAL>
 hipError_t launch_dq8(const void *q, const void *k, const void *v, const void *o,
                       const void *dout, const float *lse, float *dl, void *dq, int Nq, int Nk,
-                      int BH,
-                      float c, float scale, const StreamPlan *sp, float *ws, hipStream_t s) {
+                      int BH, float c, float scale, const StreamPlan *sp, float *ws,
+                      const Mask *mk, hipStream_t s) {
+  if (mk) {  // the window mask: one workgroup per tile over its key list
+    const int nqt = (Nq + 127) / 128;
+    hipLaunchKernelGGL((fa_bwd_dq8<T, OT, D, CAUSAL, true>), dim3((unsigned)(BH * nqt)),
+                       dim3(kThreads8), 0, s, (const T *)q, (const T *)k, (const T *)v,
+                       (const T *)o, (const T *)dout, lse, dl, (OT *)dq, ws, Nq, Nk, BH, nqt, c,
+                       scale, *mk);
+    return hipGetLastError();
+  }
   if (sp) {
     ChunkStarts cs;
     CutList cuts;
@@ -3358,23 +3399,25 @@ hipError_t launch_dq8(const void *q, const void *k, const void *v, const void *o
   const int nqt = (Nq + 127) / 128;
   hipLaunchKernelGGL((fa_bwd_dq8<T, OT, D, CAUSAL>), dim3((unsigned)(BH * nqt)),
                      dim3(kThreads8), 0, s, (const T *)q, (const T *)k, (const T *)v,
-                     (const T *)o, (const T *)dout, lse, dl, (OT *)dq, ws, Nq, Nk, BH, nqt, c, scale);
+                     (const T *)o, (const T *)dout, lse, dl, (OT *)dq, ws, Nq, Nk, BH, nqt, c,
+                     scale, Mask{});
   return hipGetLastError();
 }
 template <typename T, typename OT>
 hipError_t dq8_d(int D, bool causal, const void *q, const void *k, const void *v,
                  const void *o, const void *dout, const float *lse, float *dl, void *dq, int Nq,
                  int Nk,
-                 int BH, float c, float scale, const StreamPlan *sp, float *ws, hipStream_t s) {
+                 int BH, float c, float scale, const StreamPlan *sp, float *ws, const Mask *mk,
+                 hipStream_t s) {
   if (D == 64)
     return causal ? launch_dq8<T, OT, 64, true>(q, k, v, o, dout, lse, dl, dq, Nq, Nk, BH, c,
-                                                scale, sp, ws, s)
+                                                scale, sp, ws, mk, s)
                   : launch_dq8<T, OT, 64, false>(q, k, v, o, dout, lse, dl, dq, Nq, Nk, BH, c,
-                                                 scale, sp, ws, s);
+                                                 scale, sp, ws, mk, s);
   return causal ? launch_dq8<T, OT, 128, true>(q, k, v, o, dout, lse, dl, dq, Nq, Nk, BH, c, scale,
-                                               sp, ws, s)
+                                               sp, ws, mk, s)
                 : launch_dq8<T, OT, 128, false>(q, k, v, o, dout, lse, dl, dq, Nq, Nk, BH, c,
-                                                scale, sp, ws, s);
+                                                scale, sp, ws, mk, s);
 }
 }  // namespace
 
@@ -3510,32 +3553,41 @@ __attribute__((visibility("hidden"))) size_t fa_internal_dkv8_bytes(int64_t BH, 
 __attribute__((visibility("hidden"))) bool fa_internal_bwd_dq8(
     const void *q, const void *k, const void *v, const void *o, const void *dout,
     const float *lse, float *dl, void *dq, int Nq, int Nk, int BH, int D, int dtype, bool causal,
-    float c, float scale, void *ws, size_t ws_bytes, void *stream, hipError_t *err) {
+    float c, float scale, void *ws, size_t ws_bytes, const int *mask3, void *stream,
+    hipError_t *err) {
   if (D != 64 && D != 128) return false;
+  Mask mval{};
+  const Mask *mk = nullptr;
+  if (mask3) {
+    mval.causal = mask3[0];
+    mval.window = mask3[1];
+    mval.nglobal = mask3[2];
+    mk = &mval;
+  }
   hipStream_t s = (hipStream_t)stream;
   int cus = 0;
   StreamPlan sp;
   const StreamPlan *use = nullptr;
-  if (ws && device_cus(&cus) == FA_OK && dq8_plan(BH, Nq, Nk, D, causal, cus, sp) &&
+  if (!mk && ws && device_cus(&cus) == FA_OK && dq8_plan(BH, Nq, Nk, D, causal, cus, sp) &&
       ws_bytes >= (size_t)2 * sp.G * 128 * (size_t)D * 4)
     use = &sp;
   float *w = (float *)ws;
   switch (dtype) {
     case FA_BF16:
       *err = dq8_d<__bf16, __bf16>(D, causal, q, k, v, o, dout, lse, dl, dq, Nq, Nk, BH, c, scale,
-                                   use, w, s);
+                                   use, w, mk, s);
       return true;
     case FA_BF16_OF32:
       *err = dq8_d<__bf16, float>(D, causal, q, k, v, o, dout, lse, dl, dq, Nq, Nk, BH, c, scale,
-                                  use, w, s);
+                                  use, w, mk, s);
       return true;
     case FA_F16:
       *err = dq8_d<_Float16, _Float16>(D, causal, q, k, v, o, dout, lse, dl, dq, Nq, Nk, BH, c,
-                                       scale, use, w, s);
+                                       scale, use, w, mk, s);
       return true;
     case FA_F16_OF32:
       *err = dq8_d<_Float16, float>(D, causal, q, k, v, o, dout, lse, dl, dq, Nq, Nk, BH, c,
-                                    scale, use, w, s);
+                                    scale, use, w, mk, s);
       return true;
     default: return false;
   }
