@@ -5,7 +5,7 @@ counters and waits, no arithmetic).  Covered: the pipelined forward on the
 stream-K schedule in both layouts (pair-split 128-row tiles, 256-row tiles)
 and on the one-workgroup-per-tile grid, the masked and variable-length
 forwards, and the D = 64 / 128 backward with its dQ and dK/dV kernels on
-both schedules."""
+both schedules and under the window mask."""
 import ctypes
 import math
 
@@ -109,3 +109,15 @@ def test_backward(libs, shape, causal):
     _same(libs, lambda: fa.bwd(q, k, v, o, lse, g, causal=causal, scale=scale,
                                grad_dtype=torch.float32),
           f"bwd B{B} H{H} Nq{Nq} Nk{Nk} D{D} causal={causal}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_masked_backward(libs, D):
+    q, k, v = _dev(*gen_qkv(1, 2, 1000, 1000, D, seed=7500 + D, dtype="bf16"))
+    g = gen_grad_out(1, 2, 1000, D, seed=7600 + D, dtype="bf16").to(DEV)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = fa.fwd_masked(q, k, v, 200, 16, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    _same(libs, lambda: fa.bwd(q, k, v, o, lse, g, causal=True, scale=scale,
+                               grad_dtype=torch.float32, window=200, nglobal=16),
+          f"masked bwd D{D} window 200, 16 global")

@@ -79,7 +79,7 @@ size_t fa_internal_dq8_bytes(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, bool
 bool fa_internal_bwd_dkdv8(const void *q, const void *k, const void *v, const void *dout,
                            const float *lse, const float *dl, void *dk, void *dv, int Nq, int Nk,
                            int BH, int D, int dtype, bool causal, float c, float scale, void *ws,
-                           size_t ws_bytes, void *stream, hipError_t *err);
+                           size_t ws_bytes, const int *mask3, void *stream, hipError_t *err);
 size_t fa_internal_dkv8_bytes(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, bool causal);
 
 #include "tiles.h"
@@ -587,14 +587,16 @@ hipError_t launch_bwd(const BwdArgs &a) {
   const int nqt = ((vl ? a.maxq : a.Nq) + kTile - 1) / kTile;
   const int slices = vl ? a.BH * a.S : a.BH;
   bool done_kv = false;
-  if constexpr (!MASKED && (D == 64 || D == 128)) {
+  if constexpr (D == 64 || D == 128) {
     if (!vl) {
       constexpr bool of32 = std::is_same<OT, float>::value;
       constexpr int code = std::is_same<T, __bf16>::value ? (of32 ? FA_BF16_OF32 : FA_BF16)
                                                           : (of32 ? FA_F16_OF32 : FA_F16);
+      const int mask3[3] = {a.mk.causal, a.mk.window, a.mk.nglobal};
       done_kv = fa_internal_bwd_dkdv8(a.q, a.k, a.v, a.dout, a.lse, (const float *)a.dl, a.dk,
                                       a.dv, a.Nq, a.Nk, a.BH, D, code, CAUSAL, c, a.scale,
-                                      a.dqws, a.dqws_bytes, a.stream, &e);
+                                      a.dqws, a.dqws_bytes, MASKED ? mask3 : nullptr, a.stream,
+                                      &e);
       if (done_kv && e != hipSuccess) return e;
     }
   }

@@ -1855,14 +1855,20 @@ struct DkvLayout {
 // query tiles (64 rows) [it.kt0, it.kt1).  it.slot < 0: the whole tile,
 // stores dK (times scale) and dV in OT; else fp32 partial sums of dK^T and
 // dV^T to workspace slot it.slot (128 keys of D each, dK then dV).
-template <typename T, typename OT, int D, bool CAUSAL>
+//
+// MASKED: the local-window + global-token rule mk; the item's query tiles
+// are the list ql (entries [kt0, kt1) are list indices, query_list), blocks
+// with no visible pair are skipped, and every score is tested against the
+// rule through the interval of queries that see the lane's key.
+template <typename T, typename OT, int D, bool CAUSAL, bool MASKED = false>
 __device__ __forceinline__ void dkv8_run(const T *__restrict__ q, const T *__restrict__ k,
                                          const T *__restrict__ v, const T *__restrict__ dout,
                                          const float *__restrict__ lse,
                                          const float *__restrict__ dl, OT *__restrict__ dk,
                                          OT *__restrict__ dv, float *__restrict__ ws, int Nq,
                                          int Nk, float c, float scale, const PipeItem it,
-                                         bool reuse) {
+                                         bool reuse, const Mask mk = Mask{},
+                                         const KeyList ql = KeyList{}) {
   typedef DkvLayout<T, D> L;
   typedef Dma8<T, D, T, L> DM;
   typedef typename Mma<T>::frag frag;
@@ -1914,6 +1920,8 @@ __device__ __forceinline__ void dkv8_run(const T *__restrict__ q, const T *__res
 
   const int qt0 = it.kt0;
   const int ntiles = it.kt1 - it.kt0;
+  // query tile of entry v (MASKED: of the list)
+  auto qt_act = [&](int v) { return MASKED ? (v < ql.n1 ? v : ql.b0 + (v - ql.n1)) : v; };
 
   u32x4 kraw[QF], vraw[QF];
 #pragma unroll
@@ -1922,8 +1930,8 @@ __device__ __forceinline__ void dkv8_run(const T *__restrict__ q, const T *__res
     kraw[f] = load16_async(k_rs, off);
     vraw[f] = load16_async(v_rs, off);
   }
-  issue(qt0, 0);
-  if (ntiles > 1) issue(qt0 + 1, 1);
+  issue(qt_act(qt0), 0);
+  if (ntiles > 1) issue(qt_act(qt0 + 1), 1);
   frag kf[QF], vf[QF];
   f32x16 dka[NDB], dva[NDB];
 #pragma unroll
@@ -1936,8 +1944,8 @@ __device__ __forceinline__ void dkv8_run(const T *__restrict__ q, const T *__res
   // the stages of tiles r-2 and r-1, which tiles r+2 and r+3 now take
   auto ring_step = [&](int r) {
     ring_barrier<0>();
-    if (r + 2 < ntiles) issue(qt0 + r + 2, (r + 2) & 3);
-    if (r + 3 < ntiles) issue(qt0 + r + 3, (r + 3) & 3);
+    if (r + 2 < ntiles) issue(qt_act(qt0 + r + 2), (r + 2) & 3);
+    if (r + 3 < ntiles) issue(qt_act(qt0 + r + 3), (r + 3) & 3);
   };
   ring_step(0);
 #pragma unroll
@@ -1948,6 +1956,25 @@ __device__ __forceinline__ void dkv8_run(const T *__restrict__ q, const T *__res
   }
 
   const int mk4 = my_k - 4 * g;
+  // MASKED: query i = sx + 4g (sx = i0 + 8 r4 + e) sees key my_k iff
+  // (unsigned)(sx - bl) <= bs, or (non-causal) sx < gq: causal, the queries
+  // [my_k, my_k + window - 1], or every query from my_k on for a global key;
+  // non-causal, [my_k - window + 1, my_k + window - 1], every query for a
+  // global key, and the global queries [0, nglobal) for any key.
+  int bl = 0, gq = 0;
+  unsigned bs = 0;
+  if constexpr (MASKED) {
+    // CAUSAL is the rule's own (the host dispatches on mk.causal)
+    const bool gk = my_k < mk.nglobal;
+    if (CAUSAL) {
+      bl = mk4;
+      bs = gk ? 0x7fffffffu : (unsigned)(mk.window - 1);
+    } else {
+      bl = mk4 - (mk.window - 1);
+      bs = gk ? 0xffffffffu : (unsigned)(2 * mk.window - 2);
+      gq = mk.nglobal - 4 * g;
+    }
+  }
   // Step r: query tile qt0 + r, this wave's 32 rows (i0 .. i0 + 31).  Blocks
   // with no visible pair are skipped; every other step takes the causal test
   // (two instructions a score).  Rows past Nq need no mask: their Q, dO, L
@@ -1955,9 +1982,9 @@ __device__ __forceinline__ void dkv8_run(const T *__restrict__ q, const T *__res
   // of dO and Q in dV and dK.
   auto step = [&](int r) {
     if (r > 0 && (r & 1) == 0) ring_step(r);
-    const int i0 = (qt0 + r) * kBN + 32 * h;  // this wave's first query of the tile
+    const int i0 = qt_act(qt0 + r) * kBN + 32 * h;  // this wave's first query of the tile
     // wave-uniform: no query of the block sees a key of this wave
-    if (CAUSAL && i0 + 31 < kw) return;
+    if (MASKED ? !mk.any(i0, i0 + 31, kw, kw + 31) : (CAUSAL && i0 + 31 < kw)) return;
     if (i0 >= Nq) return;
     const int st = r & 3;
     const lds_char *qp = ring + st * L::K_BYTES + h * 32 * L::SK * 16;
@@ -1990,8 +2017,12 @@ __device__ __forceinline__ void dkv8_run(const T *__restrict__ q, const T *__res
               __builtin_fmaf(sc[x], c, -lv[e] * 1.4426950408889634f));
           // query i0 + 8 r4 + e + 4g against key my_k: the wave-uniform
           // part of the query index against a per-lane constant
-          if constexpr (CAUSAL)
+          if constexpr (MASKED) {
+            const int sx = i0 + 8 * r4 + e;
+            if (!((unsigned)(sx - bl) <= bs || (!CAUSAL && sx < gq))) pr = 0.f;
+          } else if constexpr (CAUSAL) {
             if (mk4 > i0 + 8 * r4 + e) pr = 0.f;
+          }
           p[4 * hr + e] = pr;
           ds[4 * hr + e] = pr * (dpv[x] - dv4[e]);
         }
@@ -2068,20 +2099,59 @@ __device__ __forceinline__ void dkv8_run(const T *__restrict__ q, const T *__res
 
 // One workgroup per 128-key tile, lowest keys (the most queries) first
 // under the causal mask.
-template <typename T, typename OT, int D, bool CAUSAL>
+// Query tiles (64 rows) that see some key of [k0, k1] under the window rule
+// mk, as a list like key_list's: query tiles [0, n1), then from b0 on.
+// Causal: the queries from k0 to k1 + window - 1, or to the end when the
+// tile holds a global key.  Non-causal: every query for a global key;
+// otherwise the global queries [0, nglobal) and the band [k0 - window + 1,
+// k1 + window - 1].  *n is the list's length (0: no query sees the keys).
+__device__ __forceinline__ KeyList query_list(const Mask &mk, int k0, int k1, int Nq, int *n) {
+  const int nqt = (Nq + kBN - 1) / kBN;
+  if (k0 < mk.nglobal) {  // a global key: every query from k0 on (causal) or every query
+    const int qa = mk.causal ? min(k0 / kBN, nqt) : 0;
+    *n = nqt - qa;
+    return {0, qa};
+  }
+  const int n1 = mk.causal ? 0 : (min(mk.nglobal, Nq) + kBN - 1) / kBN;
+  const int blo = mk.causal ? k0 : max(0, k0 - mk.window + 1);
+  const int bhi = min(Nq - 1, k1 + mk.window - 1);
+  if (blo > bhi) {  // no band query
+    *n = n1;
+    return {n1, n1};
+  }
+  const int b0 = blo / kBN, b1 = bhi / kBN + 1;
+  if (b0 <= n1) {  // the ranges meet: one range from tile 0
+    *n = max(n1, b1);
+    return {*n, *n};
+  }
+  *n = n1 + (b1 - b0);
+  return {n1, b0};
+}
+
+// One workgroup per 128-key tile, lowest keys (the most queries) first
+// under the causal mask.  MASKED: the tile walks its query_list.
+template <typename T, typename OT, int D, bool CAUSAL, bool MASKED = false>
 __global__ __launch_bounds__(kThreads8) void fa_bwd_dkdv8(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dl,
     OT *__restrict__ dk, OT *__restrict__ dv, float *__restrict__ ws, int Nq, int Nk, int BH,
-    int nkt, float c, float scale) {
+    int nkt, float c, float scale, Mask mk) {
   FA_DBG_BEGIN();
   const int id = blockIdx.x;
   const int bh = id % BH, t = id / BH;  // causal: t ascending = longest first
   const int k0 = t * 128;
   const int nq = (Nq + kBN - 1) / kBN;
-  const int qa = CAUSAL ? min(k0 / kBN, nq) : 0;  // first query tile with a visible key
-  const PipeItem it = {bh, k0, qa, nq, -1};
-  if (qa >= nq) {  // no query sees these keys: zero gradients
+  int qa = CAUSAL ? min(k0 / kBN, nq) : 0;  // first query tile with a visible key
+  int qn = nq;                              // end of the query tiles
+  KeyList ql{};
+  if constexpr (MASKED) {
+    int n;
+    ql = query_list(mk, k0, min(k0 + 127, Nk - 1), Nq, &n);
+    qa = 0;
+    qn = n;
+  }
+  const PipeItem it = {bh, k0, qa, qn, -1};
+  if (qa >= qn) {  // no query sees these keys: zero gradients
     for (int i = threadIdx.x; i < 128 * D; i += kThreads8) {
       const int key = k0 + i / D;
       if (key < Nk) {
@@ -2091,7 +2161,8 @@ __global__ __launch_bounds__(kThreads8) void fa_bwd_dkdv8(
     }
     return;
   }
-  dkv8_run<T, OT, D, CAUSAL>(q, k, v, dout, lse, dl, dk, dv, ws, Nq, Nk, c, scale, it, false);
+  dkv8_run<T, OT, D, CAUSAL, MASKED>(q, k, v, dout, lse, dl, dk, dv, ws, Nq, Nk, c, scale, it,
+                                     false, mk, ql);
 }
 
 // The stream-K schedule of the forward applied to key tiles: the plan's
@@ -3444,7 +3515,15 @@ template <typename T, typename OT, int D, bool CAUSAL>
 hipError_t launch_dkv8(const void *q, const void *k, const void *v, const void *dout,
                        const float *lse, const float *dl, void *dk, void *dv, int Nq, int Nk,
                        int BH, float c, float scale, const StreamPlan *sp, float *ws,
-                       hipStream_t s) {
+                       const Mask *mk, hipStream_t s) {
+  if (mk) {  // the window mask: one workgroup per key tile over its query list
+    const int nkt = (Nk + 127) / 128;
+    hipLaunchKernelGGL((fa_bwd_dkdv8<T, OT, D, CAUSAL, true>), dim3((unsigned)(BH * nkt)),
+                       dim3(kThreads8), 0, s, (const T *)q, (const T *)k, (const T *)v,
+                       (const T *)dout, lse, dl, (OT *)dk, (OT *)dv, (float *)nullptr, Nq, Nk,
+                       BH, nkt, c, scale, *mk);
+    return hipGetLastError();
+  }
   if (sp) {
     ChunkStarts cs;
     CutList cuts;
@@ -3464,31 +3543,45 @@ hipError_t launch_dkv8(const void *q, const void *k, const void *v, const void *
   hipLaunchKernelGGL((fa_bwd_dkdv8<T, OT, D, CAUSAL>), dim3((unsigned)(BH * nkt)),
                      dim3(kThreads8), 0, s, (const T *)q, (const T *)k, (const T *)v,
                      (const T *)dout, lse, dl, (OT *)dk, (OT *)dv, (float *)nullptr, Nq, Nk, BH,
-                     nkt, c, scale);
+                     nkt, c, scale, Mask{});
   return hipGetLastError();
 }
 template <typename T, typename OT>
 hipError_t dkv8_d(int D, bool causal, const void *q, const void *k, const void *v,
                   const void *dout, const float *lse, const float *dl, void *dk, void *dv,
                   int Nq, int Nk, int BH, float c, float scale, const StreamPlan *sp, float *ws,
-                  hipStream_t s) {
+                  const Mask *mk, hipStream_t s) {
   if (D == 64)
     return causal ? launch_dkv8<T, OT, 64, true>(q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH, c,
-                                                 scale, sp, ws, s)
+                                                 scale, sp, ws, mk, s)
                   : launch_dkv8<T, OT, 64, false>(q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH,
-                                                  c, scale, sp, ws, s);
+                                                  c, scale, sp, ws, mk, s);
   return causal ? launch_dkv8<T, OT, 128, true>(q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH, c,
-                                                scale, sp, ws, s)
+                                                scale, sp, ws, mk, s)
                 : launch_dkv8<T, OT, 128, false>(q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH, c,
-                                                 scale, sp, ws, s);
+                                                 scale, sp, ws, mk, s);
 }
 }  // namespace
 
 __attribute__((visibility("hidden"))) bool fa_internal_bwd_dkdv8(
     const void *q, const void *k, const void *v, const void *dout, const float *lse,
     const float *dl, void *dk, void *dv, int Nq, int Nk, int BH, int D, int dtype, bool causal,
-    float c, float scale, void *ws, size_t ws_bytes, void *stream, hipError_t *err) {
+    float c, float scale, void *ws, size_t ws_bytes, const int *mask3, void *stream,
+    hipError_t *err) {
   if (D != 64 && D != 128) return false;
+  Mask mval{};
+  const Mask *mk = nullptr;
+  if (mask3) {
+    // non-causal at D = 128 the window test's three per-lane values push the
+    // kernel past 256 VGPRs (a reload inside the loop): the 64-key kernel
+    // keeps that case
+    if (!mask3[0] && D == 128) return false;
+    mval.causal = mask3[0];
+    mval.window = mask3[1];
+    mval.nglobal = mask3[2];
+    mk = &mval;
+    causal = mval.causal != 0;  // the kernel's CAUSAL is the rule's
+  }
   // One round of 128-key workgroups leaves the causal triangle unbalanced:
   // from two tiles per compute unit on, longest-first rounds balance it
   // (measured: B8 N4096 D128 causal, one tile per unit, 211 us against 201
@@ -3499,7 +3592,7 @@ __attribute__((visibility("hidden"))) bool fa_internal_bwd_dkdv8(
   if (device_cus(&cus) != FA_OK) return false;
   StreamPlan sp;
   const StreamPlan *use = nullptr;
-  if ((int64_t)BH * ((Nk + 127) / 128) < 2LL * cus) {
+  if (!mk && (int64_t)BH * ((Nk + 127) / 128) < 2LL * cus) {
     if (!ws || !dkv8_plan(BH, Nq, Nk, D, causal, cus, sp) ||
         ws_bytes < (size_t)2 * sp.G * 2 * 128 * (size_t)D * 4)
       return false;
@@ -3510,19 +3603,19 @@ __attribute__((visibility("hidden"))) bool fa_internal_bwd_dkdv8(
   switch (dtype) {
     case FA_BF16:
       *err = dkv8_d<__bf16, __bf16>(D, causal, q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH, c,
-                                    scale, use, w, s);
+                                    scale, use, w, mk, s);
       return true;
     case FA_BF16_OF32:
       *err = dkv8_d<__bf16, float>(D, causal, q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH, c,
-                                   scale, use, w, s);
+                                   scale, use, w, mk, s);
       return true;
     case FA_F16:
       *err = dkv8_d<_Float16, _Float16>(D, causal, q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH,
-                                        c, scale, use, w, s);
+                                        c, scale, use, w, mk, s);
       return true;
     case FA_F16_OF32:
       *err = dkv8_d<_Float16, float>(D, causal, q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH, c,
-                                     scale, use, w, s);
+                                     scale, use, w, mk, s);
       return true;
     default: return false;
   }
@@ -3563,6 +3656,7 @@ __attribute__((visibility("hidden"))) bool fa_internal_bwd_dq8(
     mval.window = mask3[1];
     mval.nglobal = mask3[2];
     mk = &mval;
+    causal = mval.causal != 0;  // the kernel's CAUSAL is the rule's (longest tiles first)
   }
   hipStream_t s = (hipStream_t)stream;
   int cus = 0;
