@@ -461,8 +461,11 @@ def main() -> int:
                 raise RuntimeError(f"forward failed: {fa.fa_status_str(st)}")
             g = gen_grad_out(MB, MH, MN, MD, seed=2602, dtype="bf16").to(dev)
             dq, dk, dv = (torch.empty(x.shape, dtype=out_dt, device=dev) for x in (q, k, v))
-            ws_bytes = MB * MH * MN * 4
-            bws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+            st, ws_bytes = fa.fa_bwd_masked_workspace_size(MB, MH, MN, MN, MD, 1, W, G, code)
+            if st != 0:
+                raise RuntimeError(f"fa_bwd_masked_workspace_size failed: "
+                                   f"{fa.fa_status_str(st)}")
+            bws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
             argv = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                     g.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), MB, MH, MN, MN,
                     MD, scale, 1, W, G, code, bws.data_ptr(), ws_bytes, sp)

@@ -215,6 +215,41 @@ def test_bwd_workspace_size():
     assert fa.fa_bwd_workspace_size(2, 3, 100, 90, 64, 1, fa.FA_F32)[0] == fa.FA_ERR_DTYPE
 
 
+def test_bwd_masked_workspace_size():
+    """The row terms, plus (rounded up to 256 bytes) the parts of the key
+    tiles that hold global keys: B*H*ceil(min(G, Nk)/128) tiles, each cut
+    into ceil(query tiles / cap) parts of two 128 x D fp32 blocks, cap being
+    a band tile's query-tile count (causal: (127 + W - 1) // 64 + 2), at
+    least 32.  No device."""
+    ws = fa.fa_bwd_masked_workspace_size
+    lb = 8 * 32768 * 4
+    # B1 H8 N32768 D128 causal, window 512 + 32 global: 512 query tiles,
+    # cap 32 -> 16 parts of one tile per head
+    assert ws(1, 8, 32768, 32768, 128, 1, 512, 32, fa.FA_BF16) == (
+        fa.FA_OK, lb + 8 * 16 * 2 * 128 * 128 * 4)
+    # window 2048 + 128 global: cap (127 + 2047) // 64 + 2 = 35 -> 15 parts
+    assert ws(1, 8, 32768, 32768, 128, 1, 2048, 128, fa.FA_BF16) == (
+        fa.FA_OK, lb + 8 * 15 * 2 * 128 * 128 * 4)
+    # 300 global keys: three split tiles; D = 64
+    assert ws(1, 2, 4096, 4096, 64, 1, 100, 300, fa.FA_BF16) == (
+        fa.FA_OK, 2 * 4096 * 4 + 2 * 3 * 2 * 2 * 128 * 64 * 4)
+    # non-causal: the band cap counts both sides and the global query tiles
+    # (1 + (127 + 126) // 64 + 2 = 6 -> 32); D = 128 non-causal runs whole
+    assert ws(1, 2, 4096, 4096, 64, 0, 64, 40, fa.FA_BF16) == (
+        fa.FA_OK, 2 * 4096 * 4 + 2 * 2 * 2 * 128 * 64 * 4)
+    assert ws(1, 2, 4096, 4096, 128, 0, 64, 40, fa.FA_BF16) == (fa.FA_OK, 2 * 4096 * 4)
+    # no global key, a short sequence, or a band as long as the sequence:
+    # nothing to split
+    assert ws(1, 8, 32768, 32768, 128, 1, 512, 0, fa.FA_BF16) == (fa.FA_OK, lb)
+    assert ws(1, 2, 2048, 2048, 128, 1, 64, 16, fa.FA_BF16) == (fa.FA_OK, 2 * 2048 * 4)
+    assert ws(1, 2, 8192, 8192, 128, 1, 8192, 16, fa.FA_BF16) == (fa.FA_OK, 2 * 8192 * 4)
+    # D = 16 and 32 run the earlier kernels
+    assert ws(1, 2, 4096, 4096, 32, 1, 100, 300, fa.FA_BF16) == (fa.FA_OK, 2 * 4096 * 4)
+    assert ws(1, 2, 4096, 4096, 64, 1, 0, 3, fa.FA_BF16)[0] == fa.FA_ERR_SHAPE
+    assert ws(1, 2, 4096, 4096, 64, 1, 5, -1, fa.FA_BF16)[0] == fa.FA_ERR_SHAPE
+    assert ws(1, 2, 4096, 4096, 48, 1, 5, 3, fa.FA_BF16)[0] == fa.FA_ERR_HEAD_DIM
+
+
 # --- fa_fwd_varlen: validation precedes device work --------------------------
 CQ, CK = 0xB0000000, 0xC0000000
 

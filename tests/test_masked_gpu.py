@@ -165,6 +165,63 @@ def test_masked_bwd_unequal_lengths(causal):
     compare_bwd(1, 1, 300, 500, 64, causal, 40, 3, seed=2801)
 
 
+@pytest.mark.parametrize("D,causal,Nq,Nk,window,nglobal", [
+    (64, True, 4096, 4096, 100, 300),
+    (64, False, 4096, 4096, 64, 40),
+    (128, True, 5000, 5000, 256, 130),
+    (128, True, 4500, 3000, 200, 129),
+])
+def test_masked_bwd_split_global_tiles(D, causal, Nq, Nk, window, nglobal):
+    """Key tiles holding global keys are cut into parts whose partial sums a
+    merge kernel adds (fa_bwd_masked_workspace_size bytes of workspace):
+    every key of those tiles, ragged last tiles and global counts that are
+    not multiples of 128, against the oracle; and the same gradients with
+    only the row terms as workspace (the tiles run whole), to the same
+    bound."""
+    from workloads import gen_grad_out
+
+    st, full = fa.fa_bwd_masked_workspace_size(1, 2, Nq, Nk, D, causal, window, nglobal,
+                                               fa.FA_BF16)
+    assert st == fa.FA_OK and full > 2 * Nq * 4, "the split must be in play"
+    nsp = (min(nglobal, Nk) + 127) // 128
+    kr = np.union1d(np.concatenate([np.arange(min(nsp * 128, Nk)),
+                                    Nk + np.arange(min(nsp * 128, Nk))]),
+                    np.random.default_rng(3000 + D).integers(0, 2 * Nk, 128))
+    qr = np.union1d(np.random.default_rng(3001 + D).integers(0, 2 * Nq, 128),
+                    np.array([0, nglobal - 1, Nq - 1, Nq, 2 * Nq - 1]))
+    compare_bwd(1, 2, Nq, Nk, D, causal, window, nglobal, seed=3010 + D, qrows=qr, krows=kr)
+
+    # the unsplit grid: workspace of the row terms only
+    q, k, v = gen_qkv(1, 2, Nq, Nk, D, seed=3010 + D, dtype="bf16")
+    g = gen_grad_out(1, 2, Nq, D, seed=3011 + D, dtype="bf16")
+    scale = 1.0 / math.sqrt(D)
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, g))
+    o, lse = fa.fwd_masked(qd, kd, vd, window, nglobal, causal=causal, scale=scale)
+    split = fa.bwd(qd, kd, vd, o, lse, gd, causal=causal, scale=scale,
+                   grad_dtype=torch.float32, window=window, nglobal=nglobal)
+    whole = [torch.empty_like(x) for x in split]
+    lb = 2 * Nq * 4
+    ws = torch.empty(lb, dtype=torch.uint8, device=DEV)
+    st = fa.fa_bwd_masked(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(),
+                          lse.data_ptr(), gd.data_ptr(), whole[0].data_ptr(),
+                          whole[1].data_ptr(), whole[2].data_ptr(), 1, 2, Nq, Nk, D, scale,
+                          int(causal), window, nglobal, fa.FA_BF16_OF32, ws.data_ptr(), lb,
+                          torch.cuda.current_stream().cuda_stream)
+    assert st == fa.FA_OK, fa.fa_status_str(st)
+    torch.cuda.synchronize()
+    assert torch.equal(split[0], whole[0]), "dQ does not depend on the split"
+    qn, kn, vn, gn = (t.double().numpy() for t in (q, k, v, g))
+    ref = oracle.attention_bwd_masked(qn, kn, vn, gn, scale, causal, window, nglobal,
+                                      qrows=qr, krows=kr, magnitudes=True)
+    sel = torch.as_tensor(kr)
+    for n in (1, 2):
+        x = whole[n].reshape(-1, D)[sel].double().cpu().numpy()
+        bound = 2 * 2.0 ** -8 * ref[n + 3] + 1e-6 * float(ref[n + 3].max()) + 1e-30
+        ratio = float((np.abs(x - ref[n]) / bound).max())
+        _log(f"  unsplit {'dK' if n == 1 else 'dV'}: worst error/bound {ratio:.3f}")
+        assert ratio <= 1.0
+
+
 def _two_head_rows(H, N, n, seed):
     """n flat rows of heads 2 and 5 (of [1, H, N, ...] tensors), drawn with a
     seeded generator: the oracle then needs the statistics of two heads."""

@@ -23,6 +23,8 @@ C-ABI mirrors (same names and meaning as include/fa.h):
     fa_fwd_fp8(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Nq, Nk, D, scale,
                descale_q, descale_k, descale_v, causal, out_f32, stream) -> status
     fa_bwd_workspace_size(B, H, Nq, Nk, D, causal, dtype) -> (status, bytes)
+    fa_bwd_masked_workspace_size(B, H, Nq, Nk, D, causal, window, nglobal, dtype)
+        -> (status, bytes)
     fa_bwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_ptr,
            B, H, Nq, Nk, D, scale, causal, dtype, ws_ptr, ws_bytes, stream)
         -> status
@@ -65,7 +67,7 @@ __all__ = [
     "FA_ERR_SCALE", "FA_ERR_ALIGN", "FA_ERR_HIP", "FA_ERR_OVERLAP", "FA_ERR_WORKSPACE",
     "LIBRARY", "DEBUG_LIBRARY", "EXPORTS", "library", "debug_library", "fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws",
     "fa_fwd_noalloc", "fa_fwd_varlen", "fa_fwd_varlen_workspace_size", "fa_fwd_varlen_ws", "fa_fwd_masked", "fa_fwd_fp8", "fa_fwd_fp8_workspace_size", "fa_fwd_fp8_ws",
-    "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_varlen", "fa_bwd_masked", "fa_status_str",
+    "fa_bwd_workspace_size", "fa_bwd_masked_workspace_size", "fa_bwd", "fa_bwd_varlen", "fa_bwd_masked", "fa_status_str",
     "fa_last_hip_error", "fa_version", "fwd", "fwd_varlen", "fwd_masked", "fwd_fp8", "bwd", "bwd_varlen", "FaError",
 ]
 
@@ -82,7 +84,8 @@ FA_F32, FA_BF16, FA_BF16_OF32, FA_F16, FA_F16_OF32 = 0, 1, 2, 3, 4
 # Every symbol include/fa.h declares.
 EXPORTS = ("fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws", "fa_fwd_noalloc", "fa_fwd_varlen",
            "fa_fwd_varlen_workspace_size", "fa_fwd_varlen_ws", "fa_fwd_masked", "fa_fwd_fp8",
-           "fa_fwd_fp8_workspace_size", "fa_fwd_fp8_ws", "fa_bwd_workspace_size", "fa_bwd",
+           "fa_fwd_fp8_workspace_size", "fa_fwd_fp8_ws", "fa_bwd_workspace_size",
+           "fa_bwd_masked_workspace_size", "fa_bwd",
            "fa_bwd_varlen", "fa_bwd_masked",
            "fa_status_str", "fa_last_hip_error", "fa_version")
 
@@ -160,6 +163,10 @@ def _bind(path: str) -> ctypes.CDLL:
     lib.fa_bwd_workspace_size.restype = ctypes.c_int
     lib.fa_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int,
                                           ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+    lib.fa_bwd_masked_workspace_size.restype = ctypes.c_int
+    lib.fa_bwd_masked_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, i64,
+                                                 i64, ctypes.c_int,
+                                                 ctypes.POINTER(ctypes.c_size_t)]
     lib.fa_bwd.restype = ctypes.c_int
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                            ctypes.c_float, ctypes.c_int, ctypes.c_int, vp, ctypes.c_size_t,
@@ -270,6 +277,16 @@ def fa_bwd_workspace_size(B, H, Nq, Nk, D, causal, dtype) -> Tuple[int, int]:
     n = ctypes.c_size_t(0)
     st = int(library().fa_bwd_workspace_size(B, H, Nq, Nk, D, int(causal), int(dtype),
                                              ctypes.byref(n)))
+    return st, int(n.value)
+
+
+def fa_bwd_masked_workspace_size(B, H, Nq, Nk, D, causal, window, nglobal,
+                                 dtype) -> Tuple[int, int]:
+    """Raw C call; returns (status, workspace bytes)."""
+    n = ctypes.c_size_t(0)
+    st = int(library().fa_bwd_masked_workspace_size(B, H, Nq, Nk, D, int(causal), int(window),
+                                                    int(nglobal), int(dtype),
+                                                    ctypes.byref(n)))
     return st, int(n.value)
 
 
@@ -443,7 +460,11 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, scale: Optional[float] = None
     own_stream = stream is None
     if own_stream:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    st, nbytes = fa_bwd_workspace_size(B, H, Nq, Nk, D, causal, code)
+    if window is None:
+        st, nbytes = fa_bwd_workspace_size(B, H, Nq, Nk, D, causal, code)
+    else:
+        st, nbytes = fa_bwd_masked_workspace_size(B, H, Nq, Nk, D, causal, window, nglobal,
+                                                  code)
     if st == FA_OK:
         ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
         if not own_stream:

@@ -81,6 +81,11 @@ bool fa_internal_bwd_dkdv8(const void *q, const void *k, const void *v, const vo
                            int BH, int D, int dtype, bool causal, float c, float scale, void *ws,
                            size_t ws_bytes, const int *mask3, void *stream, hipError_t *err);
 size_t fa_internal_dkv8_bytes(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, bool causal);
+// Under the window rule mask3 the key tiles that hold global keys are cut
+// into parts whose partial sums go to ws (this many bytes; with less ws
+// they run whole).
+size_t fa_internal_masked_dkv8_bytes(int64_t BH, int64_t Nq, int64_t Nk, int64_t D,
+                                     const int *mask3);
 
 #include "tiles.h"
 
@@ -681,6 +686,23 @@ int fa_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t 
   return FA_OK;
 }
 
+int fa_bwd_masked_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+                                 int causal, int64_t window, int64_t nglobal, int dtype,
+                                 size_t *bytes) {
+  if (!bytes) return FA_ERR_NULLPTR;
+  *bytes = 0;
+  if (window < 1 || nglobal < 0) return FA_ERR_SHAPE;
+  const int st = check_shape(B, H, Nq, Nk, D, dtype);
+  if (st != FA_OK) return st;
+  const size_t lb = (size_t)(B * H * Nq) * sizeof(float);
+  const int64_t lim = (int64_t)1 << 31;
+  const int mask3[3] = {causal != 0, (int)(window < lim ? window : lim - 1),
+                        (int)(nglobal < lim ? nglobal : lim - 1)};
+  const size_t extra = fa_internal_masked_dkv8_bytes(B * H, Nq, Nk, D, mask3);
+  *bytes = extra ? (lb + 255) / 256 * 256 + extra : lb;
+  return FA_OK;
+}
+
 static int bwd_dense(const void *q, const void *k, const void *v, const void *o,
                      const float *lse, const void *dout, void *dq, void *dk, void *dv,
                      int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, float scale,
@@ -704,7 +726,14 @@ static int bwd_dense(const void *q, const void *k, const void *v, const void *o,
   // past the row terms (rounded up to 256 bytes): the stream schedules'
   // partial sums, used when the workspace holds them
   const size_t off = (lb + 255) / 256 * 256;
-  const size_t extra = mk ? 0 : stream_bytes(BH, Nq, Nk, D, causal != 0);
+  int mask3[3] = {0, 1, 0};
+  if (mk) {
+    mask3[0] = mk->causal;
+    mask3[1] = mk->window;
+    mask3[2] = mk->nglobal;
+  }
+  const size_t extra = mk ? fa_internal_masked_dkv8_bytes(BH, Nq, Nk, D, mask3)
+                          : stream_bytes(BH, Nq, Nk, D, causal != 0);
   const size_t used = extra && workspace_bytes >= off + extra ? off + extra : need;
   // written buffers against every buffer of the call
   const void *outs[4] = {dq, dk, dv, workspace};

@@ -2129,28 +2129,50 @@ __device__ __forceinline__ KeyList query_list(const Mask &mk, int k0, int k1, in
 }
 
 // One workgroup per 128-key tile, lowest keys (the most queries) first
-// under the causal mask.  MASKED: the tile walks its query_list.
+// under the causal mask.  MASKED: the tile walks its query_list; with
+// S > 1 the key tiles [0, nsp) (those that hold global keys, whose lists
+// run over nearly every query tile) come first, each as S workgroups that
+// take consecutive parts of its list and store fp32 partial sums to
+// workspace slot (bh * nsp + t) * S + p (fa_merge_dkv8_split adds them).
 template <typename T, typename OT, int D, bool CAUSAL, bool MASKED = false>
 __global__ __launch_bounds__(kThreads8) void fa_bwd_dkdv8(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dl,
     OT *__restrict__ dk, OT *__restrict__ dv, float *__restrict__ ws, int Nq, int Nk, int BH,
-    int nkt, float c, float scale, Mask mk) {
+    int nkt, float c, float scale, Mask mk, int nsp, int S) {
   FA_DBG_BEGIN();
   const int id = blockIdx.x;
-  const int bh = id % BH, t = id / BH;  // causal: t ascending = longest first
+  const int bh = id % BH, u = id / BH;  // causal: u ascending = longest first
+  int t = u, p = -1;                    // key tile, and its part (split tiles)
+  if (u < nsp * S) {
+    t = u / S;
+    p = u % S;
+  } else {
+    t = u - nsp * S + nsp;
+  }
   const int k0 = t * 128;
   const int nq = (Nq + kBN - 1) / kBN;
   int qa = CAUSAL ? min(k0 / kBN, nq) : 0;  // first query tile with a visible key
   int qn = nq;                              // end of the query tiles
+  int slot = -1;
   KeyList ql{};
   if constexpr (MASKED) {
     int n;
     ql = query_list(mk, k0, min(k0 + 127, Nk - 1), Nq, &n);
     qa = 0;
     qn = n;
+    if (p >= 0) {
+      qa = (int)((int64_t)p * n / S);
+      qn = (int)((int64_t)(p + 1) * n / S);
+      slot = (bh * nsp + t) * S + p;
+    }
   }
-  const PipeItem it = {bh, k0, qa, qn, -1};
+  const PipeItem it = {bh, k0, qa, qn, slot};
+  if (qa >= qn && slot >= 0) {  // an empty part: zero partial sums
+    float *w = ws + (size_t)slot * 2 * 128 * D;
+    for (int i = threadIdx.x; i < 2 * 128 * D; i += kThreads8) w[i] = 0.f;
+    return;
+  }
   if (qa >= qn) {  // no query sees these keys: zero gradients
     for (int i = threadIdx.x; i < 128 * D; i += kThreads8) {
       const int key = k0 + i / D;
@@ -2193,32 +2215,26 @@ __global__ __launch_bounds__(kThreads8) void fa_bwd_dkdv8_stream(
   }
 }
 
-// Sums the partial dK^T and dV^T of each cut key tile's pieces (in piece
-// order) and stores scale times the dK sum and the dV sum.
-template <typename OT, int D>
-__global__ __launch_bounds__(kThreads) void fa_merge_dkv8(const float *__restrict__ ws,
-                                                          OT *__restrict__ dk,
-                                                          OT *__restrict__ dv, int Nk,
-                                                          float scale, int nkt, bool causal,
-                                                          CutList cuts) {
+// Sums the partial dK^T and dV^T of np pieces of key tile kt (piece kk in
+// workspace slot slot_of(kk), in piece order), rows of part part of the
+// tile, and stores scale times the dK sum and the dV sum.
+template <typename OT, int D, typename F>
+__device__ __forceinline__ void merge_dkv_rows(const float *__restrict__ ws,
+                                               OT *__restrict__ dk, OT *__restrict__ dv,
+                                               int Nk, float scale, int bh, int kt, int np,
+                                               int part, F slot_of) {
   constexpr int C4 = D / 4;
   constexpr int RPP = kThreads / C4;
   constexpr int ROWS = merge_rows<D>();
-  constexpr int SPLIT = 128 / ROWS;
   constexpr int NR = ROWS / RPP;
   static_assert(NR >= 1 && ROWS % RPP == 0, "merge tiling");
-  const uint32_t w0 = cuts.w[2 * (blockIdx.x / SPLIT)];
-  const uint32_t w1 = cuts.w[2 * (blockIdx.x / SPLIT) + 1];
-  const int bh = (int)(w0 & 0xffffu), tp = (int)(w0 >> 16);
-  const int kt = causal ? nkt - 1 - tp : tp;
-  const int np = cut_pieces(w1);
   const int c4 = threadIdx.x % C4;
-  const int r0 = (blockIdx.x % SPLIT) * ROWS + threadIdx.x / C4;
+  const int r0 = part * ROWS + threadIdx.x / C4;
   f32x4 ak[NR], av[NR];
 #pragma unroll
   for (int i = 0; i < NR; ++i) ak[i] = av[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int kk = 0; kk < np; ++kk) {
-    const float *w = ws + (size_t)cut_slot(w1, kk) * 2 * 128 * D;
+    const float *w = ws + (size_t)slot_of(kk) * 2 * 128 * D;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       const size_t e = (size_t)(r0 + i * RPP) * D + 4 * c4;
@@ -2234,6 +2250,38 @@ __global__ __launch_bounds__(kThreads) void fa_merge_dkv8(const float *__restric
       store4<OT>(dv + ((size_t)bh * Nk + key) * D + 4 * c4, av[i]);
     }
   }
+}
+
+// The cut key tiles of the stream schedule (fa_bwd_dkdv8_stream).
+template <typename OT, int D>
+__global__ __launch_bounds__(kThreads) void fa_merge_dkv8(const float *__restrict__ ws,
+                                                          OT *__restrict__ dk,
+                                                          OT *__restrict__ dv, int Nk,
+                                                          float scale, int nkt, bool causal,
+                                                          CutList cuts) {
+  constexpr int SPLIT = 128 / merge_rows<D>();
+  const uint32_t w0 = cuts.w[2 * (blockIdx.x / SPLIT)];
+  const uint32_t w1 = cuts.w[2 * (blockIdx.x / SPLIT) + 1];
+  const int bh = (int)(w0 & 0xffffu), tp = (int)(w0 >> 16);
+  const int kt = causal ? nkt - 1 - tp : tp;
+  merge_dkv_rows<OT, D>(ws, dk, dv, Nk, scale, bh, kt, cut_pieces(w1), blockIdx.x % SPLIT,
+                        [&](int kk) { return cut_slot(w1, kk); });
+}
+
+// The split key tiles of the masked grid (fa_bwd_dkdv8 with S > 1): tiles
+// [0, nsp) of every slice, S parts each.
+template <typename OT, int D>
+__global__ __launch_bounds__(kThreads) void fa_merge_dkv8_split(const float *__restrict__ ws,
+                                                                OT *__restrict__ dk,
+                                                                OT *__restrict__ dv, int Nk,
+                                                                float scale, int BH, int nsp,
+                                                                int S) {
+  constexpr int SPLIT = 128 / merge_rows<D>();
+  const int c = blockIdx.x / SPLIT;
+  const int bh = c % BH, kt = c / BH;
+  const int base = (bh * nsp + kt) * S;
+  merge_dkv_rows<OT, D>(ws, dk, dv, Nk, scale, bh, kt, S, blockIdx.x % SPLIT,
+                        [&](int kk) { return base + kk; });
 }
 
 // ---------------------------------------------------------------------------
@@ -3511,17 +3559,59 @@ bool dkv8_plan(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, bool causal, int c
   return plan_rows(BH, Nk, Nq, 128, kKvLead(causal), 0, causal, cus, sp);
 }
 
+// Split of the masked grid.  A key tile that holds a global key meets every
+// query tile from its first key on (every query tile without the causal
+// rule), while a band tile meets about (127 + window) / 64 of them (plus the
+// global query tiles and the other side of the band without the causal
+// rule): one workgroup for such a tile would outlast the whole grid.  Those
+// tiles are cut into S parts of about a band tile's list each, at least 32
+// query tiles; S is limited to what the workspace holds, and below 2 the
+// tiles run whole.
+struct KvSplit {
+  int nsp = 0;  // split key tiles: [0, nsp) of every slice
+  int S = 1;    // parts per split tile
+};
+KvSplit dkv8_split(const Mask &mk, int64_t BH, int64_t Nq, int64_t Nk, int64_t D,
+                   size_t avail) {
+  KvSplit r;
+  const int64_t g = mk.nglobal < Nk ? mk.nglobal : Nk;
+  if (g <= 0 || Nq <= 0) return r;
+  const int64_t nqt = (Nq + kBN - 1) / kBN;
+  const int64_t w = mk.window;
+  const int64_t gq = mk.nglobal < Nq ? mk.nglobal : Nq;
+  int64_t band = mk.causal ? (127 + w - 1) / kBN + 2
+                           : (gq + kBN - 1) / kBN + (127 + 2 * (w - 1)) / kBN + 2;
+  if (band > nqt) band = nqt;
+  const int64_t cap = band > 32 ? band : 32;
+  const int64_t nsp = (g + 127) / 128;
+  const size_t per = (size_t)(BH * nsp) * 2 * 128 * (size_t)D * 4;  // one part of each
+  int64_t S = (nqt + cap - 1) / cap;
+  if ((size_t)S > avail / per) S = (int64_t)(avail / per);
+  if (S < 2) return r;
+  r.nsp = (int)nsp;
+  r.S = (int)S;
+  return r;
+}
+
 template <typename T, typename OT, int D, bool CAUSAL>
 hipError_t launch_dkv8(const void *q, const void *k, const void *v, const void *dout,
                        const float *lse, const float *dl, void *dk, void *dv, int Nq, int Nk,
                        int BH, float c, float scale, const StreamPlan *sp, float *ws,
-                       const Mask *mk, hipStream_t s) {
-  if (mk) {  // the window mask: one workgroup per key tile over its query list
+                       size_t ws_bytes, const Mask *mk, hipStream_t s) {
+  if (mk) {  // the window mask: one workgroup per key tile (or part) over its query list
     const int nkt = (Nk + 127) / 128;
-    hipLaunchKernelGGL((fa_bwd_dkdv8<T, OT, D, CAUSAL, true>), dim3((unsigned)(BH * nkt)),
+    const KvSplit sl = dkv8_split(*mk, BH, Nq, Nk, D, ws ? ws_bytes : 0);
+    const int units = nkt + sl.nsp * (sl.S - 1);
+    hipLaunchKernelGGL((fa_bwd_dkdv8<T, OT, D, CAUSAL, true>), dim3((unsigned)(BH * units)),
                        dim3(kThreads8), 0, s, (const T *)q, (const T *)k, (const T *)v,
-                       (const T *)dout, lse, dl, (OT *)dk, (OT *)dv, (float *)nullptr, Nq, Nk,
-                       BH, nkt, c, scale, *mk);
+                       (const T *)dout, lse, dl, (OT *)dk, (OT *)dv, ws, Nq, Nk, BH, nkt, c,
+                       scale, *mk, sl.nsp, sl.S);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || sl.S < 2) return e;
+    hipLaunchKernelGGL((fa_merge_dkv8_split<OT, D>),
+                       dim3((unsigned)(BH * sl.nsp * (128 / merge_rows<D>()))), dim3(kThreads),
+                       0, s, (const float *)ws, (OT *)dk, (OT *)dv, Nk, scale, BH, sl.nsp,
+                       sl.S);
     return hipGetLastError();
   }
   if (sp) {
@@ -3543,23 +3633,23 @@ hipError_t launch_dkv8(const void *q, const void *k, const void *v, const void *
   hipLaunchKernelGGL((fa_bwd_dkdv8<T, OT, D, CAUSAL>), dim3((unsigned)(BH * nkt)),
                      dim3(kThreads8), 0, s, (const T *)q, (const T *)k, (const T *)v,
                      (const T *)dout, lse, dl, (OT *)dk, (OT *)dv, (float *)nullptr, Nq, Nk, BH,
-                     nkt, c, scale, Mask{});
+                     nkt, c, scale, Mask{}, 0, 1);
   return hipGetLastError();
 }
 template <typename T, typename OT>
 hipError_t dkv8_d(int D, bool causal, const void *q, const void *k, const void *v,
                   const void *dout, const float *lse, const float *dl, void *dk, void *dv,
                   int Nq, int Nk, int BH, float c, float scale, const StreamPlan *sp, float *ws,
-                  const Mask *mk, hipStream_t s) {
+                  size_t ws_bytes, const Mask *mk, hipStream_t s) {
   if (D == 64)
     return causal ? launch_dkv8<T, OT, 64, true>(q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH, c,
-                                                 scale, sp, ws, mk, s)
+                                                 scale, sp, ws, ws_bytes, mk, s)
                   : launch_dkv8<T, OT, 64, false>(q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH,
-                                                  c, scale, sp, ws, mk, s);
+                                                  c, scale, sp, ws, ws_bytes, mk, s);
   return causal ? launch_dkv8<T, OT, 128, true>(q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH, c,
-                                                scale, sp, ws, mk, s)
+                                                scale, sp, ws, ws_bytes, mk, s)
                 : launch_dkv8<T, OT, 128, false>(q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH, c,
-                                                 scale, sp, ws, mk, s);
+                                                 scale, sp, ws, ws_bytes, mk, s);
 }
 }  // namespace
 
@@ -3603,22 +3693,37 @@ __attribute__((visibility("hidden"))) bool fa_internal_bwd_dkdv8(
   switch (dtype) {
     case FA_BF16:
       *err = dkv8_d<__bf16, __bf16>(D, causal, q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH, c,
-                                    scale, use, w, mk, s);
+                                    scale, use, w, ws_bytes, mk, s);
       return true;
     case FA_BF16_OF32:
       *err = dkv8_d<__bf16, float>(D, causal, q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH, c,
-                                   scale, use, w, mk, s);
+                                   scale, use, w, ws_bytes, mk, s);
       return true;
     case FA_F16:
       *err = dkv8_d<_Float16, _Float16>(D, causal, q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH,
-                                        c, scale, use, w, mk, s);
+                                        c, scale, use, w, ws_bytes, mk, s);
       return true;
     case FA_F16_OF32:
       *err = dkv8_d<_Float16, float>(D, causal, q, k, v, dout, lse, dl, dk, dv, Nq, Nk, BH, c,
-                                     scale, use, w, mk, s);
+                                     scale, use, w, ws_bytes, mk, s);
       return true;
     default: return false;
   }
+}
+
+// Bytes of dK/dV partials the split of the masked grid uses for this
+// problem and rule (0 when the pipelined kernel does not take the rule, or
+// no tile is split).
+__attribute__((visibility("hidden"))) size_t fa_internal_masked_dkv8_bytes(
+    int64_t BH, int64_t Nq, int64_t Nk, int64_t D, const int *mask3) {
+  if ((D != 64 && D != 128) || (!mask3[0] && D == 128)) return 0;
+  Mask m{};
+  m.causal = mask3[0];
+  m.window = mask3[1];
+  m.nglobal = mask3[2];
+  const KvSplit sl = dkv8_split(m, BH, Nq, Nk, D, ~(size_t)0);
+  if (sl.S < 2) return 0;
+  return (size_t)(BH * sl.nsp) * sl.S * 2 * 128 * (size_t)D * 4;
 }
 
 // Bytes of dQ partials the stream schedule may need for this problem on a
@@ -3788,7 +3893,7 @@ hipError_t dispatch_fp8(const Launch &a, int D, bool causal) {
 
 extern "C" {
 
-int fa_version(void) { return 300; }
+int fa_version(void) { return 400; }
 
 #if FA_DEBUG_BARRIERS
 // include/fa_debug.h: ring-barrier mismatches counted on the current device.
