@@ -320,6 +320,38 @@ int fa_fwd_masked(const void *q, const void *k, const void *v, void *o, float *l
                   int dtype, void *stream);
 
 /*
+ * fa_fwd_masked_workspace_size -- device scratch bytes that let
+ * fa_fwd_masked_ws split long tiles (written to *bytes; 0 when nothing is
+ * split).  Without the causal rule a 256-row tile that holds a global
+ * query sees every key, far more than a band tile: the first
+ * ceil(min(nglobal, Nq) / 256) tiles of every (batch, head) are cut into
+ * P parts along the keys (each about a band tile's key range, at least 32
+ * key tiles of 64), each leaving 256 x (D + 4) fp32 values; the size is
+ * B * H * ceil(min(nglobal, Nq) / 256) * P * 256 * (D + 4) * 4 bytes.
+ * The query needs no device.  Returns FA_OK, FA_ERR_NULLPTR, FA_ERR_SHAPE
+ * (also window < 1 or nglobal < 0), FA_ERR_HEAD_DIM or FA_ERR_DTYPE.
+ */
+int fa_fwd_masked_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                                 int64_t D, int causal, int64_t window,
+                                 int64_t nglobal, int dtype, size_t *bytes);
+
+/*
+ * fa_fwd_masked_ws -- fa_fwd_masked with a caller-owned workspace (device
+ * memory, 16-byte aligned, overlapping no other argument; NULL or fewer
+ * than fa_fwd_masked_workspace_size bytes: the long tiles run whole, as in
+ * fa_fwd_masked).  The split parts' partial results are combined by a
+ * second kernel in part order (deterministic; the same results as the
+ * unsplit call within the rounding of that combination).  Calls that share
+ * a workspace must not overlap.  Arguments and status codes otherwise as
+ * fa_fwd_masked (FA_ERR_ALIGN, FA_ERR_OVERLAP for the workspace).
+ */
+int fa_fwd_masked_ws(const void *q, const void *k, const void *v, void *o,
+                     float *lse, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                     int64_t D, float scale, int causal, int64_t window,
+                     int64_t nglobal, int dtype, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/*
  * fa_fwd_fp8 -- the forward pass with FP8 inputs (page "FlashAttention技术
  * 演进全景图" §5.3 names FP8 support; the pages give no rules, so this
  * library reads it as): q, k, v hold OCP e4m3 values (one byte each,

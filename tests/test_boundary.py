@@ -215,6 +215,28 @@ def test_bwd_workspace_size():
     assert fa.fa_bwd_workspace_size(2, 3, 100, 90, 64, 1, fa.FA_F32)[0] == fa.FA_ERR_DTYPE
 
 
+def test_fwd_masked_workspace_size():
+    """Non-causal masks with global tokens: the 256-row tiles holding global
+    queries, ceil(min(G, Nq)/256) per (batch, head), each cut into
+    ceil(key tiles / cap) parts of 256 x (D + 4) fp32, cap the band tile's
+    key-tile count ((G key tiles) + (255 + 2 (W - 1)) // 64 + 2), at least
+    32.  Causal masks and G = 0 need nothing.  No device."""
+    ws = fa.fa_fwd_masked_workspace_size
+    # B1 H8 N32768 D128, window 512 + 32 global: 512 key tiles, band 1 + 19 +
+    # 2 = 22 -> cap 32 -> 16 parts of one tile per head
+    assert ws(1, 8, 32768, 32768, 128, 0, 512, 32, fa.FA_BF16) == (
+        fa.FA_OK, 8 * 16 * 256 * 132 * 4)
+    # 300 global tokens: two split tiles; 79 key tiles -> 3 parts
+    assert ws(1, 2, 5000, 5000, 64, 0, 64, 300, fa.FA_BF16) == (
+        fa.FA_OK, 2 * 2 * 3 * 256 * 68 * 4)
+    assert ws(1, 8, 32768, 32768, 128, 1, 512, 32, fa.FA_BF16) == (fa.FA_OK, 0)
+    assert ws(1, 8, 32768, 32768, 128, 0, 512, 0, fa.FA_BF16) == (fa.FA_OK, 0)
+    assert ws(1, 2, 2048, 2048, 128, 0, 64, 16, fa.FA_BF16) == (fa.FA_OK, 0)
+    assert ws(1, 2, 4096, 4096, 64, 0, 0, 3, fa.FA_BF16)[0] == fa.FA_ERR_SHAPE
+    assert ws(1, 2, 4096, 4096, 48, 0, 5, 3, fa.FA_BF16)[0] == fa.FA_ERR_HEAD_DIM
+    assert ws(1, 2, 4096, 4096, 64, 0, 5, 3, fa.FA_F32)[0] == fa.FA_ERR_DTYPE
+
+
 def test_bwd_masked_workspace_size():
     """The row terms, plus (rounded up to 256 bytes) the parts of the key
     tiles that hold global keys: B*H*ceil(min(G, Nk)/128) tiles, each cut

@@ -109,6 +109,53 @@ def test_masked_long_sequence_sampled():
     compare(B, H, N, N, 128, True, 2048, 128, seed=2601, rows=rows)
 
 
+@pytest.mark.parametrize("D,Nq,Nk,window,nglobal,dtype", [
+    (64, 4096, 4096, 64, 40, "bf16"),
+    (128, 4096, 4096, 100, 1, "bf16"),
+    (128, 5000, 5000, 256, 300, "bf16"),
+    (64, 4500, 3000, 200, 260, "f16"),
+])
+def test_masked_split_global_query_tiles(D, Nq, Nk, window, nglobal, dtype):
+    """Without the causal rule the 256-row tiles holding global queries see
+    every key; with fa_fwd_masked_workspace_size bytes they run as parts
+    whose partial results a second kernel combines.  Every row of those
+    tiles (both outputs, fp32 and 16-bit) against the oracle, and the
+    unsplit entry (fa_fwd_masked, no workspace) to the same bound."""
+    B, H = 1, 2
+    st, nbytes = fa.fa_fwd_masked_workspace_size(B, H, Nq, Nk, D, False, window, nglobal,
+                                                 fa.FA_BF16)
+    assert st == fa.FA_OK and nbytes > 0, "the split must be in play"
+    nsp = (min(nglobal, Nq) + 255) // 256
+    tile_rows = np.arange(min(nsp * 256, Nq))
+    rows = np.union1d(np.concatenate([tile_rows, Nq + tile_rows]),
+                      np.random.default_rng(3100 + D).integers(0, B * H * Nq, 128))
+    compare(B, H, Nq, Nk, D, False, window, nglobal, seed=3110 + D, dtype=dtype, rows=rows)
+
+    q, k, v = gen_qkv(B, H, Nq, Nk, D, seed=3110 + D, dtype=dtype)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+    code = fa.FA_BF16_OF32 if dtype == "bf16" else fa.FA_F16_OF32
+    o = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=DEV)
+    st = fa.fa_fwd_masked(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(),
+                          lse.data_ptr(), B, H, Nq, Nk, D, 1.0 / math.sqrt(D), 0, window,
+                          nglobal, code, torch.cuda.current_stream().cuda_stream)
+    assert st == fa.FA_OK
+    torch.cuda.synchronize()
+    assert tdt == qd.dtype
+    ro, rl = oracle.attention_masked(q.double().numpy(), k.double().numpy(),
+                                     v.double().numpy(), 1.0 / math.sqrt(D), False, window,
+                                     nglobal, rows=rows)
+    sel = torch.as_tensor(rows)
+    g_o = o.reshape(-1, D)[sel].double().cpu().numpy()
+    g_l = lse.reshape(-1)[sel].double().cpu().numpy()
+    fin = np.isfinite(rl.reshape(-1))
+    err_o = float(np.abs(g_o - ro.reshape(-1, D)).max())
+    err_l = float(np.abs(g_l[fin] - rl.reshape(-1)[fin]).max()) if fin.any() else 0.0
+    _log(f"  unsplit: O {err_o:.2e} L {err_l:.2e}")
+    assert err_o <= 1e-2 and err_l <= 1e-3
+
+
 # --- backward under the mask (fa_bwd_masked) ------------------------------
 def compare_bwd(B, H, Nq, Nk, D, causal, window, nglobal, seed, dtype="bf16", qrows=None,
                 krows=None):

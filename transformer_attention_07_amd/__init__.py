@@ -66,7 +66,7 @@ __all__ = [
     "FA_OK", "FA_ERR_NULLPTR", "FA_ERR_SHAPE", "FA_ERR_HEAD_DIM", "FA_ERR_DTYPE",
     "FA_ERR_SCALE", "FA_ERR_ALIGN", "FA_ERR_HIP", "FA_ERR_OVERLAP", "FA_ERR_WORKSPACE",
     "LIBRARY", "DEBUG_LIBRARY", "EXPORTS", "library", "debug_library", "fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws",
-    "fa_fwd_noalloc", "fa_fwd_varlen", "fa_fwd_varlen_workspace_size", "fa_fwd_varlen_ws", "fa_fwd_masked", "fa_fwd_fp8", "fa_fwd_fp8_workspace_size", "fa_fwd_fp8_ws",
+    "fa_fwd_noalloc", "fa_fwd_varlen", "fa_fwd_varlen_workspace_size", "fa_fwd_varlen_ws", "fa_fwd_masked", "fa_fwd_masked_workspace_size", "fa_fwd_masked_ws", "fa_fwd_fp8", "fa_fwd_fp8_workspace_size", "fa_fwd_fp8_ws",
     "fa_bwd_workspace_size", "fa_bwd_masked_workspace_size", "fa_bwd", "fa_bwd_varlen", "fa_bwd_masked", "fa_status_str",
     "fa_last_hip_error", "fa_version", "fwd", "fwd_varlen", "fwd_masked", "fwd_fp8", "bwd", "bwd_varlen", "FaError",
 ]
@@ -83,7 +83,7 @@ FA_F32, FA_BF16, FA_BF16_OF32, FA_F16, FA_F16_OF32 = 0, 1, 2, 3, 4
 
 # Every symbol include/fa.h declares.
 EXPORTS = ("fa_fwd", "fa_fwd_workspace_size", "fa_fwd_ws", "fa_fwd_noalloc", "fa_fwd_varlen",
-           "fa_fwd_varlen_workspace_size", "fa_fwd_varlen_ws", "fa_fwd_masked", "fa_fwd_fp8",
+           "fa_fwd_varlen_workspace_size", "fa_fwd_varlen_ws", "fa_fwd_masked", "fa_fwd_masked_workspace_size", "fa_fwd_masked_ws", "fa_fwd_fp8",
            "fa_fwd_fp8_workspace_size", "fa_fwd_fp8_ws", "fa_bwd_workspace_size",
            "fa_bwd_masked_workspace_size", "fa_bwd",
            "fa_bwd_varlen", "fa_bwd_masked",
@@ -149,6 +149,14 @@ def _bind(path: str) -> ctypes.CDLL:
     lib.fa_fwd_masked.restype = ctypes.c_int
     lib.fa_fwd_masked.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
                                   ctypes.c_int, i64, i64, ctypes.c_int, vp]
+    lib.fa_fwd_masked_workspace_size.restype = ctypes.c_int
+    lib.fa_fwd_masked_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, i64,
+                                                 i64, ctypes.c_int,
+                                                 ctypes.POINTER(ctypes.c_size_t)]
+    lib.fa_fwd_masked_ws.restype = ctypes.c_int
+    lib.fa_fwd_masked_ws.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                     ctypes.c_float, ctypes.c_int, i64, i64, ctypes.c_int, vp,
+                                     ctypes.c_size_t, vp]
     lib.fa_fwd_fp8.restype = ctypes.c_int
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
                                ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_int,
@@ -247,6 +255,24 @@ def fa_fwd_masked(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, window, nglob
     return int(library().fa_fwd_masked(q, k, v, o, lse, B, H, Nq, Nk, D, float(scale),
                                        int(causal), int(window), int(nglobal), int(dtype),
                                        stream))
+
+
+def fa_fwd_masked_workspace_size(B, H, Nq, Nk, D, causal, window, nglobal,
+                                 dtype) -> Tuple[int, int]:
+    """Raw C call; returns (status, workspace bytes)."""
+    n = ctypes.c_size_t(0)
+    st = int(library().fa_fwd_masked_workspace_size(B, H, Nq, Nk, D, int(causal), int(window),
+                                                    int(nglobal), int(dtype),
+                                                    ctypes.byref(n)))
+    return st, int(n.value)
+
+
+def fa_fwd_masked_ws(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, window, nglobal, dtype,
+                     ws, ws_bytes, stream) -> int:
+    """Raw C call; pointers are integers (device addresses) or None."""
+    return int(library().fa_fwd_masked_ws(q, k, v, o, lse, B, H, Nq, Nk, D, float(scale),
+                                          int(causal), int(window), int(nglobal), int(dtype),
+                                          ws, int(ws_bytes), stream))
 
 
 def fa_fwd_fp8(q, k, v, o, lse, B, H, Nq, Nk, D, scale, dq, dk, dv, causal, out_f32,
@@ -618,8 +644,14 @@ def fwd_masked(q, k, v, window: int, nglobal: int = 0, causal: bool = False,
     lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = fa_fwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                       B, H, Nq, Nk, D, scale, causal, window, nglobal, code, stream)
+    st, nbytes = fa_fwd_masked_workspace_size(B, H, Nq, Nk, D, causal, window, nglobal, code)
+    if st == FA_OK:
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device) if nbytes else None
+        if ws is not None and stream != torch.cuda.current_stream(q.device).cuda_stream:
+            ws.record_stream(torch.cuda.ExternalStream(stream, device=q.device))
+        st = fa_fwd_masked_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              lse.data_ptr(), B, H, Nq, Nk, D, scale, causal, window, nglobal,
+                              code, None if ws is None else ws.data_ptr(), nbytes, stream)
     if st != FA_OK:
         msg = fa_status_str(st)
         if st == FA_ERR_HIP:

@@ -1361,13 +1361,43 @@ template <typename T, typename OT, int D, bool CAUSAL, bool PAIR, bool MASKED = 
 __global__ __launch_bounds__(kThreads8) void fa_fwd_pipe8(
     const KT *__restrict__ q, const KT *__restrict__ k, const T *__restrict__ v,
     OT *__restrict__ o, float *__restrict__ lse, int Nq, int Nk, int BH, int nqt,
-    float c, int negate, Mask mk, float osc) {
+    float c, int negate, Mask mk, float osc, float *__restrict__ ws, int nsp, int S) {
   FA_DBG_BEGIN();
   constexpr int QT = QRows<PAIR>::value;
-  const WorkItem wi = work_item(BH, nqt, CAUSAL, QT);
+  WorkItem wi = work_item(BH, nqt, CAUSAL, QT);
   if constexpr (MASKED) {
+    // Split (S > 1, without the causal rule): the first nsp * S units are
+    // S parts of each of the tiles [0, nsp) of every slice (those holding
+    // global queries, whose lists hold every key tile); part p takes list
+    // entries [p n / S, (p + 1) n / S) and leaves its partial result in
+    // workspace slot (bh * nsp + t) * S + p for fa_merge_masked_split.
+    const int u = blockIdx.x / BH;
+    int p = -1;
+    if (u < nsp * S) {
+      p = u % S;
+      wi.q0 = (u / S) * QT;
+    } else if (nsp > 0) {
+      wi.q0 = (u - nsp * S + nsp) * QT;
+    }
     int n;
     const KeyList kl = key_list(mk, wi.q0, QT, Nq, Nk, &n);
+    const int nslots = BH * nsp * S;
+    if (p >= 0) {
+      const int e0 = (int)((int64_t)p * n / S), e1 = (int)((int64_t)(p + 1) * n / S);
+      const int slot = (wi.bh * nsp + wi.q0 / QT) * S + p;
+      if (e0 >= e1) {  // an empty part: a partial result with no key
+        float *wo = ws + (size_t)slot * QT * D;
+        float *wst = ws + (size_t)nslots * QT * D + (size_t)slot * QT * 4;
+        for (int i = threadIdx.x; i < QT * D; i += kThreads8) wo[i] = 0.f;
+        for (int i = threadIdx.x; i < QT; i += kThreads8)
+          *reinterpret_cast<f32x4 *>(wst + 4 * i) = f32x4{-INFINITY, 0.f, 0.f, 0.f};
+        return;
+      }
+      const PipeItem it = {wi.bh, wi.q0, e0, e1, slot};
+      pipe8_run<T, OT, D, CAUSAL, PAIR, true>(q, k, v, o, lse, ws, Nq, Nk, c, negate, it,
+                                              nslots, mk, kl);
+      return;
+    }
     if (n == 0) {
       const int rows = min(QT, Nq - wi.q0);
       const size_t r0 = (size_t)wi.bh * Nq + wi.q0;
@@ -2601,17 +2631,97 @@ __global__ __launch_bounds__(kThreads) void fa_merge_stream(const float *__restr
 // per merge_rows<D>() rows of every (tile rank, head, sequence); tiles that
 // were not split (or lie past their sequence's end) return at once.  Same
 // rescaling as fa_merge_stream.
+// Combines the partial results of np parts of one tile (part u in slot
+// slot_of(u): the normalised O_p at ws, the record (m, l, lr, 0) at ws_s, as
+// epilogue_partial writes them) for the rows of part `part` of the tile
+// (merge_rows<D>() rows each), and stores O and L of the tile's rows below
+// nrows at o_tile and lse_tile.  A row that no part saw stores O = 0 and
+// L = -inf.
+template <typename OT, int D, int QT, typename F>
+__device__ __forceinline__ void merge_part_rows(const float *__restrict__ ws,
+                                                const float *__restrict__ ws_s, int np,
+                                                int part, F slot_of, OT *__restrict__ o_tile,
+                                                float *__restrict__ lse_tile, int nrows) {
+  constexpr int C4 = D / 4;
+  constexpr int RPP = kThreads / C4;
+  constexpr int ROWS = merge_rows<D>();
+  constexpr int NR = ROWS / RPP;
+  static_assert(NR >= 1 && ROWS % RPP == 0, "merge tiling");
+  const int c4 = threadIdx.x % C4;
+  const int r0 = part * ROWS + threadIdx.x / C4;
+  float M[NR], ls[NR], lrs[NR];
+  f32x4 acc[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    M[i] = -INFINITY;
+    ls[i] = lrs[i] = 0.f;
+    acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // four parts per round trip: their loads are issued before any is used
+  constexpr int U = 4;
+  for (int ch = 0; ch < np; ch += U) {
+    f32x4 st[U][NR], x[U][NR];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (ch + u >= np) break;
+      const size_t slot = (size_t)slot_of(ch + u);
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const size_t e = slot * QT + r0 + i * RPP;
+        st[u][i] = *reinterpret_cast<const f32x4 *>(ws_s + e * 4);
+        x[u][i] = *reinterpret_cast<const f32x4 *>(ws + e * D + 4 * c4);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (ch + u >= np) break;
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        if (st[u][i][0] == -INFINITY) continue;  // no key of this row in the part
+        const float Mn = fmaxf(M[i], st[u][i][0]);
+        const float a_old = exp2f(M[i] - Mn);  // 0 while M = -inf
+        const float a = exp2f(st[u][i][0] - Mn);
+        ls[i] = ls[i] * a_old + a * st[u][i][1];
+        lrs[i] = lrs[i] * a_old + a * st[u][i][2];
+        acc[i] = acc[i] * a_old + (a * st[u][i][2]) * x[u][i];
+        M[i] = Mn;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int r = r0 + i * RPP;
+    if (r < nrows) {
+      const float inv = lrs[i] > 0.f ? 1.0f / lrs[i] : 0.f;
+      store4<OT>(o_tile + (size_t)r * D + 4 * c4, acc[i] * inv);
+      if (c4 == 0)
+        lse_tile[r] = lrs[i] > 0.f ? (M[i] + log2f(ls[i])) * 0.69314718055994531f : -INFINITY;
+    }
+  }
+}
+
+// The split tiles of the masked grid (fa_fwd_pipe8 with S > 1): tiles
+// [0, nsp) of every slice, S parts each.
+template <typename OT, int D, int QT>
+__global__ __launch_bounds__(kThreads) void fa_merge_masked_split(
+    const float *__restrict__ ws, OT *__restrict__ o, float *__restrict__ lse, int Nq, int BH,
+    int nsp, int S) {
+  constexpr int SPLIT = QT / merge_rows<D>();
+  const int c = blockIdx.x / SPLIT;
+  const int bh = c % BH, t = c / BH;
+  const int base = (bh * nsp + t) * S;
+  const size_t r0 = (size_t)bh * Nq + (size_t)t * QT;
+  merge_part_rows<OT, D, QT>(ws, ws + (size_t)BH * nsp * S * QT * D, S, blockIdx.x % SPLIT,
+                             [&](int u) { return base + u; }, o + r0 * D, lse + r0,
+                             min(QT, Nq - t * QT));
+}
+
 template <typename OT, int D, bool CAUSAL, int QT>
 __global__ __launch_bounds__(kThreads) void fa_merge_varlen(
     const float *__restrict__ ws, OT *__restrict__ o, float *__restrict__ lse,
     const int *__restrict__ cu_q, const int *__restrict__ cu_k, int S, int H, int Tq,
     int Tk, int NC, int KC, int NT) {
-  constexpr int C4 = D / 4;
-  constexpr int RPP = kThreads / C4;
   constexpr int SPLIT = QT / merge_rows<D>();
-  constexpr int ROWS = merge_rows<D>();
-  constexpr int NR = ROWS / RPP;
-  static_assert(NR >= 1 && ROWS % RPP == 0, "merge tiling");
   const int id = blockIdx.x / SPLIT;
   const int qt = id / (H * S), hs = id % (H * S);
   const int h = hs / S, sq = hs % S;
@@ -2626,57 +2736,10 @@ __global__ __launch_bounds__(kThreads) void fa_merge_varlen(
   const int nch = varlen_split(nkt, NC, KC, kc);
   if (nch <= 1) return;  // written by its only workgroup
   const int nslots = H * NT * NC;
-  const float *ws_s = ws + (size_t)nslots * QT * D;
-  const int c4 = threadIdx.x % C4;
-  const int r0 = (blockIdx.x % SPLIT) * ROWS + threadIdx.x / C4;
-  float M[NR], ls[NR], lrs[NR];
-  f32x4 acc[NR];
-#pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    M[i] = -INFINITY;
-    ls[i] = lrs[i] = 0.f;
-    acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  // four chunks per round trip: their loads are issued before any is used
-  constexpr int U = 4;
-  for (int ch = 0; ch < nch; ch += U) {
-    f32x4 st[U][NR], x[U][NR];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (ch + u >= nch) break;
-      const size_t slot = (size_t)varlen_slot(h, NT, NC, qa, q0, QT, sq, ch + u);
-#pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        const size_t e = slot * QT + r0 + i * RPP;
-        st[u][i] = *reinterpret_cast<const f32x4 *>(ws_s + e * 4);
-        x[u][i] = *reinterpret_cast<const f32x4 *>(ws + e * D + 4 * c4);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (ch + u >= nch) break;
-#pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        if (st[u][i][0] == -INFINITY) continue;  // no key of this row in the chunk
-        const float Mn = fmaxf(M[i], st[u][i][0]);
-        const float a_old = exp2f(M[i] - Mn);  // 0 while M = -inf
-        const float a = exp2f(st[u][i][0] - Mn);
-        ls[i] = ls[i] * a_old + a * st[u][i][1];
-        lrs[i] = lrs[i] * a_old + a * st[u][i][2];
-        acc[i] = acc[i] * a_old + (a * st[u][i][2]) * x[u][i];
-        M[i] = Mn;
-      }
-    }
-  }
   const size_t base = (size_t)h * Tq + qa + q0;
-#pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    const int r = r0 + i * RPP;
-    if (q0 + r < nq) {
-      store4<OT>(o + (base + r) * D + 4 * c4, acc[i] * (1.0f / lrs[i]));
-      if (c4 == 0) lse[base + r] = (M[i] + log2f(ls[i])) * 0.69314718055994531f;
-    }
-  }
+  merge_part_rows<OT, D, QT>(ws, ws + (size_t)nslots * QT * D, nch, blockIdx.x % SPLIT,
+                             [&](int ch) { return varlen_slot(h, NT, NC, qa, q0, QT, sq, ch); },
+                             o + base * D, lse + base, nq - q0);
 }
 
 // ---------------------------------------------------------------------------
@@ -2959,7 +3022,43 @@ struct Launch {
   const CutList *cuts;        // the schedule's cut tiles
   bool masked;                // the window rule mk (grid path only)
   Mask mk;
+  size_t ws_bytes = 0;        // masked: workspace for the split tiles' parts
 };
+
+// Split of the masked grid (the rule without causality): a 256-row tile that
+// holds global queries sees every key tile, while a band tile's list holds
+// the global key tiles and about (255 + 2 (window - 1)) / 64 band tiles; one
+// workgroup walking a whole sequence would outlast the grid.  Those tiles
+// (the first ceil(min(G, Nq) / 256) of each slice) run as S parts of about a
+// band tile's list each, at least 32 key tiles; S is limited to what the
+// workspace holds, and below 2 they run whole.
+struct FwdSplit {
+  int nsp = 0, S = 1;
+};
+FwdSplit fwd_masked_split(const Mask &mk, int64_t BH, int64_t Nq, int64_t Nk, int64_t D,
+                          size_t avail) {
+  FwdSplit r;
+  const int64_t gq = mk.nglobal < Nq ? mk.nglobal : Nq;
+  if (mk.causal || gq <= 0 || Nk <= 0) return r;
+  constexpr int64_t QT = QRows<false>::value;
+  const int64_t nkt = (Nk + kBN - 1) / kBN;
+  const int64_t gk = mk.nglobal < Nk ? mk.nglobal : Nk;
+  int64_t band = (gk + kBN - 1) / kBN + (QT - 1 + 2 * ((int64_t)mk.window - 1)) / kBN + 2;
+  if (band > nkt) band = nkt;
+  const int64_t cap = band > 32 ? band : 32;
+  const int64_t nsp = (gq + QT - 1) / QT;
+  const size_t per = (size_t)(BH * nsp) * QT * (size_t)(D + 4) * 4;  // one part of each
+  int64_t S = (nkt + cap - 1) / cap;
+  if ((size_t)S > avail / per) S = (int64_t)(avail / per);
+  if (S < 2) return r;
+  r.nsp = (int)nsp;
+  r.S = (int)S;
+  return r;
+}
+size_t fwd_masked_split_bytes(const FwdSplit &sp, int64_t BH, int64_t D) {
+  if (sp.S < 2) return 0;
+  return (size_t)(BH * sp.nsp) * sp.S * QRows<false>::value * (size_t)(D + 4) * 4;
+}
 
 template <typename T, typename OT, int D, bool CAUSAL, typename KT = T>
 hipError_t launch16(const Launch &a) {
@@ -2997,18 +3096,30 @@ hipError_t launch16(const Launch &a) {
       e = go(std::false_type{});
     if (e != hipSuccess) return e;
   } else if (a.masked) {
-    if constexpr (std::is_same<KT, T>::value)
+    if constexpr (std::is_same<KT, T>::value) {
+      const FwdSplit sl = fwd_masked_split(a.mk, a.BH, a.Nq, a.Nk, D, a.ws ? a.ws_bytes : 0);
+      const int units = a.nqtg + sl.nsp * (sl.S - 1);
       hipLaunchKernelGGL((fa_fwd_pipe8<T, OT, D, CAUSAL, false, true>),
-                         dim3((unsigned)(a.BH * a.nqtg)), dim3(kThreads8), 0, a.stream,
+                         dim3((unsigned)(a.BH * units)), dim3(kThreads8), 0, a.stream,
                          (const T *)a.q, (const T *)a.k, (const T *)a.v, (OT *)a.o, a.lse,
-                         a.Nq, a.Nk, a.BH, a.nqtg, c, neg, a.mk, 1.f);
-    else
+                         a.Nq, a.Nk, a.BH, a.nqtg, c, neg, a.mk, 1.f, a.ws, sl.nsp, sl.S);
+      if (sl.S > 1) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        constexpr int QT = QRows<false>::value;
+        hipLaunchKernelGGL((fa_merge_masked_split<OT, D, QT>),
+                           dim3((unsigned)(a.BH * sl.nsp * (QT / merge_rows<D>()))),
+                           dim3(kThreads), 0, a.stream, (const float *)a.ws, (OT *)a.o, a.lse,
+                           a.Nq, a.BH, sl.nsp, sl.S);
+      }
+    } else {
       return hipErrorInvalidValue;  // the window mask runs on 16-bit inputs only
+    }
   } else {
     hipLaunchKernelGGL((fa_fwd_pipe8<T, OT, D, CAUSAL, false, false, KT>),
                        dim3((unsigned)(a.BH * a.nqtg)), dim3(kThreads8), 0, a.stream,
                        (const KT *)a.q, (const KT *)a.k, (const T *)a.v, (OT *)a.o, a.lse,
-                       a.Nq, a.Nk, a.BH, a.nqtg, c, neg, Mask{}, a.osc);
+                       a.Nq, a.Nk, a.BH, a.nqtg, c, neg, Mask{}, a.osc, (float *)nullptr, 0, 1);
   }
   return hipGetLastError();
 }
@@ -3172,8 +3283,9 @@ bool plan_ws(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, int dtype, bool caus
 int run(const void *q, const void *k, const void *v, void *o, float *lse, int64_t Nq,
         int64_t Nk, int64_t D, float scale, int causal, int dtype, const Shape &sh,
         const StreamPlan *plan, void *ws, void *stream, const Mask *mk = nullptr,
-        const Split32 *ks = nullptr) {
+        const Split32 *ks = nullptr, size_t ws_bytes = 0) {
   Launch a;
+  a.ws_bytes = ws_bytes;
   a.osc = 1.f;
   a.KC = ks ? ks->KC : 0;
   a.nsplit = ks ? ks->nsplit : 1;
@@ -3944,21 +4056,58 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int
 // every |i - j|, and keeps the rule's arithmetic in 32 bits), then one
 // workgroup per 256-row query tile of the pipelined kernel over that tile's
 // key-tile list (key_list).
-int fa_fwd_masked(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
-                  int64_t H, int64_t Nq, int64_t Nk, int64_t D, float scale, int causal,
-                  int64_t window, int64_t nglobal, int dtype, void *stream) {
-  Shape sh;
-  const int st = validate(q, k, v, o, lse, B, H, Nq, Nk, D, scale, dtype, sh);
-  if (st != FA_OK) return st;
-  if (window < 1 || nglobal < 0) return FA_ERR_SHAPE;
-  if (dtype == FA_F32) return FA_ERR_DTYPE;
+static Mask masked_rule(int64_t Nq, int64_t Nk, int causal, int64_t window, int64_t nglobal) {
   const int64_t wmax = Nq > Nk ? Nq : Nk;
   Mask mk;
   mk.causal = causal != 0;
   mk.window = (int)(window < wmax ? window : wmax);
   mk.nglobal = (int)(nglobal < wmax ? nglobal : wmax);  // >= max(Nq, Nk): every token
-  return run(q, k, v, o, lse, Nq, Nk, D, scale, causal, dtype, sh, nullptr, nullptr, stream,
-             &mk);
+  return mk;
+}
+
+int fa_fwd_masked_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+                                 int causal, int64_t window, int64_t nglobal, int dtype,
+                                 size_t *bytes) {
+  if (!bytes) return FA_ERR_NULLPTR;
+  *bytes = 0;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || window < 1 || nglobal < 0) return FA_ERR_SHAPE;
+  if (D != 16 && D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  if (dtype <= FA_F32 || dtype > FA_F16_OF32) return FA_ERR_DTYPE;
+  if (!sizes_fit(B, H, Nq, Nk, D)) return FA_ERR_SHAPE;
+  const Mask mk = masked_rule(Nq, Nk, causal, window, nglobal);
+  *bytes = fwd_masked_split_bytes(fwd_masked_split(mk, B * H, Nq, Nk, D, ~(size_t)0), B * H, D);
+  return FA_OK;
+}
+
+int fa_fwd_masked_ws(const void *q, const void *k, const void *v, void *o, float *lse,
+                     int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, float scale,
+                     int causal, int64_t window, int64_t nglobal, int dtype, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+  Shape sh;
+  const int st = validate(q, k, v, o, lse, B, H, Nq, Nk, D, scale, dtype, sh);
+  if (st != FA_OK) return st;
+  if (window < 1 || nglobal < 0) return FA_ERR_SHAPE;
+  if (dtype == FA_F32) return FA_ERR_DTYPE;
+  if (!workspace) workspace_bytes = 0;
+  if (workspace) {
+    if ((uintptr_t)workspace & 15u) return FA_ERR_ALIGN;
+    if (overlaps(workspace, workspace_bytes, q, sh.qb) ||
+        overlaps(workspace, workspace_bytes, k, sh.kb) ||
+        overlaps(workspace, workspace_bytes, v, sh.kb) ||
+        overlaps(workspace, workspace_bytes, o, sh.ob) ||
+        overlaps(workspace, workspace_bytes, lse, sh.lb))
+      return FA_ERR_OVERLAP;
+  }
+  const Mask mk = masked_rule(Nq, Nk, causal, window, nglobal);
+  return run(q, k, v, o, lse, Nq, Nk, D, scale, causal, dtype, sh, nullptr, workspace, stream,
+             &mk, nullptr, workspace_bytes);
+}
+
+int fa_fwd_masked(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
+                  int64_t H, int64_t Nq, int64_t Nk, int64_t D, float scale, int causal,
+                  int64_t window, int64_t nglobal, int dtype, void *stream) {
+  return fa_fwd_masked_ws(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, window, nglobal,
+                          dtype, nullptr, 0, stream);
 }
 
 int fa_fwd_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
