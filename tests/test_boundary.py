@@ -256,10 +256,14 @@ def test_bwd_masked_workspace_size():
     assert ws(1, 2, 4096, 4096, 64, 1, 100, 300, fa.FA_BF16) == (
         fa.FA_OK, 2 * 4096 * 4 + 2 * 3 * 2 * 2 * 128 * 64 * 4)
     # non-causal: the band cap counts both sides and the global query tiles
-    # (1 + (127 + 126) // 64 + 2 = 6 -> 32); D = 128 non-causal runs whole
+    # (1 + (127 + 126) // 64 + 2 = 6 -> 32); the dK/dV parts (larger than
+    # the dQ split's) set the size
     assert ws(1, 2, 4096, 4096, 64, 0, 64, 40, fa.FA_BF16) == (
         fa.FA_OK, 2 * 4096 * 4 + 2 * 2 * 2 * 128 * 64 * 4)
-    assert ws(1, 2, 4096, 4096, 128, 0, 64, 40, fa.FA_BF16) == (fa.FA_OK, 2 * 4096 * 4)
+    # at D = 128 non-causal dK/dV runs whole; the dQ split's query tile (40
+    # global queries: one 128-row tile, 2 parts of 128 x D fp32) is what counts
+    assert ws(1, 2, 4096, 4096, 128, 0, 64, 40, fa.FA_BF16) == (
+        fa.FA_OK, 2 * 4096 * 4 + 2 * 1 * 2 * 128 * 128 * 4)
     # no global key, a short sequence, or a band as long as the sequence:
     # nothing to split
     assert ws(1, 8, 32768, 32768, 128, 1, 512, 0, fa.FA_BF16) == (fa.FA_OK, lb)

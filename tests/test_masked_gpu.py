@@ -215,16 +215,18 @@ def test_masked_bwd_unequal_lengths(causal):
 @pytest.mark.parametrize("D,causal,Nq,Nk,window,nglobal", [
     (64, True, 4096, 4096, 100, 300),
     (64, False, 4096, 4096, 64, 40),
+    (128, False, 4500, 4500, 100, 200),
     (128, True, 5000, 5000, 256, 130),
     (128, True, 4500, 3000, 200, 129),
 ])
 def test_masked_bwd_split_global_tiles(D, causal, Nq, Nk, window, nglobal):
-    """Key tiles holding global keys are cut into parts whose partial sums a
-    merge kernel adds (fa_bwd_masked_workspace_size bytes of workspace):
-    every key of those tiles, ragged last tiles and global counts that are
-    not multiples of 128, against the oracle; and the same gradients with
-    only the row terms as workspace (the tiles run whole), to the same
-    bound."""
+    """Key tiles holding global keys (and, without the causal rule, query
+    tiles holding global queries) are cut into parts whose partial sums
+    merge kernels add (fa_bwd_masked_workspace_size bytes of workspace):
+    every key of those key tiles, every row of those query tiles, ragged
+    last tiles and global counts that are not multiples of 128, against the
+    oracle; and the same gradients with only the row terms as workspace
+    (the tiles run whole), to the same bound."""
     from workloads import gen_grad_out
 
     st, full = fa.fa_bwd_masked_workspace_size(1, 2, Nq, Nk, D, causal, window, nglobal,
@@ -234,8 +236,11 @@ def test_masked_bwd_split_global_tiles(D, causal, Nq, Nk, window, nglobal):
     kr = np.union1d(np.concatenate([np.arange(min(nsp * 128, Nk)),
                                     Nk + np.arange(min(nsp * 128, Nk))]),
                     np.random.default_rng(3000 + D).integers(0, 2 * Nk, 128))
+    nqs = 0 if causal else (min(nglobal, Nq) + 127) // 128
     qr = np.union1d(np.random.default_rng(3001 + D).integers(0, 2 * Nq, 128),
                     np.array([0, nglobal - 1, Nq - 1, Nq, 2 * Nq - 1]))
+    qr = np.union1d(qr, np.concatenate([np.arange(min(nqs * 128, Nq)),
+                                        Nq + np.arange(min(nqs * 128, Nq))]))
     compare_bwd(1, 2, Nq, Nk, D, causal, window, nglobal, seed=3010 + D, qrows=qr, krows=kr)
 
     # the unsplit grid: workspace of the row terms only
@@ -256,16 +261,17 @@ def test_masked_bwd_split_global_tiles(D, causal, Nq, Nk, window, nglobal):
                           torch.cuda.current_stream().cuda_stream)
     assert st == fa.FA_OK, fa.fa_status_str(st)
     torch.cuda.synchronize()
-    assert torch.equal(split[0], whole[0]), "dQ does not depend on the split"
+    if causal:
+        assert torch.equal(split[0], whole[0]), "causal dQ does not depend on the split"
     qn, kn, vn, gn = (t.double().numpy() for t in (q, k, v, g))
     ref = oracle.attention_bwd_masked(qn, kn, vn, gn, scale, causal, window, nglobal,
                                       qrows=qr, krows=kr, magnitudes=True)
-    sel = torch.as_tensor(kr)
-    for n in (1, 2):
+    for n in (0, 1, 2):
+        sel = torch.as_tensor(qr if n == 0 else kr)
         x = whole[n].reshape(-1, D)[sel].double().cpu().numpy()
         bound = 2 * 2.0 ** -8 * ref[n + 3] + 1e-6 * float(ref[n + 3].max()) + 1e-30
         ratio = float((np.abs(x - ref[n]) / bound).max())
-        _log(f"  unsplit {'dK' if n == 1 else 'dV'}: worst error/bound {ratio:.3f}")
+        _log(f"  unsplit {('dQ', 'dK', 'dV')[n]}: worst error/bound {ratio:.3f}")
         assert ratio <= 1.0
 
 

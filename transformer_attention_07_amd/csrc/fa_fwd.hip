@@ -1771,12 +1771,39 @@ __global__ __launch_bounds__(kThreads8) void fa_bwd_dq8(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ o, const T *__restrict__ dout, const float *__restrict__ lse,
     float *__restrict__ dl, OT *__restrict__ dq, float *__restrict__ ws, int Nq, int Nk, int BH,
-    int nqt, float c, float scale, Mask mk) {
+    int nqt, float c, float scale, Mask mk, int nsp, int S) {
   FA_DBG_BEGIN();
-  const WorkItem wi = work_item(BH, nqt, CAUSAL, 128);
+  WorkItem wi = work_item(BH, nqt, CAUSAL, 128);
   if constexpr (MASKED) {
+    // Split (S > 1, without the causal rule): the first nsp * S units are
+    // S parts of each of the tiles [0, nsp) (those holding global queries,
+    // whose lists hold every key tile); part p takes list entries
+    // [p n / S, (p + 1) n / S) and leaves fp32 partial dQ in workspace slot
+    // (bh * nsp + t) * S + p for fa_merge_dq8_split.  The first part that
+    // holds entries starts at entry 0 and writes the row terms.
+    const int u = blockIdx.x / BH;
+    int p = -1;
+    if (u < nsp * S) {
+      p = u % S;
+      wi.q0 = (u / S) * 128;
+    } else if (nsp > 0) {
+      wi.q0 = (u - nsp * S + nsp) * 128;
+    }
     int n;
     const KeyList kl = key_list(mk, wi.q0, 128, Nq, Nk, &n);
+    if (p >= 0) {
+      const int e0 = (int)((int64_t)p * n / S), e1 = (int)((int64_t)(p + 1) * n / S);
+      const int slot = (wi.bh * nsp + wi.q0 / 128) * S + p;
+      if (e0 >= e1) {  // an empty part: zero partial sums
+        float *w = ws + (size_t)slot * 128 * D;
+        for (int i = threadIdx.x; i < 128 * D; i += kThreads8) w[i] = 0.f;
+        return;
+      }
+      const PipeItem it = {wi.bh, wi.q0, e0, e1, slot};
+      dq8_run<T, OT, D, CAUSAL, true>(q, k, v, o, dout, lse, dl, dq, ws, Nq, Nk, c, scale, it,
+                                      false, mk, kl);
+      return;
+    }
     if (n == 0) {
       const int rows = min(128, Nq - wi.q0);
       const size_t r0 = (size_t)wi.bh * Nq + wi.q0;
@@ -2312,6 +2339,40 @@ __global__ __launch_bounds__(kThreads) void fa_merge_dkv8_split(const float *__r
   const int base = (bh * nsp + kt) * S;
   merge_dkv_rows<OT, D>(ws, dk, dv, Nk, scale, bh, kt, S, blockIdx.x % SPLIT,
                         [&](int kk) { return base + kk; });
+}
+
+// The split tiles of the masked dQ grid (fa_bwd_dq8 with S > 1): tiles
+// [0, nsp) of every slice, S parts each, added in part order.
+template <typename OT, int D>
+__global__ __launch_bounds__(kThreads) void fa_merge_dq8_split(const float *__restrict__ ws,
+                                                               OT *__restrict__ dq, int Nq,
+                                                               float scale, int BH, int nsp,
+                                                               int S) {
+  constexpr int C4 = D / 4;
+  constexpr int RPP = kThreads / C4;
+  constexpr int ROWS = merge_rows<D>();
+  constexpr int SPLIT = 128 / ROWS;
+  constexpr int NR = ROWS / RPP;
+  static_assert(NR >= 1 && ROWS % RPP == 0, "merge tiling");
+  const int c = blockIdx.x / SPLIT;
+  const int bh = c % BH, t = c / BH;
+  const size_t base = (size_t)(bh * nsp + t) * S;
+  const int c4 = threadIdx.x % C4;
+  const int r0 = (blockIdx.x % SPLIT) * ROWS + threadIdx.x / C4;
+  f32x4 acc[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kk = 0; kk < S; ++kk) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+      acc[i] += *reinterpret_cast<const f32x4 *>(
+          ws + ((base + kk) * 128 + r0 + i * RPP) * D + 4 * c4);
+  }
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int row = t * 128 + r0 + i * RPP;
+    if (row < Nq) store4<OT>(dq + ((size_t)bh * Nq + row) * D + 4 * c4, acc[i] * scale);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -3601,17 +3662,52 @@ bool dq8_plan(int64_t BH, int64_t Nq, int64_t Nk, int64_t D, bool causal, int cu
   return plan_rows(BH, Nq, Nk, 128, kDqLead, 0, causal, cus, sp);
 }
 
+// Split of the masked dQ grid (the rule without causality): a 128-row tile
+// that holds global queries sees every key tile, a band tile the global key
+// tiles and about (127 + 2 (window - 1)) / 64 band tiles.  Those tiles (the
+// first ceil(min(G, Nq) / 128) of each slice) run as S parts of about a
+// band tile's list each, at least 32 key tiles; S is limited to what the
+// workspace holds, and below 2 they run whole.
+struct QSplit {
+  int nsp = 0, S = 1;
+};
+QSplit dq8_split(const Mask &mk, int64_t BH, int64_t Nq, int64_t Nk, int64_t D, size_t avail) {
+  QSplit r;
+  const int64_t gq = mk.nglobal < Nq ? mk.nglobal : Nq;
+  if (mk.causal || gq <= 0 || Nk <= 0) return r;
+  const int64_t nkt = (Nk + kBN - 1) / kBN;
+  const int64_t gk = mk.nglobal < Nk ? mk.nglobal : Nk;
+  int64_t band = (gk + kBN - 1) / kBN + (127 + 2 * ((int64_t)mk.window - 1)) / kBN + 2;
+  if (band > nkt) band = nkt;
+  const int64_t cap = band > 32 ? band : 32;
+  const int64_t nsp = (gq + 127) / 128;
+  const size_t per = (size_t)(BH * nsp) * 128 * (size_t)D * 4;  // one part of each
+  int64_t S = (nkt + cap - 1) / cap;
+  if ((size_t)S > avail / per) S = (int64_t)(avail / per);
+  if (S < 2) return r;
+  r.nsp = (int)nsp;
+  r.S = (int)S;
+  return r;
+}
+
 template <typename T, typename OT, int D, bool CAUSAL>
 hipError_t launch_dq8(const void *q, const void *k, const void *v, const void *o,
                       const void *dout, const float *lse, float *dl, void *dq, int Nq, int Nk,
                       int BH, float c, float scale, const StreamPlan *sp, float *ws,
-                      const Mask *mk, hipStream_t s) {
-  if (mk) {  // the window mask: one workgroup per tile over its key list
+                      size_t ws_bytes, const Mask *mk, hipStream_t s) {
+  if (mk) {  // the window mask: one workgroup per tile (or part) over its key list
     const int nqt = (Nq + 127) / 128;
-    hipLaunchKernelGGL((fa_bwd_dq8<T, OT, D, CAUSAL, true>), dim3((unsigned)(BH * nqt)),
+    const QSplit sl = dq8_split(*mk, BH, Nq, Nk, D, ws ? ws_bytes : 0);
+    const int units = nqt + sl.nsp * (sl.S - 1);
+    hipLaunchKernelGGL((fa_bwd_dq8<T, OT, D, CAUSAL, true>), dim3((unsigned)(BH * units)),
                        dim3(kThreads8), 0, s, (const T *)q, (const T *)k, (const T *)v,
                        (const T *)o, (const T *)dout, lse, dl, (OT *)dq, ws, Nq, Nk, BH, nqt, c,
-                       scale, *mk);
+                       scale, *mk, sl.nsp, sl.S);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || sl.S < 2) return e;
+    hipLaunchKernelGGL((fa_merge_dq8_split<OT, D>),
+                       dim3((unsigned)(BH * sl.nsp * (128 / merge_rows<D>()))), dim3(kThreads),
+                       0, s, (const float *)ws, (OT *)dq, Nq, scale, BH, sl.nsp, sl.S);
     return hipGetLastError();
   }
   if (sp) {
@@ -3631,24 +3727,24 @@ hipError_t launch_dq8(const void *q, const void *k, const void *v, const void *o
   hipLaunchKernelGGL((fa_bwd_dq8<T, OT, D, CAUSAL>), dim3((unsigned)(BH * nqt)),
                      dim3(kThreads8), 0, s, (const T *)q, (const T *)k, (const T *)v,
                      (const T *)o, (const T *)dout, lse, dl, (OT *)dq, ws, Nq, Nk, BH, nqt, c,
-                     scale, Mask{});
+                     scale, Mask{}, 0, 1);
   return hipGetLastError();
 }
 template <typename T, typename OT>
 hipError_t dq8_d(int D, bool causal, const void *q, const void *k, const void *v,
                  const void *o, const void *dout, const float *lse, float *dl, void *dq, int Nq,
                  int Nk,
-                 int BH, float c, float scale, const StreamPlan *sp, float *ws, const Mask *mk,
+                 int BH, float c, float scale, const StreamPlan *sp, float *ws, size_t ws_bytes, const Mask *mk,
                  hipStream_t s) {
   if (D == 64)
     return causal ? launch_dq8<T, OT, 64, true>(q, k, v, o, dout, lse, dl, dq, Nq, Nk, BH, c,
-                                                scale, sp, ws, mk, s)
+                                                scale, sp, ws, ws_bytes, mk, s)
                   : launch_dq8<T, OT, 64, false>(q, k, v, o, dout, lse, dl, dq, Nq, Nk, BH, c,
-                                                 scale, sp, ws, mk, s);
+                                                 scale, sp, ws, ws_bytes, mk, s);
   return causal ? launch_dq8<T, OT, 128, true>(q, k, v, o, dout, lse, dl, dq, Nq, Nk, BH, c, scale,
-                                               sp, ws, mk, s)
+                                               sp, ws, ws_bytes, mk, s)
                 : launch_dq8<T, OT, 128, false>(q, k, v, o, dout, lse, dl, dq, Nq, Nk, BH, c,
-                                                scale, sp, ws, mk, s);
+                                                scale, sp, ws, ws_bytes, mk, s);
 }
 }  // namespace
 
@@ -3823,19 +3919,24 @@ __attribute__((visibility("hidden"))) bool fa_internal_bwd_dkdv8(
   }
 }
 
-// Bytes of dK/dV partials the split of the masked grid uses for this
-// problem and rule (0 when the pipelined kernel does not take the rule, or
-// no tile is split).
+// Bytes of partial sums the splits of the masked dQ and dK/dV grids use for
+// this problem and rule (the larger of the two: dQ runs first and dK/dV
+// after it; 0 when neither pipelined kernel splits a tile).
 __attribute__((visibility("hidden"))) size_t fa_internal_masked_dkv8_bytes(
     int64_t BH, int64_t Nq, int64_t Nk, int64_t D, const int *mask3) {
-  if ((D != 64 && D != 128) || (!mask3[0] && D == 128)) return 0;
+  if (D != 64 && D != 128) return 0;
   Mask m{};
   m.causal = mask3[0];
   m.window = mask3[1];
   m.nglobal = mask3[2];
   const KvSplit sl = dkv8_split(m, BH, Nq, Nk, D, ~(size_t)0);
-  if (sl.S < 2) return 0;
-  return (size_t)(BH * sl.nsp) * sl.S * 2 * 128 * (size_t)D * 4;
+  // non-causal at D = 128 dK/dV runs the earlier kernel (no split)
+  const bool kv_split = sl.S >= 2 && (mask3[0] || D != 128);
+  const size_t kv = kv_split ? (size_t)(BH * sl.nsp) * sl.S * 2 * 128 * (size_t)D * 4 : 0;
+  // dQ runs first and dK/dV after it: they share the region
+  const QSplit sq = dq8_split(m, BH, Nq, Nk, D, ~(size_t)0);
+  const size_t qb = sq.S < 2 ? 0 : (size_t)(BH * sq.nsp) * sq.S * 128 * (size_t)D * 4;
+  return kv > qb ? kv : qb;
 }
 
 // Bytes of dQ partials the stream schedule may need for this problem on a
@@ -3886,19 +3987,19 @@ __attribute__((visibility("hidden"))) bool fa_internal_bwd_dq8(
   switch (dtype) {
     case FA_BF16:
       *err = dq8_d<__bf16, __bf16>(D, causal, q, k, v, o, dout, lse, dl, dq, Nq, Nk, BH, c, scale,
-                                   use, w, mk, s);
+                                   use, w, ws_bytes, mk, s);
       return true;
     case FA_BF16_OF32:
       *err = dq8_d<__bf16, float>(D, causal, q, k, v, o, dout, lse, dl, dq, Nq, Nk, BH, c, scale,
-                                  use, w, mk, s);
+                                  use, w, ws_bytes, mk, s);
       return true;
     case FA_F16:
       *err = dq8_d<_Float16, _Float16>(D, causal, q, k, v, o, dout, lse, dl, dq, Nq, Nk, BH, c,
-                                       scale, use, w, mk, s);
+                                       scale, use, w, ws_bytes, mk, s);
       return true;
     case FA_F16_OF32:
       *err = dq8_d<_Float16, float>(D, causal, q, k, v, o, dout, lse, dl, dq, Nq, Nk, BH, c,
-                                    scale, use, w, mk, s);
+                                    scale, use, w, ws_bytes, mk, s);
       return true;
     default: return false;
   }
