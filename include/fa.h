@@ -469,13 +469,16 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o,
 /*
  * fa_bwd_masked_workspace_size -- device scratch bytes for fa_bwd_masked
  * with this rule (written to *bytes): B * H * Nq * 4 (the row terms, as
- * fa_bwd_workspace_size); at D = 64 (and D = 128 under the causal rule)
- * with nglobal > 0, when the 128-key tiles that hold global keys meet
- * many more query tiles than a band tile does, that rounded up to 256
- * bytes plus B * H * ceil(min(nglobal, Nk) / 128) * P slots of 2 x 128 x D
- * fp32, P being the number of parts each such tile's query walk is cut
- * into (each part about a band tile's walk, at least 32 query tiles of
- * 64 rows).  The query needs no device.  Returns FA_OK, FA_ERR_NULLPTR,
+ * fa_bwd_workspace_size); at D = 64 and 128 with nglobal > 0, when tiles
+ * that hold global tokens meet many more tiles than a band tile does, that
+ * rounded up to 256 bytes plus the larger of two part areas: dK/dV (D = 64,
+ * and D = 128 under the causal rule), B * H * ceil(min(nglobal, Nk) / 128)
+ * * P slots of 2 x 128 x D fp32 for the 128-key tiles that hold global
+ * keys; dQ (without the causal rule), B * H * ceil(min(nglobal, Nq) / 128)
+ * * P' slots of 128 x D fp32 for the 128-row tiles that hold global
+ * queries.  P and P' are the numbers of parts each such tile's walk is cut
+ * into (each part about a band tile's walk, at least 32 tiles of 64).
+ * The query needs no device.  Returns FA_OK, FA_ERR_NULLPTR,
  * FA_ERR_SHAPE (also window < 1 or nglobal < 0), FA_ERR_HEAD_DIM or
  * FA_ERR_DTYPE.
  */
@@ -490,8 +493,8 @@ int fa_bwd_masked_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk,
  * without a visible key get dq = 0; keys no row sees get dk = dv = 0.
  * Query and key blocks without a visible pair are skipped.  The workspace
  * needs the row terms (B * H * Nq * 4 bytes); with
- * fa_bwd_masked_workspace_size bytes the key tiles that hold global keys
- * are cut into parts that run in parallel and whose fp32 partial sums are
+ * fa_bwd_masked_workspace_size bytes the tiles that hold global tokens are
+ * cut into parts that run in parallel and whose fp32 partial sums are
  * added in part order (deterministic; with less they run whole, the same
  * results within the rounding of the sums' order).  Arguments, dtypes,
  * head dims and status codes as fa_bwd; window < 1 or nglobal < 0 is
