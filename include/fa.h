@@ -1,7 +1,8 @@
 /*
  * fa.h -- C ABI of the MI355X (gfx950) FlashAttention-2 library: the
  * forward pass (fa_fwd, fa_fwd_ws; fa_fwd_varlen and fa_fwd_varlen_ws for
- * variable-length batches, fa_fwd_masked for local-window + global-token masks, fa_fwd_fp8
+ * variable-length batches, fa_fwd_masked and fa_fwd_masked_ws for
+ * local-window + global-token masks, fa_fwd_fp8
  * and fa_fwd_fp8_ws for FP8 inputs) and its
  * backward pass (fa_bwd, fa_bwd_varlen, fa_bwd_masked).
  *
