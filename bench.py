@@ -137,6 +137,23 @@ def write_traffic(run_dir: str, workload: str = "bf16_b8_n4096_d128_causal") -> 
     return out
 
 
+def masked_visible(N: int, W: int, G: int, causal):
+    """Visible keys of each row of an N x N local-window + global-token mask
+    (the library's rule): causal, all j <= i for a global row, else the
+    window [i - W + 1, i] plus the global keys before it; non-causal, every
+    key for a global row, else the band |i - j| < W plus the global keys
+    outside it."""
+    import numpy as np
+
+    i = np.arange(N, dtype=np.int64)
+    lo = np.maximum(0, i - W + 1)
+    if causal:
+        return np.where(i < G, i + 1, (i - lo + 1) + np.minimum(G, lo))
+    hi = np.minimum(N - 1, i + W - 1)
+    band = (hi - lo + 1) + np.minimum(G, lo) + np.maximum(0, np.minimum(G, N) - hi - 1)
+    return np.where(i < G, N, band)
+
+
 def device_facts(torch, dev):
     """What the box reports about itself: compute units, the maximum shader
     clock (HIP device attribute, else the highest level the driver lists in
@@ -362,6 +379,9 @@ def main() -> int:
                     help="time fa_fwd_masked instead: B=1 H=8 N=32768 D=128 causal bf16 "
                          "under a local window W with G global tokens; flops counted "
                          "over the visible pairs only (4*D each)")
+    ap.add_argument("--noncausal", action="store_true",
+                    help="with --masked: the rule without causality (global queries see "
+                         "every key; fa_fwd_masked_ws with its workspace)")
     ap.add_argument("--write-traffic", default=None, metavar="DIR",
                     help="write profiles/traffic_<workload>.json from the rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE runs under DIR (no GPU work)")
@@ -441,17 +461,24 @@ def main() -> int:
         o = torch.empty(q.shape, dtype=out_dt, device=dev)
         lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
         scale = 1.0 / math.sqrt(MD)
-        i = np.arange(MN, dtype=np.int64)
-        lo = np.maximum(0, i - W + 1)  # causal window [lo, i]
-        # visible keys of row i: all j <= i for a global row, else the window
-        # plus the global keys before it
-        per_row = np.where(i < G, i + 1, (i - lo + 1) + np.minimum(G, lo))
+        MC = 0 if args.noncausal else 1
+        per_row = masked_visible(MN, W, G, MC)
         masked = {"window": W, "global": G, "visible_pairs": int(per_row.sum()) * MB * MH,
-                  "shape": [MB, MH, MN, MD]}
-        argv = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), MB, MH,
-                MN, MN, MD, scale, 1, W, G, code, sp)
-        call = lib.fa_fwd_masked
-        args.entry = "fa_fwd_masked"
+                  "shape": [MB, MH, MN, MD], "causal": bool(MC)}
+        if MC:
+            argv = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), MB,
+                    MH, MN, MN, MD, scale, 1, W, G, code, sp)
+            call = lib.fa_fwd_masked
+            args.entry = "fa_fwd_masked"
+        else:
+            st, fws_bytes = fa.fa_fwd_masked_workspace_size(MB, MH, MN, MN, MD, 0, W, G, code)
+            if st != 0:
+                raise RuntimeError(f"fa_fwd_masked_workspace_size: {fa.fa_status_str(st)}")
+            fws = torch.empty(max(fws_bytes, 16), dtype=torch.uint8, device=dev)
+            argv = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), MB,
+                    MH, MN, MN, MD, scale, 0, W, G, code, fws.data_ptr(), fws_bytes, sp)
+            call = lib.fa_fwd_masked_ws
+            args.entry = "fa_fwd_masked_ws"
         ws_bytes = 0
         if bwd:
             from workloads import gen_grad_out
@@ -461,14 +488,14 @@ def main() -> int:
                 raise RuntimeError(f"forward failed: {fa.fa_status_str(st)}")
             g = gen_grad_out(MB, MH, MN, MD, seed=2602, dtype="bf16").to(dev)
             dq, dk, dv = (torch.empty(x.shape, dtype=out_dt, device=dev) for x in (q, k, v))
-            st, ws_bytes = fa.fa_bwd_masked_workspace_size(MB, MH, MN, MN, MD, 1, W, G, code)
+            st, ws_bytes = fa.fa_bwd_masked_workspace_size(MB, MH, MN, MN, MD, MC, W, G, code)
             if st != 0:
                 raise RuntimeError(f"fa_bwd_masked_workspace_size failed: "
                                    f"{fa.fa_status_str(st)}")
             bws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
             argv = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                     g.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), MB, MH, MN, MN,
-                    MD, scale, 1, W, G, code, bws.data_ptr(), ws_bytes, sp)
+                    MD, scale, MC, W, G, code, bws.data_ptr(), ws_bytes, sp)
             call = lib.fa_bwd_masked
             args.entry = "fa_bwd_masked"
     if args.varlen:
@@ -617,13 +644,14 @@ def main() -> int:
     if masked is not None:
         # the masked mode runs its own long-sequence shape, named as such
         MB, MH, MN, MD = masked["shape"]
-        tag = f"B{MB} H{MH} N{MN} D{MD} causal, window {masked['window']}, " \
+        cz = "causal" if masked["causal"] else "non-causal"
+        tag = f"B{MB} H{MH} N{MN} D{MD} {cz}, window {masked['window']}, " \
               f"{masked['global']} global, visible pairs"
         metric = (f"attention {'bwd' if bwd else 'fwd'} TFLOP/s + % bf16 MFMA peak "
                   f"(masked {tag})")
-        name = (f"bf16_b{MB}_h{MH}_n{MN}_d{MD}_causal_w{masked['window']}"
+        name = (f"bf16_b{MB}_h{MH}_n{MN}_d{MD}_{cz.replace('-', '')}_w{masked['window']}"
                 f"_g{masked['global']}")
-        shape = {"B": MB, "H": MH, "Nq": MN, "Nk": MN, "D": MD, "causal": True}
+        shape = {"B": MB, "H": MH, "Nq": MN, "Nk": MN, "D": MD, "causal": masked["causal"]}
     line = {
         "metric": metric,
         "value": round(value, 2),
@@ -681,11 +709,10 @@ def main() -> int:
             MB, MH, MN, MD = masked["shape"]
             qn, kn, vn = (x.double().cpu().numpy() for x in (q, k, v))
             W, G = masked["window"], masked["global"]
-            i_all = np.arange(MN, dtype=np.int64)
-            lo = np.maximum(0, i_all - W + 1)
-            per_row = np.where(i_all < G, i_all + 1, (i_all - lo + 1) + np.minimum(G, lo))
+            per_row = masked_visible(MN, W, G, masked["causal"])
             line["cpu_baseline"] = cpu_baseline_rows(
-                lambda r: oracle.attention_masked(qn, kn, vn, scale, True, W, G, rows=r),
+                lambda r: oracle.attention_masked(qn, kn, vn, scale, masked["causal"], W, G,
+                                                  rows=r),
                 MB * MH * MN, flops, lambda r: float(per_row[np.asarray(r) % MN].sum()),
                 args.cpu_seconds, "masked oracle")
         elif fp8 is not None:
